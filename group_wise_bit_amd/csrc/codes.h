@@ -1,0 +1,238 @@
+// Code packing and unpacking for the tiled layout (see include/qlin.h), and the
+// fp16 "magic number" decode: a code c OR-ed into the low mantissa bits of
+// fp16 1024.0 reads as exactly 1024 + c, so one AND-OR per word turns two
+// codes into an fp16 pair, and subtracting 1024 + z leaves q - z exactly.
+#pragma once
+
+#include "device_common.h"
+
+namespace qlin {
+
+// ---------------------------------------------------------------- packing --
+// 64 codes (0..qmax, held as floats) -> 2*BITS words of one block.
+template <int BITS>
+__device__ __forceinline__ void pack_block(const float* code, uint32_t* out) {
+  if constexpr (BITS == 3) {
+#pragma unroll
+    for (int run = 0; run < 2; ++run) {
+      uint32_t lo0 = 0, lo1 = 0, hi = 0;
+#pragma unroll
+      for (int c = 0; c < 32; ++c) {
+        const uint32_t v = (uint32_t)code[32 * run + c];
+        const int u = c >> 4, i = c & 15, p = i >> 1, e = i & 1;
+        const int lpos = 16 * e + 2 * p;
+        if (u == 0) lo0 |= (v & 3u) << lpos; else lo1 |= (v & 3u) << lpos;
+        int hb = (p < 4 ? 2 * p + 2 : 2 * (p - 4) + 3) + 16 * e;
+        if (u == 1) hb = (hb + 8) & 31;
+        hi |= ((v >> 2) & 1u) << hb;
+      }
+      out[3 * run + 0] = lo0;
+      out[3 * run + 1] = lo1;
+      out[3 * run + 2] = hi;
+    }
+  } else {
+    constexpr int per = 32 / BITS;
+#pragma unroll
+    for (int w = 0; w < 2 * BITS; ++w) {
+      uint32_t word = 0;
+#pragma unroll
+      for (int i = 0; i < per; ++i) {
+        const uint32_t v = (uint32_t)code[w * per + i];
+        word |= v << (16 * (i & 1) + BITS * (i >> 1));
+      }
+      out[w] = word;
+    }
+  }
+}
+
+// --------------------------------------------------- GEMV decode (fp16 pairs)
+// Per (lane, block): the block's sum_k x_k * (q_k - z), unscaled, in fp32.
+// Codes come out of a word scaled by S in {1, 4, 16, 64} (their bit offset in
+// the half-word); (1024 + S*q) - (1024 + S*z) = S*(q - z) exactly in fp16, the
+// dot product with an fp16 x pair is exact per product, and each scale class
+// keeps its own fp32 accumulator, divided by S (exact) at the end.
+__device__ __forceinline__ uint32_t zconst(int z, int shift) {
+  return (0x6400u + ((uint32_t)z << shift)) * 0x00010001u;
+}
+
+template <int BITS>
+__device__ __forceinline__ float block_dot(const uint32_t* wd, const f16x2* __restrict__ xb, int z, uint32_t kMagic) {
+  if constexpr (BITS == 4) {
+    const f16x2 c1 = as_h2(zconst(z, 0)), c16 = as_h2(zconst(z, 4));
+    float a0 = 0.f, a1 = 0.f, b0 = 0.f, b1 = 0.f;
+#pragma unroll
+    for (int w = 0; w < 8; ++w) {
+      const uint32_t v = wd[w], vs = v >> 8;
+      const f16x2 h0 = as_h2((v & 0x000F000Fu) | kMagic) - c1;
+      const f16x2 h1 = as_h2((v & 0x00F000F0u) | kMagic) - c16;
+      const f16x2 h2 = as_h2((vs & 0x000F000Fu) | kMagic) - c1;
+      const f16x2 h3 = as_h2((vs & 0x00F000F0u) | kMagic) - c16;
+      a0 = __builtin_amdgcn_fdot2(h0, xb[4 * w + 0], a0, false);
+      b0 = __builtin_amdgcn_fdot2(h1, xb[4 * w + 1], b0, false);
+      a1 = __builtin_amdgcn_fdot2(h2, xb[4 * w + 2], a1, false);
+      b1 = __builtin_amdgcn_fdot2(h3, xb[4 * w + 3], b1, false);
+    }
+    return (a0 + a1) + (b0 + b1) * 0.0625f;
+  } else if constexpr (BITS == 2) {
+    f16x2 c[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) c[p] = as_h2(zconst(z, 2 * p));
+    float a[4] = {0.f, 0.f, 0.f, 0.f}, b[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const uint32_t v = wd[w], vs = v >> 8;
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const uint32_t m = (3u << (2 * p)) | (3u << (16 + 2 * p));
+        const f16x2 h = as_h2((v & m) | kMagic) - c[p];
+        const f16x2 g = as_h2((vs & m) | kMagic) - c[p];
+        a[p] = __builtin_amdgcn_fdot2(h, xb[8 * w + p], a[p], false);
+        b[p] = __builtin_amdgcn_fdot2(g, xb[8 * w + 4 + p], b[p], false);
+      }
+    }
+    return (a[0] + b[0]) + (a[1] + b[1]) * 0.25f + (a[2] + b[2]) * 0.0625f +
+           (a[3] + b[3]) * 0.015625f;
+  } else if constexpr (BITS == 3) {
+    f16x2 c[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) c[p] = as_h2(zconst(z, 2 * p));
+    float a[4] = {0.f, 0.f, 0.f, 0.f}, b[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int run = 0; run < 2; ++run) {
+      const uint32_t H = wd[3 * run + 2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const uint32_t L = wd[3 * run + u];
+        const uint32_t Hu = u ? __builtin_amdgcn_alignbit(H, H, 8) : H;
+        const uint32_t Ls = L >> 8, Hs = Hu >> 1;
+        const int xo = 16 * run + 8 * u;
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          const uint32_t m2 = (3u << (2 * p)) | (3u << (16 + 2 * p));
+          const uint32_t m1 = (1u << (2 * p + 2)) | (1u << (2 * p + 18));
+          // bit-field insert of L into H under m2, then keep the code bits
+          const uint32_t tl = (L & m2) | (Hu & ~m2), ts = (Ls & m2) | (Hs & ~m2);
+          const f16x2 h = as_h2((tl & (m2 | m1)) | kMagic) - c[p];
+          const f16x2 g = as_h2((ts & (m2 | m1)) | kMagic) - c[p];
+          a[p] = __builtin_amdgcn_fdot2(h, xb[xo + p], a[p], false);
+          b[p] = __builtin_amdgcn_fdot2(g, xb[xo + 4 + p], b[p], false);
+        }
+      }
+    }
+    return (a[0] + b[0]) + (a[1] + b[1]) * 0.25f + (a[2] + b[2]) * 0.0625f +
+           (a[3] + b[3]) * 0.015625f;
+  } else {  // BITS == 8
+    const f16x2 c = as_h2(zconst(z, 0));
+    float a0 = 0.f, a1 = 0.f, b0 = 0.f, b1 = 0.f;
+#pragma unroll
+    for (int w = 0; w < 16; w += 2) {
+      const uint32_t v = wd[w], u = wd[w + 1];
+      // bytes [b0, 0x64, b2, 0x64] and [b1, 0x64, b3, 0x64]
+      const f16x2 h0 = as_h2(__builtin_amdgcn_perm(0x64646464u, v, 0x04020400u)) - c;
+      const f16x2 h1 = as_h2(__builtin_amdgcn_perm(0x64646464u, v, 0x04030401u)) - c;
+      const f16x2 g0 = as_h2(__builtin_amdgcn_perm(0x64646464u, u, 0x04020400u)) - c;
+      const f16x2 g1 = as_h2(__builtin_amdgcn_perm(0x64646464u, u, 0x04030401u)) - c;
+      a0 = __builtin_amdgcn_fdot2(h0, xb[2 * w + 0], a0, false);
+      b0 = __builtin_amdgcn_fdot2(h1, xb[2 * w + 1], b0, false);
+      a1 = __builtin_amdgcn_fdot2(g0, xb[2 * w + 2], a1, false);
+      b1 = __builtin_amdgcn_fdot2(g1, xb[2 * w + 3], b1, false);
+    }
+    return (a0 + a1) + (b0 + b1);
+  }
+}
+
+// ------------------------------------------- MFMA operand decode (bf16 x 8)
+// Eight consecutive codes of a block ("chunk") -> the exact fp32 weights
+// s * (q - z) -> bf16 (round to nearest even).  The fp32 value is exact: the
+// product (1024 + S*q) * (s/S) has at most 22 significant bits, the constant
+// s * (1024/S + z) likewise, and their difference s * (q - z) is representable,
+// so the fma rounds nothing.
+struct Deq {
+  float sS[4];   // s / S for S = 1, 4, 16, 64
+  float cS[4];   // -s * (1024/S + z)
+};
+
+__device__ __forceinline__ Deq make_deq(float s, int z) {
+  Deq d;
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const float inv = 1.0f / (float)(1 << (2 * p));   // exact power of two
+    d.sS[p] = s * inv;
+    d.cS[p] = -s * (float)((1024 >> (2 * p)) + z);
+  }
+  return d;
+}
+
+__device__ __forceinline__ void deq_pair(uint32_t magic_pair, float sS, float cS, float& lo, float& hi) {
+  const f16x2 h = as_h2(magic_pair);
+  lo = __builtin_fmaf((float)h.x, sS, cS);
+  hi = __builtin_fmaf((float)h.y, sS, cS);
+}
+
+__device__ __forceinline__ bf16x8 to_bf16x8(const float* f) {
+  bf16x8 r;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) r[i] = (__bf16)f[i];
+  return r;
+}
+
+// int4: one word = 8 codes.  S=1 for (v & 0x000F000F), S=16 for (v & 0x00F000F0).
+__device__ __forceinline__ bf16x8 deq_chunk4(uint32_t v, const Deq& d, uint32_t kMagic) {
+  float f[8];
+  const uint32_t vs = v >> 8;
+  deq_pair((v & 0x000F000Fu) | kMagic, d.sS[0], d.cS[0], f[0], f[1]);
+  deq_pair((v & 0x00F000F0u) | kMagic, d.sS[2], d.cS[2], f[2], f[3]);
+  deq_pair((vs & 0x000F000Fu) | kMagic, d.sS[0], d.cS[0], f[4], f[5]);
+  deq_pair((vs & 0x00F000F0u) | kMagic, d.sS[2], d.cS[2], f[6], f[7]);
+  return to_bf16x8(f);
+}
+
+// int2: half `hv` of a word (0: pairs 0..3 from v, 1: pairs 4..7 from v >> 8).
+__device__ __forceinline__ bf16x8 deq_chunk2(uint32_t v, const Deq& d, uint32_t kMagic) {
+  float f[8];
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const uint32_t m = (3u << (2 * p)) | (3u << (16 + 2 * p));
+    deq_pair((v & m) | kMagic, d.sS[p], d.cS[p], f[2 * p], f[2 * p + 1]);
+  }
+  return to_bf16x8(f);
+}
+
+// int3: low-bit word L (already shifted for the upper pairs) and high-bit word
+// H (already rotated / shifted to line up with L).
+__device__ __forceinline__ bf16x8 deq_chunk3(uint32_t L, uint32_t H, const Deq& d, uint32_t kMagic) {
+  float f[8];
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const uint32_t m2 = (3u << (2 * p)) | (3u << (16 + 2 * p));
+    const uint32_t m1 = (1u << (2 * p + 2)) | (1u << (2 * p + 18));
+    const uint32_t t = (L & m2) | (H & ~m2);
+    deq_pair((t & (m2 | m1)) | kMagic, d.sS[p], d.cS[p], f[2 * p], f[2 * p + 1]);
+  }
+  return to_bf16x8(f);
+}
+
+// int8: two words = 8 codes.
+__device__ __forceinline__ bf16x8 deq_chunk8(uint32_t v, uint32_t u, const Deq& d) {
+  float f[8];
+  deq_pair(__builtin_amdgcn_perm(0x64646464u, v, 0x04020400u), d.sS[0], d.cS[0], f[0], f[1]);
+  deq_pair(__builtin_amdgcn_perm(0x64646464u, v, 0x04030401u), d.sS[0], d.cS[0], f[2], f[3]);
+  deq_pair(__builtin_amdgcn_perm(0x64646464u, u, 0x04020400u), d.sS[0], d.cS[0], f[4], f[5]);
+  deq_pair(__builtin_amdgcn_perm(0x64646464u, u, 0x04030401u), d.sS[0], d.cS[0], f[6], f[7]);
+  return to_bf16x8(f);
+}
+
+// fp16 x 8 (one uint4) -> bf16 x 8, round to nearest even.
+__device__ __forceinline__ bf16x8 h8_to_bf16x8(uint4 v) {
+  float f[8];
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const f16x2 h = as_h2(w[i]);
+    f[2 * i] = (float)h.x;
+    f[2 * i + 1] = (float)h.y;
+  }
+  return to_bf16x8(f);
+}
+
+}  // namespace qlin

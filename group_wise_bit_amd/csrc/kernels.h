@@ -1,0 +1,605 @@
+// qlin kernels for gfx950.  One wave owns one 64-row tile of W (lane = row)
+// in the quantizer and the GEMV kernels; the GEMMs feed bf16 MFMA.
+#pragma once
+
+#include "codes.h"
+
+namespace qlin {
+
+// -------------------------------------------------------------- utilities --
+// Load the 64 fp16 values of (row, block j) of a row-major fp16 matrix.
+__device__ __forceinline__ void load_row_block(const uint16_t* __restrict__ w16, int64_t ld,
+                                               int row, int j, bool valid, float* w) {
+  if (valid) {
+    const uint4* p = reinterpret_cast<const uint4*>(w16 + (int64_t)row * ld + (int64_t)j * kBlock);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint4 v = p[i];
+      const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const f16x2 h = as_h2(u[e]);
+        w[8 * i + 2 * e] = (float)h.x;
+        w[8 * i + 2 * e + 1] = (float)h.y;
+      }
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 64; ++i) w[i] = 0.f;
+  }
+}
+
+// Scale and zero from a group's extremes (fp32 subtract, IEEE divide, fp16
+// round-to-nearest-even, zero point from the stored scale, ties to even).
+__device__ __forceinline__ void scale_zero(float mn, float mx, int qmax, uint16_t& s16bits,
+                                           float& s, int& z) {
+  const float s32 = __fdiv_rn(mx - mn, (float)qmax);
+  const f16 s16 = (f16)s32;
+  s = (float)s16;
+  s16bits = __builtin_bit_cast(uint16_t, s16);
+  z = 0;
+  if (s != 0.f) {
+    const float zr = __builtin_rintf(__fdiv_rn(-mn, s));
+    z = (int)clampf(zr, 0.f, (float)qmax);
+  } else {
+    s16bits = 0;
+  }
+}
+
+template <int BITS>
+__device__ __forceinline__ void codes_and_store(const float* w, float s, int z,
+                                                uint32_t* __restrict__ dst) {
+  constexpr int qmax = (1 << BITS) - 1;
+  const RtnParams p = rtn_params(s, z, qmax);
+  float code[64];
+#pragma unroll
+  for (int c = 0; c < 64; ++c) {
+    float q0 = __builtin_rintf(w[c] * p.r);
+    q0 = rtn_fix(w[c], q0, p);
+    code[c] = clampf(q0, p.lo, p.hi) + (float)z;
+  }
+  uint32_t out[2 * BITS];
+  pack_block<BITS>(code, out);
+  if constexpr (BITS == 3) {
+    uint2* d2 = reinterpret_cast<uint2*>(dst);
+#pragma unroll
+    for (int i = 0; i < 3; ++i) d2[i] = make_uint2(out[2 * i], out[2 * i + 1]);
+  } else {
+    uint4* d4 = reinterpret_cast<uint4*>(dst);
+#pragma unroll
+    for (int i = 0; i < BITS / 2; ++i)
+      d4[i] = make_uint4(out[4 * i], out[4 * i + 1], out[4 * i + 2], out[4 * i + 3]);
+  }
+}
+
+// ------------------------------------------------------------- quantizer --
+// Group 64.  grid = (tiles, ceil(kb / WAVES)); wave w of block y handles
+// K-block j = y*WAVES + w for the 64 rows of tile x.
+template <int BITS, int WAVES>
+__global__ __launch_bounds__(WAVES * 64) void k_quantize_g64(
+    const uint16_t* __restrict__ w16, int64_t ld, int n, int kb,
+    uint32_t* __restrict__ codes, uint16_t* __restrict__ scale, uint8_t* __restrict__ zero) {
+  constexpr int qmax = (1 << BITS) - 1;
+  const int lane = lane_id(), wave = wave_id();
+  const int t = blockIdx.x;
+  const int j = blockIdx.y * WAVES + wave;
+  if (j >= kb) return;
+  const int row = t * kTile + lane;
+  float w[64];
+  load_row_block(w16, ld, row, j, row < n, w);
+  float mn = w[0], mx = w[0];
+#pragma unroll
+  for (int i = 1; i < 64; ++i) { mn = __builtin_fminf(mn, w[i]); mx = __builtin_fmaxf(mx, w[i]); }
+  uint16_t sb; float s; int z;
+  scale_zero(mn, mx, qmax, sb, s, z);
+  const int64_t mi = ((int64_t)t * kb + j) * kTile + lane;
+  scale[mi] = sb;
+  zero[mi] = (uint8_t)z;
+  if (codes != nullptr)
+    codes_and_store<BITS>(w, s, z, codes + mi * (2 * BITS));
+}
+
+// One group per row.  grid = tiles; the WAVES waves split the K-blocks, the
+// row extremes are combined through LDS, then each wave writes its blocks.
+template <int BITS, int WAVES>
+__global__ __launch_bounds__(WAVES * 64) void k_quantize_row(
+    const uint16_t* __restrict__ w16, int64_t ld, int n, int kb,
+    uint32_t* __restrict__ codes, uint16_t* __restrict__ scale, uint8_t* __restrict__ zero) {
+  constexpr int qmax = (1 << BITS) - 1;
+  __shared__ float smn[WAVES][64], smx[WAVES][64];
+  const int lane = lane_id(), wave = wave_id();
+  const int t = blockIdx.x;
+  const int row = t * kTile + lane;
+  const bool valid = row < n;
+  float mn = 0.f, mx = 0.f;
+  bool first = true;
+  for (int j = wave; j < kb; j += WAVES) {
+    float w[64];
+    load_row_block(w16, ld, row, j, valid, w);
+#pragma unroll
+    for (int i = 0; i < 64; ++i) {
+      mn = first ? w[i] : __builtin_fminf(mn, w[i]);
+      mx = first ? w[i] : __builtin_fmaxf(mx, w[i]);
+      first = false;
+    }
+  }
+  smn[wave][lane] = first ? __builtin_inff() : mn;
+  smx[wave][lane] = first ? -__builtin_inff() : mx;
+  __syncthreads();
+  mn = smn[0][lane]; mx = smx[0][lane];
+#pragma unroll
+  for (int i = 1; i < WAVES; ++i) { mn = __builtin_fminf(mn, smn[i][lane]); mx = __builtin_fmaxf(mx, smx[i][lane]); }
+  uint16_t sb; float s; int z;
+  scale_zero(mn, mx, qmax, sb, s, z);
+  if (wave == 0) {
+    scale[(int64_t)t * kTile + lane] = sb;
+    zero[(int64_t)t * kTile + lane] = (uint8_t)z;
+  }
+  if (codes == nullptr) return;
+  for (int j = wave; j < kb; j += WAVES) {
+    float w[64];
+    load_row_block(w16, ld, row, j, valid, w);
+    const int64_t bi = ((int64_t)t * kb + j) * kTile + lane;
+    codes_and_store<BITS>(w, s, z, codes + bi * (2 * BITS));
+  }
+}
+
+// ---------------------------------------------------- split-K finishing --
+// Every work-group of tile t writes its 64 partial rows to part[split][...];
+// the last one to arrive (ticket) adds the partials in split order, so the
+// result does not depend on arrival order, and re-arms the ticket.
+// `cols` = values per row of the tile handled by one lane (1 for GEMV).
+__device__ __forceinline__ bool split_ticket(uint32_t* __restrict__ tickets, int t, int splits) {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+  uint32_t prev = 0;
+  if (lane_id() == 0)
+    prev = __hip_atomic_fetch_add(&tickets[t], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  prev = __builtin_amdgcn_readfirstlane(prev);
+  if (prev != (uint32_t)(splits - 1)) return false;
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  if (lane_id() == 0)
+    __hip_atomic_store(&tickets[t], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return true;
+}
+
+// -------------------------------------------------------- packed GEMV --
+// grid = (tiles, splits), block = WAVES waves.  Wave w of split s walks
+// K-blocks j0+w, j0+w+WAVES, ... of [j0, j1); lane = row of the tile.
+// x is read with wave-uniform addresses (scalar loads, shared by all rows).
+template <int BITS, int WAVES>
+__global__ __launch_bounds__(WAVES * 64) void k_gemv_packed(
+    const uint32_t* __restrict__ codes, const uint16_t* __restrict__ scale,
+    const uint8_t* __restrict__ zero, const f16x2* __restrict__ x2, float* __restrict__ y,
+    float* __restrict__ part, uint32_t* __restrict__ tickets,
+    int n, int kb, int G, int splits, int kbps) {
+  constexpr int WPB = 2 * BITS;
+  __shared__ float red[WAVES][64];
+  const uint32_t magic = vreg_const(kMagic);
+  const int lane = lane_id(), wave = wave_id();
+  const int t = blockIdx.x, sp = blockIdx.y;
+  const int j0 = sp * kbps;
+  const int j1 = min(kb, j0 + kbps);
+  float yacc = 0.f;
+  for (int j = j0 + wave; j < j1; j += WAVES) {
+    const uint32_t* blk = codes + (((int64_t)t * kb + j) * kTile + lane) * WPB;
+    uint32_t wd[WPB];
+    if constexpr (BITS == 3) {
+      const uint2* b2 = reinterpret_cast<const uint2*>(blk);
+#pragma unroll
+      for (int i = 0; i < 3; ++i) { const uint2 v = b2[i]; wd[2 * i] = v.x; wd[2 * i + 1] = v.y; }
+    } else {
+      const uint4* b4 = reinterpret_cast<const uint4*>(blk);
+#pragma unroll
+      for (int i = 0; i < WPB / 4; ++i) {
+        const uint4 v = b4[i];
+        wd[4 * i] = v.x; wd[4 * i + 1] = v.y; wd[4 * i + 2] = v.z; wd[4 * i + 3] = v.w;
+      }
+    }
+    const int g = (G == 1) ? 0 : j;
+    const int64_t mi = ((int64_t)t * G + g) * kTile + lane;
+    const float s = h2f(scale[mi]);
+    const int z = zero[mi];
+    yacc = __builtin_fmaf(s, block_dot<BITS>(wd, x2 + (int64_t)j * 32, z, magic), yacc);
+  }
+  red[wave][lane] = yacc;
+  __syncthreads();
+  if (wave != 0) return;
+  float tot = red[0][lane];
+#pragma unroll
+  for (int w = 1; w < WAVES; ++w) tot += red[w][lane];
+  const int row = t * kTile + lane;
+  if (splits == 1) {
+    if (row < n) y[row] = tot;
+    return;
+  }
+  const int64_t np = (int64_t)gridDim.x * kTile;
+  part[(int64_t)sp * np + row] = tot;
+  if (!split_ticket(tickets, t, splits)) return;
+  float acc = 0.f;
+  for (int s2 = 0; s2 < splits; ++s2) acc += part[(int64_t)s2 * np + row];
+  if (row < n) y[row] = acc;
+}
+
+// ------------------------------------------------------ fused RTN GEMV --
+// Reads the fp16 masters, re-rounds every weight with the group's scale/zero
+// as it is read (codes never stored), accumulates x * (q - z) per group and
+// scales by s.  BITS == 16 is the unquantized control: x * w.
+template <int BITS, int WAVES>
+__global__ __launch_bounds__(WAVES * 64) void k_gemv_fused(
+    const uint16_t* __restrict__ w16, int64_t ld, const uint16_t* __restrict__ scale,
+    const uint8_t* __restrict__ zero, const f16x2* __restrict__ x2, float* __restrict__ y,
+    float* __restrict__ part, uint32_t* __restrict__ tickets,
+    int n, int kb, int G, int splits, int kbps) {
+  __shared__ float red[WAVES][64];
+  const int lane = lane_id(), wave = wave_id();
+  const int t = blockIdx.x, sp = blockIdx.y;
+  const int row = t * kTile + lane;
+  const int rrow = min(row, n - 1);
+  const uint4* wr = reinterpret_cast<const uint4*>(w16 + (int64_t)rrow * ld);
+  const int j0 = sp * kbps;
+  const int j1 = min(kb, j0 + kbps);
+  float yacc = 0.f;
+  for (int j = j0 + wave; j < j1; j += WAVES) {
+    uint4 wv[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) wv[i] = wr[(int64_t)j * 8 + i];
+    const f16x2* xb = x2 + (int64_t)j * 32;
+    if constexpr (BITS == 16) {
+      float a = 0.f, b = 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        a = __builtin_amdgcn_fdot2(as_h2(wv[i].x), xb[4 * i + 0], a, false);
+        b = __builtin_amdgcn_fdot2(as_h2(wv[i].y), xb[4 * i + 1], b, false);
+        a = __builtin_amdgcn_fdot2(as_h2(wv[i].z), xb[4 * i + 2], a, false);
+        b = __builtin_amdgcn_fdot2(as_h2(wv[i].w), xb[4 * i + 3], b, false);
+      }
+      yacc += a + b;
+    } else {
+      constexpr int qmax = (1 << BITS) - 1;
+      const int g = (G == 1) ? 0 : j;
+      const int64_t mi = ((int64_t)t * G + g) * kTile + lane;
+      const float s = h2f(scale[mi]);
+      const RtnParams p = rtn_params(s, zero[mi], qmax);
+      float a = 0.f, b = 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const uint32_t u[4] = {wv[i].x, wv[i].y, wv[i].z, wv[i].w};
+        float wf[8], q[8];
+        bool tie = false;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const f16x2 h = as_h2(u[e]);
+          wf[2 * e] = (float)h.x;
+          wf[2 * e + 1] = (float)h.y;
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          bool te;
+          q[e] = rtn_raw(wf[e], p, te);
+          tie |= te;
+        }
+        if (__builtin_amdgcn_ballot_w64(tie) != 0) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) q[e] = rtn_fix(wf[e], q[e], p);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const auto pk = __builtin_amdgcn_cvt_pkrtz(clampf(q[2 * e], p.lo, p.hi),
+                                                     clampf(q[2 * e + 1], p.lo, p.hi));
+          const f16x2 h = __builtin_bit_cast(f16x2, pk);
+          if (e & 1) b = __builtin_amdgcn_fdot2(h, xb[4 * i + e], b, false);
+          else a = __builtin_amdgcn_fdot2(h, xb[4 * i + e], a, false);
+        }
+      }
+      yacc = __builtin_fmaf(s, a + b, yacc);
+    }
+  }
+  red[wave][lane] = yacc;
+  __syncthreads();
+  if (wave != 0) return;
+  float tot = red[0][lane];
+#pragma unroll
+  for (int w = 1; w < WAVES; ++w) tot += red[w][lane];
+  if (splits == 1) {
+    if (row < n) y[row] = tot;
+    return;
+  }
+  const int64_t np = (int64_t)gridDim.x * kTile;
+  part[(int64_t)sp * np + row] = tot;
+  if (!split_ticket(tickets, t, splits)) return;
+  float acc = 0.f;
+  for (int s2 = 0; s2 < splits; ++s2) acc += part[(int64_t)s2 * np + row];
+  if (row < n) y[row] = acc;
+}
+
+// ------------------------------------------------------ skinny GEMM (M<=16)
+// v_mfma_f32_16x16x32_bf16: A = X (16 rows, zero past m), B = W^T.  Lane
+// (c = lane % 16, q = lane / 16) supplies row c and the 8 K-positions
+// 16q + 8s .. +7 of the block for instruction s in {0, 1}; both operands use
+// this same assignment of K positions, which therefore only permutes the sum.
+// The output D[4q + r][c] of column group cg is Y[4q + r][tile*64 + 16cg + c].
+template <int BITS>
+__device__ __forceinline__ void load_quarter(const uint32_t* __restrict__ blk, int q, uint32_t* wl) {
+  if constexpr (BITS == 4) {
+    const uint2 v = reinterpret_cast<const uint2*>(blk)[q];
+    wl[0] = v.x; wl[1] = v.y;
+  } else if constexpr (BITS == 2) {
+    wl[0] = blk[q];
+  } else if constexpr (BITS == 8) {
+    const uint4 v = reinterpret_cast<const uint4*>(blk)[q];
+    wl[0] = v.x; wl[1] = v.y; wl[2] = v.z; wl[3] = v.w;
+  } else {  // 3: low word 3*(q/2) + q%2, high word 3*(q/2) + 2
+    const int run = q >> 1, u = q & 1;
+    wl[0] = blk[3 * run + u];
+    const uint32_t H = blk[3 * run + 2];
+    wl[1] = u ? __builtin_amdgcn_alignbit(H, H, 8) : H;
+  }
+}
+
+// The 8 codes of the lane's quarter for instruction s (0 or 1).
+template <int BITS>
+__device__ __forceinline__ bf16x8 deq_quarter(const uint32_t* wl, int s, const Deq& d, uint32_t magic) {
+  if constexpr (BITS == 4) {
+    return deq_chunk4(wl[s], d, magic);
+  } else if constexpr (BITS == 2) {
+    return deq_chunk2(s ? (wl[0] >> 8) : wl[0], d, magic);
+  } else if constexpr (BITS == 8) {
+    return deq_chunk8(wl[2 * s], wl[2 * s + 1], d);
+  } else {
+    return deq_chunk3(s ? (wl[0] >> 8) : wl[0], s ? (wl[1] >> 1) : wl[1], d, magic);
+  }
+}
+
+template <int BITS, int WAVES>
+__global__ __launch_bounds__(WAVES * 64) void k_gemm_skinny(
+    const uint32_t* __restrict__ codes, const uint16_t* __restrict__ scale,
+    const uint8_t* __restrict__ zero, const uint16_t* __restrict__ X, int64_t ldx, int m,
+    float* __restrict__ Y, int64_t ldy, float* __restrict__ part, uint32_t* __restrict__ tickets,
+    int n, int kb, int G, int splits, int kbps) {
+  constexpr int WPB = 2 * BITS;
+  __shared__ f32x4 red[WAVES][4][64];
+  const int lane = lane_id(), wave = wave_id();
+  const int c = lane & 15, q = lane >> 4;
+  const int t = blockIdx.x, sp = blockIdx.y;
+  const int j0 = sp * kbps;
+  const int j1 = min(kb, j0 + kbps);
+  const uint32_t magic = vreg_const(kMagic);
+  f32x4 acc[4];
+#pragma unroll
+  for (int cg = 0; cg < 4; ++cg) acc[cg] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  const bool xrow = c < m;
+  const uint16_t* xr = X + (int64_t)(xrow ? c : 0) * ldx;
+  for (int j = j0 + wave; j < j1; j += WAVES) {
+    bf16x8 a[2];
+    {
+      uint4 v0 = make_uint4(0, 0, 0, 0), v1 = make_uint4(0, 0, 0, 0);
+      if (xrow) {
+        const uint4* xp = reinterpret_cast<const uint4*>(xr + (int64_t)j * kBlock + 16 * q);
+        v0 = xp[0]; v1 = xp[1];
+      }
+      a[0] = h8_to_bf16x8(v0);
+      a[1] = h8_to_bf16x8(v1);
+    }
+    const int g = (G == 1) ? 0 : j;
+#pragma unroll
+    for (int cg = 0; cg < 4; ++cg) {
+      const int r = 16 * cg + c;
+      const uint32_t* blk = codes + (((int64_t)t * kb + j) * kTile + r) * WPB;
+      uint32_t wl[4];
+      load_quarter<BITS>(blk, q, wl);
+      const int64_t mi = ((int64_t)t * G + g) * kTile + r;
+      const Deq d = make_deq(h2f(scale[mi]), zero[mi]);
+#pragma unroll
+      for (int s = 0; s < 2; ++s)
+        acc[cg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[s], deq_quarter<BITS>(wl, s, d, magic),
+                                                          acc[cg], 0, 0, 0);
+    }
+  }
+#pragma unroll
+  for (int cg = 0; cg < 4; ++cg) red[wave][cg][lane] = acc[cg];
+  __syncthreads();
+  if (wave != 0) return;
+  f32x4 tot[4];
+#pragma unroll
+  for (int cg = 0; cg < 4; ++cg) {
+    tot[cg] = red[0][cg][lane];
+#pragma unroll
+    for (int w = 1; w < WAVES; ++w) tot[cg] += red[w][cg][lane];
+  }
+  const int64_t np = (int64_t)gridDim.x * kTile;
+  if (splits > 1) {
+    // part[split][16][np]
+#pragma unroll
+    for (int cg = 0; cg < 4; ++cg)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        part[((int64_t)sp * 16 + 4 * q + r) * np + t * kTile + 16 * cg + c] = tot[cg][r];
+    if (!split_ticket(tickets, t, splits)) return;
+#pragma unroll
+    for (int cg = 0; cg < 4; ++cg)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float s2sum = 0.f;
+        for (int s2 = 0; s2 < splits; ++s2)
+          s2sum += part[((int64_t)s2 * 16 + 4 * q + r) * np + t * kTile + 16 * cg + c];
+        tot[cg][r] = s2sum;
+      }
+  }
+#pragma unroll
+  for (int cg = 0; cg < 4; ++cg)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int mrow = 4 * q + r, col = t * kTile + 16 * cg + c;
+      if (mrow < m && col < n) Y[(int64_t)mrow * ldy + col] = tot[cg][r];
+    }
+}
+
+// ----------------------------------------------------- tiled GEMM (M>16) --
+// v_mfma_f32_32x32x16_bf16.  Work-group = 4 waves; wave w owns W tile
+// blockIdx.x*4 + w (64 rows = two 32-column MFMA blocks), all MB rows of X.
+// X blocks are converted to bf16 once per work-group into LDS (double
+// buffered, rows padded to 144 bytes); the weight operand is decoded straight
+// from global memory into registers, so each code is read and decoded once
+// per work-group.  Lane (c = lane % 32, h = lane / 32) supplies row c and the
+// K positions 32h + 8s .. +7 of the block for instruction s in 0..3.
+// D[8*(r/4) + 4*h + r%4][c] is acc register r.
+constexpr int kLdsRow = 72;   // bf16 per padded LDS row
+
+template <int BITS>
+__device__ __forceinline__ void load_half(const uint32_t* __restrict__ blk, int h, uint32_t* wl) {
+  if constexpr (BITS == 4) {
+    const uint4 v = reinterpret_cast<const uint4*>(blk)[h];
+    wl[0] = v.x; wl[1] = v.y; wl[2] = v.z; wl[3] = v.w;
+  } else if constexpr (BITS == 2) {
+    const uint2 v = reinterpret_cast<const uint2*>(blk)[h];
+    wl[0] = v.x; wl[1] = v.y;
+  } else if constexpr (BITS == 8) {
+    const uint4* b4 = reinterpret_cast<const uint4*>(blk) + 2 * h;
+    const uint4 v = b4[0], u = b4[1];
+    wl[0] = v.x; wl[1] = v.y; wl[2] = v.z; wl[3] = v.w;
+    wl[4] = u.x; wl[5] = u.y; wl[6] = u.z; wl[7] = u.w;
+  } else {
+    wl[0] = blk[3 * h]; wl[1] = blk[3 * h + 1]; wl[2] = blk[3 * h + 2];
+  }
+}
+
+template <int BITS>
+__device__ __forceinline__ bf16x8 deq_half(const uint32_t* wl, int s, const Deq& d, uint32_t magic) {
+  if constexpr (BITS == 4) {
+    return deq_chunk4(wl[s], d, magic);
+  } else if constexpr (BITS == 2) {
+    const uint32_t v = wl[s >> 1];
+    return deq_chunk2((s & 1) ? (v >> 8) : v, d, magic);
+  } else if constexpr (BITS == 8) {
+    return deq_chunk8(wl[2 * s], wl[2 * s + 1], d);
+  } else {
+    const int u = s >> 1;
+    const uint32_t L = wl[u];
+    const uint32_t Hu = u ? __builtin_amdgcn_alignbit(wl[2], wl[2], 8) : wl[2];
+    return deq_chunk3((s & 1) ? (L >> 8) : L, (s & 1) ? (Hu >> 1) : Hu, d, magic);
+  }
+}
+
+template <int BITS, int MB>
+__global__ __launch_bounds__(256) void k_gemm_tiles(
+    const uint32_t* __restrict__ codes, const uint16_t* __restrict__ scale,
+    const uint8_t* __restrict__ zero, const uint16_t* __restrict__ X, int64_t ldx, int m,
+    float* __restrict__ Y, int64_t ldy, int n, int kb, int G, int tiles) {
+  constexpr int WPB = 2 * BITS;
+  constexpr int RB = MB / 32;               // 32-row MFMA blocks of X
+  constexpr int XCH = MB * 8 / 256;         // 16-byte X chunks per thread per block
+  __shared__ __attribute__((aligned(16))) __bf16 xs[2][MB][kLdsRow];
+  const int tid = threadIdx.x;
+  const int lane = lane_id(), wave = wave_id();
+  const int c = lane & 31, h = lane >> 5;
+  const int t = blockIdx.x * 4 + wave;
+  const bool tvalid = t < tiles;
+  const int m0 = blockIdx.y * MB;
+  const uint32_t magic = vreg_const(kMagic);
+
+  f32x16 acc[RB][2];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[rb][cb][r] = 0.f;
+
+  auto load_x = [&](int j, uint4* xv) {
+#pragma unroll
+    for (int i = 0; i < XCH; ++i) {
+      const int ch = tid + 256 * i;
+      const int row = ch >> 3, c8 = ch & 7;
+      xv[i] = make_uint4(0, 0, 0, 0);
+      if (m0 + row < m)
+        xv[i] = *reinterpret_cast<const uint4*>(X + (int64_t)(m0 + row) * ldx + (int64_t)j * kBlock + 8 * c8);
+    }
+  };
+  auto store_x = [&](int buf, const uint4* xv) {
+#pragma unroll
+    for (int i = 0; i < XCH; ++i) {
+      const int ch = tid + 256 * i;
+      const int row = ch >> 3, c8 = ch & 7;
+      *reinterpret_cast<bf16x8*>(&xs[buf][row][8 * c8]) = h8_to_bf16x8(xv[i]);
+    }
+  };
+  auto load_w = [&](int j, uint32_t (*wl)[WPB / 2], float* s, int* z) {
+    const int g = (G == 1) ? 0 : j;
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) {
+      const int r = 32 * cb + c;
+      if (tvalid) {
+        const uint32_t* blk = codes + (((int64_t)t * kb + j) * kTile + r) * WPB;
+        load_half<BITS>(blk, h, wl[cb]);
+        const int64_t mi = ((int64_t)t * G + g) * kTile + r;
+        s[cb] = h2f(scale[mi]);
+        z[cb] = zero[mi];
+      } else {
+#pragma unroll
+        for (int i = 0; i < WPB / 2; ++i) wl[cb][i] = 0;
+        s[cb] = 0.f; z[cb] = 0;
+      }
+    }
+  };
+
+  uint4 xv[XCH];
+  uint32_t wl[2][WPB / 2];
+  float sc[2]; int zc[2];
+  bf16x8 bfrag[2][4];
+
+  load_x(0, xv);
+  load_w(0, wl, sc, zc);
+  store_x(0, xv);
+#pragma unroll
+  for (int cb = 0; cb < 2; ++cb) {
+    const Deq d = make_deq(sc[cb], zc[cb]);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) bfrag[cb][s] = deq_half<BITS>(wl[cb], s, d, magic);
+  }
+  __syncthreads();
+
+  for (int j = 0; j < kb; ++j) {
+    const int cur = j & 1;
+    const bool more = j + 1 < kb;
+    if (more) {
+      load_x(j + 1, xv);
+      load_w(j + 1, wl, sc, zc);
+    }
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(&xs[cur][32 * rb + c][32 * h + 8 * s]);
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb)
+          acc[rb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bfrag[cb][s], acc[rb][cb], 0, 0, 0);
+      }
+    }
+    if (more) {
+      store_x(cur ^ 1, xv);
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb) {
+        const Deq d = make_deq(sc[cb], zc[cb]);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) bfrag[cb][s] = deq_half<BITS>(wl[cb], s, d, magic);
+      }
+    }
+    __syncthreads();
+  }
+
+  if (!tvalid) return;
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) {
+      const int col = t * kTile + 32 * cb + c;
+      if (col >= n) continue;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int mrow = m0 + 32 * rb + 8 * (r >> 2) + 4 * h + (r & 3);
+        if (mrow < m) Y[(int64_t)mrow * ldy + col] = acc[rb][cb][r];
+      }
+    }
+}
+
+}  // namespace qlin

@@ -1,0 +1,385 @@
+// qlin C ABI: argument validation (host only, no HIP call), launch-shape
+// selection and kernel launches on the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include <stdint.h>
+#include <string.h>
+
+#include "../../include/qlin.h"
+#include "kernels.h"
+
+using namespace qlin;
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+constexpr int kWaves = 4;                    // waves per work-group (GEMV, skinny GEMM)
+constexpr int kMaxN = 1 << 24;
+constexpr int kMaxK = 1 << 20;
+constexpr int kMaxM = 1 << 20;
+constexpr int kTargetGroups = 1024;          // work-groups a split-K launch aims for
+constexpr int kMinBlocksPerWave = 2;         // K-blocks per wave before splitting further
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+inline int64_t tiles_of(int64_t n) { return (n + kTile - 1) / kTile; }
+
+struct Range { uintptr_t lo, hi; };
+inline Range range_of(const void* p, int64_t bytes) {
+  const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+  return Range{a, a + (uintptr_t)(bytes > 0 ? bytes : 0)};
+}
+inline bool overlaps(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
+
+bool valid_bits(int bits) { return bits == 2 || bits == 3 || bits == 4 || bits == 8; }
+
+qlin_status check_nk(int32_t n, int32_t k) {
+  if (n < 1 || n > kMaxN || k < kBlock || k > kMaxK || (k % kBlock) != 0) return QLIN_ERR_SHAPE;
+  return QLIN_OK;
+}
+
+qlin_status check_group(int32_t group, int32_t k) {
+  return (group == kBlock || group == k) ? QLIN_OK : QLIN_ERR_GROUP;
+}
+
+int64_t packed_bytes(int64_t n, int64_t k, int bits) {
+  return tiles_of(n) * kTile * (k / kBlock) * 2 * bits * 4;
+}
+int64_t meta_entries(int64_t n, int64_t k, int group) {
+  return tiles_of(n) * kTile * (group == k ? 1 : k / kBlock);
+}
+
+qlin_status hip_status(hipError_t e) {
+  if (e == hipSuccess) return QLIN_OK;
+  g_last_hip_error = (int)e;
+  return QLIN_ERR_HIP;
+}
+
+// One check per process and device: the kernels are built for gfx950 only.
+qlin_status check_device() {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) { g_last_hip_error = (int)e; return QLIN_ERR_NO_DEVICE; }
+  static thread_local int cached_dev = -1;
+  static thread_local bool cached_ok = false;
+  if (dev == cached_dev) return cached_ok ? QLIN_OK : QLIN_ERR_NO_DEVICE;
+  hipDeviceProp_t prop;
+  e = hipGetDeviceProperties(&prop, dev);
+  if (e != hipSuccess) { g_last_hip_error = (int)e; return QLIN_ERR_NO_DEVICE; }
+  cached_dev = dev;
+  cached_ok = strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+  return cached_ok ? QLIN_OK : QLIN_ERR_NO_DEVICE;
+}
+
+qlin_status check_weight(const qlin_weight* w, bool allow_master, bool allow16) {
+  if (w == nullptr) return QLIN_ERR_NULL;
+  qlin_status st = check_nk(w->n, w->k);
+  if (st != QLIN_OK) return st;
+  if (w->reserved != 0) return QLIN_ERR_FORMAT;
+  if (w->format == QLIN_FMT_PACKED) {
+    if (!valid_bits(w->bits)) return QLIN_ERR_BITS;
+    if (w->ld != 0) return QLIN_ERR_SHAPE;
+  } else if (w->format == QLIN_FMT_FP16_MASTER) {
+    if (!allow_master) return QLIN_ERR_FORMAT;
+    if (!(valid_bits(w->bits) || (allow16 && w->bits == 16))) return QLIN_ERR_BITS;
+    if (w->ld < w->k) return QLIN_ERR_SHAPE;
+    if (w->ld % 8 != 0) return QLIN_ERR_ALIGN;
+  } else {
+    return QLIN_ERR_FORMAT;
+  }
+  if (w->data == nullptr) return QLIN_ERR_NULL;
+  if (!aligned16(w->data)) return QLIN_ERR_ALIGN;
+  if (w->bits != 16) {
+    st = check_group(w->group, w->k);
+    if (st != QLIN_OK) return st;
+    if (w->scale == nullptr || w->zero == nullptr) return QLIN_ERR_NULL;
+    if (!aligned16(w->scale) || !aligned16(w->zero)) return QLIN_ERR_ALIGN;
+  }
+  return QLIN_OK;
+}
+
+int64_t weight_bytes(const qlin_weight* w) {
+  if (w->format == QLIN_FMT_PACKED) return packed_bytes(w->n, w->k, w->bits);
+  return ((int64_t)(w->n - 1) * w->ld + w->k) * 2;
+}
+
+bool output_overlaps_weight(const qlin_weight* w, Range out) {
+  if (overlaps(out, range_of(w->data, weight_bytes(w)))) return true;
+  if (w->bits != 16) {
+    const int64_t me = meta_entries(w->n, w->k, w->group);
+    if (overlaps(out, range_of(w->scale, me * 2))) return true;
+    if (overlaps(out, range_of(w->zero, me))) return true;
+  }
+  return false;
+}
+
+// Split of the K-blocks over work-groups for the tile-per-work-group kernels.
+struct Split { int splits, kbps; };
+
+Split choose_split(int64_t tiles, int kb, int64_t ws_bytes, int64_t part_rows) {
+  int want = (int)((kTargetGroups + tiles - 1) / tiles);
+  const int max_by_k = kb / (kWaves * kMinBlocksPerWave);
+  if (want > max_by_k) want = max_by_k;
+  if (want < 1) want = 1;
+  // workspace: partials [splits][part_rows][tiles*64] floats + one ticket per tile
+  while (want > 1) {
+    const int64_t need = (int64_t)want * part_rows * tiles * kTile * 4 + tiles * 4;
+    if (need <= ws_bytes) break;
+    --want;
+  }
+  const int kbps = (kb + want - 1) / want;
+  const int splits = (kb + kbps - 1) / kbps;
+  return Split{splits, kbps};
+}
+
+int64_t split_ws_bytes(int64_t tiles, int kb, int64_t part_rows) {
+  const Split s = choose_split(tiles, kb, INT64_MAX, part_rows);
+  if (s.splits <= 1) return 0;
+  return (int64_t)s.splits * part_rows * tiles * kTile * 4 + tiles * 4;
+}
+
+template <int B>
+void launch_quant(const uint16_t* w16, int64_t ld, int n, int k, int group, uint32_t* codes,
+                  uint16_t* scale, uint8_t* zero, hipStream_t st) {
+  const int kb = k / kBlock;
+  const int tiles = (int)tiles_of(n);
+  if (group == kBlock) {
+    dim3 grid(tiles, (kb + kWaves - 1) / kWaves);
+    hipLaunchKernelGGL((k_quantize_g64<B, kWaves>), grid, dim3(kWaves * 64), 0, st,
+                       w16, ld, n, kb, codes, scale, zero);
+  } else {
+    hipLaunchKernelGGL((k_quantize_row<B, kWaves>), dim3(tiles), dim3(kWaves * 64), 0, st,
+                       w16, ld, n, kb, codes, scale, zero);
+  }
+}
+
+template <int B>
+void launch_gemv_packed(const qlin_weight* w, const f16x2* x2, float* y, float* part,
+                        uint32_t* tick, Split sp, hipStream_t st) {
+  const int kb = w->k / kBlock;
+  const int G = (w->group == w->k) ? 1 : kb;
+  dim3 grid((unsigned)tiles_of(w->n), sp.splits);
+  hipLaunchKernelGGL((k_gemv_packed<B, kWaves>), grid, dim3(kWaves * 64), 0, st,
+                     static_cast<const uint32_t*>(w->data), w->scale, w->zero, x2, y, part, tick,
+                     w->n, kb, G, sp.splits, sp.kbps);
+}
+
+template <int B>
+void launch_gemv_fused(const qlin_weight* w, const f16x2* x2, float* y, float* part,
+                       uint32_t* tick, Split sp, hipStream_t st) {
+  const int kb = w->k / kBlock;
+  const int G = (w->bits == 16 || w->group != w->k) ? kb : 1;
+  dim3 grid((unsigned)tiles_of(w->n), sp.splits);
+  hipLaunchKernelGGL((k_gemv_fused<B, kWaves>), grid, dim3(kWaves * 64), 0, st,
+                     static_cast<const uint16_t*>(w->data), w->ld, w->scale, w->zero, x2, y, part,
+                     tick, w->n, kb, G, sp.splits, sp.kbps);
+}
+
+template <int B>
+void launch_gemm_skinny(const qlin_weight* w, const uint16_t* X, int64_t ldx, int m, float* Y,
+                        int64_t ldy, float* part, uint32_t* tick, Split sp, hipStream_t st) {
+  const int kb = w->k / kBlock;
+  const int G = (w->group == w->k) ? 1 : kb;
+  dim3 grid((unsigned)tiles_of(w->n), sp.splits);
+  hipLaunchKernelGGL((k_gemm_skinny<B, kWaves>), grid, dim3(kWaves * 64), 0, st,
+                     static_cast<const uint32_t*>(w->data), w->scale, w->zero, X, ldx, m, Y, ldy,
+                     part, tick, w->n, kb, G, sp.splits, sp.kbps);
+}
+
+template <int B>
+void launch_gemm_tiles(const qlin_weight* w, const uint16_t* X, int64_t ldx, int m, float* Y,
+                       int64_t ldy, hipStream_t st) {
+  const int kb = w->k / kBlock;
+  const int G = (w->group == w->k) ? 1 : kb;
+  const int tiles = (int)tiles_of(w->n);
+  const unsigned gx = (unsigned)((tiles + 3) / 4);
+  if (m <= 64) {
+    dim3 grid(gx, (m + 63) / 64);
+    hipLaunchKernelGGL((k_gemm_tiles<B, 64>), grid, dim3(256), 0, st,
+                       static_cast<const uint32_t*>(w->data), w->scale, w->zero, X, ldx, m, Y,
+                       ldy, w->n, kb, G, tiles);
+  } else {
+    dim3 grid(gx, (m + 127) / 128);
+    hipLaunchKernelGGL((k_gemm_tiles<B, 128>), grid, dim3(256), 0, st,
+                       static_cast<const uint32_t*>(w->data), w->scale, w->zero, X, ldx, m, Y,
+                       ldy, w->n, kb, G, tiles);
+  }
+}
+
+constexpr int kSkinnyMaxM = 16;
+
+}  // namespace
+
+extern "C" {
+
+const char* qlin_status_string(int status) {
+  switch (status) {
+    case QLIN_OK: return "QLIN_OK";
+    case QLIN_ERR_NULL: return "QLIN_ERR_NULL: a required pointer is NULL";
+    case QLIN_ERR_SHAPE: return "QLIN_ERR_SHAPE: size or pitch out of range";
+    case QLIN_ERR_BITS: return "QLIN_ERR_BITS: unsupported bit width";
+    case QLIN_ERR_GROUP: return "QLIN_ERR_GROUP: group must be 64 or k";
+    case QLIN_ERR_ALIGN: return "QLIN_ERR_ALIGN: pointer or pitch misaligned";
+    case QLIN_ERR_FORMAT: return "QLIN_ERR_FORMAT: weight format not allowed here";
+    case QLIN_ERR_ALIAS: return "QLIN_ERR_ALIAS: output overlaps an input";
+    case QLIN_ERR_WORKSPACE: return "QLIN_ERR_WORKSPACE: workspace too small";
+    case QLIN_ERR_NO_DEVICE: return "QLIN_ERR_NO_DEVICE: no gfx950 device is current";
+    case QLIN_ERR_HIP: return "QLIN_ERR_HIP: a HIP call failed";
+    default: return "QLIN: unknown status";
+  }
+}
+
+int qlin_last_hip_error(void) { return g_last_hip_error; }
+
+int qlin_abi_version(void) { return 1; }
+
+int64_t qlin_packed_bytes(int32_t n, int32_t k, int32_t bits) {
+  if (check_nk(n, k) != QLIN_OK || !valid_bits(bits)) return 0;
+  return packed_bytes(n, k, bits);
+}
+
+int64_t qlin_meta_entries(int32_t n, int32_t k, int32_t group) {
+  if (check_nk(n, k) != QLIN_OK || check_group(group, k) != QLIN_OK) return 0;
+  return meta_entries(n, k, group);
+}
+
+qlin_status qlin_quantize(const uint16_t* w16, int64_t ld_w, int32_t n, int32_t k, int32_t bits,
+                          int32_t group, uint32_t* codes, uint16_t* scale, uint8_t* zero,
+                          hipStream_t stream) {
+  qlin_status st = check_nk(n, k);
+  if (st != QLIN_OK) return st;
+  if (!valid_bits(bits)) return QLIN_ERR_BITS;
+  st = check_group(group, k);
+  if (st != QLIN_OK) return st;
+  if (w16 == nullptr || scale == nullptr || zero == nullptr) return QLIN_ERR_NULL;
+  if (ld_w < k) return QLIN_ERR_SHAPE;
+  if (ld_w % 8 != 0) return QLIN_ERR_ALIGN;
+  if (!aligned16(w16) || !aligned16(scale) || !aligned16(zero) ||
+      (codes != nullptr && !aligned16(codes)))
+    return QLIN_ERR_ALIGN;
+  const Range in = range_of(w16, ((int64_t)(n - 1) * ld_w + k) * 2);
+  const int64_t me = meta_entries(n, k, group);
+  const Range rs = range_of(scale, me * 2), rz = range_of(zero, me);
+  if (overlaps(in, rs) || overlaps(in, rz) || overlaps(rs, rz)) return QLIN_ERR_ALIAS;
+  if (codes != nullptr) {
+    const Range rc = range_of(codes, packed_bytes(n, k, bits));
+    if (overlaps(rc, in) || overlaps(rc, rs) || overlaps(rc, rz)) return QLIN_ERR_ALIAS;
+  }
+  st = check_device();
+  if (st != QLIN_OK) return st;
+  switch (bits) {
+    case 2: launch_quant<2>(w16, ld_w, n, k, group, codes, scale, zero, stream); break;
+    case 3: launch_quant<3>(w16, ld_w, n, k, group, codes, scale, zero, stream); break;
+    case 4: launch_quant<4>(w16, ld_w, n, k, group, codes, scale, zero, stream); break;
+    default: launch_quant<8>(w16, ld_w, n, k, group, codes, scale, zero, stream); break;
+  }
+  return hip_status(hipGetLastError());
+}
+
+int64_t qlin_gemv_workspace_bytes(const qlin_weight* w) {
+  if (check_weight(w, true, true) != QLIN_OK) return 0;
+  return split_ws_bytes(tiles_of(w->n), w->k / kBlock, 1);
+}
+
+int64_t qlin_gemm_workspace_bytes(const qlin_weight* w, int32_t m) {
+  if (check_weight(w, false, false) != QLIN_OK || m < 1 || m > kMaxM) return 0;
+  if (m > kSkinnyMaxM) return 0;
+  return split_ws_bytes(tiles_of(w->n), w->k / kBlock, 16);
+}
+
+qlin_status qlin_gemv(const qlin_weight* w, const uint16_t* x, float* y, void* workspace,
+                      int64_t workspace_bytes, hipStream_t stream) {
+  qlin_status st = check_weight(w, true, true);
+  if (st != QLIN_OK) return st;
+  if (x == nullptr || y == nullptr) return QLIN_ERR_NULL;
+  if (!aligned16(x) || !aligned16(y)) return QLIN_ERR_ALIGN;
+  if (workspace_bytes < 0) return QLIN_ERR_WORKSPACE;
+  if (workspace == nullptr) workspace_bytes = 0;
+  if (workspace != nullptr && !aligned16(workspace)) return QLIN_ERR_ALIGN;
+  const Range ry = range_of(y, (int64_t)w->n * 4);
+  if (overlaps(ry, range_of(x, (int64_t)w->k * 2)) || output_overlaps_weight(w, ry))
+    return QLIN_ERR_ALIAS;
+  if (workspace_bytes > 0) {
+    const Range rw = range_of(workspace, workspace_bytes);
+    if (overlaps(rw, ry) || overlaps(rw, range_of(x, (int64_t)w->k * 2)) ||
+        output_overlaps_weight(w, rw))
+      return QLIN_ERR_ALIAS;
+  }
+  st = check_device();
+  if (st != QLIN_OK) return st;
+  const int64_t tiles = tiles_of(w->n);
+  const int kb = w->k / kBlock;
+  const Split sp = choose_split(tiles, kb, workspace_bytes, 1);
+  float* part = static_cast<float*>(workspace);
+  uint32_t* tick = nullptr;
+  if (sp.splits > 1)
+    tick = reinterpret_cast<uint32_t*>(part + (int64_t)sp.splits * tiles * kTile);
+  const f16x2* x2 = reinterpret_cast<const f16x2*>(x);
+  if (w->format == QLIN_FMT_PACKED) {
+    switch (w->bits) {
+      case 2: launch_gemv_packed<2>(w, x2, y, part, tick, sp, stream); break;
+      case 3: launch_gemv_packed<3>(w, x2, y, part, tick, sp, stream); break;
+      case 4: launch_gemv_packed<4>(w, x2, y, part, tick, sp, stream); break;
+      default: launch_gemv_packed<8>(w, x2, y, part, tick, sp, stream); break;
+    }
+  } else {
+    switch (w->bits) {
+      case 2: launch_gemv_fused<2>(w, x2, y, part, tick, sp, stream); break;
+      case 3: launch_gemv_fused<3>(w, x2, y, part, tick, sp, stream); break;
+      case 4: launch_gemv_fused<4>(w, x2, y, part, tick, sp, stream); break;
+      case 8: launch_gemv_fused<8>(w, x2, y, part, tick, sp, stream); break;
+      default: launch_gemv_fused<16>(w, x2, y, part, tick, sp, stream); break;
+    }
+  }
+  return hip_status(hipGetLastError());
+}
+
+qlin_status qlin_gemm(const qlin_weight* w, const uint16_t* X, int32_t m, int64_t ld_x, float* Y,
+                      int64_t ld_y, void* workspace, int64_t workspace_bytes,
+                      hipStream_t stream) {
+  qlin_status st = check_weight(w, false, false);
+  if (st != QLIN_OK) return st;
+  if (X == nullptr || Y == nullptr) return QLIN_ERR_NULL;
+  if (m < 1 || m > kMaxM || ld_x < w->k || ld_y < w->n) return QLIN_ERR_SHAPE;
+  if (ld_x % 8 != 0) return QLIN_ERR_ALIGN;
+  if (!aligned16(X) || !aligned16(Y)) return QLIN_ERR_ALIGN;
+  if (workspace_bytes < 0) return QLIN_ERR_WORKSPACE;
+  if (workspace == nullptr) workspace_bytes = 0;
+  if (workspace != nullptr && !aligned16(workspace)) return QLIN_ERR_ALIGN;
+  const Range rY = range_of(Y, ((int64_t)(m - 1) * ld_y + w->n) * 4);
+  const Range rX = range_of(X, ((int64_t)(m - 1) * ld_x + w->k) * 2);
+  if (overlaps(rY, rX) || output_overlaps_weight(w, rY)) return QLIN_ERR_ALIAS;
+  if (workspace_bytes > 0) {
+    const Range rw = range_of(workspace, workspace_bytes);
+    if (overlaps(rw, rY) || overlaps(rw, rX) || output_overlaps_weight(w, rw))
+      return QLIN_ERR_ALIAS;
+  }
+  st = check_device();
+  if (st != QLIN_OK) return st;
+  const uint32_t* codes = static_cast<const uint32_t*>(w->data);
+  (void)codes;
+  if (m <= kSkinnyMaxM) {
+    const int64_t tiles = tiles_of(w->n);
+    const Split sp = choose_split(tiles, w->k / kBlock, workspace_bytes, 16);
+    float* part = static_cast<float*>(workspace);
+    uint32_t* tick = nullptr;
+    if (sp.splits > 1)
+      tick = reinterpret_cast<uint32_t*>(part + (int64_t)sp.splits * 16 * tiles * kTile);
+    switch (w->bits) {
+      case 2: launch_gemm_skinny<2>(w, X, ld_x, m, Y, ld_y, part, tick, sp, stream); break;
+      case 3: launch_gemm_skinny<3>(w, X, ld_x, m, Y, ld_y, part, tick, sp, stream); break;
+      case 4: launch_gemm_skinny<4>(w, X, ld_x, m, Y, ld_y, part, tick, sp, stream); break;
+      default: launch_gemm_skinny<8>(w, X, ld_x, m, Y, ld_y, part, tick, sp, stream); break;
+    }
+  } else {
+    switch (w->bits) {
+      case 2: launch_gemm_tiles<2>(w, X, ld_x, m, Y, ld_y, stream); break;
+      case 3: launch_gemm_tiles<3>(w, X, ld_x, m, Y, ld_y, stream); break;
+      case 4: launch_gemm_tiles<4>(w, X, ld_x, m, Y, ld_y, stream); break;
+      default: launch_gemm_tiles<8>(w, X, ld_x, m, Y, ld_y, stream); break;
+    }
+  }
+  return hip_status(hipGetLastError());
+}
+
+}  // extern "C"

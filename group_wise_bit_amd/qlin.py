@@ -1,0 +1,225 @@
+"""Python binding of libqlin (include/qlin.h): argument marshalling only.
+
+Every step of the computation runs in the HIP kernels behind the C ABI.
+PyTorch supplies device memory and the current stream.  There is no fallback:
+if libqlin.so is missing or the GPU is not gfx950, calls raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libqlin.so")
+
+FMT_PACKED = 0
+FMT_FP16_MASTER = 1
+
+STATUS_NAMES = {
+    0: "QLIN_OK", 1: "QLIN_ERR_NULL", 2: "QLIN_ERR_SHAPE", 3: "QLIN_ERR_BITS",
+    4: "QLIN_ERR_GROUP", 5: "QLIN_ERR_ALIGN", 6: "QLIN_ERR_FORMAT", 7: "QLIN_ERR_ALIAS",
+    8: "QLIN_ERR_WORKSPACE", 9: "QLIN_ERR_NO_DEVICE", 10: "QLIN_ERR_HIP",
+}
+
+# Every symbol include/qlin.h declares.
+EXPORTS = (
+    "qlin_status_string", "qlin_last_hip_error", "qlin_abi_version", "qlin_packed_bytes",
+    "qlin_meta_entries", "qlin_quantize", "qlin_gemv_workspace_bytes",
+    "qlin_gemm_workspace_bytes", "qlin_gemv", "qlin_gemm",
+)
+
+
+class QlinError(RuntimeError):
+    def __init__(self, status: int, where: str, hip_error: int = 0):
+        self.status = status
+        self.hip_error = hip_error
+        msg = f"{where}: {_lib().qlin_status_string(status).decode()}"
+        if hip_error:
+            msg += f" (hip error {hip_error})"
+        super().__init__(msg)
+
+
+class QlinWeightC(ctypes.Structure):
+    _fields_ = [
+        ("n", ctypes.c_int32), ("k", ctypes.c_int32), ("bits", ctypes.c_int32),
+        ("group", ctypes.c_int32), ("format", ctypes.c_int32), ("reserved", ctypes.c_int32),
+        ("data", ctypes.c_void_p), ("ld", ctypes.c_int64),
+        ("scale", ctypes.c_void_p), ("zero", ctypes.c_void_p),
+    ]
+
+
+_LIB: Optional[ctypes.CDLL] = None
+
+
+def _lib() -> ctypes.CDLL:
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"libqlin.so not built at {LIB_PATH}; run "
+                              "`python -m group_wise_bit_amd.build` (no CPU fallback exists)")
+        lib = ctypes.CDLL(LIB_PATH)
+        i32, i64, vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p
+        wp = ctypes.POINTER(QlinWeightC)
+        lib.qlin_status_string.argtypes = [ctypes.c_int]
+        lib.qlin_status_string.restype = ctypes.c_char_p
+        lib.qlin_last_hip_error.argtypes = []
+        lib.qlin_last_hip_error.restype = ctypes.c_int
+        lib.qlin_abi_version.argtypes = []
+        lib.qlin_abi_version.restype = ctypes.c_int
+        lib.qlin_packed_bytes.argtypes = [i32, i32, i32]
+        lib.qlin_packed_bytes.restype = i64
+        lib.qlin_meta_entries.argtypes = [i32, i32, i32]
+        lib.qlin_meta_entries.restype = i64
+        lib.qlin_quantize.argtypes = [vp, i64, i32, i32, i32, i32, vp, vp, vp, vp]
+        lib.qlin_quantize.restype = ctypes.c_int
+        lib.qlin_gemv_workspace_bytes.argtypes = [wp]
+        lib.qlin_gemv_workspace_bytes.restype = i64
+        lib.qlin_gemm_workspace_bytes.argtypes = [wp, i32]
+        lib.qlin_gemm_workspace_bytes.restype = i64
+        lib.qlin_gemv.argtypes = [wp, vp, vp, vp, i64, vp]
+        lib.qlin_gemv.restype = ctypes.c_int
+        lib.qlin_gemm.argtypes = [wp, vp, i32, i64, vp, i64, vp, i64, vp]
+        lib.qlin_gemm.restype = ctypes.c_int
+        _LIB = lib
+    return _LIB
+
+
+def library() -> ctypes.CDLL:
+    """The loaded libqlin (raises ImportError when it is not built)."""
+    return _lib()
+
+
+def _check(status: int, where: str) -> None:
+    if status != 0:
+        raise QlinError(status, where, _lib().qlin_last_hip_error() if status == 10 else 0)
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def packed_bytes(n: int, k: int, bits: int) -> int:
+    return int(_lib().qlin_packed_bytes(n, k, bits))
+
+
+def meta_entries(n: int, k: int, group: int) -> int:
+    return int(_lib().qlin_meta_entries(n, k, group))
+
+
+@dataclass
+class QWeight:
+    """A weight matrix for qlin_gemv / qlin_gemm (tensors stay owned here)."""
+    n: int
+    k: int
+    bits: int
+    group: int
+    format: int
+    data: torch.Tensor
+    scale: Optional[torch.Tensor] = None
+    zero: Optional[torch.Tensor] = None
+    ld: int = 0
+
+    def c_struct(self) -> QlinWeightC:
+        return QlinWeightC(self.n, self.k, self.bits, self.group, self.format, 0,
+                           _ptr(self.data), self.ld, _ptr(self.scale), _ptr(self.zero))
+
+    @property
+    def weight_bytes(self) -> int:
+        """Bytes a matmul must read for this weight (codes or fp16 + metadata)."""
+        b = self.data.numel() * self.data.element_size() if self.format == FMT_PACKED \
+            else self.n * self.k * 2
+        if self.bits != 16:
+            b += self.scale.numel() * 2 + self.zero.numel()
+        return b
+
+
+def quantize(w16: torch.Tensor, bits: int, group: int, codes: bool = True,
+             out: Optional[QWeight] = None) -> QWeight:
+    """qlin_quantize on a cuda fp16 [n, k] tensor -> packed QWeight (codes=False:
+    scale/zero only, returned with the masters as an FP16_MASTER weight)."""
+    if w16.dtype != torch.float16 or w16.dim() != 2 or not w16.is_cuda:
+        raise TypeError("w16 must be a 2-D cuda float16 tensor")
+    if w16.stride(1) != 1:
+        raise ValueError("w16 rows must be contiguous")
+    n, k = w16.shape
+    g = k if group in ("k", "K") else int(group)
+    me = meta_entries(n, k, g)
+    pb = packed_bytes(n, k, bits) if bits in (2, 3, 4, 8) else 0
+    if out is None:
+        scale = torch.empty(max(me, 1), dtype=torch.float16, device=w16.device)
+        zero = torch.empty(max(me, 1), dtype=torch.uint8, device=w16.device)
+        cbuf = torch.empty(max(pb // 4, 1), dtype=torch.int32, device=w16.device) if codes else None
+    else:
+        scale, zero, cbuf = out.scale, out.zero, (out.data if codes else None)
+    st = _lib().qlin_quantize(w16.data_ptr(), w16.stride(0), n, k, bits, g, _ptr(cbuf),
+                              scale.data_ptr(), zero.data_ptr(), _stream())
+    _check(st, "qlin_quantize")
+    if codes:
+        return QWeight(n, k, bits, g, FMT_PACKED, cbuf, scale, zero)
+    return QWeight(n, k, bits, g, FMT_FP16_MASTER, w16, scale, zero, ld=w16.stride(0))
+
+
+def master_weight(w16: torch.Tensor, bits: int, group: int, scale=None, zero=None) -> QWeight:
+    """FP16_MASTER weight over existing masters (bits=16: the plain fp16 control)."""
+    n, k = w16.shape
+    g = k if group in ("k", "K") else int(group)
+    return QWeight(n, k, bits, g, FMT_FP16_MASTER, w16, scale, zero, ld=w16.stride(0))
+
+
+_WS: dict = {}
+
+
+def workspace(nbytes: int, device: torch.device) -> Optional[torch.Tensor]:
+    """Zero-filled workspace, cached per (device, stream); the kernels leave it
+    zero-filled again after every call."""
+    if nbytes <= 0:
+        return None
+    key = (device.index, _stream())
+    buf = _WS.get(key)
+    if buf is None or buf.numel() < nbytes:
+        buf = torch.zeros(nbytes, dtype=torch.uint8, device=device)
+        _WS[key] = buf
+    return buf
+
+
+def gemv(w: QWeight, x: torch.Tensor, y: Optional[torch.Tensor] = None,
+         ws: Optional[torch.Tensor] = "auto") -> torch.Tensor:
+    if x.dtype != torch.float16 or x.numel() != w.k or not x.is_contiguous():
+        raise TypeError("x must be a contiguous float16 tensor of k elements")
+    if y is None:
+        y = torch.empty(w.n, dtype=torch.float32, device=x.device)
+    ws_struct = w.c_struct()
+    if isinstance(ws, str):
+        need = int(_lib().qlin_gemv_workspace_bytes(ctypes.byref(ws_struct)))
+        ws = workspace(need, x.device)
+    wsb = 0 if ws is None else ws.numel() * ws.element_size()
+    st = _lib().qlin_gemv(ctypes.byref(ws_struct), x.data_ptr(), y.data_ptr(), _ptr(ws), wsb,
+                          _stream())
+    _check(st, "qlin_gemv")
+    return y
+
+
+def gemm(w: QWeight, X: torch.Tensor, Y: Optional[torch.Tensor] = None,
+         ws: Optional[torch.Tensor] = "auto") -> torch.Tensor:
+    if X.dtype != torch.float16 or X.dim() != 2 or X.shape[1] != w.k or X.stride(1) != 1:
+        raise TypeError("X must be a float16 [m, k] tensor with contiguous rows")
+    m = X.shape[0]
+    if Y is None:
+        Y = torch.empty(m, w.n, dtype=torch.float32, device=X.device)
+    ws_struct = w.c_struct()
+    if isinstance(ws, str):
+        need = int(_lib().qlin_gemm_workspace_bytes(ctypes.byref(ws_struct), m))
+        ws = workspace(need, X.device)
+    wsb = 0 if ws is None else ws.numel() * ws.element_size()
+    st = _lib().qlin_gemm(ctypes.byref(ws_struct), X.data_ptr(), m, X.stride(0), Y.data_ptr(),
+                          Y.stride(0), _ptr(ws), wsb, _stream())
+    _check(st, "qlin_gemm")
+    return Y

@@ -1,0 +1,169 @@
+/*
+ * qlin -- fused dequantize-matmul over group-wise affine low-bit weights, for
+ * AMD Instinct MI355X (gfx950).  C ABI; every entry point enqueues HIP kernels
+ * on the caller's stream and returns without synchronizing.
+ *
+ * What is computed (the Bitcrush README, sections "The machine" and "Under the
+ * hood"; the Enargeia page, section "Run it"):
+ *   - W [n, k] holds n output rows; k is the reduction axis.  Along k, each row
+ *     is cut into groups of 64 weights ("SMART"), or one group covers the whole
+ *     row ("NAIVE", one scale per output channel).
+ *   - Each group has an fp16 scale s and an integer zero point z, found by
+ *     round-to-nearest from the group's min and max:
+ *         s = fp16( fl32( fl32(max - min) / qmax ) ),  qmax = 2^bits - 1
+ *         z = clamp( rint( fl32(-min / s) ), 0, qmax )
+ *     and each weight's code is  q = clamp( rint( fl32(w / s) ) + z, 0, qmax ),
+ *     rint rounding half-way cases to even.  A group whose stored scale is 0
+ *     (all values equal) has z = 0 and all codes 0.
+ *   - The matmul uses each code as the weight s * (q - z), formed in registers
+ *     and never written to memory, and accumulates in fp32.
+ *
+ * Memory ownership: the caller allocates and frees every buffer (device memory
+ * unless noted); the library allocates nothing and keeps no state apart from
+ * the calling thread's last HIP error code.  All pointers must be 16-byte
+ * aligned device pointers.  A call that fails validation returns an error
+ * before touching the GPU.  Output buffers must not overlap any input.
+ *
+ * ---------------------------------------------------------------------------
+ * Packed-code layout ("tiled"):
+ *   Rows are taken in tiles of 64; the last tile is padded with rows whose
+ *   codes, scales and zeros are 0.  k is cut into blocks of 64 codes (k must be
+ *   a multiple of 64).  The 64 codes of row n, block j occupy 2*bits uint32
+ *   words; blocks are stored tile-major, then block, then row within the tile:
+ *       word offset = ((n / 64) * (k / 64) + j) * 64 * 2*bits + (n % 64) * 2*bits
+ *   so one block of a whole tile (64 rows) is one contiguous 128*bits-byte run.
+ *   Inside a block:
+ *   - bits 2, 4, 8: word w holds codes c = w*(32/bits) + i, i = 0 .. 32/bits-1;
+ *     even i fill the low 16 bits and odd i the high 16 bits, each half from
+ *     its least significant bit up, in order of i:
+ *         bit position of code i = 16*(i % 2) + bits*(i / 2).
+ *   - bits 3: codes form two runs of 32 (run r = c / 32), each in three words.
+ *     Words 3r and 3r+1 hold the low two bits of run codes 0..15 and 16..31 in
+ *     the 2-bit arrangement above; word 3r+2 holds bit 2 of all 32 run codes:
+ *     run code c' (0..31) with u = c'/16, i = c'%16, p = i/2, e = i%2 puts it
+ *     at position  (p < 4 ? 2p + 2 : 2(p-4) + 3) + 16e,  plus 8 (mod 32) if u = 1.
+ *   With this arrangement, masking a word (or the word shifted right by 8)
+ *   leaves two consecutive codes in the mantissas of two fp16 halves, so a
+ *   pair of codes becomes a pair of fp16 values with one AND-OR.
+ * Scale and zero tables use the same tiling: entry (n, g) of the [n, G] table
+ * (G = k/64 for group 64, G = 1 for group k) is at ((n/64)*G + g)*64 + n%64.
+ * Scales are fp16 bit patterns (uint16), zeros uint8.
+ * ---------------------------------------------------------------------------
+ */
+#ifndef QLIN_H
+#define QLIN_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum qlin_status {
+  QLIN_OK = 0,
+  QLIN_ERR_NULL = 1,        /* a required pointer is NULL                        */
+  QLIN_ERR_SHAPE = 2,       /* n, k or m out of range, k % 64 != 0, pitch < row  */
+  QLIN_ERR_BITS = 3,        /* bits not in {2,3,4,8} (16: FP16_MASTER gemv only)  */
+  QLIN_ERR_GROUP = 4,       /* group neither 64 nor k                            */
+  QLIN_ERR_ALIGN = 5,       /* a pointer not 16-byte aligned, or a pitch not a
+                               multiple of 8 elements                            */
+  QLIN_ERR_FORMAT = 6,      /* unknown weight format, or format not allowed here  */
+  QLIN_ERR_ALIAS = 7,       /* an output overlaps an input                       */
+  QLIN_ERR_WORKSPACE = 8,   /* workspace too small for the chosen launch          */
+  QLIN_ERR_NO_DEVICE = 9,   /* no gfx950 device is current                       */
+  QLIN_ERR_HIP = 10         /* a HIP call failed; see qlin_last_hip_error()       */
+} qlin_status;
+
+enum {
+  QLIN_FMT_PACKED = 0,      /* data = tiled packed codes (uint32)                 */
+  QLIN_FMT_FP16_MASTER = 1  /* data = fp16 master weights [n, ld], row-major      */
+};
+
+/* A quantized weight matrix as seen by the matmul entry points. */
+typedef struct qlin_weight {
+  int32_t n;                /* output rows                                        */
+  int32_t k;                /* reduction length, multiple of 64                   */
+  int32_t bits;             /* 2, 3, 4, 8; or 16 = unquantized (FP16_MASTER)       */
+  int32_t group;            /* 64, or k for one group per row                     */
+  int32_t format;           /* QLIN_FMT_*                                         */
+  int32_t reserved;         /* must be 0                                          */
+  const void* data;         /* codes (PACKED) or fp16 masters (FP16_MASTER)       */
+  int64_t ld;               /* FP16_MASTER: row pitch in elements (>= k, % 8 == 0);
+                               PACKED: must be 0                                  */
+  const uint16_t* scale;    /* tiled fp16 scales; unused (may be NULL) if bits=16 */
+  const uint8_t* zero;      /* tiled uint8 zeros; unused (may be NULL) if bits=16 */
+} qlin_weight;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* qlin_status_string(int status);
+
+/* The HIP error code behind the calling thread's last QLIN_ERR_HIP (0 if none). */
+int qlin_last_hip_error(void);
+
+/* ABI version of this header; bumped on any incompatible change. */
+int qlin_abi_version(void);
+
+/* Bytes of the packed code buffer of an [n, k] matrix at `bits` (0 if invalid). */
+int64_t qlin_packed_bytes(int32_t n, int32_t k, int32_t bits);
+
+/* Entries of each (tiled) scale and zero table (0 if invalid). */
+int64_t qlin_meta_entries(int32_t n, int32_t k, int32_t group);
+
+/*
+ * Round-to-nearest quantization of fp16 master weights (per-group scale/zero
+ * precompute, then codes).  Bitcrush README, "Under the hood": a scale/zero
+ * precompute pass, then the group-wise affine rounding.
+ *   w16      fp16 masters [n, ld_w] row-major, ld_w >= k, ld_w % 8 == 0.
+ *   codes    packed codes out, qlin_packed_bytes(n, k, bits) bytes; pass NULL to
+ *            compute only scale and zero (a change of bit width then needs no
+ *            new codes: the fused matmul re-rounds on the fly).
+ *   scale    out, qlin_meta_entries(n, k, group) fp16 bit patterns (tiled).
+ *   zero     out, same number of uint8 entries (tiled).
+ * Padding rows of the last tile are written as 0.  Bit-exact and deterministic.
+ */
+qlin_status qlin_quantize(const uint16_t* w16, int64_t ld_w, int32_t n, int32_t k,
+                          int32_t bits, int32_t group, uint32_t* codes,
+                          uint16_t* scale, uint8_t* zero, hipStream_t stream);
+
+/*
+ * Workspace needed by qlin_gemv / qlin_gemm for their split-K launches.  0 means
+ * the launch needs none.  A workspace must be zero-filled before its first use;
+ * every call leaves it zero-filled again.  Calls that may run at the same time
+ * must not share a workspace.
+ */
+int64_t qlin_gemv_workspace_bytes(const qlin_weight* w);
+int64_t qlin_gemm_workspace_bytes(const qlin_weight* w, int32_t m);
+
+/*
+ * Decode GEMV, M = 1:  y[n] = sum_k x[k] * s(q - z)   (fp32 out).
+ * Enargeia, "Run it": every weight is read once per output word, unpacked in
+ * registers.  Bitcrush, "Under the hood": with FP16_MASTER the codes are
+ * recomputed from the fp16 masters as they are read (bits 2..8), or the plain
+ * fp16 weights are used (bits 16, the top of the lever).
+ *   x   fp16 [k];  y  fp32 [n].
+ *   workspace may be NULL when qlin_gemv_workspace_bytes(w) is 0; a smaller or
+ *   missing workspace makes the call use fewer, longer work items instead.
+ * Deterministic: the same inputs give bitwise the same y.
+ */
+qlin_status qlin_gemv(const qlin_weight* w, const uint16_t* x, float* y,
+                      void* workspace, int64_t workspace_bytes, hipStream_t stream);
+
+/*
+ * GEMM:  Y[m, n] = sum_k X[m, k] * s(q - z),  PACKED weights only.
+ * X fp16 [m, ld_x] (ld_x >= k, % 8 == 0), Y fp32 [m, ld_y] (ld_y >= n).
+ * X and the dequantized weights are rounded to bf16 (nearest-even) and fed to
+ * the bf16 matrix cores with fp32 accumulation (Enargeia, "Measured, not
+ * asserted": prefill is the dense, tiled-matmul form of the same product).
+ * Deterministic.  Workspace as for qlin_gemv.
+ */
+qlin_status qlin_gemm(const qlin_weight* w, const uint16_t* X, int32_t m, int64_t ld_x,
+                      float* Y, int64_t ld_y, void* workspace, int64_t workspace_bytes,
+                      hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QLIN_H */

@@ -1,0 +1,154 @@
+"""The C-ABI library: it builds, loads, exports every symbol include/qlin.h
+declares, and validates arguments on the host (no GPU needed: every error
+except QLIN_ERR_HIP / QLIN_ERR_NO_DEVICE is raised before any HIP call)."""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+import oracle
+from group_wise_bit_amd import qlin
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qlin.h")
+
+OK, NULL, SHAPE, BITS, GROUP, ALIGN, FORMAT, ALIAS, WORKSPACE, NODEV, HIP = range(11)
+FAKE = 0x7F0000000000        # a 16-byte aligned address that is never dereferenced
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(qlin_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return qlin.library()
+
+
+def test_exports_every_declared_symbol(lib):
+    declared = header_functions()
+    assert len(declared) == 10
+    assert sorted(qlin.EXPORTS) == declared
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_status_strings(lib):
+    for code, name in qlin.STATUS_NAMES.items():
+        assert lib.qlin_status_string(code).decode().startswith(name)
+    assert b"unknown" in lib.qlin_status_string(99)
+    assert lib.qlin_abi_version() == 1
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4, 8])
+@pytest.mark.parametrize("n,k", [(1, 64), (63, 128), (64, 64), (65, 896), (896, 896), (151936, 896)])
+def test_size_queries_match_layout(lib, bits, n, k):
+    assert lib.qlin_packed_bytes(n, k, bits) == 4 * oracle.packed_words(n, k, bits)
+    t = oracle.n_tiles(n)
+    assert lib.qlin_meta_entries(n, k, 64) == t * 64 * (k // 64)
+    assert lib.qlin_meta_entries(n, k, k) == t * 64
+
+
+def test_size_queries_reject(lib):
+    assert lib.qlin_packed_bytes(0, 64, 4) == 0
+    assert lib.qlin_packed_bytes(8, 100, 4) == 0
+    assert lib.qlin_packed_bytes(8, 64, 5) == 0
+    assert lib.qlin_packed_bytes(8, 64, 16) == 0
+    assert lib.qlin_meta_entries(8, 128, 32) == 0
+
+
+def quant(lib, w=FAKE, ld=128, n=8, k=128, bits=4, group=64, codes=FAKE + (1 << 30),
+          scale=FAKE + (2 << 30), zero=FAKE + (3 << 30)):
+    return lib.qlin_quantize(w, ld, n, k, bits, group, codes, scale, zero, None)
+
+
+def test_quantize_validation(lib):
+    assert quant(lib, w=None) == NULL
+    assert quant(lib, scale=None) == NULL
+    assert quant(lib, zero=None) == NULL
+    assert quant(lib, n=0) == SHAPE
+    assert quant(lib, k=100) == SHAPE
+    assert quant(lib, k=0) == SHAPE
+    assert quant(lib, ld=64) == SHAPE
+    assert quant(lib, ld=132) == ALIGN
+    assert quant(lib, bits=5) == BITS
+    assert quant(lib, bits=16) == BITS
+    assert quant(lib, group=32) == GROUP
+    assert quant(lib, group=256) == GROUP
+    assert quant(lib, w=FAKE + 8) == ALIGN
+    assert quant(lib, codes=FAKE + 4) == ALIGN
+    assert quant(lib, scale=FAKE) == ALIAS
+    assert quant(lib, codes=FAKE + 256) == ALIAS
+    assert quant(lib, zero=FAKE + (2 << 30) + 16) == ALIAS
+
+
+def weight(**kw):
+    d = dict(n=8, k=128, bits=4, group=64, format=0, reserved=0, data=FAKE, ld=0,
+             scale=FAKE + (1 << 30), zero=FAKE + (2 << 30))
+    d.update(kw)
+    return qlin.QlinWeightC(d["n"], d["k"], d["bits"], d["group"], d["format"], d["reserved"],
+                            d["data"], d["ld"], d["scale"], d["zero"])
+
+
+def gemv(lib, w, x=FAKE + (3 << 30), y=FAKE + (4 << 30), ws=None, wsb=0):
+    return lib.qlin_gemv(ctypes.byref(w), x, y, ws, wsb, None)
+
+
+def gemm(lib, w, X=FAKE + (3 << 30), m=4, ldx=128, Y=FAKE + (4 << 30), ldy=8, ws=None, wsb=0):
+    return lib.qlin_gemm(ctypes.byref(w), X, m, ldx, Y, ldy, ws, wsb, None)
+
+
+def test_gemv_validation(lib):
+    assert lib.qlin_gemv(None, FAKE, FAKE, None, 0, None) == NULL
+    assert gemv(lib, weight(data=None)) == NULL
+    assert gemv(lib, weight(scale=None)) == NULL
+    assert gemv(lib, weight(), x=None) == NULL
+    assert gemv(lib, weight(), y=None) == NULL
+    assert gemv(lib, weight(n=0)) == SHAPE
+    assert gemv(lib, weight(k=96)) == SHAPE
+    assert gemv(lib, weight(ld=128)) == SHAPE           # packed weights take no pitch
+    assert gemv(lib, weight(bits=16)) == BITS           # 16 only with fp16 masters
+    assert gemv(lib, weight(bits=1)) == BITS
+    assert gemv(lib, weight(group=128 + 64, k=128)) == GROUP
+    assert gemv(lib, weight(format=3)) == FORMAT
+    assert gemv(lib, weight(reserved=1)) == FORMAT
+    assert gemv(lib, weight(data=FAKE + 4)) == ALIGN
+    assert gemv(lib, weight(), x=FAKE + (3 << 30) + 2) == ALIGN
+    assert gemv(lib, weight(format=1, ld=64)) == SHAPE
+    assert gemv(lib, weight(format=1, ld=132)) == ALIGN
+    assert gemv(lib, weight(), y=FAKE + 64) == ALIAS    # y inside the codes
+    assert gemv(lib, weight(), y=FAKE + (3 << 30) + 16) == ALIAS
+    assert gemv(lib, weight(), ws=FAKE + (4 << 30), wsb=64) == ALIAS
+    assert gemv(lib, weight(), ws=FAKE + (5 << 30), wsb=-1) == WORKSPACE
+
+
+def test_gemm_validation(lib):
+    assert gemm(lib, weight(), X=None) == NULL
+    assert gemm(lib, weight(), m=0) == SHAPE
+    assert gemm(lib, weight(), ldx=64) == SHAPE
+    assert gemm(lib, weight(), ldy=4) == SHAPE
+    assert gemm(lib, weight(), ldx=132) == ALIGN
+    assert gemm(lib, weight(format=1, ld=128)) == FORMAT  # GEMM takes packed weights only
+    assert gemm(lib, weight(), Y=FAKE + (3 << 30)) == ALIAS
+
+
+@pytest.mark.skipif(torch.cuda.is_available(), reason="checks the no-GPU path")
+def test_no_device(lib):
+    assert quant(lib) == NODEV
+    assert gemv(lib, weight()) == NODEV
+    assert gemm(lib, weight()) == NODEV
+    assert gemm(lib, weight(), m=64, ldy=64) == NODEV
+
+
+def test_workspace_queries(lib):
+    big = weight(n=4096, k=4096)
+    need = lib.qlin_gemv_workspace_bytes(ctypes.byref(big))
+    assert need > 0 and need % 4 == 0
+    small = weight(n=151936, k=896)
+    assert lib.qlin_gemv_workspace_bytes(ctypes.byref(small)) == 0
+    assert lib.qlin_gemm_workspace_bytes(ctypes.byref(big), 8) > 0
+    assert lib.qlin_gemm_workspace_bytes(ctypes.byref(weight(bits=7)), 8) == 0
