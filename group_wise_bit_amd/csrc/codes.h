@@ -141,9 +141,9 @@ __device__ __forceinline__ float block_dot(const uint32_t* wd, const f16x2* __re
   }
 }
 
-// ------------------------------------------- MFMA operand decode (bf16 x 8)
+// -------------------------------------------- MFMA operand decode (fp16 x 8)
 // Eight consecutive codes of a block ("chunk") -> the exact fp32 weights
-// s * (q - z) -> bf16 (round to nearest even).  The fp32 value is exact: the
+// s * (q - z) -> fp16 (round to nearest even, v_cvt_pk_f16_f32).  The fp32 value is exact: the
 // product (1024 + S*q) * (s/S) has at most 22 significant bits, the constant
 // s * (1024/S + z) likewise, and their difference s * (q - z) is representable,
 // so the fma rounds nothing.
@@ -169,38 +169,38 @@ __device__ __forceinline__ void deq_pair(uint32_t magic_pair, float sS, float cS
   hi = __builtin_fmaf((float)h.y, sS, cS);
 }
 
-__device__ __forceinline__ bf16x8 to_bf16x8(const float* f) {
-  bf16x8 r;
+__device__ __forceinline__ f16x8 to_f16x8(const float* f) {
+  f16x8 r;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) r[i] = (__bf16)f[i];
+  for (int i = 0; i < 8; ++i) r[i] = (f16)f[i];
   return r;
 }
 
 // int4: one word = 8 codes.  S=1 for (v & 0x000F000F), S=16 for (v & 0x00F000F0).
-__device__ __forceinline__ bf16x8 deq_chunk4(uint32_t v, const Deq& d, uint32_t kMagic) {
+__device__ __forceinline__ f16x8 deq_chunk4(uint32_t v, const Deq& d, uint32_t kMagic) {
   float f[8];
   const uint32_t vs = v >> 8;
   deq_pair((v & 0x000F000Fu) | kMagic, d.sS[0], d.cS[0], f[0], f[1]);
   deq_pair((v & 0x00F000F0u) | kMagic, d.sS[2], d.cS[2], f[2], f[3]);
   deq_pair((vs & 0x000F000Fu) | kMagic, d.sS[0], d.cS[0], f[4], f[5]);
   deq_pair((vs & 0x00F000F0u) | kMagic, d.sS[2], d.cS[2], f[6], f[7]);
-  return to_bf16x8(f);
+  return to_f16x8(f);
 }
 
 // int2: half `hv` of a word (0: pairs 0..3 from v, 1: pairs 4..7 from v >> 8).
-__device__ __forceinline__ bf16x8 deq_chunk2(uint32_t v, const Deq& d, uint32_t kMagic) {
+__device__ __forceinline__ f16x8 deq_chunk2(uint32_t v, const Deq& d, uint32_t kMagic) {
   float f[8];
 #pragma unroll
   for (int p = 0; p < 4; ++p) {
     const uint32_t m = (3u << (2 * p)) | (3u << (16 + 2 * p));
     deq_pair((v & m) | kMagic, d.sS[p], d.cS[p], f[2 * p], f[2 * p + 1]);
   }
-  return to_bf16x8(f);
+  return to_f16x8(f);
 }
 
 // int3: low-bit word L (already shifted for the upper pairs) and high-bit word
 // H (already rotated / shifted to line up with L).
-__device__ __forceinline__ bf16x8 deq_chunk3(uint32_t L, uint32_t H, const Deq& d, uint32_t kMagic) {
+__device__ __forceinline__ f16x8 deq_chunk3(uint32_t L, uint32_t H, const Deq& d, uint32_t kMagic) {
   float f[8];
 #pragma unroll
   for (int p = 0; p < 4; ++p) {
@@ -209,30 +209,20 @@ __device__ __forceinline__ bf16x8 deq_chunk3(uint32_t L, uint32_t H, const Deq& 
     const uint32_t t = (L & m2) | (H & ~m2);
     deq_pair((t & (m2 | m1)) | kMagic, d.sS[p], d.cS[p], f[2 * p], f[2 * p + 1]);
   }
-  return to_bf16x8(f);
+  return to_f16x8(f);
 }
 
 // int8: two words = 8 codes.
-__device__ __forceinline__ bf16x8 deq_chunk8(uint32_t v, uint32_t u, const Deq& d) {
+__device__ __forceinline__ f16x8 deq_chunk8(uint32_t v, uint32_t u, const Deq& d) {
   float f[8];
   deq_pair(__builtin_amdgcn_perm(0x64646464u, v, 0x04020400u), d.sS[0], d.cS[0], f[0], f[1]);
   deq_pair(__builtin_amdgcn_perm(0x64646464u, v, 0x04030401u), d.sS[0], d.cS[0], f[2], f[3]);
   deq_pair(__builtin_amdgcn_perm(0x64646464u, u, 0x04020400u), d.sS[0], d.cS[0], f[4], f[5]);
   deq_pair(__builtin_amdgcn_perm(0x64646464u, u, 0x04030401u), d.sS[0], d.cS[0], f[6], f[7]);
-  return to_bf16x8(f);
+  return to_f16x8(f);
 }
 
-// fp16 x 8 (one uint4) -> bf16 x 8, round to nearest even.
-__device__ __forceinline__ bf16x8 h8_to_bf16x8(uint4 v) {
-  float f[8];
-  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const f16x2 h = as_h2(w[i]);
-    f[2 * i] = (float)h.x;
-    f[2 * i + 1] = (float)h.y;
-  }
-  return to_bf16x8(f);
-}
+// fp16 x 8 held in one uint4, as an MFMA operand.
+__device__ __forceinline__ f16x8 u4_to_f16x8(uint4 v) { return __builtin_bit_cast(f16x8, v); }
 
 }  // namespace qlin

@@ -1,5 +1,5 @@
 // qlin kernels for gfx950.  One wave owns one 64-row tile of W (lane = row)
-// in the quantizer and the GEMV kernels; the GEMMs feed bf16 MFMA.
+// in the quantizer and the GEMV kernels; the GEMMs feed fp16 MFMA.
 #pragma once
 
 #include "codes.h"
@@ -313,7 +313,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemv_fused(
 }
 
 // ------------------------------------------------------ skinny GEMM (M<=16)
-// v_mfma_f32_16x16x32_bf16: A = X (16 rows, zero past m), B = W^T.  Lane
+// v_mfma_f32_16x16x32_f16: A = X (16 rows, zero past m), B = W^T.  Lane
 // (c = lane % 16, q = lane / 16) supplies row c and the 8 K-positions
 // 16q + 8s .. +7 of the block for instruction s in {0, 1}; both operands use
 // this same assignment of K positions, which therefore only permutes the sum.
@@ -338,7 +338,7 @@ __device__ __forceinline__ void load_quarter(const uint32_t* __restrict__ blk, i
 
 // The 8 codes of the lane's quarter for instruction s (0 or 1).
 template <int BITS>
-__device__ __forceinline__ bf16x8 deq_quarter(const uint32_t* wl, int s, const Deq& d, uint32_t magic) {
+__device__ __forceinline__ f16x8 deq_quarter(const uint32_t* wl, int s, const Deq& d, uint32_t magic) {
   if constexpr (BITS == 4) {
     return deq_chunk4(wl[s], d, magic);
   } else if constexpr (BITS == 2) {
@@ -370,15 +370,15 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_skinny(
   const bool xrow = c < m;
   const uint16_t* xr = X + (int64_t)(xrow ? c : 0) * ldx;
   for (int j = j0 + wave; j < j1; j += WAVES) {
-    bf16x8 a[2];
+    f16x8 a[2];
     {
       uint4 v0 = make_uint4(0, 0, 0, 0), v1 = make_uint4(0, 0, 0, 0);
       if (xrow) {
         const uint4* xp = reinterpret_cast<const uint4*>(xr + (int64_t)j * kBlock + 16 * q);
         v0 = xp[0]; v1 = xp[1];
       }
-      a[0] = h8_to_bf16x8(v0);
-      a[1] = h8_to_bf16x8(v1);
+      a[0] = u4_to_f16x8(v0);
+      a[1] = u4_to_f16x8(v1);
     }
     const int g = (G == 1) ? 0 : j;
 #pragma unroll
@@ -391,7 +391,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_skinny(
       const Deq d = make_deq(h2f(scale[mi]), zero[mi]);
 #pragma unroll
       for (int s = 0; s < 2; ++s)
-        acc[cg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[s], deq_quarter<BITS>(wl, s, d, magic),
+        acc[cg] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[s], deq_quarter<BITS>(wl, s, d, magic),
                                                           acc[cg], 0, 0, 0);
     }
   }
@@ -435,15 +435,15 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_skinny(
 }
 
 // ----------------------------------------------------- tiled GEMM (M>16) --
-// v_mfma_f32_32x32x16_bf16.  Work-group = 4 waves; wave w owns W tile
+// v_mfma_f32_32x32x16_f16.  Work-group = 4 waves; wave w owns W tile
 // blockIdx.x*4 + w (64 rows = two 32-column MFMA blocks), all MB rows of X.
-// X blocks are converted to bf16 once per work-group into LDS (double
+// X blocks are staged once per work-group in LDS as they are (fp16, double
 // buffered, rows padded to 144 bytes); the weight operand is decoded straight
 // from global memory into registers, so each code is read and decoded once
 // per work-group.  Lane (c = lane % 32, h = lane / 32) supplies row c and the
 // K positions 32h + 8s .. +7 of the block for instruction s in 0..3.
 // D[8*(r/4) + 4*h + r%4][c] is acc register r.
-constexpr int kLdsRow = 72;   // bf16 per padded LDS row
+constexpr int kLdsRow = 72;   // fp16 per padded LDS row
 
 template <int BITS>
 __device__ __forceinline__ void load_half(const uint32_t* __restrict__ blk, int h, uint32_t* wl) {
@@ -464,7 +464,7 @@ __device__ __forceinline__ void load_half(const uint32_t* __restrict__ blk, int 
 }
 
 template <int BITS>
-__device__ __forceinline__ bf16x8 deq_half(const uint32_t* wl, int s, const Deq& d, uint32_t magic) {
+__device__ __forceinline__ f16x8 deq_half(const uint32_t* wl, int s, const Deq& d, uint32_t magic) {
   if constexpr (BITS == 4) {
     return deq_chunk4(wl[s], d, magic);
   } else if constexpr (BITS == 2) {
@@ -488,7 +488,7 @@ __global__ __launch_bounds__(256) void k_gemm_tiles(
   constexpr int WPB = 2 * BITS;
   constexpr int RB = MB / 32;               // 32-row MFMA blocks of X
   constexpr int XCH = MB * 8 / 256;         // 16-byte X chunks per thread per block
-  __shared__ __attribute__((aligned(16))) __bf16 xs[2][MB][kLdsRow];
+  __shared__ __attribute__((aligned(16))) f16 xs[2][MB][kLdsRow];
   const int tid = threadIdx.x;
   const int lane = lane_id(), wave = wave_id();
   const int c = lane & 31, h = lane >> 5;
@@ -520,7 +520,7 @@ __global__ __launch_bounds__(256) void k_gemm_tiles(
     for (int i = 0; i < XCH; ++i) {
       const int ch = tid + 256 * i;
       const int row = ch >> 3, c8 = ch & 7;
-      *reinterpret_cast<bf16x8*>(&xs[buf][row][8 * c8]) = h8_to_bf16x8(xv[i]);
+      *reinterpret_cast<uint4*>(&xs[buf][row][8 * c8]) = xv[i];
     }
   };
   auto load_w = [&](int j, uint32_t (*wl)[WPB / 2], float* s, int* z) {
@@ -545,7 +545,7 @@ __global__ __launch_bounds__(256) void k_gemm_tiles(
   uint4 xv[XCH];
   uint32_t wl[2][WPB / 2];
   float sc[2]; int zc[2];
-  bf16x8 bfrag[2][4];
+  f16x8 bfrag[2][4];
 
   load_x(0, xv);
   load_w(0, wl, sc, zc);
@@ -569,10 +569,10 @@ __global__ __launch_bounds__(256) void k_gemm_tiles(
     for (int rb = 0; rb < RB; ++rb) {
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(&xs[cur][32 * rb + c][32 * h + 8 * s]);
+        const f16x8 a = *reinterpret_cast<const f16x8*>(&xs[cur][32 * rb + c][32 * h + 8 * s]);
 #pragma unroll
         for (int cb = 0; cb < 2; ++cb)
-          acc[rb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bfrag[cb][s], acc[rb][cb], 0, 0, 0);
+          acc[rb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, bfrag[cb][s], acc[rb][cb], 0, 0, 0);
       }
     }
     if (more) {

@@ -129,9 +129,11 @@ qlin_status qlin_quantize(const uint16_t* w16, int64_t ld_w, int32_t n, int32_t 
 
 /*
  * Workspace needed by qlin_gemv / qlin_gemm for their split-K launches.  0 means
- * the launch needs none.  A workspace must be zero-filled before its first use;
- * every call leaves it zero-filled again.  Calls that may run at the same time
- * must not share a workspace.
+ * the launch needs none.  Layout: fp32 partial sums, then one uint32 arrival
+ * counter per 64-row tile in the last 4*ceil(n/64) bytes of the size returned
+ * here.  The counters must be zero before first use (e.g. zero-fill the whole
+ * workspace once); every call leaves them zero again, the partials are scratch.
+ * Calls that may run at the same time must not share a workspace.
  */
 int64_t qlin_gemv_workspace_bytes(const qlin_weight* w);
 int64_t qlin_gemm_workspace_bytes(const qlin_weight* w, int32_t m);
@@ -153,9 +155,13 @@ qlin_status qlin_gemv(const qlin_weight* w, const uint16_t* x, float* y,
 /*
  * GEMM:  Y[m, n] = sum_k X[m, k] * s(q - z),  PACKED weights only.
  * X fp16 [m, ld_x] (ld_x >= k, % 8 == 0), Y fp32 [m, ld_y] (ld_y >= n).
- * X and the dequantized weights are rounded to bf16 (nearest-even) and fed to
- * the bf16 matrix cores with fp32 accumulation (Enargeia, "Measured, not
- * asserted": prefill is the dense, tiled-matmul form of the same product).
+ * X is used as given (fp16) and each dequantized weight s*(q - z), formed
+ * exactly in fp32, is rounded to fp16 (nearest even); both feed the fp16
+ * matrix cores with fp32 accumulation (Enargeia, "Measured, not asserted":
+ * prefill is the dense, tiled-matmul form of the same product).  fp16 rather
+ * than bf16 operands: bf16 rounding of X and of the weights alone exceeds
+ * 1e-3 * max_row sum |x w| at short reductions (k = 192), at the same
+ * matrix-core rate.
  * Deterministic.  Workspace as for qlin_gemv.
  */
 qlin_status qlin_gemm(const qlin_weight* w, const uint16_t* X, int32_t m, int64_t ld_x,
