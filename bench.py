@@ -46,7 +46,20 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--phases", default="all",
                    help="comma list of stages to run (default: all)")
+    p.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                   help="only run a plain device-to-device copy of BYTES bytes five times "
+                        "(reference for scaling HBM traffic counters), then exit")
     return p.parse_args()
+
+
+def copy_calibration(nbytes):
+    import torch
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": nbytes, "launches": 5}), flush=True)
 
 
 def main():
@@ -55,6 +68,10 @@ def main():
         print(f"bench.py: this build measures one GPU only; --gpus {args.gpus} is not supported "
               "(the path would shard output rows across GPUs; see DESIGN.md)", file=sys.stderr)
         sys.exit(2)
+
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
 
     import torch
     import synth
@@ -212,7 +229,7 @@ def main():
             "achieved": round(dec_bytes / 169 / (per_launch_us * 1e-6) / 1e9, 2),
             "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(dec_bytes / 169 / (per_launch_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": measured_traffic(),
             "algorithmic_bytes_per_launch": dec_bytes / 169,
             "avg_launch_us": round(per_launch_us, 3),
         }
@@ -226,6 +243,36 @@ def main():
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(shapes)
     print(json.dumps(out), flush=True)
+
+
+TRAFFIC_SUMMARY = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
+                               "gemv_packed_int4_qwen25_decode_hbm_traffic.txt")
+
+
+def kernel_source_hash():
+    import glob
+    import hashlib
+    csrc = os.path.join(os.path.dirname(os.path.abspath(__file__)), "group_wise_bit_amd", "csrc")
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(csrc, "*.h")) + glob.glob(os.path.join(csrc, "*.hip"))):
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per decode launch from the committed rocprofv3 counter summary,
+    or None when the kernel sources changed after the counters were taken."""
+    try:
+        text = open(TRAFFIC_SUMMARY).read()
+    except OSError:
+        return None
+    vals = dict(line.split(": ", 1) for line in text.splitlines()
+                if line.startswith(("kernel source sha256", "traffic_bytes_per_launch")))
+    key = [k for k in vals if k.startswith("kernel source sha256")]
+    if not key or vals[key[0]].strip() != kernel_source_hash():
+        return None
+    return float(vals["traffic_bytes_per_launch"])
 
 
 def cpu_baseline(shapes):

@@ -73,8 +73,9 @@ __device__ __forceinline__ float rtn_fix(float w, float q0, const RtnParams& p) 
   return q0;
 }
 
+// clamp to [lo, hi] (lo <= hi, v finite): one v_med3_f32
 __device__ __forceinline__ float clampf(float v, float lo, float hi) {
-  return __builtin_fminf(__builtin_fmaxf(v, lo), hi);
+  return __builtin_amdgcn_fmed3f(v, lo, hi);
 }
 
 }  // namespace qlin

@@ -2,6 +2,8 @@
 // in the quantizer and the GEMV kernels; the GEMMs feed fp16 MFMA.
 #pragma once
 
+#include <type_traits>
+
 #include "codes.h"
 
 namespace qlin {
@@ -163,10 +165,29 @@ __device__ __forceinline__ bool split_ticket(uint32_t* __restrict__ tickets, int
 }
 
 // -------------------------------------------------------- packed GEMV --
-// grid = (tiles, splits), block = WAVES waves.  Wave w of split s walks
-// K-blocks j0+w, j0+w+WAVES, ... of [j0, j1); lane = row of the tile.
-// x is read with wave-uniform addresses (scalar loads, shared by all rows).
-template <int BITS, int WAVES>
+// grid = (tiles, splits), block = WAVES waves.  Wave w of split s takes the
+// K-blocks j0+w, j0+w+WAVES, ... of [j0, j1) (the waves of a work-group read
+// consecutive 128*bits-byte runs); lane = row of the tile.  A wave issues the
+// loads of up to U blocks before decoding any, so a short K range costs one
+// memory round trip.  x is read with wave-uniform addresses (scalar loads,
+// shared by all rows of the tile).
+template <int BITS>
+__device__ __forceinline__ void load_block_words(const uint32_t* __restrict__ blk, uint32_t* wd) {
+  if constexpr (BITS == 3) {
+    const uint2* b2 = reinterpret_cast<const uint2*>(blk);
+#pragma unroll
+    for (int i = 0; i < 3; ++i) { const uint2 v = b2[i]; wd[2 * i] = v.x; wd[2 * i + 1] = v.y; }
+  } else {
+    const uint4* b4 = reinterpret_cast<const uint4*>(blk);
+#pragma unroll
+    for (int i = 0; i < BITS / 2; ++i) {
+      const uint4 v = b4[i];
+      wd[4 * i] = v.x; wd[4 * i + 1] = v.y; wd[4 * i + 2] = v.z; wd[4 * i + 3] = v.w;
+    }
+  }
+}
+
+template <int BITS, int WAVES, int U>
 __global__ __launch_bounds__(WAVES * 64) void k_gemv_packed(
     const uint32_t* __restrict__ codes, const uint16_t* __restrict__ scale,
     const uint8_t* __restrict__ zero, const f16x2* __restrict__ x2, float* __restrict__ y,
@@ -180,26 +201,26 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemv_packed(
   const int j0 = sp * kbps;
   const int j1 = min(kb, j0 + kbps);
   float yacc = 0.f;
-  for (int j = j0 + wave; j < j1; j += WAVES) {
-    const uint32_t* blk = codes + (((int64_t)t * kb + j) * kTile + lane) * WPB;
-    uint32_t wd[WPB];
-    if constexpr (BITS == 3) {
-      const uint2* b2 = reinterpret_cast<const uint2*>(blk);
+  for (int jb = j0 + wave; jb < j1; jb += WAVES * U) {
+    uint32_t wd[U][WPB];
+    float s[U];
+    int z[U];
 #pragma unroll
-      for (int i = 0; i < 3; ++i) { const uint2 v = b2[i]; wd[2 * i] = v.x; wd[2 * i + 1] = v.y; }
-    } else {
-      const uint4* b4 = reinterpret_cast<const uint4*>(blk);
-#pragma unroll
-      for (int i = 0; i < WPB / 4; ++i) {
-        const uint4 v = b4[i];
-        wd[4 * i] = v.x; wd[4 * i + 1] = v.y; wd[4 * i + 2] = v.z; wd[4 * i + 3] = v.w;
+    for (int u = 0; u < U; ++u) {
+      const int j = jb + u * WAVES;
+      if (j < j1) {
+        load_block_words<BITS>(codes + (((int64_t)t * kb + j) * kTile + lane) * WPB, wd[u]);
+        const int64_t mi = ((int64_t)t * G + ((G == 1) ? 0 : j)) * kTile + lane;
+        s[u] = h2f(scale[mi]);
+        z[u] = zero[mi];
       }
     }
-    const int g = (G == 1) ? 0 : j;
-    const int64_t mi = ((int64_t)t * G + g) * kTile + lane;
-    const float s = h2f(scale[mi]);
-    const int z = zero[mi];
-    yacc = __builtin_fmaf(s, block_dot<BITS>(wd, x2 + (int64_t)j * 32, z, magic), yacc);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int j = jb + u * WAVES;
+      if (j < j1)
+        yacc = __builtin_fmaf(s[u], block_dot<BITS>(wd[u], x2 + (int64_t)j * 32, z[u], magic), yacc);
+    }
   }
   red[wave][lane] = yacc;
   __syncthreads();
@@ -224,7 +245,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemv_packed(
 // Reads the fp16 masters, re-rounds every weight with the group's scale/zero
 // as it is read (codes never stored), accumulates x * (q - z) per group and
 // scales by s.  BITS == 16 is the unquantized control: x * w.
-template <int BITS, int WAVES>
+template <int BITS, int WAVES, int U>
 __global__ __launch_bounds__(WAVES * 64) void k_gemv_fused(
     const uint16_t* __restrict__ w16, int64_t ld, const uint16_t* __restrict__ scale,
     const uint8_t* __restrict__ zero, const f16x2* __restrict__ x2, float* __restrict__ y,
@@ -239,10 +260,28 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemv_fused(
   const int j0 = sp * kbps;
   const int j1 = min(kb, j0 + kbps);
   float yacc = 0.f;
-  for (int j = j0 + wave; j < j1; j += WAVES) {
-    uint4 wv[8];
+  for (int jb = j0 + wave; jb < j1; jb += WAVES * U) {
+   uint4 wvu[U][8];
+   float su[U];
+   int zu[U];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) wv[i] = wr[(int64_t)j * 8 + i];
+   for (int u = 0; u < U; ++u) {
+    const int j = jb + u * WAVES;
+    if (j < j1) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) wvu[u][i] = wr[(int64_t)j * 8 + i];
+      if constexpr (BITS != 16) {
+        const int64_t mi = ((int64_t)t * G + ((G == 1) ? 0 : j)) * kTile + lane;
+        su[u] = h2f(scale[mi]);
+        zu[u] = zero[mi];
+      }
+    }
+   }
+#pragma unroll
+   for (int u = 0; u < U; ++u) {
+    const int j = jb + u * WAVES;
+    if (j >= j1) continue;
+    const uint4* wv = wvu[u];
     const f16x2* xb = x2 + (int64_t)j * 32;
     if constexpr (BITS == 16) {
       float a = 0.f, b = 0.f;
@@ -256,10 +295,8 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemv_fused(
       yacc += a + b;
     } else {
       constexpr int qmax = (1 << BITS) - 1;
-      const int g = (G == 1) ? 0 : j;
-      const int64_t mi = ((int64_t)t * G + g) * kTile + lane;
-      const float s = h2f(scale[mi]);
-      const RtnParams p = rtn_params(s, zero[mi], qmax);
+      const float s = su[u];
+      const RtnParams p = rtn_params(s, zu[u], qmax);
       float a = 0.f, b = 0.f;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
@@ -293,6 +330,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemv_fused(
       }
       yacc = __builtin_fmaf(s, a + b, yacc);
     }
+   }
   }
   red[wave][lane] = yacc;
   __syncthreads();
@@ -350,49 +388,65 @@ __device__ __forceinline__ f16x8 deq_quarter(const uint32_t* wl, int s, const De
   }
 }
 
-template <int BITS, int WAVES>
+template <int BITS, int WAVES, int U>
 __global__ __launch_bounds__(WAVES * 64) void k_gemm_skinny(
     const uint32_t* __restrict__ codes, const uint16_t* __restrict__ scale,
     const uint8_t* __restrict__ zero, const uint16_t* __restrict__ X, int64_t ldx, int m,
     float* __restrict__ Y, int64_t ldy, float* __restrict__ part, uint32_t* __restrict__ tickets,
     int n, int kb, int G, int splits, int kbps) {
   constexpr int WPB = 2 * BITS;
+  constexpr int QW = (BITS == 3) ? 2 : BITS / 2;       // words held per quarter block
   __shared__ f32x4 red[WAVES][4][64];
+  const uint32_t magic = vreg_const(kMagic);
   const int lane = lane_id(), wave = wave_id();
   const int c = lane & 15, q = lane >> 4;
   const int t = blockIdx.x, sp = blockIdx.y;
   const int j0 = sp * kbps;
   const int j1 = min(kb, j0 + kbps);
-  const uint32_t magic = vreg_const(kMagic);
   f32x4 acc[4];
 #pragma unroll
   for (int cg = 0; cg < 4; ++cg) acc[cg] = (f32x4){0.f, 0.f, 0.f, 0.f};
   const bool xrow = c < m;
   const uint16_t* xr = X + (int64_t)(xrow ? c : 0) * ldx;
-  for (int j = j0 + wave; j < j1; j += WAVES) {
-    f16x8 a[2];
-    {
-      uint4 v0 = make_uint4(0, 0, 0, 0), v1 = make_uint4(0, 0, 0, 0);
+  for (int jb = j0 + wave; jb < j1; jb += WAVES * U) {
+    uint4 xv[U][2];
+    uint32_t wl[U][4][QW];
+    float su[U][4];
+    int zu[U][4];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int j = jb + u * WAVES;
+      if (j >= j1) continue;
+      xv[u][0] = make_uint4(0, 0, 0, 0);
+      xv[u][1] = make_uint4(0, 0, 0, 0);
       if (xrow) {
         const uint4* xp = reinterpret_cast<const uint4*>(xr + (int64_t)j * kBlock + 16 * q);
-        v0 = xp[0]; v1 = xp[1];
+        xv[u][0] = xp[0];
+        xv[u][1] = xp[1];
       }
-      a[0] = u4_to_f16x8(v0);
-      a[1] = u4_to_f16x8(v1);
+      const int g = (G == 1) ? 0 : j;
+#pragma unroll
+      for (int cg = 0; cg < 4; ++cg) {
+        const int r = 16 * cg + c;
+        load_quarter<BITS>(codes + (((int64_t)t * kb + j) * kTile + r) * WPB, q, wl[u][cg]);
+        const int64_t mi = ((int64_t)t * G + g) * kTile + r;
+        su[u][cg] = h2f(scale[mi]);
+        zu[u][cg] = zero[mi];
+      }
     }
-    const int g = (G == 1) ? 0 : j;
 #pragma unroll
-    for (int cg = 0; cg < 4; ++cg) {
-      const int r = 16 * cg + c;
-      const uint32_t* blk = codes + (((int64_t)t * kb + j) * kTile + r) * WPB;
-      uint32_t wl[4];
-      load_quarter<BITS>(blk, q, wl);
-      const int64_t mi = ((int64_t)t * G + g) * kTile + r;
-      const Deq d = make_deq(h2f(scale[mi]), zero[mi]);
+    for (int u = 0; u < U; ++u) {
+      const int j = jb + u * WAVES;
+      if (j >= j1) continue;
+      const f16x8 a0 = u4_to_f16x8(xv[u][0]), a1 = u4_to_f16x8(xv[u][1]);
 #pragma unroll
-      for (int s = 0; s < 2; ++s)
-        acc[cg] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[s], deq_quarter<BITS>(wl, s, d, magic),
-                                                          acc[cg], 0, 0, 0);
+      for (int cg = 0; cg < 4; ++cg) {
+        const Deq d = make_deq(su[u][cg], zu[u][cg]);
+        acc[cg] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, deq_quarter<BITS>(wl[u][cg], 0, d, magic),
+                                                         acc[cg], 0, 0, 0);
+        acc[cg] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, deq_quarter<BITS>(wl[u][cg], 1, d, magic),
+                                                         acc[cg], 0, 0, 0);
+      }
     }
   }
 #pragma unroll
@@ -486,6 +540,7 @@ __global__ __launch_bounds__(256) void k_gemm_tiles(
     const uint8_t* __restrict__ zero, const uint16_t* __restrict__ X, int64_t ldx, int m,
     float* __restrict__ Y, int64_t ldy, int n, int kb, int G, int tiles) {
   constexpr int WPB = 2 * BITS;
+  constexpr int HW = WPB / 2;               // words of a half block
   constexpr int RB = MB / 32;               // 32-row MFMA blocks of X
   constexpr int XCH = MB * 8 / 256;         // 16-byte X chunks per thread per block
   __shared__ __attribute__((aligned(16))) f16 xs[2][MB][kLdsRow];
@@ -494,6 +549,7 @@ __global__ __launch_bounds__(256) void k_gemm_tiles(
   const int c = lane & 31, h = lane >> 5;
   const int t = blockIdx.x * 4 + wave;
   const bool tvalid = t < tiles;
+  const int tt = tvalid ? t : 0;
   const int m0 = blockIdx.y * MB;
   const uint32_t magic = vreg_const(kMagic);
 
@@ -505,101 +561,118 @@ __global__ __launch_bounds__(256) void k_gemm_tiles(
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[rb][cb][r] = 0.f;
 
-  auto load_x = [&](int j, uint4* xv) {
+  // per-thread X chunk addresses (rows past m read row m0, then zeroed)
+  const uint16_t* xsrc[XCH];
+  bool xok[XCH];
 #pragma unroll
-    for (int i = 0; i < XCH; ++i) {
-      const int ch = tid + 256 * i;
-      const int row = ch >> 3, c8 = ch & 7;
-      xv[i] = make_uint4(0, 0, 0, 0);
-      if (m0 + row < m)
-        xv[i] = *reinterpret_cast<const uint4*>(X + (int64_t)(m0 + row) * ldx + (int64_t)j * kBlock + 8 * c8);
-    }
-  };
-  auto store_x = [&](int buf, const uint4* xv) {
+  for (int i = 0; i < XCH; ++i) {
+    const int ch = tid + 256 * i;
+    const int row = ch >> 3, c8 = ch & 7;
+    xok[i] = m0 + row < m;
+    xsrc[i] = X + (int64_t)(xok[i] ? m0 + row : 0) * ldx + 8 * c8;
+  }
+  const uint32_t* wsrc[2];
+  int64_t msrc[2];
 #pragma unroll
-    for (int i = 0; i < XCH; ++i) {
-      const int ch = tid + 256 * i;
-      const int row = ch >> 3, c8 = ch & 7;
-      *reinterpret_cast<uint4*>(&xs[buf][row][8 * c8]) = xv[i];
-    }
-  };
-  auto load_w = [&](int j, uint32_t (*wl)[WPB / 2], float* s, int* z) {
+  for (int cb = 0; cb < 2; ++cb) {
+    const int r = 32 * cb + c;
+    wsrc[cb] = codes + ((int64_t)tt * kb * kTile + r) * WPB;
+    msrc[cb] = (int64_t)tt * G * kTile + r;
+  }
+
+  uint4 xv[2][XCH];
+  uint32_t wl[2][2][HW];
+  float sc[2][2];
+  int zc[2][2];
+  f16x8 bfrag[2][2][4];      // [register set][column block][slice]
+
+  // Block data moves: issue (global -> registers, set p), land (registers ->
+  // LDS buffer p and decoded B fragments of set p), mma (LDS buffer p and B
+  // fragments of set p -> accumulators).  All set / buffer indices are
+  // compile-time, so the scheduler may interleave one block's decode with the
+  // previous block's MFMAs.
+  auto issue = [&](int j, auto setc) {
+    constexpr int P = decltype(setc)::value;
+#pragma unroll
+    for (int i = 0; i < XCH; ++i)
+      xv[P][i] = *reinterpret_cast<const uint4*>(xsrc[i] + (int64_t)j * kBlock);
     const int g = (G == 1) ? 0 : j;
 #pragma unroll
     for (int cb = 0; cb < 2; ++cb) {
-      const int r = 32 * cb + c;
-      if (tvalid) {
-        const uint32_t* blk = codes + (((int64_t)t * kb + j) * kTile + r) * WPB;
-        load_half<BITS>(blk, h, wl[cb]);
-        const int64_t mi = ((int64_t)t * G + g) * kTile + r;
-        s[cb] = h2f(scale[mi]);
-        z[cb] = zero[mi];
-      } else {
-#pragma unroll
-        for (int i = 0; i < WPB / 2; ++i) wl[cb][i] = 0;
-        s[cb] = 0.f; z[cb] = 0;
-      }
+      load_half<BITS>(wsrc[cb] + (int64_t)j * kTile * WPB, h, wl[P][cb]);
+      sc[P][cb] = h2f(scale[msrc[cb] + (int64_t)g * kTile]);
+      zc[P][cb] = zero[msrc[cb] + (int64_t)g * kTile];
     }
   };
-
-  uint4 xv[XCH];
-  uint32_t wl[2][WPB / 2];
-  float sc[2]; int zc[2];
-  f16x8 bfrag[2][4];
-
-  load_x(0, xv);
-  load_w(0, wl, sc, zc);
-  store_x(0, xv);
+  auto land = [&](auto setc) {
+    constexpr int P = decltype(setc)::value;
 #pragma unroll
-  for (int cb = 0; cb < 2; ++cb) {
-    const Deq d = make_deq(sc[cb], zc[cb]);
-#pragma unroll
-    for (int s = 0; s < 4; ++s) bfrag[cb][s] = deq_half<BITS>(wl[cb], s, d, magic);
-  }
-  __syncthreads();
-
-  for (int j = 0; j < kb; ++j) {
-    const int cur = j & 1;
-    const bool more = j + 1 < kb;
-    if (more) {
-      load_x(j + 1, xv);
-      load_w(j + 1, wl, sc, zc);
+    for (int i = 0; i < XCH; ++i) {
+      const int ch = tid + 256 * i;
+      const int row = ch >> 3, c8 = ch & 7;
+      const uint4 v = xok[i] ? xv[P][i] : make_uint4(0, 0, 0, 0);
+      *reinterpret_cast<uint4*>(&xs[P][row][8 * c8]) = v;
     }
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const f16x8 a = *reinterpret_cast<const f16x8*>(&xs[cur][32 * rb + c][32 * h + 8 * s]);
-#pragma unroll
-        for (int cb = 0; cb < 2; ++cb)
-          acc[rb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, bfrag[cb][s], acc[rb][cb], 0, 0, 0);
-      }
-    }
-    if (more) {
-      store_x(cur ^ 1, xv);
-#pragma unroll
-      for (int cb = 0; cb < 2; ++cb) {
-        const Deq d = make_deq(sc[cb], zc[cb]);
-#pragma unroll
-        for (int s = 0; s < 4; ++s) bfrag[cb][s] = deq_half<BITS>(wl[cb], s, d, magic);
-      }
-    }
-    __syncthreads();
-  }
-
-  if (!tvalid) return;
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
     for (int cb = 0; cb < 2; ++cb) {
-      const int col = t * kTile + 32 * cb + c;
-      if (col >= n) continue;
+      const float s = tvalid ? sc[P][cb] : 0.f;
+      const Deq d = make_deq(s, zc[P][cb]);
+#pragma unroll
+      for (int s4 = 0; s4 < 4; ++s4) bfrag[P][cb][s4] = deq_half<BITS>(wl[P][cb], s4, d, magic);
+    }
+  };
+  auto mma = [&](auto setc) {
+    constexpr int P = decltype(setc)::value;
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4) {
+      f16x8 a[RB];
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb)
+        a[rb] = *reinterpret_cast<const f16x8*>(&xs[P][32 * rb + c][32 * h + 8 * s4]);
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb)
+          acc[rb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[rb], bfrag[P][cb][s4], acc[rb][cb],
+                                                               0, 0, 0);
+    }
+  };
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+
+  // pipeline: block j computes while block j+1 is decoded and j+2 is loading
+  issue(0, S0{});
+  if (kb > 1) issue(1, S1{});
+  land(S0{});
+  __syncthreads();
+  int j = 0;
+  for (; j + 1 < kb; j += 2) {
+    if (j + 2 < kb) issue(j + 2, S0{});
+    mma(S0{});
+    land(S1{});
+    __syncthreads();
+    if (j + 3 < kb) issue(j + 3, S1{});
+    mma(S1{});
+    if (j + 2 < kb) land(S0{});
+    __syncthreads();
+  }
+  if (j < kb) mma(S0{});     // odd kb: the last block sits in set 0
+
+  if (!tvalid) return;
+  // rows m0 + 32rb + 8(r/4) + 4h + r%4 of columns t*64 + 32cb + c
+  float* ybase = Y + (int64_t)(m0 + 4 * h) * ldy + t * kTile + c;
+  const int mrem = m - m0 - 4 * h;
+#pragma unroll
+  for (int cb = 0; cb < 2; ++cb) {
+    if (t * kTile + 32 * cb + c >= n) continue;
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int mrow = m0 + 32 * rb + 8 * (r >> 2) + 4 * h + (r & 3);
-        if (mrow < m) Y[(int64_t)mrow * ldy + col] = acc[rb][cb][r];
+        const int dr = 32 * rb + 8 * (r >> 2) + (r & 3);
+        if (dr < mrem) ybase[(int64_t)dr * ldy + 32 * cb] = acc[rb][cb][r];
       }
-    }
+  }
 }
 
 }  // namespace qlin

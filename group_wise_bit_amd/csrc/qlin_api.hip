@@ -3,6 +3,8 @@
 #include <hip/hip_runtime.h>
 
 #include <stdint.h>
+#include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include "../../include/qlin.h"
@@ -18,7 +20,7 @@ constexpr int kWaves = 4;                    // waves per work-group (GEMV, skin
 constexpr int kMaxN = 1 << 24;
 constexpr int kMaxK = 1 << 20;
 constexpr int kMaxM = 1 << 20;
-constexpr int kTargetGroups = 1024;          // work-groups a split-K launch aims for
+constexpr int kTargetGroups = 64;            // work-groups a split-K launch aims for
 constexpr int kMinBlocksPerWave = 2;         // K-blocks per wave before splitting further
 
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -116,14 +118,26 @@ bool output_overlaps_weight(const qlin_weight* w, Range out) {
 // Split of the K-blocks over work-groups for the tile-per-work-group kernels.
 struct Split { int splits, kbps; };
 
+// Workspace layout: a fixed region of arrival counters (one uint32 per tile,
+// kCounterBytes, so calls of any shape can share one workspace without their
+// partial sums ever landing on another call's counters), then the fp32
+// partials [splits][part_rows][tiles*64].
+constexpr int64_t kCounterBytes = 65536;
+constexpr int64_t kMaxSplitTiles = kCounterBytes / 4;
+
+// Skinny-GEMM split: 4 waves per work-group, 2 K-blocks in flight per wave;
+// K is split across work-groups only for few tiles and long K (each split
+// costs an agent-scope release fence per work-group).
 Split choose_split(int64_t tiles, int kb, int64_t ws_bytes, int64_t part_rows) {
-  int want = (int)((kTargetGroups + tiles - 1) / tiles);
-  const int max_by_k = kb / (kWaves * kMinBlocksPerWave);
-  if (want > max_by_k) want = max_by_k;
-  if (want < 1) want = 1;
-  // workspace: partials [splits][part_rows][tiles*64] floats + one ticket per tile
+  constexpr int kPerGroup = kWaves * kMinBlocksPerWave;
+  int want = 1;
+  if (tiles < 32 && kb >= 4 * kPerGroup) {
+    want = (int)((kTargetGroups + tiles - 1) / tiles);
+    if (want > kb / kPerGroup) want = kb / kPerGroup;
+  }
+  if (want < 1 || tiles > kMaxSplitTiles) want = 1;
   while (want > 1) {
-    const int64_t need = (int64_t)want * part_rows * tiles * kTile * 4 + tiles * 4;
+    const int64_t need = kCounterBytes + (int64_t)want * part_rows * tiles * kTile * 4;
     if (need <= ws_bytes) break;
     --want;
   }
@@ -135,8 +149,52 @@ Split choose_split(int64_t tiles, int kb, int64_t ws_bytes, int64_t part_rows) {
 int64_t split_ws_bytes(int64_t tiles, int kb, int64_t part_rows) {
   const Split s = choose_split(tiles, kb, INT64_MAX, part_rows);
   if (s.splits <= 1) return 0;
-  return (int64_t)s.splits * part_rows * tiles * kTile * 4 + tiles * 4;
+  return kCounterBytes + (int64_t)s.splits * part_rows * tiles * kTile * 4;
 }
+
+// GEMV launch shape: one work-group per (tile, split); its waves split the
+// split's K-blocks.  Each wave keeps up to `unroll` blocks in flight, so the
+// work-group is sized to cover the K range in about one round of loads; K is
+// split across work-groups only when there are few tiles and many blocks (a
+// split costs an agent-scope release fence per work-group).
+struct GemvCfg { int waves, splits, kbps; };
+
+GemvCfg gemv_config(int64_t tiles, int kb, int unroll, int64_t ws_bytes) {
+  // Measured on MI355X (graph-replayed launches, cold weights): 16 waves per
+  // work-group is fastest up to ~1000 tiles, 8 beyond; splitting K across
+  // work-groups pays only when there are at most 64 tiles and >= 32 blocks,
+  // up to 4 ways and about 256 work-groups.
+  (void)unroll;
+  int waves = tiles > 1024 ? 8 : 16;
+  int splits = 1;
+  if (tiles <= 64 && kb >= 32) {
+    splits = kb / 16;
+    if (splits > 4) splits = 4;
+    const int64_t by_groups = 256 / tiles;
+    if (splits > by_groups) splits = (int)(by_groups > 1 ? by_groups : 1);
+  }
+  // QLIN_TUNE_GEMV="waves,splits" overrides the choice (launch-shape sweeps)
+  if (const char* e = getenv("QLIN_TUNE_GEMV")) {
+    int w = 0, sp = 0;
+    if (sscanf(e, "%d,%d", &w, &sp) == 2 && (w == 4 || w == 8 || w == 16) && sp >= 1) {
+      waves = w;
+      splits = sp < kb ? sp : kb;
+    }
+  }
+  if (tiles > kMaxSplitTiles) splits = 1;
+  while (splits > 1 && kCounterBytes + (int64_t)splits * tiles * kTile * 4 > ws_bytes) --splits;
+  const int kbps = (kb + splits - 1) / splits;
+  return GemvCfg{waves, (kb + kbps - 1) / kbps, kbps};
+}
+
+int64_t gemv_ws_bytes(int64_t tiles, int kb, int unroll) {
+  const GemvCfg c = gemv_config(tiles, kb, unroll, INT64_MAX);
+  if (c.splits <= 1) return 0;
+  return kCounterBytes + (int64_t)c.splits * tiles * kTile * 4;
+}
+
+constexpr int kPackedUnroll = 4;   // K-blocks in flight per wave, packed GEMV
+constexpr int kFusedUnroll = 2;    // K-blocks in flight per wave, fused GEMV
 
 template <int B>
 void launch_quant(const uint16_t* w16, int64_t ld, int n, int k, int group, uint32_t* codes,
@@ -153,26 +211,42 @@ void launch_quant(const uint16_t* w16, int64_t ld, int n, int k, int group, uint
   }
 }
 
-template <int B>
-void launch_gemv_packed(const qlin_weight* w, const f16x2* x2, float* y, float* part,
-                        uint32_t* tick, Split sp, hipStream_t st) {
+template <int B, int W>
+void launch_gemv_packed_w(const qlin_weight* w, const f16x2* x2, float* y, float* part,
+                          uint32_t* tick, GemvCfg c, hipStream_t st) {
   const int kb = w->k / kBlock;
   const int G = (w->group == w->k) ? 1 : kb;
-  dim3 grid((unsigned)tiles_of(w->n), sp.splits);
-  hipLaunchKernelGGL((k_gemv_packed<B, kWaves>), grid, dim3(kWaves * 64), 0, st,
+  dim3 grid((unsigned)tiles_of(w->n), c.splits);
+  hipLaunchKernelGGL((k_gemv_packed<B, W, kPackedUnroll>), grid, dim3(W * 64), 0, st,
                      static_cast<const uint32_t*>(w->data), w->scale, w->zero, x2, y, part, tick,
-                     w->n, kb, G, sp.splits, sp.kbps);
+                     w->n, kb, G, c.splits, c.kbps);
+}
+
+template <int B>
+void launch_gemv_packed(const qlin_weight* w, const f16x2* x2, float* y, float* part,
+                        uint32_t* tick, GemvCfg c, hipStream_t st) {
+  if (c.waves == 16) launch_gemv_packed_w<B, 16>(w, x2, y, part, tick, c, st);
+  else if (c.waves == 8) launch_gemv_packed_w<B, 8>(w, x2, y, part, tick, c, st);
+  else launch_gemv_packed_w<B, 4>(w, x2, y, part, tick, c, st);
+}
+
+template <int B, int W>
+void launch_gemv_fused_w(const qlin_weight* w, const f16x2* x2, float* y, float* part,
+                         uint32_t* tick, GemvCfg c, hipStream_t st) {
+  const int kb = w->k / kBlock;
+  const int G = (w->bits == 16 || w->group != w->k) ? kb : 1;
+  dim3 grid((unsigned)tiles_of(w->n), c.splits);
+  hipLaunchKernelGGL((k_gemv_fused<B, W, kFusedUnroll>), grid, dim3(W * 64), 0, st,
+                     static_cast<const uint16_t*>(w->data), w->ld, w->scale, w->zero, x2, y, part,
+                     tick, w->n, kb, G, c.splits, c.kbps);
 }
 
 template <int B>
 void launch_gemv_fused(const qlin_weight* w, const f16x2* x2, float* y, float* part,
-                       uint32_t* tick, Split sp, hipStream_t st) {
-  const int kb = w->k / kBlock;
-  const int G = (w->bits == 16 || w->group != w->k) ? kb : 1;
-  dim3 grid((unsigned)tiles_of(w->n), sp.splits);
-  hipLaunchKernelGGL((k_gemv_fused<B, kWaves>), grid, dim3(kWaves * 64), 0, st,
-                     static_cast<const uint16_t*>(w->data), w->ld, w->scale, w->zero, x2, y, part,
-                     tick, w->n, kb, G, sp.splits, sp.kbps);
+                       uint32_t* tick, GemvCfg c, hipStream_t st) {
+  if (c.waves == 16) launch_gemv_fused_w<B, 16>(w, x2, y, part, tick, c, st);
+  else if (c.waves == 8) launch_gemv_fused_w<B, 8>(w, x2, y, part, tick, c, st);
+  else launch_gemv_fused_w<B, 4>(w, x2, y, part, tick, c, st);
 }
 
 template <int B>
@@ -181,7 +255,7 @@ void launch_gemm_skinny(const qlin_weight* w, const uint16_t* X, int64_t ldx, in
   const int kb = w->k / kBlock;
   const int G = (w->group == w->k) ? 1 : kb;
   dim3 grid((unsigned)tiles_of(w->n), sp.splits);
-  hipLaunchKernelGGL((k_gemm_skinny<B, kWaves>), grid, dim3(kWaves * 64), 0, st,
+  hipLaunchKernelGGL((k_gemm_skinny<B, kWaves, 2>), grid, dim3(kWaves * 64), 0, st,
                      static_cast<const uint32_t*>(w->data), w->scale, w->zero, X, ldx, m, Y, ldy,
                      part, tick, w->n, kb, G, sp.splits, sp.kbps);
 }
@@ -278,7 +352,8 @@ qlin_status qlin_quantize(const uint16_t* w16, int64_t ld_w, int32_t n, int32_t 
 
 int64_t qlin_gemv_workspace_bytes(const qlin_weight* w) {
   if (check_weight(w, true, true) != QLIN_OK) return 0;
-  return split_ws_bytes(tiles_of(w->n), w->k / kBlock, 1);
+  return gemv_ws_bytes(tiles_of(w->n), w->k / kBlock,
+                       w->format == QLIN_FMT_PACKED ? kPackedUnroll : kFusedUnroll);
 }
 
 int64_t qlin_gemm_workspace_bytes(const qlin_weight* w, int32_t m) {
@@ -309,11 +384,12 @@ qlin_status qlin_gemv(const qlin_weight* w, const uint16_t* x, float* y, void* w
   if (st != QLIN_OK) return st;
   const int64_t tiles = tiles_of(w->n);
   const int kb = w->k / kBlock;
-  const Split sp = choose_split(tiles, kb, workspace_bytes, 1);
-  float* part = static_cast<float*>(workspace);
-  uint32_t* tick = nullptr;
-  if (sp.splits > 1)
-    tick = reinterpret_cast<uint32_t*>(part + (int64_t)sp.splits * tiles * kTile);
+  const GemvCfg sp = gemv_config(tiles, kb, w->format == QLIN_FMT_PACKED ? kPackedUnroll
+                                                                         : kFusedUnroll,
+                                 workspace_bytes);
+  uint32_t* tick = static_cast<uint32_t*>(workspace);
+  float* part = sp.splits > 1 ? reinterpret_cast<float*>(static_cast<char*>(workspace) + kCounterBytes)
+                              : nullptr;
   const f16x2* x2 = reinterpret_cast<const f16x2*>(x);
   if (w->format == QLIN_FMT_PACKED) {
     switch (w->bits) {
@@ -361,10 +437,9 @@ qlin_status qlin_gemm(const qlin_weight* w, const uint16_t* X, int32_t m, int64_
   if (m <= kSkinnyMaxM) {
     const int64_t tiles = tiles_of(w->n);
     const Split sp = choose_split(tiles, w->k / kBlock, workspace_bytes, 16);
-    float* part = static_cast<float*>(workspace);
-    uint32_t* tick = nullptr;
-    if (sp.splits > 1)
-      tick = reinterpret_cast<uint32_t*>(part + (int64_t)sp.splits * 16 * tiles * kTile);
+    uint32_t* tick = static_cast<uint32_t*>(workspace);
+    float* part = sp.splits > 1
+        ? reinterpret_cast<float*>(static_cast<char*>(workspace) + kCounterBytes) : nullptr;
     switch (w->bits) {
       case 2: launch_gemm_skinny<2>(w, X, ld_x, m, Y, ld_y, part, tick, sp, stream); break;
       case 3: launch_gemm_skinny<3>(w, X, ld_x, m, Y, ld_y, part, tick, sp, stream); break;

@@ -129,11 +129,11 @@ qlin_status qlin_quantize(const uint16_t* w16, int64_t ld_w, int32_t n, int32_t 
 
 /*
  * Workspace needed by qlin_gemv / qlin_gemm for their split-K launches.  0 means
- * the launch needs none.  Layout: fp32 partial sums, then one uint32 arrival
- * counter per 64-row tile in the last 4*ceil(n/64) bytes of the size returned
- * here.  The counters must be zero before first use (e.g. zero-fill the whole
- * workspace once); every call leaves them zero again, the partials are scratch.
- * Calls that may run at the same time must not share a workspace.
+ * the launch needs none.  Layout: the first 65536 bytes hold one uint32 arrival
+ * counter per 64-row tile, the rest fp32 partial sums.  The counter region
+ * must be zero before first use (zero-fill the workspace once); every call
+ * leaves it zero again and the partials are scratch, so calls of different
+ * shapes may share one workspace as long as they do not run at the same time.
  */
 int64_t qlin_gemv_workspace_bytes(const qlin_weight* w);
 int64_t qlin_gemm_workspace_bytes(const qlin_weight* w, int32_t m);

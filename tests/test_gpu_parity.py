@@ -253,7 +253,7 @@ def test_gemm_group_k_and_strides():
 # ----------------------------------------------------- split-K, determinism
 @pytest.mark.parametrize("bits", [2, 3, 4, 8])
 def test_split_k_paths(bits):
-    n, k = 512, 8192
+    n, k = 192, 16384
     rng = np.random.default_rng(60 + bits)
     w16 = synth.master_weights(rng, n, k)
     x16 = synth.activations(rng, 8, k)
@@ -267,10 +267,9 @@ def test_split_k_paths(bits):
     y_one = host(qlin.gemv(qw, dev(x16[0]), ws=None))
     check_tol(y_split, x16[0], what, "split")
     check_tol(y_one, x16[0], what, "nosplit")
-    tiles = (n + 63) // 64
-    tickets = ws[need - 4 * tiles: need]
-    assert torch.count_nonzero(tickets).item() == 0, "split tickets must be re-armed to zero"
-    ws[: need - 4 * tiles].fill_(0x5A)                 # partials are scratch: garbage is fine
+    counters = ws[:65536]
+    assert torch.count_nonzero(counters).item() == 0, "arrival counters must be re-armed to zero"
+    ws[65536:].fill_(0x5A)                             # partials are scratch: garbage is fine
     y_again = host(qlin.gemv(qw, dev(x16[0]), ws=ws))
     assert np.array_equal(y_split, y_again)
     say(f"split-K skinny gemm bits={bits}")
@@ -278,6 +277,27 @@ def test_split_k_paths(bits):
     check_tol(Y, x16, what, "split gemm")
     Y2 = host(qlin.gemm(qw, dev(x16), ws=None))
     check_tol(Y2, x16, what, "nosplit gemm")
+
+
+def test_shared_workspace_across_shapes():
+    """One workspace reused by calls of different shapes and kinds."""
+    rng = np.random.default_rng(2)
+    cases = [(320, 896, 1), (512, 8192, 1), (128, 4864, 8), (896, 4864, 1), (64, 1024, 16)]
+    ws = torch.zeros(64 << 20, dtype=torch.uint8, device=DEV)
+    say("shared workspace")
+    for rep in range(2):
+        for (n, k, m) in cases:
+            w16 = synth.master_weights(rng, n, k)
+            x16 = synth.activations(rng, m, k)
+            qw, codes, s16, z = oracle_packed(w16, 4, 64)
+            what = oracle.dequantize(codes, s16, z, 64)
+            if m == 1:
+                y = host(qlin.gemv(qw, dev(x16[0]), ws=ws))
+                check_tol(y, x16[0], what, f"shared ws gemv {n}x{k}")
+            else:
+                Y = host(qlin.gemm(qw, dev(x16), ws=ws))
+                check_tol(Y, x16, what, f"shared ws gemm {n}x{k} m={m}")
+    assert torch.count_nonzero(ws[:65536]).item() == 0
 
 
 def test_deterministic():
