@@ -11,6 +11,7 @@ typedef f16 f16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef f16 f16x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));  // native vector: stays in VGPRs
 
 constexpr int kTile = 64;     // rows per layout tile: one row per lane of a wave
 constexpr int kBlock = 64;    // codes per K-block (and per group)

@@ -543,6 +543,7 @@ __global__ __launch_bounds__(256) void k_gemm_tiles(
   constexpr int HW = WPB / 2;               // words of a half block
   constexpr int RB = MB / 32;               // 32-row MFMA blocks of X
   constexpr int XCH = MB * 8 / 256;         // 16-byte X chunks per thread per block
+  static_assert(XCH <= 8, "X staging covers at most 256 rows");
   __shared__ __attribute__((aligned(16))) f16 xs[2][MB][kLdsRow];
   const int tid = threadIdx.x;
   const int lane = lane_id(), wave = wave_id();
@@ -561,15 +562,15 @@ __global__ __launch_bounds__(256) void k_gemm_tiles(
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[rb][cb][r] = 0.f;
 
-  // per-thread X chunk addresses (rows past m read row m0, then zeroed)
+  // Per-thread X chunk addresses.  Rows past m read row m0 instead: an X row
+  // only feeds its own output row, which is never stored.  Likewise a wave
+  // whose tile lies past n decodes tile 0 and stores nothing.
   const uint16_t* xsrc[XCH];
-  bool xok[XCH];
 #pragma unroll
   for (int i = 0; i < XCH; ++i) {
     const int ch = tid + 256 * i;
     const int row = ch >> 3, c8 = ch & 7;
-    xok[i] = m0 + row < m;
-    xsrc[i] = X + (int64_t)(xok[i] ? m0 + row : 0) * ldx + 8 * c8;
+    xsrc[i] = X + (int64_t)(m0 + row < m ? m0 + row : m0) * ldx + 8 * c8;
   }
   const uint32_t* wsrc[2];
   int64_t msrc[2];
@@ -580,7 +581,7 @@ __global__ __launch_bounds__(256) void k_gemm_tiles(
     msrc[cb] = (int64_t)tt * G * kTile + r;
   }
 
-  uint4 xv[2][XCH];
+  u32x4 xv[2][XCH];
   uint32_t wl[2][2][HW];
   float sc[2][2];
   int zc[2][2];
@@ -588,14 +589,14 @@ __global__ __launch_bounds__(256) void k_gemm_tiles(
 
   // Block data moves: issue (global -> registers, set p), land (registers ->
   // LDS buffer p and decoded B fragments of set p), mma (LDS buffer p and B
-  // fragments of set p -> accumulators).  All set / buffer indices are
-  // compile-time, so the scheduler may interleave one block's decode with the
-  // previous block's MFMAs.
-  auto issue = [&](int j, auto setc) {
+  // fragments of set p -> accumulators).  Set and buffer indices are
+  // compile-time and the bodies are branch-free, so one block's decode can be
+  // interleaved with the previous block's MFMAs.
+  auto issue = [&](int j, auto setc) __attribute__((always_inline)) {
     constexpr int P = decltype(setc)::value;
 #pragma unroll
     for (int i = 0; i < XCH; ++i)
-      xv[P][i] = *reinterpret_cast<const uint4*>(xsrc[i] + (int64_t)j * kBlock);
+      xv[P][i] = *reinterpret_cast<const u32x4*>(xsrc[i] + (int64_t)j * kBlock);
     const int g = (G == 1) ? 0 : j;
 #pragma unroll
     for (int cb = 0; cb < 2; ++cb) {
@@ -604,59 +605,77 @@ __global__ __launch_bounds__(256) void k_gemm_tiles(
       zc[P][cb] = zero[msrc[cb] + (int64_t)g * kTile];
     }
   };
-  auto land = [&](auto setc) {
+  auto land_x = [&](auto setc, int i) __attribute__((always_inline)) {
     constexpr int P = decltype(setc)::value;
-#pragma unroll
-    for (int i = 0; i < XCH; ++i) {
-      const int ch = tid + 256 * i;
-      const int row = ch >> 3, c8 = ch & 7;
-      const uint4 v = xok[i] ? xv[P][i] : make_uint4(0, 0, 0, 0);
-      *reinterpret_cast<uint4*>(&xs[P][row][8 * c8]) = v;
-    }
-#pragma unroll
-    for (int cb = 0; cb < 2; ++cb) {
-      const float s = tvalid ? sc[P][cb] : 0.f;
-      const Deq d = make_deq(s, zc[P][cb]);
-#pragma unroll
-      for (int s4 = 0; s4 < 4; ++s4) bfrag[P][cb][s4] = deq_half<BITS>(wl[P][cb], s4, d, magic);
-    }
+    const int ch = tid + 256 * i;
+    const int row = ch >> 3, c8 = ch & 7;
+    *reinterpret_cast<u32x4*>(&xs[P][row][8 * c8]) = xv[P][i];
   };
-  auto mma = [&](auto setc) {
+  // One K-slice of block P's MFMAs, then one slice of the next block's
+  // decode (set Q) and X store: independent work placed between MFMAs so the
+  // VALU and LDS work overlaps the 32-cycle matrix-core operations.
+  auto step = [&](auto setc, auto nextc, bool decode_next) __attribute__((always_inline)) {
     constexpr int P = decltype(setc)::value;
+    constexpr int Q = decltype(nextc)::value;
+    Deq dn[2];
+    if (decode_next) {
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb) dn[cb] = make_deq(sc[Q][cb], zc[Q][cb]);
+    }
+    // A fragments of slice s4+1 are read from LDS while slice s4's MFMAs run.
+    f16x8 a[2][RB];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+      a[0][rb] = *reinterpret_cast<const f16x8*>(&xs[P][32 * rb + c][32 * h]);
 #pragma unroll
     for (int s4 = 0; s4 < 4; ++s4) {
-      f16x8 a[RB];
+      if (s4 < 3) {
 #pragma unroll
-      for (int rb = 0; rb < RB; ++rb)
-        a[rb] = *reinterpret_cast<const f16x8*>(&xs[P][32 * rb + c][32 * h + 8 * s4]);
+        for (int rb = 0; rb < RB; ++rb)
+          a[(s4 + 1) & 1][rb] =
+              *reinterpret_cast<const f16x8*>(&xs[P][32 * rb + c][32 * h + 8 * (s4 + 1)]);
+      }
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
         for (int cb = 0; cb < 2; ++cb)
-          acc[rb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[rb], bfrag[P][cb][s4], acc[rb][cb],
-                                                               0, 0, 0);
+          acc[rb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[s4 & 1][rb], bfrag[P][cb][s4],
+                                                               acc[rb][cb], 0, 0, 0);
+      if (decode_next) {
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb) bfrag[Q][cb][s4] = deq_half<BITS>(wl[Q][cb], s4, dn[cb], magic);
+        if (s4 < XCH) land_x(nextc, s4);
+        if (s4 + 4 < XCH) land_x(nextc, s4 + 4);
+      }
     }
   };
   using S0 = std::integral_constant<int, 0>;
   using S1 = std::integral_constant<int, 1>;
 
-  // pipeline: block j computes while block j+1 is decoded and j+2 is loading
+  // pipeline: block j computes while block j+1 is decoded and j+2 is loading;
+  // prefetch indices are clamped to the last block (re-read, unused) so the
+  // loop bodies have no branches.
   issue(0, S0{});
-  if (kb > 1) issue(1, S1{});
-  land(S0{});
-  __syncthreads();
-  int j = 0;
-  for (; j + 1 < kb; j += 2) {
-    if (j + 2 < kb) issue(j + 2, S0{});
-    mma(S0{});
-    land(S1{});
-    __syncthreads();
-    if (j + 3 < kb) issue(j + 3, S1{});
-    mma(S1{});
-    if (j + 2 < kb) land(S0{});
-    __syncthreads();
+  issue(kb > 1 ? 1 : 0, S1{});
+#pragma unroll
+  for (int i = 0; i < XCH; ++i) land_x(S0{}, i);
+#pragma unroll
+  for (int cb = 0; cb < 2; ++cb) {
+    const Deq d = make_deq(sc[0][cb], zc[0][cb]);
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4) bfrag[0][cb][s4] = deq_half<BITS>(wl[0][cb], s4, d, magic);
   }
-  if (j < kb) mma(S0{});     // odd kb: the last block sits in set 0
+  __syncthreads();
+  for (int j = 0;; j += 2) {
+    step(S0{}, S1{}, true);           // block j; decode block j+1
+    issue(min(j + 2, kb - 1), S0{});
+    __syncthreads();
+    if (j + 1 >= kb) break;
+    step(S1{}, S0{}, true);           // block j+1; decode block j+2
+    issue(min(j + 3, kb - 1), S1{});
+    __syncthreads();
+    if (j + 2 >= kb) break;
+  }
 
   if (!tvalid) return;
   // rows m0 + 32rb + 8(r/4) + 4h + r%4 of columns t*64 + 32cb + c

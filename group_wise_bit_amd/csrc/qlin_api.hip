@@ -267,16 +267,22 @@ void launch_gemm_tiles(const qlin_weight* w, const uint16_t* X, int64_t ldx, int
   const int G = (w->group == w->k) ? 1 : kb;
   const int tiles = (int)tiles_of(w->n);
   const unsigned gx = (unsigned)((tiles + 3) / 4);
-  if (m <= 64) {
-    dim3 grid(gx, (m + 63) / 64);
-    hipLaunchKernelGGL((k_gemm_tiles<B, 64>), grid, dim3(256), 0, st,
-                       static_cast<const uint32_t*>(w->data), w->scale, w->zero, X, ldx, m, Y,
-                       ldy, w->n, kb, G, tiles);
+  // X-tile height: 128 rows amortize each decoded weight best; shorter tiles
+  // when the grid would otherwise leave most of the 256 CUs idle.
+  int mb = 128;
+  while (mb > 32 && (int64_t)gx * ((m + mb - 1) / mb) < 256) mb /= 2;
+  if (m <= 32) mb = 32;
+  else if (m <= 64 && mb > 64) mb = 64;
+  const uint32_t* codes = static_cast<const uint32_t*>(w->data);
+  if (mb == 32) {
+    hipLaunchKernelGGL((k_gemm_tiles<B, 32>), dim3(gx, (m + 31) / 32), dim3(256), 0, st,
+                       codes, w->scale, w->zero, X, ldx, m, Y, ldy, w->n, kb, G, tiles);
+  } else if (mb == 64) {
+    hipLaunchKernelGGL((k_gemm_tiles<B, 64>), dim3(gx, (m + 63) / 64), dim3(256), 0, st,
+                       codes, w->scale, w->zero, X, ldx, m, Y, ldy, w->n, kb, G, tiles);
   } else {
-    dim3 grid(gx, (m + 127) / 128);
-    hipLaunchKernelGGL((k_gemm_tiles<B, 128>), grid, dim3(256), 0, st,
-                       static_cast<const uint32_t*>(w->data), w->scale, w->zero, X, ldx, m, Y,
-                       ldy, w->n, kb, G, tiles);
+    hipLaunchKernelGGL((k_gemm_tiles<B, 128>), dim3(gx, (m + 127) / 128), dim3(256), 0, st,
+                       codes, w->scale, w->zero, X, ldx, m, Y, ldy, w->n, kb, G, tiles);
   }
 }
 

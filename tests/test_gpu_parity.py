@@ -234,6 +234,20 @@ def test_gemm_one_hot_fp16_exact(bits, m):
         assert np.array_equal(Y.astype(np.float64), fp16_rne(what[:, cols].T))
 
 
+@pytest.mark.parametrize("bits", [3, 4])
+@pytest.mark.parametrize("m,n,k", [(2048, 4096, 256), (1024, 4096, 128), (300, 256, 960)])
+def test_gemm_tile_heights(bits, m, n, k):
+    """Large grids select the 128- and 64-row X tiles, small ones 32 rows."""
+    say(f"gemm tile heights bits={bits} m={m} n={n} k={k}")
+    rng = np.random.default_rng(m + n + k + bits)
+    w16 = synth.master_weights(rng, n, k)
+    x16 = synth.activations(rng, m, k)
+    qw, codes, s16, z = oracle_packed(w16, bits, 64)
+    what = oracle.dequantize(codes, s16, z, 64)
+    Y = host(qlin.gemm(qw, dev(x16)))
+    check_tol(Y, x16, what, f"gemm {m}x{n}x{k}")
+
+
 def test_gemm_group_k_and_strides():
     rng = np.random.default_rng(4)
     n, k, m = 130, 512, 40
