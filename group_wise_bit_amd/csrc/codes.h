@@ -56,7 +56,7 @@ __device__ __forceinline__ uint32_t zconst(int z, int shift) {
 }
 
 template <int BITS>
-__device__ __forceinline__ float block_dot(const uint32_t* wd, const f16x2* __restrict__ xb, int z, uint32_t kMagic) {
+__device__ __forceinline__ float block_dot(const uint32_t* wd, const f16x2* xb, int z, uint32_t kMagic) {
   if constexpr (BITS == 4) {
     const f16x2 c1 = as_h2(zconst(z, 0)), c16 = as_h2(zconst(z, 4));
     float a0 = 0.f, a1 = 0.f, b0 = 0.f, b1 = 0.f;

@@ -202,24 +202,36 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemv_packed(
   const int j1 = min(kb, j0 + kbps);
   float yacc = 0.f;
   for (int jb = j0 + wave; jb < j1; jb += WAVES * U) {
+    // Loads of all U blocks first, without branches: a block past the range
+    // re-reads the last block of the range and gets scale 0.  The decode of
+    // block u then only waits for its own loads, while x of block u+1 is
+    // fetched (scalar loads) during block u's decode.
     uint32_t wd[U][WPB];
     float s[U];
-    int z[U];
+    int z[U], jj[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int j = jb + u * WAVES;
-      if (j < j1) {
-        load_block_words<BITS>(codes + (((int64_t)t * kb + j) * kTile + lane) * WPB, wd[u]);
-        const int64_t mi = ((int64_t)t * G + ((G == 1) ? 0 : j)) * kTile + lane;
-        s[u] = h2f(scale[mi]);
-        z[u] = zero[mi];
-      }
+      jj[u] = j < j1 ? j : j1 - 1;
+      load_block_words<BITS>(codes + (((int64_t)t * kb + jj[u]) * kTile + lane) * WPB, wd[u]);
+      const int64_t mi = ((int64_t)t * G + ((G == 1) ? 0 : jj[u])) * kTile + lane;
+      s[u] = j < j1 ? h2f(scale[mi]) : 0.f;
+      z[u] = zero[mi];
     }
+    f16x2 xc[32], xn[32];
+#pragma unroll
+    for (int i = 0; i < 32; ++i) xc[i] = x2[(int64_t)jj[0] * 32 + i];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int j = jb + u * WAVES;
-      if (j < j1)
-        yacc = __builtin_fmaf(s[u], block_dot<BITS>(wd[u], x2 + (int64_t)j * 32, z[u], magic), yacc);
+      if (u + 1 < U) {
+#pragma unroll
+        for (int i = 0; i < 32; ++i) xn[i] = x2[(int64_t)jj[u + 1] * 32 + i];
+      }
+      yacc = __builtin_fmaf(s[u], block_dot<BITS>(wd[u], xc, z[u], magic), yacc);
+      if (u + 1 < U) {
+#pragma unroll
+        for (int i = 0; i < 32; ++i) xc[i] = xn[i];
+      }
     }
   }
   red[wave][lane] = yacc;
@@ -261,76 +273,85 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemv_fused(
   const int j1 = min(kb, j0 + kbps);
   float yacc = 0.f;
   for (int jb = j0 + wave; jb < j1; jb += WAVES * U) {
-   uint4 wvu[U][8];
-   float su[U];
-   int zu[U];
+    // as in k_gemv_packed: branch-free loads of all U blocks, x of the next
+    // block fetched during the current block's work
+    uint4 wvu[U][8];
+    float su[U];
+    int zu[U], jj[U];
 #pragma unroll
-   for (int u = 0; u < U; ++u) {
-    const int j = jb + u * WAVES;
-    if (j < j1) {
+    for (int u = 0; u < U; ++u) {
+      const int j = jb + u * WAVES;
+      jj[u] = j < j1 ? j : j1 - 1;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) wvu[u][i] = wr[(int64_t)j * 8 + i];
+      for (int i = 0; i < 8; ++i) wvu[u][i] = wr[(int64_t)jj[u] * 8 + i];
       if constexpr (BITS != 16) {
-        const int64_t mi = ((int64_t)t * G + ((G == 1) ? 0 : j)) * kTile + lane;
-        su[u] = h2f(scale[mi]);
+        const int64_t mi = ((int64_t)t * G + ((G == 1) ? 0 : jj[u])) * kTile + lane;
+        su[u] = j < j1 ? h2f(scale[mi]) : 0.f;
         zu[u] = zero[mi];
+      } else {
+        su[u] = j < j1 ? 1.f : 0.f;
+        zu[u] = 0;
       }
     }
-   }
+    f16x2 xc[32], xn[32];
 #pragma unroll
-   for (int u = 0; u < U; ++u) {
-    const int j = jb + u * WAVES;
-    if (j >= j1) continue;
-    const uint4* wv = wvu[u];
-    const f16x2* xb = x2 + (int64_t)j * 32;
-    if constexpr (BITS == 16) {
-      float a = 0.f, b = 0.f;
+    for (int i = 0; i < 32; ++i) xc[i] = x2[(int64_t)jj[0] * 32 + i];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        a = __builtin_amdgcn_fdot2(as_h2(wv[i].x), xb[4 * i + 0], a, false);
-        b = __builtin_amdgcn_fdot2(as_h2(wv[i].y), xb[4 * i + 1], b, false);
-        a = __builtin_amdgcn_fdot2(as_h2(wv[i].z), xb[4 * i + 2], a, false);
-        b = __builtin_amdgcn_fdot2(as_h2(wv[i].w), xb[4 * i + 3], b, false);
+    for (int u = 0; u < U; ++u) {
+      if (u + 1 < U) {
+#pragma unroll
+        for (int i = 0; i < 32; ++i) xn[i] = x2[(int64_t)jj[u + 1] * 32 + i];
       }
-      yacc += a + b;
-    } else {
-      constexpr int qmax = (1 << BITS) - 1;
-      const float s = su[u];
-      const RtnParams p = rtn_params(s, zu[u], qmax);
+      const uint4* wv = wvu[u];
       float a = 0.f, b = 0.f;
+      if constexpr (BITS == 16) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const uint32_t u[4] = {wv[i].x, wv[i].y, wv[i].z, wv[i].w};
-        float wf[8], q[8];
-        bool tie = false;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const f16x2 h = as_h2(u[e]);
-          wf[2 * e] = (float)h.x;
-          wf[2 * e + 1] = (float)h.y;
+        for (int i = 0; i < 8; ++i) {
+          a = __builtin_amdgcn_fdot2(as_h2(wv[i].x), xc[4 * i + 0], a, false);
+          b = __builtin_amdgcn_fdot2(as_h2(wv[i].y), xc[4 * i + 1], b, false);
+          a = __builtin_amdgcn_fdot2(as_h2(wv[i].z), xc[4 * i + 2], a, false);
+          b = __builtin_amdgcn_fdot2(as_h2(wv[i].w), xc[4 * i + 3], b, false);
         }
+      } else {
+        constexpr int qmax = (1 << BITS) - 1;
+        const RtnParams p = rtn_params(su[u], zu[u], qmax);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          bool te;
-          q[e] = rtn_raw(wf[e], p, te);
-          tie |= te;
-        }
-        if (__builtin_amdgcn_ballot_w64(tie) != 0) {
+        for (int i = 0; i < 8; ++i) {
+          const uint32_t uw[4] = {wv[i].x, wv[i].y, wv[i].z, wv[i].w};
+          float wf[8], q[8];
+          bool tie = false;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) q[e] = rtn_fix(wf[e], q[e], p);
-        }
+          for (int e = 0; e < 4; ++e) {
+            const f16x2 h = as_h2(uw[e]);
+            wf[2 * e] = (float)h.x;
+            wf[2 * e + 1] = (float)h.y;
+          }
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const auto pk = __builtin_amdgcn_cvt_pkrtz(clampf(q[2 * e], p.lo, p.hi),
-                                                     clampf(q[2 * e + 1], p.lo, p.hi));
-          const f16x2 h = __builtin_bit_cast(f16x2, pk);
-          if (e & 1) b = __builtin_amdgcn_fdot2(h, xb[4 * i + e], b, false);
-          else a = __builtin_amdgcn_fdot2(h, xb[4 * i + e], a, false);
+          for (int e = 0; e < 8; ++e) {
+            bool te;
+            q[e] = rtn_raw(wf[e], p, te);
+            tie |= te;
+          }
+          if (__builtin_amdgcn_ballot_w64(tie) != 0) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) q[e] = rtn_fix(wf[e], q[e], p);
+          }
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const auto pk = __builtin_amdgcn_cvt_pkrtz(clampf(q[2 * e], p.lo, p.hi),
+                                                       clampf(q[2 * e + 1], p.lo, p.hi));
+            const f16x2 h = __builtin_bit_cast(f16x2, pk);
+            if (e & 1) b = __builtin_amdgcn_fdot2(h, xc[4 * i + e], b, false);
+            else a = __builtin_amdgcn_fdot2(h, xc[4 * i + e], a, false);
+          }
         }
       }
-      yacc = __builtin_fmaf(s, a + b, yacc);
+      yacc = __builtin_fmaf(su[u], a + b, yacc);
+      if (u + 1 < U) {
+#pragma unroll
+        for (int i = 0; i < 32; ++i) xc[i] = xn[i];
+      }
     }
-   }
   }
   red[wave][lane] = yacc;
   __syncthreads();

@@ -152,26 +152,34 @@ int64_t split_ws_bytes(int64_t tiles, int kb, int64_t part_rows) {
   return kCounterBytes + (int64_t)s.splits * part_rows * tiles * kTile * 4;
 }
 
+constexpr int kPackedUnroll = 4;   // at most 4 K-blocks in flight per wave, packed GEMV
+constexpr int kFusedUnroll = 1;    // one K-block in flight per wave, fused GEMV
+
 // GEMV launch shape: one work-group per (tile, split); its waves split the
 // split's K-blocks.  Each wave keeps up to `unroll` blocks in flight, so the
 // work-group is sized to cover the K range in about one round of loads; K is
 // split across work-groups only when there are few tiles and many blocks (a
 // split costs an agent-scope release fence per work-group).
-struct GemvCfg { int waves, splits, kbps; };
+struct GemvCfg { int waves, splits, kbps, unroll; };
 
 GemvCfg gemv_config(int64_t tiles, int kb, int unroll, int64_t ws_bytes) {
-  // Measured on MI355X (graph-replayed launches, cold weights): 16 waves per
-  // work-group is fastest up to ~1000 tiles, 8 beyond; splitting K across
-  // work-groups pays only when there are at most 64 tiles and >= 32 blocks,
-  // up to 4 ways and about 256 work-groups.
-  (void)unroll;
-  int waves = tiles > 1024 ? 8 : 16;
+  // Measured on MI355X (graph-replayed launches over rotating cold weights,
+  // 896..151936 x 896..12288, int4): the packed kernel is fastest with 16
+  // waves per work-group; splitting K across work-groups pays only with at
+  // most 64 tiles (4 ways up to 32 tiles, 2 or 4 up to 64).  The fused kernel
+  // is ALU-heavier: one block in flight per wave, and it splits more.
+  const bool fused = unroll == kFusedUnroll;
+  int waves = fused ? 8 : 16;
   int splits = 1;
-  if (tiles <= 64 && kb >= 32) {
-    splits = kb / 16;
-    if (splits > 4) splits = 4;
+  if (tiles <= 64 && kb >= 8) {
+    if (fused) {
+      splits = kb >= 64 ? 8 : 4;
+    } else if (kb >= 32) {
+      splits = tiles <= 32 ? 4 : (kb >= 128 ? 4 : 2);
+    }
     const int64_t by_groups = 256 / tiles;
     if (splits > by_groups) splits = (int)(by_groups > 1 ? by_groups : 1);
+    if (splits > kb) splits = kb;
   }
   // QLIN_TUNE_GEMV="waves,splits" overrides the choice (launch-shape sweeps)
   if (const char* e = getenv("QLIN_TUNE_GEMV")) {
@@ -184,7 +192,11 @@ GemvCfg gemv_config(int64_t tiles, int kb, int unroll, int64_t ws_bytes) {
   if (tiles > kMaxSplitTiles) splits = 1;
   while (splits > 1 && kCounterBytes + (int64_t)splits * tiles * kTile * 4 > ws_bytes) --splits;
   const int kbps = (kb + splits - 1) / splits;
-  return GemvCfg{waves, (kb + kbps - 1) / kbps, kbps};
+  // blocks kept in flight per wave: the wave's share of the split, up to `unroll`
+  const int per_wave = (kbps + waves - 1) / waves;
+  int u = 1;
+  while (u < unroll && u < per_wave) u *= 2;
+  return GemvCfg{waves, (kb + kbps - 1) / kbps, kbps, u};
 }
 
 int64_t gemv_ws_bytes(int64_t tiles, int kb, int unroll) {
@@ -193,8 +205,6 @@ int64_t gemv_ws_bytes(int64_t tiles, int kb, int unroll) {
   return kCounterBytes + (int64_t)c.splits * tiles * kTile * 4;
 }
 
-constexpr int kPackedUnroll = 4;   // K-blocks in flight per wave, packed GEMV
-constexpr int kFusedUnroll = 2;    // K-blocks in flight per wave, fused GEMV
 
 template <int B>
 void launch_quant(const uint16_t* w16, int64_t ld, int n, int k, int group, uint32_t* codes,
@@ -211,13 +221,13 @@ void launch_quant(const uint16_t* w16, int64_t ld, int n, int k, int group, uint
   }
 }
 
-template <int B, int W>
+template <int B, int W, int U>
 void launch_gemv_packed_w(const qlin_weight* w, const f16x2* x2, float* y, float* part,
                           uint32_t* tick, GemvCfg c, hipStream_t st) {
   const int kb = w->k / kBlock;
   const int G = (w->group == w->k) ? 1 : kb;
   dim3 grid((unsigned)tiles_of(w->n), c.splits);
-  hipLaunchKernelGGL((k_gemv_packed<B, W, kPackedUnroll>), grid, dim3(W * 64), 0, st,
+  hipLaunchKernelGGL((k_gemv_packed<B, W, U>), grid, dim3(W * 64), 0, st,
                      static_cast<const uint32_t*>(w->data), w->scale, w->zero, x2, y, part, tick,
                      w->n, kb, G, c.splits, c.kbps);
 }
@@ -225,28 +235,38 @@ void launch_gemv_packed_w(const qlin_weight* w, const f16x2* x2, float* y, float
 template <int B>
 void launch_gemv_packed(const qlin_weight* w, const f16x2* x2, float* y, float* part,
                         uint32_t* tick, GemvCfg c, hipStream_t st) {
-  if (c.waves == 16) launch_gemv_packed_w<B, 16>(w, x2, y, part, tick, c, st);
-  else if (c.waves == 8) launch_gemv_packed_w<B, 8>(w, x2, y, part, tick, c, st);
-  else launch_gemv_packed_w<B, 4>(w, x2, y, part, tick, c, st);
+  if (c.waves == 16) {
+    if (c.unroll == 1) launch_gemv_packed_w<B, 16, 1>(w, x2, y, part, tick, c, st);
+    else if (c.unroll == 2) launch_gemv_packed_w<B, 16, 2>(w, x2, y, part, tick, c, st);
+    else launch_gemv_packed_w<B, 16, 4>(w, x2, y, part, tick, c, st);
+  } else if (c.waves == 8) {
+    if (c.unroll == 1) launch_gemv_packed_w<B, 8, 1>(w, x2, y, part, tick, c, st);
+    else if (c.unroll == 2) launch_gemv_packed_w<B, 8, 2>(w, x2, y, part, tick, c, st);
+    else launch_gemv_packed_w<B, 8, 4>(w, x2, y, part, tick, c, st);
+  } else {
+    if (c.unroll == 1) launch_gemv_packed_w<B, 4, 1>(w, x2, y, part, tick, c, st);
+    else if (c.unroll == 2) launch_gemv_packed_w<B, 4, 2>(w, x2, y, part, tick, c, st);
+    else launch_gemv_packed_w<B, 4, 4>(w, x2, y, part, tick, c, st);
+  }
 }
 
-template <int B, int W>
+template <int B, int W, int U>
 void launch_gemv_fused_w(const qlin_weight* w, const f16x2* x2, float* y, float* part,
                          uint32_t* tick, GemvCfg c, hipStream_t st) {
   const int kb = w->k / kBlock;
   const int G = (w->bits == 16 || w->group != w->k) ? kb : 1;
   dim3 grid((unsigned)tiles_of(w->n), c.splits);
-  hipLaunchKernelGGL((k_gemv_fused<B, W, kFusedUnroll>), grid, dim3(W * 64), 0, st,
+  hipLaunchKernelGGL((k_gemv_fused<B, W, U>), grid, dim3(W * 64), 0, st,
                      static_cast<const uint16_t*>(w->data), w->ld, w->scale, w->zero, x2, y, part,
                      tick, w->n, kb, G, c.splits, c.kbps);
 }
 
+// The fused kernel needs ~150 VGPRs: at most 8 waves (512 threads) per work-group.
 template <int B>
 void launch_gemv_fused(const qlin_weight* w, const f16x2* x2, float* y, float* part,
                        uint32_t* tick, GemvCfg c, hipStream_t st) {
-  if (c.waves == 16) launch_gemv_fused_w<B, 16>(w, x2, y, part, tick, c, st);
-  else if (c.waves == 8) launch_gemv_fused_w<B, 8>(w, x2, y, part, tick, c, st);
-  else launch_gemv_fused_w<B, 4>(w, x2, y, part, tick, c, st);
+  if (c.waves >= 8) launch_gemv_fused_w<B, 8, 1>(w, x2, y, part, tick, c, st);
+  else launch_gemv_fused_w<B, 4, 1>(w, x2, y, part, tick, c, st);
 }
 
 template <int B>
