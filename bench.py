@@ -1,27 +1,38 @@
 """Benchmark of the qlin hot path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+                    [--sections decode,qwen3_8b,qwen3_06b]
 
-Workload: the linear layers of a Qwen2.5-0.5B decode step -- 24 layers of
-q 896->896, k/v 896->128, o 896->896, gate/up 896->4864, down 4864->896, plus
-the tied 151936x896 LM head (169 matrices) -- synthetic fp16 masters
-~N(0, 0.02), fp16 activations ~N(0, 1), int4 with groups of 64 along K.
+One step runs every stage of the path once.  Sections and stages (each
+bracketed by HIP events on the stream its kernels run on; medians over the K
+timed steps):
 
-One step runs every stage of the path once over those shapes, each stage
-bracketed by HIP events on the stream its kernels run on:
-  decode_gemv      169 packed int4 GEMVs (M = 1), replayed from one HIP graph
-  prefill_m128     168 GEMMs at M = 128 (layers only; fp16 MFMA, fp32 acc)
-  prefill_m2048    168 GEMMs at M = 2048
+decode (the metric's workload) -- the linear layers of a Qwen2.5-0.5B decode
+step: 24 layers of q 896->896, k/v 896->128, o 896->896, gate/up 896->4864,
+down 4864->896 and the tied 151936x896 LM head, 169 matrices, int4 g64,
+fp16 masters ~N(0, 0.02), activations ~N(0, 1):
+  decode_gemv      169 packed GEMVs (M = 1) replayed from one HIP graph; the
+                   packed weights rotate over 4 copies (1.08 GB, more than
+                   four times the 256 MB Infinity Cache) so they come from HBM
+  prefill_m128     168 GEMMs (layers) at M = 128, fp16 MFMA, fp32 accumulate
+  prefill_m2048    the same at M = 2048
   gemm_m8          169 GEMMs at M = 8
   fused_gemv       169 fused quantize-dequantize GEMVs from the fp16 masters
-  rtn_precompute   scale/zero precompute of all 169 masters (no codes)
-  quantize_pack    scale/zero + codes of all 169 masters
-The packed weights rotate over 4 copies (>1 GB, four times the 256 MB
-Infinity Cache) so the decode stage reads them from HBM, not from cache.
+  rtn_precompute   scale/zero of all 169 masters (a change of bit width)
+  quantize_pack    scale/zero and packed codes of all 169 masters
+qwen3_8b -- 36 layers of q 4096->4096, k/v 4096->1024, o 4096->4096,
+gate/up 4096->12288, down 12288->4096 (252 matrices, 3.8 GB at int4):
+  q8_decode_int4 / _int3 / _int2   252 packed GEMVs (graph)
+  q8_m8_int4 / _int3               252 GEMMs at M = 8
+  q8_m128_int4 / _int3             252 GEMMs at M = 128
+qwen3_06b -- the 196 fp16 masters of Qwen3-0.6B (28 layers of q 1024->2048,
+k/v 1024->1024, o 2048->1024, gate/up 1024->3072, down 3072->1024):
+  q06_fused_b{8,4,3,2}_{g64,row}   196 fused GEMVs after a lever move
+  q06_lever_b{8,4,3,2}_{g64,row}   scale/zero precompute of the 196 masters
+  q06_fp16_control                 196 plain fp16 GEMVs (bits = 16)
 
-`value` is the decode stage's weight-stream rate: algorithmic bytes (packed
-codes + fp16 scales + uint8 zeros + x + y) / decode-stage time.  The prefill
-GEMM rate is reported beside it, as the metric asks.
+`value` is decode_gemv's weight-stream rate: algorithmic bytes (packed codes,
+fp16 scales, uint8 zeros, x, y) / decode-stage time.
 """
 from __future__ import annotations
 
@@ -36,6 +47,7 @@ import numpy as np
 HBM_PEAK_GBS = 8000.0
 FP16_MFMA_PEAK_TFLOPS = 2500.0
 ROTATE = 4
+HERE = os.path.dirname(os.path.abspath(__file__))
 
 
 def parse():
@@ -44,8 +56,9 @@ def parse():
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--sections", default="decode,qwen3_8b,qwen3_06b")
     p.add_argument("--phases", default="all",
-                   help="comma list of stages to run (default: all)")
+                   help="comma list of stages to run (default: all of the chosen sections)")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                    help="only run a plain device-to-device copy of BYTES bytes five times "
                         "(reference for scaling HBM traffic counters), then exit")
@@ -62,44 +75,50 @@ def copy_calibration(nbytes):
     print(json.dumps({"copy_calibration_bytes": nbytes, "launches": 5}), flush=True)
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(f"bench.py: this build measures one GPU only; --gpus {args.gpus} is not supported "
-              "(the path would shard output rows across GPUs; see DESIGN.md)", file=sys.stderr)
-        sys.exit(2)
+def wbytes(n, k, bits, group):
+    """Algorithmic bytes of one packed weight: codes + fp16 scale + uint8 zero."""
+    g = k if group == "row" else 64
+    return n * k * bits // 8 + n * (k // g) * 3
 
-    if args.copy_calibration:
-        copy_calibration(args.copy_calibration)
-        return
 
-    import torch
-    import synth
-    from group_wise_bit_amd import qlin
+class Phase:
+    def __init__(self, name, run, unit, amount, launches, peak, bound, kernel):
+        self.name, self.run, self.unit, self.amount = name, run, unit, amount
+        self.launches, self.peak, self.bound, self.kernel = launches, peak, bound, kernel
+        self.ms = []
 
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    all_phases = ["decode_gemv", "prefill_m128", "prefill_m2048", "gemm_m8", "fused_gemv",
-                  "rtn_precompute", "quantize_pack"]
-    phases = all_phases if args.phases == "all" else [p for p in args.phases.split(",") if p]
 
+def capture(torch, qlin, call_lists, ws):
+    """One HIP graph per list of (weight, x, y) GEMV calls."""
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        for calls in call_lists:
+            for w, x, y in calls:
+                qlin.gemv(w, x, y, ws=ws)
+    stream.synchronize()
+    graphs = []
+    for calls in call_lists:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for w, x, y in calls:
+                qlin.gemv(w, x, y, ws=ws)
+        graphs.append(g)
+    torch.cuda.synchronize()
+    return graphs
+
+
+def build_decode(torch, qlin, synth, dev, ws, phases, state):
     shapes = synth.qwen25_decode_shapes()              # 169 (layer, name, N, K)
     layer_idx = [i for i, s in enumerate(shapes) if s[1] != "lm_head"]
     t0 = time.time()
-    masters = []
-    for (l, nm, n, k) in shapes:
-        w = synth.master_weights(synth.layer_rng(1, l, nm), n, k)
-        masters.append(torch.from_numpy(w).to(dev))
-    xs = []
-    for (l, nm, n, k) in shapes:
-        x = synth.activations(synth.act_rng(1, l, nm), 1, k)[0]
-        xs.append(torch.from_numpy(x).to(dev))
-    print(f"[bench] masters generated and uploaded in {time.time() - t0:.1f}s", file=sys.stderr,
-          flush=True)
-
-    # packed copies for the decode stage (rotated for a cold Infinity Cache)
+    masters = [torch.from_numpy(synth.master_weights(synth.layer_rng(1, l, nm), n, k)).to(dev)
+               for (l, nm, n, k) in shapes]
+    xs = [torch.from_numpy(synth.activations(synth.act_rng(1, l, nm), 1, k)[0]).to(dev)
+          for (l, nm, n, k) in shapes]
+    print(f"[bench] decode-step masters generated in {time.time() - t0:.1f}s",
+          file=sys.stderr, flush=True)
     packed = [[qlin.quantize(w, 4, 64) for w in masters] for _ in range(ROTATE)]
-    scratch = [qlin.quantize(w, 4, 64) for w in masters]        # target of quantize_pack
+    scratch = [qlin.quantize(w, 4, 64) for w in masters]
     meta = [qlin.quantize(w, 4, 64, codes=False) for w in masters]
     fused = [qlin.master_weight(w, 4, 64, m.scale, m.zero) for w, m in zip(masters, meta)]
     ys = [torch.empty(n, dtype=torch.float32, device=dev) for (_, _, n, _) in shapes]
@@ -108,41 +127,25 @@ def main():
     X = {m: torch.from_numpy(synth.activations(np.random.default_rng([7, m]), m, kmax)).to(dev)
          for m in (8, 128, 2048)}
     Y = {m: torch.empty(m * nmax, dtype=torch.float32, device=dev) for m in (8, 128, 2048)}
-    ws = torch.zeros(64 << 20, dtype=torch.uint8, device=dev)
-    torch.cuda.synchronize()
 
     def gemm(w, m):
         # X rows keep their pitch kmax; Y is packed [m, n]
         qlin.gemm(w, X[m][:, : w.k], Y[m][: m * w.n].view(m, w.n), ws=ws)
 
-    # one HIP graph per packed copy for the decode stage (169 launches each)
     graphs = []
     if "decode_gemv" in phases:
-        stream = torch.cuda.Stream()
-        with torch.cuda.stream(stream):
-            for r in range(ROTATE):                       # warm the library's device check
-                for w, x, y in zip(packed[r], xs, ys):
-                    qlin.gemv(w, x, y, ws=ws)
-        stream.synchronize()
-        for r in range(ROTATE):
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g, stream=stream):
-                for w, x, y in zip(packed[r], xs, ys):
-                    qlin.gemv(w, x, y, ws=ws)
-            graphs.append(g)
-        torch.cuda.synchronize()
+        graphs = capture(torch, qlin, [list(zip(packed[r], xs, ys)) for r in range(ROTATE)], ws)
 
-    def run_phase(name, step):
+    def run(name):
+        r = state["step"] % ROTATE
         if name == "decode_gemv":
-            graphs[step % ROTATE].replay()
-        elif name == "prefill_m128":
+            graphs[r].replay()
+        elif name in ("prefill_m128", "prefill_m2048"):
+            m = 128 if name == "prefill_m128" else 2048
             for i in layer_idx:
-                gemm(packed[step % ROTATE][i], 128)
-        elif name == "prefill_m2048":
-            for i in layer_idx:
-                gemm(packed[step % ROTATE][i], 2048)
+                gemm(packed[r][i], m)
         elif name == "gemm_m8":
-            for w in packed[step % ROTATE]:
+            for w in packed[r]:
                 gemm(w, 8)
         elif name == "fused_gemv":
             for w, x, y in zip(fused, xs, ys):
@@ -154,58 +157,201 @@ def main():
             for w, s in zip(masters, scratch):
                 qlin.quantize(w, 4, 64, out=s)
 
-    # algorithmic work per stage
-    def wbytes(n, k, bits=4, g=64):
-        return n * k * bits // 8 + n * (k // g) * 3
-    dec_bytes = sum(wbytes(n, k) + 2 * k + 4 * n for (_, _, n, k) in shapes)
+    dec_bytes = sum(wbytes(n, k, 4, 64) + 2 * k + 4 * n for (_, _, n, k) in shapes)
     master_bytes = sum(2 * n * k for (_, _, n, k) in shapes)
     meta_bytes = sum(n * (k // 64) * 3 for (_, _, n, k) in shapes)
     code_bytes = sum(n * k // 2 for (_, _, n, k) in shapes)
     fl = {m: sum(2 * m * shapes[i][2] * shapes[i][3] for i in layer_idx) for m in (128, 2048)}
-    fl8 = sum(2 * 8 * n * k for (_, _, n, k) in shapes)
-    work = {
-        "decode_gemv": ("GB/s", dec_bytes),
-        "prefill_m128": ("TFLOP/s", fl[128]),
-        "prefill_m2048": ("TFLOP/s", fl[2048]),
-        "gemm_m8": ("GB/s", sum(wbytes(n, k) + 16 * k + 32 * n for (_, _, n, k) in shapes)),
-        "fused_gemv": ("GB/s", master_bytes + meta_bytes + sum(2 * k + 4 * n for (_, _, n, k) in shapes)),
-        "rtn_precompute": ("GB/s", master_bytes + meta_bytes),
-        "quantize_pack": ("GB/s", master_bytes + meta_bytes + code_bytes),
-    }
+    out = [
+        Phase("decode_gemv", run, "GB/s", dec_bytes, 169, HBM_PEAK_GBS, "hbm", "k_gemv_packed<4>"),
+        Phase("prefill_m128", run, "TFLOP/s", fl[128], 168, FP16_MFMA_PEAK_TFLOPS, "mfma",
+              "k_gemm_tiles<4>"),
+        Phase("prefill_m2048", run, "TFLOP/s", fl[2048], 168, FP16_MFMA_PEAK_TFLOPS, "mfma",
+              "k_gemm_tiles<4>"),
+        Phase("gemm_m8", run, "GB/s",
+              sum(wbytes(n, k, 4, 64) + 16 * k + 32 * n for (_, _, n, k) in shapes), 169,
+              HBM_PEAK_GBS, "hbm", "k_gemm_skinny<4>"),
+        Phase("fused_gemv", run, "GB/s",
+              master_bytes + meta_bytes + sum(2 * k + 4 * n for (_, _, n, k) in shapes), 169,
+              HBM_PEAK_GBS, "hbm", "k_gemv_fused<4>"),
+        Phase("rtn_precompute", run, "GB/s", master_bytes + meta_bytes, 169, HBM_PEAK_GBS,
+              "hbm", "k_quantize_g64<4> (no codes)"),
+        Phase("quantize_pack", run, "GB/s", master_bytes + meta_bytes + code_bytes, 169,
+              HBM_PEAK_GBS, "hbm", "k_quantize_g64<4>"),
+    ]
+    return [p for p in out if p.name in phases], shapes
+
+
+def build_qwen3_8b(torch, qlin, synth, dev, ws, phases):
+    """Weights drawn with the device RNG (seeded) for speed: 6.9 G weights."""
+    shapes = synth.qwen3_8b_shapes()
+    g = torch.Generator(device=dev)
+    g.manual_seed(5)
+    t0 = time.time()
+    packed = {2: [], 3: [], 4: []}
+    xs, ys = [], []
+    for (l, nm, n, k) in shapes:
+        w16 = (torch.randn(n, k, generator=g, device=dev) * 0.02).half()
+        for b in packed:
+            packed[b].append(qlin.quantize(w16, b, 64))
+        xs.append(torch.randn(k, generator=g, device=dev).half())
+        ys.append(torch.empty(n, dtype=torch.float32, device=dev))
+        del w16
+    kmax = max(k for *_, k in shapes)
+    nmax = max(n for _, _, n, _ in shapes)
+    X = {m: torch.randn(m, kmax, generator=g, device=dev).half() for m in (8, 128)}
+    Y = {m: torch.empty(m * nmax, dtype=torch.float32, device=dev) for m in (8, 128)}
+    torch.cuda.synchronize()
+    print(f"[bench] Qwen3-8B shapes quantized in {time.time() - t0:.1f}s", file=sys.stderr,
+          flush=True)
+    graphs = {}
+    for b in (4, 3, 2):
+        if f"q8_decode_int{b}" in phases:
+            graphs[b] = capture(torch, qlin, [list(zip(packed[b], xs, ys))], ws)[0]
+
+    def run(name):
+        b = int(name[-1])
+        if "decode" in name:
+            graphs[b].replay()
+        else:
+            m = 8 if "_m8_" in name else 128
+            for w in packed[b]:
+                qlin.gemm(w, X[m][:, : w.k], Y[m][: m * w.n].view(m, w.n), ws=ws)
+
+    out = []
+    for b in (4, 3, 2):
+        out.append(Phase(f"q8_decode_int{b}", run, "GB/s",
+                         sum(wbytes(n, k, b, 64) + 2 * k + 4 * n for (_, _, n, k) in shapes),
+                         252, HBM_PEAK_GBS, "hbm", f"k_gemv_packed<{b}>"))
+    for b in (4, 3):
+        out.append(Phase(f"q8_m8_int{b}", run, "GB/s",
+                         sum(wbytes(n, k, b, 64) + 16 * k + 32 * n for (_, _, n, k) in shapes),
+                         252, HBM_PEAK_GBS, "hbm", f"k_gemm_skinny<{b}>"))
+        out.append(Phase(f"q8_m128_int{b}", run, "TFLOP/s",
+                         sum(2 * 128 * n * k for (_, _, n, k) in shapes), 252,
+                         FP16_MFMA_PEAK_TFLOPS, "mfma", f"k_gemm_tiles<{b}>"))
+    return [p for p in out if p.name in phases]
+
+
+def build_qwen3_06b(torch, qlin, synth, dev, ws, phases):
+    shapes = synth.qwen3_06b_shapes()
+    g = torch.Generator(device=dev)
+    g.manual_seed(6)
+    masters = [(torch.randn(n, k, generator=g, device=dev) * 0.02).half() for (_, _, n, k) in shapes]
+    xs = [torch.randn(k, generator=g, device=dev).half() for (_, _, n, k) in shapes]
+    ys = [torch.empty(n, dtype=torch.float32, device=dev) for (_, _, n, k) in shapes]
+    combos = [(b, gr) for b in (8, 4, 3, 2) for gr in ("g64", "row")]
+    meta = {c: [qlin.quantize(w, c[0], 64 if c[1] == "g64" else "K", codes=False) for w in masters]
+            for c in combos}
+    fused = {c: [qlin.master_weight(w, c[0], 64 if c[1] == "g64" else "K", m.scale, m.zero)
+                 for w, m in zip(masters, meta[c])] for c in combos}
+    control = [qlin.master_weight(w, 16, 64) for w in masters]
+    torch.cuda.synchronize()
+
+    def run(name):
+        if name == "q06_fp16_control":
+            for w, x, y in zip(control, xs, ys):
+                qlin.gemv(w, x, y, ws=ws)
+            return
+        parts = name.split("_")
+        c = (int(parts[2][1:]), parts[3])
+        if parts[1] == "lever":
+            for w, m in zip(masters, meta[c]):
+                qlin.quantize(w, c[0], 64 if c[1] == "g64" else "K", codes=False, out=m)
+        else:
+            for w, x, y in zip(fused[c], xs, ys):
+                qlin.gemv(w, x, y, ws=ws)
+
+    master_bytes = sum(2 * n * k for (_, _, n, k) in shapes)
+    act = sum(2 * k + 4 * n for (_, _, n, k) in shapes)
+    out = []
+    for (b, gr) in combos:
+        mb = sum(n * (k // (64 if gr == "g64" else k)) * 3 for (_, _, n, k) in shapes)
+        out.append(Phase(f"q06_fused_b{b}_{gr}", run, "GB/s", master_bytes + mb + act, 196,
+                         HBM_PEAK_GBS, "hbm", f"k_gemv_fused<{b}>"))
+        out.append(Phase(f"q06_lever_b{b}_{gr}", run, "GB/s", master_bytes + mb, 196,
+                         HBM_PEAK_GBS, "hbm",
+                         f"k_quantize_{'g64' if gr == 'g64' else 'row'}<{b}> (no codes)"))
+    out.append(Phase("q06_fp16_control", run, "GB/s", master_bytes + act, 196, HBM_PEAK_GBS,
+                     "hbm", "k_gemv_fused<16>"))
+    return [p for p in out if p.name in phases]
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the path would shard output rows across GPUs; see DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
+
+    import torch
+    import synth
+    from group_wise_bit_amd import qlin
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    sections = [s for s in args.sections.split(",") if s]
+    want = None if args.phases == "all" else set(p for p in args.phases.split(",") if p)
+
+    def chosen(names):
+        return set(names) if want is None else set(names) & want
+
+    ws = torch.zeros(64 << 20, dtype=torch.uint8, device=dev)
+    state = {"step": 0}
+    phases, decode_shapes = [], None
+    if "decode" in sections:
+        names = ["decode_gemv", "prefill_m128", "prefill_m2048", "gemm_m8", "fused_gemv",
+                 "rtn_precompute", "quantize_pack"]
+        ps, decode_shapes = build_decode(torch, qlin, synth, dev, ws, chosen(names), state)
+        phases += ps
+    if "qwen3_8b" in sections:
+        names = [f"q8_decode_int{b}" for b in (4, 3, 2)] + [
+            f"q8_m{m}_int{b}" for b in (4, 3) for m in (8, 128)]
+        phases += build_qwen3_8b(torch, qlin, synth, dev, ws, chosen(names))
+    if "qwen3_06b" in sections:
+        names = [f"q06_{k}_b{b}_{g}" for k in ("fused", "lever") for b in (8, 4, 3, 2)
+                 for g in ("g64", "row")] + ["q06_fp16_control"]
+        phases += build_qwen3_06b(torch, qlin, synth, dev, ws, chosen(names))
+    torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream()
-    ev = {p: [] for p in phases}
 
-    def step(i, record):
+    def step(record):
         for p in phases:
             if record:
                 a = torch.cuda.Event(enable_timing=True)
                 b = torch.cuda.Event(enable_timing=True)
                 a.record(stream)
-            run_phase(p, i)
+            p.run(p.name)
             if record:
                 b.record(stream)
-                ev[p].append((a, b))
+                p.ms.append((a, b))
+        state["step"] += 1
 
-    for i in range(args.warmup):
-        step(i, False)
+    for _ in range(args.warmup):
+        step(False)
     torch.cuda.synchronize()
     t_start = time.perf_counter()
-    for i in range(args.steps):
-        step(args.warmup + i, True)
+    for _ in range(args.steps):
+        step(True)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
+    print(f"[bench] {args.steps} timed steps in {wall:.2f}s", file=sys.stderr, flush=True)
 
-    res = {}
+    res, rooflines = {}, {}
     for p in phases:
-        ms = np.array([a.elapsed_time(b) for a, b in ev[p]])
-        unit, amount = work[p]
+        ms = np.array([a.elapsed_time(b) for a, b in p.ms])
         med = float(np.median(ms))
-        rate = amount / (med * 1e-3) / (1e9 if unit == "GB/s" else 1e12)
-        res[p] = {"ms_median": round(med, 4), "ms_p10": round(float(np.percentile(ms, 10)), 4),
-                  "ms_p90": round(float(np.percentile(ms, 90)), 4), unit: round(rate, 2),
-                  "launches": 169 if p in ("decode_gemv", "gemm_m8", "fused_gemv",
-                                            "rtn_precompute", "quantize_pack") else 168}
+        scale = 1e9 if p.unit == "GB/s" else 1e12
+        rate = p.amount / (med * 1e-3) / scale
+        res[p.name] = {"ms_median": round(med, 4), "ms_p10": round(float(np.percentile(ms, 10)), 4),
+                       "ms_p90": round(float(np.percentile(ms, 90)), 4), p.unit: round(rate, 2),
+                       "launches": p.launches}
+        rooflines[p.name] = {"bound": p.bound, "kernel": p.kernel, "achieved": round(rate, 2),
+                             "peak": p.peak, "unit": p.unit, "frac": round(rate / p.peak, 4)}
 
     out = {
         "metric": "GEMV weight GB/s (% HBM peak) + prefill GEMM TFLOP/s, int4 g64",
@@ -216,43 +362,46 @@ def main():
         "config": {"workload": "Qwen2.5-0.5B decode step linear layers, 169 GEMVs incl. "
                                "151936x896 LM head, int4 g64, M=1",
                    "global_batch": 1, "seq_len": 1, "parallelism": "single GPU",
-                   "hip_graph": True, "weight_copies_rotated": ROTATE},
-        "phases": res,
+                   "hip_graph": True, "weight_copies_rotated": ROTATE,
+                   "sections": sections},
     }
     if "decode_gemv" in res:
         gbs = res["decode_gemv"]["GB/s"]
+        dec = [p for p in phases if p.name == "decode_gemv"][0]
+        per_launch_us = res["decode_gemv"]["ms_median"] * 1e3 / 169
+        achieved = dec.amount / 169 / (per_launch_us * 1e-6) / 1e9
         out["value"] = gbs
         out["pct_hbm_peak"] = round(100 * gbs / HBM_PEAK_GBS, 2)
-        per_launch_us = res["decode_gemv"]["ms_median"] * 1e3 / 169
         out["roofline"] = {
             "bound": "hbm", "kernel": "k_gemv_packed<4> (169 launches per step)",
-            "achieved": round(dec_bytes / 169 / (per_launch_us * 1e-6) / 1e9, 2),
-            "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(dec_bytes / 169 / (per_launch_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
-            "traffic": measured_traffic(),
-            "algorithmic_bytes_per_launch": dec_bytes / 169,
+            "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
+            "algorithmic_bytes_per_launch": round(dec.amount / 169, 1),
             "avg_launch_us": round(per_launch_us, 3),
         }
+    tf = {}
     if "prefill_m2048" in res:
-        out["prefill_gemm_tflops"] = {"M=2048": res["prefill_m2048"]["TFLOP/s"]}
-        if "prefill_m128" in res:
-            out["prefill_gemm_tflops"]["M=128"] = res["prefill_m128"]["TFLOP/s"]
-        out["prefill_pct_fp16_mfma_peak"] = round(
-            100 * res["prefill_m2048"]["TFLOP/s"] / FP16_MFMA_PEAK_TFLOPS, 2)
-
-    if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(shapes)
+        tf["M=2048"] = res["prefill_m2048"]["TFLOP/s"]
+    if "prefill_m128" in res:
+        tf["M=128"] = res["prefill_m128"]["TFLOP/s"]
+    if tf:
+        out["prefill_gemm_tflops"] = tf
+        out["prefill_pct_fp16_mfma_peak"] = {k: round(100 * v / FP16_MFMA_PEAK_TFLOPS, 2)
+                                             for k, v in tf.items()}
+    out["phases"] = res
+    out["rooflines"] = rooflines
+    if not args.no_cpu_baseline and decode_shapes is not None:
+        out["cpu_baseline"] = cpu_baseline(decode_shapes)
     print(json.dumps(out), flush=True)
 
 
-TRAFFIC_SUMMARY = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
-                               "gemv_packed_int4_qwen25_decode_hbm_traffic.txt")
+TRAFFIC_SUMMARY = os.path.join(HERE, "profiles", "gemv_packed_int4_qwen25_decode_hbm_traffic.txt")
 
 
 def kernel_source_hash():
     import glob
     import hashlib
-    csrc = os.path.join(os.path.dirname(os.path.abspath(__file__)), "group_wise_bit_amd", "csrc")
+    csrc = os.path.join(HERE, "group_wise_bit_amd", "csrc")
     h = hashlib.sha256()
     for f in sorted(glob.glob(os.path.join(csrc, "*.h")) + glob.glob(os.path.join(csrc, "*.hip"))):
         with open(f, "rb") as fh:
