@@ -147,21 +147,62 @@ __global__ __launch_bounds__(WAVES * 64) void k_quantize_row(
 }
 
 // ---------------------------------------------------- split-K finishing --
-// Every work-group of tile t writes its 64 partial rows to part[split][...];
-// the last one to arrive (ticket) adds the partials in split order, so the
-// result does not depend on arrival order, and re-arms the ticket.
-// `cols` = values per row of the tile handled by one lane (1 for GEMV).
+// Every work-group of an output tile writes its partial sums to the
+// workspace; the last one to arrive (ticket) adds the partials in split order,
+// so the result does not depend on arrival order, and re-arms the ticket.
+//
+// Partials move between work-groups, which may sit on different XCDs with
+// separate L2 caches, as device-scope atomic stores and loads (relaxed, agent
+// scope: the store is written through to the device coherence point, the load
+// reads from it).  A writer waits until all its stores are acknowledged
+// (vmcnt = 0) before it takes its ticket, so the last work-group sees every
+// partial.  This replaces an agent-scope release/acquire fence pair, whose L2
+// write-back and invalidate cost ~0.2 us each and serialize per XCD when
+// hundreds of work-groups finish together.
+__device__ __forceinline__ void put_partial(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ float get_partial(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Wait for every store this wave issued to be acknowledged.  The signal
+// fences keep the compiler from moving the atomics across the wait.
+__device__ __forceinline__ void partials_written() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// One wave: true for the last of `splits` arrivals at tickets[t] (after
+// partials_written()); the winner re-arms the ticket.
 __device__ __forceinline__ bool split_ticket(uint32_t* __restrict__ tickets, int t, int splits) {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
   uint32_t prev = 0;
   if (lane_id() == 0)
     prev = __hip_atomic_fetch_add(&tickets[t], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   prev = __builtin_amdgcn_readfirstlane(prev);
   if (prev != (uint32_t)(splits - 1)) return false;
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   if (lane_id() == 0)
     __hip_atomic_store(&tickets[t], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   return true;
+}
+
+// Sum of one output's split partials p[0], p[stride], ... in split order; the
+// loads of up to 8 splits are in flight together (a load-add chain would pay
+// one memory round trip per split).
+__device__ __forceinline__ float sum_splits(const float* __restrict__ p, int64_t stride,
+                                            int splits) {
+  float acc = 0.f;
+  for (int b = 0; b < splits; b += 8) {
+    float v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = get_partial(p + (int64_t)min(b + i, splits - 1) * stride);
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      if (b + i < splits) acc += v[i];
+  }
+  return acc;
 }
 
 // -------------------------------------------------------- packed GEMV --
@@ -246,10 +287,10 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemv_packed(
     return;
   }
   const int64_t np = (int64_t)gridDim.x * kTile;
-  part[(int64_t)sp * np + row] = tot;
+  put_partial(part + (int64_t)sp * np + row, tot);
+  partials_written();
   if (!split_ticket(tickets, t, splits)) return;
-  float acc = 0.f;
-  for (int s2 = 0; s2 < splits; ++s2) acc += part[(int64_t)s2 * np + row];
+  const float acc = sum_splits(part + row, np, splits);
   if (row < n) y[row] = acc;
 }
 
@@ -364,10 +405,10 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemv_fused(
     return;
   }
   const int64_t np = (int64_t)gridDim.x * kTile;
-  part[(int64_t)sp * np + row] = tot;
+  put_partial(part + (int64_t)sp * np + row, tot);
+  partials_written();
   if (!split_ticket(tickets, t, splits)) return;
-  float acc = 0.f;
-  for (int s2 = 0; s2 < splits; ++s2) acc += part[(int64_t)s2 * np + row];
+  const float acc = sum_splits(part + row, np, splits);
   if (row < n) y[row] = acc;
 }
 
@@ -488,17 +529,26 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_skinny(
     for (int cg = 0; cg < 4; ++cg)
 #pragma unroll
       for (int r = 0; r < 4; ++r)
-        part[((int64_t)sp * 16 + 4 * q + r) * np + t * kTile + 16 * cg + c] = tot[cg][r];
+        put_partial(part + ((int64_t)sp * 16 + 4 * q + r) * np + t * kTile + 16 * cg + c,
+                    tot[cg][r]);
+    partials_written();
     if (!split_ticket(tickets, t, splits)) return;
 #pragma unroll
-    for (int cg = 0; cg < 4; ++cg)
+    for (int cg = 0; cg < 4; ++cg) tot[cg] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    // split order; the 16 loads of one split are in flight together
+    for (int s2 = 0; s2 < splits; ++s2) {
+      float v[4][4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        float s2sum = 0.f;
-        for (int s2 = 0; s2 < splits; ++s2)
-          s2sum += part[((int64_t)s2 * 16 + 4 * q + r) * np + t * kTile + 16 * cg + c];
-        tot[cg][r] = s2sum;
-      }
+      for (int cg = 0; cg < 4; ++cg)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          v[cg][r] = get_partial(part + ((int64_t)s2 * 16 + 4 * q + r) * np + t * kTile +
+                                 16 * cg + c);
+#pragma unroll
+      for (int cg = 0; cg < 4; ++cg)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) tot[cg][r] += v[cg][r];
+    }
   }
 #pragma unroll
   for (int cg = 0; cg < 4; ++cg)
@@ -559,7 +609,8 @@ template <int BITS, int MB>
 __global__ __launch_bounds__(256) void k_gemm_tiles(
     const uint32_t* __restrict__ codes, const uint16_t* __restrict__ scale,
     const uint8_t* __restrict__ zero, const uint16_t* __restrict__ X, int64_t ldx, int m,
-    float* __restrict__ Y, int64_t ldy, int n, int kb, int G, int tiles) {
+    float* __restrict__ Y, int64_t ldy, int n, int kb, int G, int tiles,
+    int splits, int kbps, float* __restrict__ part, uint32_t* __restrict__ tickets) {
   constexpr int WPB = 2 * BITS;
   constexpr int HW = WPB / 2;               // words of a half block
   constexpr int RB = MB / 32;               // 32-row MFMA blocks of X
@@ -574,6 +625,9 @@ __global__ __launch_bounds__(256) void k_gemm_tiles(
   const int tt = tvalid ? t : 0;
   const int m0 = blockIdx.y * MB;
   const uint32_t magic = vreg_const(kMagic);
+  // K-blocks [ja, ja + nk) of split blockIdx.z
+  const int ja = blockIdx.z * kbps;
+  const int nk = min(kb, ja + kbps) - ja;
 
   f32x16 acc[RB][2];
 #pragma unroll
@@ -613,8 +667,9 @@ __global__ __launch_bounds__(256) void k_gemm_tiles(
   // fragments of set p -> accumulators).  Set and buffer indices are
   // compile-time and the bodies are branch-free, so one block's decode can be
   // interleaved with the previous block's MFMAs.
-  auto issue = [&](int j, auto setc) __attribute__((always_inline)) {
+  auto issue = [&](int jr, auto setc) __attribute__((always_inline)) {
     constexpr int P = decltype(setc)::value;
+    const int j = ja + jr;
 #pragma unroll
     for (int i = 0; i < XCH; ++i)
       xv[P][i] = *reinterpret_cast<const u32x4*>(xsrc[i] + (int64_t)j * kBlock);
@@ -677,7 +732,7 @@ __global__ __launch_bounds__(256) void k_gemm_tiles(
   // prefetch indices are clamped to the last block (re-read, unused) so the
   // loop bodies have no branches.
   issue(0, S0{});
-  issue(kb > 1 ? 1 : 0, S1{});
+  issue(nk > 1 ? 1 : 0, S1{});
 #pragma unroll
   for (int i = 0; i < XCH; ++i) land_x(S0{}, i);
 #pragma unroll
@@ -689,13 +744,67 @@ __global__ __launch_bounds__(256) void k_gemm_tiles(
   __syncthreads();
   for (int j = 0;; j += 2) {
     step(S0{}, S1{}, true);           // block j; decode block j+1
-    issue(min(j + 2, kb - 1), S0{});
+    issue(min(j + 2, nk - 1), S0{});
     __syncthreads();
-    if (j + 1 >= kb) break;
+    if (j + 1 >= nk) break;
     step(S1{}, S0{}, true);           // block j+1; decode block j+2
-    issue(min(j + 3, kb - 1), S1{});
+    issue(min(j + 3, nk - 1), S1{});
     __syncthreads();
-    if (j + 2 >= kb) break;
+    if (j + 2 >= nk) break;
+  }
+
+  if (splits > 1) {
+    // The partial tile goes to the workspace in fragment order, [split][work-
+    // group][fragment quad][thread] x 16 bytes, so every store and load moves
+    // 4 KB of consecutive bytes per work-group; the last work-group of this
+    // output tile to arrive adds the splits in order 0, 1, ... .
+    constexpr int NQ = RB * 2 * 4;          // float4 quads per thread
+    const int64_t wg = (int64_t)blockIdx.y * gridDim.x + blockIdx.x;
+    const int64_t groups = (int64_t)gridDim.x * gridDim.y;
+    float* pw = part + ((blockIdx.z * groups + wg) * NQ * 256 + tid) * 4;
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            put_partial(pw + ((rb * 2 + cb) * 4 + q) * 1024 + e, acc[rb][cb][4 * q + e]);
+    partials_written();
+    __syncthreads();
+    __shared__ uint32_t s_last;
+    if (tid == 0) {
+      const uint32_t prev = __hip_atomic_fetch_add(&tickets[wg], 1u, __ATOMIC_RELAXED,
+                                                   __HIP_MEMORY_SCOPE_AGENT);
+      s_last = prev == (uint32_t)(splits - 1);
+      if (s_last) __hip_atomic_store(&tickets[wg], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __syncthreads();
+    if (!s_last) return;
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[rb][cb][r] = 0.f;
+    const float* pr = part + (wg * NQ * 256 + tid) * 4;
+    for (int s2 = 0; s2 < splits; ++s2) {
+      f32x4 v[NQ];
+#pragma unroll
+      for (int i = 0; i < NQ; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          v[i][e] = get_partial(pr + ((int64_t)s2 * groups * NQ + i) * 1024 + e);
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[rb][cb][4 * q + e] += v[(rb * 2 + cb) * 4 + q][e];
+    }
   }
 
   if (!tvalid) return;

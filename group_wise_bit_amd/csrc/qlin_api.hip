@@ -157,29 +157,37 @@ constexpr int kFusedUnroll = 1;    // one K-block in flight per wave, fused GEMV
 
 // GEMV launch shape: one work-group per (tile, split); its waves split the
 // split's K-blocks.  Each wave keeps up to `unroll` blocks in flight, so the
-// work-group is sized to cover the K range in about one round of loads; K is
-// split across work-groups only when there are few tiles and many blocks (a
-// split costs an agent-scope release fence per work-group).
+// work-group is sized to cover the K range in about one round of loads.
 struct GemvCfg { int waves, splits, kbps, unroll; };
 
 GemvCfg gemv_config(int64_t tiles, int kb, int unroll, int64_t ws_bytes) {
   // Measured on MI355X (graph-replayed launches over rotating cold weights,
-  // 896..151936 x 896..12288, int4): the packed kernel is fastest with 16
-  // waves per work-group; splitting K across work-groups pays only with at
-  // most 64 tiles (4 ways up to 32 tiles, 2 or 4 up to 64).  The fused kernel
-  // is ALU-heavier: one block in flight per wave, and it splits more.
+  // 896..151936 x 896..12288, int4 and fp16 masters): without a split, a
+  // launch of T tiles runs on only T compute units, so shapes with up to 256
+  // tiles split K across work-groups.  The packed kernel keeps 16 waves per
+  // work-group and splits to ~16 K-blocks per split (8 with fewer than 32
+  // tiles); from 64 tiles up, 8 waves and 8-block splits.  The fused kernel
+  // is ALU-heavier: 8 waves, 4 or 8 splits, and 4 x 4 from 128 tiles up.
   const bool fused = unroll == kFusedUnroll;
   int waves = fused ? 8 : 16;
   int splits = 1;
-  if (tiles <= 64 && kb >= 8) {
+  if (tiles <= 256) {
     if (fused) {
-      splits = kb >= 64 ? 8 : 4;
-    } else if (kb >= 32) {
-      splits = tiles <= 32 ? 4 : (kb >= 128 ? 4 : 2);
+      if (tiles > 128) {
+        waves = 4;
+        splits = 4;
+      } else {
+        splits = kb >= 64 ? 8 : 4;
+      }
+    } else if (tiles <= 64) {
+      splits = (tiles < 32 && kb >= 64) ? kb / 8 : kb / 16;
+    } else {
+      waves = 8;
+      splits = kb / 8;
     }
-    const int64_t by_groups = 256 / tiles;
-    if (splits > by_groups) splits = (int)(by_groups > 1 ? by_groups : 1);
+    if (splits > 16) splits = 16;
     if (splits > kb) splits = kb;
+    if (splits < 1) splits = 1;
   }
   // QLIN_TUNE_GEMV="waves,splits" overrides the choice (launch-shape sweeps)
   if (const char* e = getenv("QLIN_TUNE_GEMV")) {
@@ -280,30 +288,69 @@ void launch_gemm_skinny(const qlin_weight* w, const uint16_t* X, int64_t ldx, in
                      part, tick, w->n, kb, G, sp.splits, sp.kbps);
 }
 
-template <int B>
-void launch_gemm_tiles(const qlin_weight* w, const uint16_t* X, int64_t ldx, int m, float* Y,
-                       int64_t ldy, hipStream_t st) {
+// Tiled-GEMM launch shape: work-group tile = MB rows of X x 256 rows of W
+// (four 64-row tiles).  Measured on MI355X (graph-replayed launches over
+// rotating cold weights, Qwen-shaped N x K, M = 32..2048, int4): a tall X tile
+// pays only when the grid is large (M = 2048); up to M = 256 the 32-row tile
+// is fastest (four waves per SIMD hide the load latency that one 128-row wave
+// cannot), and K is split up to 4 ways when there are fewer than 160
+// work-groups, keeping at least 10 K-blocks per split.
+struct TilesCfg { int mb, gx, gy, splits, kbps; };
+
+TilesCfg tiles_config(int64_t tiles, int kb, int m, int64_t ws_bytes) {
+  TilesCfg c;
+  c.gx = (int)((tiles + 3) / 4);
+  int want = 1;
+  if (m <= 256) {
+    c.mb = 32;
+    const int64_t groups = (int64_t)c.gx * ((m + 31) / 32);
+    want = (int)(320 / groups);
+    if (want > 4) want = 4;
+    if (want > kb / 10) want = kb / 10;
+  } else {
+    c.mb = 128;
+    while (c.mb > 32 && (int64_t)c.gx * ((m + c.mb - 1) / c.mb) < 256) c.mb /= 2;
+  }
+  // QLIN_TUNE_GEMM="mb,splits" overrides the choice (launch-shape sweeps)
+  if (const char* e = getenv("QLIN_TUNE_GEMM")) {
+    int mb = 0, sp = 0;
+    if (sscanf(e, "%d,%d", &mb, &sp) == 2 && (mb == 32 || mb == 64 || mb == 128) && sp >= 1) {
+      c.mb = mb;
+      want = sp < kb ? sp : kb;
+    }
+  }
+  if (want < 1) want = 1;
+  c.gy = (m + c.mb - 1) / c.mb;
+  if ((int64_t)c.gx * c.gy > kMaxSplitTiles) want = 1;
+  while (want > 1 && kCounterBytes + (int64_t)want * c.gy * c.mb * c.gx * 256 * 4 > ws_bytes)
+    --want;
+  c.kbps = (kb + want - 1) / want;
+  c.splits = (kb + c.kbps - 1) / c.kbps;
+  return c;
+}
+
+int64_t tiles_ws_bytes(int64_t tiles, int kb, int m) {
+  const TilesCfg c = tiles_config(tiles, kb, m, INT64_MAX);
+  if (c.splits <= 1) return 0;
+  return kCounterBytes + (int64_t)c.splits * c.gy * c.mb * c.gx * 256 * 4;
+}
+
+template <int B, int MB>
+void launch_tiles_mb(const qlin_weight* w, const uint16_t* X, int64_t ldx, int m, float* Y,
+                     int64_t ldy, TilesCfg c, float* part, uint32_t* tick, hipStream_t st) {
   const int kb = w->k / kBlock;
   const int G = (w->group == w->k) ? 1 : kb;
-  const int tiles = (int)tiles_of(w->n);
-  const unsigned gx = (unsigned)((tiles + 3) / 4);
-  // X-tile height: 128 rows amortize each decoded weight best; shorter tiles
-  // when the grid would otherwise leave most of the 256 CUs idle.
-  int mb = 128;
-  while (mb > 32 && (int64_t)gx * ((m + mb - 1) / mb) < 256) mb /= 2;
-  if (m <= 32) mb = 32;
-  else if (m <= 64 && mb > 64) mb = 64;
-  const uint32_t* codes = static_cast<const uint32_t*>(w->data);
-  if (mb == 32) {
-    hipLaunchKernelGGL((k_gemm_tiles<B, 32>), dim3(gx, (m + 31) / 32), dim3(256), 0, st,
-                       codes, w->scale, w->zero, X, ldx, m, Y, ldy, w->n, kb, G, tiles);
-  } else if (mb == 64) {
-    hipLaunchKernelGGL((k_gemm_tiles<B, 64>), dim3(gx, (m + 63) / 64), dim3(256), 0, st,
-                       codes, w->scale, w->zero, X, ldx, m, Y, ldy, w->n, kb, G, tiles);
-  } else {
-    hipLaunchKernelGGL((k_gemm_tiles<B, 128>), dim3(gx, (m + 127) / 128), dim3(256), 0, st,
-                       codes, w->scale, w->zero, X, ldx, m, Y, ldy, w->n, kb, G, tiles);
-  }
+  hipLaunchKernelGGL((k_gemm_tiles<B, MB>), dim3(c.gx, c.gy, c.splits), dim3(256), 0, st,
+                     static_cast<const uint32_t*>(w->data), w->scale, w->zero, X, ldx, m, Y, ldy,
+                     w->n, kb, G, (int)tiles_of(w->n), c.splits, c.kbps, part, tick);
+}
+
+template <int B>
+void launch_gemm_tiles(const qlin_weight* w, const uint16_t* X, int64_t ldx, int m, float* Y,
+                       int64_t ldy, TilesCfg c, float* part, uint32_t* tick, hipStream_t st) {
+  if (c.mb == 32) launch_tiles_mb<B, 32>(w, X, ldx, m, Y, ldy, c, part, tick, st);
+  else if (c.mb == 64) launch_tiles_mb<B, 64>(w, X, ldx, m, Y, ldy, c, part, tick, st);
+  else launch_tiles_mb<B, 128>(w, X, ldx, m, Y, ldy, c, part, tick, st);
 }
 
 constexpr int kSkinnyMaxM = 16;
@@ -384,7 +431,7 @@ int64_t qlin_gemv_workspace_bytes(const qlin_weight* w) {
 
 int64_t qlin_gemm_workspace_bytes(const qlin_weight* w, int32_t m) {
   if (check_weight(w, false, false) != QLIN_OK || m < 1 || m > kMaxM) return 0;
-  if (m > kSkinnyMaxM) return 0;
+  if (m > kSkinnyMaxM) return tiles_ws_bytes(tiles_of(w->n), w->k / kBlock, m);
   return split_ws_bytes(tiles_of(w->n), w->k / kBlock, 16);
 }
 
@@ -473,11 +520,15 @@ qlin_status qlin_gemm(const qlin_weight* w, const uint16_t* X, int32_t m, int64_
       default: launch_gemm_skinny<8>(w, X, ld_x, m, Y, ld_y, part, tick, sp, stream); break;
     }
   } else {
+    const TilesCfg c = tiles_config(tiles_of(w->n), w->k / kBlock, m, workspace_bytes);
+    uint32_t* tick = static_cast<uint32_t*>(workspace);
+    float* part = c.splits > 1
+        ? reinterpret_cast<float*>(static_cast<char*>(workspace) + kCounterBytes) : nullptr;
     switch (w->bits) {
-      case 2: launch_gemm_tiles<2>(w, X, ld_x, m, Y, ld_y, stream); break;
-      case 3: launch_gemm_tiles<3>(w, X, ld_x, m, Y, ld_y, stream); break;
-      case 4: launch_gemm_tiles<4>(w, X, ld_x, m, Y, ld_y, stream); break;
-      default: launch_gemm_tiles<8>(w, X, ld_x, m, Y, ld_y, stream); break;
+      case 2: launch_gemm_tiles<2>(w, X, ld_x, m, Y, ld_y, c, part, tick, stream); break;
+      case 3: launch_gemm_tiles<3>(w, X, ld_x, m, Y, ld_y, c, part, tick, stream); break;
+      case 4: launch_gemm_tiles<4>(w, X, ld_x, m, Y, ld_y, c, part, tick, stream); break;
+      default: launch_gemm_tiles<8>(w, X, ld_x, m, Y, ld_y, c, part, tick, stream); break;
     }
   }
   return hip_status(hipGetLastError());

@@ -293,6 +293,33 @@ def test_split_k_paths(bits):
     check_tol(Y2, x16, what, "nosplit gemm")
 
 
+@pytest.mark.parametrize("bits", [2, 3, 4, 8])
+@pytest.mark.parametrize("m,n,k", [(128, 896, 4864), (100, 192, 4096), (256, 1024, 2048),
+                                   (40, 300, 1600)])
+def test_gemm_tiles_split_k(bits, m, n, k):
+    """Tiled GEMM with K split across work-groups (uneven last split, tiles past
+    n in the last work-group) equals the unsplit launch to tolerance, re-arms
+    its counters, and ignores whatever the partial region held before."""
+    rng = np.random.default_rng([61, bits, m, n, k])
+    w16 = synth.master_weights(rng, n, k)
+    X = synth.activations(rng, m, k)
+    qw, codes, s16, z = oracle_packed(w16, bits, 64)
+    what = oracle.dequantize(codes, s16, z, 64)
+    need = qlin.library().qlin_gemm_workspace_bytes(qw.c_struct(), m)
+    assert need > 65536, "this shape is expected to split K"
+    say(f"tiled split-K gemm bits={bits} m={m} n={n} k={k} ws={need}")
+    ws = torch.zeros(need, dtype=torch.uint8, device=DEV)
+    Xd = dev(X)
+    Y = host(qlin.gemm(qw, Xd, ws=ws))
+    check_tol(Y, X, what, "split")
+    assert torch.count_nonzero(ws[:65536]).item() == 0, "arrival counters must be re-armed"
+    ws[65536:].fill_(0x5A)
+    Y2 = host(qlin.gemm(qw, Xd, ws=ws))
+    assert np.array_equal(Y, Y2)
+    Y1 = host(qlin.gemm(qw, Xd, ws=None))
+    check_tol(Y1, X, what, "nosplit")
+
+
 def test_shared_workspace_across_shapes():
     """One workspace reused by calls of different shapes and kinds."""
     rng = np.random.default_rng(2)
