@@ -128,12 +128,15 @@ qlin_status qlin_quantize(const uint16_t* w16, int64_t ld_w, int32_t n, int32_t 
                           uint16_t* scale, uint8_t* zero, hipStream_t stream);
 
 /*
- * Workspace needed by qlin_gemv / qlin_gemm for their split-K launches.  0 means
- * the launch needs none.  Layout: the first 65536 bytes hold one uint32 arrival
- * counter per 64-row tile, the rest fp32 partial sums.  The counter region
- * must be zero before first use (zero-fill the workspace once); every call
- * leaves it zero again and the partials are scratch, so calls of different
- * shapes may share one workspace as long as they do not run at the same time.
+ * Workspace needed by qlin_gemv / qlin_gemm for their split-K launches, at the
+ * launch shape the library picks for this weight and m.  0 means the launch
+ * needs none.  Layout: the first 65536 bytes hold uint32 arrival counters (one
+ * per output tile of the launch: 64 rows of W for GEMV and m <= 16, 256 rows
+ * of W x up to 128 rows of X for larger m), the rest fp32 partial sums.  The
+ * counter region must be zero before first use (zero-fill the workspace
+ * once); every call leaves it zero again and the partials are scratch, so
+ * calls of different shapes may share one workspace as long as they do not
+ * run at the same time.
  */
 int64_t qlin_gemv_workspace_bytes(const qlin_weight* w);
 int64_t qlin_gemm_workspace_bytes(const qlin_weight* w, int32_t m);
