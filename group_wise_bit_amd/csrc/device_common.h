@@ -79,4 +79,13 @@ __device__ __forceinline__ float clampf(float v, float lo, float hi) {
   return __builtin_amdgcn_fmed3f(v, lo, hi);
 }
 
+
+// Work-group barrier that orders LDS accesses only: unlike __syncthreads it
+// does not wait for the wave's global loads still in flight.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 }  // namespace qlin

@@ -206,9 +206,7 @@ __device__ __forceinline__ float sum_splits(const float* __restrict__ p, int64_t
 }
 
 // -------------------------------------------------------- packed GEMV --
-// grid = (tiles, splits), block = WAVES waves.  Wave w of split s takes the
-// K-blocks j0+w, j0+w+WAVES, ... of [j0, j1) (the waves of a work-group read
-// consecutive 128*bits-byte runs); lane = row of the tile.  A wave issues the
+// One work-group per (tile, split); lane = row of the tile.  A wave issues the
 // loads of up to U blocks before decoding any, so a short K range costs one
 // memory round trip.  x is read with wave-uniform addresses (scalar loads,
 // shared by all rows of the tile).
@@ -228,36 +226,35 @@ __device__ __forceinline__ void load_block_words(const uint32_t* __restrict__ bl
   }
 }
 
-template <int BITS, int WAVES, int U>
-__global__ __launch_bounds__(WAVES * 64) void k_gemv_packed(
-    const uint32_t* __restrict__ codes, const uint16_t* __restrict__ scale,
-    const uint8_t* __restrict__ zero, const f16x2* __restrict__ x2, float* __restrict__ y,
-    float* __restrict__ part, uint32_t* __restrict__ tickets,
-    int n, int kb, int G, int splits, int kbps) {
+// One wave's share of a tile's dot products, for NM matrices that share x
+// (NM = 2: gate and up): K-blocks jfirst, jfirst + jstep, ... below j1, U at a
+// time.  The loads of all U blocks of every matrix are issued first, without
+// branches: a block past the range re-reads the last block of the range and
+// gets scale 0.  The decode of block u then only waits for its own loads,
+// while x of block u+1 is fetched (scalar loads) during block u's decode.
+// codes_t / scale_t / zero_t point at the tile's first block / entry.
+template <int BITS, int U, int NM>
+__device__ __forceinline__ void tile_dot(const uint32_t* const (&codes_t)[NM],
+                                         const uint16_t* const (&scale_t)[NM],
+                                         const uint8_t* const (&zero_t)[NM],
+                                         const f16x2* __restrict__ x2, int G, int jfirst, int j1,
+                                         int jstep, int lane, uint32_t magic, float (&acc)[NM]) {
   constexpr int WPB = 2 * BITS;
-  __shared__ float red[WAVES][64];
-  const uint32_t magic = vreg_const(kMagic);
-  const int lane = lane_id(), wave = wave_id();
-  const int t = blockIdx.x, sp = blockIdx.y;
-  const int j0 = sp * kbps;
-  const int j1 = min(kb, j0 + kbps);
-  float yacc = 0.f;
-  for (int jb = j0 + wave; jb < j1; jb += WAVES * U) {
-    // Loads of all U blocks first, without branches: a block past the range
-    // re-reads the last block of the range and gets scale 0.  The decode of
-    // block u then only waits for its own loads, while x of block u+1 is
-    // fetched (scalar loads) during block u's decode.
-    uint32_t wd[U][WPB];
-    float s[U];
-    int z[U], jj[U];
+  for (int jb = jfirst; jb < j1; jb += jstep * U) {
+    uint32_t wd[U][NM][WPB];
+    float s[U][NM];
+    int z[U][NM], jj[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int j = jb + u * WAVES;
+      const int j = jb + u * jstep;
       jj[u] = j < j1 ? j : j1 - 1;
-      load_block_words<BITS>(codes + (((int64_t)t * kb + jj[u]) * kTile + lane) * WPB, wd[u]);
-      const int64_t mi = ((int64_t)t * G + ((G == 1) ? 0 : jj[u])) * kTile + lane;
-      s[u] = j < j1 ? h2f(scale[mi]) : 0.f;
-      z[u] = zero[mi];
+      const int64_t mi = (int64_t)((G == 1) ? 0 : jj[u]) * kTile + lane;
+#pragma unroll
+      for (int m = 0; m < NM; ++m) {
+        load_block_words<BITS>(codes_t[m] + ((int64_t)jj[u] * kTile + lane) * WPB, wd[u][m]);
+        s[u][m] = j < j1 ? h2f(scale_t[m][mi]) : 0.f;
+        z[u][m] = zero_t[m][mi];
+      }
     }
     f16x2 xc[32], xn[32];
 #pragma unroll
@@ -268,30 +265,119 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemv_packed(
 #pragma unroll
         for (int i = 0; i < 32; ++i) xn[i] = x2[(int64_t)jj[u + 1] * 32 + i];
       }
-      yacc = __builtin_fmaf(s[u], block_dot<BITS>(wd[u], xc, z[u], magic), yacc);
+#pragma unroll
+      for (int m = 0; m < NM; ++m)
+        acc[m] = __builtin_fmaf(s[u][m], block_dot<BITS>(wd[u][m], xc, z[u][m], magic), acc[m]);
       if (u + 1 < U) {
 #pragma unroll
         for (int i = 0; i < 32; ++i) xc[i] = xn[i];
       }
     }
   }
-  red[wave][lane] = yacc;
-  __syncthreads();
-  if (wave != 0) return;
-  float tot = red[0][lane];
+}
+
+// Up to kMaxMats packed matrices that share K (and x), launched together.
+// Their tiles are numbered consecutively: matrix i owns launch tiles
+// [tile_end[i-1], tile_end[i]).  With SWIGLU, matrices 0 (gate) and 1 (up)
+// have the same n and launch tile t covers tile t of both.
+constexpr int kMaxMats = 4;
+struct GemvSet {
+  const uint32_t* codes[kMaxMats];
+  const uint16_t* scale[kMaxMats];
+  const uint8_t* zero[kMaxMats];
+  float* y[kMaxMats];
+  int n[kMaxMats];
+  int tile_end[kMaxMats];
+  int count;
+};
+
+__device__ __forceinline__ float silu(float g) { return g / (1.f + __expf(-g)); }
+
+// grid = (launch tiles, splits), block = WAVES waves; lane = row of the tile.
+// Plain: the WAVES waves of split s take the K-blocks j0+w, j0+w+WAVES, ... of
+// [j0, j1) (consecutive 128*bits-byte runs); y = the tile's dot products.
+// SWIGLU: waves [0, WAVES/2) do the gate tile, the others the up tile, and
+// the output is h = silu(gate . x) * (up . x), in fp32 (y[0]) and/or fp16
+// (h16, nearest even), either may be null.
+// grid = (launch tiles, splits), block = WAVES waves; lane = row of the tile.
+// The WAVES waves of split s take the K-blocks j0+w, j0+w+WAVES, ... of
+// [j0, j1) (consecutive 128*bits-byte runs).  Plain: y = the tile's dot
+// products.  SWIGLU: every wave does its blocks of the gate and the up tile
+// (one x for both), and the output is h = silu(gate . x) * (up . x), in fp32
+// (y[0]) and/or fp16 (h16, nearest even); either may be null.
+template <int BITS, int WAVES, int U, bool SWIGLU>
+__global__ __launch_bounds__(WAVES * 64) void k_gemv_packed(
+    const GemvSet set, const f16x2* __restrict__ x2, float* __restrict__ part,
+    uint32_t* __restrict__ tickets, int kb, int G, int splits, int kbps,
+    uint16_t* __restrict__ h16) {
+  constexpr int WPB = 2 * BITS;
+  constexpr int NM = SWIGLU ? 2 : 1;                  // matrices per tile
+  __shared__ float red[NM][WAVES][64];
+  const uint32_t magic = vreg_const(kMagic);
+  const int lane = lane_id(), wave = wave_id();
+  const int sp = blockIdx.y;
+  // this work-group's matrix (uniform selects, no indexing of the argument)
+  const uint32_t* codes = set.codes[0];
+  const uint16_t* scale = set.scale[0];
+  const uint8_t* zero = set.zero[0];
+  float* y = set.y[0];
+  int n = set.n[0], tb = 0;
+  if constexpr (!SWIGLU) {
 #pragma unroll
-  for (int w = 1; w < WAVES; ++w) tot += red[w][lane];
-  const int row = t * kTile + lane;
-  if (splits == 1) {
-    if (row < n) y[row] = tot;
-    return;
+    for (int i = 1; i < kMaxMats; ++i)
+      if (i < set.count && (int)blockIdx.x >= set.tile_end[i - 1]) {
+        codes = set.codes[i]; scale = set.scale[i]; zero = set.zero[i];
+        y = set.y[i]; n = set.n[i]; tb = set.tile_end[i - 1];
+      }
   }
-  const int64_t np = (int64_t)gridDim.x * kTile;
-  put_partial(part + (int64_t)sp * np + row, tot);
-  partials_written();
-  if (!split_ticket(tickets, t, splits)) return;
-  const float acc = sum_splits(part + row, np, splits);
-  if (row < n) y[row] = acc;
+  const int t = blockIdx.x - tb;
+  const int64_t ct = (int64_t)t * kb * kTile * WPB, mt = (int64_t)t * G * kTile;
+  const uint32_t* codes_t[NM];
+  const uint16_t* scale_t[NM];
+  const uint8_t* zero_t[NM];
+  codes_t[0] = codes + ct; scale_t[0] = scale + mt; zero_t[0] = zero + mt;
+  if constexpr (SWIGLU) {
+    codes_t[NM - 1] = set.codes[1] + ct;
+    scale_t[NM - 1] = set.scale[1] + mt;
+    zero_t[NM - 1] = set.zero[1] + mt;
+  }
+  const int j0 = sp * kbps;
+  const int j1 = min(kb, j0 + kbps);
+  float acc[NM];
+#pragma unroll
+  for (int m = 0; m < NM; ++m) acc[m] = 0.f;
+  tile_dot<BITS, U, NM>(codes_t, scale_t, zero_t, x2, G, j0 + wave, j1, WAVES, lane, magic, acc);
+#pragma unroll
+  for (int m = 0; m < NM; ++m) red[m][wave][lane] = acc[m];
+  lds_barrier();
+  if (wave != 0) return;
+  float tot[NM];
+#pragma unroll
+  for (int m = 0; m < NM; ++m) {
+    tot[m] = red[m][0][lane];
+#pragma unroll
+    for (int w = 1; w < WAVES; ++w) tot[m] += red[m][w][lane];
+  }
+  if (splits > 1) {
+    // part[split][matrix][launch row]
+    const int64_t np = (int64_t)gridDim.x * kTile;
+    const int64_t grow = (int64_t)blockIdx.x * kTile + lane;
+#pragma unroll
+    for (int m = 0; m < NM; ++m) put_partial(part + ((int64_t)sp * NM + m) * np + grow, tot[m]);
+    partials_written();
+    if (!split_ticket(tickets, blockIdx.x, splits)) return;
+#pragma unroll
+    for (int m = 0; m < NM; ++m) tot[m] = sum_splits(part + m * np + grow, NM * np, splits);
+  }
+  const int row = t * kTile + lane;
+  if (row >= n) return;
+  if constexpr (SWIGLU) {
+    const float h = silu(tot[0]) * tot[NM - 1];
+    if (y != nullptr) y[row] = h;
+    if (h16 != nullptr) h16[row] = __builtin_bit_cast(uint16_t, (f16)h);
+  } else {
+    y[row] = tot[0];
+  }
 }
 
 // ------------------------------------------------------ fused RTN GEMV --

@@ -164,9 +164,10 @@ GemvCfg gemv_config(int64_t tiles, int kb, int unroll, int64_t ws_bytes) {
   // Measured on MI355X (graph-replayed launches over rotating cold weights,
   // 896..151936 x 896..12288, int4 and fp16 masters): without a split, a
   // launch of T tiles runs on only T compute units, so shapes with up to 256
-  // tiles split K across work-groups.  The packed kernel keeps 16 waves per
-  // work-group and splits to ~16 K-blocks per split (8 with fewer than 32
-  // tiles); from 64 tiles up, 8 waves and 8-block splits.  The fused kernel
+  // tiles split K across work-groups (a split costs ~2 us of partial-sum
+  // round trips, so only long K pays).  The packed kernel keeps 16 waves per
+  // work-group and splits to ~16 K-blocks per split (12 with fewer than 32
+  // tiles); above 128 tiles, 8 waves and 8-block splits.  The fused kernel
   // is ALU-heavier: 8 waves, 4 or 8 splits, and 4 x 4 from 128 tiles up.
   const bool fused = unroll == kFusedUnroll;
   int waves = fused ? 8 : 16;
@@ -179,8 +180,8 @@ GemvCfg gemv_config(int64_t tiles, int kb, int unroll, int64_t ws_bytes) {
       } else {
         splits = kb >= 64 ? 8 : 4;
       }
-    } else if (tiles <= 64) {
-      splits = (tiles < 32 && kb >= 64) ? kb / 8 : kb / 16;
+    } else if (tiles <= 128) {
+      splits = (tiles < 32 && kb >= 64) ? kb / 12 : kb / 16;
     } else {
       waves = 8;
       splits = kb / 8;
@@ -229,33 +230,101 @@ void launch_quant(const uint16_t* w16, int64_t ld, int n, int k, int group, uint
   }
 }
 
-template <int B, int W, int U>
-void launch_gemv_packed_w(const qlin_weight* w, const f16x2* x2, float* y, float* part,
-                          uint32_t* tick, GemvCfg c, hipStream_t st) {
-  const int kb = w->k / kBlock;
-  const int G = (w->group == w->k) ? 1 : kb;
-  dim3 grid((unsigned)tiles_of(w->n), c.splits);
-  hipLaunchKernelGGL((k_gemv_packed<B, W, U>), grid, dim3(W * 64), 0, st,
-                     static_cast<const uint32_t*>(w->data), w->scale, w->zero, x2, y, part, tick,
-                     w->n, kb, G, c.splits, c.kbps);
+// Packed GEMV launch over a set of matrices (shared K, bits, group).
+struct PackedLaunch {
+  GemvSet set;
+  int tiles;          // launch tiles (grid.x)
+  int kb, G;
+  bool swiglu;
+  uint16_t* h16;
+};
+
+template <int B, int W, int U, bool SW>
+void launch_gemv_packed_w(const PackedLaunch& L, const f16x2* x2, float* part, uint32_t* tick,
+                          GemvCfg c, hipStream_t st) {
+  hipLaunchKernelGGL((k_gemv_packed<B, W, U, SW>), dim3(L.tiles, c.splits), dim3(W * 64), 0, st,
+                     L.set, x2, part, tick, L.kb, L.G, c.splits, c.kbps, L.h16);
+}
+
+template <int B, bool SW>
+void launch_gemv_packed_s(const PackedLaunch& L, const f16x2* x2, float* part, uint32_t* tick,
+                          GemvCfg c, hipStream_t st) {
+  if (c.waves == 16) {
+    if (c.unroll == 1) launch_gemv_packed_w<B, 16, 1, SW>(L, x2, part, tick, c, st);
+    else if (c.unroll == 2) launch_gemv_packed_w<B, 16, 2, SW>(L, x2, part, tick, c, st);
+    else launch_gemv_packed_w<B, 16, (SW ? 2 : 4), SW>(L, x2, part, tick, c, st);
+  } else if (c.waves == 8) {
+    if (c.unroll == 1) launch_gemv_packed_w<B, 8, 1, SW>(L, x2, part, tick, c, st);
+    else if (c.unroll == 2) launch_gemv_packed_w<B, 8, 2, SW>(L, x2, part, tick, c, st);
+    else launch_gemv_packed_w<B, 8, (SW ? 2 : 4), SW>(L, x2, part, tick, c, st);
+  } else {
+    if (c.unroll == 1) launch_gemv_packed_w<B, 4, 1, SW>(L, x2, part, tick, c, st);
+    else if (c.unroll == 2) launch_gemv_packed_w<B, 4, 2, SW>(L, x2, part, tick, c, st);
+    else launch_gemv_packed_w<B, 4, (SW ? 2 : 4), SW>(L, x2, part, tick, c, st);
+  }
 }
 
 template <int B>
-void launch_gemv_packed(const qlin_weight* w, const f16x2* x2, float* y, float* part,
-                        uint32_t* tick, GemvCfg c, hipStream_t st) {
-  if (c.waves == 16) {
-    if (c.unroll == 1) launch_gemv_packed_w<B, 16, 1>(w, x2, y, part, tick, c, st);
-    else if (c.unroll == 2) launch_gemv_packed_w<B, 16, 2>(w, x2, y, part, tick, c, st);
-    else launch_gemv_packed_w<B, 16, 4>(w, x2, y, part, tick, c, st);
-  } else if (c.waves == 8) {
-    if (c.unroll == 1) launch_gemv_packed_w<B, 8, 1>(w, x2, y, part, tick, c, st);
-    else if (c.unroll == 2) launch_gemv_packed_w<B, 8, 2>(w, x2, y, part, tick, c, st);
-    else launch_gemv_packed_w<B, 8, 4>(w, x2, y, part, tick, c, st);
-  } else {
-    if (c.unroll == 1) launch_gemv_packed_w<B, 4, 1>(w, x2, y, part, tick, c, st);
-    else if (c.unroll == 2) launch_gemv_packed_w<B, 4, 2>(w, x2, y, part, tick, c, st);
-    else launch_gemv_packed_w<B, 4, 4>(w, x2, y, part, tick, c, st);
+void launch_gemv_packed(const PackedLaunch& L, const f16x2* x2, float* part, uint32_t* tick,
+                        GemvCfg c, hipStream_t st) {
+  if (L.swiglu) launch_gemv_packed_s<B, true>(L, x2, part, tick, c, st);
+  else launch_gemv_packed_s<B, false>(L, x2, part, tick, c, st);
+}
+
+// Launch shape of a gate/up pair: every wave reads its blocks of both
+// matrices, so the pair takes the split of a single-matrix launch of the same
+// tiles; up to 2 blocks of each in flight per wave.
+GemvCfg swiglu_config(int64_t tiles, int kb, int64_t ws_bytes) {
+  GemvCfg c = gemv_config(tiles, kb, 2, INT64_MAX);
+  int splits = c.splits;
+  if (tiles > kMaxSplitTiles) splits = 1;
+  while (splits > 1 && kCounterBytes + 2 * (int64_t)splits * tiles * kTile * 4 > ws_bytes)
+    --splits;
+  const int kbps = (kb + splits - 1) / splits;
+  const int per_wave = (kbps + c.waves - 1) / c.waves;
+  return GemvCfg{c.waves, (kb + kbps - 1) / kbps, kbps, per_wave >= 2 ? 2 : 1};
+}
+
+int64_t swiglu_ws_bytes(int64_t tiles, int kb) {
+  const GemvCfg c = swiglu_config(tiles, kb, INT64_MAX);
+  if (c.splits <= 1) return 0;
+  return kCounterBytes + 2 * (int64_t)c.splits * tiles * kTile * 4;
+}
+
+PackedLaunch packed_launch(const qlin_weight* const* w, float* const* y, int count) {
+  PackedLaunch L{};
+  int64_t tiles = 0;
+  for (int i = 0; i < count; ++i) {
+    L.set.codes[i] = static_cast<const uint32_t*>(w[i]->data);
+    L.set.scale[i] = w[i]->scale;
+    L.set.zero[i] = w[i]->zero;
+    L.set.y[i] = y[i];
+    L.set.n[i] = w[i]->n;
+    tiles += tiles_of(w[i]->n);
+    L.set.tile_end[i] = (int)tiles;
   }
+  L.set.count = count;
+  L.tiles = (int)tiles;
+  L.kb = w[0]->k / kBlock;
+  L.G = (w[0]->group == w[0]->k) ? 1 : L.kb;
+  L.swiglu = false;
+  L.h16 = nullptr;
+  return L;
+}
+
+qlin_status run_packed(const PackedLaunch& L, int bits, const uint16_t* x, void* workspace,
+                       GemvCfg c, hipStream_t stream) {
+  uint32_t* tick = static_cast<uint32_t*>(workspace);
+  float* part = c.splits > 1
+      ? reinterpret_cast<float*>(static_cast<char*>(workspace) + kCounterBytes) : nullptr;
+  const f16x2* x2 = reinterpret_cast<const f16x2*>(x);
+  switch (bits) {
+    case 2: launch_gemv_packed<2>(L, x2, part, tick, c, stream); break;
+    case 3: launch_gemv_packed<3>(L, x2, part, tick, c, stream); break;
+    case 4: launch_gemv_packed<4>(L, x2, part, tick, c, stream); break;
+    default: launch_gemv_packed<8>(L, x2, part, tick, c, stream); break;
+  }
+  return hip_status(hipGetLastError());
 }
 
 template <int B, int W, int U>
@@ -356,6 +425,48 @@ void launch_gemm_tiles(const qlin_weight* w, const uint16_t* X, int64_t ldx, int
 constexpr int kSkinnyMaxM = 16;
 
 }  // namespace
+
+// Checks shared by the multi-matrix GEMV entry points: `count` packed
+// weights with one k, bits and group; outputs of `out_bytes[i]` bytes that
+// overlap nothing else.
+qlin_status check_set(const qlin_weight* w, int count, const uint16_t* x, void* const* outs,
+                      const int64_t* out_bytes, int nouts, void* workspace,
+                      int64_t workspace_bytes) {
+  for (int i = 0; i < count; ++i) {
+    const qlin_status st = check_weight(&w[i], false, false);
+    if (st != QLIN_OK) return st;
+    if (w[i].k != w[0].k) return QLIN_ERR_SHAPE;
+    if (w[i].bits != w[0].bits || w[i].group != w[0].group) return QLIN_ERR_FORMAT;
+  }
+  if (x == nullptr) return QLIN_ERR_NULL;
+  if (!aligned16(x)) return QLIN_ERR_ALIGN;
+  if (workspace_bytes < 0) return QLIN_ERR_WORKSPACE;
+  if (workspace != nullptr && !aligned16(workspace)) return QLIN_ERR_ALIGN;
+  const Range rx = range_of(x, (int64_t)w[0].k * 2);
+  const Range rw = range_of(workspace, workspace != nullptr ? workspace_bytes : 0);
+  for (int i = 0; i < nouts; ++i) {
+    if (outs[i] == nullptr) continue;
+    if (!aligned16(outs[i])) return QLIN_ERR_ALIGN;
+    const Range r = range_of(outs[i], out_bytes[i]);
+    if (overlaps(r, rx) || overlaps(r, rw)) return QLIN_ERR_ALIAS;
+    for (int j = 0; j < count; ++j)
+      if (output_overlaps_weight(&w[j], r)) return QLIN_ERR_ALIAS;
+    for (int j = 0; j < i; ++j)
+      if (outs[j] != nullptr && overlaps(r, range_of(outs[j], out_bytes[j]))) return QLIN_ERR_ALIAS;
+  }
+  if (rw.hi > rw.lo) {
+    if (overlaps(rw, rx)) return QLIN_ERR_ALIAS;
+    for (int j = 0; j < count; ++j)
+      if (output_overlaps_weight(&w[j], rw)) return QLIN_ERR_ALIAS;
+  }
+  return QLIN_OK;
+}
+
+int64_t set_tiles(const qlin_weight* w, int count) {
+  int64_t t = 0;
+  for (int i = 0; i < count; ++i) t += tiles_of(w[i].n);
+  return t;
+}
 
 extern "C" {
 
@@ -460,18 +571,13 @@ qlin_status qlin_gemv(const qlin_weight* w, const uint16_t* x, float* y, void* w
   const GemvCfg sp = gemv_config(tiles, kb, w->format == QLIN_FMT_PACKED ? kPackedUnroll
                                                                          : kFusedUnroll,
                                  workspace_bytes);
+  if (w->format == QLIN_FMT_PACKED)
+    return run_packed(packed_launch(&w, &y, 1), w->bits, x, workspace, sp, stream);
   uint32_t* tick = static_cast<uint32_t*>(workspace);
   float* part = sp.splits > 1 ? reinterpret_cast<float*>(static_cast<char*>(workspace) + kCounterBytes)
                               : nullptr;
   const f16x2* x2 = reinterpret_cast<const f16x2*>(x);
-  if (w->format == QLIN_FMT_PACKED) {
-    switch (w->bits) {
-      case 2: launch_gemv_packed<2>(w, x2, y, part, tick, sp, stream); break;
-      case 3: launch_gemv_packed<3>(w, x2, y, part, tick, sp, stream); break;
-      case 4: launch_gemv_packed<4>(w, x2, y, part, tick, sp, stream); break;
-      default: launch_gemv_packed<8>(w, x2, y, part, tick, sp, stream); break;
-    }
-  } else {
+  {
     switch (w->bits) {
       case 2: launch_gemv_fused<2>(w, x2, y, part, tick, sp, stream); break;
       case 3: launch_gemv_fused<3>(w, x2, y, part, tick, sp, stream); break;
@@ -481,6 +587,66 @@ qlin_status qlin_gemv(const qlin_weight* w, const uint16_t* x, float* y, void* w
     }
   }
   return hip_status(hipGetLastError());
+}
+
+int64_t qlin_gemv_multi_workspace_bytes(const qlin_weight* w, int32_t count) {
+  if (w == nullptr || count < 1 || count > kMaxMats) return 0;
+  for (int i = 0; i < count; ++i)
+    if (check_weight(&w[i], false, false) != QLIN_OK || w[i].k != w[0].k) return 0;
+  return gemv_ws_bytes(set_tiles(w, count), w[0].k / kBlock, kPackedUnroll);
+}
+
+qlin_status qlin_gemv_multi(const qlin_weight* w, int32_t count, const uint16_t* x,
+                            float* const* y, void* workspace, int64_t workspace_bytes,
+                            hipStream_t stream) {
+  if (w == nullptr || y == nullptr) return QLIN_ERR_NULL;
+  if (count < 1 || count > kMaxMats) return QLIN_ERR_SHAPE;
+  void* outs[kMaxMats];
+  int64_t out_bytes[kMaxMats];
+  for (int i = 0; i < count; ++i) {
+    if (y[i] == nullptr) return QLIN_ERR_NULL;
+    outs[i] = y[i];
+    out_bytes[i] = (int64_t)w[i].n * 4;
+  }
+  qlin_status st = check_set(w, count, x, outs, out_bytes, count, workspace, workspace_bytes);
+  if (st != QLIN_OK) return st;
+  if (workspace == nullptr) workspace_bytes = 0;
+  st = check_device();
+  if (st != QLIN_OK) return st;
+  const qlin_weight* wp[kMaxMats];
+  for (int i = 0; i < count; ++i) wp[i] = &w[i];
+  const PackedLaunch L = packed_launch(wp, y, count);
+  const GemvCfg c = gemv_config(L.tiles, L.kb, kPackedUnroll, workspace_bytes);
+  return run_packed(L, w[0].bits, x, workspace, c, stream);
+}
+
+int64_t qlin_gemv_swiglu_workspace_bytes(const qlin_weight* gate) {
+  if (check_weight(gate, false, false) != QLIN_OK) return 0;
+  return swiglu_ws_bytes(tiles_of(gate->n), gate->k / kBlock);
+}
+
+qlin_status qlin_gemv_swiglu(const qlin_weight* gate, const qlin_weight* up, const uint16_t* x,
+                             float* h, uint16_t* h16, void* workspace, int64_t workspace_bytes,
+                             hipStream_t stream) {
+  if (gate == nullptr || up == nullptr) return QLIN_ERR_NULL;
+  if (h == nullptr && h16 == nullptr) return QLIN_ERR_NULL;
+  const qlin_weight pair[2] = {*gate, *up};
+  void* outs[2] = {h, h16};
+  const int64_t out_bytes[2] = {(int64_t)gate->n * 4, (int64_t)gate->n * 2};
+  qlin_status st = check_set(pair, 2, x, outs, out_bytes, 2, workspace, workspace_bytes);
+  if (st != QLIN_OK) return st;
+  if (up->n != gate->n) return QLIN_ERR_SHAPE;
+  if (workspace == nullptr) workspace_bytes = 0;
+  st = check_device();
+  if (st != QLIN_OK) return st;
+  const qlin_weight* wp[2] = {gate, up};
+  float* ys[2] = {h, nullptr};
+  PackedLaunch L = packed_launch(wp, ys, 2);
+  L.tiles = (int)tiles_of(gate->n);
+  L.swiglu = true;
+  L.h16 = h16;
+  const GemvCfg c = swiglu_config(L.tiles, L.kb, workspace_bytes);
+  return run_packed(L, gate->bits, x, workspace, c, stream);
 }
 
 qlin_status qlin_gemm(const qlin_weight* w, const uint16_t* X, int32_t m, int64_t ld_x, float* Y,

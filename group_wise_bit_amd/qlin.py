@@ -9,7 +9,7 @@ from __future__ import annotations
 import ctypes
 import os
 from dataclasses import dataclass
-from typing import Optional
+from typing import List, Optional, Sequence, Tuple
 
 import torch
 
@@ -30,6 +30,8 @@ EXPORTS = (
     "qlin_status_string", "qlin_last_hip_error", "qlin_abi_version", "qlin_packed_bytes",
     "qlin_meta_entries", "qlin_quantize", "qlin_gemv_workspace_bytes",
     "qlin_gemm_workspace_bytes", "qlin_gemv", "qlin_gemm",
+    "qlin_gemv_multi_workspace_bytes", "qlin_gemv_multi",
+    "qlin_gemv_swiglu_workspace_bytes", "qlin_gemv_swiglu",
 )
 
 
@@ -84,6 +86,14 @@ def _lib() -> ctypes.CDLL:
         lib.qlin_gemv.restype = ctypes.c_int
         lib.qlin_gemm.argtypes = [wp, vp, i32, i64, vp, i64, vp, i64, vp]
         lib.qlin_gemm.restype = ctypes.c_int
+        lib.qlin_gemv_multi_workspace_bytes.argtypes = [wp, i32]
+        lib.qlin_gemv_multi_workspace_bytes.restype = i64
+        lib.qlin_gemv_multi.argtypes = [wp, i32, vp, ctypes.POINTER(vp), vp, i64, vp]
+        lib.qlin_gemv_multi.restype = ctypes.c_int
+        lib.qlin_gemv_swiglu_workspace_bytes.argtypes = [wp]
+        lib.qlin_gemv_swiglu_workspace_bytes.restype = i64
+        lib.qlin_gemv_swiglu.argtypes = [wp, wp, vp, vp, vp, vp, i64, vp]
+        lib.qlin_gemv_swiglu.restype = ctypes.c_int
         _LIB = lib
     return _LIB
 
@@ -223,3 +233,45 @@ def gemm(w: QWeight, X: torch.Tensor, Y: Optional[torch.Tensor] = None,
                           Y.stride(0), _ptr(ws), wsb, _stream())
     _check(st, "qlin_gemm")
     return Y
+
+
+def gemv_multi(ws_list: Sequence[QWeight], x: torch.Tensor,
+               ys: Optional[Sequence[torch.Tensor]] = None,
+               ws: Optional[torch.Tensor] = "auto") -> List[torch.Tensor]:
+    """qlin_gemv_multi: y_i = W_i . x for up to 4 packed weights sharing x, one launch."""
+    if x.dtype != torch.float16 or not x.is_contiguous():
+        raise TypeError("x must be a contiguous float16 tensor")
+    count = len(ws_list)
+    arr = (QlinWeightC * max(count, 1))(*[w.c_struct() for w in ws_list])
+    if ys is None:
+        ys = [torch.empty(w.n, dtype=torch.float32, device=x.device) for w in ws_list]
+    yp = (ctypes.c_void_p * max(count, 1))(*[y.data_ptr() for y in ys])
+    if isinstance(ws, str):
+        need = int(_lib().qlin_gemv_multi_workspace_bytes(arr, count))
+        ws = workspace(need, x.device)
+    wsb = 0 if ws is None else ws.numel() * ws.element_size()
+    st = _lib().qlin_gemv_multi(arr, count, x.data_ptr(), yp, _ptr(ws), wsb, _stream())
+    _check(st, "qlin_gemv_multi")
+    return list(ys)
+
+
+def gemv_swiglu(gate: QWeight, up: QWeight, x: torch.Tensor,
+                h: Optional[torch.Tensor] = None, h16: Optional[torch.Tensor] = None,
+                ws: Optional[torch.Tensor] = "auto", want_h: bool = True,
+                want_h16: bool = True) -> Tuple[Optional[torch.Tensor], Optional[torch.Tensor]]:
+    """qlin_gemv_swiglu: h = silu(gate . x) * (up . x), fp32 and/or fp16, one launch."""
+    if x.dtype != torch.float16 or not x.is_contiguous():
+        raise TypeError("x must be a contiguous float16 tensor")
+    if h is None and want_h:
+        h = torch.empty(gate.n, dtype=torch.float32, device=x.device)
+    if h16 is None and want_h16:
+        h16 = torch.empty(gate.n, dtype=torch.float16, device=x.device)
+    g, u = gate.c_struct(), up.c_struct()
+    if isinstance(ws, str):
+        need = int(_lib().qlin_gemv_swiglu_workspace_bytes(ctypes.byref(g)))
+        ws = workspace(need, x.device)
+    wsb = 0 if ws is None else ws.numel() * ws.element_size()
+    st = _lib().qlin_gemv_swiglu(ctypes.byref(g), ctypes.byref(u), x.data_ptr(), _ptr(h),
+                                 _ptr(h16), _ptr(ws), wsb, _stream())
+    _check(st, "qlin_gemv_swiglu")
+    return h, h16

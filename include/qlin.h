@@ -171,6 +171,39 @@ qlin_status qlin_gemm(const qlin_weight* w, const uint16_t* X, int32_t m, int64_
                       float* Y, int64_t ld_y, void* workspace, int64_t workspace_bytes,
                       hipStream_t stream);
 
+/*
+ * Several decode GEMVs that share x, in one launch (the Enargeia page, "One
+ * decode step": the per-token dispatch list, where q, k and v, and gate and
+ * up, each read the same normalized activation):
+ *     y_i[n] = sum_k x[k] * s_i(q_i - z_i),   i = 0 .. count-1,  count <= 4.
+ * w points to `count` PACKED weights with the same k, bits and group (n may
+ * differ); y to `count` fp32 output pointers (y_i has w[i].n entries).  Each
+ * y_i equals what qlin_gemv gives for w[i] to the same tolerance.
+ * Workspace as for qlin_gemv, sized by qlin_gemv_multi_workspace_bytes.
+ * Errors: count outside 1..4 -> QLIN_ERR_SHAPE; different k -> SHAPE; different
+ * bits or group, or an FP16_MASTER weight -> QLIN_ERR_FORMAT.
+ */
+int64_t qlin_gemv_multi_workspace_bytes(const qlin_weight* w, int32_t count);
+qlin_status qlin_gemv_multi(const qlin_weight* w, int32_t count, const uint16_t* x,
+                            float* const* y, void* workspace, int64_t workspace_bytes,
+                            hipStream_t stream);
+
+/*
+ * Gated MLP input of a decode step in one launch (the Bitcrush README, "Under
+ * the hood": the SwiGLU kernel that follows the gate and up projections):
+ *     h[n] = silu(g[n]) * u[n],   g = gate . x,  u = up . x,
+ *     silu(g) = g / (1 + exp(-g)),
+ * with g and u accumulated as in qlin_gemv and never written to memory.
+ * gate and up are PACKED weights with the same n, k, bits and group.  h (fp32,
+ * [n]) and h16 (fp16 bit patterns, [n], h rounded to nearest even, ready as
+ * the next GEMV's x) are outputs; either may be NULL, not both.
+ * Workspace sized by qlin_gemv_swiglu_workspace_bytes(gate).
+ */
+int64_t qlin_gemv_swiglu_workspace_bytes(const qlin_weight* gate);
+qlin_status qlin_gemv_swiglu(const qlin_weight* gate, const qlin_weight* up, const uint16_t* x,
+                             float* h, uint16_t* h16, void* workspace, int64_t workspace_bytes,
+                             hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -159,3 +159,43 @@ def fused_weights(w16: np.ndarray, scale16: np.ndarray, zero: np.ndarray,
         return np.asarray(w16, dtype=np.float16).astype(np.float64)
     return dequantize(rtn_codes(w16, scale16, zero, bits, group),
                       scale16, zero, group)
+
+
+def silu(g: np.ndarray) -> np.ndarray:
+    """silu(g) = g * sigmoid(g) = g / (1 + exp(-g)), in binary64.
+
+    The activation of the gated MLP that follows the gate and up projections
+    (Bitcrush README, "Under the hood": the SwiGLU kernel of the decode path).
+    exp(-g) overflows to inf for g < -709; g / inf is then the correct -0."""
+    g = np.asarray(g, dtype=np.float64)
+    with np.errstate(over="ignore"):
+        return g / (1.0 + np.exp(-g))
+
+
+def swiglu_ref(x16: np.ndarray, w_gate: np.ndarray, w_up: np.ndarray) -> np.ndarray:
+    """h = silu(x . W_gate^T) * (x . W_up^T): the two decode GEMVs that share
+    the MLP input, combined elementwise (binary64 throughout)."""
+    return silu(matmul_ref(x16, w_gate)) * matmul_ref(x16, w_up)
+
+
+# Largest slope of silu: silu'(g) = s(g) (1 + g (1 - s(g))), s the logistic
+# function, peaks at 1.0998 near g = 2.40; 1.1 bounds it.
+SILU_SLOPE_MAX = 1.1
+
+
+def swiglu_tolerance(x16: np.ndarray, w_gate: np.ndarray, w_up: np.ndarray,
+                     rel: float = 1e-3, fp32_rel: float = 4e-6) -> np.ndarray:
+    """Per-output bound on |h_gpu - h_ref| implied by the GEMV tolerance.
+
+    The GEMV contract bounds the gate and up sums by eg = rel * T_gate and
+    eu = rel * T_up (T = max_row sum |x w|).  With |silu'| <= 1.1:
+        |silu(g + dg)(u + du) - silu(g) u|
+            <= 1.1 eg (|u| + eu) + |silu(g)| eu,
+    and the fp32 evaluation of silu and of the product adds at most
+    fp32_rel * |h| (a few ulp of binary32)."""
+    g = matmul_ref(x16, w_gate)
+    u = matmul_ref(x16, w_up)
+    eg = rel * tolerance_scale(x16, w_gate)
+    eu = rel * tolerance_scale(x16, w_up)
+    prop = SILU_SLOPE_MAX * eg * (np.abs(u) + eu) + np.abs(silu(g)) * eu
+    return prop * (1.0 + fp32_rel) + fp32_rel * np.abs(silu(g) * u)

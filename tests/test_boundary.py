@@ -31,7 +31,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     declared = header_functions()
-    assert len(declared) == 10
+    assert len(declared) == 14
     assert sorted(qlin.EXPORTS) == declared
     for name in declared:
         assert hasattr(lib, name), name
@@ -136,12 +136,77 @@ def test_gemm_validation(lib):
     assert gemm(lib, weight(), Y=FAKE + (3 << 30)) == ALIAS
 
 
+def weights(*ws):
+    return (qlin.QlinWeightC * len(ws))(*ws)
+
+
+def ptrs(*ps):
+    return (ctypes.c_void_p * len(ps))(*ps)
+
+
+Y0, Y1, Y2 = FAKE + (4 << 30), FAKE + (5 << 30), FAKE + (6 << 30)
+
+
+def multi(lib, ws, ys, x=FAKE + (3 << 30), count=None, ws_=None, wsb=0):
+    count = len(ws) if count is None else count
+    return lib.qlin_gemv_multi(weights(*ws), count, x, ptrs(*ys), ws_, wsb, None)
+
+
+def swiglu(lib, g, u, x=FAKE + (3 << 30), h=Y0, h16=Y1, ws_=None, wsb=0):
+    return lib.qlin_gemv_swiglu(ctypes.byref(g), ctypes.byref(u), x, h, h16, ws_, wsb, None)
+
+
+def other_weight(i, **kw):
+    # a second / third weight at its own addresses
+    base = FAKE + ((8 + 4 * i) << 30)
+    d = dict(data=base, scale=base + (1 << 30), zero=base + (2 << 30))
+    d.update(kw)
+    return weight(**d)
+
+
+def test_gemv_multi_validation(lib):
+    w0, w1, w2 = weight(), other_weight(0, n=200), other_weight(1, n=1)
+    assert lib.qlin_gemv_multi(None, 1, FAKE, ptrs(Y0), None, 0, None) == NULL
+    assert lib.qlin_gemv_multi(weights(w0), 1, FAKE + (3 << 30), None, None, 0, None) == NULL
+    assert multi(lib, [w0], [None]) == NULL
+    assert multi(lib, [w0], [Y0], x=None) == NULL
+    assert multi(lib, [w0], [Y0], count=0) == SHAPE
+    assert multi(lib, [w0, w1, w2, w0, w1], [Y0, Y1, Y2, Y0, Y1]) == SHAPE   # at most 4
+    assert multi(lib, [w0, other_weight(0, k=256)], [Y0, Y1]) == SHAPE      # one k
+    assert multi(lib, [w0, other_weight(0, bits=3)], [Y0, Y1]) == FORMAT
+    assert multi(lib, [w0, other_weight(0, group=128)], [Y0, Y1]) == FORMAT
+    assert multi(lib, [w0, other_weight(0, format=1, ld=128)], [Y0, Y1]) == FORMAT
+    assert multi(lib, [w0, w1], [Y0, Y0 + 16]) == ALIAS                     # outputs overlap
+    assert multi(lib, [w0, w1], [Y0, FAKE + (8 << 30) + 64]) == ALIAS       # y inside w1
+    assert multi(lib, [w0, w1], [Y0, FAKE + (3 << 30)]) == ALIAS            # y on x
+    assert multi(lib, [w0, w1], [Y0, Y1 + 4]) == ALIGN
+    assert multi(lib, [w0, w1], [Y0, Y1], ws_=Y1, wsb=64) == ALIAS
+    assert multi(lib, [w0, w1], [Y0, Y1], ws_=FAKE + (7 << 30), wsb=-1) == WORKSPACE
+
+
+def test_gemv_swiglu_validation(lib):
+    g, u = weight(), other_weight(0)
+    assert lib.qlin_gemv_swiglu(None, ctypes.byref(u), FAKE, Y0, Y1, None, 0, None) == NULL
+    assert swiglu(lib, g, u, h=None, h16=None) == NULL
+    assert swiglu(lib, g, u, x=None) == NULL
+    assert swiglu(lib, g, other_weight(0, n=16)) == SHAPE
+    assert swiglu(lib, g, other_weight(0, k=256)) == SHAPE
+    assert swiglu(lib, g, other_weight(0, bits=8)) == FORMAT
+    assert swiglu(lib, g, other_weight(0, format=1, ld=128)) == FORMAT
+    assert swiglu(lib, g, u, h16=Y0 + 16) == ALIAS                          # h16 inside h
+    assert swiglu(lib, g, u, h=FAKE + 32) == ALIAS                           # h on gate codes
+    assert swiglu(lib, g, u, h16=Y1 + 2) == ALIGN
+
+
 @pytest.mark.skipif(torch.cuda.is_available(), reason="checks the no-GPU path")
 def test_no_device(lib):
     assert quant(lib) == NODEV
     assert gemv(lib, weight()) == NODEV
     assert gemm(lib, weight()) == NODEV
     assert gemm(lib, weight(), m=64, ldy=64) == NODEV
+    assert multi(lib, [weight(), other_weight(0)], [Y0, Y1]) == NODEV
+    assert swiglu(lib, weight(), other_weight(0)) == NODEV
+    assert swiglu(lib, weight(), other_weight(0), h=None) == NODEV
 
 
 def test_workspace_queries(lib):
@@ -152,3 +217,9 @@ def test_workspace_queries(lib):
     assert lib.qlin_gemv_workspace_bytes(ctypes.byref(small)) == 0
     assert lib.qlin_gemm_workspace_bytes(ctypes.byref(big), 8) > 65536
     assert lib.qlin_gemm_workspace_bytes(ctypes.byref(weight(bits=7)), 8) == 0
+    # multi: the launch's tiles add up; swiglu: two partials per row
+    pair = weights(big, big)
+    assert lib.qlin_gemv_multi_workspace_bytes(pair, 2) >= need
+    assert lib.qlin_gemv_multi_workspace_bytes(pair, 0) == 0
+    assert lib.qlin_gemv_multi_workspace_bytes(weights(big, weight(k=256)), 2) == 0
+    assert lib.qlin_gemv_swiglu_workspace_bytes(ctypes.byref(big)) > 65536
