@@ -27,6 +27,8 @@ fp16 masters ~N(0, 0.02), activations ~N(0, 1):
   quantize_pack    scale/zero and packed codes of all 169 masters
 qwen3_8b -- 36 layers of q 4096->4096, k/v 4096->1024, o 4096->4096,
 gate/up 4096->12288, down 12288->4096 (252 matrices, 3.8 GB at int4):
+  q8_step_int4 / _int3 / _int2     the 252 GEMVs grouped as in decode_step:
+                                   144 launches (graph)
   q8_decode_int4 / _int3 / _int2   252 packed GEMVs (graph)
   q8_m8_int4 / _int3               252 GEMMs at M = 8
   q8_m128_int4 / _int3             252 GEMMs at M = 128
@@ -131,7 +133,7 @@ def capture_calls(torch, call_lists):
     return graphs
 
 
-def grouped_step_calls(qlin, shapes, weights, xs, dev, torch, ws):
+def grouped_step_calls(qlin, shapes, weights, xs, dev, torch, ws, bits=4):
     """The decode step's linear layers as the per-token dispatch list groups
     them: per layer one launch for q/k/v (shared x), o, one gate/up launch with
     the SwiGLU combination (fp16 h), and down reading that h; then the LM head.
@@ -154,7 +156,7 @@ def grouped_step_calls(qlin, shapes, weights, xs, dev, torch, ws):
             lambda wd=wd, h16=h16, y=yd: qlin.gemv(wd, h16, y, ws=ws),
         ]
         kk = shapes[q][3]
-        nbytes += sum(wbytes(shapes[i][2], shapes[i][3], 4, 64) for i in (q, k, v, o, g, u, d))
+        nbytes += sum(wbytes(shapes[i][2], shapes[i][3], bits, 64) for i in (q, k, v, o, g, u, d))
         nbytes += 2 * kk + 4 * sum(shapes[i][2] for i in (q, k, v))          # qkv: x, y
         nbytes += 2 * shapes[o][3] + 4 * shapes[o][2]                         # o
         nbytes += 2 * shapes[g][3] + 2 * shapes[g][2]                         # gate/up: x, h16
@@ -163,7 +165,8 @@ def grouped_step_calls(qlin, shapes, weights, xs, dev, torch, ws):
     if lm is not None:
         ylm = torch.empty(shapes[lm][2], dtype=torch.float32, device=dev)
         calls.append(lambda w=weights[lm], x=xs[lm], y=ylm: qlin.gemv(w, x, y, ws=ws))
-        nbytes += wbytes(shapes[lm][2], shapes[lm][3], 4, 64) + 2 * shapes[lm][3] + 4 * shapes[lm][2]
+        nbytes += (wbytes(shapes[lm][2], shapes[lm][3], bits, 64) + 2 * shapes[lm][3] +
+                   4 * shapes[lm][2])
     return calls, nbytes, len(calls)
 
 
@@ -276,14 +279,20 @@ def build_qwen3_8b(torch, qlin, synth, dev, ws, phases):
     torch.cuda.synchronize()
     print(f"[bench] Qwen3-8B shapes quantized in {time.time() - t0:.1f}s", file=sys.stderr,
           flush=True)
-    graphs = {}
+    graphs, steps, step_bytes = {}, {}, {}
     for b in (4, 3, 2):
         if f"q8_decode_int{b}" in phases:
             graphs[b] = capture(torch, qlin, [list(zip(packed[b], xs, ys))], ws)[0]
+        if f"q8_step_int{b}" in phases:
+            calls, step_bytes[b], _ = grouped_step_calls(qlin, shapes, packed[b], xs, dev, torch,
+                                                         ws, bits=b)
+            steps[b] = capture_calls(torch, [calls])[0]
 
     def run(name):
         b = int(name[-1])
-        if "decode" in name:
+        if "step" in name:
+            steps[b].replay()
+        elif "decode" in name:
             graphs[b].replay()
         else:
             m = 8 if "_m8_" in name else 128
@@ -292,6 +301,8 @@ def build_qwen3_8b(torch, qlin, synth, dev, ws, phases):
 
     out = []
     for b in (4, 3, 2):
+        out.append(Phase(f"q8_step_int{b}", run, "GB/s", step_bytes.get(b, 0), 144, HBM_PEAK_GBS,
+                         "hbm", f"k_gemv_packed<{b}> (q/k/v set, o, gate/up+SwiGLU, down)"))
         out.append(Phase(f"q8_decode_int{b}", run, "GB/s",
                          sum(wbytes(n, k, b, 64) + 2 * k + 4 * n for (_, _, n, k) in shapes),
                          252, HBM_PEAK_GBS, "hbm", f"k_gemv_packed<{b}>"))
@@ -380,7 +391,7 @@ def main():
         ps, decode_shapes = build_decode(torch, qlin, synth, dev, ws, chosen(names), state)
         phases += ps
     if "qwen3_8b" in sections:
-        names = [f"q8_decode_int{b}" for b in (4, 3, 2)] + [
+        names = [f"q8_{s}_int{b}" for b in (4, 3, 2) for s in ("step", "decode")] + [
             f"q8_m{m}_int{b}" for b in (4, 3) for m in (8, 128)]
         phases += build_qwen3_8b(torch, qlin, synth, dev, ws, chosen(names))
     if "qwen3_06b" in sections:

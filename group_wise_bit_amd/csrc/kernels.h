@@ -648,10 +648,11 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_skinny(
 // ----------------------------------------------------- tiled GEMM (M>16) --
 // v_mfma_f32_32x32x16_f16.  Work-group = 4 waves; wave w owns W tile
 // blockIdx.x*4 + w (64 rows = two 32-column MFMA blocks), all MB rows of X.
-// X blocks are staged once per work-group in LDS as they are (fp16, double
-// buffered, rows padded to 144 bytes); the weight operand is decoded straight
-// from global memory into registers, so each code is read and decoded once
-// per work-group.  Lane (c = lane % 32, h = lane / 32) supplies row c and the
+// Register-staged form, used for 32-row X tiles (several work-groups per CU
+// hide its load latency): X blocks go global -> registers -> LDS (fp16,
+// double buffered, rows padded to 144 bytes); the weight operand is decoded
+// straight from global memory into registers, so each code is read and
+// decoded once per work-group.  Lane (c = lane % 32, h = lane / 32) supplies row c and the
 // K positions 32h + 8s .. +7 of the block for instruction s in 0..3.
 // D[8*(r/4) + 4*h + r%4][c] is acc register r.
 constexpr int kLdsRow = 72;   // fp16 per padded LDS row
@@ -845,6 +846,264 @@ __global__ __launch_bounds__(256) void k_gemm_tiles(
     // 4 KB of consecutive bytes per work-group; the last work-group of this
     // output tile to arrive adds the splits in order 0, 1, ... .
     constexpr int NQ = RB * 2 * 4;          // float4 quads per thread
+    const int64_t wg = (int64_t)blockIdx.y * gridDim.x + blockIdx.x;
+    const int64_t groups = (int64_t)gridDim.x * gridDim.y;
+    float* pw = part + ((blockIdx.z * groups + wg) * NQ * 256 + tid) * 4;
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            put_partial(pw + ((rb * 2 + cb) * 4 + q) * 1024 + e, acc[rb][cb][4 * q + e]);
+    partials_written();
+    __syncthreads();
+    __shared__ uint32_t s_last;
+    if (tid == 0) {
+      const uint32_t prev = __hip_atomic_fetch_add(&tickets[wg], 1u, __ATOMIC_RELAXED,
+                                                   __HIP_MEMORY_SCOPE_AGENT);
+      s_last = prev == (uint32_t)(splits - 1);
+      if (s_last) __hip_atomic_store(&tickets[wg], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __syncthreads();
+    if (!s_last) return;
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[rb][cb][r] = 0.f;
+    const float* pr = part + (wg * NQ * 256 + tid) * 4;
+    for (int s2 = 0; s2 < splits; ++s2) {
+      f32x4 v[NQ];
+#pragma unroll
+      for (int i = 0; i < NQ; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          v[i][e] = get_partial(pr + ((int64_t)s2 * groups * NQ + i) * 1024 + e);
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[rb][cb][4 * q + e] += v[(rb * 2 + cb) * 4 + q][e];
+    }
+  }
+
+  if (!tvalid) return;
+  // rows m0 + 32rb + 8(r/4) + 4h + r%4 of columns t*64 + 32cb + c
+  float* ybase = Y + (int64_t)(m0 + 4 * h) * ldy + t * kTile + c;
+  const int mrem = m - m0 - 4 * h;
+#pragma unroll
+  for (int cb = 0; cb < 2; ++cb) {
+    if (t * kTile + 32 * cb + c >= n) continue;
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int dr = 32 * rb + 8 * (r >> 2) + (r & 3);
+        if (dr < mrem) ybase[(int64_t)dr * ldy + 32 * cb] = acc[rb][cb][r];
+      }
+  }
+}
+
+// ------------------------------------------ tiled GEMM, LDS-DMA pipeline --
+// Same tiling and MFMA lane layout as k_gemm_tiles; the difference is how the
+// operands arrive.  Every K-block's X tile (MB x 64 fp16), the four 64-row
+// code blocks and their scales/zeros are copied global -> LDS by the
+// direct-to-LDS loads of gfx950 (global_load_lds_dword[x4]), S blocks
+// deep, into S separate LDS stages: no registers hold data in flight, so the
+// loads of block j + S - 1 are issued while block j computes and the memory
+// latency is hidden behind S - 1 blocks of MFMA work.  Each wave copies a
+// quarter of the X tile and its own tile's codes and metadata.  X chunks are
+// XOR-swizzled within a row (16-byte chunk c8 of row r at position
+// c8 ^ (r & 7)), so the A-fragment reads are free of bank conflicts.
+// One direct-to-LDS load of SZ bytes per lane: lane l's bytes land at
+// lds + SZ * l (lds wave-uniform).
+template <int SZ>
+__device__ __forceinline__ void dma_to_lds(const void* src, void* lds) {
+  typedef __attribute__((address_space(3))) void lds_void;
+  static_assert(SZ == 4 || SZ == 16, "direct-to-LDS load size");
+  if constexpr (SZ == 16) __builtin_amdgcn_global_load_lds(src, (lds_void*)lds, 16, 0, 0);
+  else __builtin_amdgcn_global_load_lds(src, (lds_void*)lds, 4, 0, 0);
+}
+
+template <int BITS, int MB>
+struct GemmStage {
+  f16 x[MB * 64];                    // X tile, swizzled 16-byte chunks
+  uint32_t w[4][64 * 2 * BITS];      // codes of the four tiles' block, as in HBM
+  uint32_t meta[4][64];              // per tile: 64 fp16 scales, then 64 uint8 zeros
+};
+
+// One LDS variable per stage (distinct objects let the compiler track which
+// direct-to-LDS loads a read depends on).
+template <int BITS, int MB, int I>
+__device__ __forceinline__ GemmStage<BITS, MB>& gemm_stage() {
+  __shared__ __attribute__((aligned(16))) GemmStage<BITS, MB> st;
+  return st;
+}
+
+// s_waitcnt vmcnt(N) (expcnt and lgkmcnt not waited on); gfx9 encoding.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Direct-to-LDS load pieces per wave for one tile's code block (64 rows x
+// 2*BITS words): {bytes per lane, instructions}.  (The 3-byte-per-code
+// block, 1536 bytes, goes as dwords.)
+template <int BITS> struct WDma;
+template <> struct WDma<2> { static constexpr int SZ = 16, N = 1; };
+template <> struct WDma<3> { static constexpr int SZ = 4, N = 6; };
+template <> struct WDma<4> { static constexpr int SZ = 16, N = 2; };
+template <> struct WDma<8> { static constexpr int SZ = 16, N = 4; };
+
+template <int BITS, int MB, int S>
+__global__ __launch_bounds__(256, 2) void k_gemm_lds(
+    const uint32_t* __restrict__ codes, const uint16_t* __restrict__ scale,
+    const uint8_t* __restrict__ zero, const uint16_t* __restrict__ X, int64_t ldx, int m,
+    float* __restrict__ Y, int64_t ldy, int n, int kb, int G, int tiles,
+    int splits, int kbps, float* __restrict__ part, uint32_t* __restrict__ tickets) {
+  constexpr int WPB = 2 * BITS;
+  constexpr int RB = MB / 32;               // 32-row MFMA blocks of X
+  constexpr int XQ = MB / 32;               // X pieces (16 B) per thread per block
+  constexpr int NDMA = XQ + WDma<BITS>::N + 1;
+  static_assert(S >= 2 && (S - 1) * NDMA < 64, "stages");
+  static_assert(WDma<BITS>::SZ * 64 * WDma<BITS>::N == 64 * WPB * 4, "code block pieces");
+  const int tid = threadIdx.x;
+  const int lane = lane_id(), wave = wave_id();
+  const int c = lane & 31, h = lane >> 5;
+  const int t = blockIdx.x * 4 + wave;
+  const bool tvalid = t < tiles;
+  const int tt = tvalid ? t : 0;
+  const int m0 = blockIdx.y * MB;
+  const uint32_t magic = vreg_const(kMagic);
+  const int ja = blockIdx.z * kbps;
+  const int nk = min(kb, ja + kbps) - ja;
+
+  // per-lane global sources of this lane's pieces (block 0 of the range)
+  const char* xsrc[XQ];
+#pragma unroll
+  for (int i = 0; i < XQ; ++i) {
+    const int q = tid + 256 * i;            // LDS position of the piece
+    const int row = q >> 3, c8 = (q & 7) ^ (row & 7);
+    const int xr = m0 + row < m ? m0 + row : m0;
+    xsrc[i] = reinterpret_cast<const char*>(X + (int64_t)xr * ldx + 8 * c8);
+  }
+  const char* wsrc = reinterpret_cast<const char*>(codes + (int64_t)tt * kb * kTile * WPB) +
+                     lane * WDma<BITS>::SZ;
+  // metadata piece: lanes 0-31 two scales each, lanes 32-63 four zeros each
+  // (lanes 48-63 repeat 32-47 into the unused upper quarter)
+  const char* msrc = lane < 32
+      ? reinterpret_cast<const char*>(scale + (int64_t)tt * G * kTile) + 4 * lane
+      : reinterpret_cast<const char*>(zero + (int64_t)tt * G * kTile) + 4 * ((lane - 32) & 15);
+
+  auto issue = [&](int j, auto stc) __attribute__((always_inline)) {
+    constexpr int I = decltype(stc)::value;
+    GemmStage<BITS, MB>& st = gemm_stage<BITS, MB, I>();
+    const int jg = ja + j;
+#pragma unroll
+    for (int i = 0; i < XQ; ++i)
+      dma_to_lds<16>(xsrc[i] + (int64_t)jg * kBlock * 2, st.x + (256 * i + 64 * wave) * 8);
+#pragma unroll
+    for (int i = 0; i < WDma<BITS>::N; ++i)
+      dma_to_lds<WDma<BITS>::SZ>(wsrc + ((int64_t)jg * kTile * WPB) * 4 + i * 64 * WDma<BITS>::SZ,
+                                 reinterpret_cast<char*>(st.w[wave]) + i * 64 * WDma<BITS>::SZ);
+    const int64_t g = (G == 1) ? 0 : jg;
+    dma_to_lds<4>(msrc + (lane < 32 ? g * kTile * 2 : g * kTile), st.meta[wave]);
+  };
+
+  f32x16 acc[RB][2];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[rb][cb][r] = 0.f;
+
+  // Block j from stage I: decode this wave's B operand from the staged codes
+  // slice by slice, interleaved with the MFMAs of the previous slice.
+  auto compute = [&](auto stc) __attribute__((always_inline)) {
+    constexpr int I = decltype(stc)::value;
+    const GemmStage<BITS, MB>& st = gemm_stage<BITS, MB, I>();
+    uint32_t wl[2][(BITS == 3) ? 3 : BITS];
+    Deq d[2];
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) {
+      const int r = 32 * cb + c;
+      load_half<BITS>(st.w[wave] + r * WPB, h, wl[cb]);
+      const uint16_t sb = reinterpret_cast<const uint16_t*>(st.meta[wave])[r];
+      const int zb = reinterpret_cast<const uint8_t*>(st.meta[wave])[128 + r];
+      d[cb] = make_deq(h2f(sb), zb);
+    }
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4) {
+      f16x8 a[RB], b[2];
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        const int row = 32 * rb + c, c8 = (4 * h + s4) ^ (row & 7);
+        a[rb] = *reinterpret_cast<const f16x8*>(st.x + row * 64 + 8 * c8);
+      }
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb) b[cb] = deq_half<BITS>(wl[cb], s4, d[cb], magic);
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb)
+          acc[rb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[rb], b[cb], acc[rb][cb], 0, 0, 0);
+    }
+  };
+
+  // Wait until this wave's loads of block j are in LDS (rem = blocks issued
+  // after it), then a barrier makes every wave's part visible; the stage
+  // freed by block j-1 is refilled with block j+S-1 right after.
+  auto wait_block = [&](int rem) __attribute__((always_inline)) {
+    if constexpr (S > 4) { if (rem >= 3) { wait_vm<3 * NDMA>(); return; } }
+    if constexpr (S > 3) { if (rem >= 2) { wait_vm<2 * NDMA>(); return; } }
+    if constexpr (S > 2) { if (rem >= 1) { wait_vm<NDMA>(); return; } }
+    wait_vm<0>();
+  };
+  auto step = [&](int j, auto stc) __attribute__((always_inline)) {
+    constexpr int I = decltype(stc)::value;
+    wait_block(min(S - 2, nk - 1 - j));
+    lds_barrier();
+    if (j + S - 1 < nk) issue(j + S - 1, std::integral_constant<int, (I + S - 1) % S>{});
+    compute(stc);
+  };
+
+  issue(0, std::integral_constant<int, 0>{});
+  if (S > 2 && 1 < nk) issue(1, std::integral_constant<int, 1 % S>{});
+  if (S > 3 && 2 < nk) issue(2, std::integral_constant<int, 2 % S>{});
+  if (S > 4 && 3 < nk) issue(3, std::integral_constant<int, 3 % S>{});
+  for (int j = 0;; j += S) {
+    step(j, std::integral_constant<int, 0>{});
+    if (j + 1 >= nk) break;
+    step(j + 1, std::integral_constant<int, 1 % S>{});
+    if (j + 2 >= nk) break;
+    if constexpr (S > 2) {
+      step(j + 2, std::integral_constant<int, 2 % S>{});
+      if (j + 3 >= nk) break;
+    }
+    if constexpr (S > 3) {
+      step(j + 3, std::integral_constant<int, 3 % S>{});
+      if (j + 4 >= nk) break;
+    }
+    if constexpr (S > 4) {
+      step(j + 4, std::integral_constant<int, 4 % S>{});
+      if (j + 5 >= nk) break;
+    }
+  }
+
+  if (splits > 1) {
+    // partial tile -> workspace in fragment order [split][work-group][quad]
+    // [thread] x 16 bytes; the last work-group of the output tile to arrive
+    // adds the splits in order 0, 1, ...
+    constexpr int NQ = RB * 2 * 4;
     const int64_t wg = (int64_t)blockIdx.y * gridDim.x + blockIdx.x;
     const int64_t groups = (int64_t)gridDim.x * gridDim.y;
     float* pw = part + ((blockIdx.z * groups + wg) * NQ * 256 + tid) * 4;

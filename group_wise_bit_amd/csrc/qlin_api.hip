@@ -360,10 +360,10 @@ void launch_gemm_skinny(const qlin_weight* w, const uint16_t* X, int64_t ldx, in
 // Tiled-GEMM launch shape: work-group tile = MB rows of X x 256 rows of W
 // (four 64-row tiles).  Measured on MI355X (graph-replayed launches over
 // rotating cold weights, Qwen-shaped N x K, M = 32..2048, int4): a tall X tile
-// pays only when the grid is large (M = 2048); up to M = 256 the 32-row tile
-// is fastest (four waves per SIMD hide the load latency that one 128-row wave
-// cannot), and K is split up to 4 ways when there are fewer than 160
-// work-groups, keeping at least 10 K-blocks per split.
+// pays only when the grid is large; up to M = 256 the 32-row tile is fastest
+// (several work-groups per CU hide the load latency), and K is split up to 4
+// ways when there are fewer than 160 work-groups, keeping at least 10
+// K-blocks per split.
 struct TilesCfg { int mb, gx, gy, splits, kbps; };
 
 TilesCfg tiles_config(int64_t tiles, int kb, int m, int64_t ws_bytes) {
@@ -377,8 +377,13 @@ TilesCfg tiles_config(int64_t tiles, int kb, int m, int64_t ws_bytes) {
     if (want > 4) want = 4;
     if (want > kb / 10) want = kb / 10;
   } else {
+    // 128-row tiles when that already gives more work-groups than CUs (two
+    // fit per CU), else 64 when that fills the chip, else 32
     c.mb = 128;
-    while (c.mb > 32 && (int64_t)c.gx * ((m + c.mb - 1) / c.mb) < 256) c.mb /= 2;
+    if ((int64_t)c.gx * ((m + 127) / 128) < 288) {
+      c.mb = 64;
+      if ((int64_t)c.gx * ((m + 63) / 64) < 256) c.mb = 32;
+    }
   }
   // QLIN_TUNE_GEMM="mb,splits" overrides the choice (launch-shape sweeps)
   if (const char* e = getenv("QLIN_TUNE_GEMM")) {
@@ -404,14 +409,23 @@ int64_t tiles_ws_bytes(int64_t tiles, int kb, int m) {
   return kCounterBytes + (int64_t)c.splits * c.gy * c.mb * c.gx * 256 * 4;
 }
 
+// MB = 32: the register-staged kernel (several work-groups per CU hide its
+// load latency); MB = 64 / 128: the LDS-DMA pipeline, 4 / 3 stages deep
+// (two work-groups per CU).
 template <int B, int MB>
 void launch_tiles_mb(const qlin_weight* w, const uint16_t* X, int64_t ldx, int m, float* Y,
                      int64_t ldy, TilesCfg c, float* part, uint32_t* tick, hipStream_t st) {
   const int kb = w->k / kBlock;
   const int G = (w->group == w->k) ? 1 : kb;
-  hipLaunchKernelGGL((k_gemm_tiles<B, MB>), dim3(c.gx, c.gy, c.splits), dim3(256), 0, st,
-                     static_cast<const uint32_t*>(w->data), w->scale, w->zero, X, ldx, m, Y, ldy,
-                     w->n, kb, G, (int)tiles_of(w->n), c.splits, c.kbps, part, tick);
+  if constexpr (MB == 32)
+    hipLaunchKernelGGL((k_gemm_tiles<B, MB>), dim3(c.gx, c.gy, c.splits), dim3(256), 0, st,
+                       static_cast<const uint32_t*>(w->data), w->scale, w->zero, X, ldx, m, Y, ldy,
+                       w->n, kb, G, (int)tiles_of(w->n), c.splits, c.kbps, part, tick);
+  else
+    hipLaunchKernelGGL((k_gemm_lds<B, MB, (MB == 128 ? 3 : 4)>), dim3(c.gx, c.gy, c.splits),
+                       dim3(256), 0, st, static_cast<const uint32_t*>(w->data), w->scale, w->zero,
+                       X, ldx, m, Y, ldy, w->n, kb, G, (int)tiles_of(w->n), c.splits, c.kbps,
+                       part, tick);
 }
 
 template <int B>

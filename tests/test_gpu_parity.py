@@ -234,10 +234,13 @@ def test_gemm_one_hot_fp16_exact(bits, m):
         assert np.array_equal(Y.astype(np.float64), fp16_rne(what[:, cols].T))
 
 
-@pytest.mark.parametrize("bits", [3, 4])
-@pytest.mark.parametrize("m,n,k", [(2048, 4096, 256), (1024, 4096, 128), (300, 256, 960)])
+@pytest.mark.parametrize("bits", [2, 3, 4, 8])
+@pytest.mark.parametrize("m,n,k", [(2048, 8192, 192), (1100, 12288, 128), (2048, 4096, 256),
+                                   (1000, 4160, 320), (300, 256, 960)])
 def test_gemm_tile_heights(bits, m, n, k):
-    """Large grids select the 128- and 64-row X tiles, small ones 32 rows."""
+    """Large grids select the 128-row X tiles (LDS pipeline, 3 stages), mid
+    ones 64 rows (4 stages), small ones 32 rows (register-staged); ragged M and
+    N in the last work-groups."""
     say(f"gemm tile heights bits={bits} m={m} n={n} k={k}")
     rng = np.random.default_rng(m + n + k + bits)
     w16 = synth.master_weights(rng, n, k)
@@ -246,6 +249,24 @@ def test_gemm_tile_heights(bits, m, n, k):
     what = oracle.dequantize(codes, s16, z, 64)
     Y = host(qlin.gemm(qw, dev(x16)))
     check_tol(Y, x16, what, f"gemm {m}x{n}x{k}")
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4, 8])
+@pytest.mark.parametrize("m", [512, 1024])
+def test_gemm_lds_one_hot_fp16_exact(bits, m):
+    """The 64- and 128-row X tiles (n = 16384 fills the chip): X row i = e_(i mod k)
+    gives Y[i, :] = column (i mod k) of the dequantized weights, fp16-rounded."""
+    n, k = 16384, 256
+    rng = np.random.default_rng(950 + bits + m)
+    w16 = synth.edge_groups(bits, rng, n_rows=n, k=k)
+    qw, codes, s16, z = oracle_packed(w16, bits, 64)
+    what = oracle.dequantize(codes, s16, z, 64)
+    say(f"gemm lds one-hot bits={bits} m={m}")
+    cols = np.arange(m) % k
+    X = np.zeros((m, k), np.float16)
+    X[np.arange(m), cols] = 1
+    Y = host(qlin.gemm(qw, dev(X)))
+    assert np.array_equal(Y.astype(np.float64), fp16_rne(what[:, cols].T))
 
 
 def test_gemm_group_k_and_strides():
