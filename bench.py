@@ -483,7 +483,7 @@ def main():
     print(json.dumps(out), flush=True)
 
 
-TRAFFIC_SUMMARY = os.path.join(HERE, "profiles", "gemv_packed_int4_qwen25_decode_hbm_traffic.txt")
+TRAFFIC_SUMMARY = os.path.join(HERE, "profiles", "gemv_packed_int4_qwen25_decode_step_hbm_traffic.txt")
 
 
 def kernel_source_hash():
