@@ -25,6 +25,9 @@ fp16 masters ~N(0, 0.02), activations ~N(0, 1):
   fused_gemv       169 fused quantize-dequantize GEMVs from the fp16 masters
   rtn_precompute   scale/zero of all 169 masters (a change of bit width)
   quantize_pack    scale/zero and packed codes of all 169 masters
+  lm_head_int8     the tied 151936x896 table at 8 bits, g64: LM-head GEMV
+  embed_gather     the same table: one token's embedding row, dequantized to
+                   fp16 (a latency figure)
 qwen3_8b -- 36 layers of q 4096->4096, k/v 4096->1024, o 4096->4096,
 gate/up 4096->12288, down 12288->4096 (252 matrices, 3.8 GB at int4):
   q8_step_int4 / _int3 / _int2     the 252 GEMVs grouped as in decode_step:
@@ -195,6 +198,14 @@ def build_decode(torch, qlin, synth, dev, ws, phases, state):
         # X rows keep their pitch kmax; Y is packed [m, n]
         qlin.gemm(w, X[m][:, : w.k], Y[m][: m * w.n].view(m, w.n), ws=ws)
 
+    lm_idx = next(i for i, (_, nm, _, _) in enumerate(shapes) if nm == "lm_head")
+    lm8, ids, y_lm = [], None, None
+    if "lm_head_int8" in phases or "embed_gather" in phases:
+        # the tied table at 8 bits (NEXT-2 of the path): LM-head GEMV + row gather
+        lm8 = [qlin.quantize(masters[lm_idx], 8, 64) for _ in range(ROTATE)]
+        ids = torch.tensor([12345], dtype=torch.int32, device=dev)
+        y_lm = torch.empty(shapes[lm_idx][2], dtype=torch.float32, device=dev)
+
     graphs = []
     if "decode_gemv" in phases:
         graphs = capture(torch, qlin, [list(zip(packed[r], xs, ys)) for r in range(ROTATE)], ws)
@@ -229,6 +240,10 @@ def build_decode(torch, qlin, synth, dev, ws, phases, state):
         elif name == "quantize_pack":
             for w, s in zip(masters, scratch):
                 qlin.quantize(w, 4, 64, out=s)
+        elif name == "lm_head_int8":
+            qlin.gemv(lm8[r], xs[lm_idx], y_lm, ws=ws)
+        elif name == "embed_gather":
+            qlin.embed_rows(lm8[r], ids)
 
     dec_bytes = sum(wbytes(n, k, 4, 64) + 2 * k + 4 * n for (_, _, n, k) in shapes)
     master_bytes = sum(2 * n * k for (_, _, n, k) in shapes)
@@ -253,6 +268,11 @@ def build_decode(torch, qlin, synth, dev, ws, phases, state):
               "hbm", "k_quantize_g64<4> (no codes)"),
         Phase("quantize_pack", run, "GB/s", master_bytes + meta_bytes + code_bytes, 169,
               HBM_PEAK_GBS, "hbm", "k_quantize_g64<4>"),
+        Phase("lm_head_int8", run, "GB/s",
+              wbytes(shapes[lm_idx][2], shapes[lm_idx][3], 8, 64) + 2 * shapes[lm_idx][3] +
+              4 * shapes[lm_idx][2], 1, HBM_PEAK_GBS, "hbm", "k_gemv_packed<8>"),
+        Phase("embed_gather", run, "GB/s", 896 + 14 * 3 + 2 * 896 + 4, 1, HBM_PEAK_GBS, "hbm",
+              "k_embed_rows<8> (one token; latency)"),
     ]
     return [p for p in out if p.name in phases], shapes
 
@@ -387,7 +407,7 @@ def main():
     phases, decode_shapes = [], None
     if "decode" in sections:
         names = ["decode_step", "decode_gemv", "prefill_m128", "prefill_m2048", "gemm_m8", "fused_gemv",
-                 "rtn_precompute", "quantize_pack"]
+                 "rtn_precompute", "quantize_pack", "lm_head_int8", "embed_gather"]
         ps, decode_shapes = build_decode(torch, qlin, synth, dev, ws, chosen(names), state)
         phases += ps
     if "qwen3_8b" in sections:

@@ -45,6 +45,24 @@ __device__ __forceinline__ void pack_block(const float* code, uint32_t* out) {
   }
 }
 
+// Code c (0..63) of one row's 64-code block, read back from the packed words
+// (the inverse of pack_block, element by element).
+template <int BITS>
+__device__ __forceinline__ uint32_t code_at(const uint32_t* words, int c) {
+  if constexpr (BITS == 3) {
+    const int run = c >> 5, cr = c & 31;
+    const int u = cr >> 4, i = cr & 15, p = i >> 1, e = i & 1;
+    const uint32_t lo = (words[3 * run + u] >> (16 * e + 2 * p)) & 3u;
+    int hb = (p < 4 ? 2 * p + 2 : 2 * (p - 4) + 3) + 16 * e;
+    if (u == 1) hb = (hb + 8) & 31;
+    return lo | (((words[3 * run + 2] >> hb) & 1u) << 2);
+  } else {
+    constexpr int per = 32 / BITS;
+    const int w = c / per, i = c % per;
+    return (words[w] >> (16 * (i & 1) + BITS * (i >> 1))) & ((1u << BITS) - 1u);
+  }
+}
+
 // --------------------------------------------------- GEMV decode (fp16 pairs)
 // Per (lane, block): the block's sum_k x_k * (q_k - z), unscaled, in fp32.
 // Codes come out of a word scaled by S in {1, 4, 16, 64} (their bit offset in

@@ -911,6 +911,45 @@ __global__ __launch_bounds__(256) void k_gemm_tiles(
   }
 }
 
+// ------------------------------------------------- embedding-row gather --
+// Rows ids[i] of a packed weight, dequantized: out32 = s*(q - z) (exact in
+// fp32), out16 = that value rounded to fp16 (nearest even).  One work-group
+// per id; thread = 8 consecutive columns.  An id outside [0, n) gives a row of
+// zeros.
+template <int BITS>
+__global__ __launch_bounds__(256) void k_embed_rows(
+    const uint32_t* __restrict__ codes, const uint16_t* __restrict__ scale,
+    const uint8_t* __restrict__ zero, const int32_t* __restrict__ ids, int n, int kb, int G,
+    uint16_t* __restrict__ out16, float* __restrict__ out32, int64_t ld_out) {
+  constexpr int WPB = 2 * BITS;
+  const int id = ids[blockIdx.x];
+  const bool valid = id >= 0 && id < n;
+  const int r = valid ? id : 0;
+  const int t = r / kTile, rl = r % kTile;
+  for (int c8 = threadIdx.x; c8 < kb * 8; c8 += 256) {
+    const int j = c8 >> 3, c0 = (c8 & 7) * 8;
+    const uint32_t* words = codes + (((int64_t)t * kb + j) * kTile + rl) * WPB;
+    const int64_t mi = ((int64_t)t * G + ((G == 1) ? 0 : j)) * kTile + rl;
+    const float s = valid ? h2f(scale[mi]) : 0.f;
+    const int z = zero[mi];
+    float v[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = s * (float)((int)code_at<BITS>(words, c0 + e) - z);
+    const int64_t o = (int64_t)blockIdx.x * ld_out + 8 * c8;
+    if (out32 != nullptr) {
+      f32x4* d = reinterpret_cast<f32x4*>(out32 + o);
+      d[0] = (f32x4){v[0], v[1], v[2], v[3]};
+      d[1] = (f32x4){v[4], v[5], v[6], v[7]};
+    }
+    if (out16 != nullptr) {
+      f16x8 h;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) h[e] = (f16)v[e];
+      *reinterpret_cast<f16x8*>(out16 + o) = h;
+    }
+  }
+}
+
 // ------------------------------------------ tiled GEMM, LDS-DMA pipeline --
 // Same tiling and MFMA lane layout as k_gemm_tiles; the difference is how the
 // operands arrive.  Every K-block's X tile (MB x 64 fp16), the four 64-row

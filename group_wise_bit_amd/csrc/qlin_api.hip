@@ -168,7 +168,8 @@ GemvCfg gemv_config(int64_t tiles, int kb, int unroll, int64_t ws_bytes) {
   // round trips, so only long K pays).  The packed kernel keeps 16 waves per
   // work-group and splits to ~16 K-blocks per split (12 with fewer than 32
   // tiles); above 128 tiles, 8 waves and 8-block splits.  The fused kernel
-  // is ALU-heavier: 8 waves, 4 or 8 splits, and 4 x 4 from 128 tiles up.
+  // is ALU-heavier (about 7 VALU ops per weight): 8 waves and about 4 K-blocks
+  // per split (at most 8 splits), 4 waves x 4 splits above 128 tiles.
   const bool fused = unroll == kFusedUnroll;
   int waves = fused ? 8 : 16;
   int splits = 1;
@@ -178,7 +179,8 @@ GemvCfg gemv_config(int64_t tiles, int kb, int unroll, int64_t ws_bytes) {
         waves = 4;
         splits = 4;
       } else {
-        splits = kb >= 64 ? 8 : 4;
+        splits = (kb + 3) / 4;        // ~4 K-blocks per split, at most 8 splits
+        if (splits > 8) splits = 8;
       }
     } else if (tiles <= 128) {
       splits = (tiles < 32 && kb >= 64) ? kb / 12 : kb / 16;
@@ -661,6 +663,44 @@ qlin_status qlin_gemv_swiglu(const qlin_weight* gate, const qlin_weight* up, con
   L.h16 = h16;
   const GemvCfg c = swiglu_config(L.tiles, L.kb, workspace_bytes);
   return run_packed(L, gate->bits, x, workspace, c, stream);
+}
+
+qlin_status qlin_embed_rows(const qlin_weight* w, const int32_t* ids, int32_t count,
+                            uint16_t* out16, float* out32, int64_t ld_out, hipStream_t stream) {
+  qlin_status st = check_weight(w, false, false);
+  if (st != QLIN_OK) return st;
+  if (count < 0 || count > kMaxM || ld_out < w->k) return QLIN_ERR_SHAPE;
+  if (count == 0) return QLIN_OK;
+  if (ids == nullptr || (out16 == nullptr && out32 == nullptr)) return QLIN_ERR_NULL;
+  if (ld_out % 8 != 0) return QLIN_ERR_ALIGN;
+  if (!aligned16(out16) || !aligned16(out32)) return QLIN_ERR_ALIGN;
+  if ((reinterpret_cast<uintptr_t>(ids) & 3u) != 0) return QLIN_ERR_ALIGN;
+  const int64_t span = ((int64_t)(count - 1) * ld_out + w->k);
+  const Range r16 = range_of(out16, out16 != nullptr ? span * 2 : 0);
+  const Range r32 = range_of(out32, out32 != nullptr ? span * 4 : 0);
+  const Range rid = range_of(ids, (int64_t)count * 4);
+  if (overlaps(r16, r32) || overlaps(r16, rid) || overlaps(r32, rid) ||
+      output_overlaps_weight(w, r16) || output_overlaps_weight(w, r32))
+    return QLIN_ERR_ALIAS;
+  st = check_device();
+  if (st != QLIN_OK) return st;
+  const int kb = w->k / kBlock;
+  const int G = (w->group == w->k) ? 1 : kb;
+  const uint32_t* codes = static_cast<const uint32_t*>(w->data);
+  switch (w->bits) {
+#define QLIN_EMBED(B)                                                                         \
+    case B:                                                                                   \
+      hipLaunchKernelGGL((k_embed_rows<B>), dim3(count), dim3(256), 0, stream, codes, w->scale, \
+                         w->zero, ids, w->n, kb, G, out16, out32, ld_out);                    \
+      break;
+    QLIN_EMBED(2)
+    QLIN_EMBED(3)
+    QLIN_EMBED(4)
+    QLIN_EMBED(8)
+#undef QLIN_EMBED
+    default: return QLIN_ERR_BITS;
+  }
+  return hip_status(hipGetLastError());
 }
 
 qlin_status qlin_gemm(const qlin_weight* w, const uint16_t* X, int32_t m, int64_t ld_x, float* Y,

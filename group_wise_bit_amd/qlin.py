@@ -31,7 +31,7 @@ EXPORTS = (
     "qlin_meta_entries", "qlin_quantize", "qlin_gemv_workspace_bytes",
     "qlin_gemm_workspace_bytes", "qlin_gemv", "qlin_gemm",
     "qlin_gemv_multi_workspace_bytes", "qlin_gemv_multi",
-    "qlin_gemv_swiglu_workspace_bytes", "qlin_gemv_swiglu",
+    "qlin_gemv_swiglu_workspace_bytes", "qlin_gemv_swiglu", "qlin_embed_rows",
 )
 
 
@@ -94,6 +94,8 @@ def _lib() -> ctypes.CDLL:
         lib.qlin_gemv_swiglu_workspace_bytes.restype = i64
         lib.qlin_gemv_swiglu.argtypes = [wp, wp, vp, vp, vp, vp, i64, vp]
         lib.qlin_gemv_swiglu.restype = ctypes.c_int
+        lib.qlin_embed_rows.argtypes = [wp, vp, i32, vp, vp, i64, vp]
+        lib.qlin_embed_rows.restype = ctypes.c_int
         _LIB = lib
     return _LIB
 
@@ -275,3 +277,18 @@ def gemv_swiglu(gate: QWeight, up: QWeight, x: torch.Tensor,
                                  _ptr(h16), _ptr(ws), wsb, _stream())
     _check(st, "qlin_gemv_swiglu")
     return h, h16
+
+
+def embed_rows(w: QWeight, ids: torch.Tensor, want16: bool = True, want32: bool = False
+               ) -> Tuple[Optional[torch.Tensor], Optional[torch.Tensor]]:
+    """qlin_embed_rows: dequantized rows ids of a packed weight, fp16 and/or fp32 [len(ids), k]."""
+    if ids.dtype != torch.int32 or ids.dim() != 1 or not ids.is_contiguous():
+        raise TypeError("ids must be a contiguous 1-D int32 tensor")
+    count = ids.numel()
+    out16 = torch.empty(count, w.k, dtype=torch.float16, device=ids.device) if want16 else None
+    out32 = torch.empty(count, w.k, dtype=torch.float32, device=ids.device) if want32 else None
+    ws_struct = w.c_struct()
+    st = _lib().qlin_embed_rows(ctypes.byref(ws_struct), ids.data_ptr(), count, _ptr(out16),
+                                _ptr(out32), w.k, _stream())
+    _check(st, "qlin_embed_rows")
+    return out16, out32

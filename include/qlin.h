@@ -204,6 +204,21 @@ qlin_status qlin_gemv_swiglu(const qlin_weight* gate, const qlin_weight* up, con
                              float* h, uint16_t* h16, void* workspace, int64_t workspace_bytes,
                              hipStream_t stream);
 
+/*
+ * Embedding-row gather from a packed weight (the Enargeia page, "Run it": the
+ * tied token-embedding table, stored at 8 bits, serves both the input lookup
+ * and the LM-head GEMV):
+ *     out[i, :] = s(q - z) of row ids[i],   i = 0 .. count-1,
+ * out32 exact in fp32, out16 the same values rounded to fp16 (nearest even:
+ * ready as the first layer's input).  Either output may be NULL, not both;
+ * both are [count, ld_out] row-major, ld_out >= k and a multiple of 8.
+ * ids: int32 device array, 4-byte aligned.  An id outside [0, n) yields a row
+ * of zeros (ids are not read on the host).  count = 0 is a no-op.
+ * PACKED weights only (QLIN_ERR_FORMAT otherwise).
+ */
+qlin_status qlin_embed_rows(const qlin_weight* w, const int32_t* ids, int32_t count,
+                            uint16_t* out16, float* out32, int64_t ld_out, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -31,7 +31,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     declared = header_functions()
-    assert len(declared) == 14
+    assert len(declared) == 15
     assert sorted(qlin.EXPORTS) == declared
     for name in declared:
         assert hasattr(lib, name), name
@@ -198,8 +198,30 @@ def test_gemv_swiglu_validation(lib):
     assert swiglu(lib, g, u, h16=Y1 + 2) == ALIGN
 
 
+def embed(lib, w, ids=FAKE + (3 << 30), count=4, o16=Y0, o32=Y1, ld=128):
+    return lib.qlin_embed_rows(ctypes.byref(w), ids, count, o16, o32, ld, None)
+
+
+def test_embed_rows_validation(lib):
+    assert lib.qlin_embed_rows(None, FAKE, 1, Y0, None, 128, None) == NULL
+    assert embed(lib, weight(), count=0) == OK                  # nothing to do, no device needed
+    assert embed(lib, weight(), ids=None) == NULL
+    assert embed(lib, weight(), o16=None, o32=None) == NULL
+    assert embed(lib, weight(), count=-1) == SHAPE
+    assert embed(lib, weight(), ld=64) == SHAPE
+    assert embed(lib, weight(), ld=132) == ALIGN
+    assert embed(lib, weight(), o16=Y0 + 2) == ALIGN
+    assert embed(lib, weight(), ids=FAKE + (3 << 30) + 2) == ALIGN
+    assert embed(lib, weight(format=1, ld=128)) == FORMAT
+    assert embed(lib, weight(bits=16)) == BITS
+    assert embed(lib, weight(), o32=Y0 + 64) == ALIAS            # outputs overlap
+    assert embed(lib, weight(), o16=FAKE + 16) == ALIAS          # output on the codes
+    assert embed(lib, weight(), o32=FAKE + (3 << 30)) == ALIAS   # output on the ids
+
+
 @pytest.mark.skipif(torch.cuda.is_available(), reason="checks the no-GPU path")
 def test_no_device(lib):
+    assert embed(lib, weight()) == NODEV
     assert quant(lib) == NODEV
     assert gemv(lib, weight()) == NODEV
     assert gemm(lib, weight()) == NODEV
