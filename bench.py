@@ -23,8 +23,9 @@ fp16 masters ~N(0, 0.02), activations ~N(0, 1):
   prefill_m2048    the same at M = 2048
   gemm_m8          169 GEMMs at M = 8
   fused_gemv       169 fused quantize-dequantize GEMVs from the fp16 masters
-  rtn_precompute   scale/zero of all 169 masters (a change of bit width)
-  quantize_pack    scale/zero and packed codes of all 169 masters
+  rtn_precompute   scale/zero of all 169 masters (a change of bit width),
+                   batched: 64 matrices per launch
+  quantize_pack    scale/zero and packed codes of all 169 masters, batched
   lm_head_int8     the tied 151936x896 table at 8 bits, g64: LM-head GEMV
   embed_gather     the same table: one token's embedding row, dequantized to
                    fp16 (a latency figure)
@@ -38,7 +39,8 @@ gate/up 4096->12288, down 12288->4096 (252 matrices, 3.8 GB at int4):
 qwen3_06b -- the 196 fp16 masters of Qwen3-0.6B (28 layers of q 1024->2048,
 k/v 1024->1024, o 2048->1024, gate/up 1024->3072, down 3072->1024):
   q06_fused_b{8,4,3,2}_{g64,row}   196 fused GEMVs after a lever move
-  q06_lever_b{8,4,3,2}_{g64,row}   scale/zero precompute of the 196 masters
+  q06_lever_b{8,4,3,2}_{g64,row}   a lever move: scale/zero of the 196 masters,
+                                   64 per launch
   q06_fp16_control                 196 plain fp16 GEMVs (bits = 16)
 
 `value` is decode_step's weight-stream rate: algorithmic bytes (packed codes,
@@ -112,6 +114,7 @@ def capture(torch, qlin, call_lists, ws):
         with torch.cuda.graph(g, stream=stream):
             for w, x, y in calls:
                 qlin.gemv(w, x, y, ws=ws)
+        g.keepalive = calls           # the tensors the graph's kernels address
         graphs.append(g)
     torch.cuda.synchronize()
     return graphs
@@ -131,6 +134,11 @@ def capture_calls(torch, call_lists):
         with torch.cuda.graph(g, stream=stream):
             for f in calls:
                 f()
+        # The launch functions hold (as default arguments and closures) every
+        # tensor the graph's kernels address.  They must outlive the graph:
+        # each later capture empties torch's cache, so a tensor freed here
+        # would be returned to the driver and a replay would fault.
+        g.keepalive = calls
         graphs.append(g)
     torch.cuda.synchronize()
     return graphs
@@ -218,32 +226,45 @@ def build_decode(torch, qlin, synth, dev, ws, phases, state):
             lists.append(calls)
         grouped = capture_calls(torch, lists)
 
+    # Every other stage is one HIP graph per weight rotation as well, so the
+    # timed region holds the GPU work only (no per-launch host overhead).
+    def per_rotation(make):
+        return capture_calls(torch, [make(r) for r in range(ROTATE)])
+
+    staged = {}
+    for m in (128, 2048):
+        if f"prefill_m{m}" in phases:
+            staged[f"prefill_m{m}"] = per_rotation(
+                lambda r, m=m: [lambda w=packed[r][i], m=m: gemm(w, m) for i in layer_idx])
+    if "gemm_m8" in phases:
+        staged["gemm_m8"] = per_rotation(lambda r: [lambda w=w: gemm(w, 8) for w in packed[r]])
+    if "fused_gemv" in phases:
+        staged["fused_gemv"] = capture_calls(torch, [[
+            lambda w=w, x=x, y=y: qlin.gemv(w, x, y, ws=ws) for w, x, y in zip(fused, xs, ys)]])
+    if "rtn_precompute" in phases:
+        staged["rtn_precompute"] = capture_calls(torch, [[
+            lambda: qlin.quantize_batch(masters, 4, 64, codes=False, outs=meta)]])
+    if "quantize_pack" in phases:
+        staged["quantize_pack"] = capture_calls(torch, [[
+            lambda: qlin.quantize_batch(masters, 4, 64, outs=scratch)]])
+    if "lm_head_int8" in phases:
+        staged["lm_head_int8"] = per_rotation(
+            lambda r: [lambda w=lm8[r]: qlin.gemv(w, xs[lm_idx], y_lm, ws=ws)])
+    if "embed_gather" in phases:
+        staged["embed_gather"] = per_rotation(lambda r: [lambda w=lm8[r]: qlin.embed_rows(w, ids)])
+
+    hold = (masters, xs, ys, packed, scratch, meta, fused, X, Y, lm8, ids, y_lm)
+
     def run(name):
+        assert hold is not None       # every buffer the graphs address stays alive
         r = state["step"] % ROTATE
         if name == "decode_gemv":
             graphs[r].replay()
         elif name == "decode_step":
             grouped[r].replay()
-        elif name in ("prefill_m128", "prefill_m2048"):
-            m = 128 if name == "prefill_m128" else 2048
-            for i in layer_idx:
-                gemm(packed[r][i], m)
-        elif name == "gemm_m8":
-            for w in packed[r]:
-                gemm(w, 8)
-        elif name == "fused_gemv":
-            for w, x, y in zip(fused, xs, ys):
-                qlin.gemv(w, x, y, ws=ws)
-        elif name == "rtn_precompute":
-            for w, m in zip(masters, meta):
-                qlin.quantize(w, 4, 64, codes=False, out=m)
-        elif name == "quantize_pack":
-            for w, s in zip(masters, scratch):
-                qlin.quantize(w, 4, 64, out=s)
-        elif name == "lm_head_int8":
-            qlin.gemv(lm8[r], xs[lm_idx], y_lm, ws=ws)
-        elif name == "embed_gather":
-            qlin.embed_rows(lm8[r], ids)
+        else:
+            g = staged[name]
+            g[r % len(g)].replay()
 
     dec_bytes = sum(wbytes(n, k, 4, 64) + 2 * k + 4 * n for (_, _, n, k) in shapes)
     master_bytes = sum(2 * n * k for (_, _, n, k) in shapes)
@@ -264,10 +285,10 @@ def build_decode(torch, qlin, synth, dev, ws, phases, state):
         Phase("fused_gemv", run, "GB/s",
               master_bytes + meta_bytes + sum(2 * k + 4 * n for (_, _, n, k) in shapes), 169,
               HBM_PEAK_GBS, "hbm", "k_gemv_fused<4>"),
-        Phase("rtn_precompute", run, "GB/s", master_bytes + meta_bytes, 169, HBM_PEAK_GBS,
-              "hbm", "k_quantize_g64<4> (no codes)"),
-        Phase("quantize_pack", run, "GB/s", master_bytes + meta_bytes + code_bytes, 169,
-              HBM_PEAK_GBS, "hbm", "k_quantize_g64<4>"),
+        Phase("rtn_precompute", run, "GB/s", master_bytes + meta_bytes, 3, HBM_PEAK_GBS,
+              "hbm", "k_quantize_g64<4> (no codes; 169 matrices in 3 launches)"),
+        Phase("quantize_pack", run, "GB/s", master_bytes + meta_bytes + code_bytes, 3,
+              HBM_PEAK_GBS, "hbm", "k_quantize_g64<4> (169 matrices in 3 launches)"),
         Phase("lm_head_int8", run, "GB/s",
               wbytes(shapes[lm_idx][2], shapes[lm_idx][3], 8, 64) + 2 * shapes[lm_idx][3] +
               4 * shapes[lm_idx][2], 1, HBM_PEAK_GBS, "hbm", "k_gemv_packed<8>"),
@@ -308,16 +329,25 @@ def build_qwen3_8b(torch, qlin, synth, dev, ws, phases):
                                                          ws, bits=b)
             steps[b] = capture_calls(torch, [calls])[0]
 
+    gemms = {}
+    for b in (4, 3):
+        for m in (8, 128):
+            if f"q8_m{m}_int{b}" in phases:
+                gemms[(b, m)] = capture_calls(torch, [[
+                    lambda w=w, m=m: qlin.gemm(w, X[m][:, : w.k], Y[m][: m * w.n].view(m, w.n),
+                                               ws=ws) for w in packed[b]]])[0]
+
+    hold = (packed, xs, ys, X, Y)
+
     def run(name):
+        assert hold is not None       # every buffer the graphs address stays alive
         b = int(name[-1])
         if "step" in name:
             steps[b].replay()
         elif "decode" in name:
             graphs[b].replay()
         else:
-            m = 8 if "_m8_" in name else 128
-            for w in packed[b]:
-                qlin.gemm(w, X[m][:, : w.k], Y[m][: m * w.n].view(m, w.n), ws=ws)
+            gemms[(b, 8 if "_m8_" in name else 128)].replay()
 
     out = []
     for b in (4, 3, 2):
@@ -351,19 +381,27 @@ def build_qwen3_06b(torch, qlin, synth, dev, ws, phases):
     control = [qlin.master_weight(w, 16, 64) for w in masters]
     torch.cuda.synchronize()
 
+    def gemvs(ws_list):
+        return [lambda w=w, x=x, y=y: qlin.gemv(w, x, y, ws=ws) for w, x, y in zip(ws_list, xs, ys)]
+
+    staged = {}
+    if "q06_fp16_control" in phases:
+        staged["q06_fp16_control"] = capture_calls(torch, [gemvs(control)])[0]
+    for c in combos:
+        tag = f"b{c[0]}_{c[1]}"
+        if f"q06_fused_{tag}" in phases:
+            staged[f"q06_fused_{tag}"] = capture_calls(torch, [gemvs(fused[c])])[0]
+        if f"q06_lever_{tag}" in phases:
+            # a lever move: all 196 masters re-quantized, 64 per launch
+            staged[f"q06_lever_{tag}"] = capture_calls(torch, [[
+                lambda c=c: qlin.quantize_batch(masters, c[0], 64 if c[1] == "g64" else "K",
+                                                codes=False, outs=meta[c])]])[0]
+
+    hold = (masters, xs, ys, meta, fused, control)
+
     def run(name):
-        if name == "q06_fp16_control":
-            for w, x, y in zip(control, xs, ys):
-                qlin.gemv(w, x, y, ws=ws)
-            return
-        parts = name.split("_")
-        c = (int(parts[2][1:]), parts[3])
-        if parts[1] == "lever":
-            for w, m in zip(masters, meta[c]):
-                qlin.quantize(w, c[0], 64 if c[1] == "g64" else "K", codes=False, out=m)
-        else:
-            for w, x, y in zip(fused[c], xs, ys):
-                qlin.gemv(w, x, y, ws=ws)
+        assert hold is not None       # every buffer the graphs address stays alive
+        staged[name].replay()
 
     master_bytes = sum(2 * n * k for (_, _, n, k) in shapes)
     act = sum(2 * k + 4 * n for (_, _, n, k) in shapes)
@@ -372,7 +410,7 @@ def build_qwen3_06b(torch, qlin, synth, dev, ws, phases):
         mb = sum(n * (k // (64 if gr == "g64" else k)) * 3 for (_, _, n, k) in shapes)
         out.append(Phase(f"q06_fused_b{b}_{gr}", run, "GB/s", master_bytes + mb + act, 196,
                          HBM_PEAK_GBS, "hbm", f"k_gemv_fused<{b}>"))
-        out.append(Phase(f"q06_lever_b{b}_{gr}", run, "GB/s", master_bytes + mb, 196,
+        out.append(Phase(f"q06_lever_b{b}_{gr}", run, "GB/s", master_bytes + mb, 4,
                          HBM_PEAK_GBS, "hbm",
                          f"k_quantize_{'g64' if gr == 'g64' else 'row'}<{b}> (no codes)"))
     out.append(Phase("q06_fp16_control", run, "GB/s", master_bytes + act, 196, HBM_PEAK_GBS,

@@ -6,5 +6,5 @@ include/qlin.h); this package is its Python binding.
 from .qlin import (  # noqa: F401
     FMT_FP16_MASTER, FMT_PACKED, EXPORTS, LIB_PATH, QWeight, QlinError, embed_rows, gemm, gemv,
     gemv_multi, gemv_swiglu, library, master_weight, meta_entries, packed_bytes, quantize,
-    workspace,
+    quantize_batch, workspace,
 )

@@ -75,58 +75,88 @@ __device__ __forceinline__ void codes_and_store(const float* w, float s, int z,
 }
 
 // ------------------------------------------------------------- quantizer --
-// Group 64.  grid = (tiles, ceil(kb / WAVES)); wave w of block y handles
-// K-block j = y*WAVES + w for the 64 rows of tile x.
+// A launch quantizes a batch of up to kQuantBatch matrices (one bit width and
+// group kind): the jobs travel in the kernel arguments, work items are
+// numbered consecutively over the jobs (end[i] = items of jobs 0..i), and
+// each work-group finds its job by a scan over the ends.
+constexpr int kQuantBatch = 64;
+struct QuantJob {
+  const uint16_t* w16;
+  int64_t ld;
+  uint32_t* codes;       // null: scale/zero only
+  uint16_t* scale;
+  uint8_t* zero;
+  int n, kb;
+};
+struct QuantBatch {
+  QuantJob job[kQuantBatch];
+  int end[kQuantBatch];
+  int count;
+};
+
+__device__ __forceinline__ int quant_job_of(const QuantBatch& b, int item, int& first) {
+  int ji = 0;
+  for (int i = 0; i + 1 < b.count; ++i)
+    if (item >= b.end[i]) ji = i + 1;
+  first = ji == 0 ? 0 : b.end[ji - 1];
+  return ji;
+}
+
+// Group 64.  Work item = (tile, y) of a job, y = ceil(kb / WAVES) per tile;
+// wave w handles K-block j = y*WAVES + w for the 64 rows of the tile.
 template <int BITS, int WAVES>
-__global__ __launch_bounds__(WAVES * 64) void k_quantize_g64(
-    const uint16_t* __restrict__ w16, int64_t ld, int n, int kb,
-    uint32_t* __restrict__ codes, uint16_t* __restrict__ scale, uint8_t* __restrict__ zero) {
+__global__ __launch_bounds__(WAVES * 64) void k_quantize_g64(const QuantBatch b) {
   constexpr int qmax = (1 << BITS) - 1;
   const int lane = lane_id(), wave = wave_id();
-  const int t = blockIdx.x;
-  const int j = blockIdx.y * WAVES + wave;
-  if (j >= kb) return;
+  int first;
+  const QuantJob& q = b.job[quant_job_of(b, blockIdx.x, first)];
+  const int ny = (q.kb + WAVES - 1) / WAVES;
+  const int item = blockIdx.x - first;
+  const int t = item / ny;
+  const int j = (item % ny) * WAVES + wave;
+  if (j >= q.kb) return;
   const int row = t * kTile + lane;
   float w[64];
-  load_row_block(w16, ld, row, j, row < n, w);
+  load_row_block(q.w16, q.ld, row, j, row < q.n, w);
   float mn = w[0], mx = w[0];
 #pragma unroll
   for (int i = 1; i < 64; ++i) { mn = __builtin_fminf(mn, w[i]); mx = __builtin_fmaxf(mx, w[i]); }
   uint16_t sb; float s; int z;
   scale_zero(mn, mx, qmax, sb, s, z);
-  const int64_t mi = ((int64_t)t * kb + j) * kTile + lane;
-  scale[mi] = sb;
-  zero[mi] = (uint8_t)z;
-  if (codes != nullptr)
-    codes_and_store<BITS>(w, s, z, codes + mi * (2 * BITS));
+  const int64_t mi = ((int64_t)t * q.kb + j) * kTile + lane;
+  q.scale[mi] = sb;
+  q.zero[mi] = (uint8_t)z;
+  if (q.codes != nullptr)
+    codes_and_store<BITS>(w, s, z, q.codes + mi * (2 * BITS));
 }
 
-// One group per row.  grid = tiles; the WAVES waves split the K-blocks, the
-// row extremes are combined through LDS, then each wave writes its blocks.
+// One group per row.  Work item = tile; the WAVES waves split the K-blocks,
+// the row extremes are combined through LDS, then each wave writes its blocks.
 template <int BITS, int WAVES>
-__global__ __launch_bounds__(WAVES * 64) void k_quantize_row(
-    const uint16_t* __restrict__ w16, int64_t ld, int n, int kb,
-    uint32_t* __restrict__ codes, uint16_t* __restrict__ scale, uint8_t* __restrict__ zero) {
+__global__ __launch_bounds__(WAVES * 64) void k_quantize_row(const QuantBatch b) {
   constexpr int qmax = (1 << BITS) - 1;
   __shared__ float smn[WAVES][64], smx[WAVES][64];
   const int lane = lane_id(), wave = wave_id();
-  const int t = blockIdx.x;
+  int first;
+  const QuantJob& q = b.job[quant_job_of(b, blockIdx.x, first)];
+  const int t = blockIdx.x - first;
+  const int kb = q.kb;
   const int row = t * kTile + lane;
-  const bool valid = row < n;
+  const bool valid = row < q.n;
   float mn = 0.f, mx = 0.f;
-  bool first = true;
+  bool empty = true;
   for (int j = wave; j < kb; j += WAVES) {
     float w[64];
-    load_row_block(w16, ld, row, j, valid, w);
+    load_row_block(q.w16, q.ld, row, j, valid, w);
 #pragma unroll
     for (int i = 0; i < 64; ++i) {
-      mn = first ? w[i] : __builtin_fminf(mn, w[i]);
-      mx = first ? w[i] : __builtin_fmaxf(mx, w[i]);
-      first = false;
+      mn = empty ? w[i] : __builtin_fminf(mn, w[i]);
+      mx = empty ? w[i] : __builtin_fmaxf(mx, w[i]);
+      empty = false;
     }
   }
-  smn[wave][lane] = first ? __builtin_inff() : mn;
-  smx[wave][lane] = first ? -__builtin_inff() : mx;
+  smn[wave][lane] = empty ? __builtin_inff() : mn;
+  smx[wave][lane] = empty ? -__builtin_inff() : mx;
   __syncthreads();
   mn = smn[0][lane]; mx = smx[0][lane];
 #pragma unroll
@@ -134,15 +164,15 @@ __global__ __launch_bounds__(WAVES * 64) void k_quantize_row(
   uint16_t sb; float s; int z;
   scale_zero(mn, mx, qmax, sb, s, z);
   if (wave == 0) {
-    scale[(int64_t)t * kTile + lane] = sb;
-    zero[(int64_t)t * kTile + lane] = (uint8_t)z;
+    q.scale[(int64_t)t * kTile + lane] = sb;
+    q.zero[(int64_t)t * kTile + lane] = (uint8_t)z;
   }
-  if (codes == nullptr) return;
+  if (q.codes == nullptr) return;
   for (int j = wave; j < kb; j += WAVES) {
     float w[64];
-    load_row_block(w16, ld, row, j, valid, w);
+    load_row_block(q.w16, q.ld, row, j, valid, w);
     const int64_t bi = ((int64_t)t * kb + j) * kTile + lane;
-    codes_and_store<BITS>(w, s, z, codes + bi * (2 * BITS));
+    codes_and_store<BITS>(w, s, z, q.codes + bi * (2 * BITS));
   }
 }
 

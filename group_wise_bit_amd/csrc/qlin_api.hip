@@ -7,6 +7,8 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <vector>
+
 #include "../../include/qlin.h"
 #include "kernels.h"
 
@@ -217,19 +219,63 @@ int64_t gemv_ws_bytes(int64_t tiles, int kb, int unroll) {
 }
 
 
+// One launch per kQuantBatch jobs (same bits, same group kind).
 template <int B>
-void launch_quant(const uint16_t* w16, int64_t ld, int n, int k, int group, uint32_t* codes,
-                  uint16_t* scale, uint8_t* zero, hipStream_t st) {
-  const int kb = k / kBlock;
-  const int tiles = (int)tiles_of(n);
-  if (group == kBlock) {
-    dim3 grid(tiles, (kb + kWaves - 1) / kWaves);
-    hipLaunchKernelGGL((k_quantize_g64<B, kWaves>), grid, dim3(kWaves * 64), 0, st,
-                       w16, ld, n, kb, codes, scale, zero);
-  } else {
-    hipLaunchKernelGGL((k_quantize_row<B, kWaves>), dim3(tiles), dim3(kWaves * 64), 0, st,
-                       w16, ld, n, kb, codes, scale, zero);
+void launch_quant_batch(const QuantJob* jobs, int count, bool row, hipStream_t st) {
+  for (int c0 = 0; c0 < count; c0 += kQuantBatch) {
+    QuantBatch qb;
+    qb.count = count - c0 < kQuantBatch ? count - c0 : kQuantBatch;
+    int items = 0;
+    for (int i = 0; i < qb.count; ++i) {
+      qb.job[i] = jobs[c0 + i];
+      const int tiles = (int)tiles_of(qb.job[i].n);
+      items += row ? tiles : tiles * ((qb.job[i].kb + kWaves - 1) / kWaves);
+      qb.end[i] = items;
+    }
+    for (int i = qb.count; i < kQuantBatch; ++i) qb.end[i] = items;
+    if (row)
+      hipLaunchKernelGGL((k_quantize_row<B, kWaves>), dim3(items), dim3(kWaves * 64), 0, st, qb);
+    else
+      hipLaunchKernelGGL((k_quantize_g64<B, kWaves>), dim3(items), dim3(kWaves * 64), 0, st, qb);
   }
+}
+
+qlin_status run_quant(const QuantJob* jobs, int count, int bits, bool row, hipStream_t st) {
+  switch (bits) {
+    case 2: launch_quant_batch<2>(jobs, count, row, st); break;
+    case 3: launch_quant_batch<3>(jobs, count, row, st); break;
+    case 4: launch_quant_batch<4>(jobs, count, row, st); break;
+    default: launch_quant_batch<8>(jobs, count, row, st); break;
+  }
+  return hip_status(hipGetLastError());
+}
+
+// Host checks of one quantization job; the ranges it reads and writes.
+struct QuantRanges { Range in, codes, scale, zero; };
+
+qlin_status check_quant_job(const uint16_t* w16, int64_t ld_w, int32_t n, int32_t k, int32_t bits,
+                            int32_t group, const uint32_t* codes, const uint16_t* scale,
+                            const uint8_t* zero, QuantRanges& r) {
+  qlin_status st = check_nk(n, k);
+  if (st != QLIN_OK) return st;
+  if (!valid_bits(bits)) return QLIN_ERR_BITS;
+  st = check_group(group, k);
+  if (st != QLIN_OK) return st;
+  if (w16 == nullptr || scale == nullptr || zero == nullptr) return QLIN_ERR_NULL;
+  if (ld_w < k) return QLIN_ERR_SHAPE;
+  if (ld_w % 8 != 0) return QLIN_ERR_ALIGN;
+  if (!aligned16(w16) || !aligned16(scale) || !aligned16(zero) ||
+      (codes != nullptr && !aligned16(codes)))
+    return QLIN_ERR_ALIGN;
+  r.in = range_of(w16, ((int64_t)(n - 1) * ld_w + k) * 2);
+  const int64_t me = meta_entries(n, k, group);
+  r.scale = range_of(scale, me * 2);
+  r.zero = range_of(zero, me);
+  r.codes = range_of(codes, codes != nullptr ? packed_bytes(n, k, bits) : 0);
+  if (overlaps(r.in, r.scale) || overlaps(r.in, r.zero) || overlaps(r.scale, r.zero) ||
+      overlaps(r.codes, r.in) || overlaps(r.codes, r.scale) || overlaps(r.codes, r.zero))
+    return QLIN_ERR_ALIAS;
+  return QLIN_OK;
 }
 
 // Packed GEMV launch over a set of matrices (shared K, bits, group).
@@ -520,34 +566,43 @@ int64_t qlin_meta_entries(int32_t n, int32_t k, int32_t group) {
 qlin_status qlin_quantize(const uint16_t* w16, int64_t ld_w, int32_t n, int32_t k, int32_t bits,
                           int32_t group, uint32_t* codes, uint16_t* scale, uint8_t* zero,
                           hipStream_t stream) {
-  qlin_status st = check_nk(n, k);
+  QuantRanges r;
+  qlin_status st = check_quant_job(w16, ld_w, n, k, bits, group, codes, scale, zero, r);
   if (st != QLIN_OK) return st;
-  if (!valid_bits(bits)) return QLIN_ERR_BITS;
-  st = check_group(group, k);
-  if (st != QLIN_OK) return st;
-  if (w16 == nullptr || scale == nullptr || zero == nullptr) return QLIN_ERR_NULL;
-  if (ld_w < k) return QLIN_ERR_SHAPE;
-  if (ld_w % 8 != 0) return QLIN_ERR_ALIGN;
-  if (!aligned16(w16) || !aligned16(scale) || !aligned16(zero) ||
-      (codes != nullptr && !aligned16(codes)))
-    return QLIN_ERR_ALIGN;
-  const Range in = range_of(w16, ((int64_t)(n - 1) * ld_w + k) * 2);
-  const int64_t me = meta_entries(n, k, group);
-  const Range rs = range_of(scale, me * 2), rz = range_of(zero, me);
-  if (overlaps(in, rs) || overlaps(in, rz) || overlaps(rs, rz)) return QLIN_ERR_ALIAS;
-  if (codes != nullptr) {
-    const Range rc = range_of(codes, packed_bytes(n, k, bits));
-    if (overlaps(rc, in) || overlaps(rc, rs) || overlaps(rc, rz)) return QLIN_ERR_ALIAS;
-  }
   st = check_device();
   if (st != QLIN_OK) return st;
-  switch (bits) {
-    case 2: launch_quant<2>(w16, ld_w, n, k, group, codes, scale, zero, stream); break;
-    case 3: launch_quant<3>(w16, ld_w, n, k, group, codes, scale, zero, stream); break;
-    case 4: launch_quant<4>(w16, ld_w, n, k, group, codes, scale, zero, stream); break;
-    default: launch_quant<8>(w16, ld_w, n, k, group, codes, scale, zero, stream); break;
+  const QuantJob job{w16, ld_w, codes, scale, zero, n, k / kBlock};
+  return run_quant(&job, 1, bits, group != kBlock, stream);
+}
+
+qlin_status qlin_quantize_batch(const qlin_quant_job* jobs, int32_t count, int32_t bits,
+                                int32_t group, hipStream_t stream) {
+  if (count < 0) return QLIN_ERR_SHAPE;
+  if (count == 0) return QLIN_OK;
+  if (jobs == nullptr) return QLIN_ERR_NULL;
+  if (group != kBlock && group != 0) return QLIN_ERR_GROUP;
+  std::vector<QuantRanges> rs((size_t)count);
+  std::vector<QuantJob> qj((size_t)count);
+  for (int i = 0; i < count; ++i) {
+    const qlin_quant_job& j = jobs[i];
+    qlin_status st = check_quant_job(j.w16, j.ld_w, j.n, j.k, bits, group == 0 ? j.k : kBlock,
+                                     j.codes, j.scale, j.zero, rs[(size_t)i]);
+    if (st != QLIN_OK) return st;
+    qj[(size_t)i] = QuantJob{j.w16, j.ld_w, j.codes, j.scale, j.zero, j.n, j.k / kBlock};
   }
-  return hip_status(hipGetLastError());
+  // no job's outputs may overlap another job's inputs or outputs
+  for (int i = 0; i < count; ++i)
+    for (int j = 0; j < count; ++j) {
+      if (i == j) continue;
+      const QuantRanges& a = rs[(size_t)i];
+      const QuantRanges& b = rs[(size_t)j];
+      for (const Range& o : {a.codes, a.scale, a.zero})
+        if (overlaps(o, b.in) || overlaps(o, b.codes) || overlaps(o, b.scale) || overlaps(o, b.zero))
+          return QLIN_ERR_ALIAS;
+    }
+  qlin_status st = check_device();
+  if (st != QLIN_OK) return st;
+  return run_quant(qj.data(), count, bits, group == 0, stream);
 }
 
 int64_t qlin_gemv_workspace_bytes(const qlin_weight* w) {

@@ -32,6 +32,7 @@ EXPORTS = (
     "qlin_gemm_workspace_bytes", "qlin_gemv", "qlin_gemm",
     "qlin_gemv_multi_workspace_bytes", "qlin_gemv_multi",
     "qlin_gemv_swiglu_workspace_bytes", "qlin_gemv_swiglu", "qlin_embed_rows",
+    "qlin_quantize_batch",
 )
 
 
@@ -51,6 +52,14 @@ class QlinWeightC(ctypes.Structure):
         ("group", ctypes.c_int32), ("format", ctypes.c_int32), ("reserved", ctypes.c_int32),
         ("data", ctypes.c_void_p), ("ld", ctypes.c_int64),
         ("scale", ctypes.c_void_p), ("zero", ctypes.c_void_p),
+    ]
+
+
+class QlinQuantJobC(ctypes.Structure):
+    _fields_ = [
+        ("w16", ctypes.c_void_p), ("ld_w", ctypes.c_int64), ("n", ctypes.c_int32),
+        ("k", ctypes.c_int32), ("codes", ctypes.c_void_p), ("scale", ctypes.c_void_p),
+        ("zero", ctypes.c_void_p),
     ]
 
 
@@ -96,6 +105,8 @@ def _lib() -> ctypes.CDLL:
         lib.qlin_gemv_swiglu.restype = ctypes.c_int
         lib.qlin_embed_rows.argtypes = [wp, vp, i32, vp, vp, i64, vp]
         lib.qlin_embed_rows.restype = ctypes.c_int
+        lib.qlin_quantize_batch.argtypes = [ctypes.POINTER(QlinQuantJobC), i32, i32, i32, vp]
+        lib.qlin_quantize_batch.restype = ctypes.c_int
         _LIB = lib
     return _LIB
 
@@ -292,3 +303,36 @@ def embed_rows(w: QWeight, ids: torch.Tensor, want16: bool = True, want32: bool 
                                 _ptr(out32), w.k, _stream())
     _check(st, "qlin_embed_rows")
     return out16, out32
+
+
+def quantize_batch(masters: Sequence[torch.Tensor], bits: int, group, codes: bool = True,
+                   outs: Optional[Sequence[QWeight]] = None) -> List[QWeight]:
+    """qlin_quantize_batch: every cuda fp16 [n, k] master quantized at one bit
+    width, group 64 or "K" (per row), one launch per 64 matrices.  outs: the
+    QWeights of an earlier call to overwrite (scale/zero, and codes)."""
+    row = group in ("k", "K")
+    if not row and int(group) != 64:
+        raise ValueError("group must be 64 or 'K'")
+    res, jobs = [], []
+    for i, w16 in enumerate(masters):
+        if w16.dtype != torch.float16 or w16.dim() != 2 or not w16.is_cuda or w16.stride(1) != 1:
+            raise TypeError("masters must be 2-D cuda float16 tensors with contiguous rows")
+        n, k = w16.shape
+        g = k if row else 64
+        if outs is not None:
+            o = outs[i]
+            scale, zero, cbuf = o.scale, o.zero, (o.data if codes else None)
+        else:
+            me = meta_entries(n, k, g)
+            scale = torch.empty(max(me, 1), dtype=torch.float16, device=w16.device)
+            zero = torch.empty(max(me, 1), dtype=torch.uint8, device=w16.device)
+            cbuf = (torch.empty(max(packed_bytes(n, k, bits) // 4, 1), dtype=torch.int32,
+                                device=w16.device) if codes else None)
+        jobs.append(QlinQuantJobC(w16.data_ptr(), w16.stride(0), n, k, _ptr(cbuf),
+                                  scale.data_ptr(), zero.data_ptr()))
+        res.append(QWeight(n, k, bits, g, FMT_PACKED, cbuf, scale, zero) if codes else
+                   QWeight(n, k, bits, g, FMT_FP16_MASTER, w16, scale, zero, ld=w16.stride(0)))
+    arr = (QlinQuantJobC * max(len(jobs), 1))(*jobs)
+    st = _lib().qlin_quantize_batch(arr, len(jobs), bits, 0 if row else 64, _stream())
+    _check(st, "qlin_quantize_batch")
+    return res

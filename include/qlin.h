@@ -128,6 +128,29 @@ qlin_status qlin_quantize(const uint16_t* w16, int64_t ld_w, int32_t n, int32_t 
                           uint16_t* scale, uint8_t* zero, hipStream_t stream);
 
 /*
+ * Batched quantization (the Bitcrush README, "The machine" and "Under the
+ * hood": a move of the bit-width lever re-quantizes every weight matrix of the
+ * model from its fp16 master, on the GPU, without re-uploading anything):
+ * qlin_quantize on each job, all jobs with the same bits and group kind,
+ * group = 64 (per 64-group) or 0 (one group per row, i.e. group = k of each
+ * job).  Jobs are launched 64 at a time (one kernel launch per 64 jobs);
+ * results are identical to one qlin_quantize per job.  codes may be NULL in
+ * any job (scale/zero only).  No job's outputs may overlap another job's
+ * inputs or outputs (QLIN_ERR_ALIAS).  count = 0 is a no-op.
+ */
+typedef struct {
+  const uint16_t* w16;   /* fp16 master [n, ld_w] */
+  int64_t ld_w;
+  int32_t n, k;
+  uint32_t* codes;       /* NULL: scale/zero only */
+  uint16_t* scale;
+  uint8_t* zero;
+} qlin_quant_job;
+
+qlin_status qlin_quantize_batch(const qlin_quant_job* jobs, int32_t count, int32_t bits,
+                                int32_t group, hipStream_t stream);
+
+/*
  * Workspace needed by qlin_gemv / qlin_gemm for their split-K launches, at the
  * launch shape the library picks for this weight and m.  0 means the launch
  * needs none.  Layout: the first 65536 bytes hold uint32 arrival counters (one

@@ -31,7 +31,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     declared = header_functions()
-    assert len(declared) == 15
+    assert len(declared) == 16
     assert sorted(qlin.EXPORTS) == declared
     for name in declared:
         assert hasattr(lib, name), name
@@ -219,8 +219,36 @@ def test_embed_rows_validation(lib):
     assert embed(lib, weight(), o32=FAKE + (3 << 30)) == ALIAS   # output on the ids
 
 
+def qjob(i, **kw):
+    base = FAKE + ((20 + 4 * i) << 30)
+    d = dict(w16=base, ld_w=128, n=8, k=128, codes=base + (1 << 30), scale=base + (2 << 30),
+             zero=base + (3 << 30))
+    d.update(kw)
+    return qlin.QlinQuantJobC(d["w16"], d["ld_w"], d["n"], d["k"], d["codes"], d["scale"], d["zero"])
+
+
+def qbatch(lib, jobs, bits=4, group=64, count=None):
+    arr = (qlin.QlinQuantJobC * max(len(jobs), 1))(*jobs)
+    return lib.qlin_quantize_batch(arr, len(jobs) if count is None else count, bits, group, None)
+
+
+def test_quantize_batch_validation(lib):
+    assert qbatch(lib, [], count=0) == OK
+    assert lib.qlin_quantize_batch(None, 1, 4, 64, None) == NULL
+    assert qbatch(lib, [qjob(0)], count=-1) == SHAPE
+    assert qbatch(lib, [qjob(0)], group=128) == GROUP         # 64 or 0 (per row) only
+    assert qbatch(lib, [qjob(0)], bits=5) == BITS
+    assert qbatch(lib, [qjob(0), qjob(1, k=100)]) == SHAPE
+    assert qbatch(lib, [qjob(0), qjob(1, scale=None)]) == NULL
+    assert qbatch(lib, [qjob(0), qjob(1, ld_w=132)]) == ALIGN
+    assert qbatch(lib, [qjob(0), qjob(1, zero=FAKE + (20 << 30))]) == ALIAS   # on job 0's master
+    assert qbatch(lib, [qjob(0), qjob(1, codes=FAKE + (21 << 30) + 64)]) == ALIAS  # on job 0's codes
+    assert qbatch(lib, [qjob(0, codes=None), qjob(1, codes=None)], group=0) in (OK, NODEV)
+
+
 @pytest.mark.skipif(torch.cuda.is_available(), reason="checks the no-GPU path")
 def test_no_device(lib):
+    assert qbatch(lib, [qjob(0), qjob(1)]) == NODEV
     assert embed(lib, weight()) == NODEV
     assert quant(lib) == NODEV
     assert gemv(lib, weight()) == NODEV
