@@ -991,6 +991,15 @@ __global__ __launch_bounds__(256) void k_embed_rows(
 // quarter of the X tile and its own tile's codes and metadata.  X chunks are
 // XOR-swizzled within a row (16-byte chunk c8 of row r at position
 // c8 ^ (r & 7)), so the A-fragment reads are free of bank conflicts.
+// f(std::integral_constant<int, I>) for I = B .. E-1, unrolled.
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
+
 // One direct-to-LDS load of SZ bytes per lane: lane l's bytes land at
 // lds + SZ * l (lds wave-uniform).
 template <int SZ>
@@ -1132,10 +1141,10 @@ __global__ __launch_bounds__(256, 2) void k_gemm_lds(
   // after it), then a barrier makes every wave's part visible; the stage
   // freed by block j-1 is refilled with block j+S-1 right after.
   auto wait_block = [&](int rem) __attribute__((always_inline)) {
-    if constexpr (S > 4) { if (rem >= 3) { wait_vm<3 * NDMA>(); return; } }
-    if constexpr (S > 3) { if (rem >= 2) { wait_vm<2 * NDMA>(); return; } }
-    if constexpr (S > 2) { if (rem >= 1) { wait_vm<NDMA>(); return; } }
-    wait_vm<0>();
+    static_for<0, S - 1>([&](auto rc) __attribute__((always_inline)) {
+      constexpr int R = decltype(rc)::value;
+      if (rem == R) wait_vm<R * NDMA>();
+    });
   };
   auto step = [&](int j, auto stc) __attribute__((always_inline)) {
     constexpr int I = decltype(stc)::value;
@@ -1145,27 +1154,17 @@ __global__ __launch_bounds__(256, 2) void k_gemm_lds(
     compute(stc);
   };
 
-  issue(0, std::integral_constant<int, 0>{});
-  if (S > 2 && 1 < nk) issue(1, std::integral_constant<int, 1 % S>{});
-  if (S > 3 && 2 < nk) issue(2, std::integral_constant<int, 2 % S>{});
-  if (S > 4 && 3 < nk) issue(3, std::integral_constant<int, 3 % S>{});
-  for (int j = 0;; j += S) {
-    step(j, std::integral_constant<int, 0>{});
-    if (j + 1 >= nk) break;
-    step(j + 1, std::integral_constant<int, 1 % S>{});
-    if (j + 2 >= nk) break;
-    if constexpr (S > 2) {
-      step(j + 2, std::integral_constant<int, 2 % S>{});
-      if (j + 3 >= nk) break;
-    }
-    if constexpr (S > 3) {
-      step(j + 3, std::integral_constant<int, 3 % S>{});
-      if (j + 4 >= nk) break;
-    }
-    if constexpr (S > 4) {
-      step(j + 4, std::integral_constant<int, 4 % S>{});
-      if (j + 5 >= nk) break;
-    }
+  // prologue: blocks 0 .. S-2 into stages 0 .. S-2
+  static_for<0, S - 1>([&](auto ic) __attribute__((always_inline)) {
+    constexpr int I = decltype(ic)::value;
+    if (I < nk) issue(I, ic);
+  });
+  // the loop body covers S blocks, so every stage index is a constant
+  for (int j = 0; j < nk; j += S) {
+    static_for<0, S>([&](auto ic) __attribute__((always_inline)) {
+      constexpr int I = decltype(ic)::value;
+      if (j + I < nk) step(j + I, ic);
+    });
   }
 
   if (splits > 1) {
