@@ -19,7 +19,11 @@ fp16 masters ~N(0, 0.02), activations ~N(0, 1):
                    than four times the 256 MB Infinity Cache) so they come
                    from HBM
   decode_gemv      the same 169 matrices as 169 separate packed GEMVs
-  prefill_m128     168 GEMMs (layers) at M = 128, fp16 MFMA, fp32 accumulate
+  prefill_step_m128  the 168 layer matrices at M = 128 grouped as the dispatch
+                   list groups them: per layer q/k/v in one launch, o, gate/up
+                   in one launch, down (96 launches); fp16 MFMA, fp32 accumulate
+  prefill_step_m2048 the same at M = 2048
+  prefill_m128     the 168 layer GEMMs as separate launches, M = 128
   prefill_m2048    the same at M = 2048
   gemm_m8          169 GEMMs at M = 8
   fused_gemv       169 fused quantize-dequantize GEMVs from the fp16 masters
@@ -232,6 +236,35 @@ def build_decode(torch, qlin, synth, dev, ws, phases, state):
         return capture_calls(torch, [make(r) for r in range(ROTATE)])
 
     staged = {}
+    # prefill as the dispatch list groups it: per layer q/k/v (one launch), o,
+    # gate/up (one launch), down
+    idx = {(l, nm): i for i, (l, nm, _, _) in enumerate(shapes)}
+    layers = sorted(set(l for (l, nm, _, _) in shapes if nm != "lm_head"))
+    Yg = {}
+    for m in (128, 2048):
+        if f"prefill_step_m{m}" not in phases:
+            continue
+        Yg[m] = {nm: torch.empty(m, shapes[idx[(0, nm)]][2], dtype=torch.float32, device=dev)
+                 for nm in ("q", "k", "v", "o", "gate", "up", "down")}
+
+        def step_calls(r, m=m):
+            Xm = X[m]
+            calls = []
+            for l in layers:
+                w = {nm: packed[r][idx[(l, nm)]] for nm in ("q", "k", "v", "o", "gate", "up", "down")}
+                k1, k2 = w["q"].k, w["down"].k
+                calls += [
+                    lambda w=w, m=m, k1=k1: qlin.gemm_multi(
+                        [w["q"], w["k"], w["v"]], Xm[:, :k1],
+                        [Yg[m]["q"], Yg[m]["k"], Yg[m]["v"]], ws=ws),
+                    lambda w=w, m=m, k1=k1: qlin.gemm(w["o"], Xm[:, :k1], Yg[m]["o"], ws=ws),
+                    lambda w=w, m=m, k1=k1: qlin.gemm_multi(
+                        [w["gate"], w["up"]], Xm[:, :k1], [Yg[m]["gate"], Yg[m]["up"]], ws=ws),
+                    lambda w=w, m=m, k2=k2: qlin.gemm(w["down"], Xm[:, :k2], Yg[m]["down"],
+                                                      ws=ws),
+                ]
+            return calls
+        staged[f"prefill_step_m{m}"] = per_rotation(step_calls)
     for m in (128, 2048):
         if f"prefill_m{m}" in phases:
             staged[f"prefill_m{m}"] = per_rotation(
@@ -253,7 +286,7 @@ def build_decode(torch, qlin, synth, dev, ws, phases, state):
     if "embed_gather" in phases:
         staged["embed_gather"] = per_rotation(lambda r: [lambda w=lm8[r]: qlin.embed_rows(w, ids)])
 
-    hold = (masters, xs, ys, packed, scratch, meta, fused, X, Y, lm8, ids, y_lm)
+    hold = (masters, xs, ys, packed, scratch, meta, fused, X, Y, Yg, lm8, ids, y_lm)
 
     def run(name):
         assert hold is not None       # every buffer the graphs address stays alive
@@ -275,6 +308,10 @@ def build_decode(torch, qlin, synth, dev, ws, phases, state):
         Phase("decode_step", run, "GB/s", grp_bytes, grp_launches, HBM_PEAK_GBS, "hbm",
               "k_gemv_packed<4> (q/k/v set, o, gate/up+SwiGLU, down; LM head)"),
         Phase("decode_gemv", run, "GB/s", dec_bytes, 169, HBM_PEAK_GBS, "hbm", "k_gemv_packed<4>"),
+        Phase("prefill_step_m128", run, "TFLOP/s", fl[128], 96, FP16_MFMA_PEAK_TFLOPS, "mfma",
+              "k_gemm_tiles<4, 32> (q/k/v set, o, gate/up set, down)"),
+        Phase("prefill_step_m2048", run, "TFLOP/s", fl[2048], 96, FP16_MFMA_PEAK_TFLOPS,
+              "mfma", "k_gemm_lds<4, 128|64> / k_gemm_tiles<4, 32> (q/k/v set, o, gate/up set, down)"),
         Phase("prefill_m128", run, "TFLOP/s", fl[128], 168, FP16_MFMA_PEAK_TFLOPS, "mfma",
               "k_gemm_tiles<4>"),
         Phase("prefill_m2048", run, "TFLOP/s", fl[2048], 168, FP16_MFMA_PEAK_TFLOPS, "mfma",
@@ -444,7 +481,8 @@ def main():
     state = {"step": 0}
     phases, decode_shapes = [], None
     if "decode" in sections:
-        names = ["decode_step", "decode_gemv", "prefill_m128", "prefill_m2048", "gemm_m8", "fused_gemv",
+        names = ["decode_step", "decode_gemv", "prefill_step_m128", "prefill_step_m2048",
+                 "prefill_m128", "prefill_m2048", "gemm_m8", "fused_gemv",
                  "rtn_precompute", "quantize_pack", "lm_head_int8", "embed_gather"]
         ps, decode_shapes = build_decode(torch, qlin, synth, dev, ws, chosen(names), state)
         phases += ps
@@ -526,10 +564,11 @@ def main():
             "avg_launch_us": round(per_launch_us, 3),
         }
     tf = {}
-    if "prefill_m2048" in res:
-        tf["M=2048"] = res["prefill_m2048"]["TFLOP/s"]
-    if "prefill_m128" in res:
-        tf["M=128"] = res["prefill_m128"]["TFLOP/s"]
+    for m in (2048, 128):
+        for key in (f"prefill_step_m{m}", f"prefill_m{m}"):
+            if key in res:
+                tf[f"M={m}"] = res[key]["TFLOP/s"]
+                break
     if tf:
         out["prefill_gemm_tflops"] = tf
         out["prefill_pct_fp16_mfma_peak"] = {k: round(100 * v / FP16_MFMA_PEAK_TFLOPS, 2)

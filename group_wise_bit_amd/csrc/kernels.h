@@ -566,19 +566,64 @@ __device__ __forceinline__ f16x8 deq_quarter(const uint32_t* wl, int s, const De
   }
 }
 
+// Up to kMaxMats packed matrices that share K (and X), multiplied in one
+// launch (q/k/v, or gate/up, of a prefill).  Launch columns are numbered
+// consecutively over the matrices: matrix i owns columns [end[i-1], end[i])
+// (a column is a 64-row tile for M <= 16, four tiles for the tiled GEMM).
+struct GemmSet {
+  const uint32_t* codes[kMaxMats];
+  const uint16_t* scale[kMaxMats];
+  const uint8_t* zero[kMaxMats];
+  float* y[kMaxMats];
+  int64_t ldy[kMaxMats];
+  int n[kMaxMats];
+  int end[kMaxMats];
+  int count;
+};
+
+struct GemmMat {
+  const uint32_t* codes;
+  const uint16_t* scale;
+  const uint8_t* zero;
+  float* y;
+  int64_t ldy;
+  int n, tiles, col;     // col: the launch column within the matrix
+};
+
+__device__ __forceinline__ GemmMat gemm_mat(const GemmSet& s, int x) {
+  int i = 0;
+  for (int k = 0; k + 1 < s.count; ++k)
+    if (x >= s.end[k]) i = k + 1;
+  GemmMat g;
+  g.codes = s.codes[i];
+  g.scale = s.scale[i];
+  g.zero = s.zero[i];
+  g.y = s.y[i];
+  g.ldy = s.ldy[i];
+  g.n = s.n[i];
+  g.tiles = (g.n + kTile - 1) / kTile;
+  g.col = x - (i == 0 ? 0 : s.end[i - 1]);
+  return g;
+}
+
 template <int BITS, int WAVES, int U>
 __global__ __launch_bounds__(WAVES * 64) void k_gemm_skinny(
-    const uint32_t* __restrict__ codes, const uint16_t* __restrict__ scale,
-    const uint8_t* __restrict__ zero, const uint16_t* __restrict__ X, int64_t ldx, int m,
-    float* __restrict__ Y, int64_t ldy, float* __restrict__ part, uint32_t* __restrict__ tickets,
-    int n, int kb, int G, int splits, int kbps) {
+    const GemmSet set, const uint16_t* __restrict__ X, int64_t ldx, int m,
+    float* __restrict__ part, uint32_t* __restrict__ tickets, int kb, int G, int splits,
+    int kbps) {
   constexpr int WPB = 2 * BITS;
   constexpr int QW = (BITS == 3) ? 2 : BITS / 2;       // words held per quarter block
   __shared__ f32x4 red[WAVES][4][64];
   const uint32_t magic = vreg_const(kMagic);
   const int lane = lane_id(), wave = wave_id();
   const int c = lane & 15, q = lane >> 4;
-  const int t = blockIdx.x, sp = blockIdx.y;
+  const GemmMat mat = gemm_mat(set, blockIdx.x);
+  const uint32_t* __restrict__ codes = mat.codes;
+  const uint16_t* __restrict__ scale = mat.scale;
+  const uint8_t* __restrict__ zero = mat.zero;
+  const int n = mat.n;
+  const int t = mat.col, sp = blockIdx.y;
+  const int tg = blockIdx.x;                 // launch tile (tickets, partials)
   const int j0 = sp * kbps;
   const int j1 = min(kb, j0 + kbps);
   f32x4 acc[4];
@@ -645,10 +690,10 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_skinny(
     for (int cg = 0; cg < 4; ++cg)
 #pragma unroll
       for (int r = 0; r < 4; ++r)
-        put_partial(part + ((int64_t)sp * 16 + 4 * q + r) * np + t * kTile + 16 * cg + c,
+        put_partial(part + ((int64_t)sp * 16 + 4 * q + r) * np + tg * kTile + 16 * cg + c,
                     tot[cg][r]);
     partials_written();
-    if (!split_ticket(tickets, t, splits)) return;
+    if (!split_ticket(tickets, tg, splits)) return;
 #pragma unroll
     for (int cg = 0; cg < 4; ++cg) tot[cg] = (f32x4){0.f, 0.f, 0.f, 0.f};
     // split order; the 16 loads of one split are in flight together
@@ -658,7 +703,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_skinny(
       for (int cg = 0; cg < 4; ++cg)
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-          v[cg][r] = get_partial(part + ((int64_t)s2 * 16 + 4 * q + r) * np + t * kTile +
+          v[cg][r] = get_partial(part + ((int64_t)s2 * 16 + 4 * q + r) * np + tg * kTile +
                                  16 * cg + c);
 #pragma unroll
       for (int cg = 0; cg < 4; ++cg)
@@ -671,7 +716,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_skinny(
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int mrow = 4 * q + r, col = t * kTile + 16 * cg + c;
-      if (mrow < m && col < n) Y[(int64_t)mrow * ldy + col] = tot[cg][r];
+      if (mrow < m && col < n) mat.y[(int64_t)mrow * mat.ldy + col] = tot[cg][r];
     }
 }
 
@@ -724,9 +769,7 @@ __device__ __forceinline__ f16x8 deq_half(const uint32_t* wl, int s, const Deq& 
 
 template <int BITS, int MB>
 __global__ __launch_bounds__(256) void k_gemm_tiles(
-    const uint32_t* __restrict__ codes, const uint16_t* __restrict__ scale,
-    const uint8_t* __restrict__ zero, const uint16_t* __restrict__ X, int64_t ldx, int m,
-    float* __restrict__ Y, int64_t ldy, int n, int kb, int G, int tiles,
+    const GemmSet set, const uint16_t* __restrict__ X, int64_t ldx, int m, int kb, int G,
     int splits, int kbps, float* __restrict__ part, uint32_t* __restrict__ tickets) {
   constexpr int WPB = 2 * BITS;
   constexpr int HW = WPB / 2;               // words of a half block
@@ -737,8 +780,13 @@ __global__ __launch_bounds__(256) void k_gemm_tiles(
   const int tid = threadIdx.x;
   const int lane = lane_id(), wave = wave_id();
   const int c = lane & 31, h = lane >> 5;
-  const int t = blockIdx.x * 4 + wave;
-  const bool tvalid = t < tiles;
+  const GemmMat mat = gemm_mat(set, blockIdx.x);
+  const uint32_t* __restrict__ codes = mat.codes;
+  const uint16_t* __restrict__ scale = mat.scale;
+  const uint8_t* __restrict__ zero = mat.zero;
+  const int n = mat.n;
+  const int t = mat.col * 4 + wave;
+  const bool tvalid = t < mat.tiles;
   const int tt = tvalid ? t : 0;
   const int m0 = blockIdx.y * MB;
   const uint32_t magic = vreg_const(kMagic);
@@ -926,7 +974,8 @@ __global__ __launch_bounds__(256) void k_gemm_tiles(
 
   if (!tvalid) return;
   // rows m0 + 32rb + 8(r/4) + 4h + r%4 of columns t*64 + 32cb + c
-  float* ybase = Y + (int64_t)(m0 + 4 * h) * ldy + t * kTile + c;
+  const int64_t ldy = mat.ldy;
+  float* ybase = mat.y + (int64_t)(m0 + 4 * h) * ldy + t * kTile + c;
   const int mrem = m - m0 - 4 * h;
 #pragma unroll
   for (int cb = 0; cb < 2; ++cb) {
@@ -1043,9 +1092,7 @@ template <> struct WDma<8> { static constexpr int SZ = 16, N = 4; };
 
 template <int BITS, int MB, int S>
 __global__ __launch_bounds__(256, 2) void k_gemm_lds(
-    const uint32_t* __restrict__ codes, const uint16_t* __restrict__ scale,
-    const uint8_t* __restrict__ zero, const uint16_t* __restrict__ X, int64_t ldx, int m,
-    float* __restrict__ Y, int64_t ldy, int n, int kb, int G, int tiles,
+    const GemmSet set, const uint16_t* __restrict__ X, int64_t ldx, int m, int kb, int G,
     int splits, int kbps, float* __restrict__ part, uint32_t* __restrict__ tickets) {
   constexpr int WPB = 2 * BITS;
   constexpr int RB = MB / 32;               // 32-row MFMA blocks of X
@@ -1056,8 +1103,13 @@ __global__ __launch_bounds__(256, 2) void k_gemm_lds(
   const int tid = threadIdx.x;
   const int lane = lane_id(), wave = wave_id();
   const int c = lane & 31, h = lane >> 5;
-  const int t = blockIdx.x * 4 + wave;
-  const bool tvalid = t < tiles;
+  const GemmMat mat = gemm_mat(set, blockIdx.x);
+  const uint32_t* __restrict__ codes = mat.codes;
+  const uint16_t* __restrict__ scale = mat.scale;
+  const uint8_t* __restrict__ zero = mat.zero;
+  const int n = mat.n;
+  const int t = mat.col * 4 + wave;
+  const bool tvalid = t < mat.tiles;
   const int tt = tvalid ? t : 0;
   const int m0 = blockIdx.y * MB;
   const uint32_t magic = vreg_const(kMagic);
@@ -1222,7 +1274,8 @@ __global__ __launch_bounds__(256, 2) void k_gemm_lds(
 
   if (!tvalid) return;
   // rows m0 + 32rb + 8(r/4) + 4h + r%4 of columns t*64 + 32cb + c
-  float* ybase = Y + (int64_t)(m0 + 4 * h) * ldy + t * kTile + c;
+  const int64_t ldy = mat.ldy;
+  float* ybase = mat.y + (int64_t)(m0 + 4 * h) * ldy + t * kTile + c;
   const int mrem = m - m0 - 4 * h;
 #pragma unroll
   for (int cb = 0; cb < 2; ++cb) {

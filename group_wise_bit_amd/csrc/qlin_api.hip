@@ -394,29 +394,59 @@ void launch_gemv_fused(const qlin_weight* w, const f16x2* x2, float* y, float* p
   else launch_gemv_fused_w<B, 4, 1>(w, x2, y, part, tick, c, st);
 }
 
+// A GEMM launch over a set of matrices (shared K, bits, group; one X).
+struct GemmPlan {
+  GemmSet set;
+  int64_t tiles;      // all 64-row tiles of the set
+  int cols4;          // all work-group columns of four tiles (tiled GEMM)
+  int kb, G, bits;
+};
+
+GemmPlan gemm_plan(const qlin_weight* const* w, float* const* Y, const int64_t* ldy, int count,
+                   bool skinny) {
+  GemmPlan p{};
+  int64_t tiles = 0, cols4 = 0;
+  for (int i = 0; i < count; ++i) {
+    p.set.codes[i] = static_cast<const uint32_t*>(w[i]->data);
+    p.set.scale[i] = w[i]->scale;
+    p.set.zero[i] = w[i]->zero;
+    p.set.y[i] = Y[i];
+    p.set.ldy[i] = ldy[i];
+    p.set.n[i] = w[i]->n;
+    const int64_t t = tiles_of(w[i]->n);
+    tiles += t;
+    cols4 += (t + 3) / 4;
+    p.set.end[i] = (int)(skinny ? tiles : cols4);
+  }
+  p.set.count = count;
+  p.tiles = tiles;
+  p.cols4 = (int)cols4;
+  p.kb = w[0]->k / kBlock;
+  p.G = (w[0]->group == w[0]->k) ? 1 : p.kb;
+  p.bits = w[0]->bits;
+  return p;
+}
+
 template <int B>
-void launch_gemm_skinny(const qlin_weight* w, const uint16_t* X, int64_t ldx, int m, float* Y,
-                        int64_t ldy, float* part, uint32_t* tick, Split sp, hipStream_t st) {
-  const int kb = w->k / kBlock;
-  const int G = (w->group == w->k) ? 1 : kb;
-  dim3 grid((unsigned)tiles_of(w->n), sp.splits);
-  hipLaunchKernelGGL((k_gemm_skinny<B, kWaves, 2>), grid, dim3(kWaves * 64), 0, st,
-                     static_cast<const uint32_t*>(w->data), w->scale, w->zero, X, ldx, m, Y, ldy,
-                     part, tick, w->n, kb, G, sp.splits, sp.kbps);
+void launch_gemm_skinny(const GemmPlan& p, const uint16_t* X, int64_t ldx, int m, float* part,
+                        uint32_t* tick, Split sp, hipStream_t st) {
+  hipLaunchKernelGGL((k_gemm_skinny<B, kWaves, 2>), dim3((unsigned)p.tiles, sp.splits),
+                     dim3(kWaves * 64), 0, st, p.set, X, ldx, m, part, tick, p.kb, p.G,
+                     sp.splits, sp.kbps);
 }
 
 // Tiled-GEMM launch shape: work-group tile = MB rows of X x 256 rows of W
-// (four 64-row tiles).  Measured on MI355X (graph-replayed launches over
-// rotating cold weights, Qwen-shaped N x K, M = 32..2048, int4): a tall X tile
-// pays only when the grid is large; up to M = 256 the 32-row tile is fastest
-// (several work-groups per CU hide the load latency), and K is split up to 4
-// ways when there are fewer than 160 work-groups, keeping at least 10
-// K-blocks per split.
+// (four 64-row tiles); gx = work-group columns.  Measured on MI355X
+// (graph-replayed launches over rotating cold weights, Qwen-shaped N x K,
+// M = 32..2048, int4): a tall X tile pays only when the grid is large; up to
+// M = 256 the 32-row tile is fastest (several work-groups per CU hide the load
+// latency), and K is split up to 4 ways when there are fewer than 160
+// work-groups, keeping at least 10 K-blocks per split.
 struct TilesCfg { int mb, gx, gy, splits, kbps; };
 
-TilesCfg tiles_config(int64_t tiles, int kb, int m, int64_t ws_bytes) {
+TilesCfg tiles_config(int64_t gx, int kb, int m, int64_t ws_bytes) {
   TilesCfg c;
-  c.gx = (int)((tiles + 3) / 4);
+  c.gx = (int)gx;
   int want = 1;
   if (m <= 256) {
     c.mb = 32;
@@ -451,8 +481,8 @@ TilesCfg tiles_config(int64_t tiles, int kb, int m, int64_t ws_bytes) {
   return c;
 }
 
-int64_t tiles_ws_bytes(int64_t tiles, int kb, int m) {
-  const TilesCfg c = tiles_config(tiles, kb, m, INT64_MAX);
+int64_t tiles_ws_bytes(int64_t gx, int kb, int m) {
+  const TilesCfg c = tiles_config(gx, kb, m, INT64_MAX);
   if (c.splits <= 1) return 0;
   return kCounterBytes + (int64_t)c.splits * c.gy * c.mb * c.gx * 256 * 4;
 }
@@ -461,27 +491,23 @@ int64_t tiles_ws_bytes(int64_t tiles, int kb, int m) {
 // load latency); MB = 64 / 128: the LDS-DMA pipeline, 4 / 3 stages deep
 // (two work-groups per CU).
 template <int B, int MB>
-void launch_tiles_mb(const qlin_weight* w, const uint16_t* X, int64_t ldx, int m, float* Y,
-                     int64_t ldy, TilesCfg c, float* part, uint32_t* tick, hipStream_t st) {
-  const int kb = w->k / kBlock;
-  const int G = (w->group == w->k) ? 1 : kb;
+void launch_tiles_mb(const GemmPlan& p, const uint16_t* X, int64_t ldx, int m, TilesCfg c,
+                     float* part, uint32_t* tick, hipStream_t st) {
   if constexpr (MB == 32)
     hipLaunchKernelGGL((k_gemm_tiles<B, MB>), dim3(c.gx, c.gy, c.splits), dim3(256), 0, st,
-                       static_cast<const uint32_t*>(w->data), w->scale, w->zero, X, ldx, m, Y, ldy,
-                       w->n, kb, G, (int)tiles_of(w->n), c.splits, c.kbps, part, tick);
+                       p.set, X, ldx, m, p.kb, p.G, c.splits, c.kbps, part, tick);
   else
     hipLaunchKernelGGL((k_gemm_lds<B, MB, (MB == 128 ? 3 : 4)>), dim3(c.gx, c.gy, c.splits),
-                       dim3(256), 0, st, static_cast<const uint32_t*>(w->data), w->scale, w->zero,
-                       X, ldx, m, Y, ldy, w->n, kb, G, (int)tiles_of(w->n), c.splits, c.kbps,
-                       part, tick);
+                       dim3(256), 0, st, p.set, X, ldx, m, p.kb, p.G, c.splits, c.kbps, part,
+                       tick);
 }
 
 template <int B>
-void launch_gemm_tiles(const qlin_weight* w, const uint16_t* X, int64_t ldx, int m, float* Y,
-                       int64_t ldy, TilesCfg c, float* part, uint32_t* tick, hipStream_t st) {
-  if (c.mb == 32) launch_tiles_mb<B, 32>(w, X, ldx, m, Y, ldy, c, part, tick, st);
-  else if (c.mb == 64) launch_tiles_mb<B, 64>(w, X, ldx, m, Y, ldy, c, part, tick, st);
-  else launch_tiles_mb<B, 128>(w, X, ldx, m, Y, ldy, c, part, tick, st);
+void launch_gemm_tiles(const GemmPlan& p, const uint16_t* X, int64_t ldx, int m, TilesCfg c,
+                       float* part, uint32_t* tick, hipStream_t st) {
+  if (c.mb == 32) launch_tiles_mb<B, 32>(p, X, ldx, m, c, part, tick, st);
+  else if (c.mb == 64) launch_tiles_mb<B, 64>(p, X, ldx, m, c, part, tick, st);
+  else launch_tiles_mb<B, 128>(p, X, ldx, m, c, part, tick, st);
 }
 
 constexpr int kSkinnyMaxM = 16;
@@ -611,10 +637,24 @@ int64_t qlin_gemv_workspace_bytes(const qlin_weight* w) {
                        w->format == QLIN_FMT_PACKED ? kPackedUnroll : kFusedUnroll);
 }
 
+int64_t gemm_set_ws_bytes(const qlin_weight* w, int count, int32_t m) {
+  if (w == nullptr || count < 1 || count > kMaxMats || m < 1 || m > kMaxM) return 0;
+  int64_t tiles = 0, cols4 = 0;
+  for (int i = 0; i < count; ++i) {
+    if (check_weight(&w[i], false, false) != QLIN_OK || w[i].k != w[0].k) return 0;
+    tiles += tiles_of(w[i].n);
+    cols4 += (tiles_of(w[i].n) + 3) / 4;
+  }
+  if (m > kSkinnyMaxM) return tiles_ws_bytes(cols4, w[0].k / kBlock, m);
+  return split_ws_bytes(tiles, w[0].k / kBlock, 16);
+}
+
 int64_t qlin_gemm_workspace_bytes(const qlin_weight* w, int32_t m) {
-  if (check_weight(w, false, false) != QLIN_OK || m < 1 || m > kMaxM) return 0;
-  if (m > kSkinnyMaxM) return tiles_ws_bytes(tiles_of(w->n), w->k / kBlock, m);
-  return split_ws_bytes(tiles_of(w->n), w->k / kBlock, 16);
+  return gemm_set_ws_bytes(w, 1, m);
+}
+
+int64_t qlin_gemm_multi_workspace_bytes(const qlin_weight* w, int32_t count, int32_t m) {
+  return gemm_set_ws_bytes(w, count, m);
 }
 
 qlin_status qlin_gemv(const qlin_weight* w, const uint16_t* x, float* y, void* workspace,
@@ -758,55 +798,78 @@ qlin_status qlin_embed_rows(const qlin_weight* w, const int32_t* ids, int32_t co
   return hip_status(hipGetLastError());
 }
 
-qlin_status qlin_gemm(const qlin_weight* w, const uint16_t* X, int32_t m, int64_t ld_x, float* Y,
-                      int64_t ld_y, void* workspace, int64_t workspace_bytes,
-                      hipStream_t stream) {
-  qlin_status st = check_weight(w, false, false);
-  if (st != QLIN_OK) return st;
-  if (X == nullptr || Y == nullptr) return QLIN_ERR_NULL;
-  if (m < 1 || m > kMaxM || ld_x < w->k || ld_y < w->n) return QLIN_ERR_SHAPE;
-  if (ld_x % 8 != 0) return QLIN_ERR_ALIGN;
-  if (!aligned16(X) || !aligned16(Y)) return QLIN_ERR_ALIGN;
-  if (workspace_bytes < 0) return QLIN_ERR_WORKSPACE;
-  if (workspace == nullptr) workspace_bytes = 0;
-  if (workspace != nullptr && !aligned16(workspace)) return QLIN_ERR_ALIGN;
-  const Range rY = range_of(Y, ((int64_t)(m - 1) * ld_y + w->n) * 4);
-  const Range rX = range_of(X, ((int64_t)(m - 1) * ld_x + w->k) * 2);
-  if (overlaps(rY, rX) || output_overlaps_weight(w, rY)) return QLIN_ERR_ALIAS;
-  if (workspace_bytes > 0) {
-    const Range rw = range_of(workspace, workspace_bytes);
-    if (overlaps(rw, rY) || overlaps(rw, rX) || output_overlaps_weight(w, rw))
-      return QLIN_ERR_ALIAS;
-  }
-  st = check_device();
-  if (st != QLIN_OK) return st;
-  const uint32_t* codes = static_cast<const uint32_t*>(w->data);
-  (void)codes;
+// Launches a checked GEMM plan (M <= 16: skinny kernel, else tiled).
+qlin_status run_gemm(const GemmPlan& p, const uint16_t* X, int m, int64_t ld_x, void* workspace,
+                     int64_t workspace_bytes, hipStream_t stream) {
+  uint32_t* tick = static_cast<uint32_t*>(workspace);
+  char* pbase = static_cast<char*>(workspace) + kCounterBytes;
   if (m <= kSkinnyMaxM) {
-    const int64_t tiles = tiles_of(w->n);
-    const Split sp = choose_split(tiles, w->k / kBlock, workspace_bytes, 16);
-    uint32_t* tick = static_cast<uint32_t*>(workspace);
-    float* part = sp.splits > 1
-        ? reinterpret_cast<float*>(static_cast<char*>(workspace) + kCounterBytes) : nullptr;
-    switch (w->bits) {
-      case 2: launch_gemm_skinny<2>(w, X, ld_x, m, Y, ld_y, part, tick, sp, stream); break;
-      case 3: launch_gemm_skinny<3>(w, X, ld_x, m, Y, ld_y, part, tick, sp, stream); break;
-      case 4: launch_gemm_skinny<4>(w, X, ld_x, m, Y, ld_y, part, tick, sp, stream); break;
-      default: launch_gemm_skinny<8>(w, X, ld_x, m, Y, ld_y, part, tick, sp, stream); break;
+    const Split sp = choose_split(p.tiles, p.kb, workspace_bytes, 16);
+    float* part = sp.splits > 1 ? reinterpret_cast<float*>(pbase) : nullptr;
+    switch (p.bits) {
+      case 2: launch_gemm_skinny<2>(p, X, ld_x, m, part, tick, sp, stream); break;
+      case 3: launch_gemm_skinny<3>(p, X, ld_x, m, part, tick, sp, stream); break;
+      case 4: launch_gemm_skinny<4>(p, X, ld_x, m, part, tick, sp, stream); break;
+      default: launch_gemm_skinny<8>(p, X, ld_x, m, part, tick, sp, stream); break;
     }
   } else {
-    const TilesCfg c = tiles_config(tiles_of(w->n), w->k / kBlock, m, workspace_bytes);
-    uint32_t* tick = static_cast<uint32_t*>(workspace);
-    float* part = c.splits > 1
-        ? reinterpret_cast<float*>(static_cast<char*>(workspace) + kCounterBytes) : nullptr;
-    switch (w->bits) {
-      case 2: launch_gemm_tiles<2>(w, X, ld_x, m, Y, ld_y, c, part, tick, stream); break;
-      case 3: launch_gemm_tiles<3>(w, X, ld_x, m, Y, ld_y, c, part, tick, stream); break;
-      case 4: launch_gemm_tiles<4>(w, X, ld_x, m, Y, ld_y, c, part, tick, stream); break;
-      default: launch_gemm_tiles<8>(w, X, ld_x, m, Y, ld_y, c, part, tick, stream); break;
+    const TilesCfg c = tiles_config(p.cols4, p.kb, m, workspace_bytes);
+    float* part = c.splits > 1 ? reinterpret_cast<float*>(pbase) : nullptr;
+    switch (p.bits) {
+      case 2: launch_gemm_tiles<2>(p, X, ld_x, m, c, part, tick, stream); break;
+      case 3: launch_gemm_tiles<3>(p, X, ld_x, m, c, part, tick, stream); break;
+      case 4: launch_gemm_tiles<4>(p, X, ld_x, m, c, part, tick, stream); break;
+      default: launch_gemm_tiles<8>(p, X, ld_x, m, c, part, tick, stream); break;
     }
   }
   return hip_status(hipGetLastError());
+}
+
+qlin_status qlin_gemm(const qlin_weight* w, const uint16_t* X, int32_t m, int64_t ld_x, float* Y,
+                      int64_t ld_y, void* workspace, int64_t workspace_bytes,
+                      hipStream_t stream) {
+  return qlin_gemm_multi(w, 1, X, m, ld_x, &Y, &ld_y, workspace, workspace_bytes, stream);
+}
+
+qlin_status qlin_gemm_multi(const qlin_weight* w, int32_t count, const uint16_t* X, int32_t m,
+                            int64_t ld_x, float* const* Y, const int64_t* ld_y, void* workspace,
+                            int64_t workspace_bytes, hipStream_t stream) {
+  if (w == nullptr || Y == nullptr || ld_y == nullptr) return QLIN_ERR_NULL;
+  if (count < 1 || count > kMaxMats) return QLIN_ERR_SHAPE;
+  for (int i = 0; i < count; ++i) {
+    const qlin_status st = check_weight(&w[i], false, false);
+    if (st != QLIN_OK) return st;
+    if (w[i].k != w[0].k) return QLIN_ERR_SHAPE;
+    if (w[i].bits != w[0].bits || w[i].group != w[0].group) return QLIN_ERR_FORMAT;
+  }
+  if (X == nullptr) return QLIN_ERR_NULL;
+  if (m < 1 || m > kMaxM || ld_x < w[0].k) return QLIN_ERR_SHAPE;
+  if (ld_x % 8 != 0 || !aligned16(X)) return QLIN_ERR_ALIGN;
+  if (workspace_bytes < 0) return QLIN_ERR_WORKSPACE;
+  if (workspace == nullptr) workspace_bytes = 0;
+  if (workspace != nullptr && !aligned16(workspace)) return QLIN_ERR_ALIGN;
+  const Range rX = range_of(X, ((int64_t)(m - 1) * ld_x + w[0].k) * 2);
+  const Range rw = range_of(workspace, workspace_bytes);
+  if (overlaps(rw, rX)) return QLIN_ERR_ALIAS;
+  for (int i = 0; i < count; ++i) {
+    if (output_overlaps_weight(&w[i], rw)) return QLIN_ERR_ALIAS;
+    if (Y[i] == nullptr) return QLIN_ERR_NULL;
+    if (ld_y[i] < w[i].n) return QLIN_ERR_SHAPE;
+    if (!aligned16(Y[i])) return QLIN_ERR_ALIGN;
+    const Range rY = range_of(Y[i], ((int64_t)(m - 1) * ld_y[i] + w[i].n) * 4);
+    if (overlaps(rY, rX) || overlaps(rY, rw)) return QLIN_ERR_ALIAS;
+    for (int j = 0; j < count; ++j)
+      if (output_overlaps_weight(&w[j], rY)) return QLIN_ERR_ALIAS;
+    for (int j = 0; j < i; ++j)
+      if (overlaps(rY, range_of(Y[j], ((int64_t)(m - 1) * ld_y[j] + w[j].n) * 4)))
+        return QLIN_ERR_ALIAS;
+  }
+  const qlin_status st = check_device();
+  if (st != QLIN_OK) return st;
+  const qlin_weight* wp[kMaxMats];
+  for (int i = 0; i < count; ++i) wp[i] = &w[i];
+  const GemmPlan p = gemm_plan(wp, Y, ld_y, count, m <= kSkinnyMaxM);
+  return run_gemm(p, X, m, ld_x, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

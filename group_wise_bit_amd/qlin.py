@@ -32,7 +32,7 @@ EXPORTS = (
     "qlin_gemm_workspace_bytes", "qlin_gemv", "qlin_gemm",
     "qlin_gemv_multi_workspace_bytes", "qlin_gemv_multi",
     "qlin_gemv_swiglu_workspace_bytes", "qlin_gemv_swiglu", "qlin_embed_rows",
-    "qlin_quantize_batch",
+    "qlin_quantize_batch", "qlin_gemm_multi_workspace_bytes", "qlin_gemm_multi",
 )
 
 
@@ -107,6 +107,11 @@ def _lib() -> ctypes.CDLL:
         lib.qlin_embed_rows.restype = ctypes.c_int
         lib.qlin_quantize_batch.argtypes = [ctypes.POINTER(QlinQuantJobC), i32, i32, i32, vp]
         lib.qlin_quantize_batch.restype = ctypes.c_int
+        lib.qlin_gemm_multi_workspace_bytes.argtypes = [wp, i32, i32]
+        lib.qlin_gemm_multi_workspace_bytes.restype = i64
+        lib.qlin_gemm_multi.argtypes = [wp, i32, vp, i32, i64, ctypes.POINTER(vp),
+                                        ctypes.POINTER(i64), vp, i64, vp]
+        lib.qlin_gemm_multi.restype = ctypes.c_int
         _LIB = lib
     return _LIB
 
@@ -336,3 +341,25 @@ def quantize_batch(masters: Sequence[torch.Tensor], bits: int, group, codes: boo
     st = _lib().qlin_quantize_batch(arr, len(jobs), bits, 0 if row else 64, _stream())
     _check(st, "qlin_quantize_batch")
     return res
+
+
+def gemm_multi(ws_list: Sequence[QWeight], X: torch.Tensor,
+               Ys: Optional[Sequence[torch.Tensor]] = None,
+               ws: Optional[torch.Tensor] = "auto") -> List[torch.Tensor]:
+    """qlin_gemm_multi: Y_i = X . W_i^T for up to 4 packed weights sharing X, one launch."""
+    if X.dtype != torch.float16 or X.dim() != 2 or X.stride(1) != 1:
+        raise TypeError("X must be a float16 [m, k] tensor with contiguous rows")
+    m, count = X.shape[0], len(ws_list)
+    if Ys is None:
+        Ys = [torch.empty(m, w.n, dtype=torch.float32, device=X.device) for w in ws_list]
+    arr = (QlinWeightC * max(count, 1))(*[w.c_struct() for w in ws_list])
+    yp = (ctypes.c_void_p * max(count, 1))(*[y.data_ptr() for y in Ys])
+    ld = (ctypes.c_int64 * max(count, 1))(*[y.stride(0) for y in Ys])
+    if isinstance(ws, str):
+        need = int(_lib().qlin_gemm_multi_workspace_bytes(arr, count, m))
+        ws = workspace(need, X.device)
+    wsb = 0 if ws is None else ws.numel() * ws.element_size()
+    st = _lib().qlin_gemm_multi(arr, count, X.data_ptr(), m, X.stride(0), yp, ld, _ptr(ws), wsb,
+                                _stream())
+    _check(st, "qlin_gemm_multi")
+    return list(Ys)

@@ -195,6 +195,22 @@ qlin_status qlin_gemm(const qlin_weight* w, const uint16_t* X, int32_t m, int64_
                       hipStream_t stream);
 
 /*
+ * Several GEMMs that share X, in one launch (the prefill form of the decode
+ * step's grouping: q, k and v, or gate and up, of a layer read the same
+ * normalized activations):  Y_i = X . W_i^T,  i = 0 .. count-1, count <= 4.
+ * w: `count` PACKED weights with the same k, bits and group; Y[i] fp32
+ * [m, ld_y[i]] (ld_y[i] >= w[i].n).  Each Y_i is what qlin_gemm gives for
+ * w[i] to the same tolerance.  Workspace sized by
+ * qlin_gemm_multi_workspace_bytes(w, count, m).  Errors as for qlin_gemm,
+ * plus count outside 1..4 or different k -> QLIN_ERR_SHAPE, different bits or
+ * group -> QLIN_ERR_FORMAT.
+ */
+int64_t qlin_gemm_multi_workspace_bytes(const qlin_weight* w, int32_t count, int32_t m);
+qlin_status qlin_gemm_multi(const qlin_weight* w, int32_t count, const uint16_t* X, int32_t m,
+                            int64_t ld_x, float* const* Y, const int64_t* ld_y, void* workspace,
+                            int64_t workspace_bytes, hipStream_t stream);
+
+/*
  * Several decode GEMVs that share x, in one launch (the Enargeia page, "One
  * decode step": the per-token dispatch list, where q, k and v, and gate and
  * up, each read the same normalized activation):

@@ -31,7 +31,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     declared = header_functions()
-    assert len(declared) == 16
+    assert len(declared) == 18
     assert sorted(qlin.EXPORTS) == declared
     for name in declared:
         assert hasattr(lib, name), name
@@ -246,8 +246,32 @@ def test_quantize_batch_validation(lib):
     assert qbatch(lib, [qjob(0, codes=None), qjob(1, codes=None)], group=0) in (OK, NODEV)
 
 
+def gmulti(lib, ws, ys, lds, X=FAKE + (3 << 30), m=4, ldx=128, count=None, ws_=None, wsb=0):
+    count = len(ws) if count is None else count
+    return lib.qlin_gemm_multi(weights(*ws), count, X, m, ldx, ptrs(*ys),
+                               (ctypes.c_int64 * len(lds))(*lds), ws_, wsb, None)
+
+
+def test_gemm_multi_validation(lib):
+    w0, w1 = weight(), other_weight(0, n=200)
+    assert gmulti(lib, [w0, w1], [Y0, Y1], [8, 200], X=None) == NULL
+    assert gmulti(lib, [w0, w1], [Y0, None], [8, 200]) == NULL
+    assert gmulti(lib, [w0, w1], [Y0, Y1], [8, 200], count=5) == SHAPE
+    assert gmulti(lib, [w0, w1], [Y0, Y1], [8, 100]) == SHAPE            # ld_y < n
+    assert gmulti(lib, [w0, other_weight(0, k=256)], [Y0, Y1], [8, 8]) == SHAPE
+    assert gmulti(lib, [w0, other_weight(0, bits=2)], [Y0, Y1], [8, 8]) == FORMAT
+    assert gmulti(lib, [w0, w1], [Y0, Y0 + 64], [8, 200]) == ALIAS       # outputs overlap
+    assert gmulti(lib, [w0, w1], [Y0, FAKE + 128], [8, 200]) == ALIAS    # output on w0 codes
+    assert gmulti(lib, [w0, w1], [Y0, Y1 + 4], [8, 200]) == ALIGN
+    assert gmulti(lib, [w0, w1], [Y0, Y1], [8, 200], m=0) == SHAPE
+    assert lib.qlin_gemm_multi_workspace_bytes(weights(w0, w1), 2, 4) == 0
+    big = weight(n=128, k=16384)
+    assert lib.qlin_gemm_multi_workspace_bytes(weights(big, big), 2, 8) > 65536
+
+
 @pytest.mark.skipif(torch.cuda.is_available(), reason="checks the no-GPU path")
 def test_no_device(lib):
+    assert gmulti(lib, [weight(), other_weight(0, n=200)], [Y0, Y1], [8, 200]) == NODEV
     assert qbatch(lib, [qjob(0), qjob(1)]) == NODEV
     assert embed(lib, weight()) == NODEV
     assert quant(lib) == NODEV

@@ -156,3 +156,31 @@ def test_gemv_swiglu_extremes():
     hh, hh16 = host(h), host(h16)
     assert not np.any(np.isnan(hh))
     check_swiglu(hh, hh16, x16, wg, wu, "extremes")
+
+
+GEMM_MULTI_CASES = [
+    ((896, 128, 128), 896, 8),       # skinny (M <= 16)
+    ((896, 128, 128), 896, 17),
+    ((896, 128, 128), 896, 128),
+    ((200, 64, 1, 130), 192, 100),   # four ragged matrices
+    ((4864, 4864), 896, 2048),       # gate/up at M = 2048: 128-row tiles
+    ((896, 128, 128), 896, 300),
+    ((640, 128), 8192, 100),         # split K
+    ((2048, 1024, 1024), 1024, 1),
+]
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4, 8])
+@pytest.mark.parametrize("ns,k,m", GEMM_MULTI_CASES)
+def test_gemm_multi(bits, ns, k, m):
+    rng = np.random.default_rng([75, bits, k, m, len(ns)])
+    mats = [packed(synth.master_weights(rng, n, k), bits, 64) for n in ns]
+    X = synth.activations(rng, m, k)
+    say(f"gemm_multi bits={bits} ns={ns} k={k} m={m}")
+    Xd = dev(X)
+    Ys = [host(y) for y in qlin.gemm_multi([q for q, _ in mats], Xd)]
+    for i, (Y, (_, what)) in enumerate(zip(Ys, mats)):
+        check_tol(Y, X, what, f"matrix {i}")
+    again = [host(y) for y in qlin.gemm_multi([q for q, _ in mats], Xd)]
+    for a, b in zip(Ys, again):
+        assert np.array_equal(a, b)
