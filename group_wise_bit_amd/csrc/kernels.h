@@ -80,6 +80,9 @@ __device__ __forceinline__ void codes_and_store(const float* w, float s, int z,
 // numbered consecutively over the jobs (end[i] = items of jobs 0..i), and
 // each work-group finds its job by a scan over the ends.
 constexpr int kQuantBatch = 64;
+// Widths with a packed layout; 5-7 bits exist only as scale/zero of fp16 masters.
+template <int BITS>
+constexpr bool kPackable = BITS == 2 || BITS == 3 || BITS == 4 || BITS == 8;
 struct QuantJob {
   const uint16_t* w16;
   int64_t ld;
@@ -126,8 +129,9 @@ __global__ __launch_bounds__(WAVES * 64) void k_quantize_g64(const QuantBatch b)
   const int64_t mi = ((int64_t)t * q.kb + j) * kTile + lane;
   q.scale[mi] = sb;
   q.zero[mi] = (uint8_t)z;
-  if (q.codes != nullptr)
-    codes_and_store<BITS>(w, s, z, q.codes + mi * (2 * BITS));
+  if constexpr (kPackable<BITS>) {
+    if (q.codes != nullptr) codes_and_store<BITS>(w, s, z, q.codes + mi * (2 * BITS));
+  }
 }
 
 // One group per row.  Work item = tile; the WAVES waves split the K-blocks,
@@ -167,12 +171,14 @@ __global__ __launch_bounds__(WAVES * 64) void k_quantize_row(const QuantBatch b)
     q.scale[(int64_t)t * kTile + lane] = sb;
     q.zero[(int64_t)t * kTile + lane] = (uint8_t)z;
   }
-  if (q.codes == nullptr) return;
-  for (int j = wave; j < kb; j += WAVES) {
-    float w[64];
-    load_row_block(q.w16, q.ld, row, j, valid, w);
-    const int64_t bi = ((int64_t)t * kb + j) * kTile + lane;
-    codes_and_store<BITS>(w, s, z, q.codes + bi * (2 * BITS));
+  if constexpr (kPackable<BITS>) {
+    if (q.codes == nullptr) return;
+    for (int j = wave; j < kb; j += WAVES) {
+      float w[64];
+      load_row_block(q.w16, q.ld, row, j, valid, w);
+      const int64_t bi = ((int64_t)t * kb + j) * kTile + lane;
+      codes_and_store<BITS>(w, s, z, q.codes + bi * (2 * BITS));
+    }
   }
 }
 

@@ -35,7 +35,10 @@ inline Range range_of(const void* p, int64_t bytes) {
 }
 inline bool overlaps(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
 
+// Widths with a packed-code layout, and every width of the lever (scale/zero
+// precompute and the fused re-quantizing GEMV from fp16 masters).
 bool valid_bits(int bits) { return bits == 2 || bits == 3 || bits == 4 || bits == 8; }
+bool lever_bits(int bits) { return bits >= 2 && bits <= 8; }
 
 qlin_status check_nk(int32_t n, int32_t k) {
   if (n < 1 || n > kMaxN || k < kBlock || k > kMaxK || (k % kBlock) != 0) return QLIN_ERR_SHAPE;
@@ -85,7 +88,7 @@ qlin_status check_weight(const qlin_weight* w, bool allow_master, bool allow16) 
     if (w->ld != 0) return QLIN_ERR_SHAPE;
   } else if (w->format == QLIN_FMT_FP16_MASTER) {
     if (!allow_master) return QLIN_ERR_FORMAT;
-    if (!(valid_bits(w->bits) || (allow16 && w->bits == 16))) return QLIN_ERR_BITS;
+    if (!(lever_bits(w->bits) || (allow16 && w->bits == 16))) return QLIN_ERR_BITS;
     if (w->ld < w->k) return QLIN_ERR_SHAPE;
     if (w->ld % 8 != 0) return QLIN_ERR_ALIGN;
   } else {
@@ -245,6 +248,9 @@ qlin_status run_quant(const QuantJob* jobs, int count, int bits, bool row, hipSt
     case 2: launch_quant_batch<2>(jobs, count, row, st); break;
     case 3: launch_quant_batch<3>(jobs, count, row, st); break;
     case 4: launch_quant_batch<4>(jobs, count, row, st); break;
+    case 5: launch_quant_batch<5>(jobs, count, row, st); break;
+    case 6: launch_quant_batch<6>(jobs, count, row, st); break;
+    case 7: launch_quant_batch<7>(jobs, count, row, st); break;
     default: launch_quant_batch<8>(jobs, count, row, st); break;
   }
   return hip_status(hipGetLastError());
@@ -258,7 +264,7 @@ qlin_status check_quant_job(const uint16_t* w16, int64_t ld_w, int32_t n, int32_
                             const uint8_t* zero, QuantRanges& r) {
   qlin_status st = check_nk(n, k);
   if (st != QLIN_OK) return st;
-  if (!valid_bits(bits)) return QLIN_ERR_BITS;
+  if (!lever_bits(bits) || (codes != nullptr && !valid_bits(bits))) return QLIN_ERR_BITS;
   st = check_group(group, k);
   if (st != QLIN_OK) return st;
   if (w16 == nullptr || scale == nullptr || zero == nullptr) return QLIN_ERR_NULL;
@@ -693,6 +699,9 @@ qlin_status qlin_gemv(const qlin_weight* w, const uint16_t* x, float* y, void* w
       case 2: launch_gemv_fused<2>(w, x2, y, part, tick, sp, stream); break;
       case 3: launch_gemv_fused<3>(w, x2, y, part, tick, sp, stream); break;
       case 4: launch_gemv_fused<4>(w, x2, y, part, tick, sp, stream); break;
+      case 5: launch_gemv_fused<5>(w, x2, y, part, tick, sp, stream); break;
+      case 6: launch_gemv_fused<6>(w, x2, y, part, tick, sp, stream); break;
+      case 7: launch_gemv_fused<7>(w, x2, y, part, tick, sp, stream); break;
       case 8: launch_gemv_fused<8>(w, x2, y, part, tick, sp, stream); break;
       default: launch_gemv_fused<16>(w, x2, y, part, tick, sp, stream); break;
     }

@@ -65,7 +65,7 @@ typedef enum qlin_status {
   QLIN_OK = 0,
   QLIN_ERR_NULL = 1,        /* a required pointer is NULL                        */
   QLIN_ERR_SHAPE = 2,       /* n, k or m out of range, k % 64 != 0, pitch < row  */
-  QLIN_ERR_BITS = 3,        /* bits not in {2,3,4,8} (16: FP16_MASTER gemv only)  */
+  QLIN_ERR_BITS = 3,        /* bits not allowed for the call (see qlin_weight)      */
   QLIN_ERR_GROUP = 4,       /* group neither 64 nor k                            */
   QLIN_ERR_ALIGN = 5,       /* a pointer not 16-byte aligned, or a pitch not a
                                multiple of 8 elements                            */
@@ -85,7 +85,8 @@ enum {
 typedef struct qlin_weight {
   int32_t n;                /* output rows                                        */
   int32_t k;                /* reduction length, multiple of 64                   */
-  int32_t bits;             /* 2, 3, 4, 8; or 16 = unquantized (FP16_MASTER)       */
+  int32_t bits;             /* PACKED: 2, 3, 4, 8.  FP16_MASTER: 2 .. 8, or 16 =
+                               unquantized (the whole lever)                       */
   int32_t group;            /* 64, or k for one group per row                     */
   int32_t format;           /* QLIN_FMT_*                                         */
   int32_t reserved;         /* must be 0                                          */
@@ -116,6 +117,8 @@ int64_t qlin_meta_entries(int32_t n, int32_t k, int32_t group);
  * precompute, then codes).  Bitcrush README, "Under the hood": a scale/zero
  * precompute pass, then the group-wise affine rounding.
  *   w16      fp16 masters [n, ld_w] row-major, ld_w >= k, ld_w % 8 == 0.
+ *   bits     2 .. 8; codes need a packed layout: 2, 3, 4 or 8 (5 .. 7 with
+ *            codes != NULL -> QLIN_ERR_BITS).
  *   codes    packed codes out, qlin_packed_bytes(n, k, bits) bytes; pass NULL to
  *            compute only scale and zero (a change of bit width then needs no
  *            new codes: the fused matmul re-rounds on the fly).

@@ -5,7 +5,7 @@ Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
 its binding, and they import nothing from it.
 """
 from .reference import (  # noqa: F401
-    SUPPORTED_BITS, qmax_for, rtn_scale_zero, rtn_codes, quantize, dequantize,
+    SUPPORTED_BITS, LEVER_BITS, qmax_for, rtn_scale_zero, rtn_codes, quantize, dequantize,
     matmul_ref, tolerance_scale, fused_weights, silu, swiglu_ref, swiglu_tolerance,
     SILU_SLOPE_MAX,
 )

@@ -28,13 +28,17 @@ from __future__ import annotations
 import numpy as np
 
 F32 = np.float32
+# Bit widths with a packed-code layout; the quantizer arithmetic itself holds
+# at every width of the lever (Bitcrush README, "The machine": the lever runs
+# from 16 bits down to 2), used with the fp16 masters at 5, 6 and 7 bits.
 SUPPORTED_BITS = (2, 3, 4, 8)
+LEVER_BITS = (2, 3, 4, 5, 6, 7, 8)
 
 
 def qmax_for(bits: int) -> int:
     """Largest code at ``bits`` bits (codes are unsigned, 0..2^bits-1)."""
-    if bits not in SUPPORTED_BITS:
-        raise ValueError(f"bits must be one of {SUPPORTED_BITS}, got {bits}")
+    if bits not in LEVER_BITS:
+        raise ValueError(f"bits must be one of {LEVER_BITS}, got {bits}")
     return (1 << bits) - 1
 
 

@@ -80,6 +80,26 @@ def test_quantize_bit_exact(bits, group, shape):
     assert np.array_equal(host(only.zero), oracle.tile_meta(z))
 
 
+@pytest.mark.parametrize("bits", [5, 6, 7])
+@pytest.mark.parametrize("group", [64, "K"])
+def test_quantize_scale_zero_lever_widths(bits, group):
+    """5-7 bits (no packed layout): scale and zero bit-exact, also batched."""
+    rng = np.random.default_rng(700 + bits)
+    w16 = np.concatenate([synth.master_weights(rng, 130, 448),
+                          synth.edge_groups(bits, rng, n_rows=64, k=448)])
+    g = 448 if group == "K" else 64
+    say(f"quantize scale/zero bits={bits} group={g}")
+    q = qlin.quantize(dev(w16), bits, group, codes=False)
+    qb = qlin.quantize_batch([dev(w16)], bits, group, codes=False)[0]
+    s16, z = oracle.rtn_scale_zero(w16, bits, g)
+    for got in (q, qb):
+        assert np.array_equal(host(got.scale).view(np.uint16)[:oracle.tile_meta(s16).size],
+                              oracle.tile_meta(s16).view(np.uint16))
+        assert np.array_equal(host(got.zero)[:oracle.tile_meta(z).size], oracle.tile_meta(z))
+    with pytest.raises(qlin.QlinError):
+        qlin.quantize(dev(w16), bits, group, codes=True)
+
+
 @pytest.mark.parametrize("bits", [2, 3, 4, 8])
 @pytest.mark.parametrize("group", [64, "K"])
 def test_quantize_edge_groups(bits, group):
@@ -131,7 +151,7 @@ def test_gemv_packed(bits, group, shape):
         assert np.array_equal(ye.astype(np.float64), what[:, kk]), f"one-hot k={kk}"
 
 
-@pytest.mark.parametrize("bits", [2, 3, 4, 8, 16])
+@pytest.mark.parametrize("bits", [2, 3, 4, 5, 6, 7, 8, 16])
 @pytest.mark.parametrize("group", [64, "K"])
 @pytest.mark.parametrize("shape", [(896, 896), (200, 192), (1, 64), (1024, 2048)])
 def test_gemv_fused(bits, group, shape):
@@ -160,7 +180,7 @@ def test_gemv_fused(bits, group, shape):
         assert np.array_equal(ye.astype(np.float64), what[:, kk]), f"one-hot k={kk}"
 
 
-@pytest.mark.parametrize("bits", [2, 3, 4, 8])
+@pytest.mark.parametrize("bits", [2, 3, 4, 5, 6, 7, 8])
 def test_gemv_fused_edge_groups_exact(bits):
     """Every implicit code of the fused kernel, on groups full of exact ties,
     clamps, constant and one-signed groups: one-hot x over all 256 columns."""

@@ -71,7 +71,7 @@ def exact_quantize(w16: np.ndarray, bits: int, group: int):
     return codes, scales, zeros
 
 
-@pytest.mark.parametrize("bits", [2, 3, 4, 8])
+@pytest.mark.parametrize("bits", [2, 3, 4, 5, 6, 7, 8])
 @pytest.mark.parametrize("group", [64, 128])
 def test_quantizer_matches_exact_arithmetic(bits, group):
     rng = np.random.default_rng(100 + bits)

@@ -18,7 +18,7 @@ import oracle
 import synth
 
 
-@pytest.mark.parametrize("bits", [2, 3, 4, 8])
+@pytest.mark.parametrize("bits", [2, 3, 4, 5, 6, 7, 8])
 @pytest.mark.parametrize("group", [64, "K"])
 def test_round_trip_bounds(bits, group):
     rng = np.random.default_rng(bits * 10 + (1 if group == "K" else 0))
@@ -52,7 +52,7 @@ def test_round_trip_bounds(bits, group):
     assert np.all(what[s == 0] == 0)
 
 
-@pytest.mark.parametrize("bits", [3, 4, 8])
+@pytest.mark.parametrize("bits", [3, 4, 5, 6, 7, 8])
 def test_mse_is_uniform_noise(bits):
     rng = np.random.default_rng(42)
     w16 = synth.master_weights(rng, 512, 1024)
