@@ -241,6 +241,20 @@ __device__ __forceinline__ float sum_splits(const float* __restrict__ p, int64_t
   return acc;
 }
 
+// Scale of a block that may lie past the wave's range (its address clamped by
+// the caller): the load is always issued, and the converted value multiplied
+// by 1 or 0 where it is used.  A select would let the compiler move the load
+// into a branch, where its conversion waits for it at once (vmcnt(0)) and
+// serializes the blocks that were meant to be in flight together.
+__device__ __forceinline__ float masked_scale(uint16_t raw, bool valid) {
+  return h2f(raw) * (valid ? 1.f : 0.f);
+}
+
+// Keeps the compiler's scheduler from moving work across this point: placed
+// after the loads of all blocks in flight, so that every load is issued before
+// the first decode waits for its data.
+__device__ __forceinline__ void loads_issued() { __builtin_amdgcn_sched_barrier(0); }
+
 // -------------------------------------------------------- packed GEMV --
 // One work-group per (tile, split); lane = row of the tile.  A wave issues the
 // loads of up to U blocks before decoding any, so a short K range costs one
@@ -278,7 +292,7 @@ __device__ __forceinline__ void tile_dot(const uint32_t* const (&codes_t)[NM],
   constexpr int WPB = 2 * BITS;
   for (int jb = jfirst; jb < j1; jb += jstep * U) {
     uint32_t wd[U][NM][WPB];
-    float s[U][NM];
+    uint16_t sr[U][NM];
     int z[U][NM], jj[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -288,10 +302,11 @@ __device__ __forceinline__ void tile_dot(const uint32_t* const (&codes_t)[NM],
 #pragma unroll
       for (int m = 0; m < NM; ++m) {
         load_block_words<BITS>(codes_t[m] + ((int64_t)jj[u] * kTile + lane) * WPB, wd[u][m]);
-        s[u][m] = j < j1 ? h2f(scale_t[m][mi]) : 0.f;
+        sr[u][m] = scale_t[m][mi];
         z[u][m] = zero_t[m][mi];
       }
     }
+    if constexpr (U > 1) loads_issued();
     f16x2 xc[32], xn[32];
 #pragma unroll
     for (int i = 0; i < 32; ++i) xc[i] = x2[(int64_t)jj[0] * 32 + i];
@@ -303,7 +318,8 @@ __device__ __forceinline__ void tile_dot(const uint32_t* const (&codes_t)[NM],
       }
 #pragma unroll
       for (int m = 0; m < NM; ++m)
-        acc[m] = __builtin_fmaf(s[u][m], block_dot<BITS>(wd[u][m], xc, z[u][m], magic), acc[m]);
+        acc[m] = __builtin_fmaf(masked_scale(sr[u][m], jb + u * jstep < j1),
+                                block_dot<BITS>(wd[u][m], xc, z[u][m], magic), acc[m]);
       if (u + 1 < U) {
 #pragma unroll
         for (int i = 0; i < 32; ++i) xc[i] = xn[i];
@@ -416,6 +432,267 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemv_packed(
   }
 }
 
+// ------------------------------------------------ narrow packed GEMV --
+// For launches of few tiles: a work-group covers 64/NG rows of a tile (grid.x =
+// NG x launch tiles), so a small matrix is spread over NG times as many
+// compute units as one work-group per tile would reach.  Lane = NG*r + g: row
+// r of the work-group's rows and slice g of every 64-code block (codes
+// (64/NG)*g onwards), so the lanes of a wave read one contiguous run of the
+// block per instruction.  x differs between slices and is read with vector
+// loads (128/NG bytes per lane and block; NG distinct addresses per wave).
+template <int BITS, int NG>
+struct SliceWords {
+  static constexpr int n = BITS == 3 ? 2 : (NG == 4 ? BITS / 2 : (BITS == 2 ? 1 : BITS / 4));
+};
+
+// The words holding slice g of one row's block (row_blk = the row's first word).
+template <int BITS, int NG>
+__device__ __forceinline__ void load_slice_words(const uint32_t* __restrict__ row_blk, int g,
+                                                 uint32_t* wd) {
+  constexpr int CPS = 64 / NG;                        // codes per slice
+  if constexpr (BITS == 3) {
+    // the low-bit word of the slice's 16-code half-run, the run's third-bit word
+    const int c0 = CPS * g, run = c0 >> 5, u = (c0 >> 4) & 1;
+    wd[0] = row_blk[3 * run + u];
+    wd[1] = row_blk[3 * run + 2];
+  } else if constexpr (BITS == 2 && NG == 8) {
+    wd[0] = row_blk[g >> 1];                          // 16 codes per word
+  } else {
+    constexpr int W = SliceWords<BITS, NG>::n;        // whole words
+    if constexpr (W == 1) {
+      wd[0] = row_blk[g];
+    } else if constexpr (W == 2) {
+      const uint2 v = reinterpret_cast<const uint2*>(row_blk)[g];
+      wd[0] = v.x; wd[1] = v.y;
+    } else {
+      const uint4 v = reinterpret_cast<const uint4*>(row_blk)[g];
+      wd[0] = v.x; wd[1] = v.y; wd[2] = v.z; wd[3] = v.w;
+    }
+  }
+}
+
+// 2- and 3-bit terms of 8 codes: the pairs (2p, 2p+1) of the 8, p = 0..3,
+// come out of v under the mask of p with scale class S = 4^p; xs[p] is their
+// x pair.  Returns their sum over the 8 codes of x_k * (q_k - z), unscaled.
+__device__ __forceinline__ float low_bits8(uint32_t v, const f16x2* xs, int z, uint32_t kMagic) {
+  float a[4];
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const uint32_t m = (3u << (2 * p)) | (3u << (16 + 2 * p));
+    const f16x2 h = as_h2((v & m) | kMagic) - as_h2(zconst(z, 2 * p));
+    a[p] = __builtin_amdgcn_fdot2(h, xs[p], 0.f, false);
+  }
+  return a[0] + a[1] * 0.25f + a[2] * 0.0625f + a[3] * 0.015625f;
+}
+
+// 3-bit: low bits L and third bits H (already aligned like the 2-bit fields).
+__device__ __forceinline__ float three_bits8(uint32_t L, uint32_t H, const f16x2* xs, int z,
+                                             uint32_t kMagic) {
+  float a[4];
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const uint32_t m2 = (3u << (2 * p)) | (3u << (16 + 2 * p));
+    const uint32_t m1 = (1u << (2 * p + 2)) | (1u << (2 * p + 18));
+    const uint32_t t = (L & m2) | (H & ~m2);          // bit-field insert
+    const f16x2 h = as_h2((t & (m2 | m1)) | kMagic) - as_h2(zconst(z, 2 * p));
+    a[p] = __builtin_amdgcn_fdot2(h, xs[p], 0.f, false);
+  }
+  return a[0] + a[1] * 0.25f + a[2] * 0.0625f + a[3] * 0.015625f;
+}
+
+// 4-bit terms of the 8 codes of word v (x pairs xs[0..3]).
+__device__ __forceinline__ float four_bits8(uint32_t v, const f16x2* xs, int z, uint32_t kMagic) {
+  const f16x2 c1 = as_h2(zconst(z, 0)), c16 = as_h2(zconst(z, 4));
+  const uint32_t vs = v >> 8;
+  const float a0 = __builtin_amdgcn_fdot2(as_h2((v & 0x000F000Fu) | kMagic) - c1, xs[0], 0.f, false);
+  const float b0 = __builtin_amdgcn_fdot2(as_h2((v & 0x00F000F0u) | kMagic) - c16, xs[1], 0.f, false);
+  const float a1 = __builtin_amdgcn_fdot2(as_h2((vs & 0x000F000Fu) | kMagic) - c1, xs[2], 0.f, false);
+  const float b1 = __builtin_amdgcn_fdot2(as_h2((vs & 0x00F000F0u) | kMagic) - c16, xs[3], 0.f, false);
+  return (a0 + a1) + (b0 + b1) * 0.0625f;
+}
+
+// 8-bit terms of the 8 codes of words v, u (x pairs xs[0..3]).
+__device__ __forceinline__ float eight_bits8(uint32_t v, uint32_t u, const f16x2* xs, int z,
+                                             uint32_t kMagic) {
+  const f16x2 c = as_h2(zconst(z, 0));
+  const f16x2 h0 = as_h2(__builtin_amdgcn_perm(0x64646464u, v, 0x04020400u)) - c;
+  const f16x2 h1 = as_h2(__builtin_amdgcn_perm(0x64646464u, v, 0x04030401u)) - c;
+  const f16x2 g0 = as_h2(__builtin_amdgcn_perm(0x64646464u, u, 0x04020400u)) - c;
+  const f16x2 g1 = as_h2(__builtin_amdgcn_perm(0x64646464u, u, 0x04030401u)) - c;
+  const float a0 = __builtin_amdgcn_fdot2(h0, xs[0], 0.f, false);
+  const float b0 = __builtin_amdgcn_fdot2(h1, xs[1], 0.f, false);
+  const float a1 = __builtin_amdgcn_fdot2(g0, xs[2], 0.f, false);
+  const float b1 = __builtin_amdgcn_fdot2(g1, xs[3], 0.f, false);
+  return (a0 + a1) + (b0 + b1);
+}
+
+// sum over the codes of slice g of x_k * (q_k - z), unscaled; xs = the
+// slice's x pairs.  The decode of block_dot, restricted to the slice.  A
+// slice of 16 codes is two 8-code halves; the second half of a 2- or 3-bit
+// half-run sits 8 bits (low bits) / 1 bit (aligned third bits) higher.
+template <int BITS, int NG>
+__device__ __forceinline__ float slice_dot(const uint32_t* wd, const f16x2* xs, int z, int g,
+                                           uint32_t kMagic) {
+  if constexpr (BITS == 4) {
+    if constexpr (NG == 4) return four_bits8(wd[0], xs, z, kMagic) + four_bits8(wd[1], xs + 4, z, kMagic);
+    else return four_bits8(wd[0], xs, z, kMagic);
+  } else if constexpr (BITS == 8) {
+    if constexpr (NG == 4)
+      return eight_bits8(wd[0], wd[1], xs, z, kMagic) + eight_bits8(wd[2], wd[3], xs + 4, z, kMagic);
+    else return eight_bits8(wd[0], wd[1], xs, z, kMagic);
+  } else if constexpr (BITS == 2) {
+    if constexpr (NG == 4) {
+      return low_bits8(wd[0], xs, z, kMagic) + low_bits8(wd[0] >> 8, xs + 4, z, kMagic);
+    } else {
+      return low_bits8(wd[0] >> (8 * (g & 1)), xs, z, kMagic);
+    }
+  } else {  // BITS == 3
+    const uint32_t H = wd[1];
+    const int c0 = (64 / NG) * g;
+    const uint32_t Hu = ((c0 >> 4) & 1) ? __builtin_amdgcn_alignbit(H, H, 8) : H;
+    if constexpr (NG == 4) {
+      return three_bits8(wd[0], Hu, xs, z, kMagic) + three_bits8(wd[0] >> 8, Hu >> 1, xs + 4, z, kMagic);
+    } else {
+      const bool hi = (c0 >> 3) & 1;
+      return three_bits8(hi ? wd[0] >> 8 : wd[0], hi ? Hu >> 1 : Hu, xs, z, kMagic);
+    }
+  }
+}
+
+// Sum over the NG consecutive lanes of a row's slices, the same order for
+// every row: pairs, then quads (DPP), then octets (swizzle).
+template <int NG>
+__device__ __forceinline__ float slice_sum(float v) {
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
+                                                             0xB1, 0xF, 0xF, false));  // [1,0,3,2]
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
+                                                             0x4E, 0xF, 0xF, false));  // [2,3,0,1]
+  if constexpr (NG == 8)
+    v += __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v),
+                                                               0x1F | (4 << 10)));     // lane ^ 4
+  return v;
+}
+
+// grid = (NG x launch tiles, splits), block = WAVES waves.  Work-group b
+// covers rows RW*(b % NG) .. +RW-1 (RW = 64/NG) of launch tile b / NG; its
+// waves take the K-blocks j0+w, j0+w+WAVES, ... of the split's range, U at a
+// time, all loads of the U blocks issued before any decode.  Outputs, sets,
+// SwiGLU pairs and split-K partials as in k_gemv_packed (partials per launch
+// row, tickets per work-group).
+template <int BITS, int NG, int WAVES, int U, bool SWIGLU>
+__global__ __launch_bounds__(WAVES * 64) void k_gemv_narrow(
+    const GemvSet set, const f16x2* __restrict__ x2, float* __restrict__ part,
+    uint32_t* __restrict__ tickets, int kb, int G, int splits, int kbps,
+    uint16_t* __restrict__ h16) {
+  constexpr int WPB = 2 * BITS;
+  constexpr int NM = SWIGLU ? 2 : 1;
+  constexpr int RW = kTile / NG;                      // rows per work-group
+  constexpr int SW = SliceWords<BITS, NG>::n;
+  constexpr int XP = 32 / NG;                         // x pairs per slice
+  __shared__ float red[NM][WAVES][RW];
+  const uint32_t magic = vreg_const(kMagic);
+  const int lane = lane_id(), wave = wave_id();
+  const int r = lane / NG, g = lane % NG;
+  const int sp = blockIdx.y;
+  const int lt = blockIdx.x / NG, part_i = blockIdx.x % NG;
+  const uint32_t* codes = set.codes[0];
+  const uint16_t* scale = set.scale[0];
+  const uint8_t* zero = set.zero[0];
+  float* y = set.y[0];
+  int n = set.n[0], tb = 0;
+  if constexpr (!SWIGLU) {
+#pragma unroll
+    for (int i = 1; i < kMaxMats; ++i)
+      if (i < set.count && lt >= set.tile_end[i - 1]) {
+        codes = set.codes[i]; scale = set.scale[i]; zero = set.zero[i];
+        y = set.y[i]; n = set.n[i]; tb = set.tile_end[i - 1];
+      }
+  }
+  const int t = lt - tb;
+  const int R = part_i * RW + r;                      // row within the tile
+  const int64_t ct = (int64_t)t * kb * kTile * WPB, mt = (int64_t)t * G * kTile;
+  const uint32_t* codes_t[NM];
+  const uint16_t* scale_t[NM];
+  const uint8_t* zero_t[NM];
+  codes_t[0] = codes + ct; scale_t[0] = scale + mt; zero_t[0] = zero + mt;
+  if constexpr (SWIGLU) {
+    codes_t[NM - 1] = set.codes[1] + ct;
+    scale_t[NM - 1] = set.scale[1] + mt;
+    zero_t[NM - 1] = set.zero[1] + mt;
+  }
+  const int j0 = sp * kbps;
+  const int j1 = min(kb, j0 + kbps);
+  float acc[NM];
+#pragma unroll
+  for (int m = 0; m < NM; ++m) acc[m] = 0.f;
+  for (int jb = j0 + wave; jb < j1; jb += WAVES * U) {
+    uint32_t wd[U][NM][SW];
+    uint16_t sr[U][NM];
+    int z[U][NM];
+    f16x2 xs[U][XP];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int j = jb + u * WAVES;
+      const int jj = j < j1 ? j : j1 - 1;     // past the range: re-read, scale 0
+      const int64_t mi = (int64_t)((G == 1) ? 0 : jj) * kTile + R;
+#pragma unroll
+      for (int m = 0; m < NM; ++m) {
+        load_slice_words<BITS, NG>(codes_t[m] + ((int64_t)jj * kTile + R) * WPB, g, wd[u][m]);
+        sr[u][m] = scale_t[m][mi];
+        z[u][m] = zero_t[m][mi];
+      }
+      const uint4* xp = reinterpret_cast<const uint4*>(x2 + (int64_t)jj * 32 + XP * g);
+#pragma unroll
+      for (int i = 0; i < XP / 4; ++i) {
+        const uint4 xv = xp[i];
+        xs[u][4 * i + 0] = as_h2(xv.x); xs[u][4 * i + 1] = as_h2(xv.y);
+        xs[u][4 * i + 2] = as_h2(xv.z); xs[u][4 * i + 3] = as_h2(xv.w);
+      }
+    }
+    if constexpr (U > 1) loads_issued();
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int m = 0; m < NM; ++m)
+        acc[m] = __builtin_fmaf(masked_scale(sr[u][m], jb + u * WAVES < j1),
+                                slice_dot<BITS, NG>(wd[u][m], xs[u], z[u][m], g, magic), acc[m]);
+  }
+#pragma unroll
+  for (int m = 0; m < NM; ++m) {
+    acc[m] = slice_sum<NG>(acc[m]);
+    if (g == 0) red[m][wave][r] = acc[m];
+  }
+  lds_barrier();
+  if (wave != 0 || lane >= RW) return;
+  float tot[NM];
+#pragma unroll
+  for (int m = 0; m < NM; ++m) {
+    tot[m] = red[m][0][lane];
+#pragma unroll
+    for (int w = 1; w < WAVES; ++w) tot[m] += red[m][w][lane];
+  }
+  if (splits > 1) {
+    // part[split][matrix][launch row], launch row = RW * work-group + lane
+    const int64_t np = (int64_t)gridDim.x * RW;
+    const int64_t grow = (int64_t)blockIdx.x * RW + lane;
+#pragma unroll
+    for (int m = 0; m < NM; ++m) put_partial(part + ((int64_t)sp * NM + m) * np + grow, tot[m]);
+    partials_written();
+    if (!split_ticket(tickets, blockIdx.x, splits)) return;
+#pragma unroll
+    for (int m = 0; m < NM; ++m) tot[m] = sum_splits(part + m * np + grow, NM * np, splits);
+  }
+  const int row = t * kTile + part_i * RW + lane;
+  if (row >= n) return;
+  if constexpr (SWIGLU) {
+    const float h = silu(tot[0]) * tot[NM - 1];
+    if (y != nullptr) y[row] = h;
+    if (h16 != nullptr) h16[row] = __builtin_bit_cast(uint16_t, (f16)h);
+  } else {
+    y[row] = tot[0];
+  }
+}
+
 // ------------------------------------------------------ fused RTN GEMV --
 // Reads the fp16 masters, re-rounds every weight with the group's scale/zero
 // as it is read (codes never stored), accumulates x * (q - z) per group and
@@ -449,7 +726,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemv_fused(
       for (int i = 0; i < 8; ++i) wvu[u][i] = wr[(int64_t)jj[u] * 8 + i];
       if constexpr (BITS != 16) {
         const int64_t mi = ((int64_t)t * G + ((G == 1) ? 0 : jj[u])) * kTile + lane;
-        su[u] = j < j1 ? h2f(scale[mi]) : 0.f;
+        su[u] = masked_scale(scale[mi], j < j1);
         zu[u] = zero[mi];
       } else {
         su[u] = j < j1 ? 1.f : 0.f;

@@ -163,23 +163,32 @@ constexpr int kFusedUnroll = 1;    // one K-block in flight per wave, fused GEMV
 // GEMV launch shape: one work-group per (tile, split); its waves split the
 // split's K-blocks.  Each wave keeps up to `unroll` blocks in flight, so the
 // work-group is sized to cover the K range in about one round of loads.
-struct GemvCfg { int waves, splits, kbps, unroll; };
+struct GemvCfg {
+  int waves, splits, kbps, unroll;
+  int rows;     // packed kernels: rows per work-group, 64 (k_gemv_packed) or 16, 8 (k_gemv_narrow)
+};
 
-GemvCfg gemv_config(int64_t tiles, int kb, int unroll, int64_t ws_bytes) {
-  // Measured on MI355X (graph-replayed launches over rotating cold weights,
-  // 896..151936 x 896..12288, int4 and fp16 masters): without a split, a
-  // launch of T tiles runs on only T compute units, so shapes with up to 256
-  // tiles split K across work-groups (a split costs ~2 us of partial-sum
-  // round trips, so only long K pays).  The packed kernel keeps 16 waves per
-  // work-group and splits to ~16 K-blocks per split (12 with fewer than 32
-  // tiles); above 128 tiles, 8 waves and 8-block splits.  The fused kernel
-  // is ALU-heavier (about 7 VALU ops per weight): 8 waves and about 4 K-blocks
-  // per split (at most 8 splits), 4 waves x 4 splits above 128 tiles.
+GemvCfg gemv_config(int64_t tiles, int kb, int unroll, int64_t ws_bytes, bool pair = false,
+                    int bits = 4) {
+  // Measured on MI355X (graph-replayed launches over rotating cold weights;
+  // bits 2, 3, 4, 8; the Qwen2.5-0.5B, Qwen3-0.6B and Qwen3-8B layer shapes,
+  // q/k/v sets and gate/up pairs; fp16 masters for the fused kernel).  A
+  // launch of few tiles is latency-bound and runs on as many compute units as
+  // it has work-groups, while a K split costs ~1.3 us of partial-sum round
+  // trips.  So the packed kernels narrow the work-group first (8 or 16 rows
+  // over 8 / 4 slices of each block) while tiles x K-blocks <= 4096, and split
+  // K when one wave would otherwise decode many blocks in sequence (long K
+  // over up to 128 tiles; 3-bit decode, the costliest, also over 129-256
+  // tiles).  Launches of many tiles use 4-wave work-groups, so that the tail
+  // of the grid is short.  The fused kernel is ALU-heavier (about 7 VALU ops
+  // per weight): 8 waves and about 4 K-blocks per split (at most 8 splits),
+  // 4 waves x 4 splits from 129 to 256 tiles.
   const bool fused = unroll == kFusedUnroll;
   int waves = fused ? 8 : 16;
   int splits = 1;
-  if (tiles <= 256) {
-    if (fused) {
+  int rows = 64;
+  if (fused) {
+    if (tiles <= 256) {
       if (tiles > 128) {
         waves = 4;
         splits = 4;
@@ -187,36 +196,47 @@ GemvCfg gemv_config(int64_t tiles, int kb, int unroll, int64_t ws_bytes) {
         splits = (kb + 3) / 4;        // ~4 K-blocks per split, at most 8 splits
         if (splits > 8) splits = 8;
       }
-    } else if (tiles <= 128) {
-      splits = (tiles < 32 && kb >= 64) ? kb / 12 : kb / 16;
-    } else {
-      waves = 8;
-      splits = kb / 8;
     }
-    if (splits > 16) splits = 16;
-    if (splits > kb) splits = kb;
-    if (splits < 1) splits = 1;
+  } else if (tiles > 256) {
+    waves = 4;
+  } else if (tiles > 128) {
+    if (bits == 3) {
+      waves = 8;
+      splits = 4;
+    }
+  } else if (tiles * kb <= 4096) {
+    rows = (pair || tiles >= 48) ? 16 : 8;
+    waves = (pair || kb >= 32) ? 16 : 8;
+    if (kb >= 128) splits = kb / 64;   // very long K over a few tiles
+  } else {
+    splits = kb >= 128 ? kb / 64 : kb / 16;
   }
-  // QLIN_TUNE_GEMV="waves,splits" overrides the choice (launch-shape sweeps)
+  if (splits > 16) splits = 16;
+  if (splits > kb) splits = kb;
+  if (splits < 1) splits = 1;
+  // QLIN_TUNE_GEMV="waves,splits[,rows]" overrides the choice (launch-shape sweeps)
   if (const char* e = getenv("QLIN_TUNE_GEMV")) {
-    int w = 0, sp = 0;
-    if (sscanf(e, "%d,%d", &w, &sp) == 2 && (w == 4 || w == 8 || w == 16) && sp >= 1) {
+    int w = 0, sp = 0, rw = 64;
+    const int got = sscanf(e, "%d,%d,%d", &w, &sp, &rw);
+    if (got >= 2 && (w == 4 || w == 8 || w == 16) && sp >= 1 && (rw == 8 || rw == 16 || rw == 64)) {
       waves = w;
       splits = sp < kb ? sp : kb;
+      if (!fused) rows = rw;
     }
   }
-  if (tiles > kMaxSplitTiles) splits = 1;
+  // split-K tickets: one per work-group of the launch's first split
+  if (tiles * (kTile / rows) > kMaxSplitTiles) splits = 1;
   while (splits > 1 && kCounterBytes + (int64_t)splits * tiles * kTile * 4 > ws_bytes) --splits;
   const int kbps = (kb + splits - 1) / splits;
   // blocks kept in flight per wave: the wave's share of the split, up to `unroll`
   const int per_wave = (kbps + waves - 1) / waves;
   int u = 1;
   while (u < unroll && u < per_wave) u *= 2;
-  return GemvCfg{waves, (kb + kbps - 1) / kbps, kbps, u};
+  return GemvCfg{waves, (kb + kbps - 1) / kbps, kbps, u, rows};
 }
 
-int64_t gemv_ws_bytes(int64_t tiles, int kb, int unroll) {
-  const GemvCfg c = gemv_config(tiles, kb, unroll, INT64_MAX);
+int64_t gemv_ws_bytes(int64_t tiles, int kb, int unroll, int bits) {
+  const GemvCfg c = gemv_config(tiles, kb, unroll, INT64_MAX, false, bits);
   if (c.splits <= 1) return 0;
   return kCounterBytes + (int64_t)c.splits * tiles * kTile * 4;
 }
@@ -296,8 +316,15 @@ struct PackedLaunch {
 template <int B, int W, int U, bool SW>
 void launch_gemv_packed_w(const PackedLaunch& L, const f16x2* x2, float* part, uint32_t* tick,
                           GemvCfg c, hipStream_t st) {
-  hipLaunchKernelGGL((k_gemv_packed<B, W, U, SW>), dim3(L.tiles, c.splits), dim3(W * 64), 0, st,
-                     L.set, x2, part, tick, L.kb, L.G, c.splits, c.kbps, L.h16);
+  if (c.rows == 16)
+    hipLaunchKernelGGL((k_gemv_narrow<B, 4, W, U, SW>), dim3(4 * L.tiles, c.splits), dim3(W * 64),
+                       0, st, L.set, x2, part, tick, L.kb, L.G, c.splits, c.kbps, L.h16);
+  else if (c.rows == 8)
+    hipLaunchKernelGGL((k_gemv_narrow<B, 8, W, U, SW>), dim3(8 * L.tiles, c.splits), dim3(W * 64),
+                       0, st, L.set, x2, part, tick, L.kb, L.G, c.splits, c.kbps, L.h16);
+  else
+    hipLaunchKernelGGL((k_gemv_packed<B, W, U, SW>), dim3(L.tiles, c.splits), dim3(W * 64), 0, st,
+                       L.set, x2, part, tick, L.kb, L.G, c.splits, c.kbps, L.h16);
 }
 
 template <int B, bool SW>
@@ -328,19 +355,19 @@ void launch_gemv_packed(const PackedLaunch& L, const f16x2* x2, float* part, uin
 // Launch shape of a gate/up pair: every wave reads its blocks of both
 // matrices, so the pair takes the split of a single-matrix launch of the same
 // tiles; up to 2 blocks of each in flight per wave.
-GemvCfg swiglu_config(int64_t tiles, int kb, int64_t ws_bytes) {
-  GemvCfg c = gemv_config(tiles, kb, 2, INT64_MAX);
+GemvCfg swiglu_config(int64_t tiles, int kb, int64_t ws_bytes, int bits) {
+  GemvCfg c = gemv_config(tiles, kb, 2, INT64_MAX, true, bits);
   int splits = c.splits;
-  if (tiles > kMaxSplitTiles) splits = 1;
+  if (tiles * (kTile / c.rows) > kMaxSplitTiles) splits = 1;
   while (splits > 1 && kCounterBytes + 2 * (int64_t)splits * tiles * kTile * 4 > ws_bytes)
     --splits;
   const int kbps = (kb + splits - 1) / splits;
   const int per_wave = (kbps + c.waves - 1) / c.waves;
-  return GemvCfg{c.waves, (kb + kbps - 1) / kbps, kbps, per_wave >= 2 ? 2 : 1};
+  return GemvCfg{c.waves, (kb + kbps - 1) / kbps, kbps, per_wave >= 2 ? 2 : 1, c.rows};
 }
 
-int64_t swiglu_ws_bytes(int64_t tiles, int kb) {
-  const GemvCfg c = swiglu_config(tiles, kb, INT64_MAX);
+int64_t swiglu_ws_bytes(int64_t tiles, int kb, int bits) {
+  const GemvCfg c = swiglu_config(tiles, kb, INT64_MAX, bits);
   if (c.splits <= 1) return 0;
   return kCounterBytes + 2 * (int64_t)c.splits * tiles * kTile * 4;
 }
@@ -640,7 +667,7 @@ qlin_status qlin_quantize_batch(const qlin_quant_job* jobs, int32_t count, int32
 int64_t qlin_gemv_workspace_bytes(const qlin_weight* w) {
   if (check_weight(w, true, true) != QLIN_OK) return 0;
   return gemv_ws_bytes(tiles_of(w->n), w->k / kBlock,
-                       w->format == QLIN_FMT_PACKED ? kPackedUnroll : kFusedUnroll);
+                       w->format == QLIN_FMT_PACKED ? kPackedUnroll : kFusedUnroll, w->bits);
 }
 
 int64_t gemm_set_ws_bytes(const qlin_weight* w, int count, int32_t m) {
@@ -687,7 +714,7 @@ qlin_status qlin_gemv(const qlin_weight* w, const uint16_t* x, float* y, void* w
   const int kb = w->k / kBlock;
   const GemvCfg sp = gemv_config(tiles, kb, w->format == QLIN_FMT_PACKED ? kPackedUnroll
                                                                          : kFusedUnroll,
-                                 workspace_bytes);
+                                 workspace_bytes, false, w->bits);
   if (w->format == QLIN_FMT_PACKED)
     return run_packed(packed_launch(&w, &y, 1), w->bits, x, workspace, sp, stream);
   uint32_t* tick = static_cast<uint32_t*>(workspace);
@@ -713,7 +740,7 @@ int64_t qlin_gemv_multi_workspace_bytes(const qlin_weight* w, int32_t count) {
   if (w == nullptr || count < 1 || count > kMaxMats) return 0;
   for (int i = 0; i < count; ++i)
     if (check_weight(&w[i], false, false) != QLIN_OK || w[i].k != w[0].k) return 0;
-  return gemv_ws_bytes(set_tiles(w, count), w[0].k / kBlock, kPackedUnroll);
+  return gemv_ws_bytes(set_tiles(w, count), w[0].k / kBlock, kPackedUnroll, w[0].bits);
 }
 
 qlin_status qlin_gemv_multi(const qlin_weight* w, int32_t count, const uint16_t* x,
@@ -736,13 +763,13 @@ qlin_status qlin_gemv_multi(const qlin_weight* w, int32_t count, const uint16_t*
   const qlin_weight* wp[kMaxMats];
   for (int i = 0; i < count; ++i) wp[i] = &w[i];
   const PackedLaunch L = packed_launch(wp, y, count);
-  const GemvCfg c = gemv_config(L.tiles, L.kb, kPackedUnroll, workspace_bytes);
+  const GemvCfg c = gemv_config(L.tiles, L.kb, kPackedUnroll, workspace_bytes, false, w[0].bits);
   return run_packed(L, w[0].bits, x, workspace, c, stream);
 }
 
 int64_t qlin_gemv_swiglu_workspace_bytes(const qlin_weight* gate) {
   if (check_weight(gate, false, false) != QLIN_OK) return 0;
-  return swiglu_ws_bytes(tiles_of(gate->n), gate->k / kBlock);
+  return swiglu_ws_bytes(tiles_of(gate->n), gate->k / kBlock, gate->bits);
 }
 
 qlin_status qlin_gemv_swiglu(const qlin_weight* gate, const qlin_weight* up, const uint16_t* x,
@@ -765,7 +792,7 @@ qlin_status qlin_gemv_swiglu(const qlin_weight* gate, const qlin_weight* up, con
   L.tiles = (int)tiles_of(gate->n);
   L.swiglu = true;
   L.h16 = h16;
-  const GemvCfg c = swiglu_config(L.tiles, L.kb, workspace_bytes);
+  const GemvCfg c = swiglu_config(L.tiles, L.kb, workspace_bytes, gate->bits);
   return run_packed(L, gate->bits, x, workspace, c, stream);
 }
 

@@ -53,7 +53,7 @@ MULTI_CASES = [
     ((896, 128, 128), 896),          # Qwen2.5-0.5B q, k, v
     ((200, 64, 1, 130), 192),        # ragged rows, four matrices
     ((2048, 1024, 1024), 1024),      # Qwen3-0.6B q, k, v
-    ((4096, 1024, 1024), 4096),      # Qwen3-8B q, k, v (split-K)
+    ((4096, 1024, 1024), 4096),      # Qwen3-8B q, k, v
     ((77,), 640),                    # a set of one
 ]
 
@@ -118,6 +118,43 @@ def check_swiglu(h, h16, x16, wg, wu, label):
         assert np.all(err16 <= b16), f"{label}: h16 outside bound"
     if h is not None and h16 is not None:
         assert np.array_equal(h.astype(np.float16).view(np.uint16), h16.view(np.uint16))
+
+
+# launch shapes "waves,splits,rows per work-group" (whole tiles, 16 / 8 rows)
+ROW_WIDTHS = ["16,1,64", "8,1,16", "16,1,8", "4,3,8", "8,2,16", "8,3,64"]
+
+
+@pytest.mark.parametrize("bits", [3, 4])
+@pytest.mark.parametrize("cfg", ROW_WIDTHS)
+@pytest.mark.parametrize("ns,k", [((200, 64, 1, 130), 192), ((896, 128, 128), 896)])
+def test_gemv_multi_row_widths(bits, cfg, ns, k, monkeypatch):
+    """Sets of matrices at every work-group width: each output within its
+    matrix's tolerance; one-hot x exact."""
+    monkeypatch.setenv("QLIN_TUNE_GEMV", cfg)
+    rng = np.random.default_rng([75, bits, k, len(ns)])
+    mats = [packed(synth.master_weights(rng, n, k), bits, 64) for n in ns]
+    x16 = synth.activations(rng, 1, k)[0]
+    say(f"gemv_multi cfg={cfg} bits={bits} ns={ns} k={k}")
+    for i, (y, (_, what)) in enumerate(zip(qlin.gemv_multi([m[0] for m in mats], dev(x16)), mats)):
+        check_tol(host(y), x16, what, f"{cfg} matrix {i}")
+    for c in (0, 37, k - 1):
+        e = np.zeros(k, dtype=np.float16); e[c] = 1
+        for y, (_, what) in zip(qlin.gemv_multi([m[0] for m in mats], dev(e)), mats):
+            assert np.array_equal(host(y).astype(np.float64), what[:, c]), f"{cfg} one-hot {c}"
+
+
+@pytest.mark.parametrize("bits", [3, 4])
+@pytest.mark.parametrize("cfg", ROW_WIDTHS)
+@pytest.mark.parametrize("n,k", [(130, 192), (200, 1024)])
+def test_gemv_swiglu_row_widths(bits, cfg, n, k, monkeypatch):
+    monkeypatch.setenv("QLIN_TUNE_GEMV", cfg)
+    rng = np.random.default_rng([76, bits, n, k])
+    gate, wg = packed(synth.master_weights(rng, n, k), bits, 64)
+    up, wu = packed(synth.master_weights(rng, n, k), bits, 64)
+    x16 = synth.activations(rng, 1, k)[0]
+    say(f"gemv_swiglu cfg={cfg} bits={bits} n={n} k={k}")
+    h, h16 = qlin.gemv_swiglu(gate, up, dev(x16))
+    check_swiglu(host(h), host(h16), x16, wg, wu, f"{cfg} swiglu {n}x{k}")
 
 
 @pytest.mark.parametrize("bits", [2, 3, 4, 8])

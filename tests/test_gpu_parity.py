@@ -151,6 +151,36 @@ def test_gemv_packed(bits, group, shape):
         assert np.array_equal(ye.astype(np.float64), what[:, kk]), f"one-hot k={kk}"
 
 
+# launch shapes "waves,splits,rows per work-group": whole 64-row tiles, and
+# 16 / 8 rows over 4 / 8 slices of every block, with and without a K split
+ROW_WIDTHS = ["16,1,64", "8,1,16", "16,1,8", "4,3,8", "8,2,16"]
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4, 8])
+@pytest.mark.parametrize("group", [64, "K"])
+@pytest.mark.parametrize("shape", [(200, 192), (130, 4096), (1, 64), (896, 896)])
+@pytest.mark.parametrize("cfg", ROW_WIDTHS)
+def test_gemv_row_widths(bits, group, shape, cfg, monkeypatch):
+    """Every work-group width of the packed GEMV: within tolerance, and one-hot
+    x at positions covering every slice of the first and last block reproduces
+    the dequantized column exactly."""
+    monkeypatch.setenv("QLIN_TUNE_GEMV", cfg)
+    n, k = shape
+    g = k if group == "K" else 64
+    say(f"gemv packed cfg={cfg} bits={bits} group={g} shape={shape}")
+    rng = np.random.default_rng([n, k, bits, 5])
+    w16 = synth.master_weights(rng, n, k)
+    x16 = synth.activations(rng, 1, k)[0]
+    qw, codes, s16, z = oracle_packed(w16, bits, g)
+    what = oracle.dequantize(codes, s16, z, g)
+    check_tol(host(qlin.gemv(qw, dev(x16))), x16, what, cfg)
+    for kk in sorted(set(range(0, 64, 7)) | set(range(k - 64, k, 9))):
+        e = np.zeros(k, np.float16)
+        e[kk] = 1
+        ye = host(qlin.gemv(qw, dev(e)))
+        assert np.array_equal(ye.astype(np.float64), what[:, kk]), f"{cfg} one-hot k={kk}"
+
+
 @pytest.mark.parametrize("bits", [2, 3, 4, 5, 6, 7, 8, 16])
 @pytest.mark.parametrize("group", [64, "K"])
 @pytest.mark.parametrize("shape", [(896, 896), (200, 192), (1, 64), (1024, 2048)])
@@ -332,6 +362,28 @@ def test_split_k_paths(bits):
     check_tol(Y, x16, what, "split gemm")
     Y2 = host(qlin.gemm(qw, dev(x16), ws=None))
     check_tol(Y2, x16, what, "nosplit gemm")
+
+
+@pytest.mark.parametrize("bits", [3, 4])
+def test_split_k_full_tiles(bits):
+    """GEMV with K split across work-groups of whole 64-row tiles (many tiles,
+    long K): within tolerance, counters re-armed, partial region scratch."""
+    n, k = 2560, 8192
+    rng = np.random.default_rng(62 + bits)
+    w16 = synth.master_weights(rng, n, k)
+    x16 = synth.activations(rng, 1, k)[0]
+    qw, codes, s16, z = oracle_packed(w16, bits, 64)
+    what = oracle.dequantize(codes, s16, z, 64)
+    need = qlin.library().qlin_gemv_workspace_bytes(qw.c_struct())
+    assert need > 65536, "this shape is expected to split K"
+    say(f"split-K gemv, 64-row tiles, bits={bits}")
+    ws = torch.zeros(need, dtype=torch.uint8, device=DEV)
+    y = host(qlin.gemv(qw, dev(x16), ws=ws))
+    check_tol(y, x16, what, "split")
+    assert torch.count_nonzero(ws[:65536]).item() == 0
+    ws[65536:].fill_(0x5A)
+    assert np.array_equal(y, host(qlin.gemv(qw, dev(x16), ws=ws)))
+    check_tol(host(qlin.gemv(qw, dev(x16), ws=None)), x16, what, "nosplit")
 
 
 @pytest.mark.parametrize("bits", [2, 3, 4, 8])
