@@ -811,6 +811,113 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemv_fused(
   if (row < n) y[row] = acc;
 }
 
+// Narrow form for launches of few tiles: a work-group covers 8 rows of a
+// tile (grid.x = 8 x tiles); lane = 8*r + g takes weights 8g .. 8g+7 of row
+// r's block, so a wave reads 8 whole 128-byte block rows per load.  Every
+// weight is re-rounded exactly as in k_gemv_fused; the 8 lanes of a row add
+// their sums in a fixed order.
+template <int BITS, int WAVES, int U>
+__global__ __launch_bounds__(WAVES * 64) void k_gemv_fused_narrow(
+    const uint16_t* __restrict__ w16, int64_t ld, const uint16_t* __restrict__ scale,
+    const uint8_t* __restrict__ zero, const f16x2* __restrict__ x2, float* __restrict__ y,
+    float* __restrict__ part, uint32_t* __restrict__ tickets,
+    int n, int kb, int G, int splits, int kbps) {
+  constexpr int NG = 8, RW = kTile / NG;
+  __shared__ float red[WAVES][RW];
+  const int lane = lane_id(), wave = wave_id();
+  const int r = lane / NG, g = lane % NG;
+  const int t = blockIdx.x / NG, part_i = blockIdx.x % NG, sp = blockIdx.y;
+  const int R = part_i * RW + r;
+  const int row = t * kTile + R;
+  const int rrow = min(row, n - 1);
+  const uint4* wr = reinterpret_cast<const uint4*>(w16 + (int64_t)rrow * ld) + g;
+  const int j0 = sp * kbps;
+  const int j1 = min(kb, j0 + kbps);
+  float yacc = 0.f;
+  for (int jb = j0 + wave; jb < j1; jb += WAVES * U) {
+    uint4 wv[U], xv[U];
+    uint16_t sr[U];
+    int zu[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int j = jb + u * WAVES;
+      const int jj = j < j1 ? j : j1 - 1;      // past the range: re-read, scale 0
+      wv[u] = wr[(int64_t)jj * 8];
+      xv[u] = reinterpret_cast<const uint4*>(x2 + (int64_t)jj * 32)[g];
+      if constexpr (BITS != 16) {
+        const int64_t mi = ((int64_t)t * G + ((G == 1) ? 0 : jj)) * kTile + R;
+        sr[u] = scale[mi];
+        zu[u] = zero[mi];
+      }
+    }
+    if constexpr (U > 1) loads_issued();
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const bool valid = jb + u * WAVES < j1;
+      const uint32_t uw[4] = {wv[u].x, wv[u].y, wv[u].z, wv[u].w};
+      const f16x2 xs[4] = {as_h2(xv[u].x), as_h2(xv[u].y), as_h2(xv[u].z), as_h2(xv[u].w)};
+      float a = 0.f, b = 0.f, s;
+      if constexpr (BITS == 16) {
+        s = valid ? 1.f : 0.f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          if (e & 1) b = __builtin_amdgcn_fdot2(as_h2(uw[e]), xs[e], b, false);
+          else a = __builtin_amdgcn_fdot2(as_h2(uw[e]), xs[e], a, false);
+        }
+      } else {
+        constexpr int qmax = (1 << BITS) - 1;
+        s = masked_scale(sr[u], valid);
+        const RtnParams p = rtn_params(s, zu[u], qmax);
+        float wf[8], q[8];
+        bool tie = false;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const f16x2 h = as_h2(uw[e]);
+          wf[2 * e] = (float)h.x;
+          wf[2 * e + 1] = (float)h.y;
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          bool te;
+          q[e] = rtn_raw(wf[e], p, te);
+          tie |= te;
+        }
+        if (__builtin_amdgcn_ballot_w64(tie) != 0) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) q[e] = rtn_fix(wf[e], q[e], p);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const auto pk = __builtin_amdgcn_cvt_pkrtz(clampf(q[2 * e], p.lo, p.hi),
+                                                     clampf(q[2 * e + 1], p.lo, p.hi));
+          const f16x2 h = __builtin_bit_cast(f16x2, pk);
+          if (e & 1) b = __builtin_amdgcn_fdot2(h, xs[e], b, false);
+          else a = __builtin_amdgcn_fdot2(h, xs[e], a, false);
+        }
+      }
+      yacc = __builtin_fmaf(s, a + b, yacc);
+    }
+  }
+  yacc = slice_sum<NG>(yacc);
+  if (g == 0) red[wave][r] = yacc;
+  lds_barrier();
+  if (wave != 0 || lane >= RW) return;
+  float tot = red[0][lane];
+#pragma unroll
+  for (int w = 1; w < WAVES; ++w) tot += red[w][lane];
+  const int orow = t * kTile + part_i * RW + lane;
+  if (splits > 1) {
+    // part[split][launch row], launch row = RW * work-group + lane
+    const int64_t np = (int64_t)gridDim.x * RW;
+    const int64_t grow = (int64_t)blockIdx.x * RW + lane;
+    put_partial(part + (int64_t)sp * np + grow, tot);
+    partials_written();
+    if (!split_ticket(tickets, blockIdx.x, splits)) return;
+    tot = sum_splits(part + grow, np, splits);
+  }
+  if (orow < n) y[orow] = tot;
+}
+
 // ------------------------------------------------------ skinny GEMM (M<=16)
 // v_mfma_f32_16x16x32_f16: A = X (16 rows, zero past m), B = W^T.  Lane
 // (c = lane % 16, q = lane / 16) supplies row c and the 8 K-positions

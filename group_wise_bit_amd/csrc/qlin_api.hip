@@ -157,19 +157,21 @@ int64_t split_ws_bytes(int64_t tiles, int kb, int64_t part_rows) {
   return kCounterBytes + (int64_t)s.splits * part_rows * tiles * kTile * 4;
 }
 
-constexpr int kPackedUnroll = 4;   // at most 4 K-blocks in flight per wave, packed GEMV
-constexpr int kFusedUnroll = 1;    // one K-block in flight per wave, fused GEMV
+// GEMV launch kinds: packed codes (single matrix or a set), a gate/up pair
+// with the SwiGLU combination, fp16 masters re-rounded on the fly.
+enum class GemvKind { kPacked, kPair, kFused };
 
-// GEMV launch shape: one work-group per (tile, split); its waves split the
-// split's K-blocks.  Each wave keeps up to `unroll` blocks in flight, so the
-// work-group is sized to cover the K range in about one round of loads.
+// GEMV launch shape: work-groups of `rows` rows of one tile (64: a whole tile,
+// lane = row; 16 / 8: 4 / 8 lanes per row over slices of each block) per K
+// split; the waves of a work-group split the K-blocks of its split.  Each wave
+// keeps up to `unroll` blocks in flight, so the work-group is sized to cover
+// its K range in about one round of loads.
 struct GemvCfg {
   int waves, splits, kbps, unroll;
-  int rows;     // packed kernels: rows per work-group, 64 (k_gemv_packed) or 16, 8 (k_gemv_narrow)
+  int rows;
 };
 
-GemvCfg gemv_config(int64_t tiles, int kb, int unroll, int64_t ws_bytes, bool pair = false,
-                    int bits = 4) {
+GemvCfg gemv_config(int64_t tiles, int kb, GemvKind kind, int bits, int64_t ws_bytes) {
   // Measured on MI355X (graph-replayed launches over rotating cold weights;
   // bits 2, 3, 4, 8; the Qwen2.5-0.5B, Qwen3-0.6B and Qwen3-8B layer shapes,
   // q/k/v sets and gate/up pairs; fp16 masters for the fused kernel).  A
@@ -180,22 +182,18 @@ GemvCfg gemv_config(int64_t tiles, int kb, int unroll, int64_t ws_bytes, bool pa
   // K when one wave would otherwise decode many blocks in sequence (long K
   // over up to 128 tiles; 3-bit decode, the costliest, also over 129-256
   // tiles).  Launches of many tiles use 4-wave work-groups, so that the tail
-  // of the grid is short.  The fused kernel is ALU-heavier (about 7 VALU ops
-  // per weight): 8 waves and about 4 K-blocks per split (at most 8 splits),
-  // 4 waves x 4 splits from 129 to 256 tiles.
-  const bool fused = unroll == kFusedUnroll;
+  // of the grid is short.  The fused kernel reads 2 bytes per weight and does
+  // about 7 VALU ops per weight: 8-row work-groups up to 256 tiles (16 waves,
+  // 8 for short K over many tiles), whole tiles beyond.
+  const bool fused = kind == GemvKind::kFused, pair = kind == GemvKind::kPair;
   int waves = fused ? 8 : 16;
   int splits = 1;
   int rows = 64;
   if (fused) {
     if (tiles <= 256) {
-      if (tiles > 128) {
-        waves = 4;
-        splits = 4;
-      } else {
-        splits = (kb + 3) / 4;        // ~4 K-blocks per split, at most 8 splits
-        if (splits > 8) splits = 8;
-      }
+      rows = 8;
+      waves = (kb <= 16 && tiles >= 64) ? 8 : 16;
+      if (kb >= 128) splits = kb / 64;
     }
   } else if (tiles > 256) {
     waves = 4;
@@ -221,24 +219,29 @@ GemvCfg gemv_config(int64_t tiles, int kb, int unroll, int64_t ws_bytes, bool pa
     if (got >= 2 && (w == 4 || w == 8 || w == 16) && sp >= 1 && (rw == 8 || rw == 16 || rw == 64)) {
       waves = w;
       splits = sp < kb ? sp : kb;
-      if (!fused) rows = rw;
+      rows = rw;
     }
   }
-  // split-K tickets: one per work-group of the launch's first split
+  if (fused && rows == 16) rows = 8;   // the fused kernel comes in 64- and 8-row forms
+  // split-K: one ticket per work-group of the launch's first split; partial
+  // sums for every launch row (two per row for a gate/up pair)
+  const int64_t part_rows = (pair ? 2 : 1) * tiles * kTile;
   if (tiles * (kTile / rows) > kMaxSplitTiles) splits = 1;
-  while (splits > 1 && kCounterBytes + (int64_t)splits * tiles * kTile * 4 > ws_bytes) --splits;
+  while (splits > 1 && kCounterBytes + (int64_t)splits * part_rows * 4 > ws_bytes) --splits;
   const int kbps = (kb + splits - 1) / splits;
-  // blocks kept in flight per wave: the wave's share of the split, up to `unroll`
+  // blocks kept in flight per wave: the wave's share of the split, up to 4
+  // (packed), 2 (gate/up pairs, 8-row fused) or 1 (64-row fused)
+  const int unroll = fused ? (rows == 64 ? 1 : 2) : (pair ? 2 : 4);
   const int per_wave = (kbps + waves - 1) / waves;
   int u = 1;
   while (u < unroll && u < per_wave) u *= 2;
   return GemvCfg{waves, (kb + kbps - 1) / kbps, kbps, u, rows};
 }
 
-int64_t gemv_ws_bytes(int64_t tiles, int kb, int unroll, int bits) {
-  const GemvCfg c = gemv_config(tiles, kb, unroll, INT64_MAX, false, bits);
+int64_t gemv_ws_bytes(int64_t tiles, int kb, GemvKind kind, int bits) {
+  const GemvCfg c = gemv_config(tiles, kb, kind, bits, INT64_MAX);
   if (c.splits <= 1) return 0;
-  return kCounterBytes + (int64_t)c.splits * tiles * kTile * 4;
+  return kCounterBytes + (int64_t)c.splits * (kind == GemvKind::kPair ? 2 : 1) * tiles * kTile * 4;
 }
 
 
@@ -352,26 +355,6 @@ void launch_gemv_packed(const PackedLaunch& L, const f16x2* x2, float* part, uin
   else launch_gemv_packed_s<B, false>(L, x2, part, tick, c, st);
 }
 
-// Launch shape of a gate/up pair: every wave reads its blocks of both
-// matrices, so the pair takes the split of a single-matrix launch of the same
-// tiles; up to 2 blocks of each in flight per wave.
-GemvCfg swiglu_config(int64_t tiles, int kb, int64_t ws_bytes, int bits) {
-  GemvCfg c = gemv_config(tiles, kb, 2, INT64_MAX, true, bits);
-  int splits = c.splits;
-  if (tiles * (kTile / c.rows) > kMaxSplitTiles) splits = 1;
-  while (splits > 1 && kCounterBytes + 2 * (int64_t)splits * tiles * kTile * 4 > ws_bytes)
-    --splits;
-  const int kbps = (kb + splits - 1) / splits;
-  const int per_wave = (kbps + c.waves - 1) / c.waves;
-  return GemvCfg{c.waves, (kb + kbps - 1) / kbps, kbps, per_wave >= 2 ? 2 : 1, c.rows};
-}
-
-int64_t swiglu_ws_bytes(int64_t tiles, int kb, int bits) {
-  const GemvCfg c = swiglu_config(tiles, kb, INT64_MAX, bits);
-  if (c.splits <= 1) return 0;
-  return kCounterBytes + 2 * (int64_t)c.splits * tiles * kTile * 4;
-}
-
 PackedLaunch packed_launch(const qlin_weight* const* w, float* const* y, int count) {
   PackedLaunch L{};
   int64_t tiles = 0;
@@ -419,12 +402,38 @@ void launch_gemv_fused_w(const qlin_weight* w, const f16x2* x2, float* y, float*
                      tick, w->n, kb, G, c.splits, c.kbps);
 }
 
-// The fused kernel needs ~150 VGPRs: at most 8 waves (512 threads) per work-group.
+template <int B, int W, int U>
+void launch_gemv_fused_narrow_w(const qlin_weight* w, const f16x2* x2, float* y, float* part,
+                                uint32_t* tick, GemvCfg c, hipStream_t st) {
+  const int kb = w->k / kBlock;
+  const int G = (w->bits == 16 || w->group != w->k) ? kb : 1;
+  dim3 grid((unsigned)(8 * tiles_of(w->n)), c.splits);
+  hipLaunchKernelGGL((k_gemv_fused_narrow<B, W, U>), grid, dim3(W * 64), 0, st,
+                     static_cast<const uint16_t*>(w->data), w->ld, w->scale, w->zero, x2, y, part,
+                     tick, w->n, kb, G, c.splits, c.kbps);
+}
+
+// The 64-row fused kernel needs ~150 VGPRs: at most 8 waves (512 threads) per
+// work-group.
 template <int B>
 void launch_gemv_fused(const qlin_weight* w, const f16x2* x2, float* y, float* part,
                        uint32_t* tick, GemvCfg c, hipStream_t st) {
-  if (c.waves >= 8) launch_gemv_fused_w<B, 8, 1>(w, x2, y, part, tick, c, st);
-  else launch_gemv_fused_w<B, 4, 1>(w, x2, y, part, tick, c, st);
+  if (c.rows == 8) {
+    if (c.waves == 16) {
+      if (c.unroll == 1) launch_gemv_fused_narrow_w<B, 16, 1>(w, x2, y, part, tick, c, st);
+      else launch_gemv_fused_narrow_w<B, 16, 2>(w, x2, y, part, tick, c, st);
+    } else if (c.waves == 8) {
+      if (c.unroll == 1) launch_gemv_fused_narrow_w<B, 8, 1>(w, x2, y, part, tick, c, st);
+      else launch_gemv_fused_narrow_w<B, 8, 2>(w, x2, y, part, tick, c, st);
+    } else {
+      if (c.unroll == 1) launch_gemv_fused_narrow_w<B, 4, 1>(w, x2, y, part, tick, c, st);
+      else launch_gemv_fused_narrow_w<B, 4, 2>(w, x2, y, part, tick, c, st);
+    }
+  } else if (c.waves >= 8) {
+    launch_gemv_fused_w<B, 8, 1>(w, x2, y, part, tick, c, st);
+  } else {
+    launch_gemv_fused_w<B, 4, 1>(w, x2, y, part, tick, c, st);
+  }
 }
 
 // A GEMM launch over a set of matrices (shared K, bits, group; one X).
@@ -667,7 +676,7 @@ qlin_status qlin_quantize_batch(const qlin_quant_job* jobs, int32_t count, int32
 int64_t qlin_gemv_workspace_bytes(const qlin_weight* w) {
   if (check_weight(w, true, true) != QLIN_OK) return 0;
   return gemv_ws_bytes(tiles_of(w->n), w->k / kBlock,
-                       w->format == QLIN_FMT_PACKED ? kPackedUnroll : kFusedUnroll, w->bits);
+                       w->format == QLIN_FMT_PACKED ? GemvKind::kPacked : GemvKind::kFused, w->bits);
 }
 
 int64_t gemm_set_ws_bytes(const qlin_weight* w, int count, int32_t m) {
@@ -712,9 +721,9 @@ qlin_status qlin_gemv(const qlin_weight* w, const uint16_t* x, float* y, void* w
   if (st != QLIN_OK) return st;
   const int64_t tiles = tiles_of(w->n);
   const int kb = w->k / kBlock;
-  const GemvCfg sp = gemv_config(tiles, kb, w->format == QLIN_FMT_PACKED ? kPackedUnroll
-                                                                         : kFusedUnroll,
-                                 workspace_bytes, false, w->bits);
+  const GemvCfg sp = gemv_config(
+      tiles, kb, w->format == QLIN_FMT_PACKED ? GemvKind::kPacked : GemvKind::kFused, w->bits,
+      workspace_bytes);
   if (w->format == QLIN_FMT_PACKED)
     return run_packed(packed_launch(&w, &y, 1), w->bits, x, workspace, sp, stream);
   uint32_t* tick = static_cast<uint32_t*>(workspace);
@@ -740,7 +749,7 @@ int64_t qlin_gemv_multi_workspace_bytes(const qlin_weight* w, int32_t count) {
   if (w == nullptr || count < 1 || count > kMaxMats) return 0;
   for (int i = 0; i < count; ++i)
     if (check_weight(&w[i], false, false) != QLIN_OK || w[i].k != w[0].k) return 0;
-  return gemv_ws_bytes(set_tiles(w, count), w[0].k / kBlock, kPackedUnroll, w[0].bits);
+  return gemv_ws_bytes(set_tiles(w, count), w[0].k / kBlock, GemvKind::kPacked, w[0].bits);
 }
 
 qlin_status qlin_gemv_multi(const qlin_weight* w, int32_t count, const uint16_t* x,
@@ -763,13 +772,13 @@ qlin_status qlin_gemv_multi(const qlin_weight* w, int32_t count, const uint16_t*
   const qlin_weight* wp[kMaxMats];
   for (int i = 0; i < count; ++i) wp[i] = &w[i];
   const PackedLaunch L = packed_launch(wp, y, count);
-  const GemvCfg c = gemv_config(L.tiles, L.kb, kPackedUnroll, workspace_bytes, false, w[0].bits);
+  const GemvCfg c = gemv_config(L.tiles, L.kb, GemvKind::kPacked, w[0].bits, workspace_bytes);
   return run_packed(L, w[0].bits, x, workspace, c, stream);
 }
 
 int64_t qlin_gemv_swiglu_workspace_bytes(const qlin_weight* gate) {
   if (check_weight(gate, false, false) != QLIN_OK) return 0;
-  return swiglu_ws_bytes(tiles_of(gate->n), gate->k / kBlock, gate->bits);
+  return gemv_ws_bytes(tiles_of(gate->n), gate->k / kBlock, GemvKind::kPair, gate->bits);
 }
 
 qlin_status qlin_gemv_swiglu(const qlin_weight* gate, const qlin_weight* up, const uint16_t* x,
@@ -792,7 +801,7 @@ qlin_status qlin_gemv_swiglu(const qlin_weight* gate, const qlin_weight* up, con
   L.tiles = (int)tiles_of(gate->n);
   L.swiglu = true;
   L.h16 = h16;
-  const GemvCfg c = swiglu_config(L.tiles, L.kb, workspace_bytes, gate->bits);
+  const GemvCfg c = gemv_config(L.tiles, L.kb, GemvKind::kPair, gate->bits, workspace_bytes);
   return run_packed(L, gate->bits, x, workspace, c, stream);
 }
 

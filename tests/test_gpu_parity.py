@@ -250,6 +250,80 @@ def test_gemv_fused_scale_sweep():
         assert np.array_equal(got, want), f"s={float(s)}"
 
 
+# fused launch shapes "waves,splits,rows": whole tiles, 8-row work-groups
+FUSED_WIDTHS = ["8,1,64", "4,4,64", "8,1,8", "16,2,8", "4,3,8"]
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4, 8, 16])
+@pytest.mark.parametrize("shape", [(200, 192), (130, 4096), (1, 64)])
+@pytest.mark.parametrize("cfg", FUSED_WIDTHS)
+def test_gemv_fused_row_widths(bits, shape, cfg, monkeypatch):
+    """The fused kernel at every work-group width and split: within tolerance,
+    one-hot x at positions covering every 8-weight slice of the first and last
+    block exact."""
+    monkeypatch.setenv("QLIN_TUNE_GEMV", cfg)
+    n, k = shape
+    say(f"gemv fused cfg={cfg} bits={bits} shape={shape}")
+    rng = np.random.default_rng([n, k, bits, 9])
+    w16 = synth.master_weights(rng, n, k)
+    x16 = synth.activations(rng, 1, k)[0]
+    wd = dev(w16)
+    if bits == 16:
+        qw = qlin.master_weight(wd, 16, 64)
+        what = w16.astype(np.float64)
+    else:
+        s16, z = oracle.rtn_scale_zero(w16, bits, 64)
+        qw = qlin.master_weight(wd, bits, 64, dev(oracle.tile_meta(s16)), dev(oracle.tile_meta(z)))
+        what = oracle.fused_weights(w16, s16, z, bits, 64)
+    check_tol(host(qlin.gemv(qw, dev(x16))), x16, what, cfg)
+    for kk in sorted(set(range(0, 64, 7)) | set(range(k - 64, k, 9))):
+        e = np.zeros(k, np.float16)
+        e[kk] = 1
+        ye = host(qlin.gemv(qw, dev(e)))
+        assert np.array_equal(ye.astype(np.float64), what[:, kk]), f"{cfg} one-hot k={kk}"
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4, 8])
+@pytest.mark.parametrize("cfg", ["8,1,64", "8,1,8"])
+def test_gemv_fused_edge_groups_widths(bits, cfg, monkeypatch):
+    """Edge-case groups (ties, clamps, constant, one-signed) through both
+    fused kernels: one-hot x over all 256 columns, exact."""
+    monkeypatch.setenv("QLIN_TUNE_GEMV", cfg)
+    rng = np.random.default_rng(520 + bits)
+    w16 = synth.edge_groups(bits, rng, n_rows=64, k=256)
+    say(f"gemv fused edge groups cfg={cfg} bits={bits}")
+    s16, z = oracle.rtn_scale_zero(w16, bits, 64)
+    what = oracle.fused_weights(w16, s16, z, bits, 64)
+    qw = qlin.master_weight(dev(w16), bits, 64, dev(oracle.tile_meta(s16)), dev(oracle.tile_meta(z)))
+    eye = torch.eye(256, dtype=torch.float16, device=DEV)
+    got = np.stack([host(qlin.gemv(qw, eye[i].contiguous())) for i in range(256)], axis=1)
+    assert np.array_equal(got.astype(np.float64), what)
+
+
+@pytest.mark.parametrize("cfg", ["8,1,64", "8,1,8"])
+def test_gemv_fused_scale_sweep_all_columns(cfg, monkeypatch):
+    """Every finite fp16 weight spread over all 64 columns of a block (so every
+    lane slice of the narrow kernel sees them), 8-bit, zero 128, six scales,
+    read back column by column through one-hot x."""
+    monkeypatch.setenv("QLIN_TUNE_GEMV", cfg)
+    allw = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16).view(np.float16)
+    allw = allw[np.isfinite(allw)]
+    n = (allw.size + 63) // 64
+    flat = np.zeros(n * 64, np.float16)
+    flat[: allw.size] = allw
+    w16 = flat.reshape(n, 64)
+    wd = dev(w16)
+    z = np.full((n, 1), 128, np.uint8)
+    eye = torch.eye(64, dtype=torch.float16, device=DEV)
+    for s in np.array([2.0 ** -10, 0.00123, 0.125, 1.0, 7.0, 1000.0], np.float16):
+        say(f"fused scale sweep cfg={cfg} s={float(s)}")
+        s16 = np.full((n, 1), s, np.float16)
+        qw = qlin.master_weight(wd, 8, 64, dev(oracle.tile_meta(s16)), dev(oracle.tile_meta(z)))
+        got = np.stack([host(qlin.gemv(qw, eye[i].contiguous())) for i in range(64)], axis=1)
+        want = oracle.fused_weights(w16, s16, z, 8, 64)
+        assert np.array_equal(got.astype(np.float64), want), f"s={float(s)}"
+
+
 # ------------------------------------------------------------------ GEMM --
 @pytest.mark.parametrize("bits", [2, 3, 4, 8])
 @pytest.mark.parametrize("m", [1, 5, 8, 16, 17, 64, 100, 128, 256])
