@@ -1380,6 +1380,127 @@ __global__ __launch_bounds__(256) void k_gemm_tiles(
   }
 }
 
+// ---------------------------------------- small-M GEMM (K split in the WG)
+// For small M over few tiles: work-group = 32 rows of X x one 64-row W tile
+// over its split's K range.  Its 4 waves take the K-blocks j0+w, j0+w+4, ...
+// and issue the loads of up to U blocks (X A-fragments straight from global
+// memory, codes, scales, zeros) before decoding any, so a short K range costs
+// about one memory round trip; the 4 partial 32x64 tiles are then added in
+// LDS in wave order.  Operand layout as in k_gemm_tiles (lane (c, h): X row
+// c / W row 32cb + c, K positions 32h + 8s .. +7 for instruction s).
+template <int BITS, int U>
+__global__ __launch_bounds__(256) void k_gemm_ksplit(
+    const GemmSet set, const uint16_t* __restrict__ X, int64_t ldx, int m, int kb, int G,
+    int splits, int kbps, float* __restrict__ part, uint32_t* __restrict__ tickets) {
+  constexpr int WPB = 2 * BITS;
+  constexpr int HW = WPB / 2;                 // words of a half block
+  __shared__ float red[4][2048];
+  const int tid = threadIdx.x;
+  const int lane = lane_id(), wave = wave_id();
+  const int c = lane & 31, h = lane >> 5;
+  const GemmMat mat = gemm_mat(set, blockIdx.x);
+  const int t = mat.col;
+  const int m0 = blockIdx.y * 32;
+  const uint32_t magic = vreg_const(kMagic);
+  const int j0 = blockIdx.z * kbps;
+  const int j1 = min(kb, j0 + kbps);
+  // rows past m read row m0: an X row only feeds its own output row, never stored
+  const uint16_t* xrow = X + (int64_t)(m0 + c < m ? m0 + c : m0) * ldx + 32 * h;
+  const uint32_t* wsrc[2];
+  int64_t msrc[2];
+#pragma unroll
+  for (int cb = 0; cb < 2; ++cb) {
+    const int r = 32 * cb + c;
+    wsrc[cb] = mat.codes + ((int64_t)t * kb * kTile + r) * WPB;
+    msrc[cb] = (int64_t)t * G * kTile + r;
+  }
+  f32x16 acc[2];
+#pragma unroll
+  for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[cb][r] = 0.f;
+
+  for (int jb = j0 + wave; jb < j1; jb += 4 * U) {
+    f16x8 xa[U][4];
+    uint32_t wl[U][2][HW];
+    uint16_t sr[U][2];
+    int zc[U][2];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int j = jb + 4 * u;
+      const int jj = j < j1 ? j : j1 - 1;     // past the range: re-read, scale 0
+      const f16x8* xp = reinterpret_cast<const f16x8*>(xrow + (int64_t)jj * kBlock);
+#pragma unroll
+      for (int s = 0; s < 4; ++s) xa[u][s] = xp[s];
+      const int64_t g = (G == 1) ? 0 : jj;
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb) {
+        load_half<BITS>(wsrc[cb] + (int64_t)jj * kTile * WPB, h, wl[u][cb]);
+        sr[u][cb] = mat.scale[msrc[cb] + g * kTile];
+        zc[u][cb] = mat.zero[msrc[cb] + g * kTile];
+      }
+    }
+    if constexpr (U > 1) loads_issued();
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const bool valid = jb + 4 * u < j1;
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb) {
+        const Deq d = make_deq(masked_scale(sr[u][cb], valid), zc[u][cb]);
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+          acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+              xa[u][s], deq_half<BITS>(wl[u][cb], s, d, magic), acc[cb], 0, 0, 0);
+      }
+    }
+  }
+  // element e = 1024 cb + 64 r + lane of a wave's two accumulators
+#pragma unroll
+  for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) red[wave][1024 * cb + 64 * r + lane] = acc[cb][r];
+  __syncthreads();
+  float v[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int e = tid + 256 * i;
+    v[i] = ((red[0][e] + red[1][e]) + red[2][e]) + red[3][e];
+  }
+  if (splits > 1) {
+    // partials [split][work-group][element]; the last work-group of this
+    // output tile to arrive adds the splits in order 0, 1, ...
+    const int64_t wg = (int64_t)blockIdx.y * gridDim.x + blockIdx.x;
+    const int64_t groups = (int64_t)gridDim.x * gridDim.y;
+    float* pw = part + (blockIdx.z * groups + wg) * 2048;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) put_partial(pw + tid + 256 * i, v[i]);
+    partials_written();
+    __syncthreads();
+    __shared__ uint32_t s_last;
+    if (tid == 0) {
+      const uint32_t prev = __hip_atomic_fetch_add(&tickets[wg], 1u, __ATOMIC_RELAXED,
+                                                   __HIP_MEMORY_SCOPE_AGENT);
+      s_last = prev == (uint32_t)(splits - 1);
+      if (s_last) __hip_atomic_store(&tickets[wg], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __syncthreads();
+    if (!s_last) return;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      v[i] = sum_splits(part + wg * 2048 + tid + 256 * i, groups * 2048, splits);
+  }
+  const int n = mat.n;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int e = tid + 256 * i;
+    const int cb = e >> 10, r = (e >> 6) & 15, l = e & 63;
+    const int row = m0 + 8 * (r >> 2) + 4 * (l >> 5) + (r & 3);
+    const int col = t * kTile + 32 * cb + (l & 31);
+    if (row < m && col < n) mat.y[(int64_t)row * mat.ldy + col] = v[i];
+  }
+}
+
+
 // ------------------------------------------------- embedding-row gather --
 // Rows ids[i] of a packed weight, dequantized: out32 = s*(q - z) (exact in
 // fp32), out16 = that value rounded to fp16 (nearest even).  One work-group

@@ -442,6 +442,7 @@ struct GemmPlan {
   int64_t tiles;      // all 64-row tiles of the set
   int cols4;          // all work-group columns of four tiles (tiled GEMM)
   int kb, G, bits;
+  int end_tiles[kMaxMats], end_cols4[kMaxMats];   // set.end in either unit
 };
 
 GemmPlan gemm_plan(const qlin_weight* const* w, float* const* Y, const int64_t* ldy, int count,
@@ -458,6 +459,8 @@ GemmPlan gemm_plan(const qlin_weight* const* w, float* const* Y, const int64_t* 
     const int64_t t = tiles_of(w[i]->n);
     tiles += t;
     cols4 += (t + 3) / 4;
+    p.end_tiles[i] = (int)tiles;
+    p.end_cols4[i] = (int)cols4;
     p.set.end[i] = (int)(skinny ? tiles : cols4);
   }
   p.set.count = count;
@@ -478,19 +481,31 @@ void launch_gemm_skinny(const GemmPlan& p, const uint16_t* X, int64_t ldx, int m
 }
 
 // Tiled-GEMM launch shape: work-group tile = MB rows of X x 256 rows of W
-// (four 64-row tiles); gx = work-group columns.  Measured on MI355X
-// (graph-replayed launches over rotating cold weights, Qwen-shaped N x K,
-// M = 32..2048, int4): a tall X tile pays only when the grid is large; up to
-// M = 256 the 32-row tile is fastest (several work-groups per CU hide the load
-// latency), and K is split up to 4 ways when there are fewer than 160
-// work-groups, keeping at least 10 K-blocks per split.
-struct TilesCfg { int mb, gx, gy, splits, kbps; };
+// (four 64-row tiles), gx = work-group columns; or (mb = 0) the K-split
+// kernel, 32 rows of X x one 64-row tile.  Measured on MI355X (graph-replayed
+// launches over rotating cold weights, the Qwen2.5-0.5B and Qwen3-8B layer
+// shapes and q/k/v, gate/up sets, M = 32..2048, int4): up to M = 256 the
+// K-split kernel is 1.1-2x faster below 256 tiles (all loads of a wave's
+// K-blocks in flight at once); with more tiles the 32-row tiled kernel, K
+// split up to 4 ways when there are fewer than 160 work-groups.  Above M =
+// 256 a tall X tile pays only when the grid is large.
+struct TilesCfg { int mb, gx, gy, splits, kbps; };   // mb = 0: k_gemm_ksplit, gx in tiles
 
-TilesCfg tiles_config(int64_t gx, int kb, int m, int64_t ws_bytes) {
+TilesCfg tiles_config(int64_t gx, int64_t tiles, int kb, int m, int64_t ws_bytes) {
   TilesCfg c;
   c.gx = (int)gx;
   int want = 1;
-  if (m <= 256) {
+  if (m <= 256 && tiles < 256) {
+    // the K-split kernel: one 64-row W tile x 32 X rows per work-group; K is
+    // split across work-groups only when the grid is under 256 work-groups,
+    // keeping at least 8 K-blocks per split
+    c.mb = 0;
+    const int64_t groups = tiles * ((m + 31) / 32);
+    if (groups < 256) {
+      want = (int)((512 + groups - 1) / groups);
+      if (want > kb / 8) want = kb / 8;
+    }
+  } else if (m <= 256) {
     c.mb = 32;
     const int64_t groups = (int64_t)c.gx * ((m + 31) / 32);
     want = (int)(320 / groups);
@@ -505,28 +520,34 @@ TilesCfg tiles_config(int64_t gx, int kb, int m, int64_t ws_bytes) {
       if ((int64_t)c.gx * ((m + 63) / 64) < 256) c.mb = 32;
     }
   }
-  // QLIN_TUNE_GEMM="mb,splits" overrides the choice (launch-shape sweeps)
+  // QLIN_TUNE_GEMM="mb,splits" overrides the choice (launch-shape sweeps;
+  // mb = 0: the K-split kernel)
   if (const char* e = getenv("QLIN_TUNE_GEMM")) {
     int mb = 0, sp = 0;
-    if (sscanf(e, "%d,%d", &mb, &sp) == 2 && (mb == 32 || mb == 64 || mb == 128) && sp >= 1) {
+    if (sscanf(e, "%d,%d", &mb, &sp) == 2 && (mb == 0 || mb == 32 || mb == 64 || mb == 128) &&
+        sp >= 1) {
       c.mb = mb;
       want = sp < kb ? sp : kb;
     }
   }
   if (want < 1) want = 1;
-  c.gy = (m + c.mb - 1) / c.mb;
+  if (c.mb == 0) c.gx = (int)tiles;
+  const int rows = c.mb == 0 ? 32 : c.mb;
+  const int64_t wg_outputs = (int64_t)rows * (c.mb == 0 ? kTile : 256);
+  c.gy = (m + rows - 1) / rows;
   if ((int64_t)c.gx * c.gy > kMaxSplitTiles) want = 1;
-  while (want > 1 && kCounterBytes + (int64_t)want * c.gy * c.mb * c.gx * 256 * 4 > ws_bytes)
+  while (want > 1 && kCounterBytes + (int64_t)want * c.gy * c.gx * wg_outputs * 4 > ws_bytes)
     --want;
   c.kbps = (kb + want - 1) / want;
   c.splits = (kb + c.kbps - 1) / c.kbps;
   return c;
 }
 
-int64_t tiles_ws_bytes(int64_t gx, int kb, int m) {
-  const TilesCfg c = tiles_config(gx, kb, m, INT64_MAX);
+int64_t tiles_ws_bytes(int64_t gx, int64_t tiles, int kb, int m) {
+  const TilesCfg c = tiles_config(gx, tiles, kb, m, INT64_MAX);
   if (c.splits <= 1) return 0;
-  return kCounterBytes + (int64_t)c.splits * c.gy * c.mb * c.gx * 256 * 4;
+  const int64_t wg_outputs = c.mb == 0 ? 32 * kTile : (int64_t)c.mb * 256;
+  return kCounterBytes + (int64_t)c.splits * c.gy * c.gx * wg_outputs * 4;
 }
 
 // MB = 32: the register-staged kernel (several work-groups per CU hide its
@@ -545,9 +566,29 @@ void launch_tiles_mb(const GemmPlan& p, const uint16_t* X, int64_t ldx, int m, T
 }
 
 template <int B>
+void launch_gemm_ksplit(const GemmPlan& p, const uint16_t* X, int64_t ldx, int m, TilesCfg c,
+                        float* part, uint32_t* tick, hipStream_t st) {
+  GemmSet set = p.set;
+  for (int i = 0; i < set.count; ++i) set.end[i] = p.end_tiles[i];
+  // blocks in flight per wave: the wave's share of the split, up to 4
+  const int per_wave = (c.kbps + 3) / 4;
+  const dim3 grid(c.gx, c.gy, c.splits);
+  if (per_wave >= 4)
+    hipLaunchKernelGGL((k_gemm_ksplit<B, 4>), grid, dim3(256), 0, st, set, X, ldx, m, p.kb, p.G,
+                       c.splits, c.kbps, part, tick);
+  else if (per_wave >= 2)
+    hipLaunchKernelGGL((k_gemm_ksplit<B, 2>), grid, dim3(256), 0, st, set, X, ldx, m, p.kb, p.G,
+                       c.splits, c.kbps, part, tick);
+  else
+    hipLaunchKernelGGL((k_gemm_ksplit<B, 1>), grid, dim3(256), 0, st, set, X, ldx, m, p.kb, p.G,
+                       c.splits, c.kbps, part, tick);
+}
+
+template <int B>
 void launch_gemm_tiles(const GemmPlan& p, const uint16_t* X, int64_t ldx, int m, TilesCfg c,
                        float* part, uint32_t* tick, hipStream_t st) {
-  if (c.mb == 32) launch_tiles_mb<B, 32>(p, X, ldx, m, c, part, tick, st);
+  if (c.mb == 0) launch_gemm_ksplit<B>(p, X, ldx, m, c, part, tick, st);
+  else if (c.mb == 32) launch_tiles_mb<B, 32>(p, X, ldx, m, c, part, tick, st);
   else if (c.mb == 64) launch_tiles_mb<B, 64>(p, X, ldx, m, c, part, tick, st);
   else launch_tiles_mb<B, 128>(p, X, ldx, m, c, part, tick, st);
 }
@@ -687,7 +728,7 @@ int64_t gemm_set_ws_bytes(const qlin_weight* w, int count, int32_t m) {
     tiles += tiles_of(w[i].n);
     cols4 += (tiles_of(w[i].n) + 3) / 4;
   }
-  if (m > kSkinnyMaxM) return tiles_ws_bytes(cols4, w[0].k / kBlock, m);
+  if (m > kSkinnyMaxM) return tiles_ws_bytes(cols4, tiles, w[0].k / kBlock, m);
   return split_ws_bytes(tiles, w[0].k / kBlock, 16);
 }
 
@@ -858,7 +899,7 @@ qlin_status run_gemm(const GemmPlan& p, const uint16_t* X, int m, int64_t ld_x, 
       default: launch_gemm_skinny<8>(p, X, ld_x, m, part, tick, sp, stream); break;
     }
   } else {
-    const TilesCfg c = tiles_config(p.cols4, p.kb, m, workspace_bytes);
+    const TilesCfg c = tiles_config(p.cols4, p.tiles, p.kb, m, workspace_bytes);
     float* part = c.splits > 1 ? reinterpret_cast<float*>(pbase) : nullptr;
     switch (p.bits) {
       case 2: launch_gemm_tiles<2>(p, X, ld_x, m, c, part, tick, stream); break;

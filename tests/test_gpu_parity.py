@@ -358,6 +358,65 @@ def test_gemm_one_hot_fp16_exact(bits, m):
         assert np.array_equal(Y.astype(np.float64), fp16_rne(what[:, cols].T))
 
 
+# K-split GEMM launch shapes "0,splits" (32 X rows x one 64-row W tile per
+# work-group, its 4 waves splitting K), with and without a K split across
+# work-groups
+KSPLIT = ["0,1", "0,2", "0,5"]
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4, 8])
+@pytest.mark.parametrize("cfg", KSPLIT)
+@pytest.mark.parametrize("m,n,k,group", [(17, 200, 192, 64), (100, 130, 1600, 64),
+                                         (128, 320, 896, "K"), (256, 64, 4096, 64)])
+def test_gemm_ksplit(bits, cfg, m, n, k, group, monkeypatch):
+    """The K-split GEMM within tolerance on ragged M and N, per-group and
+    per-channel scales, and one-hot X rows reproduce fp16-rounded dequantized
+    columns exactly (every decoded weight of the columns hit)."""
+    monkeypatch.setenv("QLIN_TUNE_GEMM", cfg)
+    g = k if group == "K" else 64
+    rng = np.random.default_rng([m, n, k, bits, 11])
+    w16 = synth.master_weights(rng, n, k)
+    x16 = synth.activations(rng, m, k)
+    qw, codes, s16, z = oracle_packed(w16, bits, g)
+    what = oracle.dequantize(codes, s16, z, g)
+    say(f"gemm ksplit cfg={cfg} bits={bits} m={m} n={n} k={k} group={g}")
+    check_tol(host(qlin.gemm(qw, dev(x16))), x16, what, f"ksplit {cfg}")
+    cols = (np.arange(m) * 37) % k
+    X = np.zeros((m, k), np.float16)
+    X[np.arange(m), cols] = 1
+    Y = host(qlin.gemm(qw, dev(X)))
+    assert np.array_equal(Y.astype(np.float64), fp16_rne(what[:, cols].T))
+
+
+@pytest.mark.parametrize("bits", [3, 4])
+@pytest.mark.parametrize("cfg", KSPLIT)
+def test_gemm_ksplit_sets_and_workspace(bits, cfg, monkeypatch):
+    """A ragged set of three matrices in one K-split launch, an explicit
+    workspace reused twice (counters re-armed, partial region scratch)."""
+    monkeypatch.setenv("QLIN_TUNE_GEMM", cfg)
+    rng = np.random.default_rng([bits, 12])
+    k, m = 1024, 72
+    mats = []
+    for n in (200, 64, 1):
+        w16 = synth.master_weights(rng, n, k)
+        qw, codes, s16, z = oracle_packed(w16, bits, 64)
+        mats.append((qw, oracle.dequantize(codes, s16, z, 64)))
+    x16 = synth.activations(rng, m, k)
+    need = qlin.library().qlin_gemm_multi_workspace_bytes(
+        (qlin.QlinWeightC * 3)(*[q.c_struct() for q, _ in mats]), 3, m)
+    ws = torch.zeros(max(need, 16), dtype=torch.uint8, device=DEV)
+    say(f"gemm ksplit set cfg={cfg} bits={bits} ws={need}")
+    Ys = [host(y) for y in qlin.gemm_multi([q for q, _ in mats], dev(x16), ws=ws)]
+    for Y, (_, what) in zip(Ys, mats):
+        check_tol(Y, x16, what, f"set {cfg}")
+    if need > 65536:
+        assert torch.count_nonzero(ws[:65536]).item() == 0
+        ws[65536:].fill_(0x5A)
+    Ys2 = [host(y) for y in qlin.gemm_multi([q for q, _ in mats], dev(x16), ws=ws)]
+    for a, b in zip(Ys, Ys2):
+        assert np.array_equal(a, b)
+
+
 @pytest.mark.parametrize("bits", [2, 3, 4, 8])
 @pytest.mark.parametrize("m,n,k", [(2048, 8192, 192), (1100, 12288, 128), (2048, 4096, 256),
                                    (1000, 4160, 320), (300, 256, 960)])
@@ -463,10 +522,14 @@ def test_split_k_full_tiles(bits):
 @pytest.mark.parametrize("bits", [2, 3, 4, 8])
 @pytest.mark.parametrize("m,n,k", [(128, 896, 4864), (100, 192, 4096), (256, 1024, 2048),
                                    (40, 300, 1600)])
-def test_gemm_tiles_split_k(bits, m, n, k):
-    """Tiled GEMM with K split across work-groups (uneven last split, tiles past
-    n in the last work-group) equals the unsplit launch to tolerance, re-arms
-    its counters, and ignores whatever the partial region held before."""
+@pytest.mark.parametrize("cfg", [None, "32,3"])
+def test_gemm_tiles_split_k(bits, m, n, k, cfg, monkeypatch):
+    """GEMM with K split across work-groups (uneven last split, tiles past n in
+    the last work-group; the default K-split kernel and the 32-row tiled one)
+    equals the unsplit launch to tolerance, re-arms its counters, and ignores
+    whatever the partial region held before."""
+    if cfg is not None:
+        monkeypatch.setenv("QLIN_TUNE_GEMM", cfg)
     rng = np.random.default_rng([61, bits, m, n, k])
     w16 = synth.master_weights(rng, n, k)
     X = synth.activations(rng, m, k)
