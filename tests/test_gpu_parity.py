@@ -340,6 +340,26 @@ def test_gemm(bits, m):
 
 
 @pytest.mark.parametrize("bits", [2, 3, 4, 8])
+@pytest.mark.parametrize("m", [1, 5, 16])
+def test_gemm_skinny_forced(bits, m, monkeypatch):
+    """The skinny (M <= 16) kernel, forced: within tolerance and one-hot exact."""
+    monkeypatch.setenv("QLIN_TUNE_GEMM", "16,1")
+    n, k = 200, 640
+    rng = np.random.default_rng([bits, m, 13])
+    w16 = synth.master_weights(rng, n, k)
+    x16 = synth.activations(rng, m, k)
+    qw, codes, s16, z = oracle_packed(w16, bits, 64)
+    what = oracle.dequantize(codes, s16, z, 64)
+    say(f"gemm skinny forced bits={bits} m={m}")
+    check_tol(host(qlin.gemm(qw, dev(x16))), x16, what, f"skinny m={m}")
+    cols = (np.arange(m) * 53 + 7) % k
+    X = np.zeros((m, k), np.float16)
+    X[np.arange(m), cols] = 1
+    Y = host(qlin.gemm(qw, dev(X)))
+    assert np.array_equal(Y.astype(np.float64), fp16_rne(what[:, cols].T))
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4, 8])
 @pytest.mark.parametrize("m", [16, 128])
 def test_gemm_one_hot_fp16_exact(bits, m):
     """X rows one-hot: Y[i, :] is column k_i of the dequantized weights rounded
@@ -366,7 +386,8 @@ KSPLIT = ["0,1", "0,2", "0,5"]
 
 @pytest.mark.parametrize("bits", [2, 3, 4, 8])
 @pytest.mark.parametrize("cfg", KSPLIT)
-@pytest.mark.parametrize("m,n,k,group", [(17, 200, 192, 64), (100, 130, 1600, 64),
+@pytest.mark.parametrize("m,n,k,group", [(1, 200, 192, 64), (5, 130, 1600, 64), (16, 64, 896, "K"),
+                                         (17, 200, 192, 64), (100, 130, 1600, 64),
                                          (128, 320, 896, "K"), (256, 64, 4096, 64)])
 def test_gemm_ksplit(bits, cfg, m, n, k, group, monkeypatch):
     """The K-split GEMM within tolerance on ragged M and N, per-group and
