@@ -1381,31 +1381,37 @@ __global__ __launch_bounds__(256) void k_gemm_tiles(
 }
 
 // ---------------------------------------- small-M GEMM (K split in the WG)
-// For small M over few tiles: work-group = 32 rows of X x one 64-row W tile
-// over its split's K range.  Its 4 waves take the K-blocks j0+w, j0+w+4, ...
+// For small M over few tiles: work-group = 32*RB rows of X x one 64-row W
+// tile over its split's K range.  Its 4 waves take the K-blocks j0+w, j0+w+4, ...
 // and issue the loads of up to U blocks (X A-fragments straight from global
 // memory, codes, scales, zeros) before decoding any, so a short K range costs
 // about one memory round trip; the 4 partial 32x64 tiles are then added in
 // LDS in wave order.  Operand layout as in k_gemm_tiles (lane (c, h): X row
-// c / W row 32cb + c, K positions 32h + 8s .. +7 for instruction s).
-template <int BITS, int U>
+// 32rb + c / W row 32cb + c, K positions 32h + 8s .. +7 for instruction s).
+template <int BITS, int U, int RB>
 __global__ __launch_bounds__(256) void k_gemm_ksplit(
     const GemmSet set, const uint16_t* __restrict__ X, int64_t ldx, int m, int kb, int G,
     int splits, int kbps, float* __restrict__ part, uint32_t* __restrict__ tickets) {
   constexpr int WPB = 2 * BITS;
   constexpr int HW = WPB / 2;                 // words of a half block
-  __shared__ float red[4][2048];
+  constexpr int NE = RB * 2048;              // elements of a wave's partial tile
+  __shared__ float red[4][NE];
   const int tid = threadIdx.x;
   const int lane = lane_id(), wave = wave_id();
   const int c = lane & 31, h = lane >> 5;
   const GemmMat mat = gemm_mat(set, blockIdx.x);
   const int t = mat.col;
-  const int m0 = blockIdx.y * 32;
+  const int m0 = blockIdx.y * 32 * RB;
   const uint32_t magic = vreg_const(kMagic);
   const int j0 = blockIdx.z * kbps;
   const int j1 = min(kb, j0 + kbps);
   // rows past m read row m0: an X row only feeds its own output row, never stored
-  const uint16_t* xrow = X + (int64_t)(m0 + c < m ? m0 + c : m0) * ldx + 32 * h;
+  const uint16_t* xrow[RB];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    const int xr = m0 + 32 * rb + c;
+    xrow[rb] = X + (int64_t)(xr < m ? xr : m0) * ldx + 32 * h;
+  }
   const uint32_t* wsrc[2];
   int64_t msrc[2];
 #pragma unroll
@@ -1414,14 +1420,16 @@ __global__ __launch_bounds__(256) void k_gemm_ksplit(
     wsrc[cb] = mat.codes + ((int64_t)t * kb * kTile + r) * WPB;
     msrc[cb] = (int64_t)t * G * kTile + r;
   }
-  f32x16 acc[2];
+  f32x16 acc[RB][2];
 #pragma unroll
-  for (int cb = 0; cb < 2; ++cb)
+  for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) acc[cb][r] = 0.f;
+    for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[rb][cb][r] = 0.f;
 
   for (int jb = j0 + wave; jb < j1; jb += 4 * U) {
-    f16x8 xa[U][4];
+    f16x8 xa[U][RB][4];
     uint32_t wl[U][2][HW];
     uint16_t sr[U][2];
     int zc[U][2];
@@ -1429,9 +1437,12 @@ __global__ __launch_bounds__(256) void k_gemm_ksplit(
     for (int u = 0; u < U; ++u) {
       const int j = jb + 4 * u;
       const int jj = j < j1 ? j : j1 - 1;     // past the range: re-read, scale 0
-      const f16x8* xp = reinterpret_cast<const f16x8*>(xrow + (int64_t)jj * kBlock);
 #pragma unroll
-      for (int s = 0; s < 4; ++s) xa[u][s] = xp[s];
+      for (int rb = 0; rb < RB; ++rb) {
+        const f16x8* xp = reinterpret_cast<const f16x8*>(xrow[rb] + (int64_t)jj * kBlock);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) xa[u][rb][s] = xp[s];
+      }
       const int64_t g = (G == 1) ? 0 : jj;
 #pragma unroll
       for (int cb = 0; cb < 2; ++cb) {
@@ -1448,21 +1459,28 @@ __global__ __launch_bounds__(256) void k_gemm_ksplit(
       for (int cb = 0; cb < 2; ++cb) {
         const Deq d = make_deq(masked_scale(sr[u][cb], valid), zc[u][cb]);
 #pragma unroll
-        for (int s = 0; s < 4; ++s)
-          acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
-              xa[u][s], deq_half<BITS>(wl[u][cb], s, d, magic), acc[cb], 0, 0, 0);
+        for (int s = 0; s < 4; ++s) {
+          const f16x8 bf = deq_half<BITS>(wl[u][cb], s, d, magic);
+#pragma unroll
+          for (int rb = 0; rb < RB; ++rb)
+            acc[rb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(xa[u][rb][s], bf, acc[rb][cb],
+                                                                 0, 0, 0);
+        }
       }
     }
   }
-  // element e = 1024 cb + 64 r + lane of a wave's two accumulators
+  // element e = 2048 rb + 1024 cb + 64 r + lane of a wave's accumulators
 #pragma unroll
-  for (int cb = 0; cb < 2; ++cb)
+  for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) red[wave][1024 * cb + 64 * r + lane] = acc[cb][r];
+    for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) red[wave][2048 * rb + 1024 * cb + 64 * r + lane] = acc[rb][cb][r];
   __syncthreads();
-  float v[8];
+  constexpr int PT = NE / 256;               // elements per thread
+  float v[PT];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
+  for (int i = 0; i < PT; ++i) {
     const int e = tid + 256 * i;
     v[i] = ((red[0][e] + red[1][e]) + red[2][e]) + red[3][e];
   }
@@ -1471,9 +1489,9 @@ __global__ __launch_bounds__(256) void k_gemm_ksplit(
     // output tile to arrive adds the splits in order 0, 1, ...
     const int64_t wg = (int64_t)blockIdx.y * gridDim.x + blockIdx.x;
     const int64_t groups = (int64_t)gridDim.x * gridDim.y;
-    float* pw = part + (blockIdx.z * groups + wg) * 2048;
+    float* pw = part + (blockIdx.z * groups + wg) * NE;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) put_partial(pw + tid + 256 * i, v[i]);
+    for (int i = 0; i < PT; ++i) put_partial(pw + tid + 256 * i, v[i]);
     partials_written();
     __syncthreads();
     __shared__ uint32_t s_last;
@@ -1486,15 +1504,15 @@ __global__ __launch_bounds__(256) void k_gemm_ksplit(
     __syncthreads();
     if (!s_last) return;
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-      v[i] = sum_splits(part + wg * 2048 + tid + 256 * i, groups * 2048, splits);
+    for (int i = 0; i < PT; ++i)
+      v[i] = sum_splits(part + wg * NE + tid + 256 * i, groups * NE, splits);
   }
   const int n = mat.n;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
+  for (int i = 0; i < PT; ++i) {
     const int e = tid + 256 * i;
-    const int cb = e >> 10, r = (e >> 6) & 15, l = e & 63;
-    const int row = m0 + 8 * (r >> 2) + 4 * (l >> 5) + (r & 3);
+    const int rb = e >> 11, cb = (e >> 10) & 1, r = (e >> 6) & 15, l = e & 63;
+    const int row = m0 + 32 * rb + 8 * (r >> 2) + 4 * (l >> 5) + (r & 3);
     const int col = t * kTile + 32 * cb + (l & 31);
     if (row < m && col < n) mat.y[(int64_t)row * mat.ldy + col] = v[i];
   }

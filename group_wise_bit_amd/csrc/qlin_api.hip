@@ -482,58 +482,60 @@ void launch_gemm_skinny(const GemmPlan& p, const uint16_t* X, int64_t ldx, int m
 
 // Tiled-GEMM launch shape: work-group tile = MB rows of X x 256 rows of W
 // (four 64-row tiles), gx = work-group columns; or (mb = 0) the K-split
-// kernel, 32 rows of X x one 64-row tile.  Measured on MI355X (graph-replayed
-// launches over rotating cold weights, the Qwen2.5-0.5B and Qwen3-8B layer
-// shapes and q/k/v, gate/up sets, M = 32..2048, int4): up to M = 256 the
-// K-split kernel is 1.1-2x faster below 256 tiles (all loads of a wave's
-// K-blocks in flight at once); with more tiles the 32-row tiled kernel, K
-// split up to 4 ways when there are fewer than 160 work-groups.  Above M =
-// 256 a tall X tile pays only when the grid is large.
-struct TilesCfg { int mb, gx, gy, splits, kbps; };   // mb = 0: k_gemm_ksplit, gx in tiles
+// kernel, 32 or 64 rows of X x one 64-row tile.  Measured on MI355X
+// (graph-replayed launches over rotating cold weights, the Qwen2.5-0.5B and
+// Qwen3-8B layer shapes and q/k/v, gate/up sets, M = 8..2048, int4): up to
+// M = 256 the K-split kernel is 1.1-2x faster (all loads of a wave's K-blocks
+// in flight at once; 64 X rows from 256 tiles up).  Above M = 256 a tall X
+// tile pays only when the grid is large.
+// mb = 0 / 1: k_gemm_ksplit with 32 / 64 X rows, gx in tiles
+struct TilesCfg { int mb, gx, gy, splits, kbps; };
 
-TilesCfg tiles_config(int64_t gx, int64_t tiles, int kb, int m, int64_t ws_bytes) {
+TilesCfg tiles_config(int64_t gx, int64_t tiles, int kb, int m, int count,
+                      int64_t ws_bytes) {
   TilesCfg c;
   c.gx = (int)gx;
   int want = 1;
   if (m <= 256 && (tiles < 256 || m <= 16)) {
     // the K-split kernel: one 64-row W tile x 32 X rows per work-group; K is
-    // split across work-groups only when the grid is under 256 work-groups,
-    // keeping at least 8 K-blocks per split
+    // split across work-groups (at most 8 ways) only when the grid is under
+    // 256 work-groups, keeping at least 8 K-blocks per split
     c.mb = 0;
     const int64_t groups = tiles * ((m + 31) / 32);
     if (groups < 256) {
       want = (int)((512 + groups - 1) / groups);
+      if (want > 8) want = 8;
       if (want > kb / 8) want = kb / 8;
     }
   } else if (m <= 256) {
-    c.mb = 32;
-    const int64_t groups = (int64_t)c.gx * ((m + 31) / 32);
-    want = (int)(320 / groups);
-    if (want > 4) want = 4;
-    if (want > kb / 10) want = kb / 10;
+    c.mb = 1;                              // K-split kernel, 64 X rows
   } else {
     // 128-row tiles when that already gives more work-groups than CUs (two
-    // fit per CU), else 64 when that fills the chip, else 32
+    // fit per CU), else 64 when that fills the chip; a smaller grid takes
+    // the K-split kernel (64 X rows) for long K, 32-row tiles for short K
+    // (the K-split kernel with 32 X rows for sets, whose partly filled
+    // four-tile columns idle waves of the tiled kernel)
     c.mb = 128;
     if ((int64_t)c.gx * ((m + 127) / 128) < 288) {
       c.mb = 64;
-      if ((int64_t)c.gx * ((m + 63) / 64) < 256) c.mb = 32;
+      if ((int64_t)c.gx * ((m + 63) / 64) < 256) c.mb = kb >= 32 ? 1 : (count > 1 ? 0 : 32);
     }
   }
   // QLIN_TUNE_GEMM="mb,splits" overrides the choice (launch-shape sweeps;
   // mb = 0: the K-split kernel)
   if (const char* e = getenv("QLIN_TUNE_GEMM")) {
     int mb = 0, sp = 0;
-    if (sscanf(e, "%d,%d", &mb, &sp) == 2 && (mb == 0 || mb == 32 || mb == 64 || mb == 128) &&
-        sp >= 1) {
+    if (sscanf(e, "%d,%d", &mb, &sp) == 2 &&
+        (mb == 0 || mb == 1 || mb == 32 || mb == 64 || mb == 128) && sp >= 1) {
       c.mb = mb;
       want = sp < kb ? sp : kb;
     }
   }
   if (want < 1) want = 1;
-  if (c.mb == 0) c.gx = (int)tiles;
-  const int rows = c.mb == 0 ? 32 : c.mb;
-  const int64_t wg_outputs = (int64_t)rows * (c.mb == 0 ? kTile : 256);
+  const bool ks = c.mb <= 1;
+  if (ks) c.gx = (int)tiles;
+  const int rows = ks ? 32 * (c.mb + 1) : c.mb;
+  const int64_t wg_outputs = (int64_t)rows * (ks ? kTile : 256);
   c.gy = (m + rows - 1) / rows;
   if ((int64_t)c.gx * c.gy > kMaxSplitTiles) want = 1;
   while (want > 1 && kCounterBytes + (int64_t)want * c.gy * c.gx * wg_outputs * 4 > ws_bytes)
@@ -543,10 +545,10 @@ TilesCfg tiles_config(int64_t gx, int64_t tiles, int kb, int m, int64_t ws_bytes
   return c;
 }
 
-int64_t tiles_ws_bytes(int64_t gx, int64_t tiles, int kb, int m) {
-  const TilesCfg c = tiles_config(gx, tiles, kb, m, INT64_MAX);
+int64_t tiles_ws_bytes(int64_t gx, int64_t tiles, int kb, int m, int count) {
+  const TilesCfg c = tiles_config(gx, tiles, kb, m, count, INT64_MAX);
   if (c.splits <= 1) return 0;
-  const int64_t wg_outputs = c.mb == 0 ? 32 * kTile : (int64_t)c.mb * 256;
+  const int64_t wg_outputs = c.mb <= 1 ? 32 * (c.mb + 1) * kTile : (int64_t)c.mb * 256;
   return kCounterBytes + (int64_t)c.splits * c.gy * c.gx * wg_outputs * 4;
 }
 
@@ -565,29 +567,38 @@ void launch_tiles_mb(const GemmPlan& p, const uint16_t* X, int64_t ldx, int m, T
                        tick);
 }
 
+template <int B, int RB>
+void launch_gemm_ksplit_rb(const GemmSet& set, const GemmPlan& p, const uint16_t* X,
+                           int64_t ldx, int m, TilesCfg c, float* part, uint32_t* tick,
+                           hipStream_t st) {
+  // blocks in flight per wave: the wave's share of the split, up to 4 (2 for
+  // 64-row X tiles, whose X fragments take twice the registers)
+  const int per_wave = (c.kbps + 3) / 4;
+  const dim3 grid(c.gx, c.gy, c.splits);
+  if (per_wave >= 4 && RB == 1)
+    hipLaunchKernelGGL((k_gemm_ksplit<B, 4, RB>), grid, dim3(256), 0, st, set, X, ldx, m, p.kb,
+                       p.G, c.splits, c.kbps, part, tick);
+  else if (per_wave >= 2)
+    hipLaunchKernelGGL((k_gemm_ksplit<B, 2, RB>), grid, dim3(256), 0, st, set, X, ldx, m, p.kb,
+                       p.G, c.splits, c.kbps, part, tick);
+  else
+    hipLaunchKernelGGL((k_gemm_ksplit<B, 1, RB>), grid, dim3(256), 0, st, set, X, ldx, m, p.kb,
+                       p.G, c.splits, c.kbps, part, tick);
+}
+
 template <int B>
 void launch_gemm_ksplit(const GemmPlan& p, const uint16_t* X, int64_t ldx, int m, TilesCfg c,
                         float* part, uint32_t* tick, hipStream_t st) {
   GemmSet set = p.set;
   for (int i = 0; i < set.count; ++i) set.end[i] = p.end_tiles[i];
-  // blocks in flight per wave: the wave's share of the split, up to 4
-  const int per_wave = (c.kbps + 3) / 4;
-  const dim3 grid(c.gx, c.gy, c.splits);
-  if (per_wave >= 4)
-    hipLaunchKernelGGL((k_gemm_ksplit<B, 4>), grid, dim3(256), 0, st, set, X, ldx, m, p.kb, p.G,
-                       c.splits, c.kbps, part, tick);
-  else if (per_wave >= 2)
-    hipLaunchKernelGGL((k_gemm_ksplit<B, 2>), grid, dim3(256), 0, st, set, X, ldx, m, p.kb, p.G,
-                       c.splits, c.kbps, part, tick);
-  else
-    hipLaunchKernelGGL((k_gemm_ksplit<B, 1>), grid, dim3(256), 0, st, set, X, ldx, m, p.kb, p.G,
-                       c.splits, c.kbps, part, tick);
+  if (c.mb == 1) launch_gemm_ksplit_rb<B, 2>(set, p, X, ldx, m, c, part, tick, st);
+  else launch_gemm_ksplit_rb<B, 1>(set, p, X, ldx, m, c, part, tick, st);
 }
 
 template <int B>
 void launch_gemm_tiles(const GemmPlan& p, const uint16_t* X, int64_t ldx, int m, TilesCfg c,
                        float* part, uint32_t* tick, hipStream_t st) {
-  if (c.mb == 0) launch_gemm_ksplit<B>(p, X, ldx, m, c, part, tick, st);
+  if (c.mb <= 1) launch_gemm_ksplit<B>(p, X, ldx, m, c, part, tick, st);
   else if (c.mb == 32) launch_tiles_mb<B, 32>(p, X, ldx, m, c, part, tick, st);
   else if (c.mb == 64) launch_tiles_mb<B, 64>(p, X, ldx, m, c, part, tick, st);
   else launch_tiles_mb<B, 128>(p, X, ldx, m, c, part, tick, st);
@@ -745,7 +756,7 @@ int64_t gemm_set_ws_bytes(const qlin_weight* w, int count, int32_t m) {
     cols4 += (tiles_of(w[i].n) + 3) / 4;
   }
   if (m > kSkinnyMaxM || skinny_by_ksplit(tiles, w[0].k / kBlock))
-    return tiles_ws_bytes(cols4, tiles, w[0].k / kBlock, m);
+    return tiles_ws_bytes(cols4, tiles, w[0].k / kBlock, m, count);
   return split_ws_bytes(tiles, w[0].k / kBlock, 16);
 }
 
@@ -916,7 +927,7 @@ qlin_status run_gemm(const GemmPlan& p, const uint16_t* X, int m, int64_t ld_x, 
       default: launch_gemm_skinny<8>(p, X, ld_x, m, part, tick, sp, stream); break;
     }
   } else {
-    const TilesCfg c = tiles_config(p.cols4, p.tiles, p.kb, m, workspace_bytes);
+    const TilesCfg c = tiles_config(p.cols4, p.tiles, p.kb, m, p.set.count, workspace_bytes);
     float* part = c.splits > 1 ? reinterpret_cast<float*>(pbase) : nullptr;
     switch (p.bits) {
       case 2: launch_gemm_tiles<2>(p, X, ld_x, m, c, part, tick, stream); break;

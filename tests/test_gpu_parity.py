@@ -381,7 +381,7 @@ def test_gemm_one_hot_fp16_exact(bits, m):
 # K-split GEMM launch shapes "0,splits" (32 X rows x one 64-row W tile per
 # work-group, its 4 waves splitting K), with and without a K split across
 # work-groups
-KSPLIT = ["0,1", "0,2", "0,5"]
+KSPLIT = ["0,1", "0,2", "0,5", "1,1", "1,3"]
 
 
 @pytest.mark.parametrize("bits", [2, 3, 4, 8])
