@@ -1566,9 +1566,10 @@ __global__ __launch_bounds__(256) void k_embed_rows(
 // deep, into S separate LDS stages: no registers hold data in flight, so the
 // loads of block j + S - 1 are issued while block j computes and the memory
 // latency is hidden behind S - 1 blocks of MFMA work.  Each wave copies a
-// quarter of the X tile and its own tile's codes and metadata.  X chunks are
-// XOR-swizzled within a row (16-byte chunk c8 of row r at position
-// c8 ^ (r & 7)), so the A-fragment reads are free of bank conflicts.
+// quarter of the X tile and its own tile's codes and metadata.  The 16-byte
+// chunks of X rows and of 4- and 8-bit code rows are XOR-swizzled in LDS (the
+// direct-to-LDS loads pick their global source per lane accordingly) so that
+// the fragment reads of 8 or 16 consecutive lanes touch distinct banks.
 // f(std::integral_constant<int, I>) for I = B .. E-1, unrolled.
 template <int B, int E, typename F>
 __device__ __forceinline__ void static_for(F&& f) {
@@ -1587,6 +1588,22 @@ __device__ __forceinline__ void dma_to_lds(const void* src, void* lds) {
   if constexpr (SZ == 16) __builtin_amdgcn_global_load_lds(src, (lds_void*)lds, 16, 0, 0);
   else __builtin_amdgcn_global_load_lds(src, (lds_void*)lds, 4, 0, 0);
 }
+
+// LDS slot (16-byte chunk within the row) of X chunk c8 of row r: distinct
+// for the 8 consecutive rows, and for the 8 even or 8 odd rows of 16
+// consecutive rows, that one A-fragment read touches.
+__device__ __forceinline__ int xswz(int r, int c8) { return c8 ^ (r & 7) ^ ((r >> 3) & 1); }
+
+// Code rows of P = 2*BITS/4 chunks (4 bits: 2, 8 bits: 4): chunk e of row r
+// sits in slot P*r + (e ^ cswz(r)); a B-fragment read of lanes c = 0..15
+// (rows c, one chunk index each) then hits distinct banks.
+template <int BITS>
+__device__ __forceinline__ int cswz(int r) {
+  if constexpr (BITS == 4) return ((r >> 2) ^ (r >> 3)) & 1;
+  else if constexpr (BITS == 8) return ((r >> 1) ^ (r >> 2)) & 3;
+  else return 0;
+}
+template <int BITS> constexpr bool kCodeSwz = BITS == 4 || BITS == 8;
 
 template <int BITS, int MB>
 struct GemmStage {
@@ -1650,12 +1667,24 @@ __global__ __launch_bounds__(256, 2) void k_gemm_lds(
 #pragma unroll
   for (int i = 0; i < XQ; ++i) {
     const int q = tid + 256 * i;            // LDS position of the piece
-    const int row = q >> 3, c8 = (q & 7) ^ (row & 7);
+    const int row = q >> 3, c8 = xswz(row, q & 7);
     const int xr = m0 + row < m ? m0 + row : m0;
     xsrc[i] = reinterpret_cast<const char*>(X + (int64_t)xr * ldx + 8 * c8);
   }
-  const char* wsrc = reinterpret_cast<const char*>(codes + (int64_t)tt * kb * kTile * WPB) +
-                     lane * WDma<BITS>::SZ;
+  const char* wsrc = reinterpret_cast<const char*>(codes + (int64_t)tt * kb * kTile * WPB);
+  // source byte offset (within the code block) of this lane's piece i
+  int woff[WDma<BITS>::N];
+#pragma unroll
+  for (int i = 0; i < WDma<BITS>::N; ++i) {
+    const int slot = 64 * i + lane;
+    if constexpr (kCodeSwz<BITS>) {
+      constexpr int P = WPB / 4;
+      const int r = slot / P;
+      woff[i] = 16 * (P * r + ((slot % P) ^ cswz<BITS>(r)));
+    } else {
+      woff[i] = slot * WDma<BITS>::SZ;
+    }
+  }
   // metadata piece: lanes 0-31 two scales each, lanes 32-63 four zeros each
   // (lanes 48-63 repeat 32-47 into the unused upper quarter)
   const char* msrc = lane < 32
@@ -1671,7 +1700,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm_lds(
       dma_to_lds<16>(xsrc[i] + (int64_t)jg * kBlock * 2, st.x + (256 * i + 64 * wave) * 8);
 #pragma unroll
     for (int i = 0; i < WDma<BITS>::N; ++i)
-      dma_to_lds<WDma<BITS>::SZ>(wsrc + ((int64_t)jg * kTile * WPB) * 4 + i * 64 * WDma<BITS>::SZ,
+      dma_to_lds<WDma<BITS>::SZ>(wsrc + ((int64_t)jg * kTile * WPB) * 4 + woff[i],
                                  reinterpret_cast<char*>(st.w[wave]) + i * 64 * WDma<BITS>::SZ);
     const int64_t g = (G == 1) ? 0 : jg;
     dma_to_lds<4>(msrc + (lane < 32 ? g * kTile * 2 : g * kTile), st.meta[wave]);
@@ -1695,7 +1724,17 @@ __global__ __launch_bounds__(256, 2) void k_gemm_lds(
 #pragma unroll
     for (int cb = 0; cb < 2; ++cb) {
       const int r = 32 * cb + c;
-      load_half<BITS>(st.w[wave] + r * WPB, h, wl[cb]);
+      if constexpr (BITS == 4) {
+        const uint4 v = reinterpret_cast<const uint4*>(st.w[wave])[2 * r + (h ^ cswz<4>(r))];
+        wl[cb][0] = v.x; wl[cb][1] = v.y; wl[cb][2] = v.z; wl[cb][3] = v.w;
+      } else if constexpr (BITS == 8) {
+        const uint4* w4 = reinterpret_cast<const uint4*>(st.w[wave]) + 4 * r;
+        const uint4 v = w4[(2 * h) ^ cswz<8>(r)], u = w4[(2 * h + 1) ^ cswz<8>(r)];
+        wl[cb][0] = v.x; wl[cb][1] = v.y; wl[cb][2] = v.z; wl[cb][3] = v.w;
+        wl[cb][4] = u.x; wl[cb][5] = u.y; wl[cb][6] = u.z; wl[cb][7] = u.w;
+      } else {
+        load_half<BITS>(st.w[wave] + r * WPB, h, wl[cb]);
+      }
       const uint16_t sb = reinterpret_cast<const uint16_t*>(st.meta[wave])[r];
       const int zb = reinterpret_cast<const uint8_t*>(st.meta[wave])[128 + r];
       d[cb] = make_deq(h2f(sb), zb);
@@ -1705,7 +1744,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm_lds(
       f16x8 a[RB], b[2];
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
-        const int row = 32 * rb + c, c8 = (4 * h + s4) ^ (row & 7);
+        const int row = 32 * rb + c, c8 = xswz(row, 4 * h + s4);
         a[rb] = *reinterpret_cast<const f16x8*>(st.x + row * 64 + 8 * c8);
       }
 #pragma unroll
