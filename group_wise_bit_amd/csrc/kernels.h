@@ -432,6 +432,22 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemv_packed(
   }
 }
 
+// Work-groups go to the 8 XCDs (each with its own L2) round-robin by their
+// flattened id.  This maps the flattened id to a grid position (x fastest)
+// such that every XCD gets one contiguous range of positions, so that
+// neighbouring positions (the parts of one tile, which share its scale and
+// zero lines) are fetched into one L2.  A bijection of the grid onto itself.
+constexpr int kXcds = 8;
+__device__ __forceinline__ void xcd_grid_pos(int& x, int& y) {
+  const int nx = gridDim.x, n = nx * gridDim.y;
+  const int f = blockIdx.x + nx * blockIdx.y;
+  const int per = n / kXcds, rem = n % kXcds, xcd = f % kXcds, local = f / kXcds;
+  const int lin = xcd < rem ? xcd * (per + 1) + local
+                            : rem * (per + 1) + (xcd - rem) * per + local;
+  x = lin % nx;
+  y = lin / nx;
+}
+
 // ------------------------------------------------ narrow packed GEMV --
 // For launches of few tiles: a work-group covers 64/NG rows of a tile (grid.x =
 // NG x launch tiles), so a small matrix is spread over NG times as many
@@ -593,8 +609,9 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemv_narrow(
   const uint32_t magic = vreg_const(kMagic);
   const int lane = lane_id(), wave = wave_id();
   const int r = lane / NG, g = lane % NG;
-  const int sp = blockIdx.y;
-  const int lt = blockIdx.x / NG, part_i = blockIdx.x % NG;
+  int bx, sp;
+  xcd_grid_pos(bx, sp);
+  const int lt = bx / NG, part_i = bx % NG;
   const uint32_t* codes = set.codes[0];
   const uint16_t* scale = set.scale[0];
   const uint8_t* zero = set.zero[0];
@@ -672,13 +689,13 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemv_narrow(
     for (int w = 1; w < WAVES; ++w) tot[m] += red[m][w][lane];
   }
   if (splits > 1) {
-    // part[split][matrix][launch row], launch row = RW * work-group + lane
+    // part[split][matrix][launch row], launch row = RW * position + lane
     const int64_t np = (int64_t)gridDim.x * RW;
-    const int64_t grow = (int64_t)blockIdx.x * RW + lane;
+    const int64_t grow = (int64_t)bx * RW + lane;
 #pragma unroll
     for (int m = 0; m < NM; ++m) put_partial(part + ((int64_t)sp * NM + m) * np + grow, tot[m]);
     partials_written();
-    if (!split_ticket(tickets, blockIdx.x, splits)) return;
+    if (!split_ticket(tickets, bx, splits)) return;
 #pragma unroll
     for (int m = 0; m < NM; ++m) tot[m] = sum_splits(part + m * np + grow, NM * np, splits);
   }
@@ -826,7 +843,8 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemv_fused_narrow(
   __shared__ float red[WAVES][RW];
   const int lane = lane_id(), wave = wave_id();
   const int r = lane / NG, g = lane % NG;
-  const int t = blockIdx.x / NG, part_i = blockIdx.x % NG, sp = blockIdx.y;
+  const int bx = blockIdx.x, sp = blockIdx.y;
+  const int t = bx / NG, part_i = bx % NG;
   const int R = part_i * RW + r;
   const int row = t * kTile + R;
   const int rrow = min(row, n - 1);
@@ -907,12 +925,12 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemv_fused_narrow(
   for (int w = 1; w < WAVES; ++w) tot += red[w][lane];
   const int orow = t * kTile + part_i * RW + lane;
   if (splits > 1) {
-    // part[split][launch row], launch row = RW * work-group + lane
+    // part[split][launch row], launch row = RW * position + lane
     const int64_t np = (int64_t)gridDim.x * RW;
-    const int64_t grow = (int64_t)blockIdx.x * RW + lane;
+    const int64_t grow = (int64_t)bx * RW + lane;
     put_partial(part + (int64_t)sp * np + grow, tot);
     partials_written();
-    if (!split_ticket(tickets, blockIdx.x, splits)) return;
+    if (!split_ticket(tickets, bx, splits)) return;
     tot = sum_splits(part + grow, np, splits);
   }
   if (orow < n) y[orow] = tot;
