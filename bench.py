@@ -306,22 +306,24 @@ def build_decode(torch, qlin, synth, dev, ws, phases, state):
     fl = {m: sum(2 * m * shapes[i][2] * shapes[i][3] for i in layer_idx) for m in (128, 2048)}
     out = [
         Phase("decode_step", run, "GB/s", grp_bytes, grp_launches, HBM_PEAK_GBS, "hbm",
-              "k_gemv_packed<4> (q/k/v set, o, gate/up+SwiGLU, down; LM head)"),
-        Phase("decode_gemv", run, "GB/s", dec_bytes, 169, HBM_PEAK_GBS, "hbm", "k_gemv_packed<4>"),
+              "k_gemv_narrow<4> (q/k/v set, o, gate/up+SwiGLU, down) + k_gemv_packed<4> (LM head)"),
+        Phase("decode_gemv", run, "GB/s", dec_bytes, 169, HBM_PEAK_GBS, "hbm",
+              "k_gemv_narrow<4> + k_gemv_packed<4> (LM head)"),
         Phase("prefill_step_m128", run, "TFLOP/s", fl[128], 96, FP16_MFMA_PEAK_TFLOPS, "mfma",
-              "k_gemm_tiles<4, 32> (q/k/v set, o, gate/up set, down)"),
+              "k_gemm_ksplit<4> (q/k/v set, o, gate/up set, down)"),
         Phase("prefill_step_m2048", run, "TFLOP/s", fl[2048], 96, FP16_MFMA_PEAK_TFLOPS,
-              "mfma", "k_gemm_lds<4, 128|64> / k_gemm_tiles<4, 32> (q/k/v set, o, gate/up set, down)"),
+              "mfma",
+              "k_gemm_lds<4, 128> (gate/up set), k_gemm_ksplit<4> (q/k/v set, down), k_gemm_tiles<4, 32> (o)"),
         Phase("prefill_m128", run, "TFLOP/s", fl[128], 168, FP16_MFMA_PEAK_TFLOPS, "mfma",
-              "k_gemm_tiles<4>"),
+              "k_gemm_ksplit<4>"),
         Phase("prefill_m2048", run, "TFLOP/s", fl[2048], 168, FP16_MFMA_PEAK_TFLOPS, "mfma",
-              "k_gemm_tiles<4>"),
+              "k_gemm_lds<4> / k_gemm_tiles<4> / k_gemm_ksplit<4>"),
         Phase("gemm_m8", run, "GB/s",
               sum(wbytes(n, k, 4, 64) + 16 * k + 32 * n for (_, _, n, k) in shapes), 169,
-              HBM_PEAK_GBS, "hbm", "k_gemm_skinny<4>"),
+              HBM_PEAK_GBS, "hbm", "k_gemm_ksplit<4> + k_gemm_skinny<4> (down)"),
         Phase("fused_gemv", run, "GB/s",
               master_bytes + meta_bytes + sum(2 * k + 4 * n for (_, _, n, k) in shapes), 169,
-              HBM_PEAK_GBS, "hbm", "k_gemv_fused<4>"),
+              HBM_PEAK_GBS, "hbm", "k_gemv_fused_narrow<4> + k_gemv_fused<4> (LM head)"),
         Phase("rtn_precompute", run, "GB/s", master_bytes + meta_bytes, 3, HBM_PEAK_GBS,
               "hbm", "k_quantize_g64<4> (no codes; 169 matrices in 3 launches)"),
         Phase("quantize_pack", run, "GB/s", master_bytes + meta_bytes + code_bytes, 3,
@@ -389,17 +391,17 @@ def build_qwen3_8b(torch, qlin, synth, dev, ws, phases):
     out = []
     for b in (4, 3, 2):
         out.append(Phase(f"q8_step_int{b}", run, "GB/s", step_bytes.get(b, 0), 144, HBM_PEAK_GBS,
-                         "hbm", f"k_gemv_packed<{b}> (q/k/v set, o, gate/up+SwiGLU, down)"))
+                         "hbm", f"k_gemv_packed<{b}> (q/k/v set, gate/up+SwiGLU, down), k_gemv_narrow<{b}> (o)"))
         out.append(Phase(f"q8_decode_int{b}", run, "GB/s",
                          sum(wbytes(n, k, b, 64) + 2 * k + 4 * n for (_, _, n, k) in shapes),
-                         252, HBM_PEAK_GBS, "hbm", f"k_gemv_packed<{b}>"))
+                         252, HBM_PEAK_GBS, "hbm", f"k_gemv_packed<{b}> + k_gemv_narrow<{b}>"))
     for b in (4, 3):
         out.append(Phase(f"q8_m8_int{b}", run, "GB/s",
                          sum(wbytes(n, k, b, 64) + 16 * k + 32 * n for (_, _, n, k) in shapes),
-                         252, HBM_PEAK_GBS, "hbm", f"k_gemm_skinny<{b}>"))
+                         252, HBM_PEAK_GBS, "hbm", f"k_gemm_ksplit<{b}>"))
         out.append(Phase(f"q8_m128_int{b}", run, "TFLOP/s",
                          sum(2 * 128 * n * k for (_, _, n, k) in shapes), 252,
-                         FP16_MFMA_PEAK_TFLOPS, "mfma", f"k_gemm_tiles<{b}>"))
+                         FP16_MFMA_PEAK_TFLOPS, "mfma", f"k_gemm_ksplit<{b}>"))
     return [p for p in out if p.name in phases]
 
 
@@ -446,12 +448,12 @@ def build_qwen3_06b(torch, qlin, synth, dev, ws, phases):
     for (b, gr) in combos:
         mb = sum(n * (k // (64 if gr == "g64" else k)) * 3 for (_, _, n, k) in shapes)
         out.append(Phase(f"q06_fused_b{b}_{gr}", run, "GB/s", master_bytes + mb + act, 196,
-                         HBM_PEAK_GBS, "hbm", f"k_gemv_fused<{b}>"))
+                         HBM_PEAK_GBS, "hbm", f"k_gemv_fused_narrow<{b}>"))
         out.append(Phase(f"q06_lever_b{b}_{gr}", run, "GB/s", master_bytes + mb, 4,
                          HBM_PEAK_GBS, "hbm",
                          f"k_quantize_{'g64' if gr == 'g64' else 'row'}<{b}> (no codes)"))
     out.append(Phase("q06_fp16_control", run, "GB/s", master_bytes + act, 196, HBM_PEAK_GBS,
-                     "hbm", "k_gemv_fused<16>"))
+                     "hbm", "k_gemv_fused_narrow<16>"))
     return [p for p in out if p.name in phases]
 
 
@@ -580,7 +582,7 @@ def main():
     print(json.dumps(out), flush=True)
 
 
-TRAFFIC_SUMMARY = os.path.join(HERE, "profiles", "gemv_packed_int4_qwen25_decode_step_hbm_traffic.txt")
+TRAFFIC_SUMMARY = os.path.join(HERE, "profiles", "gemv_int4_qwen25_decode_step_hbm_traffic.txt")
 
 
 def kernel_source_hash():
