@@ -6,13 +6,26 @@
 
 #include "device_common.h"
 
+#include <type_traits>
+
 namespace qlin {
 
 // ---------------------------------------------------------------- packing --
 // 64 codes (0..qmax, held as floats) -> 2*BITS words of one block.
 template <int BITS>
 __device__ __forceinline__ void pack_block(const float* code, uint32_t* out) {
-  if constexpr (BITS == 3) {
+  if constexpr (BITS >= 5 && BITS <= 7) {
+    // split planes: low 4 bits as a 4-bit block, the rest as a (BITS-4)-bit one
+    float lo[64], hi[64];
+#pragma unroll
+    for (int c = 0; c < 64; ++c) {
+      const uint32_t v = (uint32_t)code[c];
+      lo[c] = (float)(v & 15u);
+      hi[c] = (float)(v >> 4);
+    }
+    pack_block<4>(lo, out);
+    pack_block<BITS - 4>(hi, out + 8);
+  } else if constexpr (BITS == 3) {
 #pragma unroll
     for (int run = 0; run < 2; ++run) {
       uint32_t lo0 = 0, lo1 = 0, hi = 0;
@@ -49,7 +62,9 @@ __device__ __forceinline__ void pack_block(const float* code, uint32_t* out) {
 // (the inverse of pack_block, element by element).
 template <int BITS>
 __device__ __forceinline__ uint32_t code_at(const uint32_t* words, int c) {
-  if constexpr (BITS == 3) {
+  if constexpr (BITS >= 5 && BITS <= 7) {
+    return code_at<4>(words, c) | (code_at<BITS - 4>(words + 8, c) << 4);
+  } else if constexpr (BITS == 3) {
     const int run = c >> 5, cr = c & 31;
     const int u = cr >> 4, i = cr & 15, p = i >> 1, e = i & 1;
     const uint32_t lo = (words[3 * run + u] >> (16 * e + 2 * p)) & 3u;
@@ -74,8 +89,39 @@ __device__ __forceinline__ uint32_t zconst(int z, int shift) {
 }
 
 template <int BITS>
+__device__ __forceinline__ float block_dot(const uint32_t* wd, const f16x2* xb, int z, uint32_t kMagic);
+
+// 1-bit plane (the high bit of 5-bit codes): word w holds codes 32w + i, bit
+// p of each half pairs codes (2p, 2p+1) with scale class S = 2^(p mod 8);
+// z is 0 or 1.
+__device__ __forceinline__ float block_dot1(const uint32_t* wd, const f16x2* xb, int z,
+                                            uint32_t kMagic) {
+  float a[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int w = 0; w < 2; ++w) {
+    const uint32_t v = wd[w], vs = v >> 8;
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+      const uint32_t m = (1u << p) | (1u << (16 + p));
+      const f16x2 c = as_h2(zconst(z, p));
+      a[p] = __builtin_amdgcn_fdot2(as_h2((v & m) | kMagic) - c, xb[16 * w + p], a[p], false);
+      a[p] = __builtin_amdgcn_fdot2(as_h2((vs & m) | kMagic) - c, xb[16 * w + 8 + p], a[p], false);
+    }
+  }
+  return ((a[0] + a[1] * 0.5f) + (a[2] * 0.25f + a[3] * 0.125f)) +
+         ((a[4] * 0.0625f + a[5] * 0.03125f) + (a[6] * 0.015625f + a[7] * 0.0078125f));
+}
+
+template <int BITS>
 __device__ __forceinline__ float block_dot(const uint32_t* wd, const f16x2* xb, int z, uint32_t kMagic) {
-  if constexpr (BITS == 4) {
+  if constexpr (BITS >= 5 && BITS <= 7) {
+    // q - z = (lo - z % 16) + 16 * (hi - z / 16) over the two planes (each
+    // plane's zero fits its own magic constant)
+    float hi;
+    if constexpr (BITS == 5) hi = block_dot1(wd + 8, xb, z >> 4, kMagic);
+    else hi = block_dot<BITS - 4>(wd + 8, xb, z >> 4, kMagic);
+    return block_dot<4>(wd, xb, z & 15, kMagic) + 16.f * hi;
+  } else if constexpr (BITS == 4) {
     const f16x2 c1 = as_h2(zconst(z, 0)), c16 = as_h2(zconst(z, 4));
     float a0 = 0.f, a1 = 0.f, b0 = 0.f, b1 = 0.f;
 #pragma unroll
@@ -194,32 +240,29 @@ __device__ __forceinline__ f16x8 to_f16x8(const float* f) {
   return r;
 }
 
+// Exact fp32 weights of 8 codes (before the rounding to fp16).
 // int4: one word = 8 codes.  S=1 for (v & 0x000F000F), S=16 for (v & 0x00F000F0).
-__device__ __forceinline__ f16x8 deq_chunk4(uint32_t v, const Deq& d, uint32_t kMagic) {
-  float f[8];
+__device__ __forceinline__ void deq_chunk4f(uint32_t v, const Deq& d, uint32_t kMagic, float* f) {
   const uint32_t vs = v >> 8;
   deq_pair((v & 0x000F000Fu) | kMagic, d.sS[0], d.cS[0], f[0], f[1]);
   deq_pair((v & 0x00F000F0u) | kMagic, d.sS[2], d.cS[2], f[2], f[3]);
   deq_pair((vs & 0x000F000Fu) | kMagic, d.sS[0], d.cS[0], f[4], f[5]);
   deq_pair((vs & 0x00F000F0u) | kMagic, d.sS[2], d.cS[2], f[6], f[7]);
-  return to_f16x8(f);
 }
 
-// int2: half `hv` of a word (0: pairs 0..3 from v, 1: pairs 4..7 from v >> 8).
-__device__ __forceinline__ f16x8 deq_chunk2(uint32_t v, const Deq& d, uint32_t kMagic) {
-  float f[8];
+// int2: pairs 0..3 of v (the caller passes v >> 8 for the upper pairs).
+__device__ __forceinline__ void deq_chunk2f(uint32_t v, const Deq& d, uint32_t kMagic, float* f) {
 #pragma unroll
   for (int p = 0; p < 4; ++p) {
     const uint32_t m = (3u << (2 * p)) | (3u << (16 + 2 * p));
     deq_pair((v & m) | kMagic, d.sS[p], d.cS[p], f[2 * p], f[2 * p + 1]);
   }
-  return to_f16x8(f);
 }
 
 // int3: low-bit word L (already shifted for the upper pairs) and high-bit word
 // H (already rotated / shifted to line up with L).
-__device__ __forceinline__ f16x8 deq_chunk3(uint32_t L, uint32_t H, const Deq& d, uint32_t kMagic) {
-  float f[8];
+__device__ __forceinline__ void deq_chunk3f(uint32_t L, uint32_t H, const Deq& d, uint32_t kMagic,
+                                            float* f) {
 #pragma unroll
   for (int p = 0; p < 4; ++p) {
     const uint32_t m2 = (3u << (2 * p)) | (3u << (16 + 2 * p));
@@ -227,6 +270,33 @@ __device__ __forceinline__ f16x8 deq_chunk3(uint32_t L, uint32_t H, const Deq& d
     const uint32_t t = (L & m2) | (H & ~m2);
     deq_pair((t & (m2 | m1)) | kMagic, d.sS[p], d.cS[p], f[2 * p], f[2 * p + 1]);
   }
+}
+
+// 1-bit plane: bits 0..3 of each half of v (the caller shifts v to the chunk),
+// scale classes S = 1, 2, 4, 8 (d from make_deq_pow2).
+__device__ __forceinline__ void deq_chunk1f(uint32_t v, const Deq& d, uint32_t kMagic, float* f) {
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const uint32_t m = (1u << p) | (1u << (16 + p));
+    deq_pair((v & m) | kMagic, d.sS[p], d.cS[p], f[2 * p], f[2 * p + 1]);
+  }
+}
+
+__device__ __forceinline__ f16x8 deq_chunk4(uint32_t v, const Deq& d, uint32_t kMagic) {
+  float f[8];
+  deq_chunk4f(v, d, kMagic, f);
+  return to_f16x8(f);
+}
+
+__device__ __forceinline__ f16x8 deq_chunk2(uint32_t v, const Deq& d, uint32_t kMagic) {
+  float f[8];
+  deq_chunk2f(v, d, kMagic, f);
+  return to_f16x8(f);
+}
+
+__device__ __forceinline__ f16x8 deq_chunk3(uint32_t L, uint32_t H, const Deq& d, uint32_t kMagic) {
+  float f[8];
+  deq_chunk3f(L, H, d, kMagic, f);
   return to_f16x8(f);
 }
 
@@ -238,6 +308,39 @@ __device__ __forceinline__ f16x8 deq_chunk8(uint32_t v, uint32_t u, const Deq& d
   deq_pair(__builtin_amdgcn_perm(0x64646464u, u, 0x04020400u), d.sS[0], d.cS[0], f[4], f[5]);
   deq_pair(__builtin_amdgcn_perm(0x64646464u, u, 0x04030401u), d.sS[0], d.cS[0], f[6], f[7]);
   return to_f16x8(f);
+}
+
+// 5-7 bits (split planes): s*(q - z) = s*(lo - z%16) + 16s*(hi - z/16), each
+// term exact in fp32 and so their sum (|q - z| <= 127, an 18-bit multiple of
+// the scale's last place), rounded to fp16 once.
+__device__ __forceinline__ Deq make_deq_pow2(float s, int z) {
+  Deq d;
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const float inv = 1.0f / (float)(1 << p);          // exact power of two
+    d.sS[p] = s * inv;
+    d.cS[p] = -s * (float)((1024 >> p) + z);
+  }
+  return d;
+}
+
+struct Deq2 {
+  Deq lo, hi;
+};
+
+template <int BITS>
+using DeqT = typename std::conditional<(BITS >= 5 && BITS <= 7), Deq2, Deq>::type;
+
+template <int BITS>
+__device__ __forceinline__ DeqT<BITS> make_deq_b(float s, int z) {
+  if constexpr (BITS >= 5 && BITS <= 7) {
+    Deq2 d;
+    d.lo = make_deq(s, z & 15);
+    d.hi = BITS == 5 ? make_deq_pow2(16.f * s, z >> 4) : make_deq(16.f * s, z >> 4);
+    return d;
+  } else {
+    return make_deq(s, z);
+  }
 }
 
 // fp16 x 8 held in one uint4, as an MFMA operand.

@@ -62,10 +62,11 @@ __device__ __forceinline__ void codes_and_store(const float* w, float s, int z,
   }
   uint32_t out[2 * BITS];
   pack_block<BITS>(code, out);
-  if constexpr (BITS == 3) {
+  if constexpr (BITS % 2 == 1) {
+    // 2*BITS words, 8-byte aligned rows (3, 5, 7 bits)
     uint2* d2 = reinterpret_cast<uint2*>(dst);
 #pragma unroll
-    for (int i = 0; i < 3; ++i) d2[i] = make_uint2(out[2 * i], out[2 * i + 1]);
+    for (int i = 0; i < BITS; ++i) d2[i] = make_uint2(out[2 * i], out[2 * i + 1]);
   } else {
     uint4* d4 = reinterpret_cast<uint4*>(dst);
 #pragma unroll
@@ -80,9 +81,9 @@ __device__ __forceinline__ void codes_and_store(const float* w, float s, int z,
 // numbered consecutively over the jobs (end[i] = items of jobs 0..i), and
 // each work-group finds its job by a scan over the ends.
 constexpr int kQuantBatch = 64;
-// Widths with a packed layout; 5-7 bits exist only as scale/zero of fp16 masters.
+// Widths with a packed layout (all of the lever's quantized widths).
 template <int BITS>
-constexpr bool kPackable = BITS == 2 || BITS == 3 || BITS == 4 || BITS == 8;
+constexpr bool kPackable = BITS >= 2 && BITS <= 8;
 struct QuantJob {
   const uint16_t* w16;
   int64_t ld;
@@ -262,10 +263,11 @@ __device__ __forceinline__ void loads_issued() { __builtin_amdgcn_sched_barrier(
 // shared by all rows of the tile).
 template <int BITS>
 __device__ __forceinline__ void load_block_words(const uint32_t* __restrict__ blk, uint32_t* wd) {
-  if constexpr (BITS == 3) {
+  if constexpr (BITS % 2 == 1) {
+    // 2*BITS words, 8-byte aligned rows (3, 5, 7 bits)
     const uint2* b2 = reinterpret_cast<const uint2*>(blk);
 #pragma unroll
-    for (int i = 0; i < 3; ++i) { const uint2 v = b2[i]; wd[2 * i] = v.x; wd[2 * i + 1] = v.y; }
+    for (int i = 0; i < BITS; ++i) { const uint2 v = b2[i]; wd[2 * i] = v.x; wd[2 * i + 1] = v.y; }
   } else {
     const uint4* b4 = reinterpret_cast<const uint4*>(blk);
 #pragma unroll
@@ -457,8 +459,19 @@ __device__ __forceinline__ void xcd_grid_pos(int& x, int& y) {
 // block per instruction.  x differs between slices and is read with vector
 // loads (128/NG bytes per lane and block; NG distinct addresses per wave).
 template <int BITS, int NG>
+constexpr int slice_words() {
+  if constexpr (BITS >= 5 && BITS <= 7) {
+    // the 4-bit plane's slice words, then the high plane's (one word for the
+    // 1-bit plane)
+    if constexpr (BITS == 5) return slice_words<4, NG>() + 1;
+    else return slice_words<4, NG>() + slice_words<BITS - 4, NG>();
+  } else {
+    return BITS == 3 ? 2 : (NG == 4 ? BITS / 2 : (BITS == 2 ? 1 : BITS / 4));
+  }
+}
+template <int BITS, int NG>
 struct SliceWords {
-  static constexpr int n = BITS == 3 ? 2 : (NG == 4 ? BITS / 2 : (BITS == 2 ? 1 : BITS / 4));
+  static constexpr int n = slice_words<BITS, NG>();
 };
 
 // The words holding slice g of one row's block (row_blk = the row's first word).
@@ -466,7 +479,12 @@ template <int BITS, int NG>
 __device__ __forceinline__ void load_slice_words(const uint32_t* __restrict__ row_blk, int g,
                                                  uint32_t* wd) {
   constexpr int CPS = 64 / NG;                        // codes per slice
-  if constexpr (BITS == 3) {
+  if constexpr (BITS >= 5 && BITS <= 7) {
+    constexpr int W4 = SliceWords<4, NG>::n;
+    load_slice_words<4, NG>(row_blk, g, wd);
+    if constexpr (BITS == 5) wd[W4] = row_blk[8 + (NG == 4 ? g >> 1 : g >> 2)];   // 32 codes/word
+    else load_slice_words<BITS - 4, NG>(row_blk + 8, g, wd + W4);
+  } else if constexpr (BITS == 3) {
     // the low-bit word of the slice's 16-code half-run, the run's third-bit word
     const int c0 = CPS * g, run = c0 >> 5, u = (c0 >> 4) & 1;
     wd[0] = row_blk[3 * run + u];
@@ -542,6 +560,21 @@ __device__ __forceinline__ float eight_bits8(uint32_t v, uint32_t u, const f16x2
   return (a0 + a1) + (b0 + b1);
 }
 
+// 1-bit plane: NP code pairs from bits 0..NP-1 of each half of v (shifted to
+// the slice by the caller), scale class S = 2^p; z is 0 or 1.
+template <int NP>
+__device__ __forceinline__ float one_bits(uint32_t v, const f16x2* xs, int z, uint32_t kMagic) {
+  // sum over p of dot_p / 2^p, evaluated as a Horner scheme in 1/2
+  float acc = 0.f;
+#pragma unroll
+  for (int p = NP - 1; p >= 0; --p) {
+    const uint32_t m = (1u << p) | (1u << (16 + p));
+    const f16x2 h = as_h2((v & m) | kMagic) - as_h2(zconst(z, p));
+    acc = __builtin_amdgcn_fdot2(h, xs[p], acc * 0.5f, false);
+  }
+  return acc;
+}
+
 // sum over the codes of slice g of x_k * (q_k - z), unscaled; xs = the
 // slice's x pairs.  The decode of block_dot, restricted to the slice.  A
 // slice of 16 codes is two 8-code halves; the second half of a 2- or 3-bit
@@ -562,6 +595,19 @@ __device__ __forceinline__ float slice_dot(const uint32_t* wd, const f16x2* xs, 
     } else {
       return low_bits8(wd[0] >> (8 * (g & 1)), xs, z, kMagic);
     }
+  } else if constexpr (BITS >= 5 && BITS <= 7) {
+    // q - z = (lo - z % 16) + 16 * (hi - z / 16)
+    constexpr int W4 = SliceWords<4, NG>::n;
+    const float lo = slice_dot<4, NG>(wd, xs, z & 15, g, kMagic);
+    float hi;
+    if constexpr (BITS == 5) {
+      // 1-bit plane: NG = 4 takes 8 pairs at bit 8*(g%2), NG = 8 four at 4*(g%4)
+      if constexpr (NG == 4) hi = one_bits<8>(wd[W4] >> (8 * (g & 1)), xs, z >> 4, kMagic);
+      else hi = one_bits<4>(wd[W4] >> (4 * (g & 3)), xs, z >> 4, kMagic);
+    } else {
+      hi = slice_dot<BITS - 4, NG>(wd + W4, xs, z >> 4, g, kMagic);
+    }
+    return lo + 16.f * hi;
   } else {  // BITS == 3
     const uint32_t H = wd[1];
     const int c0 = (64 / NG) * g;
@@ -1142,7 +1188,15 @@ constexpr int kLdsRow = 72;   // fp16 per padded LDS row
 
 template <int BITS>
 __device__ __forceinline__ void load_half(const uint32_t* __restrict__ blk, int h, uint32_t* wl) {
-  if constexpr (BITS == 4) {
+  if constexpr (BITS >= 5 && BITS <= 7) {
+    // wl[0..3]: the 4-bit plane's half (words 4h..4h+3, read as two 8-byte
+    // pairs: 5- and 7-bit rows are 8-byte aligned); then the high plane's half
+    const uint2* b2 = reinterpret_cast<const uint2*>(blk) + 2 * h;
+    const uint2 v = b2[0], u = b2[1];
+    wl[0] = v.x; wl[1] = v.y; wl[2] = u.x; wl[3] = u.y;
+    if constexpr (BITS == 5) wl[4] = blk[8 + h];
+    else load_half<BITS - 4>(blk + 8, h, wl + 4);
+  } else if constexpr (BITS == 4) {
     const uint4 v = reinterpret_cast<const uint4*>(blk)[h];
     wl[0] = v.x; wl[1] = v.y; wl[2] = v.z; wl[3] = v.w;
   } else if constexpr (BITS == 2) {
@@ -1159,8 +1213,26 @@ __device__ __forceinline__ void load_half(const uint32_t* __restrict__ blk, int 
 }
 
 template <int BITS>
-__device__ __forceinline__ f16x8 deq_half(const uint32_t* wl, int s, const Deq& d, uint32_t magic) {
-  if constexpr (BITS == 4) {
+__device__ __forceinline__ f16x8 deq_half(const uint32_t* wl, int s, const DeqT<BITS>& d,
+                                          uint32_t magic) {
+  if constexpr (BITS >= 5 && BITS <= 7) {
+    float f[8], g[8];
+    deq_chunk4f(wl[s], d.lo, magic, f);
+    if constexpr (BITS == 5) {
+      deq_chunk1f(wl[4] >> (4 * s), d.hi, magic, g);
+    } else if constexpr (BITS == 6) {
+      const uint32_t v = wl[4 + (s >> 1)];
+      deq_chunk2f((s & 1) ? (v >> 8) : v, d.hi, magic, g);
+    } else {
+      const int u = s >> 1;
+      const uint32_t L = wl[4 + u];
+      const uint32_t Hu = u ? __builtin_amdgcn_alignbit(wl[6], wl[6], 8) : wl[6];
+      deq_chunk3f((s & 1) ? (L >> 8) : L, (s & 1) ? (Hu >> 1) : Hu, d.hi, magic, g);
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) f[i] += g[i];
+    return to_f16x8(f);
+  } else if constexpr (BITS == 4) {
     return deq_chunk4(wl[s], d, magic);
   } else if constexpr (BITS == 2) {
     const uint32_t v = wl[s >> 1];
@@ -1266,10 +1338,10 @@ __global__ __launch_bounds__(256) void k_gemm_tiles(
   auto step = [&](auto setc, auto nextc, bool decode_next) __attribute__((always_inline)) {
     constexpr int P = decltype(setc)::value;
     constexpr int Q = decltype(nextc)::value;
-    Deq dn[2];
+    DeqT<BITS> dn[2];
     if (decode_next) {
 #pragma unroll
-      for (int cb = 0; cb < 2; ++cb) dn[cb] = make_deq(sc[Q][cb], zc[Q][cb]);
+      for (int cb = 0; cb < 2; ++cb) dn[cb] = make_deq_b<BITS>(sc[Q][cb], zc[Q][cb]);
     }
     // A fragments of slice s4+1 are read from LDS while slice s4's MFMAs run.
     f16x8 a[2][RB];
@@ -1310,7 +1382,7 @@ __global__ __launch_bounds__(256) void k_gemm_tiles(
   for (int i = 0; i < XCH; ++i) land_x(S0{}, i);
 #pragma unroll
   for (int cb = 0; cb < 2; ++cb) {
-    const Deq d = make_deq(sc[0][cb], zc[0][cb]);
+    const DeqT<BITS> d = make_deq_b<BITS>(sc[0][cb], zc[0][cb]);
 #pragma unroll
     for (int s4 = 0; s4 < 4; ++s4) bfrag[0][cb][s4] = deq_half<BITS>(wl[0][cb], s4, d, magic);
   }
@@ -1475,7 +1547,7 @@ __global__ __launch_bounds__(256) void k_gemm_ksplit(
       const bool valid = jb + 4 * u < j1;
 #pragma unroll
       for (int cb = 0; cb < 2; ++cb) {
-        const Deq d = make_deq(masked_scale(sr[u][cb], valid), zc[u][cb]);
+        const DeqT<BITS> d = make_deq_b<BITS>(masked_scale(sr[u][cb], valid), zc[u][cb]);
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
           const f16x8 bf = deq_half<BITS>(wl[u][cb], s, d, magic);
@@ -1653,6 +1725,9 @@ template <> struct WDma<2> { static constexpr int SZ = 16, N = 1; };
 template <> struct WDma<3> { static constexpr int SZ = 4, N = 6; };
 template <> struct WDma<4> { static constexpr int SZ = 16, N = 2; };
 template <> struct WDma<8> { static constexpr int SZ = 16, N = 4; };
+template <> struct WDma<5> { static constexpr int SZ = 4, N = 10; };
+template <> struct WDma<6> { static constexpr int SZ = 16, N = 3; };
+template <> struct WDma<7> { static constexpr int SZ = 4, N = 14; };
 
 template <int BITS, int MB, int S>
 __global__ __launch_bounds__(256, 2) void k_gemm_lds(
@@ -1737,8 +1812,8 @@ __global__ __launch_bounds__(256, 2) void k_gemm_lds(
   auto compute = [&](auto stc) __attribute__((always_inline)) {
     constexpr int I = decltype(stc)::value;
     const GemmStage<BITS, MB>& st = gemm_stage<BITS, MB, I>();
-    uint32_t wl[2][(BITS == 3) ? 3 : BITS];
-    Deq d[2];
+    uint32_t wl[2][BITS];
+    DeqT<BITS> d[2];
 #pragma unroll
     for (int cb = 0; cb < 2; ++cb) {
       const int r = 32 * cb + c;
@@ -1755,7 +1830,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm_lds(
       }
       const uint16_t sb = reinterpret_cast<const uint16_t*>(st.meta[wave])[r];
       const int zb = reinterpret_cast<const uint8_t*>(st.meta[wave])[128 + r];
-      d[cb] = make_deq(h2f(sb), zb);
+      d[cb] = make_deq_b<BITS>(h2f(sb), zb);
     }
 #pragma unroll
     for (int s4 = 0; s4 < 4; ++s4) {

@@ -36,8 +36,8 @@ inline Range range_of(const void* p, int64_t bytes) {
 inline bool overlaps(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
 
 // Widths with a packed-code layout, and every width of the lever (scale/zero
-// precompute and the fused re-quantizing GEMV from fp16 masters).
-bool valid_bits(int bits) { return bits == 2 || bits == 3 || bits == 4 || bits == 8; }
+// precompute and the fused re-quantizing GEMV from fp16 masters): the same.
+bool valid_bits(int bits) { return bits >= 2 && bits <= 8; }
 bool lever_bits(int bits) { return bits >= 2 && bits <= 8; }
 
 qlin_status check_nk(int32_t n, int32_t k) {
@@ -386,6 +386,9 @@ qlin_status run_packed(const PackedLaunch& L, int bits, const uint16_t* x, void*
     case 2: launch_gemv_packed<2>(L, x2, part, tick, c, stream); break;
     case 3: launch_gemv_packed<3>(L, x2, part, tick, c, stream); break;
     case 4: launch_gemv_packed<4>(L, x2, part, tick, c, stream); break;
+    case 5: launch_gemv_packed<5>(L, x2, part, tick, c, stream); break;
+    case 6: launch_gemv_packed<6>(L, x2, part, tick, c, stream); break;
+    case 7: launch_gemv_packed<7>(L, x2, part, tick, c, stream); break;
     default: launch_gemv_packed<8>(L, x2, part, tick, c, stream); break;
   }
   return hip_status(hipGetLastError());
@@ -609,8 +612,10 @@ constexpr int kSkinnyMaxM = 16;
 // M <= 16: the K-split kernel (measured 1.1-2.5x faster than the skinny one
 // on the Qwen2.5-0.5B and Qwen3-8B shapes at M = 8, int4), except for long K
 // over fewer than 32 tiles, where the skinny kernel's split is cheaper.
-// QLIN_TUNE_GEMM="0,splits" / "16,1" force the K-split / skinny kernel.
-bool skinny_by_ksplit(int64_t tiles, int kb) {
+// QLIN_TUNE_GEMM="0,splits" / "16,1" force the K-split / skinny kernel.  The
+// skinny kernel exists for 2, 3, 4 and 8 bits only.
+bool skinny_by_ksplit(int64_t tiles, int kb, int bits) {
+  if (bits >= 5 && bits <= 7) return true;
   if (const char* e = getenv("QLIN_TUNE_GEMM")) {
     int mb = -1, sp = 0;
     if (sscanf(e, "%d,%d", &mb, &sp) == 2 && sp >= 1) {
@@ -755,7 +760,7 @@ int64_t gemm_set_ws_bytes(const qlin_weight* w, int count, int32_t m) {
     tiles += tiles_of(w[i].n);
     cols4 += (tiles_of(w[i].n) + 3) / 4;
   }
-  if (m > kSkinnyMaxM || skinny_by_ksplit(tiles, w[0].k / kBlock))
+  if (m > kSkinnyMaxM || skinny_by_ksplit(tiles, w[0].k / kBlock, w[0].bits))
     return tiles_ws_bytes(cols4, tiles, w[0].k / kBlock, m, count);
   return split_ws_bytes(tiles, w[0].k / kBlock, 16);
 }
@@ -905,6 +910,9 @@ qlin_status qlin_embed_rows(const qlin_weight* w, const int32_t* ids, int32_t co
     QLIN_EMBED(2)
     QLIN_EMBED(3)
     QLIN_EMBED(4)
+    QLIN_EMBED(5)
+    QLIN_EMBED(6)
+    QLIN_EMBED(7)
     QLIN_EMBED(8)
 #undef QLIN_EMBED
     default: return QLIN_ERR_BITS;
@@ -917,7 +925,7 @@ qlin_status run_gemm(const GemmPlan& p, const uint16_t* X, int m, int64_t ld_x, 
                      int64_t workspace_bytes, hipStream_t stream) {
   uint32_t* tick = static_cast<uint32_t*>(workspace);
   char* pbase = static_cast<char*>(workspace) + kCounterBytes;
-  if (m <= kSkinnyMaxM && !skinny_by_ksplit(p.tiles, p.kb)) {
+  if (m <= kSkinnyMaxM && !skinny_by_ksplit(p.tiles, p.kb, p.bits)) {
     const Split sp = choose_split(p.tiles, p.kb, workspace_bytes, 16);
     float* part = sp.splits > 1 ? reinterpret_cast<float*>(pbase) : nullptr;
     switch (p.bits) {
@@ -933,6 +941,9 @@ qlin_status run_gemm(const GemmPlan& p, const uint16_t* X, int m, int64_t ld_x, 
       case 2: launch_gemm_tiles<2>(p, X, ld_x, m, c, part, tick, stream); break;
       case 3: launch_gemm_tiles<3>(p, X, ld_x, m, c, part, tick, stream); break;
       case 4: launch_gemm_tiles<4>(p, X, ld_x, m, c, part, tick, stream); break;
+      case 5: launch_gemm_tiles<5>(p, X, ld_x, m, c, part, tick, stream); break;
+      case 6: launch_gemm_tiles<6>(p, X, ld_x, m, c, part, tick, stream); break;
+      case 7: launch_gemm_tiles<7>(p, X, ld_x, m, c, part, tick, stream); break;
       default: launch_gemm_tiles<8>(p, X, ld_x, m, c, part, tick, stream); break;
     }
   }

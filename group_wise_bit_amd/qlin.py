@@ -169,6 +169,15 @@ class QWeight:
         return b
 
 
+def _check_room(cbuf, code_bytes, scale, zero, entries) -> None:
+    """The output buffers must hold what the library writes (it cannot check)."""
+    if cbuf is not None and cbuf.numel() * cbuf.element_size() < code_bytes:
+        raise ValueError(f"codes buffer holds {cbuf.numel() * cbuf.element_size()} bytes, "
+                         f"{code_bytes} needed")
+    if scale.numel() < entries or zero.numel() < entries:
+        raise ValueError(f"scale/zero buffers hold fewer than {entries} entries")
+
+
 def quantize(w16: torch.Tensor, bits: int, group: int, codes: bool = True,
              out: Optional[QWeight] = None) -> QWeight:
     """qlin_quantize on a cuda fp16 [n, k] tensor -> packed QWeight (codes=False:
@@ -180,13 +189,14 @@ def quantize(w16: torch.Tensor, bits: int, group: int, codes: bool = True,
     n, k = w16.shape
     g = k if group in ("k", "K") else int(group)
     me = meta_entries(n, k, g)
-    pb = packed_bytes(n, k, bits) if bits in (2, 3, 4, 8) else 0
+    pb = packed_bytes(n, k, bits)
     if out is None:
         scale = torch.empty(max(me, 1), dtype=torch.float16, device=w16.device)
         zero = torch.empty(max(me, 1), dtype=torch.uint8, device=w16.device)
         cbuf = torch.empty(max(pb // 4, 1), dtype=torch.int32, device=w16.device) if codes else None
     else:
         scale, zero, cbuf = out.scale, out.zero, (out.data if codes else None)
+    _check_room(cbuf, pb, scale, zero, me)
     st = _lib().qlin_quantize(w16.data_ptr(), w16.stride(0), n, k, bits, g, _ptr(cbuf),
                               scale.data_ptr(), zero.data_ptr(), _stream())
     _check(st, "qlin_quantize")
@@ -324,11 +334,12 @@ def quantize_batch(masters: Sequence[torch.Tensor], bits: int, group, codes: boo
             raise TypeError("masters must be 2-D cuda float16 tensors with contiguous rows")
         n, k = w16.shape
         g = k if row else 64
+        me = meta_entries(n, k, g)
         if outs is not None:
             o = outs[i]
             scale, zero, cbuf = o.scale, o.zero, (o.data if codes else None)
+            _check_room(cbuf, packed_bytes(n, k, bits), scale, zero, me)
         else:
-            me = meta_entries(n, k, g)
             scale = torch.empty(max(me, 1), dtype=torch.float16, device=w16.device)
             zero = torch.empty(max(me, 1), dtype=torch.uint8, device=w16.device)
             cbuf = (torch.empty(max(packed_bytes(n, k, bits) // 4, 1), dtype=torch.int32,

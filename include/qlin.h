@@ -42,6 +42,10 @@
  *     the 2-bit arrangement above; word 3r+2 holds bit 2 of all 32 run codes:
  *     run code c' (0..31) with u = c'/16, i = c'%16, p = i/2, e = i%2 puts it
  *     at position  (p < 4 ? 2p + 2 : 2(p-4) + 3) + 16e,  plus 8 (mod 32) if u = 1.
+ *   - bits 5, 6, 7 ("split planes"): words 0..7 hold bits 0..3 of the 64 codes
+ *     in the 4-bit arrangement; words 8 .. 2*bits-1 hold bits 4 .. bits-1 as a
+ *     (bits-4)-bit code in the 1-, 2- or 3-bit arrangement, where 1 bit
+ *     follows the rule for bits 2, 4, 8 (word w: codes 32w + i at 16*(i%2) + i/2).
  *   With this arrangement, masking a word (or the word shifted right by 8)
  *   leaves two consecutive codes in the mantissas of two fp16 halves, so a
  *   pair of codes becomes a pair of fp16 values with one AND-OR.
@@ -85,7 +89,7 @@ enum {
 typedef struct qlin_weight {
   int32_t n;                /* output rows                                        */
   int32_t k;                /* reduction length, multiple of 64                   */
-  int32_t bits;             /* PACKED: 2, 3, 4, 8.  FP16_MASTER: 2 .. 8, or 16 =
+  int32_t bits;             /* PACKED: 2 .. 8.  FP16_MASTER: 2 .. 8, or 16 =
                                unquantized (the whole lever)                       */
   int32_t group;            /* 64, or k for one group per row                     */
   int32_t format;           /* QLIN_FMT_*                                         */
@@ -117,8 +121,7 @@ int64_t qlin_meta_entries(int32_t n, int32_t k, int32_t group);
  * precompute, then codes).  Bitcrush README, "Under the hood": a scale/zero
  * precompute pass, then the group-wise affine rounding.
  *   w16      fp16 masters [n, ld_w] row-major, ld_w >= k, ld_w % 8 == 0.
- *   bits     2 .. 8; codes need a packed layout: 2, 3, 4 or 8 (5 .. 7 with
- *            codes != NULL -> QLIN_ERR_BITS).
+ *   bits     2 .. 8 (every width has a packed layout).
  *   codes    packed codes out, qlin_packed_bytes(n, k, bits) bytes; pass NULL to
  *            compute only scale and zero (a change of bit width then needs no
  *            new codes: the fused matmul re-rounds on the fly).

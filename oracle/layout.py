@@ -21,6 +21,11 @@ The layout (restated here so this file stands on its own):
   the run's 32 codes.  For run code c' (0..31): u = c' // 16, i = c' % 16,
   p = i // 2, e = i % 2; the bit sits at position
   (2p + 2 if p < 4 else 2(p - 4) + 3) + 16e, plus 8 modulo 32 when u = 1.
+* bits in {5, 6, 7} ("split planes"): words 0..7 hold bits 0..3 of the 64
+  codes, arranged as for bits=4; words 8 .. 2*bits-1 hold bits 4 .. bits-1 of
+  the 64 codes as a (bits-4)-bit code, arranged as for 1, 2 or 3 bits.  The
+  1-bit arrangement follows the rule for {2, 4, 8}: word w holds codes
+  c = 32w + i at bit position 16*(i % 2) + (i // 2).
 
 Scales and zero points use the same tiling: entry (n, g) of the [N, G]
 table is stored at ``((n // 64) * G + g) * 64 + (n % 64)``; padding rows hold 0.
@@ -33,10 +38,39 @@ TILE_ROWS = 64
 KBLOCK = 64
 
 
+PACKED_BITS = (2, 3, 4, 5, 6, 7, 8)
+
+
 def words_per_block(bits: int) -> int:
-    if bits not in (2, 3, 4, 8):
+    if bits not in PACKED_BITS:
         raise ValueError(f"unsupported bits {bits}")
     return 2 * bits
+
+
+def _plain_bits(bits: int, c: int, word0: int, code_bit0: int):
+    """Entries of code c (0..63) in the arrangement for 1, 2, 3, 4 or 8 bits,
+    its words counted from word0, its bits counted from code_bit0."""
+    entries = []
+    if bits in (1, 2, 4, 8):
+        per_word = 32 // bits
+        w, i = divmod(c, per_word)
+        pos = 16 * (i % 2) + bits * (i // 2)
+        for b in range(bits):
+            entries.append((code_bit0 + b, word0 + w, pos + b))
+    else:  # bits == 3
+        run, cr = divmod(c, 32)
+        u, i = divmod(cr, 16)
+        low_word = word0 + 3 * run + u
+        pos = 16 * (i % 2) + 2 * (i // 2)
+        entries.append((code_bit0, low_word, pos))
+        entries.append((code_bit0 + 1, low_word, pos + 1))
+        p, e = divmod(i, 2)
+        hb = (2 * p + 2) if p < 4 else (2 * (p - 4) + 3)
+        hb += 16 * e
+        if u == 1:
+            hb = (hb + 8) % 32
+        entries.append((code_bit0 + 2, word0 + 3 * run + 2, hb))
+    return entries
 
 
 def code_bit_map(bits: int):
@@ -44,29 +78,13 @@ def code_bit_map(bits: int):
     ``(code_bit, word, bit_position)``: bit ``code_bit`` of code c is stored at
     ``bit_position`` of block word ``word``.  Direct transcription of the
     definition in the module docstring."""
+    words_per_block(bits)
     table = []
     for c in range(KBLOCK):
-        entries = []
-        if bits in (2, 4, 8):
-            per_word = 32 // bits
-            w, i = divmod(c, per_word)
-            pos = 16 * (i % 2) + bits * (i // 2)
-            for b in range(bits):
-                entries.append((b, w, pos + b))
-        else:  # bits == 3
-            run, cr = divmod(c, 32)
-            u, i = divmod(cr, 16)
-            low_word = 3 * run + u
-            pos = 16 * (i % 2) + 2 * (i // 2)
-            entries.append((0, low_word, pos))
-            entries.append((1, low_word, pos + 1))
-            p, e = divmod(i, 2)
-            hb = (2 * p + 2) if p < 4 else (2 * (p - 4) + 3)
-            hb += 16 * e
-            if u == 1:
-                hb = (hb + 8) % 32
-            entries.append((2, 3 * run + 2, hb))
-        table.append(entries)
+        if bits <= 4 or bits == 8:
+            table.append(_plain_bits(bits, c, 0, 0))
+        else:  # split planes: low 4 bits, then the high bits - 4
+            table.append(_plain_bits(4, c, 0, 0) + _plain_bits(bits - 4, c, 8, 4))
     return table
 
 

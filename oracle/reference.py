@@ -28,10 +28,10 @@ from __future__ import annotations
 import numpy as np
 
 F32 = np.float32
-# Bit widths with a packed-code layout; the quantizer arithmetic itself holds
-# at every width of the lever (Bitcrush README, "The machine": the lever runs
-# from 16 bits down to 2), used with the fp16 masters at 5, 6 and 7 bits.
-SUPPORTED_BITS = (2, 3, 4, 8)
+# Every width of the lever (Bitcrush README, "The machine": the lever runs
+# from 16 bits down to 2) has the same quantizer arithmetic and a packed-code
+# layout (layout.py).
+SUPPORTED_BITS = (2, 3, 4, 5, 6, 7, 8)
 LEVER_BITS = (2, 3, 4, 5, 6, 7, 8)
 
 

@@ -44,7 +44,7 @@ def test_status_strings(lib):
     assert lib.qlin_abi_version() == 1
 
 
-@pytest.mark.parametrize("bits", [2, 3, 4, 8])
+@pytest.mark.parametrize("bits", [2, 3, 4, 5, 6, 7, 8])
 @pytest.mark.parametrize("n,k", [(1, 64), (63, 128), (64, 64), (65, 896), (896, 896), (151936, 896)])
 def test_size_queries_match_layout(lib, bits, n, k):
     assert lib.qlin_packed_bytes(n, k, bits) == 4 * oracle.packed_words(n, k, bits)
@@ -56,7 +56,8 @@ def test_size_queries_match_layout(lib, bits, n, k):
 def test_size_queries_reject(lib):
     assert lib.qlin_packed_bytes(0, 64, 4) == 0
     assert lib.qlin_packed_bytes(8, 100, 4) == 0
-    assert lib.qlin_packed_bytes(8, 64, 5) == 0
+    assert lib.qlin_packed_bytes(8, 64, 1) == 0
+    assert lib.qlin_packed_bytes(8, 64, 9) == 0
     assert lib.qlin_packed_bytes(8, 64, 16) == 0
     assert lib.qlin_meta_entries(8, 128, 32) == 0
 
@@ -75,7 +76,7 @@ def test_quantize_validation(lib):
     assert quant(lib, k=0) == SHAPE
     assert quant(lib, ld=64) == SHAPE
     assert quant(lib, ld=132) == ALIGN
-    assert quant(lib, bits=5) == BITS                       # no packed layout at 5 bits
+    assert quant(lib, bits=1) == BITS
     assert quant(lib, bits=9) == BITS
     assert quant(lib, bits=16) == BITS
     assert quant(lib, group=32) == GROUP
@@ -114,7 +115,7 @@ def test_gemv_validation(lib):
     assert gemv(lib, weight(ld=128)) == SHAPE           # packed weights take no pitch
     assert gemv(lib, weight(bits=16)) == BITS           # 16 only with fp16 masters
     assert gemv(lib, weight(bits=1)) == BITS
-    assert gemv(lib, weight(bits=6)) == BITS            # packed: 2, 3, 4, 8 only
+    assert gemv(lib, weight(bits=9)) == BITS            # packed: 2 .. 8
     assert gemv(lib, weight(format=1, ld=128, bits=9)) == BITS
     assert gemv(lib, weight(group=128 + 64, k=128)) == GROUP
     assert gemv(lib, weight(format=3)) == FORMAT
@@ -240,7 +241,7 @@ def test_quantize_batch_validation(lib):
     assert lib.qlin_quantize_batch(None, 1, 4, 64, None) == NULL
     assert qbatch(lib, [qjob(0)], count=-1) == SHAPE
     assert qbatch(lib, [qjob(0)], group=128) == GROUP         # 64 or 0 (per row) only
-    assert qbatch(lib, [qjob(0)], bits=5) == BITS
+    assert qbatch(lib, [qjob(0)], bits=9) == BITS
     assert qbatch(lib, [qjob(0), qjob(1, k=100)]) == SHAPE
     assert qbatch(lib, [qjob(0), qjob(1, scale=None)]) == NULL
     assert qbatch(lib, [qjob(0), qjob(1, ld_w=132)]) == ALIGN
@@ -296,7 +297,7 @@ def test_workspace_queries(lib):
     small = weight(n=151936, k=896)
     assert lib.qlin_gemv_workspace_bytes(ctypes.byref(small)) == 0
     assert lib.qlin_gemm_workspace_bytes(ctypes.byref(big), 8) > 65536
-    assert lib.qlin_gemm_workspace_bytes(ctypes.byref(weight(bits=7)), 8) == 0
+    assert lib.qlin_gemm_workspace_bytes(ctypes.byref(weight(bits=9)), 8) == 0
     # multi: the launch's tiles add up; swiglu: two partials per row
     pair = weights(big, big)
     assert lib.qlin_gemv_multi_workspace_bytes(pair, 2) >= need

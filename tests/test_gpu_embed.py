@@ -31,7 +31,7 @@ def packed(w16, bits, group):
     return qw, codes, s16, z
 
 
-@pytest.mark.parametrize("bits", [2, 3, 4, 8])
+@pytest.mark.parametrize("bits", [2, 3, 4, 5, 6, 7, 8])
 @pytest.mark.parametrize("group", [64, "K"])
 def test_embed_rows_exact(bits, group):
     n, k = 1000, 896

@@ -58,7 +58,7 @@ MULTI_CASES = [
 ]
 
 
-@pytest.mark.parametrize("bits", [2, 3, 4, 8])
+@pytest.mark.parametrize("bits", [2, 3, 4, 5, 6, 7, 8])
 @pytest.mark.parametrize("group", [64, "K"])
 @pytest.mark.parametrize("ns,k", MULTI_CASES)
 def test_gemv_multi(bits, group, ns, k):
@@ -124,7 +124,7 @@ def check_swiglu(h, h16, x16, wg, wu, label):
 ROW_WIDTHS = ["16,1,64", "8,1,16", "16,1,8", "4,3,8", "8,2,16", "8,3,64"]
 
 
-@pytest.mark.parametrize("bits", [3, 4])
+@pytest.mark.parametrize("bits", [3, 4, 6])
 @pytest.mark.parametrize("cfg", ROW_WIDTHS)
 @pytest.mark.parametrize("ns,k", [((200, 64, 1, 130), 192), ((896, 128, 128), 896)])
 def test_gemv_multi_row_widths(bits, cfg, ns, k, monkeypatch):
@@ -143,7 +143,7 @@ def test_gemv_multi_row_widths(bits, cfg, ns, k, monkeypatch):
             assert np.array_equal(host(y).astype(np.float64), what[:, c]), f"{cfg} one-hot {c}"
 
 
-@pytest.mark.parametrize("bits", [3, 4])
+@pytest.mark.parametrize("bits", [3, 4, 6])
 @pytest.mark.parametrize("cfg", ROW_WIDTHS)
 @pytest.mark.parametrize("n,k", [(130, 192), (200, 1024)])
 def test_gemv_swiglu_row_widths(bits, cfg, n, k, monkeypatch):
@@ -157,7 +157,7 @@ def test_gemv_swiglu_row_widths(bits, cfg, n, k, monkeypatch):
     check_swiglu(host(h), host(h16), x16, wg, wu, f"{cfg} swiglu {n}x{k}")
 
 
-@pytest.mark.parametrize("bits", [2, 3, 4, 8])
+@pytest.mark.parametrize("bits", [2, 3, 4, 5, 6, 7, 8])
 @pytest.mark.parametrize("group", [64, "K"])
 @pytest.mark.parametrize("n,k", SWIGLU_CASES)
 def test_gemv_swiglu(bits, group, n, k):
@@ -207,7 +207,7 @@ GEMM_MULTI_CASES = [
 ]
 
 
-@pytest.mark.parametrize("bits", [2, 3, 4, 8])
+@pytest.mark.parametrize("bits", [2, 3, 4, 5, 6, 7, 8])
 @pytest.mark.parametrize("ns,k,m", GEMM_MULTI_CASES)
 def test_gemm_multi(bits, ns, k, m):
     rng = np.random.default_rng([75, bits, k, m, len(ns)])

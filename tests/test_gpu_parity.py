@@ -60,7 +60,7 @@ SHAPES = [(896, 896), (200, 192), (64, 64), (1, 64), (130, 256)]
 
 
 # ------------------------------------------------------------- quantize --
-@pytest.mark.parametrize("bits", [2, 3, 4, 8])
+@pytest.mark.parametrize("bits", [2, 3, 4, 5, 6, 7, 8])
 @pytest.mark.parametrize("group", [64, "K"])
 @pytest.mark.parametrize("shape", SHAPES + [(2048, 1024)])
 def test_quantize_bit_exact(bits, group, shape):
@@ -83,7 +83,9 @@ def test_quantize_bit_exact(bits, group, shape):
 @pytest.mark.parametrize("bits", [5, 6, 7])
 @pytest.mark.parametrize("group", [64, "K"])
 def test_quantize_scale_zero_lever_widths(bits, group):
-    """5-7 bits (no packed layout): scale and zero bit-exact, also batched."""
+    """5-7 bits, scale and zero only (the fused path's precompute): bit-exact,
+    also batched, on random and edge-case groups; the packed codes of the
+    same call bit-exact too."""
     rng = np.random.default_rng(700 + bits)
     w16 = np.concatenate([synth.master_weights(rng, 130, 448),
                           synth.edge_groups(bits, rng, n_rows=64, k=448)])
@@ -96,11 +98,12 @@ def test_quantize_scale_zero_lever_widths(bits, group):
         assert np.array_equal(host(got.scale).view(np.uint16)[:oracle.tile_meta(s16).size],
                               oracle.tile_meta(s16).view(np.uint16))
         assert np.array_equal(host(got.zero)[:oracle.tile_meta(z).size], oracle.tile_meta(z))
-    with pytest.raises(qlin.QlinError):
-        qlin.quantize(dev(w16), bits, group, codes=True)
+    packed = qlin.quantize(dev(w16), bits, group, codes=True)
+    codes = oracle.quantize(w16, bits, g)[0]
+    assert np.array_equal(host(packed.data).view(np.uint32), oracle.pack_codes(codes, bits))
 
 
-@pytest.mark.parametrize("bits", [2, 3, 4, 8])
+@pytest.mark.parametrize("bits", [2, 3, 4, 5, 6, 7, 8])
 @pytest.mark.parametrize("group", [64, "K"])
 def test_quantize_edge_groups(bits, group):
     rng = np.random.default_rng(77 + bits)
@@ -130,7 +133,7 @@ def test_quantize_worked_example_and_pitch():
 
 
 # ------------------------------------------------------------------ GEMV --
-@pytest.mark.parametrize("bits", [2, 3, 4, 8])
+@pytest.mark.parametrize("bits", [2, 3, 4, 5, 6, 7, 8])
 @pytest.mark.parametrize("group", [64, "K"])
 @pytest.mark.parametrize("shape", SHAPES + [(1024, 4096), (128, 896)])
 def test_gemv_packed(bits, group, shape):
@@ -156,7 +159,7 @@ def test_gemv_packed(bits, group, shape):
 ROW_WIDTHS = ["16,1,64", "8,1,16", "16,1,8", "4,3,8", "8,2,16"]
 
 
-@pytest.mark.parametrize("bits", [2, 3, 4, 8])
+@pytest.mark.parametrize("bits", [2, 3, 4, 5, 6, 7, 8])
 @pytest.mark.parametrize("group", [64, "K"])
 @pytest.mark.parametrize("shape", [(200, 192), (130, 4096), (1, 64), (896, 896)])
 @pytest.mark.parametrize("cfg", ROW_WIDTHS)
@@ -283,7 +286,7 @@ def test_gemv_fused_row_widths(bits, shape, cfg, monkeypatch):
         assert np.array_equal(ye.astype(np.float64), what[:, kk]), f"{cfg} one-hot k={kk}"
 
 
-@pytest.mark.parametrize("bits", [2, 3, 4, 8])
+@pytest.mark.parametrize("bits", [2, 3, 4, 5, 6, 7, 8])
 @pytest.mark.parametrize("cfg", ["8,1,64", "8,1,8"])
 def test_gemv_fused_edge_groups_widths(bits, cfg, monkeypatch):
     """Edge-case groups (ties, clamps, constant, one-signed) through both
@@ -325,7 +328,7 @@ def test_gemv_fused_scale_sweep_all_columns(cfg, monkeypatch):
 
 
 # ------------------------------------------------------------------ GEMM --
-@pytest.mark.parametrize("bits", [2, 3, 4, 8])
+@pytest.mark.parametrize("bits", [2, 3, 4, 5, 6, 7, 8])
 @pytest.mark.parametrize("m", [1, 5, 8, 16, 17, 64, 100, 128, 256])
 def test_gemm(bits, m):
     n, k = (320, 896) if m != 100 else (200, 192)
@@ -339,7 +342,7 @@ def test_gemm(bits, m):
     check_tol(Y, x16, what, f"gemm m={m}")
 
 
-@pytest.mark.parametrize("bits", [2, 3, 4, 8])
+@pytest.mark.parametrize("bits", [2, 3, 4, 5, 6, 7, 8])
 @pytest.mark.parametrize("m", [1, 5, 16])
 def test_gemm_skinny_forced(bits, m, monkeypatch):
     """The skinny (M <= 16) kernel, forced: within tolerance and one-hot exact."""
@@ -359,7 +362,7 @@ def test_gemm_skinny_forced(bits, m, monkeypatch):
     assert np.array_equal(Y.astype(np.float64), fp16_rne(what[:, cols].T))
 
 
-@pytest.mark.parametrize("bits", [2, 3, 4, 8])
+@pytest.mark.parametrize("bits", [2, 3, 4, 5, 6, 7, 8])
 @pytest.mark.parametrize("m", [16, 128])
 def test_gemm_one_hot_fp16_exact(bits, m):
     """X rows one-hot: Y[i, :] is column k_i of the dequantized weights rounded
@@ -384,7 +387,7 @@ def test_gemm_one_hot_fp16_exact(bits, m):
 KSPLIT = ["0,1", "0,2", "0,5", "1,1", "1,3"]
 
 
-@pytest.mark.parametrize("bits", [2, 3, 4, 8])
+@pytest.mark.parametrize("bits", [2, 3, 4, 5, 6, 7, 8])
 @pytest.mark.parametrize("cfg", KSPLIT)
 @pytest.mark.parametrize("m,n,k,group", [(1, 200, 192, 64), (5, 130, 1600, 64), (16, 64, 896, "K"),
                                          (17, 200, 192, 64), (100, 130, 1600, 64),
@@ -409,7 +412,7 @@ def test_gemm_ksplit(bits, cfg, m, n, k, group, monkeypatch):
     assert np.array_equal(Y.astype(np.float64), fp16_rne(what[:, cols].T))
 
 
-@pytest.mark.parametrize("bits", [3, 4])
+@pytest.mark.parametrize("bits", [3, 4, 6])
 @pytest.mark.parametrize("cfg", KSPLIT)
 def test_gemm_ksplit_sets_and_workspace(bits, cfg, monkeypatch):
     """A ragged set of three matrices in one K-split launch, an explicit
@@ -438,7 +441,7 @@ def test_gemm_ksplit_sets_and_workspace(bits, cfg, monkeypatch):
         assert np.array_equal(a, b)
 
 
-@pytest.mark.parametrize("bits", [2, 3, 4, 8])
+@pytest.mark.parametrize("bits", [2, 3, 4, 5, 6, 7, 8])
 @pytest.mark.parametrize("m,n,k", [(2048, 8192, 192), (1100, 12288, 128), (2048, 4096, 256),
                                    (1000, 4160, 320), (300, 256, 960)])
 def test_gemm_tile_heights(bits, m, n, k):
@@ -455,7 +458,7 @@ def test_gemm_tile_heights(bits, m, n, k):
     check_tol(Y, x16, what, f"gemm {m}x{n}x{k}")
 
 
-@pytest.mark.parametrize("bits", [2, 3, 4, 8])
+@pytest.mark.parametrize("bits", [2, 3, 4, 5, 6, 7, 8])
 @pytest.mark.parametrize("m", [512, 1024])
 def test_gemm_lds_one_hot_fp16_exact(bits, m):
     """The 64- and 128-row X tiles (n = 16384 fills the chip): X row i = e_(i mod k)
@@ -490,7 +493,7 @@ def test_gemm_group_k_and_strides():
 
 
 # ----------------------------------------------------- split-K, determinism
-@pytest.mark.parametrize("bits", [2, 3, 4, 8])
+@pytest.mark.parametrize("bits", [2, 3, 4, 5, 6, 7, 8])
 def test_split_k_paths(bits):
     n, k = 192, 16384
     rng = np.random.default_rng(60 + bits)
@@ -518,7 +521,7 @@ def test_split_k_paths(bits):
     check_tol(Y2, x16, what, "nosplit gemm")
 
 
-@pytest.mark.parametrize("bits", [3, 4])
+@pytest.mark.parametrize("bits", [3, 4, 6])
 def test_split_k_full_tiles(bits):
     """GEMV with K split across work-groups of whole 64-row tiles (many tiles,
     long K): within tolerance, counters re-armed, partial region scratch."""
@@ -540,7 +543,7 @@ def test_split_k_full_tiles(bits):
     check_tol(host(qlin.gemv(qw, dev(x16), ws=None)), x16, what, "nosplit")
 
 
-@pytest.mark.parametrize("bits", [2, 3, 4, 8])
+@pytest.mark.parametrize("bits", [2, 3, 4, 5, 6, 7, 8])
 @pytest.mark.parametrize("m,n,k", [(128, 896, 4864), (100, 192, 4096), (256, 1024, 2048),
                                    (40, 300, 1600)])
 @pytest.mark.parametrize("cfg", [None, "32,3"])

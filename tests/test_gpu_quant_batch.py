@@ -25,7 +25,7 @@ def dev(a):
 SHAPES = [(200, 192), (64, 64), (1, 128), (130, 896), (896, 896), (128, 4864), (300, 320)]
 
 
-@pytest.mark.parametrize("bits", [2, 3, 4, 8])
+@pytest.mark.parametrize("bits", [2, 3, 4, 5, 6, 7, 8])
 @pytest.mark.parametrize("group", [64, "K"])
 @pytest.mark.parametrize("codes", [True, False])
 def test_quantize_batch_matches_oracle(bits, group, codes):

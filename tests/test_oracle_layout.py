@@ -79,7 +79,7 @@ def test_int3_high_word_positions_are_a_bijection():
         assert sorted(pos) == list(range(32))
 
 
-@pytest.mark.parametrize("bits", [2, 3, 4, 8])
+@pytest.mark.parametrize("bits", [2, 3, 4, 5, 6, 7, 8])
 def test_every_bit_used_once(bits):
     seen = set()
     for entries in oracle.code_bit_map(bits):
@@ -91,7 +91,7 @@ def test_every_bit_used_once(bits):
     assert len(seen) == 64 * bits
 
 
-@pytest.mark.parametrize("bits", [2, 3, 4, 8])
+@pytest.mark.parametrize("bits", [2, 3, 4, 5, 6, 7, 8])
 @pytest.mark.parametrize("n", [1, 63, 64, 65, 200])
 def test_round_trip(bits, n):
     rng = np.random.default_rng(n * 7 + bits)
@@ -123,3 +123,44 @@ def test_meta_tiling():
     assert flat[(0 * g + 1) * 64 + 10] == t[10, 1]
     assert np.array_equal(oracle.untile_meta(flat, n, g), t)
     assert np.all(flat[(1 * g + 0) * 64 + 6:(1 * g + 1) * 64] == 0)
+
+
+def test_split_plane_words_by_hand():
+    """5-7 bits: bits 0..3 in words 0..7 as for 4 bits, the rest in words
+    8.. as a 1-, 2- or 3-bit code."""
+    codes = np.zeros(64, np.uint8)
+    codes[:4] = [0x1F, 0x10, 0x0F, 0x11]
+    w = _block_words(codes, 5)
+    # low nibbles F, 0, F, 1 -> word 0: even codes (F, F) low half, odd (0, 1) high half
+    assert w[0] == (0x10 << 16) | 0xFF
+    assert np.all(w[1:8] == 0)
+    # bit 4 of codes 0, 1, 3 (1-bit arrangement: even codes low half, odd high)
+    assert w[8] == (1 << 0) | (1 << 16) | (1 << 17)
+    assert w[9] == 0
+    codes = np.zeros(64, np.uint8)
+    codes[63] = 0x3F
+    w = _block_words(codes, 6)
+    assert w[7] == 0xF << 28                  # code 63: odd, i = 7 of word 7
+    assert w[11] == 0x3 << 30                 # 2-bit word 3, i = 15: 16 + 2*7
+    codes = np.zeros(64, np.uint8)
+    codes[0] = 0x70                           # high bits 0b111 of code 0, 7 bits
+    w = _block_words(codes, 7)
+    assert np.all(w[:8] == 0)
+    # 3-bit arrangement of run 0, code 0: low two bits at 0, 1 of word 8, bit 2
+    # at position 2 of word 10
+    assert w[8] == 0x3 and w[9] == 0 and w[10] == 1 << 2
+    assert np.all(w[11:] == 0)
+
+
+@pytest.mark.parametrize("bits", [5, 6, 7])
+def test_split_plane_is_two_plain_layouts(bits):
+    """The 5-7 bit block equals the 4-bit packing of the low nibbles followed
+    by the (bits-4)-bit packing of the high bits (for 2 and 3 high bits)."""
+    rng = np.random.default_rng(bits)
+    codes = rng.integers(0, 1 << bits, size=(130, 256)).astype(np.uint8)
+    words = oracle.pack_codes(codes, bits).reshape(-1, 2 * bits)
+    lo = oracle.pack_codes(codes & 15, 4).reshape(-1, 8)
+    assert np.array_equal(words[:, :8], lo)
+    if bits > 5:
+        hi = oracle.pack_codes(codes >> 4, bits - 4).reshape(-1, 2 * (bits - 4))
+        assert np.array_equal(words[:, 8:], hi)
