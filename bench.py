@@ -42,10 +42,12 @@ gate/up 4096->12288, down 12288->4096 (252 matrices, 3.8 GB at int4):
   q8_m128_int4 / _int3             252 GEMMs at M = 128
 qwen3_06b -- the 196 fp16 masters of Qwen3-0.6B (28 layers of q 1024->2048,
 k/v 1024->1024, o 2048->1024, gate/up 1024->3072, down 3072->1024):
-  q06_fused_b{8,4,3,2}_{g64,row}   196 fused GEMVs after a lever move
-  q06_lever_b{8,4,3,2}_{g64,row}   a lever move: scale/zero of the 196 masters,
+  q06_fused_b{8..2}_{g64,row}      196 fused GEMVs after a lever move
+  q06_lever_b{8..2}_{g64,row}      a lever move: scale/zero of the 196 masters,
                                    64 per launch
   q06_fp16_control                 196 plain fp16 GEMVs (bits = 16)
+  q06_packed_b{8..2}               196 packed GEMVs at each width of the lever
+                                   (g64, copies rotated past the caches)
 
 `value` is decode_step's weight-stream rate: algorithmic bytes (packed codes,
 fp16 scales, uint8 zeros, x, y, h) / decode-step time.
@@ -412,7 +414,7 @@ def build_qwen3_06b(torch, qlin, synth, dev, ws, phases):
     masters = [(torch.randn(n, k, generator=g, device=dev) * 0.02).half() for (_, _, n, k) in shapes]
     xs = [torch.randn(k, generator=g, device=dev).half() for (_, _, n, k) in shapes]
     ys = [torch.empty(n, dtype=torch.float32, device=dev) for (_, _, n, k) in shapes]
-    combos = [(b, gr) for b in (8, 4, 3, 2) for gr in ("g64", "row")]
+    combos = [(b, gr) for b in (8, 7, 6, 5, 4, 3, 2) for gr in ("g64", "row")]
     meta = {c: [qlin.quantize(w, c[0], 64 if c[1] == "g64" else "K", codes=False) for w in masters]
             for c in combos}
     fused = {c: [qlin.master_weight(w, c[0], 64 if c[1] == "g64" else "K", m.scale, m.zero)
@@ -436,11 +438,29 @@ def build_qwen3_06b(torch, qlin, synth, dev, ws, phases):
                 lambda c=c: qlin.quantize_batch(masters, c[0], 64 if c[1] == "g64" else "K",
                                                 codes=False, outs=meta[c])]])[0]
 
-    hold = (masters, xs, ys, meta, fused, control)
+    # the packed lever: codes at every width, copies rotated so that one pass
+    # set exceeds the 256 MB Infinity Cache several times over
+    packed = {}
+    for b in (8, 7, 6, 5, 4, 3, 2):
+        if f"q06_packed_b{b}" not in phases:
+            continue
+        per_copy = sum(wbytes(n, k, b, 64) for (_, _, n, k) in shapes)
+        copies = max(2, -(-1_100_000_000 // per_copy))
+        packed[b] = [qlin.quantize_batch(masters, b, 64) for _ in range(copies)]
+        staged[f"q06_packed_b{b}"] = capture_calls(torch, [gemvs(cp) for cp in packed[b]])
+    torch.cuda.synchronize()
+    turn = {"n": 0}
+
+    hold = (masters, xs, ys, meta, fused, control, packed)
 
     def run(name):
         assert hold is not None       # every buffer the graphs address stays alive
-        staged[name].replay()
+        g = staged[name]
+        if isinstance(g, list):
+            turn["n"] += 1
+            g[turn["n"] % len(g)].replay()
+        else:
+            g.replay()
 
     master_bytes = sum(2 * n * k for (_, _, n, k) in shapes)
     act = sum(2 * k + 4 * n for (_, _, n, k) in shapes)
@@ -454,6 +474,10 @@ def build_qwen3_06b(torch, qlin, synth, dev, ws, phases):
                          f"k_quantize_{'g64' if gr == 'g64' else 'row'}<{b}> (no codes)"))
     out.append(Phase("q06_fp16_control", run, "GB/s", master_bytes + act, 196, HBM_PEAK_GBS,
                      "hbm", "k_gemv_fused_narrow<16>"))
+    for b in (8, 7, 6, 5, 4, 3, 2):
+        out.append(Phase(f"q06_packed_b{b}", run, "GB/s",
+                         sum(wbytes(n, k, b, 64) for (_, _, n, k) in shapes) + act, 196,
+                         HBM_PEAK_GBS, "hbm", f"k_gemv_narrow<{b}> + k_gemv_packed<{b}>"))
     return [p for p in out if p.name in phases]
 
 
@@ -493,8 +517,9 @@ def main():
             f"q8_m{m}_int{b}" for b in (4, 3) for m in (8, 128)]
         phases += build_qwen3_8b(torch, qlin, synth, dev, ws, chosen(names))
     if "qwen3_06b" in sections:
-        names = [f"q06_{k}_b{b}_{g}" for k in ("fused", "lever") for b in (8, 4, 3, 2)
-                 for g in ("g64", "row")] + ["q06_fp16_control"]
+        names = ([f"q06_{k}_b{b}_{g}" for k in ("fused", "lever") for b in (8, 7, 6, 5, 4, 3, 2)
+                  for g in ("g64", "row")] + ["q06_fp16_control"] +
+                 [f"q06_packed_b{b}" for b in (8, 7, 6, 5, 4, 3, 2)])
         phases += build_qwen3_06b(torch, qlin, synth, dev, ws, chosen(names))
     torch.cuda.synchronize()
 
