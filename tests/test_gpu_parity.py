@@ -184,6 +184,35 @@ def test_gemv_row_widths(bits, group, shape, cfg, monkeypatch):
         assert np.array_equal(ye.astype(np.float64), what[:, kk]), f"{cfg} one-hot k={kk}"
 
 
+@pytest.mark.parametrize("bits", [2, 3, 4, 5, 6, 7, 8])
+@pytest.mark.parametrize("group", [64, "K"])
+@pytest.mark.parametrize("shape", [(200, 4864), (70, 8192), (896, 4864)])
+@pytest.mark.parametrize("cfg", [None, "16,1,8", "16,1,16"])
+def test_gemv_narrow_long_k(bits, group, shape, cfg, monkeypatch):
+    """16-wave 8- and 16-row work-groups over 65..128 K-blocks, where each wave
+    takes two rounds of loads (the Qwen2.5-0.5B down projection, k = 4864,
+    takes this form by default): within tolerance, and one-hot x in the first
+    and last blocks gives the dequantized column exactly."""
+    if cfg is None:
+        monkeypatch.delenv("QLIN_TUNE_GEMV", raising=False)
+    else:
+        monkeypatch.setenv("QLIN_TUNE_GEMV", cfg)
+    n, k = shape
+    g = k if group == "K" else 64
+    say(f"gemv narrow long-k cfg={cfg} bits={bits} group={g} shape={shape}")
+    rng = np.random.default_rng([n, k, bits, 11])
+    w16 = synth.master_weights(rng, n, k)
+    x16 = synth.activations(rng, 1, k)[0]
+    qw, codes, s16, z = oracle_packed(w16, bits, g)
+    what = oracle.dequantize(codes, s16, z, g)
+    check_tol(host(qlin.gemv(qw, dev(x16))), x16, what, str(cfg))
+    for kk in (0, 37, k - 64, k - 1):
+        e = np.zeros(k, np.float16)
+        e[kk] = 1
+        ye = host(qlin.gemv(qw, dev(e)))
+        assert np.array_equal(ye.astype(np.float64), what[:, kk]), f"{cfg} one-hot k={kk}"
+
+
 @pytest.mark.parametrize("bits", [2, 3, 4, 5, 6, 7, 8, 16])
 @pytest.mark.parametrize("group", [64, "K"])
 @pytest.mark.parametrize("shape", [(896, 896), (200, 192), (1, 64), (1024, 2048)])
