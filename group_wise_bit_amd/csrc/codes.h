@@ -206,126 +206,131 @@ __device__ __forceinline__ float block_dot(const uint32_t* wd, const f16x2* xb, 
 }
 
 // -------------------------------------------- MFMA operand decode (fp16 x 8)
-// Eight consecutive codes of a block ("chunk") -> the exact fp32 weights
-// s * (q - z) -> fp16 (round to nearest even, v_cvt_pk_f16_f32).  The fp32 value is exact: the
-// product (1024 + S*q) * (s/S) has at most 22 significant bits, the constant
-// s * (1024/S + z) likewise, and their difference s * (q - z) is representable,
-// so the fma rounds nothing.
+// Eight consecutive codes of a block ("chunk") -> fp16 s * (q - z), rounded
+// once to nearest even, in packed fp16 arithmetic.  The magic-number trick
+// turns a pair of codes into fp16 1024 + S*q, S the code's place within its
+// half-word (1, 4, 16, 64; 1, 2, 4, 8 for a 1-bit plane).  One packed fma by
+// the exact power of two 1/S and by -(1024/S + z) gives q - z, an integer of
+// at most 9 bits that fp16 holds exactly, so that fma rounds nothing; one
+// packed multiply by s then rounds the exact product s * (q - z) once.  The
+// result is the exact value rounded to fp16, as if formed in fp32 (where it
+// is exact) and converted.
 struct Deq {
-  float sS[4];   // s / S for S = 1, 4, 16, 64
-  float cS[4];   // -s * (1024/S + z)
+  f16x2 s;        // (s, s)
+  f16x2 inv[4];   // (1/S, 1/S)
+  f16x2 c[4];     // (-(1024/S + z), same)
 };
 
+// S = 1, 4, 16, 64 (SH = 2) or S = 1, 2, 4, 8 (SH = 1, a 1-bit plane)
+template <int SH = 2>
 __device__ __forceinline__ Deq make_deq(float s, int z) {
   Deq d;
+  const f16 sh = (f16)s;                              // s is an fp16 value (or 0)
+  d.s = (f16x2){sh, sh};
 #pragma unroll
   for (int p = 0; p < 4; ++p) {
-    const float inv = 1.0f / (float)(1 << (2 * p));   // exact power of two
-    d.sS[p] = s * inv;
-    d.cS[p] = -s * (float)((1024 >> (2 * p)) + z);
+    const f16 inv = (f16)(1.0f / (float)(1 << (SH * p)));
+    const f16 c = (f16)(-(float)((1024 >> (SH * p)) + z));
+    d.inv[p] = (f16x2){inv, inv};
+    d.c[p] = (f16x2){c, c};
   }
   return d;
 }
 
-__device__ __forceinline__ void deq_pair(uint32_t magic_pair, float sS, float cS, float& lo, float& hi) {
-  const f16x2 h = as_h2(magic_pair);
-  lo = __builtin_fmaf((float)h.x, sS, cS);
-  hi = __builtin_fmaf((float)h.y, sS, cS);
+// q - z of a pair of codes, exact
+__device__ __forceinline__ f16x2 qz_pair(uint32_t magic_pair, const Deq& d, int p) {
+  return __builtin_elementwise_fma(as_h2(magic_pair), d.inv[p], d.c[p]);
 }
 
-__device__ __forceinline__ f16x8 to_f16x8(const float* f) {
+__device__ __forceinline__ f16x8 scaled8(const f16x2* qz, f16x2 s) {
   f16x8 r;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) r[i] = (f16)f[i];
+  for (int p = 0; p < 4; ++p) {
+    const f16x2 w = qz[p] * s;
+    r[2 * p] = w.x;
+    r[2 * p + 1] = w.y;
+  }
   return r;
 }
 
-// Exact fp32 weights of 8 codes (before the rounding to fp16).
+// q - z of 8 codes, pairs in K order.
 // int4: one word = 8 codes.  S=1 for (v & 0x000F000F), S=16 for (v & 0x00F000F0).
-__device__ __forceinline__ void deq_chunk4f(uint32_t v, const Deq& d, uint32_t kMagic, float* f) {
+__device__ __forceinline__ void qz_chunk4(uint32_t v, const Deq& d, uint32_t kMagic, f16x2* o) {
   const uint32_t vs = v >> 8;
-  deq_pair((v & 0x000F000Fu) | kMagic, d.sS[0], d.cS[0], f[0], f[1]);
-  deq_pair((v & 0x00F000F0u) | kMagic, d.sS[2], d.cS[2], f[2], f[3]);
-  deq_pair((vs & 0x000F000Fu) | kMagic, d.sS[0], d.cS[0], f[4], f[5]);
-  deq_pair((vs & 0x00F000F0u) | kMagic, d.sS[2], d.cS[2], f[6], f[7]);
+  o[0] = qz_pair((v & 0x000F000Fu) | kMagic, d, 0);
+  o[1] = qz_pair((v & 0x00F000F0u) | kMagic, d, 2);
+  o[2] = qz_pair((vs & 0x000F000Fu) | kMagic, d, 0);
+  o[3] = qz_pair((vs & 0x00F000F0u) | kMagic, d, 2);
 }
 
 // int2: pairs 0..3 of v (the caller passes v >> 8 for the upper pairs).
-__device__ __forceinline__ void deq_chunk2f(uint32_t v, const Deq& d, uint32_t kMagic, float* f) {
+__device__ __forceinline__ void qz_chunk2(uint32_t v, const Deq& d, uint32_t kMagic, f16x2* o) {
 #pragma unroll
   for (int p = 0; p < 4; ++p) {
     const uint32_t m = (3u << (2 * p)) | (3u << (16 + 2 * p));
-    deq_pair((v & m) | kMagic, d.sS[p], d.cS[p], f[2 * p], f[2 * p + 1]);
+    o[p] = qz_pair((v & m) | kMagic, d, p);
   }
 }
 
 // int3: low-bit word L (already shifted for the upper pairs) and high-bit word
 // H (already rotated / shifted to line up with L).
-__device__ __forceinline__ void deq_chunk3f(uint32_t L, uint32_t H, const Deq& d, uint32_t kMagic,
-                                            float* f) {
+__device__ __forceinline__ void qz_chunk3(uint32_t L, uint32_t H, const Deq& d, uint32_t kMagic,
+                                          f16x2* o) {
 #pragma unroll
   for (int p = 0; p < 4; ++p) {
     const uint32_t m2 = (3u << (2 * p)) | (3u << (16 + 2 * p));
     const uint32_t m1 = (1u << (2 * p + 2)) | (1u << (2 * p + 18));
     const uint32_t t = (L & m2) | (H & ~m2);
-    deq_pair((t & (m2 | m1)) | kMagic, d.sS[p], d.cS[p], f[2 * p], f[2 * p + 1]);
+    o[p] = qz_pair((t & (m2 | m1)) | kMagic, d, p);
   }
 }
 
 // 1-bit plane: bits 0..3 of each half of v (the caller shifts v to the chunk),
-// scale classes S = 1, 2, 4, 8 (d from make_deq_pow2).
-__device__ __forceinline__ void deq_chunk1f(uint32_t v, const Deq& d, uint32_t kMagic, float* f) {
+// S = 1, 2, 4, 8 (d from make_deq<1>).
+__device__ __forceinline__ void qz_chunk1(uint32_t v, const Deq& d, uint32_t kMagic, f16x2* o) {
 #pragma unroll
   for (int p = 0; p < 4; ++p) {
     const uint32_t m = (1u << p) | (1u << (16 + p));
-    deq_pair((v & m) | kMagic, d.sS[p], d.cS[p], f[2 * p], f[2 * p + 1]);
+    o[p] = qz_pair((v & m) | kMagic, d, p);
   }
+}
+
+// int8: two words = 8 codes; the byte permute builds 1024 + q directly (S = 1).
+__device__ __forceinline__ void qz_chunk8(uint32_t v, uint32_t u, const Deq& d, f16x2* o) {
+  o[0] = qz_pair(__builtin_amdgcn_perm(0x64646464u, v, 0x04020400u), d, 0);
+  o[1] = qz_pair(__builtin_amdgcn_perm(0x64646464u, v, 0x04030401u), d, 0);
+  o[2] = qz_pair(__builtin_amdgcn_perm(0x64646464u, u, 0x04020400u), d, 0);
+  o[3] = qz_pair(__builtin_amdgcn_perm(0x64646464u, u, 0x04030401u), d, 0);
 }
 
 __device__ __forceinline__ f16x8 deq_chunk4(uint32_t v, const Deq& d, uint32_t kMagic) {
-  float f[8];
-  deq_chunk4f(v, d, kMagic, f);
-  return to_f16x8(f);
+  f16x2 o[4];
+  qz_chunk4(v, d, kMagic, o);
+  return scaled8(o, d.s);
 }
 
 __device__ __forceinline__ f16x8 deq_chunk2(uint32_t v, const Deq& d, uint32_t kMagic) {
-  float f[8];
-  deq_chunk2f(v, d, kMagic, f);
-  return to_f16x8(f);
+  f16x2 o[4];
+  qz_chunk2(v, d, kMagic, o);
+  return scaled8(o, d.s);
 }
 
 __device__ __forceinline__ f16x8 deq_chunk3(uint32_t L, uint32_t H, const Deq& d, uint32_t kMagic) {
-  float f[8];
-  deq_chunk3f(L, H, d, kMagic, f);
-  return to_f16x8(f);
+  f16x2 o[4];
+  qz_chunk3(L, H, d, kMagic, o);
+  return scaled8(o, d.s);
 }
 
-// int8: two words = 8 codes.
 __device__ __forceinline__ f16x8 deq_chunk8(uint32_t v, uint32_t u, const Deq& d) {
-  float f[8];
-  deq_pair(__builtin_amdgcn_perm(0x64646464u, v, 0x04020400u), d.sS[0], d.cS[0], f[0], f[1]);
-  deq_pair(__builtin_amdgcn_perm(0x64646464u, v, 0x04030401u), d.sS[0], d.cS[0], f[2], f[3]);
-  deq_pair(__builtin_amdgcn_perm(0x64646464u, u, 0x04020400u), d.sS[0], d.cS[0], f[4], f[5]);
-  deq_pair(__builtin_amdgcn_perm(0x64646464u, u, 0x04030401u), d.sS[0], d.cS[0], f[6], f[7]);
-  return to_f16x8(f);
+  f16x2 o[4];
+  qz_chunk8(v, u, d, o);
+  return scaled8(o, d.s);
 }
 
-// 5-7 bits (split planes): s*(q - z) = s*(lo - z%16) + 16s*(hi - z/16), each
-// term exact in fp32 and so their sum (|q - z| <= 127, an 18-bit multiple of
-// the scale's last place), rounded to fp16 once.
-__device__ __forceinline__ Deq make_deq_pow2(float s, int z) {
-  Deq d;
-#pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    const float inv = 1.0f / (float)(1 << p);          // exact power of two
-    d.sS[p] = s * inv;
-    d.cS[p] = -s * (float)((1024 >> p) + z);
-  }
-  return d;
-}
-
+// 5-7 bits (split planes): q - z = (lo - z%16) + 16 (hi - z/16), both terms
+// and the sum (|q - z| <= 127) exact in fp16; then one multiply by s.
 struct Deq2 {
-  Deq lo, hi;
+  Deq lo, hi;    // hi.s unused
 };
 
 template <int BITS>
@@ -336,7 +341,7 @@ __device__ __forceinline__ DeqT<BITS> make_deq_b(float s, int z) {
   if constexpr (BITS >= 5 && BITS <= 7) {
     Deq2 d;
     d.lo = make_deq(s, z & 15);
-    d.hi = BITS == 5 ? make_deq_pow2(16.f * s, z >> 4) : make_deq(16.f * s, z >> 4);
+    d.hi = BITS == 5 ? make_deq<1>(s, z >> 4) : make_deq(s, z >> 4);
     return d;
   } else {
     return make_deq(s, z);

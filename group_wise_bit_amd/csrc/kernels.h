@@ -1216,22 +1216,23 @@ template <int BITS>
 __device__ __forceinline__ f16x8 deq_half(const uint32_t* wl, int s, const DeqT<BITS>& d,
                                           uint32_t magic) {
   if constexpr (BITS >= 5 && BITS <= 7) {
-    float f[8], g[8];
-    deq_chunk4f(wl[s], d.lo, magic, f);
+    f16x2 lo[4], hi[4];
+    qz_chunk4(wl[s], d.lo, magic, lo);
     if constexpr (BITS == 5) {
-      deq_chunk1f(wl[4] >> (4 * s), d.hi, magic, g);
+      qz_chunk1(wl[4] >> (4 * s), d.hi, magic, hi);
     } else if constexpr (BITS == 6) {
       const uint32_t v = wl[4 + (s >> 1)];
-      deq_chunk2f((s & 1) ? (v >> 8) : v, d.hi, magic, g);
+      qz_chunk2((s & 1) ? (v >> 8) : v, d.hi, magic, hi);
     } else {
       const int u = s >> 1;
       const uint32_t L = wl[4 + u];
       const uint32_t Hu = u ? __builtin_amdgcn_alignbit(wl[6], wl[6], 8) : wl[6];
-      deq_chunk3f((s & 1) ? (L >> 8) : L, (s & 1) ? (Hu >> 1) : Hu, d.hi, magic, g);
+      qz_chunk3((s & 1) ? (L >> 8) : L, (s & 1) ? (Hu >> 1) : Hu, d.hi, magic, hi);
     }
+    const f16x2 sixteen = {(f16)16.0f, (f16)16.0f};
 #pragma unroll
-    for (int i = 0; i < 8; ++i) f[i] += g[i];
-    return to_f16x8(f);
+    for (int p = 0; p < 4; ++p) lo[p] = __builtin_elementwise_fma(hi[p], sixteen, lo[p]);
+    return scaled8(lo, d.lo.s);
   } else if constexpr (BITS == 4) {
     return deq_chunk4(wl[s], d, magic);
   } else if constexpr (BITS == 2) {

@@ -187,8 +187,8 @@ qlin_status qlin_gemv(const qlin_weight* w, const uint16_t* x, float* y,
 /*
  * GEMM:  Y[m, n] = sum_k X[m, k] * s(q - z),  PACKED weights only.
  * X fp16 [m, ld_x] (ld_x >= k, % 8 == 0), Y fp32 [m, ld_y] (ld_y >= n).
- * X is used as given (fp16) and each dequantized weight s*(q - z), formed
- * exactly in fp32, is rounded to fp16 (nearest even); both feed the fp16
+ * X is used as given (fp16) and each dequantized weight s*(q - z) is its
+ * exact value rounded once to fp16 (nearest even); both feed the fp16
  * matrix cores with fp32 accumulation (Enargeia, "Measured, not asserted":
  * prefill is the dense, tiled-matmul form of the same product).  fp16 rather
  * than bf16 operands: bf16 rounding of X and of the weights alone exceeds
