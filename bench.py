@@ -21,7 +21,8 @@ fp16 masters ~N(0, 0.02), activations ~N(0, 1):
   decode_gemv      the same 169 matrices as 169 separate packed GEMVs
   prefill_step_m128  the 168 layer matrices at M = 128 grouped as the dispatch
                    list groups them: per layer q/k/v in one launch, o, gate/up
-                   in one launch, down (96 launches); fp16 MFMA, fp32 accumulate
+                   in one launch with the SwiGLU combination (fp16 h), down
+                   reading h (96 launches); fp16 MFMA, fp32 accumulate
   prefill_step_m2048 the same at M = 2048
   prefill_m128     the 168 layer GEMMs as separate launches, M = 128
   prefill_m2048    the same at M = 2048
@@ -247,23 +248,25 @@ def build_decode(torch, qlin, synth, dev, ws, phases, state):
         if f"prefill_step_m{m}" not in phases:
             continue
         Yg[m] = {nm: torch.empty(m, shapes[idx[(0, nm)]][2], dtype=torch.float32, device=dev)
-                 for nm in ("q", "k", "v", "o", "gate", "up", "down")}
+                 for nm in ("q", "k", "v", "o", "down")}
+        Yg[m]["h16"] = torch.empty(m, shapes[idx[(0, "gate")]][2], dtype=torch.float16,
+                                   device=dev)
 
         def step_calls(r, m=m):
             Xm = X[m]
             calls = []
             for l in layers:
                 w = {nm: packed[r][idx[(l, nm)]] for nm in ("q", "k", "v", "o", "gate", "up", "down")}
-                k1, k2 = w["q"].k, w["down"].k
+                k1 = w["q"].k
                 calls += [
                     lambda w=w, m=m, k1=k1: qlin.gemm_multi(
                         [w["q"], w["k"], w["v"]], Xm[:, :k1],
                         [Yg[m]["q"], Yg[m]["k"], Yg[m]["v"]], ws=ws),
                     lambda w=w, m=m, k1=k1: qlin.gemm(w["o"], Xm[:, :k1], Yg[m]["o"], ws=ws),
-                    lambda w=w, m=m, k1=k1: qlin.gemm_multi(
-                        [w["gate"], w["up"]], Xm[:, :k1], [Yg[m]["gate"], Yg[m]["up"]], ws=ws),
-                    lambda w=w, m=m, k2=k2: qlin.gemm(w["down"], Xm[:, :k2], Yg[m]["down"],
-                                                      ws=ws),
+                    lambda w=w, m=m, k1=k1: qlin.gemm_swiglu(
+                        w["gate"], w["up"], Xm[:, :k1], None, Yg[m]["h16"], ws=ws,
+                        want_h=False),
+                    lambda w=w, m=m: qlin.gemm(w["down"], Yg[m]["h16"], Yg[m]["down"], ws=ws),
                 ]
             return calls
         staged[f"prefill_step_m{m}"] = per_rotation(step_calls)
@@ -312,10 +315,10 @@ def build_decode(torch, qlin, synth, dev, ws, phases, state):
         Phase("decode_gemv", run, "GB/s", dec_bytes, 169, HBM_PEAK_GBS, "hbm",
               "k_gemv_narrow<4> + k_gemv_packed<4> (LM head)"),
         Phase("prefill_step_m128", run, "TFLOP/s", fl[128], 96, FP16_MFMA_PEAK_TFLOPS, "mfma",
-              "k_gemm_ksplit<4> (q/k/v set, o, gate/up set, down)"),
+              "k_gemm_ksplit<4> (q/k/v set, o, gate/up+SwiGLU pair, down)"),
         Phase("prefill_step_m2048", run, "TFLOP/s", fl[2048], 96, FP16_MFMA_PEAK_TFLOPS,
               "mfma",
-              "k_gemm_lds<4, 128> (gate/up set), k_gemm_ksplit<4> (q/k/v set, down), k_gemm_tiles<4, 32> (o)"),
+              "k_gemm_lds<4, 128> (gate/up+SwiGLU pair), k_gemm_ksplit<4> (q/k/v set, down), k_gemm_tiles<4, 32> (o)"),
         Phase("prefill_m128", run, "TFLOP/s", fl[128], 168, FP16_MFMA_PEAK_TFLOPS, "mfma",
               "k_gemm_ksplit<4>"),
         Phase("prefill_m2048", run, "TFLOP/s", fl[2048], 168, FP16_MFMA_PEAK_TFLOPS, "mfma",

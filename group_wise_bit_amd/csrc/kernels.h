@@ -345,7 +345,11 @@ struct GemvSet {
   int count;
 };
 
-__device__ __forceinline__ float silu(float g) { return g / (1.f + __expf(-g)); }
+// silu(g) = g / (1 + exp(-g)) with the hardware reciprocal (1 ulp); g << 0
+// gives 1/inf = 0 and so -0
+__device__ __forceinline__ float silu(float g) {
+  return g * __builtin_amdgcn_rcpf(1.f + __expf(-g));
+}
 
 // grid = (launch tiles, splits), block = WAVES waves; lane = row of the tile.
 // Plain: the WAVES waves of split s take the K-blocks j0+w, j0+w+WAVES, ... of
@@ -1033,6 +1037,7 @@ struct GemmSet {
   int n[kMaxMats];
   int end[kMaxMats];
   int count;
+  uint16_t* h16;         // gate/up pairs: fp16 h (leading dimension ldy[0]), or null
 };
 
 struct GemmMat {
@@ -1479,13 +1484,18 @@ __global__ __launch_bounds__(256) void k_gemm_tiles(
 // about one memory round trip; the 4 partial 32x64 tiles are then added in
 // LDS in wave order.  Operand layout as in k_gemm_tiles (lane (c, h): X row
 // 32rb + c / W row 32cb + c, K positions 32h + 8s .. +7 for instruction s).
-template <int BITS, int U, int RB>
+// PAIR: the set is (gate, up) with equal n; each wave multiplies its X
+// fragments by the same tile of both, the two tiles are reduced one after
+// the other, and the output is h = silu(gate . x) * (up . x) in fp32 (y[0],
+// if not null) and/or fp16 (set.h16), both with leading dimension ldy[0].
+template <int BITS, int U, int RB, bool PAIR = false>
 __global__ __launch_bounds__(256) void k_gemm_ksplit(
     const GemmSet set, const uint16_t* __restrict__ X, int64_t ldx, int m, int kb, int G,
     int splits, int kbps, float* __restrict__ part, uint32_t* __restrict__ tickets) {
   constexpr int WPB = 2 * BITS;
   constexpr int HW = WPB / 2;                 // words of a half block
   constexpr int NE = RB * 2048;              // elements of a wave's partial tile
+  constexpr int NM = PAIR ? 2 : 1;           // matrices per work-group
   __shared__ float red[4][NE];
   const int tid = threadIdx.x;
   const int lane = lane_id(), wave = wave_id();
@@ -1503,27 +1513,36 @@ __global__ __launch_bounds__(256) void k_gemm_ksplit(
     const int xr = m0 + 32 * rb + c;
     xrow[rb] = X + (int64_t)(xr < m ? xr : m0) * ldx + 32 * h;
   }
-  const uint32_t* wsrc[2];
+  const uint32_t* wsrc[NM][2];
+  const uint16_t* ssrc[NM];
+  const uint8_t* zsrc[NM];
   int64_t msrc[2];
 #pragma unroll
-  for (int cb = 0; cb < 2; ++cb) {
-    const int r = 32 * cb + c;
-    wsrc[cb] = mat.codes + ((int64_t)t * kb * kTile + r) * WPB;
-    msrc[cb] = (int64_t)t * G * kTile + r;
-  }
-  f32x16 acc[RB][2];
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb)
+  for (int mi = 0; mi < NM; ++mi) {
+    const uint32_t* codes = PAIR ? set.codes[mi] : mat.codes;
+    ssrc[mi] = PAIR ? set.scale[mi] : mat.scale;
+    zsrc[mi] = PAIR ? set.zero[mi] : mat.zero;
 #pragma unroll
     for (int cb = 0; cb < 2; ++cb)
+      wsrc[mi][cb] = codes + ((int64_t)t * kb * kTile + 32 * cb + c) * WPB;
+  }
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[rb][cb][r] = 0.f;
+  for (int cb = 0; cb < 2; ++cb) msrc[cb] = (int64_t)t * G * kTile + 32 * cb + c;
+  f32x16 acc[NM][RB][2];
+#pragma unroll
+  for (int mi = 0; mi < NM; ++mi)
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[mi][rb][cb][r] = 0.f;
 
   for (int jb = j0 + wave; jb < j1; jb += 4 * U) {
     f16x8 xa[U][RB][4];
-    uint32_t wl[U][2][HW];
-    uint16_t sr[U][2];
-    int zc[U][2];
+    uint32_t wl[U][NM][2][HW];
+    uint16_t sr[U][NM][2];
+    int zc[U][NM][2];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int j = jb + 4 * u;
@@ -1536,53 +1555,64 @@ __global__ __launch_bounds__(256) void k_gemm_ksplit(
       }
       const int64_t g = (G == 1) ? 0 : jj;
 #pragma unroll
-      for (int cb = 0; cb < 2; ++cb) {
-        load_half<BITS>(wsrc[cb] + (int64_t)jj * kTile * WPB, h, wl[u][cb]);
-        sr[u][cb] = mat.scale[msrc[cb] + g * kTile];
-        zc[u][cb] = mat.zero[msrc[cb] + g * kTile];
-      }
+      for (int mi = 0; mi < NM; ++mi)
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb) {
+          load_half<BITS>(wsrc[mi][cb] + (int64_t)jj * kTile * WPB, h, wl[u][mi][cb]);
+          sr[u][mi][cb] = ssrc[mi][msrc[cb] + g * kTile];
+          zc[u][mi][cb] = zsrc[mi][msrc[cb] + g * kTile];
+        }
     }
-    if constexpr (U > 1) loads_issued();
+    if constexpr (U > 1 || PAIR) loads_issued();
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const bool valid = jb + 4 * u < j1;
 #pragma unroll
-      for (int cb = 0; cb < 2; ++cb) {
-        const DeqT<BITS> d = make_deq_b<BITS>(masked_scale(sr[u][cb], valid), zc[u][cb]);
+      for (int mi = 0; mi < NM; ++mi)
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          const f16x8 bf = deq_half<BITS>(wl[u][cb], s, d, magic);
+        for (int cb = 0; cb < 2; ++cb) {
+          const DeqT<BITS> d = make_deq_b<BITS>(masked_scale(sr[u][mi][cb], valid), zc[u][mi][cb]);
 #pragma unroll
-          for (int rb = 0; rb < RB; ++rb)
-            acc[rb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(xa[u][rb][s], bf, acc[rb][cb],
-                                                                 0, 0, 0);
+          for (int s = 0; s < 4; ++s) {
+            const f16x8 bf = deq_half<BITS>(wl[u][mi][cb], s, d, magic);
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb)
+              acc[mi][rb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(xa[u][rb][s], bf,
+                                                                       acc[mi][rb][cb], 0, 0, 0);
+          }
         }
-      }
     }
   }
   // element e = 2048 rb + 1024 cb + 64 r + lane of a wave's accumulators
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-    for (int cb = 0; cb < 2; ++cb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) red[wave][2048 * rb + 1024 * cb + 64 * r + lane] = acc[rb][cb][r];
-  __syncthreads();
   constexpr int PT = NE / 256;               // elements per thread
-  float v[PT];
+  float v[NM][PT];
 #pragma unroll
-  for (int i = 0; i < PT; ++i) {
-    const int e = tid + 256 * i;
-    v[i] = ((red[0][e] + red[1][e]) + red[2][e]) + red[3][e];
+  for (int mi = 0; mi < NM; ++mi) {
+    if (mi > 0) __syncthreads();             // the previous matrix's sums are read
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          red[wave][2048 * rb + 1024 * cb + 64 * r + lane] = acc[mi][rb][cb][r];
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < PT; ++i) {
+      const int e = tid + 256 * i;
+      v[mi][i] = ((red[0][e] + red[1][e]) + red[2][e]) + red[3][e];
+    }
   }
   if (splits > 1) {
-    // partials [split][work-group][element]; the last work-group of this
-    // output tile to arrive adds the splits in order 0, 1, ...
+    // partials [split][work-group][matrix][element]; the last work-group of
+    // this output tile to arrive adds the splits in order 0, 1, ...
     const int64_t wg = (int64_t)blockIdx.y * gridDim.x + blockIdx.x;
     const int64_t groups = (int64_t)gridDim.x * gridDim.y;
-    float* pw = part + (blockIdx.z * groups + wg) * NE;
+    float* pw = part + (blockIdx.z * groups + wg) * NM * NE;
 #pragma unroll
-    for (int i = 0; i < PT; ++i) put_partial(pw + tid + 256 * i, v[i]);
+    for (int mi = 0; mi < NM; ++mi)
+#pragma unroll
+      for (int i = 0; i < PT; ++i) put_partial(pw + mi * NE + tid + 256 * i, v[mi][i]);
     partials_written();
     __syncthreads();
     __shared__ uint32_t s_last;
@@ -1595,8 +1625,11 @@ __global__ __launch_bounds__(256) void k_gemm_ksplit(
     __syncthreads();
     if (!s_last) return;
 #pragma unroll
-    for (int i = 0; i < PT; ++i)
-      v[i] = sum_splits(part + wg * NE + tid + 256 * i, groups * NE, splits);
+    for (int mi = 0; mi < NM; ++mi)
+#pragma unroll
+      for (int i = 0; i < PT; ++i)
+        v[mi][i] = sum_splits(part + (wg * NM + mi) * NE + tid + 256 * i, groups * NM * NE,
+                              splits);
   }
   const int n = mat.n;
 #pragma unroll
@@ -1605,7 +1638,15 @@ __global__ __launch_bounds__(256) void k_gemm_ksplit(
     const int rb = e >> 11, cb = (e >> 10) & 1, r = (e >> 6) & 15, l = e & 63;
     const int row = m0 + 32 * rb + 8 * (r >> 2) + 4 * (l >> 5) + (r & 3);
     const int col = t * kTile + 32 * cb + (l & 31);
-    if (row < m && col < n) mat.y[(int64_t)row * mat.ldy + col] = v[i];
+    if (row >= m || col >= n) continue;
+    const int64_t o = (int64_t)row * mat.ldy + col;
+    if constexpr (PAIR) {
+      const float hv = silu(v[0][i]) * v[NM - 1][i];
+      if (mat.y != nullptr) mat.y[o] = hv;
+      if (set.h16 != nullptr) set.h16[o] = __builtin_bit_cast(uint16_t, (f16)hv);
+    } else {
+      mat.y[o] = v[0][i];
+    }
   }
 }
 
@@ -1730,7 +1771,15 @@ template <> struct WDma<5> { static constexpr int SZ = 4, N = 10; };
 template <> struct WDma<6> { static constexpr int SZ = 16, N = 3; };
 template <> struct WDma<7> { static constexpr int SZ = 4, N = 14; };
 
-template <int BITS, int MB, int S>
+// PAIR: the set is (gate, up) with equal n, and a work-group covers two
+// 64-row tiles of each: waves 0 and 1 multiply gate tiles 2x and 2x + 1,
+// waves 2 and 3 the same tiles of up.  After the K loop each gate wave and
+// the up wave of its tile swap halves of their accumulators through the
+// (then idle) LDS stages, one 32-row block at a time: the gate wave finishes
+// columns 0-31 of the tile, the up wave columns 32-63, each writing
+// h = silu(g) * u in fp32 (y[0], if not null) and/or fp16 (set.h16),
+// leading dimension ldy[0].
+template <int BITS, int MB, int S, bool PAIR = false>
 __global__ __launch_bounds__(256, 2) void k_gemm_lds(
     const GemmSet set, const uint16_t* __restrict__ X, int64_t ldx, int m, int kb, int G,
     int splits, int kbps, float* __restrict__ part, uint32_t* __restrict__ tickets) {
@@ -1744,11 +1793,12 @@ __global__ __launch_bounds__(256, 2) void k_gemm_lds(
   const int lane = lane_id(), wave = wave_id();
   const int c = lane & 31, h = lane >> 5;
   const GemmMat mat = gemm_mat(set, blockIdx.x);
-  const uint32_t* __restrict__ codes = mat.codes;
-  const uint16_t* __restrict__ scale = mat.scale;
-  const uint8_t* __restrict__ zero = mat.zero;
+  const int mi = PAIR ? (wave >> 1) : 0;
+  const uint32_t* __restrict__ codes = PAIR ? set.codes[mi] : mat.codes;
+  const uint16_t* __restrict__ scale = PAIR ? set.scale[mi] : mat.scale;
+  const uint8_t* __restrict__ zero = PAIR ? set.zero[mi] : mat.zero;
   const int n = mat.n;
-  const int t = mat.col * 4 + wave;
+  const int t = PAIR ? mat.col * 2 + (wave & 1) : mat.col * 4 + wave;
   const bool tvalid = t < mat.tiles;
   const int tt = tvalid ? t : 0;
   const int m0 = blockIdx.y * MB;
@@ -1934,11 +1984,44 @@ __global__ __launch_bounds__(256, 2) void k_gemm_lds(
     }
   }
 
-  if (!tvalid) return;
   // rows m0 + 32rb + 8(r/4) + 4h + r%4 of columns t*64 + 32cb + c
   const int64_t ldy = mat.ldy;
-  float* ybase = mat.y + (int64_t)(m0 + 4 * h) * ldy + t * kTile + c;
   const int mrem = m - m0 - 4 * h;
+  if constexpr (PAIR) {
+    // every wave has passed its last read of the stages (and every load into
+    // them has landed) once all are at this barrier
+    __syncthreads();
+    const bool up_wave = wave >= 2;
+    const int keep = up_wave ? 1 : 0;          // the column half this wave finishes
+    // the pair's exchange area: [column half][r][lane], 8 KB
+    float* xch = reinterpret_cast<float*>((wave & 1) ? (void*)&gemm_stage<BITS, MB, 1>()
+                                                     : (void*)&gemm_stage<BITS, MB, 0>());
+    const int col = t * kTile + 32 * keep + c;
+    const int64_t obase = (int64_t)(m0 + 4 * h) * ldy + col;
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) xch[((1 - keep) * 16 + r) * 64 + lane] = acc[rb][1 - keep][r];
+      __syncthreads();
+      if (tvalid && col < n) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int dr = 32 * rb + 8 * (r >> 2) + (r & 3);
+          if (dr >= mrem) continue;
+          const float other = xch[(keep * 16 + r) * 64 + lane];
+          const float mine = acc[rb][keep][r];
+          const float hv = up_wave ? silu(other) * mine : silu(mine) * other;
+          const int64_t o = obase + (int64_t)dr * ldy;
+          if (mat.y != nullptr) mat.y[o] = hv;
+          if (set.h16 != nullptr) set.h16[o] = __builtin_bit_cast(uint16_t, (f16)hv);
+        }
+      }
+      __syncthreads();
+    }
+    return;
+  }
+  if (!tvalid) return;
+  float* ybase = mat.y + (int64_t)(m0 + 4 * h) * ldy + t * kTile + c;
 #pragma unroll
   for (int cb = 0; cb < 2; ++cb) {
     if (t * kTile + 32 * cb + c >= n) continue;

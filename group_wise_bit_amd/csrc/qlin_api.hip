@@ -627,6 +627,89 @@ bool skinny_by_ksplit(int64_t tiles, int kb, int bits) {
 }
 
 
+// Gate/up GEMM with the SwiGLU combination (one launch, h written once).
+// mb as in TilesCfg: 0 / 1 the K-split kernel with 32 / 64 X rows and both
+// matrices' tile t in each work-group (gx = tiles); 64 / 128 the LDS-DMA
+// pipeline over two tiles of each matrix (gx = tiles / 2, rounded up).  The
+// choice follows tiles_config for the equivalent two-matrix set.
+TilesCfg swiglu_config(int64_t tiles, int kb, int m, int64_t ws_bytes) {
+  TilesCfg c;
+  int want = 1;
+  const int64_t cols2 = (tiles + 1) / 2;
+  if (m <= 256) {
+    c.mb = (2 * tiles < 256 || m <= 16) ? 0 : 1;
+    if (c.mb == 0) {
+      // counted as for the two-matrix set: a pair work-group does the work
+      // of two of its work-groups
+      const int64_t groups = 2 * tiles * ((m + 31) / 32);
+      if (groups < 256) {
+        want = (int)((512 + groups - 1) / groups);
+        if (want > 8) want = 8;
+        if (want > kb / 8) want = kb / 8;
+      }
+    }
+  } else {
+    c.mb = 128;
+    if (cols2 * ((m + 127) / 128) < 288) {
+      c.mb = 64;
+      if (cols2 * ((m + 63) / 64) < 256) c.mb = 1;
+    }
+  }
+  // QLIN_TUNE_GEMM="mb,splits" overrides the choice (mb 32 runs as 64)
+  if (const char* e = getenv("QLIN_TUNE_GEMM")) {
+    int mb = 0, sp = 0;
+    if (sscanf(e, "%d,%d", &mb, &sp) == 2 &&
+        (mb == 0 || mb == 1 || mb == 32 || mb == 64 || mb == 128) && sp >= 1) {
+      c.mb = mb == 32 ? 64 : mb;
+      want = sp < kb ? sp : kb;
+    }
+  }
+  if (want < 1) want = 1;
+  const bool ks = c.mb <= 1;
+  c.gx = (int)(ks ? tiles : cols2);
+  const int rows = ks ? 32 * (c.mb + 1) : c.mb;
+  const int64_t wg_outputs = (int64_t)rows * (ks ? 2 * kTile : 256);
+  c.gy = (m + rows - 1) / rows;
+  if ((int64_t)c.gx * c.gy > kMaxSplitTiles) want = 1;
+  while (want > 1 && kCounterBytes + (int64_t)want * c.gy * c.gx * wg_outputs * 4 > ws_bytes)
+    --want;
+  c.kbps = (kb + want - 1) / want;
+  c.splits = (kb + c.kbps - 1) / c.kbps;
+  return c;
+}
+
+int64_t swiglu_ws_bytes(int64_t tiles, int kb, int m) {
+  const TilesCfg c = swiglu_config(tiles, kb, m, INT64_MAX);
+  if (c.splits <= 1) return 0;
+  const bool ks = c.mb <= 1;
+  const int64_t wg_outputs = ks ? 32 * (c.mb + 1) * 2 * kTile : (int64_t)c.mb * 256;
+  return kCounterBytes + (int64_t)c.splits * c.gy * c.gx * wg_outputs * 4;
+}
+
+template <int B>
+void launch_gemm_swiglu(const GemmSet& set, const uint16_t* X, int64_t ldx, int m, int kb, int G,
+                        TilesCfg c, float* part, uint32_t* tick, hipStream_t st) {
+  const dim3 grid(c.gx, c.gy, c.splits);
+  if (c.mb == 128)
+    hipLaunchKernelGGL((k_gemm_lds<B, 128, 3, true>), grid, dim3(256), 0, st, set, X, ldx, m, kb,
+                       G, c.splits, c.kbps, part, tick);
+  else if (c.mb == 64)
+    hipLaunchKernelGGL((k_gemm_lds<B, 64, 4, true>), grid, dim3(256), 0, st, set, X, ldx, m, kb,
+                       G, c.splits, c.kbps, part, tick);
+  else if (c.mb == 1)
+    hipLaunchKernelGGL((k_gemm_ksplit<B, 1, 2, true>), grid, dim3(256), 0, st, set, X, ldx, m,
+                       kb, G, c.splits, c.kbps, part, tick);
+  else if (B <= 4 && (c.kbps + 3) / 4 >= 4)   // (wider codes: 1 wave per SIMD at 4 blocks)
+    hipLaunchKernelGGL((k_gemm_ksplit<B, (B <= 4 ? 4 : 2), 1, true>), grid, dim3(256), 0, st,
+                       set, X, ldx, m, kb, G, c.splits, c.kbps, part, tick);
+  else if ((c.kbps + 3) / 4 >= 2)
+    hipLaunchKernelGGL((k_gemm_ksplit<B, 2, 1, true>), grid, dim3(256), 0, st, set, X, ldx, m,
+                       kb, G, c.splits, c.kbps, part, tick);
+  else
+    hipLaunchKernelGGL((k_gemm_ksplit<B, 1, 1, true>), grid, dim3(256), 0, st, set, X, ldx, m,
+                       kb, G, c.splits, c.kbps, part, tick);
+}
+
 }  // namespace
 
 // Checks shared by the multi-matrix GEMV entry points: `count` packed
@@ -995,6 +1078,76 @@ qlin_status qlin_gemm_multi(const qlin_weight* w, int32_t count, const uint16_t*
   for (int i = 0; i < count; ++i) wp[i] = &w[i];
   const GemmPlan p = gemm_plan(wp, Y, ld_y, count, m <= kSkinnyMaxM);
   return run_gemm(p, X, m, ld_x, workspace, workspace_bytes, stream);
+}
+
+int64_t qlin_gemm_swiglu_workspace_bytes(const qlin_weight* gate, int32_t m) {
+  if (check_weight(gate, false, false) != QLIN_OK || m < 1 || m > kMaxM) return 0;
+  return swiglu_ws_bytes(tiles_of(gate->n), gate->k / kBlock, m);
+}
+
+qlin_status qlin_gemm_swiglu(const qlin_weight* gate, const qlin_weight* up, const uint16_t* X,
+                             int32_t m, int64_t ld_x, float* H, uint16_t* H16, int64_t ld_h,
+                             void* workspace, int64_t workspace_bytes, hipStream_t stream) {
+  if (gate == nullptr || up == nullptr || X == nullptr) return QLIN_ERR_NULL;
+  if (H == nullptr && H16 == nullptr) return QLIN_ERR_NULL;
+  const qlin_weight* wp[2] = {gate, up};
+  for (int i = 0; i < 2; ++i) {
+    const qlin_status st = check_weight(wp[i], false, false);
+    if (st != QLIN_OK) return st;
+  }
+  if (up->k != gate->k || up->n != gate->n) return QLIN_ERR_SHAPE;
+  if (up->bits != gate->bits || up->group != gate->group) return QLIN_ERR_FORMAT;
+  const int n = gate->n, k = gate->k;
+  if (m < 1 || m > kMaxM || ld_x < k || ld_h < n) return QLIN_ERR_SHAPE;
+  if (ld_x % 8 != 0 || !aligned16(X) || !aligned16(H) || !aligned16(H16)) return QLIN_ERR_ALIGN;
+  if (workspace_bytes < 0) return QLIN_ERR_WORKSPACE;
+  if (workspace == nullptr) workspace_bytes = 0;
+  if (workspace != nullptr && !aligned16(workspace)) return QLIN_ERR_ALIGN;
+  const int64_t span = (int64_t)(m - 1) * ld_h + n;
+  const Range rX = range_of(X, ((int64_t)(m - 1) * ld_x + k) * 2);
+  const Range rw = range_of(workspace, workspace_bytes);
+  const Range rH = range_of(H, H != nullptr ? span * 4 : 0);
+  const Range rH16 = range_of(H16, H16 != nullptr ? span * 2 : 0);
+  const Range outs[3] = {rw, rH, rH16};
+  for (int i = 0; i < 3; ++i) {
+    if (overlaps(outs[i], rX)) return QLIN_ERR_ALIAS;
+    for (int j = 0; j < i; ++j)
+      if (overlaps(outs[i], outs[j])) return QLIN_ERR_ALIAS;
+    for (int j = 0; j < 2; ++j)
+      if (output_overlaps_weight(wp[j], outs[i])) return QLIN_ERR_ALIAS;
+  }
+  const qlin_status st = check_device();
+  if (st != QLIN_OK) return st;
+  const int64_t tiles = tiles_of(n);
+  const int kb = k / kBlock;
+  const int G = (gate->group == k) ? 1 : kb;
+  const TilesCfg c = swiglu_config(tiles, kb, m, workspace_bytes);
+  GemmSet set{};
+  for (int i = 0; i < 2; ++i) {
+    set.codes[i] = static_cast<const uint32_t*>(wp[i]->data);
+    set.scale[i] = wp[i]->scale;
+    set.zero[i] = wp[i]->zero;
+    set.n[i] = n;
+    set.ldy[i] = ld_h;
+  }
+  set.y[0] = H;
+  set.end[0] = c.gx;                 // every launch column is matrix 0's (the pair's)
+  set.end[1] = c.gx;
+  set.count = 2;
+  set.h16 = H16;
+  uint32_t* tick = static_cast<uint32_t*>(workspace);
+  float* part = c.splits > 1
+      ? reinterpret_cast<float*>(static_cast<char*>(workspace) + kCounterBytes) : nullptr;
+  switch (gate->bits) {
+    case 2: launch_gemm_swiglu<2>(set, X, ld_x, m, kb, G, c, part, tick, stream); break;
+    case 3: launch_gemm_swiglu<3>(set, X, ld_x, m, kb, G, c, part, tick, stream); break;
+    case 4: launch_gemm_swiglu<4>(set, X, ld_x, m, kb, G, c, part, tick, stream); break;
+    case 5: launch_gemm_swiglu<5>(set, X, ld_x, m, kb, G, c, part, tick, stream); break;
+    case 6: launch_gemm_swiglu<6>(set, X, ld_x, m, kb, G, c, part, tick, stream); break;
+    case 7: launch_gemm_swiglu<7>(set, X, ld_x, m, kb, G, c, part, tick, stream); break;
+    default: launch_gemm_swiglu<8>(set, X, ld_x, m, kb, G, c, part, tick, stream); break;
+  }
+  return hip_status(hipGetLastError());
 }
 
 }  // extern "C"

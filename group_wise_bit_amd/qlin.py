@@ -33,6 +33,7 @@ EXPORTS = (
     "qlin_gemv_multi_workspace_bytes", "qlin_gemv_multi",
     "qlin_gemv_swiglu_workspace_bytes", "qlin_gemv_swiglu", "qlin_embed_rows",
     "qlin_quantize_batch", "qlin_gemm_multi_workspace_bytes", "qlin_gemm_multi",
+    "qlin_gemm_swiglu_workspace_bytes", "qlin_gemm_swiglu",
 )
 
 
@@ -112,6 +113,10 @@ def _lib() -> ctypes.CDLL:
         lib.qlin_gemm_multi.argtypes = [wp, i32, vp, i32, i64, ctypes.POINTER(vp),
                                         ctypes.POINTER(i64), vp, i64, vp]
         lib.qlin_gemm_multi.restype = ctypes.c_int
+        lib.qlin_gemm_swiglu_workspace_bytes.argtypes = [wp, i32]
+        lib.qlin_gemm_swiglu_workspace_bytes.restype = i64
+        lib.qlin_gemm_swiglu.argtypes = [wp, wp, vp, i32, i64, vp, vp, i64, vp, i64, vp]
+        lib.qlin_gemm_swiglu.restype = ctypes.c_int
         _LIB = lib
     return _LIB
 
@@ -374,3 +379,33 @@ def gemm_multi(ws_list: Sequence[QWeight], X: torch.Tensor,
                                 _stream())
     _check(st, "qlin_gemm_multi")
     return list(Ys)
+
+
+def gemm_swiglu(gate: QWeight, up: QWeight, X: torch.Tensor,
+                H: Optional[torch.Tensor] = None, H16: Optional[torch.Tensor] = None,
+                ws: Optional[torch.Tensor] = "auto", want_h: bool = True,
+                want_h16: bool = True) -> Tuple[Optional[torch.Tensor], Optional[torch.Tensor]]:
+    """qlin_gemm_swiglu: H = silu(X . gate^T) * (X . up^T), fp32 and/or fp16 [m, n], one launch.
+    H and H16, when both given, must share one row stride."""
+    if X.dtype != torch.float16 or X.dim() != 2 or X.stride(1) != 1:
+        raise TypeError("X must be a float16 [m, k] tensor with contiguous rows")
+    m = X.shape[0]
+    if H is None and want_h:
+        H = torch.empty(m, gate.n, dtype=torch.float32, device=X.device)
+    if H16 is None and want_h16:
+        H16 = torch.empty(m, gate.n, dtype=torch.float16, device=X.device)
+    outs = [t for t in (H, H16) if t is not None]
+    if any(t.dim() != 2 or t.stride(1) != 1 for t in outs):
+        raise TypeError("H and H16 must be 2-D with contiguous rows")
+    ld = outs[0].stride(0) if outs else gate.n
+    if any(t.stride(0) != ld for t in outs):
+        raise ValueError("H and H16 must share one row stride")
+    g, u = gate.c_struct(), up.c_struct()
+    if isinstance(ws, str):
+        need = int(_lib().qlin_gemm_swiglu_workspace_bytes(ctypes.byref(g), m))
+        ws = workspace(need, X.device)
+    wsb = 0 if ws is None else ws.numel() * ws.element_size()
+    st = _lib().qlin_gemm_swiglu(ctypes.byref(g), ctypes.byref(u), X.data_ptr(), m, X.stride(0),
+                                 _ptr(H), _ptr(H16), ld, _ptr(ws), wsb, _stream())
+    _check(st, "qlin_gemm_swiglu")
+    return H, H16

@@ -217,6 +217,30 @@ qlin_status qlin_gemm_multi(const qlin_weight* w, int32_t count, const uint16_t*
                             int64_t workspace_bytes, hipStream_t stream);
 
 /*
+ * Gated MLP input of a prefill in one launch: the prefill (M-row) form of
+ * qlin_gemv_swiglu (the Bitcrush README, "Under the hood": the SwiGLU kernel
+ * after the gate and up projections; the Enargeia page, "Measured, not
+ * asserted": prefill is the tiled-matmul form of the same products):
+ *     H[m, n] = silu(G[m, n]) * U[m, n],   G = X . gate^T,  U = X . up^T,
+ *     silu(g) = g / (1 + exp(-g)),
+ * with G and U formed as qlin_gemm forms Y (same operand rounding, fp32
+ * accumulation) and never written to memory.  gate and up are PACKED weights
+ * with the same n, k, bits and group.  X fp16 [m, ld_x] (ld_x >= k, % 8 == 0).
+ * Outputs, either may be NULL (not both), leading dimension ld_h >= n for
+ * both: H fp32 [m, ld_h]; H16 fp16 bit patterns [m, ld_h], H rounded to
+ * nearest even (ready as the down projection's X when ld_h % 8 == 0).
+ * Writes a quarter of the bytes of the two fp32 outputs of qlin_gemm_multi.
+ * Deterministic.  Workspace as for qlin_gemm, sized by
+ * qlin_gemm_swiglu_workspace_bytes(gate, m).  Errors: different n or k ->
+ * QLIN_ERR_SHAPE, different bits or group -> QLIN_ERR_FORMAT, otherwise as
+ * for qlin_gemm.
+ */
+int64_t qlin_gemm_swiglu_workspace_bytes(const qlin_weight* gate, int32_t m);
+qlin_status qlin_gemm_swiglu(const qlin_weight* gate, const qlin_weight* up, const uint16_t* X,
+                             int32_t m, int64_t ld_x, float* H, uint16_t* H16, int64_t ld_h,
+                             void* workspace, int64_t workspace_bytes, hipStream_t stream);
+
+/*
  * Several decode GEMVs that share x, in one launch (the Enargeia page, "One
  * decode step": the per-token dispatch list, where q, k and v, and gate and
  * up, each read the same normalized activation):

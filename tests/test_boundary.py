@@ -31,7 +31,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     declared = header_functions()
-    assert len(declared) == 18
+    assert len(declared) == 20
     assert sorted(qlin.EXPORTS) == declared
     for name in declared:
         assert hasattr(lib, name), name
@@ -272,6 +272,40 @@ def test_gemm_multi_validation(lib):
     assert lib.qlin_gemm_multi_workspace_bytes(weights(big, big), 2, 8) > 65536
 
 
+def gswiglu(lib, g, u, X=FAKE + (3 << 30), m=4, ldx=128, H=Y0, H16=Y1, ldh=8, ws_=None, wsb=0):
+    return lib.qlin_gemm_swiglu(ctypes.byref(g), ctypes.byref(u), X, m, ldx, H, H16, ldh, ws_,
+                                wsb, None)
+
+
+def test_gemm_swiglu_validation(lib):
+    g, u = weight(), other_weight(0)
+    assert lib.qlin_gemm_swiglu(None, ctypes.byref(u), FAKE, 4, 128, Y0, Y1, 8, None, 0,
+                                None) == NULL
+    assert gswiglu(lib, g, u, X=None) == NULL
+    assert gswiglu(lib, g, u, H=None, H16=None) == NULL
+    assert gswiglu(lib, g, other_weight(0, n=16)) == SHAPE                  # one n
+    assert gswiglu(lib, g, other_weight(0, k=256)) == SHAPE                 # one k
+    assert gswiglu(lib, g, other_weight(0, bits=8)) == FORMAT
+    assert gswiglu(lib, g, other_weight(0, group=128)) == FORMAT
+    assert gswiglu(lib, g, other_weight(0, format=1, ld=128)) == FORMAT     # packed only
+    assert gswiglu(lib, g, u, m=0) == SHAPE
+    assert gswiglu(lib, g, u, ldx=64) == SHAPE
+    assert gswiglu(lib, g, u, ldh=4) == SHAPE
+    assert gswiglu(lib, g, u, ldx=132) == ALIGN
+    assert gswiglu(lib, g, u, H16=Y1 + 2) == ALIGN
+    assert gswiglu(lib, g, u, H16=Y0 + 16) == ALIAS                         # H16 inside H
+    assert gswiglu(lib, g, u, H=FAKE + 32) == ALIAS                         # H on gate codes
+    assert gswiglu(lib, g, u, H16=FAKE + (8 << 30) + 64) == ALIAS           # H16 on up codes
+    assert gswiglu(lib, g, u, H=FAKE + (3 << 30)) == ALIAS                  # H on X
+    assert gswiglu(lib, g, u, ws_=Y0, wsb=64) == ALIAS
+    assert gswiglu(lib, g, u, ws_=FAKE + (7 << 30), wsb=-1) == WORKSPACE
+    assert lib.qlin_gemm_swiglu_workspace_bytes(ctypes.byref(g), 4) == 0
+    big = weight(n=128, k=16384)               # two tiles, 256 K-blocks: split across groups
+    assert lib.qlin_gemm_swiglu_workspace_bytes(ctypes.byref(big), 8) > 65536
+    assert lib.qlin_gemm_swiglu_workspace_bytes(ctypes.byref(big), 0) == 0
+    assert lib.qlin_gemm_swiglu_workspace_bytes(ctypes.byref(weight(bits=9)), 8) == 0
+
+
 @pytest.mark.skipif(torch.cuda.is_available(), reason="checks the no-GPU path")
 def test_no_device(lib):
     # calls that pass every host check (with fake addresses: never run on a GPU)
@@ -288,6 +322,8 @@ def test_no_device(lib):
     assert multi(lib, [weight(), other_weight(0)], [Y0, Y1]) == NODEV
     assert swiglu(lib, weight(), other_weight(0)) == NODEV
     assert swiglu(lib, weight(), other_weight(0), h=None) == NODEV
+    assert gswiglu(lib, weight(), other_weight(0)) == NODEV
+    assert gswiglu(lib, weight(), other_weight(0), H=None, m=300) == NODEV
 
 
 def test_workspace_queries(lib):
