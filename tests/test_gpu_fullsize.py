@@ -6,7 +6,8 @@ bench.py times (the same calls, a 64 MB workspace), checked on sampled whole
 * the Qwen2.5-0.5B decode step: all 169 matrices (incl. the 151936x896 LM
   head) quantized on the GPU, codes/scales/zeros of sampled tiles bit-exact,
   GEMV rows of sampled tiles within tolerance;
-* prefill GEMMs at M = 128 and 2048 on the layer shapes;
+* prefill GEMMs at M = 128 and 2048 on the layer shapes, and the gate/up
+  pair with the SwiGLU epilogue;
 * the Qwen3-0.6B fused re-quantization sweep (bits 8/4/3/2, per-group and
   per-channel) on all 196 matrices for two settings and on two layers for all;
 * Qwen3-8B layer shapes at int4 and int3 for M = 1, 8, 128.
@@ -116,6 +117,28 @@ def test_qwen25_prefill_full(ws, m):
         codes, s16, z = oracle.quantize(w16[rows], 4, 64)
         check_tol(Y[:, rows], X[:, :k], oracle.dequantize(codes, s16, z, 64),
                   f"M={m} {nm}")
+
+
+@pytest.mark.parametrize("m", [128, 2048])
+def test_qwen25_prefill_swiglu_full(ws, m):
+    """The prefill step's gate/up launch (qlin_gemm_swiglu, fp16 h only, as
+    bench.py calls it): sampled tiles of h within the SwiGLU bound."""
+    rng = np.random.default_rng([9, m])
+    n, k = 4864, 896
+    X = synth.activations(np.random.default_rng([7, m]), m, k)
+    wg16 = synth.master_weights(synth.layer_rng(1, 0, "gate"), n, k)
+    wu16 = synth.master_weights(synth.layer_rng(1, 0, "up"), n, k)
+    say(f"prefill gate/up SwiGLU M={m}")
+    gate, up = qlin.quantize(dev(wg16), 4, 64), qlin.quantize(dev(wu16), 4, 64)
+    _, H16 = qlin.gemm_swiglu(gate, up, dev(X), ws=ws, want_h=False)
+    h16 = H16.cpu().numpy()
+    rows = np.concatenate([tile_rows(t, n) for t in sample_tiles(n, rng)])
+    wg = oracle.dequantize(*oracle.quantize(wg16[rows], 4, 64), 64)
+    wu = oracle.dequantize(*oracle.quantize(wu16[rows], 4, 64), 64)
+    ref = oracle.swiglu_ref(X, wg, wu)
+    bound = oracle.swiglu_tolerance(X, wg, wu) + np.abs(ref) * 2.0 ** -11 + 2.0 ** -25
+    err = np.abs(h16[:, rows].astype(np.float64) - ref)
+    assert np.all(err <= bound), f"M={m}: max err {err.max():.3e}"
 
 
 def _fused_case(ws, l, nm, n, k, bits, grp, rng):
