@@ -500,12 +500,25 @@ TilesCfg tiles_config(int64_t gx, int64_t tiles, int kb, int m, int count,
   c.gx = (int)gx;
   int want = 1;
   if (m <= 256 && (tiles < 256 || m <= 16)) {
-    // the K-split kernel: one 64-row W tile x 32 X rows per work-group; K is
-    // split across work-groups (at most 8 ways) only when the grid is under
-    // 256 work-groups, keeping at least 8 K-blocks per split
+    // the K-split kernel: one 64-row W tile x 32 X rows per work-group; for
+    // M > 16, K is split across work-groups (at most 8 ways) only when the
+    // grid is under 256 work-groups, keeping at least 8 K-blocks per split
     c.mb = 0;
     const int64_t groups = tiles * ((m + 31) / 32);
-    if (groups < 256) {
+    if (m <= 16) {
+      // M <= 16 (measured at M = 8 on the Qwen2.5-0.5B and Qwen3-8B shapes):
+      // a work-group's K range is one or two rounds of loads already, so a
+      // split mostly adds its partial-sum round trip; split only launches of
+      // under 32 work-groups, and very long K (about 48 K-blocks per split)
+      if (groups < 32) {
+        want = (int)((256 + groups - 1) / groups);
+        if (want > 8) want = 8;
+        if (want > kb / 8) want = kb / 8;
+      } else if (kb >= 128) {
+        want = kb / 48;
+        if (want > 8) want = 8;
+      }
+    } else if (groups < 256) {
       want = (int)((512 + groups - 1) / groups);
       if (want > 8) want = 8;
       if (want > kb / 8) want = kb / 8;
