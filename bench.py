@@ -40,6 +40,10 @@ gate/up 4096->12288, down 12288->4096 (252 matrices, 3.8 GB at int4):
                                    144 launches (graph)
   q8_decode_int4 / _int3 / _int2   252 packed GEMVs (graph)
   q8_m8_int4 / _int3               252 GEMMs at M = 8
+  q8_m8_step_int4 / _int3          the same grouped as in decode_step: per
+                                   layer q/k/v in one launch, o, gate/up with
+                                   the SwiGLU epilogue (fp16 h), down reading
+                                   h (144 launches)
   q8_m128_int4 / _int3             252 GEMMs at M = 128
 qwen3_06b -- the 196 fp16 masters of Qwen3-0.6B (28 layers of q 1024->2048,
 k/v 1024->1024, o 2048->1024, gate/up 1024->3072, down 3072->1024):
@@ -381,12 +385,45 @@ def build_qwen3_8b(torch, qlin, synth, dev, ws, phases):
                     lambda w=w, m=m: qlin.gemm(w, X[m][:, : w.k], Y[m][: m * w.n].view(m, w.n),
                                                ws=ws) for w in packed[b]]])[0]
 
-    hold = (packed, xs, ys, X, Y)
+    # M = 8 grouped like the decode step; h of the gate/up pair feeds down
+    idx = {(l, nm): i for i, (l, nm, _, _) in enumerate(shapes)}
+    layers = sorted(set(l for (l, *_) in shapes))
+    n_of = {nm: shapes[idx[(0, nm)]][2] for nm in ("q", "k", "v", "o", "gate", "down")}
+    Y8 = {nm: torch.empty(8, n_of[nm], dtype=torch.float32, device=dev)
+          for nm in ("q", "k", "v", "o", "down")}
+    H8 = torch.empty(8, n_of["gate"], dtype=torch.float16, device=dev)
+    m8_steps, m8_bytes = {}, {}
+    for b in (4, 3):
+        if f"q8_m8_step_int{b}" not in phases:
+            continue
+        calls, nbytes = [], 0
+        for l in layers:
+            w = {nm: packed[b][idx[(l, nm)]] for nm in ("q", "k", "v", "o", "gate", "up", "down")}
+            k1 = w["q"].k
+            calls += [
+                lambda w=w, k1=k1: qlin.gemm_multi([w["q"], w["k"], w["v"]], X[8][:, :k1],
+                                                   [Y8["q"], Y8["k"], Y8["v"]], ws=ws),
+                lambda w=w, k1=k1: qlin.gemm(w["o"], X[8][:, :k1], Y8["o"], ws=ws),
+                lambda w=w, k1=k1: qlin.gemm_swiglu(w["gate"], w["up"], X[8][:, :k1], None, H8,
+                                                    ws=ws, want_h=False),
+                lambda w=w: qlin.gemm(w["down"], H8, Y8["down"], ws=ws),
+            ]
+            # weights + X read once per launch + outputs (fp32 Y, fp16 h)
+            nbytes += sum(wbytes(x.n, x.k, b, 64) for x in w.values())
+            nbytes += 4 * 16 * k1 + 16 * w["down"].k
+            nbytes += 32 * (w["q"].n + w["k"].n + w["v"].n + w["o"].n + w["down"].n)
+            nbytes += 16 * w["gate"].n
+        m8_steps[b] = capture_calls(torch, [calls])[0]
+        m8_bytes[b] = nbytes
+
+    hold = (packed, xs, ys, X, Y, Y8, H8)
 
     def run(name):
         assert hold is not None       # every buffer the graphs address stays alive
         b = int(name[-1])
-        if "step" in name:
+        if "m8_step" in name:
+            m8_steps[b].replay()
+        elif "step" in name:
             steps[b].replay()
         elif "decode" in name:
             graphs[b].replay()
@@ -404,6 +441,9 @@ def build_qwen3_8b(torch, qlin, synth, dev, ws, phases):
         out.append(Phase(f"q8_m8_int{b}", run, "GB/s",
                          sum(wbytes(n, k, b, 64) + 16 * k + 32 * n for (_, _, n, k) in shapes),
                          252, HBM_PEAK_GBS, "hbm", f"k_gemm_ksplit<{b}>"))
+        out.append(Phase(f"q8_m8_step_int{b}", run, "GB/s", m8_bytes.get(b, 0), 144,
+                         HBM_PEAK_GBS, "hbm",
+                         f"k_gemm_ksplit<{b}> (q/k/v set, o, gate/up+SwiGLU pair, down)"))
         out.append(Phase(f"q8_m128_int{b}", run, "TFLOP/s",
                          sum(2 * 128 * n * k for (_, _, n, k) in shapes), 252,
                          FP16_MFMA_PEAK_TFLOPS, "mfma", f"k_gemm_ksplit<{b}>"))
@@ -517,7 +557,8 @@ def main():
         phases += ps
     if "qwen3_8b" in sections:
         names = [f"q8_{s}_int{b}" for b in (4, 3, 2) for s in ("step", "decode")] + [
-            f"q8_m{m}_int{b}" for b in (4, 3) for m in (8, 128)]
+            f"q8_m{m}_int{b}" for b in (4, 3) for m in (8, 128)] + [
+            f"q8_m8_step_int{b}" for b in (4, 3)]
         phases += build_qwen3_8b(torch, qlin, synth, dev, ws, chosen(names))
     if "qwen3_06b" in sections:
         names = ([f"q06_{k}_b{b}_{g}" for k in ("fused", "lever") for b in (8, 7, 6, 5, 4, 3, 2)

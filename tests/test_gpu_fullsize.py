@@ -10,7 +10,8 @@ bench.py times (the same calls, a 64 MB workspace), checked on sampled whole
   pair with the SwiGLU epilogue;
 * the Qwen3-0.6B fused re-quantization sweep (bits 8/4/3/2, per-group and
   per-channel) on all 196 matrices for two settings and on two layers for all;
-* Qwen3-8B layer shapes at int4 and int3 for M = 1, 8, 128.
+* Qwen3-8B layer shapes at int4 and int3 for M = 1, 8, 128, and its gate/up
+  pair with the SwiGLU epilogue at M = 8 and 128.
 """
 import numpy as np
 import pytest
@@ -197,3 +198,26 @@ def test_qwen3_8b_layer_full(ws, bits):
         for m in (8, 128):
             Y = qlin.gemm(qw, Xd[:m], ws=ws).cpu().numpy()
             check_tol(Y[:, rows], X[:m], what, f"{nm} M={m}")
+
+
+@pytest.mark.parametrize("bits", [4, 3])
+def test_qwen3_8b_swiglu_full(ws, bits):
+    """The 12288x4096 gate/up pair with the SwiGLU epilogue at M = 8 and 128
+    (the grouped M = 8 step's launch): sampled tiles of h within the bound."""
+    rng = np.random.default_rng(30 + bits)
+    n, k = 12288, 4096
+    wg16 = synth.master_weights(synth.layer_rng(5, 0, "gate"), n, k)
+    wu16 = synth.master_weights(synth.layer_rng(5, 0, "up"), n, k)
+    X = synth.activations(synth.act_rng(5, 0, "gate"), 128, k)
+    say(f"Qwen3-8B gate/up SwiGLU b={bits}")
+    gate, up = qlin.quantize(dev(wg16), bits, 64), qlin.quantize(dev(wu16), bits, 64)
+    rows = np.concatenate([tile_rows(t, n) for t in sample_tiles(n, rng)])
+    wg = oracle.dequantize(*oracle.quantize(wg16[rows], bits, 64), 64)
+    wu = oracle.dequantize(*oracle.quantize(wu16[rows], bits, 64), 64)
+    Xd = dev(X)
+    for m in (8, 128):
+        _, H16 = qlin.gemm_swiglu(gate, up, Xd[:m], ws=ws, want_h=False)
+        ref = oracle.swiglu_ref(X[:m], wg, wu)
+        bound = oracle.swiglu_tolerance(X[:m], wg, wu) + np.abs(ref) * 2.0 ** -11 + 2.0 ** -25
+        err = np.abs(H16.cpu().numpy()[:, rows].astype(np.float64) - ref)
+        assert np.all(err <= bound), f"M={m}: max err {err.max():.3e}"
