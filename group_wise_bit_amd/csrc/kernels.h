@@ -1512,20 +1512,31 @@ __global__ __launch_bounds__(256) void k_gemm_tiles(
 // fragments by the same tile of both, the two tiles are reduced one after
 // the other, and the output is h = silu(gate . x) * (up . x) in fp32 (y[0],
 // if not null) and/or fp16 (set.h16), both with leading dimension ldy[0].
-template <int BITS, int U, int RB, bool PAIR = false>
+// DUAL: one matrix, and a work-group covers its tiles 2x and 2x + 1 (grid.x
+// = tile pairs): each X fragment feeds twice the MFMAs, so a tall X tile over
+// few tiles moves half the X bytes per MFMA through L1.
+template <int BITS, int U, int RB, bool PAIR = false, bool DUAL = false>
 __global__ __launch_bounds__(256) void k_gemm_ksplit(
     const GemmSet set, const uint16_t* __restrict__ X, int64_t ldx, int m, int kb, int G,
     int splits, int kbps, float* __restrict__ part, uint32_t* __restrict__ tickets) {
   constexpr int WPB = 2 * BITS;
   constexpr int HW = WPB / 2;                 // words of a half block
   constexpr int NE = RB * 2048;              // elements of a wave's partial tile
-  constexpr int NM = PAIR ? 2 : 1;           // matrices per work-group
+  constexpr int NM = (PAIR || DUAL) ? 2 : 1; // tiles per work-group
+  static_assert(!(PAIR && DUAL), "one of PAIR, DUAL");
   __shared__ float red[4][NE];
   const int tid = threadIdx.x;
   const int lane = lane_id(), wave = wave_id();
   const int c = lane & 31, h = lane >> 5;
   const GemmMat mat = gemm_mat(set, blockIdx.x);
-  const int t = mat.col;
+  // tile of each of the NM products (DUAL: a tile past the matrix re-reads
+  // its last one and is not stored)
+  int tm[NM], tl[NM];
+#pragma unroll
+  for (int mi = 0; mi < NM; ++mi) {
+    tm[mi] = DUAL ? 2 * mat.col + mi : mat.col;
+    tl[mi] = min(tm[mi], mat.tiles - 1);
+  }
   const int m0 = blockIdx.y * 32 * RB;
   const uint32_t magic = vreg_const(kMagic);
   const int j0 = blockIdx.z * kbps;
@@ -1540,18 +1551,16 @@ __global__ __launch_bounds__(256) void k_gemm_ksplit(
   const uint32_t* wsrc[NM][2];
   const uint16_t* ssrc[NM];
   const uint8_t* zsrc[NM];
-  int64_t msrc[2];
 #pragma unroll
   for (int mi = 0; mi < NM; ++mi) {
     const uint32_t* codes = PAIR ? set.codes[mi] : mat.codes;
-    ssrc[mi] = PAIR ? set.scale[mi] : mat.scale;
-    zsrc[mi] = PAIR ? set.zero[mi] : mat.zero;
+    const int64_t mt = (int64_t)tl[mi] * G * kTile + c;
+    ssrc[mi] = (PAIR ? set.scale[mi] : mat.scale) + mt;
+    zsrc[mi] = (PAIR ? set.zero[mi] : mat.zero) + mt;
 #pragma unroll
     for (int cb = 0; cb < 2; ++cb)
-      wsrc[mi][cb] = codes + ((int64_t)t * kb * kTile + 32 * cb + c) * WPB;
+      wsrc[mi][cb] = codes + ((int64_t)tl[mi] * kb * kTile + 32 * cb + c) * WPB;
   }
-#pragma unroll
-  for (int cb = 0; cb < 2; ++cb) msrc[cb] = (int64_t)t * G * kTile + 32 * cb + c;
   f32x16 acc[NM][RB][2];
 #pragma unroll
   for (int mi = 0; mi < NM; ++mi)
@@ -1583,8 +1592,8 @@ __global__ __launch_bounds__(256) void k_gemm_ksplit(
 #pragma unroll
         for (int cb = 0; cb < 2; ++cb) {
           load_half<BITS>(wsrc[mi][cb] + (int64_t)jj * kTile * WPB, h, wl[u][mi][cb]);
-          sr[u][mi][cb] = ssrc[mi][msrc[cb] + g * kTile];
-          zc[u][mi][cb] = zsrc[mi][msrc[cb] + g * kTile];
+          sr[u][mi][cb] = ssrc[mi][32 * cb + g * kTile];
+          zc[u][mi][cb] = zsrc[mi][32 * cb + g * kTile];
         }
     }
     if constexpr (U > 1 || PAIR) loads_issued();
@@ -1661,15 +1670,21 @@ __global__ __launch_bounds__(256) void k_gemm_ksplit(
     const int e = tid + 256 * i;
     const int rb = e >> 11, cb = (e >> 10) & 1, r = (e >> 6) & 15, l = e & 63;
     const int row = m0 + 32 * rb + 8 * (r >> 2) + 4 * (l >> 5) + (r & 3);
-    const int col = t * kTile + 32 * cb + (l & 31);
-    if (row >= m || col >= n) continue;
-    const int64_t o = (int64_t)row * mat.ldy + col;
+    const int cl = 32 * cb + (l & 31);
+    if (row >= m) continue;
     if constexpr (PAIR) {
+      const int col = tm[0] * kTile + cl;
+      if (col >= n) continue;
+      const int64_t o = (int64_t)row * mat.ldy + col;
       const float hv = silu(v[0][i]) * v[NM - 1][i];
       if (mat.y != nullptr) mat.y[o] = hv;
       if (set.h16 != nullptr) set.h16[o] = __builtin_bit_cast(uint16_t, (f16)hv);
     } else {
-      mat.y[o] = v[0][i];
+#pragma unroll
+      for (int mi = 0; mi < NM; ++mi) {
+        const int col = tm[mi] * kTile + cl;
+        if (col < n) mat.y[(int64_t)row * mat.ldy + col] = v[mi][i];
+      }
     }
   }
 }

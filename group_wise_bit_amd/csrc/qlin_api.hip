@@ -491,13 +491,15 @@ void launch_gemm_skinny(const GemmPlan& p, const uint16_t* X, int64_t ldx, int m
 // M = 256 the K-split kernel is 1.1-2x faster (all loads of a wave's K-blocks
 // in flight at once; 64 X rows from 256 tiles up).  Above M = 256 a tall X
 // tile pays only when the grid is large.
-// mb = 0 / 1: k_gemm_ksplit with 32 / 64 X rows, gx in tiles
-struct TilesCfg { int mb, gx, gy, splits, kbps; };
+// mb = 0 / 1: k_gemm_ksplit with 32 / 64 X rows, gx in tiles (dual: in tile
+// pairs of a single matrix)
+struct TilesCfg { int mb, gx, gy, splits, kbps; bool dual; };
 
 TilesCfg tiles_config(int64_t gx, int64_t tiles, int kb, int m, int count,
                       int64_t ws_bytes) {
   TilesCfg c;
   c.gx = (int)gx;
+  c.dual = false;
   int want = 1;
   if (m <= 256 && (tiles < 256 || m <= 16)) {
     // the K-split kernel: one 64-row W tile x 32 X rows per work-group; for
@@ -536,22 +538,30 @@ TilesCfg tiles_config(int64_t gx, int64_t tiles, int kb, int m, int count,
       c.mb = 64;
       if ((int64_t)c.gx * ((m + 63) / 64) < 256) c.mb = kb >= 32 ? 1 : (count > 1 ? 0 : 32);
     }
+    // the K-split kernel over a tall M reads its X fragments through L1 for
+    // every tile: over tile pairs each fragment feeds twice the MFMAs
+    // (Qwen2.5-0.5B down projection at M = 2048: 52 -> 38 us)
+    c.dual = c.mb == 1;
   }
   // QLIN_TUNE_GEMM="mb,splits" overrides the choice (launch-shape sweeps;
-  // mb = 0: the K-split kernel)
+  // mb = 0 / 1: the K-split kernel, 2 / 3: the same with 64 / 32 X rows over
+  // tile pairs)
   if (const char* e = getenv("QLIN_TUNE_GEMM")) {
     int mb = 0, sp = 0;
     if (sscanf(e, "%d,%d", &mb, &sp) == 2 &&
-        (mb == 0 || mb == 1 || mb == 32 || mb == 64 || mb == 128) && sp >= 1) {
-      c.mb = mb;
+        (mb == 0 || mb == 1 || mb == 2 || mb == 3 || mb == 32 || mb == 64 || mb == 128) &&
+        sp >= 1) {
+      c.mb = mb == 2 ? 1 : mb == 3 ? 0 : mb;
+      c.dual = mb == 2 || mb == 3;
       want = sp < kb ? sp : kb;
     }
   }
+  if (count > 1) c.dual = false;       // tile pairs of one matrix only
   if (want < 1) want = 1;
   const bool ks = c.mb <= 1;
-  if (ks) c.gx = (int)tiles;
+  if (ks) c.gx = (int)(c.dual ? (tiles + 1) / 2 : tiles);
   const int rows = ks ? 32 * (c.mb + 1) : c.mb;
-  const int64_t wg_outputs = (int64_t)rows * (ks ? kTile : 256);
+  const int64_t wg_outputs = (int64_t)rows * (ks ? kTile * (c.dual ? 2 : 1) : 256);
   c.gy = (m + rows - 1) / rows;
   if ((int64_t)c.gx * c.gy > kMaxSplitTiles) want = 1;
   while (want > 1 && kCounterBytes + (int64_t)want * c.gy * c.gx * wg_outputs * 4 > ws_bytes)
@@ -564,7 +574,8 @@ TilesCfg tiles_config(int64_t gx, int64_t tiles, int kb, int m, int count,
 int64_t tiles_ws_bytes(int64_t gx, int64_t tiles, int kb, int m, int count) {
   const TilesCfg c = tiles_config(gx, tiles, kb, m, count, INT64_MAX);
   if (c.splits <= 1) return 0;
-  const int64_t wg_outputs = c.mb <= 1 ? 32 * (c.mb + 1) * kTile : (int64_t)c.mb * 256;
+  const int64_t wg_outputs = c.mb <= 1 ? 32 * (c.mb + 1) * kTile * (c.dual ? 2 : 1)
+                                       : (int64_t)c.mb * 256;
   return kCounterBytes + (int64_t)c.splits * c.gy * c.gx * wg_outputs * 4;
 }
 
@@ -591,7 +602,15 @@ void launch_gemm_ksplit_rb(const GemmSet& set, const GemmPlan& p, const uint16_t
   // 64-row X tiles, whose X fragments take twice the registers)
   const int per_wave = (c.kbps + 3) / 4;
   const dim3 grid(c.gx, c.gy, c.splits);
-  if (per_wave >= 4 && RB == 1)
+  if (c.dual) {   // tile pairs: two accumulator sets, so at most 2 blocks in flight
+                  // (1 with 64 X rows, to keep 2 waves per SIMD)
+    if (RB == 1 && per_wave >= 2)
+      hipLaunchKernelGGL((k_gemm_ksplit<B, 2, RB, false, true>), grid, dim3(256), 0, st, set, X,
+                         ldx, m, p.kb, p.G, c.splits, c.kbps, part, tick);
+    else
+      hipLaunchKernelGGL((k_gemm_ksplit<B, 1, RB, false, true>), grid, dim3(256), 0, st, set, X,
+                         ldx, m, p.kb, p.G, c.splits, c.kbps, part, tick);
+  } else if (per_wave >= 4 && RB == 1)
     hipLaunchKernelGGL((k_gemm_ksplit<B, 4, RB>), grid, dim3(256), 0, st, set, X, ldx, m, p.kb,
                        p.G, c.splits, c.kbps, part, tick);
   else if (per_wave >= 2)
@@ -606,7 +625,7 @@ template <int B>
 void launch_gemm_ksplit(const GemmPlan& p, const uint16_t* X, int64_t ldx, int m, TilesCfg c,
                         float* part, uint32_t* tick, hipStream_t st) {
   GemmSet set = p.set;
-  for (int i = 0; i < set.count; ++i) set.end[i] = p.end_tiles[i];
+  for (int i = 0; i < set.count; ++i) set.end[i] = c.dual ? c.gx : p.end_tiles[i];
   if (c.mb == 1) launch_gemm_ksplit_rb<B, 2>(set, p, X, ldx, m, c, part, tick, st);
   else launch_gemm_ksplit_rb<B, 1>(set, p, X, ldx, m, c, part, tick, st);
 }
@@ -632,7 +651,7 @@ bool skinny_by_ksplit(int64_t tiles, int kb, int bits) {
   if (const char* e = getenv("QLIN_TUNE_GEMM")) {
     int mb = -1, sp = 0;
     if (sscanf(e, "%d,%d", &mb, &sp) == 2 && sp >= 1) {
-      if (mb == 0) return true;
+      if (mb == 0 || mb == 2 || mb == 3) return true;   // the K-split kernel, forced
       if (mb == 16) return false;
     }
   }
@@ -647,6 +666,7 @@ bool skinny_by_ksplit(int64_t tiles, int kb, int bits) {
 // choice follows tiles_config for the equivalent two-matrix set.
 TilesCfg swiglu_config(int64_t tiles, int kb, int m, int64_t ws_bytes) {
   TilesCfg c;
+  c.dual = false;
   int want = 1;
   const int64_t cols2 = (tiles + 1) / 2;
   if (m <= 256) {
