@@ -1515,13 +1515,18 @@ __global__ __launch_bounds__(256) void k_gemm_tiles(
 // DUAL: one matrix, and a work-group covers its tiles 2x and 2x + 1 (grid.x
 // = tile pairs): each X fragment feeds twice the MFMAs, so a tall X tile over
 // few tiles moves half the X bytes per MFMA through L1.
-template <int BITS, int U, int RB, bool PAIR = false, bool DUAL = false>
+// CB = 1: a work-group covers one 32-row half of each tile (grid.x = half
+// tiles, half = x mod 2), twice the work-groups for a grid too small to fill
+// the chip.
+template <int BITS, int U, int RB, bool PAIR = false, bool DUAL = false, int CB = 2>
 __global__ __launch_bounds__(256) void k_gemm_ksplit(
     const GemmSet set, const uint16_t* __restrict__ X, int64_t ldx, int m, int kb, int G,
     int splits, int kbps, float* __restrict__ part, uint32_t* __restrict__ tickets) {
   constexpr int WPB = 2 * BITS;
   constexpr int HW = WPB / 2;                 // words of a half block
-  constexpr int NE = RB * 2048;              // elements of a wave's partial tile
+  constexpr int NE = RB * CB * 1024;         // elements of a wave's partial tile
+  static_assert(CB == 1 || CB == 2, "column blocks per tile");
+  static_assert(CB == 2 || !DUAL, "tile pairs take whole tiles");
   constexpr int NM = (PAIR || DUAL) ? 2 : 1; // tiles per work-group
   static_assert(!(PAIR && DUAL), "one of PAIR, DUAL");
   __shared__ float red[4][NE];
@@ -1530,11 +1535,13 @@ __global__ __launch_bounds__(256) void k_gemm_ksplit(
   const int c = lane & 31, h = lane >> 5;
   const GemmMat mat = gemm_mat(set, blockIdx.x);
   // tile of each of the NM products (DUAL: a tile past the matrix re-reads
-  // its last one and is not stored)
+  // its last one and is not stored); column block of cb = cb0 + cb
+  const int col = CB == 2 ? mat.col : mat.col >> 1;
+  const int cb0 = CB == 2 ? 0 : mat.col & 1;
   int tm[NM], tl[NM];
 #pragma unroll
   for (int mi = 0; mi < NM; ++mi) {
-    tm[mi] = DUAL ? 2 * mat.col + mi : mat.col;
+    tm[mi] = DUAL ? 2 * col + mi : col;
     tl[mi] = min(tm[mi], mat.tiles - 1);
   }
   const int m0 = blockIdx.y * 32 * RB;
@@ -1548,7 +1555,7 @@ __global__ __launch_bounds__(256) void k_gemm_ksplit(
     const int xr = m0 + 32 * rb + c;
     xrow[rb] = X + (int64_t)(xr < m ? xr : m0) * ldx + 32 * h;
   }
-  const uint32_t* wsrc[NM][2];
+  const uint32_t* wsrc[NM][CB];
   const uint16_t* ssrc[NM];
   const uint8_t* zsrc[NM];
 #pragma unroll
@@ -1558,24 +1565,24 @@ __global__ __launch_bounds__(256) void k_gemm_ksplit(
     ssrc[mi] = (PAIR ? set.scale[mi] : mat.scale) + mt;
     zsrc[mi] = (PAIR ? set.zero[mi] : mat.zero) + mt;
 #pragma unroll
-    for (int cb = 0; cb < 2; ++cb)
-      wsrc[mi][cb] = codes + ((int64_t)tl[mi] * kb * kTile + 32 * cb + c) * WPB;
+    for (int cb = 0; cb < CB; ++cb)
+      wsrc[mi][cb] = codes + ((int64_t)tl[mi] * kb * kTile + 32 * (cb0 + cb) + c) * WPB;
   }
-  f32x16 acc[NM][RB][2];
+  f32x16 acc[NM][RB][CB];
 #pragma unroll
   for (int mi = 0; mi < NM; ++mi)
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-      for (int cb = 0; cb < 2; ++cb)
+      for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[mi][rb][cb][r] = 0.f;
 
   for (int jb = j0 + wave; jb < j1; jb += 4 * U) {
     f16x8 xa[U][RB][4];
-    uint32_t wl[U][NM][2][HW];
-    uint16_t sr[U][NM][2];
-    int zc[U][NM][2];
+    uint32_t wl[U][NM][CB][HW];
+    uint16_t sr[U][NM][CB];
+    int zc[U][NM][CB];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int j = jb + 4 * u;
@@ -1590,10 +1597,10 @@ __global__ __launch_bounds__(256) void k_gemm_ksplit(
 #pragma unroll
       for (int mi = 0; mi < NM; ++mi)
 #pragma unroll
-        for (int cb = 0; cb < 2; ++cb) {
+        for (int cb = 0; cb < CB; ++cb) {
           load_half<BITS>(wsrc[mi][cb] + (int64_t)jj * kTile * WPB, h, wl[u][mi][cb]);
-          sr[u][mi][cb] = ssrc[mi][32 * cb + g * kTile];
-          zc[u][mi][cb] = zsrc[mi][32 * cb + g * kTile];
+          sr[u][mi][cb] = ssrc[mi][32 * (cb0 + cb) + g * kTile];
+          zc[u][mi][cb] = zsrc[mi][32 * (cb0 + cb) + g * kTile];
         }
     }
     if constexpr (U > 1 || PAIR) loads_issued();
@@ -1603,7 +1610,7 @@ __global__ __launch_bounds__(256) void k_gemm_ksplit(
 #pragma unroll
       for (int mi = 0; mi < NM; ++mi)
 #pragma unroll
-        for (int cb = 0; cb < 2; ++cb) {
+        for (int cb = 0; cb < CB; ++cb) {
           const DeqT<BITS> d = make_deq_b<BITS>(masked_scale(sr[u][mi][cb], valid), zc[u][mi][cb]);
 #pragma unroll
           for (int s = 0; s < 4; ++s) {
@@ -1616,7 +1623,7 @@ __global__ __launch_bounds__(256) void k_gemm_ksplit(
         }
     }
   }
-  // element e = 2048 rb + 1024 cb + 64 r + lane of a wave's accumulators
+  // element e = 1024 (CB rb + cb) + 64 r + lane of a wave's accumulators
   constexpr int PT = NE / 256;               // elements per thread
   float v[NM][PT];
 #pragma unroll
@@ -1625,10 +1632,10 @@ __global__ __launch_bounds__(256) void k_gemm_ksplit(
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-      for (int cb = 0; cb < 2; ++cb)
+      for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
         for (int r = 0; r < 16; ++r)
-          red[wave][2048 * rb + 1024 * cb + 64 * r + lane] = acc[mi][rb][cb][r];
+          red[wave][1024 * (CB * rb + cb) + 64 * r + lane] = acc[mi][rb][cb][r];
     __syncthreads();
 #pragma unroll
     for (int i = 0; i < PT; ++i) {
@@ -1668,9 +1675,9 @@ __global__ __launch_bounds__(256) void k_gemm_ksplit(
 #pragma unroll
   for (int i = 0; i < PT; ++i) {
     const int e = tid + 256 * i;
-    const int rb = e >> 11, cb = (e >> 10) & 1, r = (e >> 6) & 15, l = e & 63;
+    const int rb = (e >> 10) / CB, cb = (e >> 10) % CB, r = (e >> 6) & 15, l = e & 63;
     const int row = m0 + 32 * rb + 8 * (r >> 2) + 4 * (l >> 5) + (r & 3);
-    const int cl = 32 * cb + (l & 31);
+    const int cl = 32 * (cb0 + cb) + (l & 31);
     if (row >= m) continue;
     if constexpr (PAIR) {
       const int col = tm[0] * kTile + cl;

@@ -492,28 +492,34 @@ void launch_gemm_skinny(const GemmPlan& p, const uint16_t* X, int64_t ldx, int m
 // in flight at once; 64 X rows from 256 tiles up).  Above M = 256 a tall X
 // tile pays only when the grid is large.
 // mb = 0 / 1: k_gemm_ksplit with 32 / 64 X rows, gx in tiles (dual: in tile
-// pairs of a single matrix)
-struct TilesCfg { int mb, gx, gy, splits, kbps; bool dual; };
+// pairs of a single matrix; half: in 32-row halves of tiles)
+struct TilesCfg { int mb, gx, gy, splits, kbps; bool dual, half; };
 
 TilesCfg tiles_config(int64_t gx, int64_t tiles, int kb, int m, int count,
                       int64_t ws_bytes) {
   TilesCfg c;
   c.gx = (int)gx;
   c.dual = false;
+  c.half = false;
   int want = 1;
   if (m <= 256 && (tiles < 256 || m <= 16)) {
     // the K-split kernel: one 64-row W tile x 32 X rows per work-group; for
     // M > 16, K is split across work-groups (at most 8 ways) only when the
     // grid is under 256 work-groups, keeping at least 8 K-blocks per split
     c.mb = 0;
-    const int64_t groups = tiles * ((m + 31) / 32);
+    // a grid of under 128 work-groups runs over half tiles: twice the
+    // work-groups, no partial-sum round trip (measured at M = 8 and 128:
+    // Qwen2.5-0.5B q/k/v, o, down and Qwen3-8B k 15-25 % faster)
+    const int64_t groups0 = tiles * ((m + 31) / 32);
+    c.half = groups0 < 128;
+    const int64_t groups = c.half ? 2 * groups0 : groups0;
     if (m <= 16) {
       // M <= 16 (measured at M = 8 on the Qwen2.5-0.5B and Qwen3-8B shapes):
       // a work-group's K range is one or two rounds of loads already, so a
       // split mostly adds its partial-sum round trip; split only launches of
-      // under 32 work-groups, and very long K (about 48 K-blocks per split)
-      if (groups < 32) {
-        want = (int)((256 + groups - 1) / groups);
+      // under 64 work-groups, and very long K (about 48 K-blocks per split)
+      if (groups < 64) {
+        want = (int)((128 + groups - 1) / groups);
         if (want > 8) want = 8;
         if (want > kb / 8) want = kb / 8;
       } else if (kb >= 128) {
@@ -544,24 +550,26 @@ TilesCfg tiles_config(int64_t gx, int64_t tiles, int kb, int m, int count,
     c.dual = c.mb == 1;
   }
   // QLIN_TUNE_GEMM="mb,splits" overrides the choice (launch-shape sweeps;
-  // mb = 0 / 1: the K-split kernel, 2 / 3: the same with 64 / 32 X rows over
-  // tile pairs)
+  // mb = 0 / 1: the K-split kernel with 32 / 64 X rows, 2 / 3: the same with
+  // 64 / 32 X rows over tile pairs, 4 / 5: with 32 / 64 X rows over half tiles)
   if (const char* e = getenv("QLIN_TUNE_GEMM")) {
     int mb = 0, sp = 0;
     if (sscanf(e, "%d,%d", &mb, &sp) == 2 &&
-        (mb == 0 || mb == 1 || mb == 2 || mb == 3 || mb == 32 || mb == 64 || mb == 128) &&
-        sp >= 1) {
-      c.mb = mb == 2 ? 1 : mb == 3 ? 0 : mb;
+        ((mb >= 0 && mb <= 5) || mb == 32 || mb == 64 || mb == 128) && sp >= 1) {
+      c.mb = (mb == 2 || mb == 5) ? 1 : (mb == 3 || mb == 4) ? 0 : mb;
       c.dual = mb == 2 || mb == 3;
+      c.half = mb == 4 || mb == 5;
       want = sp < kb ? sp : kb;
     }
   }
   if (count > 1) c.dual = false;       // tile pairs of one matrix only
   if (want < 1) want = 1;
   const bool ks = c.mb <= 1;
-  if (ks) c.gx = (int)(c.dual ? (tiles + 1) / 2 : tiles);
+  if (!ks) c.dual = c.half = false;
+  if (ks) c.gx = (int)(c.dual ? (tiles + 1) / 2 : c.half ? 2 * tiles : tiles);
   const int rows = ks ? 32 * (c.mb + 1) : c.mb;
-  const int64_t wg_outputs = (int64_t)rows * (ks ? kTile * (c.dual ? 2 : 1) : 256);
+  const int64_t wg_outputs =
+      (int64_t)rows * (ks ? (c.dual ? 2 * kTile : c.half ? kTile / 2 : kTile) : 256);
   c.gy = (m + rows - 1) / rows;
   if ((int64_t)c.gx * c.gy > kMaxSplitTiles) want = 1;
   while (want > 1 && kCounterBytes + (int64_t)want * c.gy * c.gx * wg_outputs * 4 > ws_bytes)
@@ -574,8 +582,9 @@ TilesCfg tiles_config(int64_t gx, int64_t tiles, int kb, int m, int count,
 int64_t tiles_ws_bytes(int64_t gx, int64_t tiles, int kb, int m, int count) {
   const TilesCfg c = tiles_config(gx, tiles, kb, m, count, INT64_MAX);
   if (c.splits <= 1) return 0;
-  const int64_t wg_outputs = c.mb <= 1 ? 32 * (c.mb + 1) * kTile * (c.dual ? 2 : 1)
-                                       : (int64_t)c.mb * 256;
+  const int64_t wg_outputs =
+      c.mb <= 1 ? 32 * (c.mb + 1) * (c.dual ? 2 * kTile : c.half ? kTile / 2 : kTile)
+                : (int64_t)c.mb * 256;
   return kCounterBytes + (int64_t)c.splits * c.gy * c.gx * wg_outputs * 4;
 }
 
@@ -602,8 +611,18 @@ void launch_gemm_ksplit_rb(const GemmSet& set, const GemmPlan& p, const uint16_t
   // 64-row X tiles, whose X fragments take twice the registers)
   const int per_wave = (c.kbps + 3) / 4;
   const dim3 grid(c.gx, c.gy, c.splits);
-  if (c.dual) {   // tile pairs: two accumulator sets, so at most 2 blocks in flight
-                  // (1 with 64 X rows, to keep 2 waves per SIMD)
+  if (c.half) {   // half tiles: half the codes and accumulators per wave
+    if (per_wave >= 4 && RB == 1)
+      hipLaunchKernelGGL((k_gemm_ksplit<B, 4, RB, false, false, 1>), grid, dim3(256), 0, st, set,
+                         X, ldx, m, p.kb, p.G, c.splits, c.kbps, part, tick);
+    else if (per_wave >= 2)
+      hipLaunchKernelGGL((k_gemm_ksplit<B, 2, RB, false, false, 1>), grid, dim3(256), 0, st, set,
+                         X, ldx, m, p.kb, p.G, c.splits, c.kbps, part, tick);
+    else
+      hipLaunchKernelGGL((k_gemm_ksplit<B, 1, RB, false, false, 1>), grid, dim3(256), 0, st, set,
+                         X, ldx, m, p.kb, p.G, c.splits, c.kbps, part, tick);
+  } else if (c.dual) {   // tile pairs: two accumulator sets, so at most 2 blocks in flight
+                         // (1 with 64 X rows, to keep 2 waves per SIMD)
     if (RB == 1 && per_wave >= 2)
       hipLaunchKernelGGL((k_gemm_ksplit<B, 2, RB, false, true>), grid, dim3(256), 0, st, set, X,
                          ldx, m, p.kb, p.G, c.splits, c.kbps, part, tick);
@@ -625,7 +644,8 @@ template <int B>
 void launch_gemm_ksplit(const GemmPlan& p, const uint16_t* X, int64_t ldx, int m, TilesCfg c,
                         float* part, uint32_t* tick, hipStream_t st) {
   GemmSet set = p.set;
-  for (int i = 0; i < set.count; ++i) set.end[i] = c.dual ? c.gx : p.end_tiles[i];
+  for (int i = 0; i < set.count; ++i)
+    set.end[i] = c.dual ? c.gx : c.half ? 2 * p.end_tiles[i] : p.end_tiles[i];
   if (c.mb == 1) launch_gemm_ksplit_rb<B, 2>(set, p, X, ldx, m, c, part, tick, st);
   else launch_gemm_ksplit_rb<B, 1>(set, p, X, ldx, m, c, part, tick, st);
 }
@@ -642,20 +662,19 @@ void launch_gemm_tiles(const GemmPlan& p, const uint16_t* X, int64_t ldx, int m,
 constexpr int kSkinnyMaxM = 16;
 
 // M <= 16: the K-split kernel (measured 1.1-2.5x faster than the skinny one
-// on the Qwen2.5-0.5B and Qwen3-8B shapes at M = 8, int4), except for long K
-// over fewer than 32 tiles, where the skinny kernel's split is cheaper.
-// QLIN_TUNE_GEMM="0,splits" / "16,1" force the K-split / skinny kernel.  The
-// skinny kernel exists for 2, 3, 4 and 8 bits only.
+// on the Qwen2.5-0.5B and Qwen3-8B shapes at M = 8, int4; over half tiles it
+// also beats it on long K over few tiles, where the skinny kernel's split
+// used to be cheaper).  QLIN_TUNE_GEMM="16,1" forces the skinny kernel,
+// which exists for 2, 3, 4 and 8 bits only.
 bool skinny_by_ksplit(int64_t tiles, int kb, int bits) {
+  (void)tiles;
+  (void)kb;
   if (bits >= 5 && bits <= 7) return true;
   if (const char* e = getenv("QLIN_TUNE_GEMM")) {
     int mb = -1, sp = 0;
-    if (sscanf(e, "%d,%d", &mb, &sp) == 2 && sp >= 1) {
-      if (mb == 0 || mb == 2 || mb == 3) return true;   // the K-split kernel, forced
-      if (mb == 16) return false;
-    }
+    if (sscanf(e, "%d,%d", &mb, &sp) == 2 && sp >= 1 && mb == 16) return false;
   }
-  return !(tiles < 32 && kb >= 64);
+  return true;
 }
 
 
@@ -666,7 +685,7 @@ bool skinny_by_ksplit(int64_t tiles, int kb, int bits) {
 // choice follows tiles_config for the equivalent two-matrix set.
 TilesCfg swiglu_config(int64_t tiles, int kb, int m, int64_t ws_bytes) {
   TilesCfg c;
-  c.dual = false;
+  c.dual = c.half = false;
   int want = 1;
   const int64_t cols2 = (tiles + 1) / 2;
   if (m <= 256) {

@@ -413,9 +413,11 @@ def test_gemm_one_hot_fp16_exact(bits, m):
 # K-split GEMM launch shapes "0,splits" (32 X rows x one 64-row W tile per
 # work-group, its 4 waves splitting K), with and without a K split across
 # work-groups
-# "mb,splits": K-split with 32 (0) / 64 (1) X rows, and over tile pairs of
-# one matrix with 64 (2) / 32 (3) X rows (sets run these as 1 / 0)
-KSPLIT = ["0,1", "0,2", "0,5", "1,1", "1,3", "2,1", "2,3", "3,1", "3,2"]
+# "mb,splits": K-split with 32 (0) / 64 (1) X rows, over tile pairs of one
+# matrix with 64 (2) / 32 (3) X rows (sets run these as 1 / 0), and over half
+# tiles with 32 (4) / 64 (5) X rows
+KSPLIT = ["0,1", "0,2", "0,5", "1,1", "1,3", "2,1", "2,3", "3,1", "3,2", "4,1", "4,3", "5,1",
+          "5,2"]
 
 
 @pytest.mark.parametrize("bits", [2, 3, 4, 5, 6, 7, 8])
