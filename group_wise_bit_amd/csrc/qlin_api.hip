@@ -691,10 +691,24 @@ TilesCfg swiglu_config(int64_t tiles, int kb, int m, int64_t ws_bytes) {
   if (m <= 256) {
     c.mb = (2 * tiles < 256 || m <= 16) ? 0 : 1;
     if (c.mb == 0) {
-      // counted as for the two-matrix set: a pair work-group does the work
-      // of two of its work-groups
-      const int64_t groups = 2 * tiles * ((m + 31) / 32);
-      if (groups < 256) {
+      // under 512 pair work-groups: over half tiles (as many work-groups as
+      // the two-matrix set has, each loading X once for both matrices;
+      // measured at M = 8 and 128 on the Qwen2.5-0.5B, Qwen3-0.6B and
+      // Qwen3-8B pairs)
+      const int64_t pairs = tiles * ((m + 31) / 32);
+      c.half = pairs < 512;
+      // splits counted as for the two-matrix set, with its rules
+      const int64_t groups = 2 * pairs;
+      if (m <= 16) {
+        if (groups < 64) {
+          want = (int)((128 + groups - 1) / groups);
+          if (want > 8) want = 8;
+          if (want > kb / 8) want = kb / 8;
+        } else if (kb >= 128) {
+          want = kb / 48;
+          if (want > 8) want = 8;
+        }
+      } else if (groups < 256) {
         want = (int)((512 + groups - 1) / groups);
         if (want > 8) want = 8;
         if (want > kb / 8) want = kb / 8;
@@ -707,20 +721,24 @@ TilesCfg swiglu_config(int64_t tiles, int kb, int m, int64_t ws_bytes) {
       if (cols2 * ((m + 63) / 64) < 256) c.mb = 1;
     }
   }
-  // QLIN_TUNE_GEMM="mb,splits" overrides the choice (mb 32 runs as 64)
+  // QLIN_TUNE_GEMM="mb,splits" overrides the choice (mb 32 runs as 64; 4 / 5:
+  // the K-split pair over half tiles with 32 / 64 X rows)
   if (const char* e = getenv("QLIN_TUNE_GEMM")) {
     int mb = 0, sp = 0;
     if (sscanf(e, "%d,%d", &mb, &sp) == 2 &&
-        (mb == 0 || mb == 1 || mb == 32 || mb == 64 || mb == 128) && sp >= 1) {
-      c.mb = mb == 32 ? 64 : mb;
+        (mb == 0 || mb == 1 || mb == 4 || mb == 5 || mb == 32 || mb == 64 || mb == 128) &&
+        sp >= 1) {
+      c.mb = mb == 32 ? 64 : mb == 4 ? 0 : mb == 5 ? 1 : mb;
+      c.half = mb == 4 || mb == 5;
       want = sp < kb ? sp : kb;
     }
   }
   if (want < 1) want = 1;
   const bool ks = c.mb <= 1;
-  c.gx = (int)(ks ? tiles : cols2);
+  if (!ks) c.half = false;
+  c.gx = (int)(ks ? (c.half ? 2 * tiles : tiles) : cols2);
   const int rows = ks ? 32 * (c.mb + 1) : c.mb;
-  const int64_t wg_outputs = (int64_t)rows * (ks ? 2 * kTile : 256);
+  const int64_t wg_outputs = (int64_t)rows * (ks ? (c.half ? kTile : 2 * kTile) : 256);
   c.gy = (m + rows - 1) / rows;
   if ((int64_t)c.gx * c.gy > kMaxSplitTiles) want = 1;
   while (want > 1 && kCounterBytes + (int64_t)want * c.gy * c.gx * wg_outputs * 4 > ws_bytes)
@@ -734,7 +752,8 @@ int64_t swiglu_ws_bytes(int64_t tiles, int kb, int m) {
   const TilesCfg c = swiglu_config(tiles, kb, m, INT64_MAX);
   if (c.splits <= 1) return 0;
   const bool ks = c.mb <= 1;
-  const int64_t wg_outputs = ks ? 32 * (c.mb + 1) * 2 * kTile : (int64_t)c.mb * 256;
+  const int64_t wg_outputs =
+      ks ? 32 * (c.mb + 1) * (c.half ? kTile : 2 * kTile) : (int64_t)c.mb * 256;
   return kCounterBytes + (int64_t)c.splits * c.gy * c.gx * wg_outputs * 4;
 }
 
@@ -748,7 +767,20 @@ void launch_gemm_swiglu(const GemmSet& set, const uint16_t* X, int64_t ldx, int 
   else if (c.mb == 64)
     hipLaunchKernelGGL((k_gemm_lds<B, 64, 4, true>), grid, dim3(256), 0, st, set, X, ldx, m, kb,
                        G, c.splits, c.kbps, part, tick);
-  else if (c.mb == 1)
+  else if (c.half) {   // half tiles of both matrices
+    if (c.mb == 1)
+      hipLaunchKernelGGL((k_gemm_ksplit<B, 1, 2, true, false, 1>), grid, dim3(256), 0, st, set,
+                         X, ldx, m, kb, G, c.splits, c.kbps, part, tick);
+    else if ((c.kbps + 3) / 4 >= 4)
+      hipLaunchKernelGGL((k_gemm_ksplit<B, 4, 1, true, false, 1>), grid, dim3(256), 0, st, set,
+                         X, ldx, m, kb, G, c.splits, c.kbps, part, tick);
+    else if ((c.kbps + 3) / 4 >= 2)
+      hipLaunchKernelGGL((k_gemm_ksplit<B, 2, 1, true, false, 1>), grid, dim3(256), 0, st, set,
+                         X, ldx, m, kb, G, c.splits, c.kbps, part, tick);
+    else
+      hipLaunchKernelGGL((k_gemm_ksplit<B, 1, 1, true, false, 1>), grid, dim3(256), 0, st, set,
+                         X, ldx, m, kb, G, c.splits, c.kbps, part, tick);
+  } else if (c.mb == 1)
     hipLaunchKernelGGL((k_gemm_ksplit<B, 1, 2, true>), grid, dim3(256), 0, st, set, X, ldx, m,
                        kb, G, c.splits, c.kbps, part, tick);
   else if (B <= 4 && (c.kbps + 3) / 4 >= 4)   // (wider codes: 1 wave per SIMD at 4 blocks)

@@ -7,8 +7,9 @@ combination) against the CPU oracle.
 * One-hot X rows: g and u are then single dequantized weights rounded to fp16
   (the GEMM's operand rounding), so H must equal silu(g) * u of those fp16
   values to within the fp32 evaluation of silu and the product.
-* Every kernel form (K-split with 32 / 64 X rows, LDS pipeline with 64 / 128
-  X rows, with and without a K split across work-groups), ragged n (an odd
+* Every kernel form (K-split with 32 / 64 X rows, also over half tiles, LDS
+  pipeline with 64 / 128 X rows, with and without a K split across
+  work-groups), ragged n (an odd
   tile count leaves half of the last pair's work-group without a tile) and
   ragged m; reruns bitwise identical; either output alone gives the same
   values.
@@ -138,9 +139,11 @@ def test_gemm_swiglu_prefill_m2048(bits, monkeypatch):
     assert np.array_equal(hh.astype(np.float16).view(np.uint16), hh16.view(np.uint16))
 
 
-# "mb,splits": K-split with 32 (0) / 64 (1) X rows, LDS pipeline with 64 / 128
-# X rows (32 runs as 64), with and without a K split across work-groups
-FORCED = ["0,1", "0,3", "1,1", "1,2", "32,1", "64,1", "64,2", "128,1", "128,3"]
+# "mb,splits": K-split with 32 (0) / 64 (1) X rows, the same over half tiles
+# (4 / 5), LDS pipeline with 64 / 128 X rows (32 runs as 64), with and without
+# a K split across work-groups
+FORCED = ["0,1", "0,3", "1,1", "1,2", "4,1", "4,3", "5,1", "5,2", "32,1", "64,1", "64,2",
+          "128,1", "128,3"]
 
 
 @pytest.mark.parametrize("bits", [2, 3, 4, 5, 6, 7, 8])
