@@ -495,8 +495,10 @@ void launch_gemm_skinny(const GemmPlan& p, const uint16_t* X, int64_t ldx, int m
 // pairs of a single matrix; half: in 32-row halves of tiles)
 struct TilesCfg { int mb, gx, gy, splits, kbps; bool dual, half; };
 
-TilesCfg tiles_config(int64_t gx, int64_t tiles, int kb, int m, int count,
-                      int64_t ws_bytes) {
+// pairable: tile pairs stay within one matrix (one matrix, or every
+// matrix of the set has an even tile count)
+TilesCfg tiles_config(int64_t gx, int64_t tiles, int kb, int m, int count, bool pairable,
+                      int bits, int64_t ws_bytes) {
   TilesCfg c;
   c.gx = (int)gx;
   c.dual = false;
@@ -533,7 +535,18 @@ TilesCfg tiles_config(int64_t gx, int64_t tiles, int kb, int m, int count,
     }
   } else if (m <= 256) {
     c.mb = 1;                              // K-split kernel, 64 X rows
-  } else {
+  }
+  if (m > 16 && m <= 256 && pairable && bits <= 4 && kb >= 32 &&
+      tiles * ((m + 31) / 32) >= 384) {
+    // a large grid of long-K work-groups: 32 X rows over tile pairs, each X
+    // fragment feeding twice the MFMAs (Qwen3-8B int4 at M = 128: the gate/up
+    // set 61 -> 49 us, the q/k/v set 25 -> 20 us, gate alone 36 -> 32 us;
+    // wider codes, whose decode costs more, gain nothing)
+    c.mb = 0;
+    c.half = false;
+    c.dual = true;
+    want = 1;
+  } else if (m > 256) {
     // 128-row tiles when that already gives more work-groups than CUs (two
     // fit per CU), else 64 when that fills the chip; a smaller grid takes
     // the K-split kernel (64 X rows) for long K, 32-row tiles for short K
@@ -562,7 +575,7 @@ TilesCfg tiles_config(int64_t gx, int64_t tiles, int kb, int m, int count,
       want = sp < kb ? sp : kb;
     }
   }
-  if (count > 1) c.dual = false;       // tile pairs of one matrix only
+  if (!pairable) c.dual = false;       // tile pairs within one matrix only
   if (want < 1) want = 1;
   const bool ks = c.mb <= 1;
   if (!ks) c.dual = c.half = false;
@@ -579,8 +592,9 @@ TilesCfg tiles_config(int64_t gx, int64_t tiles, int kb, int m, int count,
   return c;
 }
 
-int64_t tiles_ws_bytes(int64_t gx, int64_t tiles, int kb, int m, int count) {
-  const TilesCfg c = tiles_config(gx, tiles, kb, m, count, INT64_MAX);
+int64_t tiles_ws_bytes(int64_t gx, int64_t tiles, int kb, int m, int count, bool pairable,
+                       int bits) {
+  const TilesCfg c = tiles_config(gx, tiles, kb, m, count, pairable, bits, INT64_MAX);
   if (c.splits <= 1) return 0;
   const int64_t wg_outputs =
       c.mb <= 1 ? 32 * (c.mb + 1) * (c.dual ? 2 * kTile : c.half ? kTile / 2 : kTile)
@@ -645,7 +659,9 @@ void launch_gemm_ksplit(const GemmPlan& p, const uint16_t* X, int64_t ldx, int m
                         float* part, uint32_t* tick, hipStream_t st) {
   GemmSet set = p.set;
   for (int i = 0; i < set.count; ++i)
-    set.end[i] = c.dual ? c.gx : c.half ? 2 * p.end_tiles[i] : p.end_tiles[i];
+    set.end[i] = c.dual   ? (p.end_tiles[i] + 1) / 2
+                 : c.half ? 2 * p.end_tiles[i]
+                          : p.end_tiles[i];
   if (c.mb == 1) launch_gemm_ksplit_rb<B, 2>(set, p, X, ldx, m, c, part, tick, st);
   else launch_gemm_ksplit_rb<B, 1>(set, p, X, ldx, m, c, part, tick, st);
 }
@@ -922,13 +938,15 @@ int64_t qlin_gemv_workspace_bytes(const qlin_weight* w) {
 int64_t gemm_set_ws_bytes(const qlin_weight* w, int count, int32_t m) {
   if (w == nullptr || count < 1 || count > kMaxMats || m < 1 || m > kMaxM) return 0;
   int64_t tiles = 0, cols4 = 0;
+  bool pairable = true;
   for (int i = 0; i < count; ++i) {
     if (check_weight(&w[i], false, false) != QLIN_OK || w[i].k != w[0].k) return 0;
     tiles += tiles_of(w[i].n);
     cols4 += (tiles_of(w[i].n) + 3) / 4;
+    if (count > 1 && tiles_of(w[i].n) % 2 != 0) pairable = false;
   }
   if (m > kSkinnyMaxM || skinny_by_ksplit(tiles, w[0].k / kBlock, w[0].bits))
-    return tiles_ws_bytes(cols4, tiles, w[0].k / kBlock, m, count);
+    return tiles_ws_bytes(cols4, tiles, w[0].k / kBlock, m, count, pairable, w[0].bits);
   return split_ws_bytes(tiles, w[0].k / kBlock, 16);
 }
 
@@ -1102,7 +1120,11 @@ qlin_status run_gemm(const GemmPlan& p, const uint16_t* X, int m, int64_t ld_x, 
       default: launch_gemm_skinny<8>(p, X, ld_x, m, part, tick, sp, stream); break;
     }
   } else {
-    const TilesCfg c = tiles_config(p.cols4, p.tiles, p.kb, m, p.set.count, workspace_bytes);
+    bool pairable = true;
+    for (int i = 0; p.set.count > 1 && i < p.set.count; ++i)
+      if ((p.end_tiles[i] - (i == 0 ? 0 : p.end_tiles[i - 1])) % 2 != 0) pairable = false;
+    const TilesCfg c = tiles_config(p.cols4, p.tiles, p.kb, m, p.set.count, pairable, p.bits,
+                                    workspace_bytes);
     float* part = c.splits > 1 ? reinterpret_cast<float*>(pbase) : nullptr;
     switch (p.bits) {
       case 2: launch_gemm_tiles<2>(p, X, ld_x, m, c, part, tick, stream); break;

@@ -554,6 +554,32 @@ def test_split_k_paths(bits):
     check_tol(Y2, x16, what, "nosplit gemm")
 
 
+@pytest.mark.parametrize("bits", [2, 3, 4, 5, 8])
+@pytest.mark.parametrize("cfg", ["2,1", "2,3", "3,1", "3,2"])
+def test_gemm_ksplit_pairable_set(bits, cfg, monkeypatch):
+    """A set whose matrices all have an even tile count (4, 2, 2: the
+    Qwen2.5-0.5B q/k/v form) runs over tile pairs: within tolerance, and one-hot
+    X rows reproduce every matrix's fp16-rounded columns exactly."""
+    monkeypatch.setenv("QLIN_TUNE_GEMM", cfg)
+    rng = np.random.default_rng([bits, 13])
+    k, m = 640, 90
+    mats = []
+    for n in (200, 128, 100):
+        w16 = synth.master_weights(rng, n, k)
+        qw, codes, s16, z = oracle_packed(w16, bits, 64)
+        mats.append((qw, oracle.dequantize(codes, s16, z, 64)))
+    x16 = synth.activations(rng, m, k)
+    say(f"gemm ksplit pairable set cfg={cfg} bits={bits}")
+    Ys = [host(y) for y in qlin.gemm_multi([q for q, _ in mats], dev(x16))]
+    for Y, (_, what) in zip(Ys, mats):
+        check_tol(Y, x16, what, f"pairable set {cfg}")
+    cols = (np.arange(m) * 37) % k
+    X = np.zeros((m, k), np.float16)
+    X[np.arange(m), cols] = 1
+    for Y, (_, what) in zip(qlin.gemm_multi([q for q, _ in mats], dev(X)), mats):
+        assert np.array_equal(host(Y).astype(np.float64), fp16_rne(what[:, cols].T))
+
+
 @pytest.mark.parametrize("bits", [3, 4, 6])
 def test_split_k_full_tiles(bits):
     """GEMV with K split across work-groups of whole 64-row tiles (many tiles,
