@@ -559,8 +559,9 @@ TilesCfg tiles_config(int64_t gx, int64_t tiles, int kb, int m, int count, bool 
     }
     // the K-split kernel over a tall M reads its X fragments through L1 for
     // every tile: over tile pairs each fragment feeds twice the MFMAs
-    // (Qwen2.5-0.5B down projection at M = 2048: 52 -> 38 us)
-    c.dual = c.mb == 1;
+    // (Qwen2.5-0.5B at M = 2048: down 52 -> 38 us, the q/k/v set 17.4 ->
+    // 16.5 us)
+    c.dual = c.mb <= 1;
   }
   // QLIN_TUNE_GEMM="mb,splits" overrides the choice (launch-shape sweeps;
   // mb = 0 / 1: the K-split kernel with 32 / 64 X rows, 2 / 3: the same with
