@@ -203,8 +203,10 @@ GemvCfg gemv_config(int64_t tiles, int kb, GemvKind kind, int bits, int64_t ws_b
       splits = 4;
     }
   } else if (tiles * kb <= 4096) {
-    rows = (pair || tiles >= 48) ? 16 : 8;
-    waves = (pair || kb >= 32) ? 16 : 8;
+    // (a gate/up pair of 64+ tiles: 8-row, 8-wave work-groups; Qwen2.5-0.5B
+    // gate/up 4.6 -> 4.4 us)
+    rows = ((pair && tiles < 64) || (!pair && tiles >= 48)) ? 16 : 8;
+    waves = ((pair && tiles < 64) || kb >= 32) ? 16 : 8;
     if (kb >= 128) splits = kb / 64;   // very long K over a few tiles
   } else {
     splits = kb >= 128 ? kb / 64 : kb / 16;
