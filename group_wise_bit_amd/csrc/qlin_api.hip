@@ -486,15 +486,18 @@ void launch_gemm_skinny(const GemmPlan& p, const uint16_t* X, int64_t ldx, int m
 }
 
 // Tiled-GEMM launch shape: work-group tile = MB rows of X x 256 rows of W
-// (four 64-row tiles), gx = work-group columns; or (mb = 0) the K-split
-// kernel, 32 or 64 rows of X x one 64-row tile.  Measured on MI355X
+// (four 64-row tiles), gx = work-group columns; or (mb = 0 / 1) the K-split
+// kernel, 32 or 64 rows of X x one 64-row tile, or x two adjacent tiles
+// (dual), or x one 32-row half of a tile (half).  Measured on MI355X
 // (graph-replayed launches over rotating cold weights, the Qwen2.5-0.5B and
 // Qwen3-8B layer shapes and q/k/v, gate/up sets, M = 8..2048, int4): up to
 // M = 256 the K-split kernel is 1.1-2x faster (all loads of a wave's K-blocks
-// in flight at once; 64 X rows from 256 tiles up).  Above M = 256 a tall X
-// tile pays only when the grid is large.
+// in flight at once; 64 X rows from 256 tiles up); half tiles double a grid
+// too small to fill the chip, tile pairs halve the X bytes per MFMA of a
+// large or tall one.  Above M = 256 a tall X tile pays only when the grid is
+// large.
 // mb = 0 / 1: k_gemm_ksplit with 32 / 64 X rows, gx in tiles (dual: in tile
-// pairs of a single matrix; half: in 32-row halves of tiles)
+// pairs; half: in 32-row halves of tiles)
 struct TilesCfg { int mb, gx, gy, splits, kbps; bool dual, half; };
 
 // pairable: tile pairs stay within one matrix (one matrix, or every
