@@ -352,12 +352,6 @@ __device__ __forceinline__ float silu(float g) {
 }
 
 // grid = (launch tiles, splits), block = WAVES waves; lane = row of the tile.
-// Plain: the WAVES waves of split s take the K-blocks j0+w, j0+w+WAVES, ... of
-// [j0, j1) (consecutive 128*bits-byte runs); y = the tile's dot products.
-// SWIGLU: waves [0, WAVES/2) do the gate tile, the others the up tile, and
-// the output is h = silu(gate . x) * (up . x), in fp32 (y[0]) and/or fp16
-// (h16, nearest even), either may be null.
-// grid = (launch tiles, splits), block = WAVES waves; lane = row of the tile.
 // The WAVES waves of split s take the K-blocks j0+w, j0+w+WAVES, ... of
 // [j0, j1) (consecutive 128*bits-byte runs).  Plain: y = the tile's dot
 // products.  SWIGLU: every wave does its blocks of the gate and the up tile
