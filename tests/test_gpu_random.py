@@ -123,3 +123,37 @@ def test_random_case(case, monkeypatch):
         else:
             _, H16 = qlin.gemm_swiglu(gate, up, dev(x16), want_h=False)
             swiglu_within(host(H16), x16, wg, wu, label)
+
+
+LARGE_M_CASES = 36
+
+
+@pytest.mark.parametrize("case", range(LARGE_M_CASES))
+def test_random_case_large_m(case, monkeypatch):
+    """Prefill sizes (M = 257 .. 2048), where the policy picks among the
+    LDS-pipeline, tiled and K-split GEMMs by grid size."""
+    monkeypatch.delenv("QLIN_TUNE_GEMM", raising=False)
+    rng = np.random.default_rng([98, case])
+    kind = ("gemm", "gemm_multi", "gemm_swiglu")[case % 3]
+    bits = int(rng.integers(2, 9))
+    k = 64 * int(rng.integers(1, 17))
+    g = k if rng.integers(0, 4) == 0 else 64
+    n = int(rng.integers(1, 1601))
+    m = int(rng.integers(257, 2049))
+    label = f"large-M case {case} {kind} bits={bits} group={g} n={n} k={k} m={m}"
+    say(label)
+    x16 = synth.activations(rng, m, k)
+    if kind == "gemm":
+        qw, what = packed(synth.master_weights(rng, n, k), bits, g)
+        within(host(qlin.gemm(qw, dev(x16))), x16, what, label)
+    elif kind == "gemm_multi":
+        ns = [n, int(rng.integers(1, 401))]
+        mats = [packed(synth.master_weights(rng, ni, k), bits, g) for ni in ns]
+        Ys = qlin.gemm_multi([q for q, _ in mats], dev(x16))
+        for i, (Y, (_, what)) in enumerate(zip(Ys, mats)):
+            within(host(Y), x16, what, f"{label} matrix {i} n={ns[i]}")
+    else:
+        gate, wg = packed(synth.master_weights(rng, n, k), bits, g)
+        up, wu = packed(synth.master_weights(rng, n, k), bits, g)
+        _, H16 = qlin.gemm_swiglu(gate, up, dev(x16), want_h=False)
+        swiglu_within(host(H16), x16, wg, wu, label)
