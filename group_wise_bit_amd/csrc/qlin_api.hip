@@ -7,10 +7,12 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <atomic>
 #include <vector>
 
 #include "../../include/qlin.h"
-#include "kernels.h"
+#include "../../include/qlin_tune.h"
+#include "plan.h"
 
 using namespace qlin;
 
@@ -18,7 +20,20 @@ namespace {
 
 thread_local int g_last_hip_error = 0;
 
-constexpr int kWaves = 4;                    // waves per work-group (GEMV, skinny GEMM)
+// Launch-shape overrides set through qlin_set_launch_override (sweeps and
+// tests only): per family one word, bit 63 = set, then three 16-bit fields.
+// One atomic load per call gives a consistent snapshot.
+std::atomic<uint64_t> g_override[2];
+
+bool launch_override(int family, int& a, int& b, int& c) {
+  const uint64_t v = g_override[family].load(std::memory_order_relaxed);
+  if ((v >> 63) == 0) return false;
+  a = (int)(v & 0xFFFFu);
+  b = (int)((v >> 16) & 0xFFFFu);
+  c = (int)((v >> 32) & 0xFFFFu);
+  return true;
+}
+
 constexpr int kMaxN = 1 << 24;
 constexpr int kMaxK = 1 << 20;
 constexpr int kMaxM = 1 << 20;
@@ -26,7 +41,6 @@ constexpr int kTargetGroups = 64;            // work-groups a split-K launch aim
 constexpr int kMinBlocksPerWave = 2;         // K-blocks per wave before splitting further
 
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
-inline int64_t tiles_of(int64_t n) { return (n + kTile - 1) / kTile; }
 
 struct Range { uintptr_t lo, hi; };
 inline Range range_of(const void* p, int64_t bytes) {
@@ -120,14 +134,7 @@ bool output_overlaps_weight(const qlin_weight* w, Range out) {
   return false;
 }
 
-// Split of the K-blocks over work-groups for the tile-per-work-group kernels.
-struct Split { int splits, kbps; };
 
-// Workspace layout: a fixed region of arrival counters (one uint32 per tile,
-// kCounterBytes, so calls of any shape can share one workspace without their
-// partial sums ever landing on another call's counters), then the fp32
-// partials [splits][part_rows][tiles*64].
-constexpr int64_t kCounterBytes = 65536;
 constexpr int64_t kMaxSplitTiles = kCounterBytes / 4;
 
 // Skinny-GEMM split: 4 waves per work-group, 2 K-blocks in flight per wave;
@@ -157,19 +164,7 @@ int64_t split_ws_bytes(int64_t tiles, int kb, int64_t part_rows) {
   return kCounterBytes + (int64_t)s.splits * part_rows * tiles * kTile * 4;
 }
 
-// GEMV launch kinds: packed codes (single matrix or a set), a gate/up pair
-// with the SwiGLU combination, fp16 masters re-rounded on the fly.
-enum class GemvKind { kPacked, kPair, kFused };
 
-// GEMV launch shape: work-groups of `rows` rows of one tile (64: a whole tile,
-// lane = row; 16 / 8: 4 / 8 lanes per row over slices of each block) per K
-// split; the waves of a work-group split the K-blocks of its split.  Each wave
-// keeps up to `unroll` blocks in flight, so the work-group is sized to cover
-// its K range in about one round of loads.
-struct GemvCfg {
-  int waves, splits, kbps, unroll;
-  int rows;
-};
 
 GemvCfg gemv_config(int64_t tiles, int kb, GemvKind kind, int bits, int64_t ws_bytes) {
   // Measured on MI355X (graph-replayed launches over rotating cold weights;
@@ -215,10 +210,10 @@ GemvCfg gemv_config(int64_t tiles, int kb, GemvKind kind, int bits, int64_t ws_b
   if (splits > kb) splits = kb;
   if (splits < 1) splits = 1;
   // QLIN_TUNE_GEMV="waves,splits[,rows]" overrides the choice (launch-shape sweeps)
-  if (const char* e = getenv("QLIN_TUNE_GEMV")) {
-    int w = 0, sp = 0, rw = 64;
-    const int got = sscanf(e, "%d,%d,%d", &w, &sp, &rw);
-    if (got >= 2 && (w == 4 || w == 8 || w == 16) && sp >= 1 && (rw == 8 || rw == 16 || rw == 64)) {
+  // a launch-shape override (qlin_set_launch_override: sweeps and tests)
+  {
+    int w, sp, rw;
+    if (launch_override(QLIN_TUNE_GEMV, w, sp, rw)) {
       waves = w;
       splits = sp < kb ? sp : kb;
       rows = rw;
@@ -247,26 +242,6 @@ int64_t gemv_ws_bytes(int64_t tiles, int kb, GemvKind kind, int bits) {
 }
 
 
-// One launch per kQuantBatch jobs (same bits, same group kind).
-template <int B>
-void launch_quant_batch(const QuantJob* jobs, int count, bool row, hipStream_t st) {
-  for (int c0 = 0; c0 < count; c0 += kQuantBatch) {
-    QuantBatch qb;
-    qb.count = count - c0 < kQuantBatch ? count - c0 : kQuantBatch;
-    int items = 0;
-    for (int i = 0; i < qb.count; ++i) {
-      qb.job[i] = jobs[c0 + i];
-      const int tiles = (int)tiles_of(qb.job[i].n);
-      items += row ? tiles : tiles * ((qb.job[i].kb + kWaves - 1) / kWaves);
-      qb.end[i] = items;
-    }
-    for (int i = qb.count; i < kQuantBatch; ++i) qb.end[i] = items;
-    if (row)
-      hipLaunchKernelGGL((k_quantize_row<B, kWaves>), dim3(items), dim3(kWaves * 64), 0, st, qb);
-    else
-      hipLaunchKernelGGL((k_quantize_g64<B, kWaves>), dim3(items), dim3(kWaves * 64), 0, st, qb);
-  }
-}
 
 qlin_status run_quant(const QuantJob* jobs, int count, int bits, bool row, hipStream_t st) {
   switch (bits) {
@@ -309,53 +284,7 @@ qlin_status check_quant_job(const uint16_t* w16, int64_t ld_w, int32_t n, int32_
   return QLIN_OK;
 }
 
-// Packed GEMV launch over a set of matrices (shared K, bits, group).
-struct PackedLaunch {
-  GemvSet set;
-  int tiles;          // launch tiles (grid.x)
-  int kb, G;
-  bool swiglu;
-  uint16_t* h16;
-};
 
-template <int B, int W, int U, bool SW>
-void launch_gemv_packed_w(const PackedLaunch& L, const f16x2* x2, float* part, uint32_t* tick,
-                          GemvCfg c, hipStream_t st) {
-  if (c.rows == 16)
-    hipLaunchKernelGGL((k_gemv_narrow<B, 4, W, U, SW>), dim3(4 * L.tiles, c.splits), dim3(W * 64),
-                       0, st, L.set, x2, part, tick, L.kb, L.G, c.splits, c.kbps, L.h16);
-  else if (c.rows == 8)
-    hipLaunchKernelGGL((k_gemv_narrow<B, 8, W, U, SW>), dim3(8 * L.tiles, c.splits), dim3(W * 64),
-                       0, st, L.set, x2, part, tick, L.kb, L.G, c.splits, c.kbps, L.h16);
-  else
-    hipLaunchKernelGGL((k_gemv_packed<B, W, U, SW>), dim3(L.tiles, c.splits), dim3(W * 64), 0, st,
-                       L.set, x2, part, tick, L.kb, L.G, c.splits, c.kbps, L.h16);
-}
-
-template <int B, bool SW>
-void launch_gemv_packed_s(const PackedLaunch& L, const f16x2* x2, float* part, uint32_t* tick,
-                          GemvCfg c, hipStream_t st) {
-  if (c.waves == 16) {
-    if (c.unroll == 1) launch_gemv_packed_w<B, 16, 1, SW>(L, x2, part, tick, c, st);
-    else if (c.unroll == 2) launch_gemv_packed_w<B, 16, 2, SW>(L, x2, part, tick, c, st);
-    else launch_gemv_packed_w<B, 16, (SW ? 2 : 4), SW>(L, x2, part, tick, c, st);
-  } else if (c.waves == 8) {
-    if (c.unroll == 1) launch_gemv_packed_w<B, 8, 1, SW>(L, x2, part, tick, c, st);
-    else if (c.unroll == 2) launch_gemv_packed_w<B, 8, 2, SW>(L, x2, part, tick, c, st);
-    else launch_gemv_packed_w<B, 8, (SW ? 2 : 4), SW>(L, x2, part, tick, c, st);
-  } else {
-    if (c.unroll == 1) launch_gemv_packed_w<B, 4, 1, SW>(L, x2, part, tick, c, st);
-    else if (c.unroll == 2) launch_gemv_packed_w<B, 4, 2, SW>(L, x2, part, tick, c, st);
-    else launch_gemv_packed_w<B, 4, (SW ? 2 : 4), SW>(L, x2, part, tick, c, st);
-  }
-}
-
-template <int B>
-void launch_gemv_packed(const PackedLaunch& L, const f16x2* x2, float* part, uint32_t* tick,
-                        GemvCfg c, hipStream_t st) {
-  if (L.swiglu) launch_gemv_packed_s<B, true>(L, x2, part, tick, c, st);
-  else launch_gemv_packed_s<B, false>(L, x2, part, tick, c, st);
-}
 
 PackedLaunch packed_launch(const qlin_weight* const* w, float* const* y, int count) {
   PackedLaunch L{};
@@ -396,59 +325,7 @@ qlin_status run_packed(const PackedLaunch& L, int bits, const uint16_t* x, void*
   return hip_status(hipGetLastError());
 }
 
-template <int B, int W, int U>
-void launch_gemv_fused_w(const qlin_weight* w, const f16x2* x2, float* y, float* part,
-                         uint32_t* tick, GemvCfg c, hipStream_t st) {
-  const int kb = w->k / kBlock;
-  const int G = (w->bits == 16 || w->group != w->k) ? kb : 1;
-  dim3 grid((unsigned)tiles_of(w->n), c.splits);
-  hipLaunchKernelGGL((k_gemv_fused<B, W, U>), grid, dim3(W * 64), 0, st,
-                     static_cast<const uint16_t*>(w->data), w->ld, w->scale, w->zero, x2, y, part,
-                     tick, w->n, kb, G, c.splits, c.kbps);
-}
 
-template <int B, int W, int U>
-void launch_gemv_fused_narrow_w(const qlin_weight* w, const f16x2* x2, float* y, float* part,
-                                uint32_t* tick, GemvCfg c, hipStream_t st) {
-  const int kb = w->k / kBlock;
-  const int G = (w->bits == 16 || w->group != w->k) ? kb : 1;
-  dim3 grid((unsigned)(8 * tiles_of(w->n)), c.splits);
-  hipLaunchKernelGGL((k_gemv_fused_narrow<B, W, U>), grid, dim3(W * 64), 0, st,
-                     static_cast<const uint16_t*>(w->data), w->ld, w->scale, w->zero, x2, y, part,
-                     tick, w->n, kb, G, c.splits, c.kbps);
-}
-
-// The 64-row fused kernel needs ~150 VGPRs: at most 8 waves (512 threads) per
-// work-group.
-template <int B>
-void launch_gemv_fused(const qlin_weight* w, const f16x2* x2, float* y, float* part,
-                       uint32_t* tick, GemvCfg c, hipStream_t st) {
-  if (c.rows == 8) {
-    if (c.waves == 16) {
-      if (c.unroll == 1) launch_gemv_fused_narrow_w<B, 16, 1>(w, x2, y, part, tick, c, st);
-      else launch_gemv_fused_narrow_w<B, 16, 2>(w, x2, y, part, tick, c, st);
-    } else if (c.waves == 8) {
-      if (c.unroll == 1) launch_gemv_fused_narrow_w<B, 8, 1>(w, x2, y, part, tick, c, st);
-      else launch_gemv_fused_narrow_w<B, 8, 2>(w, x2, y, part, tick, c, st);
-    } else {
-      if (c.unroll == 1) launch_gemv_fused_narrow_w<B, 4, 1>(w, x2, y, part, tick, c, st);
-      else launch_gemv_fused_narrow_w<B, 4, 2>(w, x2, y, part, tick, c, st);
-    }
-  } else if (c.waves >= 8) {
-    launch_gemv_fused_w<B, 8, 1>(w, x2, y, part, tick, c, st);
-  } else {
-    launch_gemv_fused_w<B, 4, 1>(w, x2, y, part, tick, c, st);
-  }
-}
-
-// A GEMM launch over a set of matrices (shared K, bits, group; one X).
-struct GemmPlan {
-  GemmSet set;
-  int64_t tiles;      // all 64-row tiles of the set
-  int cols4;          // all work-group columns of four tiles (tiled GEMM)
-  int kb, G, bits;
-  int end_tiles[kMaxMats], end_cols4[kMaxMats];   // set.end in either unit
-};
 
 GemmPlan gemm_plan(const qlin_weight* const* w, float* const* Y, const int64_t* ldy, int count,
                    bool skinny) {
@@ -477,28 +354,7 @@ GemmPlan gemm_plan(const qlin_weight* const* w, float* const* Y, const int64_t* 
   return p;
 }
 
-template <int B>
-void launch_gemm_skinny(const GemmPlan& p, const uint16_t* X, int64_t ldx, int m, float* part,
-                        uint32_t* tick, Split sp, hipStream_t st) {
-  hipLaunchKernelGGL((k_gemm_skinny<B, kWaves, 2>), dim3((unsigned)p.tiles, sp.splits),
-                     dim3(kWaves * 64), 0, st, p.set, X, ldx, m, part, tick, p.kb, p.G,
-                     sp.splits, sp.kbps);
-}
 
-// Tiled-GEMM launch shape: work-group tile = MB rows of X x 256 rows of W
-// (four 64-row tiles), gx = work-group columns; or (mb = 0 / 1) the K-split
-// kernel, 32 or 64 rows of X x one 64-row tile, or x two adjacent tiles
-// (dual), or x one 32-row half of a tile (half).  Measured on MI355X
-// (graph-replayed launches over rotating cold weights, the Qwen2.5-0.5B and
-// Qwen3-8B layer shapes and q/k/v, gate/up sets, M = 8..2048, int4): up to
-// M = 256 the K-split kernel is 1.1-2x faster (all loads of a wave's K-blocks
-// in flight at once; 64 X rows from 256 tiles up); half tiles double a grid
-// too small to fill the chip, tile pairs halve the X bytes per MFMA of a
-// large or tall one.  Above M = 256 a tall X tile pays only when the grid is
-// large.
-// mb = 0 / 1: k_gemm_ksplit with 32 / 64 X rows, gx in tiles (dual: in tile
-// pairs; half: in 32-row halves of tiles)
-struct TilesCfg { int mb, gx, gy, splits, kbps; bool dual, half; };
 
 // pairable: tile pairs stay within one matrix (one matrix, or every
 // matrix of the set has an even tile count)
@@ -571,10 +427,9 @@ TilesCfg tiles_config(int64_t gx, int64_t tiles, int kb, int m, int count, bool 
   // QLIN_TUNE_GEMM="mb,splits" overrides the choice (launch-shape sweeps;
   // mb = 0 / 1: the K-split kernel with 32 / 64 X rows, 2 / 3: the same with
   // 64 / 32 X rows over tile pairs, 4 / 5: with 32 / 64 X rows over half tiles)
-  if (const char* e = getenv("QLIN_TUNE_GEMM")) {
-    int mb = 0, sp = 0;
-    if (sscanf(e, "%d,%d", &mb, &sp) == 2 &&
-        ((mb >= 0 && mb <= 5) || mb == 32 || mb == 64 || mb == 128) && sp >= 1) {
+  {
+    int mb, sp, unused;
+    if (launch_override(QLIN_TUNE_GEMM, mb, sp, unused) && mb != 16) {
       c.mb = (mb == 2 || mb == 5) ? 1 : (mb == 3 || mb == 4) ? 0 : mb;
       c.dual = mb == 2 || mb == 3;
       c.half = mb == 4 || mb == 5;
@@ -608,78 +463,6 @@ int64_t tiles_ws_bytes(int64_t gx, int64_t tiles, int kb, int m, int count, bool
   return kCounterBytes + (int64_t)c.splits * c.gy * c.gx * wg_outputs * 4;
 }
 
-// MB = 32: the register-staged kernel (several work-groups per CU hide its
-// load latency); MB = 64 / 128: the LDS-DMA pipeline, 4 / 3 stages deep
-// (two work-groups per CU).
-template <int B, int MB>
-void launch_tiles_mb(const GemmPlan& p, const uint16_t* X, int64_t ldx, int m, TilesCfg c,
-                     float* part, uint32_t* tick, hipStream_t st) {
-  if constexpr (MB == 32)
-    hipLaunchKernelGGL((k_gemm_tiles<B, MB>), dim3(c.gx, c.gy, c.splits), dim3(256), 0, st,
-                       p.set, X, ldx, m, p.kb, p.G, c.splits, c.kbps, part, tick);
-  else
-    hipLaunchKernelGGL((k_gemm_lds<B, MB, (MB == 128 ? 3 : 4)>), dim3(c.gx, c.gy, c.splits),
-                       dim3(256), 0, st, p.set, X, ldx, m, p.kb, p.G, c.splits, c.kbps, part,
-                       tick);
-}
-
-template <int B, int RB>
-void launch_gemm_ksplit_rb(const GemmSet& set, const GemmPlan& p, const uint16_t* X,
-                           int64_t ldx, int m, TilesCfg c, float* part, uint32_t* tick,
-                           hipStream_t st) {
-  // blocks in flight per wave: the wave's share of the split, up to 4 (2 for
-  // 64-row X tiles, whose X fragments take twice the registers)
-  const int per_wave = (c.kbps + 3) / 4;
-  const dim3 grid(c.gx, c.gy, c.splits);
-  if (c.half) {   // half tiles: half the codes and accumulators per wave
-    if (per_wave >= 4 && RB == 1)
-      hipLaunchKernelGGL((k_gemm_ksplit<B, 4, RB, false, false, 1>), grid, dim3(256), 0, st, set,
-                         X, ldx, m, p.kb, p.G, c.splits, c.kbps, part, tick);
-    else if (per_wave >= 2)
-      hipLaunchKernelGGL((k_gemm_ksplit<B, 2, RB, false, false, 1>), grid, dim3(256), 0, st, set,
-                         X, ldx, m, p.kb, p.G, c.splits, c.kbps, part, tick);
-    else
-      hipLaunchKernelGGL((k_gemm_ksplit<B, 1, RB, false, false, 1>), grid, dim3(256), 0, st, set,
-                         X, ldx, m, p.kb, p.G, c.splits, c.kbps, part, tick);
-  } else if (c.dual) {   // tile pairs: two accumulator sets, so at most 2 blocks in flight
-                         // (1 with 64 X rows, to keep 2 waves per SIMD)
-    if (RB == 1 && per_wave >= 2)
-      hipLaunchKernelGGL((k_gemm_ksplit<B, 2, RB, false, true>), grid, dim3(256), 0, st, set, X,
-                         ldx, m, p.kb, p.G, c.splits, c.kbps, part, tick);
-    else
-      hipLaunchKernelGGL((k_gemm_ksplit<B, 1, RB, false, true>), grid, dim3(256), 0, st, set, X,
-                         ldx, m, p.kb, p.G, c.splits, c.kbps, part, tick);
-  } else if (per_wave >= 4 && RB == 1)
-    hipLaunchKernelGGL((k_gemm_ksplit<B, 4, RB>), grid, dim3(256), 0, st, set, X, ldx, m, p.kb,
-                       p.G, c.splits, c.kbps, part, tick);
-  else if (per_wave >= 2)
-    hipLaunchKernelGGL((k_gemm_ksplit<B, 2, RB>), grid, dim3(256), 0, st, set, X, ldx, m, p.kb,
-                       p.G, c.splits, c.kbps, part, tick);
-  else
-    hipLaunchKernelGGL((k_gemm_ksplit<B, 1, RB>), grid, dim3(256), 0, st, set, X, ldx, m, p.kb,
-                       p.G, c.splits, c.kbps, part, tick);
-}
-
-template <int B>
-void launch_gemm_ksplit(const GemmPlan& p, const uint16_t* X, int64_t ldx, int m, TilesCfg c,
-                        float* part, uint32_t* tick, hipStream_t st) {
-  GemmSet set = p.set;
-  for (int i = 0; i < set.count; ++i)
-    set.end[i] = c.dual   ? (p.end_tiles[i] + 1) / 2
-                 : c.half ? 2 * p.end_tiles[i]
-                          : p.end_tiles[i];
-  if (c.mb == 1) launch_gemm_ksplit_rb<B, 2>(set, p, X, ldx, m, c, part, tick, st);
-  else launch_gemm_ksplit_rb<B, 1>(set, p, X, ldx, m, c, part, tick, st);
-}
-
-template <int B>
-void launch_gemm_tiles(const GemmPlan& p, const uint16_t* X, int64_t ldx, int m, TilesCfg c,
-                       float* part, uint32_t* tick, hipStream_t st) {
-  if (c.mb <= 1) launch_gemm_ksplit<B>(p, X, ldx, m, c, part, tick, st);
-  else if (c.mb == 32) launch_tiles_mb<B, 32>(p, X, ldx, m, c, part, tick, st);
-  else if (c.mb == 64) launch_tiles_mb<B, 64>(p, X, ldx, m, c, part, tick, st);
-  else launch_tiles_mb<B, 128>(p, X, ldx, m, c, part, tick, st);
-}
 
 constexpr int kSkinnyMaxM = 16;
 
@@ -692,10 +475,8 @@ bool skinny_by_ksplit(int64_t tiles, int kb, int bits) {
   (void)tiles;
   (void)kb;
   if (bits >= 5 && bits <= 7) return true;
-  if (const char* e = getenv("QLIN_TUNE_GEMM")) {
-    int mb = -1, sp = 0;
-    if (sscanf(e, "%d,%d", &mb, &sp) == 2 && sp >= 1 && mb == 16) return false;
-  }
+  int mb, sp, unused;
+  if (launch_override(QLIN_TUNE_GEMM, mb, sp, unused) && mb == 16) return false;
   return true;
 }
 
@@ -745,11 +526,10 @@ TilesCfg swiglu_config(int64_t tiles, int kb, int m, int64_t ws_bytes) {
   }
   // QLIN_TUNE_GEMM="mb,splits" overrides the choice (mb 32 runs as 64; 4 / 5:
   // the K-split pair over half tiles with 32 / 64 X rows)
-  if (const char* e = getenv("QLIN_TUNE_GEMM")) {
-    int mb = 0, sp = 0;
-    if (sscanf(e, "%d,%d", &mb, &sp) == 2 &&
-        (mb == 0 || mb == 1 || mb == 4 || mb == 5 || mb == 32 || mb == 64 || mb == 128) &&
-        sp >= 1) {
+  {
+    int mb, sp, unused;
+    if (launch_override(QLIN_TUNE_GEMM, mb, sp, unused) &&
+        (mb == 0 || mb == 1 || mb == 4 || mb == 5 || mb == 32 || mb == 64 || mb == 128)) {
       c.mb = mb == 32 ? 64 : mb == 4 ? 0 : mb == 5 ? 1 : mb;
       c.half = mb == 4 || mb == 5;
       want = sp < kb ? sp : kb;
@@ -779,42 +559,6 @@ int64_t swiglu_ws_bytes(int64_t tiles, int kb, int m) {
   return kCounterBytes + (int64_t)c.splits * c.gy * c.gx * wg_outputs * 4;
 }
 
-template <int B>
-void launch_gemm_swiglu(const GemmSet& set, const uint16_t* X, int64_t ldx, int m, int kb, int G,
-                        TilesCfg c, float* part, uint32_t* tick, hipStream_t st) {
-  const dim3 grid(c.gx, c.gy, c.splits);
-  if (c.mb == 128)
-    hipLaunchKernelGGL((k_gemm_lds<B, 128, 3, true>), grid, dim3(256), 0, st, set, X, ldx, m, kb,
-                       G, c.splits, c.kbps, part, tick);
-  else if (c.mb == 64)
-    hipLaunchKernelGGL((k_gemm_lds<B, 64, 4, true>), grid, dim3(256), 0, st, set, X, ldx, m, kb,
-                       G, c.splits, c.kbps, part, tick);
-  else if (c.half) {   // half tiles of both matrices
-    if (c.mb == 1)
-      hipLaunchKernelGGL((k_gemm_ksplit<B, 1, 2, true, false, 1>), grid, dim3(256), 0, st, set,
-                         X, ldx, m, kb, G, c.splits, c.kbps, part, tick);
-    else if ((c.kbps + 3) / 4 >= 4)
-      hipLaunchKernelGGL((k_gemm_ksplit<B, 4, 1, true, false, 1>), grid, dim3(256), 0, st, set,
-                         X, ldx, m, kb, G, c.splits, c.kbps, part, tick);
-    else if ((c.kbps + 3) / 4 >= 2)
-      hipLaunchKernelGGL((k_gemm_ksplit<B, 2, 1, true, false, 1>), grid, dim3(256), 0, st, set,
-                         X, ldx, m, kb, G, c.splits, c.kbps, part, tick);
-    else
-      hipLaunchKernelGGL((k_gemm_ksplit<B, 1, 1, true, false, 1>), grid, dim3(256), 0, st, set,
-                         X, ldx, m, kb, G, c.splits, c.kbps, part, tick);
-  } else if (c.mb == 1)
-    hipLaunchKernelGGL((k_gemm_ksplit<B, 1, 2, true>), grid, dim3(256), 0, st, set, X, ldx, m,
-                       kb, G, c.splits, c.kbps, part, tick);
-  else if (B <= 4 && (c.kbps + 3) / 4 >= 4)   // (wider codes: 1 wave per SIMD at 4 blocks)
-    hipLaunchKernelGGL((k_gemm_ksplit<B, (B <= 4 ? 4 : 2), 1, true>), grid, dim3(256), 0, st,
-                       set, X, ldx, m, kb, G, c.splits, c.kbps, part, tick);
-  else if ((c.kbps + 3) / 4 >= 2)
-    hipLaunchKernelGGL((k_gemm_ksplit<B, 2, 1, true>), grid, dim3(256), 0, st, set, X, ldx, m,
-                       kb, G, c.splits, c.kbps, part, tick);
-  else
-    hipLaunchKernelGGL((k_gemm_ksplit<B, 1, 1, true>), grid, dim3(256), 0, st, set, X, ldx, m,
-                       kb, G, c.splits, c.kbps, part, tick);
-}
 
 }  // namespace
 
@@ -1093,10 +837,10 @@ qlin_status qlin_embed_rows(const qlin_weight* w, const int32_t* ids, int32_t co
   const int G = (w->group == w->k) ? 1 : kb;
   const uint32_t* codes = static_cast<const uint32_t*>(w->data);
   switch (w->bits) {
-#define QLIN_EMBED(B)                                                                         \
-    case B:                                                                                   \
-      hipLaunchKernelGGL((k_embed_rows<B>), dim3(count), dim3(256), 0, stream, codes, w->scale, \
-                         w->zero, ids, w->n, kb, G, out16, out32, ld_out);                    \
+#define QLIN_EMBED(B)                                                                        \
+    case B:                                                                                  \
+      launch_embed_rows<B>(codes, w->scale, w->zero, ids, count, w->n, kb, G, out16, out32,  \
+                           ld_out, stream);                                                  \
       break;
     QLIN_EMBED(2)
     QLIN_EMBED(3)
@@ -1132,14 +876,18 @@ qlin_status run_gemm(const GemmPlan& p, const uint16_t* X, int m, int64_t ld_x, 
     const TilesCfg c = tiles_config(p.cols4, p.tiles, p.kb, m, p.set.count, pairable, p.bits,
                                     workspace_bytes);
     float* part = c.splits > 1 ? reinterpret_cast<float*>(pbase) : nullptr;
+    // launch columns of each matrix in the chosen kernel's unit: four-tile
+    // columns for the tiled kernels (the K-split launcher sets its own)
+    GemmPlan q = p;
+    for (int i = 0; i < q.set.count; ++i) q.set.end[i] = c.mb >= 32 ? p.end_cols4[i] : p.end_tiles[i];
     switch (p.bits) {
-      case 2: launch_gemm_tiles<2>(p, X, ld_x, m, c, part, tick, stream); break;
-      case 3: launch_gemm_tiles<3>(p, X, ld_x, m, c, part, tick, stream); break;
-      case 4: launch_gemm_tiles<4>(p, X, ld_x, m, c, part, tick, stream); break;
-      case 5: launch_gemm_tiles<5>(p, X, ld_x, m, c, part, tick, stream); break;
-      case 6: launch_gemm_tiles<6>(p, X, ld_x, m, c, part, tick, stream); break;
-      case 7: launch_gemm_tiles<7>(p, X, ld_x, m, c, part, tick, stream); break;
-      default: launch_gemm_tiles<8>(p, X, ld_x, m, c, part, tick, stream); break;
+      case 2: launch_gemm_tiles<2>(q, X, ld_x, m, c, part, tick, stream); break;
+      case 3: launch_gemm_tiles<3>(q, X, ld_x, m, c, part, tick, stream); break;
+      case 4: launch_gemm_tiles<4>(q, X, ld_x, m, c, part, tick, stream); break;
+      case 5: launch_gemm_tiles<5>(q, X, ld_x, m, c, part, tick, stream); break;
+      case 6: launch_gemm_tiles<6>(q, X, ld_x, m, c, part, tick, stream); break;
+      case 7: launch_gemm_tiles<7>(q, X, ld_x, m, c, part, tick, stream); break;
+      default: launch_gemm_tiles<8>(q, X, ld_x, m, c, part, tick, stream); break;
     }
   }
   return hip_status(hipGetLastError());
@@ -1260,6 +1008,25 @@ qlin_status qlin_gemm_swiglu(const qlin_weight* gate, const qlin_weight* up, con
     default: launch_gemm_swiglu<8>(set, X, ld_x, m, kb, G, c, part, tick, stream); break;
   }
   return hip_status(hipGetLastError());
+}
+
+qlin_status qlin_set_launch_override(int32_t family, const int32_t* params) {
+  if (family != QLIN_TUNE_GEMV && family != QLIN_TUNE_GEMM) return QLIN_ERR_SHAPE;
+  if (params == nullptr) {
+    g_override[family].store(0, std::memory_order_relaxed);
+    return QLIN_OK;
+  }
+  const int a = params[0], b = params[1], c = family == QLIN_TUNE_GEMV ? params[2] : 0;
+  if (b < 1 || b > 0xFFFF) return QLIN_ERR_SHAPE;
+  if (family == QLIN_TUNE_GEMV) {
+    if (!(a == 4 || a == 8 || a == 16) || !(c == 8 || c == 16 || c == 64)) return QLIN_ERR_SHAPE;
+  } else if (!((a >= 0 && a <= 5) || a == 16 || a == 32 || a == 64 || a == 128)) {
+    return QLIN_ERR_SHAPE;
+  }
+  g_override[family].store((1ull << 63) | (uint64_t)(uint32_t)a | ((uint64_t)(uint32_t)b << 16) |
+                               ((uint64_t)(uint32_t)c << 32),
+                           std::memory_order_relaxed);
+  return QLIN_OK;
 }
 
 }  // extern "C"

@@ -35,6 +35,9 @@ EXPORTS = (
     "qlin_quantize_batch", "qlin_gemm_multi_workspace_bytes", "qlin_gemm_multi",
     "qlin_gemm_swiglu_workspace_bytes", "qlin_gemm_swiglu",
 )
+# include/qlin_tune.h (launch-shape sweeps and tests only)
+TUNE_EXPORTS = ("qlin_set_launch_override",)
+TUNE_FAMILIES = {"gemv": 0, "gemm": 1}
 
 
 class QlinError(RuntimeError):
@@ -117,6 +120,8 @@ def _lib() -> ctypes.CDLL:
         lib.qlin_gemm_swiglu_workspace_bytes.restype = i64
         lib.qlin_gemm_swiglu.argtypes = [wp, wp, vp, i32, i64, vp, vp, i64, vp, i64, vp]
         lib.qlin_gemm_swiglu.restype = ctypes.c_int
+        lib.qlin_set_launch_override.argtypes = [i32, ctypes.POINTER(i32)]
+        lib.qlin_set_launch_override.restype = ctypes.c_int
         _LIB = lib
     return _LIB
 
@@ -133,6 +138,45 @@ def _check(status: int, where: str) -> None:
 
 def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
     return None if t is None else t.data_ptr()
+
+
+def _need_out(t: torch.Tensor, dtype: torch.dtype, device: torch.device, rows: int, cols: int,
+              name: str) -> None:
+    """An output the library writes (it cannot see buffer sizes): the right
+    dtype, on the inputs' device, unit-stride rows, room for rows x cols
+    (rows = 0: a vector of cols elements)."""
+    if not isinstance(t, torch.Tensor) or t.dtype != dtype:
+        raise TypeError(f"{name} must be a {dtype} tensor")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, the inputs on {device}")
+    if rows == 0:
+        if not t.is_contiguous() or t.numel() < cols:
+            raise ValueError(f"{name} must be contiguous with at least {cols} elements")
+        return
+    if t.dim() != 2 or t.stride(1) != 1 or t.shape[0] < rows or t.shape[1] < cols:
+        raise ValueError(f"{name} must be 2-D [>= {rows}, >= {cols}] with contiguous rows, "
+                         f"got shape {tuple(t.shape)} strides {t.stride()}")
+
+
+def _need_x(w: "QWeight", x: torch.Tensor) -> None:
+    if x.dtype != torch.float16 or x.numel() != w.k or not x.is_contiguous():
+        raise TypeError(f"x must be a contiguous float16 tensor of k = {w.k} elements")
+
+
+def set_launch_override(family: str, cfg=None) -> None:
+    """qlin_set_launch_override (include/qlin_tune.h): force the launch shape of
+    every later GEMV ("gemv": waves, splits[, rows]) or GEMM ("gemm": form,
+    splits) call, or restore the library's own choice (cfg None).  cfg is a
+    tuple or a "a,b[,c]" string.  For launch-shape sweeps and tests."""
+    fam = TUNE_FAMILIES[family]
+    if cfg is None:
+        _check(_lib().qlin_set_launch_override(fam, None), "qlin_set_launch_override")
+        return
+    vals = [int(v) for v in cfg.split(",")] if isinstance(cfg, str) else [int(v) for v in cfg]
+    if family == "gemv" and len(vals) == 2:
+        vals.append(64)
+    arr = (ctypes.c_int32 * 3)(*(vals + [0] * (3 - len(vals))))
+    _check(_lib().qlin_set_launch_override(fam, arr), "qlin_set_launch_override")
 
 
 def _stream() -> int:
@@ -235,10 +279,10 @@ def workspace(nbytes: int, device: torch.device) -> Optional[torch.Tensor]:
 
 def gemv(w: QWeight, x: torch.Tensor, y: Optional[torch.Tensor] = None,
          ws: Optional[torch.Tensor] = "auto") -> torch.Tensor:
-    if x.dtype != torch.float16 or x.numel() != w.k or not x.is_contiguous():
-        raise TypeError("x must be a contiguous float16 tensor of k elements")
+    _need_x(w, x)
     if y is None:
         y = torch.empty(w.n, dtype=torch.float32, device=x.device)
+    _need_out(y, torch.float32, x.device, 0, w.n, "y")
     ws_struct = w.c_struct()
     if isinstance(ws, str):
         need = int(_lib().qlin_gemv_workspace_bytes(ctypes.byref(ws_struct)))
@@ -257,6 +301,7 @@ def gemm(w: QWeight, X: torch.Tensor, Y: Optional[torch.Tensor] = None,
     m = X.shape[0]
     if Y is None:
         Y = torch.empty(m, w.n, dtype=torch.float32, device=X.device)
+    _need_out(Y, torch.float32, X.device, m, w.n, "Y")
     ws_struct = w.c_struct()
     if isinstance(ws, str):
         need = int(_lib().qlin_gemm_workspace_bytes(ctypes.byref(ws_struct), m))
@@ -272,12 +317,16 @@ def gemv_multi(ws_list: Sequence[QWeight], x: torch.Tensor,
                ys: Optional[Sequence[torch.Tensor]] = None,
                ws: Optional[torch.Tensor] = "auto") -> List[torch.Tensor]:
     """qlin_gemv_multi: y_i = W_i . x for up to 4 packed weights sharing x, one launch."""
-    if x.dtype != torch.float16 or not x.is_contiguous():
-        raise TypeError("x must be a contiguous float16 tensor")
     count = len(ws_list)
+    for w in ws_list:
+        _need_x(w, x)
     arr = (QlinWeightC * max(count, 1))(*[w.c_struct() for w in ws_list])
     if ys is None:
         ys = [torch.empty(w.n, dtype=torch.float32, device=x.device) for w in ws_list]
+    if len(ys) != count:
+        raise ValueError("one output per weight")
+    for i, (w, y) in enumerate(zip(ws_list, ys)):
+        _need_out(y, torch.float32, x.device, 0, w.n, f"ys[{i}]")
     yp = (ctypes.c_void_p * max(count, 1))(*[y.data_ptr() for y in ys])
     if isinstance(ws, str):
         need = int(_lib().qlin_gemv_multi_workspace_bytes(arr, count))
@@ -293,12 +342,16 @@ def gemv_swiglu(gate: QWeight, up: QWeight, x: torch.Tensor,
                 ws: Optional[torch.Tensor] = "auto", want_h: bool = True,
                 want_h16: bool = True) -> Tuple[Optional[torch.Tensor], Optional[torch.Tensor]]:
     """qlin_gemv_swiglu: h = silu(gate . x) * (up . x), fp32 and/or fp16, one launch."""
-    if x.dtype != torch.float16 or not x.is_contiguous():
-        raise TypeError("x must be a contiguous float16 tensor")
+    _need_x(gate, x)
+    _need_x(up, x)
     if h is None and want_h:
         h = torch.empty(gate.n, dtype=torch.float32, device=x.device)
     if h16 is None and want_h16:
         h16 = torch.empty(gate.n, dtype=torch.float16, device=x.device)
+    if h is not None:
+        _need_out(h, torch.float32, x.device, 0, gate.n, "h")
+    if h16 is not None:
+        _need_out(h16, torch.float16, x.device, 0, gate.n, "h16")
     g, u = gate.c_struct(), up.c_struct()
     if isinstance(ws, str):
         need = int(_lib().qlin_gemv_swiglu_workspace_bytes(ctypes.byref(g)))
@@ -368,6 +421,12 @@ def gemm_multi(ws_list: Sequence[QWeight], X: torch.Tensor,
     m, count = X.shape[0], len(ws_list)
     if Ys is None:
         Ys = [torch.empty(m, w.n, dtype=torch.float32, device=X.device) for w in ws_list]
+    if len(Ys) != count:
+        raise ValueError("one output per weight")
+    for i, (w, Y) in enumerate(zip(ws_list, Ys)):
+        if X.shape[1] != w.k:
+            raise TypeError(f"X has {X.shape[1]} columns, weight {i} k = {w.k}")
+        _need_out(Y, torch.float32, X.device, m, w.n, f"Ys[{i}]")
     arr = (QlinWeightC * max(count, 1))(*[w.c_struct() for w in ws_list])
     yp = (ctypes.c_void_p * max(count, 1))(*[y.data_ptr() for y in Ys])
     ld = (ctypes.c_int64 * max(count, 1))(*[y.stride(0) for y in Ys])
@@ -394,9 +453,13 @@ def gemm_swiglu(gate: QWeight, up: QWeight, X: torch.Tensor,
         H = torch.empty(m, gate.n, dtype=torch.float32, device=X.device)
     if H16 is None and want_h16:
         H16 = torch.empty(m, gate.n, dtype=torch.float16, device=X.device)
+    if X.shape[1] != gate.k or X.shape[1] != up.k:
+        raise TypeError("X must have k columns")
+    if H is not None:
+        _need_out(H, torch.float32, X.device, m, gate.n, "H")
+    if H16 is not None:
+        _need_out(H16, torch.float16, X.device, m, gate.n, "H16")
     outs = [t for t in (H, H16) if t is not None]
-    if any(t.dim() != 2 or t.stride(1) != 1 for t in outs):
-        raise TypeError("H and H16 must be 2-D with contiguous rows")
     ld = outs[0].stride(0) if outs else gate.n
     if any(t.stride(0) != ld for t in outs):
         raise ValueError("H and H16 must share one row stride")

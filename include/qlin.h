@@ -23,6 +23,10 @@
  * the calling thread's last HIP error code.  All pointers must be 16-byte
  * aligned device pointers.  A call that fails validation returns an error
  * before touching the GPU.  Output buffers must not overlap any input.
+ * Under HIP stream (graph) capture a call records its kernel launches with the
+ * pointers it was given: every buffer a captured call addresses (codes,
+ * scales, zeros, x, outputs, workspace) must stay allocated at the same
+ * address for as long as the graph may be replayed.
  *
  * ---------------------------------------------------------------------------
  * Packed-code layout ("tiled"):

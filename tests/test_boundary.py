@@ -340,3 +340,87 @@ def test_workspace_queries(lib):
     assert lib.qlin_gemv_multi_workspace_bytes(pair, 0) == 0
     assert lib.qlin_gemv_multi_workspace_bytes(weights(big, weight(k=256)), 2) == 0
     assert lib.qlin_gemv_swiglu_workspace_bytes(ctypes.byref(big)) > 65536
+
+
+TUNE_HEADER = os.path.join(ROOT, "include", "qlin_tune.h")
+
+
+def test_tune_header_exports(lib):
+    text = re.sub(r"/\*.*?\*/", "", open(TUNE_HEADER).read(), flags=re.S)
+    declared = sorted(set(re.findall(r"\b(qlin_[a-z0-9_]+)\s*\(", text)))
+    assert declared == sorted(qlin.TUNE_EXPORTS)
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_launch_override_validation(lib):
+    """The sweep/test override is validated on the host; NULL clears it."""
+    def ov(fam, vals):
+        arr = None if vals is None else (ctypes.c_int32 * 3)(*vals)
+        return lib.qlin_set_launch_override(fam, arr)
+    assert ov(0, (16, 2, 64)) == OK
+    assert ov(0, None) == OK
+    assert ov(0, (12, 1, 64)) == SHAPE      # waves
+    assert ov(0, (16, 0, 64)) == SHAPE      # splits
+    assert ov(0, (16, 1, 32)) == SHAPE      # rows
+    assert ov(1, (0, 1, 0)) == OK
+    assert ov(1, (128, 3, 0)) == OK
+    assert ov(1, (16, 1, 0)) == OK
+    assert ov(1, (7, 1, 0)) == SHAPE
+    assert ov(1, (96, 1, 0)) == SHAPE
+    assert ov(1, None) == OK
+    assert ov(2, (16, 1, 64)) == SHAPE
+    qlin.set_launch_override("gemv", "8,2")     # rows default to whole tiles
+    qlin.set_launch_override("gemv", None)
+    with pytest.raises(qlin.QlinError):
+        qlin.set_launch_override("gemm", (9, 1))
+
+
+def _cpu_weight(n=128, k=128, bits=4):
+    t = oracle.n_tiles(n) * 64
+    return qlin.QWeight(n, k, bits, 64, qlin.FMT_PACKED,
+                        torch.zeros(qlin.packed_bytes(n, k, bits) // 4, dtype=torch.int32),
+                        torch.zeros(t * (k // 64), dtype=torch.float16),
+                        torch.zeros(t * (k // 64), dtype=torch.uint8))
+
+
+def test_binding_refuses_bad_outputs_before_any_launch():
+    """The C ABI cannot see buffer sizes: the binding checks every output
+    (dtype, device, unit-stride rows, room) and every x length first."""
+    w = _cpu_weight()
+    x = torch.zeros(128, dtype=torch.float16)
+    with pytest.raises(TypeError):
+        qlin.gemv(w, torch.zeros(64, dtype=torch.float16))
+    with pytest.raises(TypeError):
+        qlin.gemv(w, x, torch.zeros(128, dtype=torch.float16))
+    with pytest.raises(ValueError):
+        qlin.gemv(w, x, torch.zeros(127, dtype=torch.float32))
+    with pytest.raises(ValueError):
+        qlin.gemv(w, x, torch.zeros(128, dtype=torch.float32, device="meta"))
+    with pytest.raises(ValueError):
+        qlin.gemv(w, x, torch.zeros(256, dtype=torch.float32)[::2])
+    X = torch.zeros(8, 128, dtype=torch.float16)
+    with pytest.raises(ValueError):
+        qlin.gemm(w, X, torch.zeros(8, 127, dtype=torch.float32))
+    with pytest.raises(ValueError):
+        qlin.gemm(w, X, torch.zeros(7, 128, dtype=torch.float32))
+    with pytest.raises(TypeError):
+        qlin.gemm(w, X, torch.zeros(8, 128, dtype=torch.float16))
+    with pytest.raises(ValueError):
+        qlin.gemm(w, X, torch.zeros(128, 8, dtype=torch.float32).t())
+    with pytest.raises(TypeError):
+        qlin.gemv_multi([w, w], torch.zeros(64, dtype=torch.float16))
+    with pytest.raises(ValueError):
+        qlin.gemv_multi([w, w], x, [torch.zeros(128), torch.zeros(100)])
+    with pytest.raises(TypeError):
+        qlin.gemv_swiglu(w, w, x, None, torch.zeros(128, dtype=torch.float32))
+    with pytest.raises(ValueError):
+        qlin.gemv_swiglu(w, w, x, torch.zeros(64, dtype=torch.float32), None)
+    with pytest.raises(TypeError):
+        qlin.gemv_swiglu(w, w, torch.zeros(127, dtype=torch.float16))
+    with pytest.raises(ValueError):
+        qlin.gemm_multi([w], X, [torch.zeros(8, 64, dtype=torch.float32)])
+    with pytest.raises(ValueError):
+        qlin.gemm_swiglu(w, w, X, None, torch.zeros(4, 128, dtype=torch.float16))
+    with pytest.raises(TypeError):
+        qlin.gemm_swiglu(w, w, X, torch.zeros(8, 128, dtype=torch.float16), None)

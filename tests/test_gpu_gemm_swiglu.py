@@ -92,8 +92,8 @@ DEFAULT_CASES = [
 @pytest.mark.parametrize("bits", [2, 3, 4, 5, 6, 7, 8])
 @pytest.mark.parametrize("group", [64, "K"])
 @pytest.mark.parametrize("n,k,m", DEFAULT_CASES)
-def test_gemm_swiglu(bits, group, n, k, m, monkeypatch):
-    monkeypatch.delenv("QLIN_TUNE_GEMM", raising=False)
+def test_gemm_swiglu(bits, group, n, k, m, launch_override):
+    launch_override("gemm", None)
     g = k if group == "K" else group
     rng = np.random.default_rng([81, bits, n, k, m])
     gate, wg = packed(synth.master_weights(rng, n, k), bits, g)
@@ -113,10 +113,10 @@ def test_gemm_swiglu(bits, group, n, k, m, monkeypatch):
 
 
 @pytest.mark.parametrize("bits", [3, 4, 8])
-def test_gemm_swiglu_prefill_m2048(bits, monkeypatch):
+def test_gemm_swiglu_prefill_m2048(bits, launch_override):
     """The Qwen2.5-0.5B gate/up shape at M = 2048: the LDS pipeline with
     128-row X tiles; sampled rows checked against the oracle."""
-    monkeypatch.delenv("QLIN_TUNE_GEMM", raising=False)
+    launch_override("gemm", None)
     n, k, m = 4864, 896, 2048
     rng = np.random.default_rng([82, bits])
     gate, wg = packed(synth.master_weights(rng, n, k), bits, 64)
@@ -149,8 +149,8 @@ FORCED = ["0,1", "0,3", "1,1", "1,2", "4,1", "4,3", "5,1", "5,2", "32,1", "64,1"
 @pytest.mark.parametrize("bits", [2, 3, 4, 5, 6, 7, 8])
 @pytest.mark.parametrize("cfg", FORCED)
 @pytest.mark.parametrize("n,k,m", [(130, 640, 150), (256, 192, 70), (64, 1024, 3)])
-def test_gemm_swiglu_forms(bits, cfg, n, k, m, monkeypatch):
-    monkeypatch.setenv("QLIN_TUNE_GEMM", cfg)
+def test_gemm_swiglu_forms(bits, cfg, n, k, m, launch_override):
+    launch_override("gemm", cfg)
     rng = np.random.default_rng([83, bits, n, k, m])
     gate, wg = packed(synth.master_weights(rng, n, k), bits, 64)
     up, wu = packed(synth.master_weights(rng, n, k), bits, 64)
@@ -165,10 +165,10 @@ def test_gemm_swiglu_forms(bits, cfg, n, k, m, monkeypatch):
     check_one_hot(gate, up, wg, wu, k, cfg, rng)
 
 
-def test_gemm_swiglu_strided_outputs(monkeypatch):
+def test_gemm_swiglu_strided_outputs(launch_override):
     """H and H16 with a row stride above n (ld_h = n + 24): the padding is
     left untouched, the rows hold what the packed call gives."""
-    monkeypatch.delenv("QLIN_TUNE_GEMM", raising=False)
+    launch_override("gemm", None)
     n, k, m = 200, 192, 300
     rng = np.random.default_rng(84)
     gate, wg = packed(synth.master_weights(rng, n, k), 4, 64)
@@ -184,9 +184,9 @@ def test_gemm_swiglu_strided_outputs(monkeypatch):
     assert np.all(hp[:, n:] == 7.0) and np.all(h16p[:, n:] == 3.0)
 
 
-def test_gemm_swiglu_extremes(monkeypatch):
+def test_gemm_swiglu_extremes(launch_override):
     """Large |g|: silu saturates to g (g >> 0) and to -0 (g << 0) without nan."""
-    monkeypatch.delenv("QLIN_TUNE_GEMM", raising=False)
+    launch_override("gemm", None)
     rng = np.random.default_rng(85)
     n, k, m = 256, 256, 40
     gate, wg = packed(synth.master_weights(rng, n, k) * np.float16(40), 8, 64)

@@ -127,10 +127,10 @@ ROW_WIDTHS = ["16,1,64", "8,1,16", "16,1,8", "4,3,8", "8,2,16", "8,3,64"]
 @pytest.mark.parametrize("bits", [3, 4, 6])
 @pytest.mark.parametrize("cfg", ROW_WIDTHS)
 @pytest.mark.parametrize("ns,k", [((200, 64, 1, 130), 192), ((896, 128, 128), 896)])
-def test_gemv_multi_row_widths(bits, cfg, ns, k, monkeypatch):
+def test_gemv_multi_row_widths(bits, cfg, ns, k, launch_override):
     """Sets of matrices at every work-group width: each output within its
     matrix's tolerance; one-hot x exact."""
-    monkeypatch.setenv("QLIN_TUNE_GEMV", cfg)
+    launch_override("gemv", cfg)
     rng = np.random.default_rng([75, bits, k, len(ns)])
     mats = [packed(synth.master_weights(rng, n, k), bits, 64) for n in ns]
     x16 = synth.activations(rng, 1, k)[0]
@@ -146,8 +146,8 @@ def test_gemv_multi_row_widths(bits, cfg, ns, k, monkeypatch):
 @pytest.mark.parametrize("bits", [3, 4, 6])
 @pytest.mark.parametrize("cfg", ROW_WIDTHS)
 @pytest.mark.parametrize("n,k", [(130, 192), (200, 1024)])
-def test_gemv_swiglu_row_widths(bits, cfg, n, k, monkeypatch):
-    monkeypatch.setenv("QLIN_TUNE_GEMV", cfg)
+def test_gemv_swiglu_row_widths(bits, cfg, n, k, launch_override):
+    launch_override("gemv", cfg)
     rng = np.random.default_rng([76, bits, n, k])
     gate, wg = packed(synth.master_weights(rng, n, k), bits, 64)
     up, wu = packed(synth.master_weights(rng, n, k), bits, 64)

@@ -163,11 +163,11 @@ ROW_WIDTHS = ["16,1,64", "8,1,16", "16,1,8", "4,3,8", "8,2,16"]
 @pytest.mark.parametrize("group", [64, "K"])
 @pytest.mark.parametrize("shape", [(200, 192), (130, 4096), (1, 64), (896, 896)])
 @pytest.mark.parametrize("cfg", ROW_WIDTHS)
-def test_gemv_row_widths(bits, group, shape, cfg, monkeypatch):
+def test_gemv_row_widths(bits, group, shape, cfg, launch_override):
     """Every work-group width of the packed GEMV: within tolerance, and one-hot
     x at positions covering every slice of the first and last block reproduces
     the dequantized column exactly."""
-    monkeypatch.setenv("QLIN_TUNE_GEMV", cfg)
+    launch_override("gemv", cfg)
     n, k = shape
     g = k if group == "K" else 64
     say(f"gemv packed cfg={cfg} bits={bits} group={g} shape={shape}")
@@ -188,15 +188,15 @@ def test_gemv_row_widths(bits, group, shape, cfg, monkeypatch):
 @pytest.mark.parametrize("group", [64, "K"])
 @pytest.mark.parametrize("shape", [(200, 4864), (70, 8192), (896, 4864)])
 @pytest.mark.parametrize("cfg", [None, "16,1,8", "16,1,16"])
-def test_gemv_narrow_long_k(bits, group, shape, cfg, monkeypatch):
+def test_gemv_narrow_long_k(bits, group, shape, cfg, launch_override):
     """16-wave 8- and 16-row work-groups over 65..128 K-blocks, where each wave
     takes two rounds of loads (the Qwen2.5-0.5B down projection, k = 4864,
     takes this form by default): within tolerance, and one-hot x in the first
     and last blocks gives the dequantized column exactly."""
     if cfg is None:
-        monkeypatch.delenv("QLIN_TUNE_GEMV", raising=False)
+        launch_override("gemv", None)
     else:
-        monkeypatch.setenv("QLIN_TUNE_GEMV", cfg)
+        launch_override("gemv", cfg)
     n, k = shape
     g = k if group == "K" else 64
     say(f"gemv narrow long-k cfg={cfg} bits={bits} group={g} shape={shape}")
@@ -289,11 +289,11 @@ FUSED_WIDTHS = ["8,1,64", "4,4,64", "8,1,8", "16,2,8", "4,3,8"]
 @pytest.mark.parametrize("bits", [2, 3, 4, 8, 16])
 @pytest.mark.parametrize("shape", [(200, 192), (130, 4096), (1, 64)])
 @pytest.mark.parametrize("cfg", FUSED_WIDTHS)
-def test_gemv_fused_row_widths(bits, shape, cfg, monkeypatch):
+def test_gemv_fused_row_widths(bits, shape, cfg, launch_override):
     """The fused kernel at every work-group width and split: within tolerance,
     one-hot x at positions covering every 8-weight slice of the first and last
     block exact."""
-    monkeypatch.setenv("QLIN_TUNE_GEMV", cfg)
+    launch_override("gemv", cfg)
     n, k = shape
     say(f"gemv fused cfg={cfg} bits={bits} shape={shape}")
     rng = np.random.default_rng([n, k, bits, 9])
@@ -317,10 +317,10 @@ def test_gemv_fused_row_widths(bits, shape, cfg, monkeypatch):
 
 @pytest.mark.parametrize("bits", [2, 3, 4, 5, 6, 7, 8])
 @pytest.mark.parametrize("cfg", ["8,1,64", "8,1,8"])
-def test_gemv_fused_edge_groups_widths(bits, cfg, monkeypatch):
+def test_gemv_fused_edge_groups_widths(bits, cfg, launch_override):
     """Edge-case groups (ties, clamps, constant, one-signed) through both
     fused kernels: one-hot x over all 256 columns, exact."""
-    monkeypatch.setenv("QLIN_TUNE_GEMV", cfg)
+    launch_override("gemv", cfg)
     rng = np.random.default_rng(520 + bits)
     w16 = synth.edge_groups(bits, rng, n_rows=64, k=256)
     say(f"gemv fused edge groups cfg={cfg} bits={bits}")
@@ -333,11 +333,11 @@ def test_gemv_fused_edge_groups_widths(bits, cfg, monkeypatch):
 
 
 @pytest.mark.parametrize("cfg", ["8,1,64", "8,1,8"])
-def test_gemv_fused_scale_sweep_all_columns(cfg, monkeypatch):
+def test_gemv_fused_scale_sweep_all_columns(cfg, launch_override):
     """Every finite fp16 weight spread over all 64 columns of a block (so every
     lane slice of the narrow kernel sees them), 8-bit, zero 128, six scales,
     read back column by column through one-hot x."""
-    monkeypatch.setenv("QLIN_TUNE_GEMV", cfg)
+    launch_override("gemv", cfg)
     allw = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16).view(np.float16)
     allw = allw[np.isfinite(allw)]
     n = (allw.size + 63) // 64
@@ -373,9 +373,9 @@ def test_gemm(bits, m):
 
 @pytest.mark.parametrize("bits", [2, 3, 4, 5, 6, 7, 8])
 @pytest.mark.parametrize("m", [1, 5, 16])
-def test_gemm_skinny_forced(bits, m, monkeypatch):
+def test_gemm_skinny_forced(bits, m, launch_override):
     """The skinny (M <= 16) kernel, forced: within tolerance and one-hot exact."""
-    monkeypatch.setenv("QLIN_TUNE_GEMM", "16,1")
+    launch_override("gemm", "16,1")
     n, k = 200, 640
     rng = np.random.default_rng([bits, m, 13])
     w16 = synth.master_weights(rng, n, k)
@@ -425,11 +425,11 @@ KSPLIT = ["0,1", "0,2", "0,5", "1,1", "1,3", "2,1", "2,3", "3,1", "3,2", "4,1", 
 @pytest.mark.parametrize("m,n,k,group", [(1, 200, 192, 64), (5, 130, 1600, 64), (16, 64, 896, "K"),
                                          (17, 200, 192, 64), (100, 130, 1600, 64),
                                          (128, 320, 896, "K"), (256, 64, 4096, 64)])
-def test_gemm_ksplit(bits, cfg, m, n, k, group, monkeypatch):
+def test_gemm_ksplit(bits, cfg, m, n, k, group, launch_override):
     """The K-split GEMM within tolerance on ragged M and N, per-group and
     per-channel scales, and one-hot X rows reproduce fp16-rounded dequantized
     columns exactly (every decoded weight of the columns hit)."""
-    monkeypatch.setenv("QLIN_TUNE_GEMM", cfg)
+    launch_override("gemm", cfg)
     g = k if group == "K" else 64
     rng = np.random.default_rng([m, n, k, bits, 11])
     w16 = synth.master_weights(rng, n, k)
@@ -447,10 +447,10 @@ def test_gemm_ksplit(bits, cfg, m, n, k, group, monkeypatch):
 
 @pytest.mark.parametrize("bits", [3, 4, 6])
 @pytest.mark.parametrize("cfg", KSPLIT)
-def test_gemm_ksplit_sets_and_workspace(bits, cfg, monkeypatch):
+def test_gemm_ksplit_sets_and_workspace(bits, cfg, launch_override):
     """A ragged set of three matrices in one K-split launch, an explicit
     workspace reused twice (counters re-armed, partial region scratch)."""
-    monkeypatch.setenv("QLIN_TUNE_GEMM", cfg)
+    launch_override("gemm", cfg)
     rng = np.random.default_rng([bits, 12])
     k, m = 1024, 72
     mats = []
@@ -556,11 +556,11 @@ def test_split_k_paths(bits):
 
 @pytest.mark.parametrize("bits", [2, 3, 4, 5, 8])
 @pytest.mark.parametrize("cfg", ["2,1", "2,3", "3,1", "3,2"])
-def test_gemm_ksplit_pairable_set(bits, cfg, monkeypatch):
+def test_gemm_ksplit_pairable_set(bits, cfg, launch_override):
     """A set whose matrices all have an even tile count (4, 2, 2: the
     Qwen2.5-0.5B q/k/v form) runs over tile pairs: within tolerance, and one-hot
     X rows reproduce every matrix's fp16-rounded columns exactly."""
-    monkeypatch.setenv("QLIN_TUNE_GEMM", cfg)
+    launch_override("gemm", cfg)
     rng = np.random.default_rng([bits, 13])
     k, m = 640, 90
     mats = []
@@ -606,13 +606,13 @@ def test_split_k_full_tiles(bits):
 @pytest.mark.parametrize("m,n,k", [(128, 896, 4864), (100, 192, 4096), (256, 1024, 2048),
                                    (40, 300, 1600)])
 @pytest.mark.parametrize("cfg", [None, "32,3"])
-def test_gemm_tiles_split_k(bits, m, n, k, cfg, monkeypatch):
+def test_gemm_tiles_split_k(bits, m, n, k, cfg, launch_override):
     """GEMM with K split across work-groups (uneven last split, tiles past n in
     the last work-group; the default K-split kernel and the 32-row tiled one)
     equals the unsplit launch to tolerance, re-arms its counters, and ignores
     whatever the partial region held before."""
     if cfg is not None:
-        monkeypatch.setenv("QLIN_TUNE_GEMM", cfg)
+        launch_override("gemm", cfg)
     rng = np.random.default_rng([61, bits, m, n, k])
     w16 = synth.master_weights(rng, n, k)
     X = synth.activations(rng, m, k)

@@ -64,9 +64,9 @@ def swiglu_within(h16, x16, wg, wu, label):
 
 
 @pytest.mark.parametrize("case", range(CASES))
-def test_random_case(case, monkeypatch):
-    monkeypatch.delenv("QLIN_TUNE_GEMV", raising=False)
-    monkeypatch.delenv("QLIN_TUNE_GEMM", raising=False)
+def test_random_case(case, launch_override):
+    launch_override("gemv", None)
+    launch_override("gemm", None)
     rng = np.random.default_rng([97, case])
     kind = KINDS[case % len(KINDS)]
     bits = int(rng.integers(2, 9))
@@ -129,10 +129,10 @@ LARGE_M_CASES = 36
 
 
 @pytest.mark.parametrize("case", range(LARGE_M_CASES))
-def test_random_case_large_m(case, monkeypatch):
+def test_random_case_large_m(case, launch_override):
     """Prefill sizes (M = 257 .. 2048), where the policy picks among the
     LDS-pipeline, tiled and K-split GEMMs by grid size."""
-    monkeypatch.delenv("QLIN_TUNE_GEMM", raising=False)
+    launch_override("gemm", None)
     rng = np.random.default_rng([98, case])
     kind = ("gemm", "gemm_multi", "gemm_swiglu")[case % 3]
     bits = int(rng.integers(2, 9))
