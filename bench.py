@@ -68,8 +68,12 @@ import time
 import numpy as np
 
 HBM_PEAK_GBS = 8000.0
+HEADLINE = "q8_step_int4"
 FP16_MFMA_PEAK_TFLOPS = 2500.0
 ROTATE = 4
+C1_CALLS = 64
+PEAK_READ_BYTES = 4 << 30
+PEAK_MFMA_ITERS = 4096
 HERE = os.path.dirname(os.path.abspath(__file__))
 
 
@@ -79,7 +83,7 @@ def parse():
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--sections", default="decode,qwen3_8b,qwen3_06b")
+    p.add_argument("--sections", default="decode,qwen3_8b,qwen3_06b,peaks")
     p.add_argument("--phases", default="all",
                    help="comma list of stages to run (default: all of the chosen sections)")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
@@ -295,7 +299,19 @@ def build_decode(torch, qlin, synth, dev, ws, phases, state):
     if "embed_gather" in phases:
         staged["embed_gather"] = per_rotation(lambda r: [lambda w=lm8[r]: qlin.embed_rows(w, ids)])
 
-    hold = (masters, xs, ys, packed, scratch, meta, fused, X, Y, Yg, lm8, ids, y_lm)
+    # the single 896x896 int4 g64 GEMV (seed 0): 64 back-to-back calls on the
+    # same weight from one graph (the weight stays in L2: a latency figure)
+    c1 = None
+    if "c1_gemv_latency" in phases:
+        w0, x0 = synth.single_gemv_case(0)
+        c1w = qlin.quantize(torch.from_numpy(w0).to(dev), 4, 64)
+        c1x = torch.from_numpy(x0).to(dev)
+        c1y = torch.empty(896, dtype=torch.float32, device=dev)
+        c1 = (c1w, c1x, c1y)
+        staged["c1_gemv_latency"] = capture_calls(torch, [[
+            lambda: qlin.gemv(c1w, c1x, c1y, ws=ws) for _ in range(C1_CALLS)]])
+
+    hold = (masters, xs, ys, packed, scratch, meta, fused, X, Y, Yg, lm8, ids, y_lm, c1)
 
     def run(name):
         assert hold is not None       # every buffer the graphs address stays alive
@@ -342,6 +358,9 @@ def build_decode(torch, qlin, synth, dev, ws, phases, state):
               4 * shapes[lm_idx][2], 1, HBM_PEAK_GBS, "hbm", "k_gemv_packed<8>"),
         Phase("embed_gather", run, "GB/s", 896 + 14 * 3 + 2 * 896 + 4, 1, HBM_PEAK_GBS, "hbm",
               "k_embed_rows<8> (one token; latency)"),
+        Phase("c1_gemv_latency", run, "GB/s", C1_CALLS * (wbytes(896, 896, 4, 64) + 2 * 896 +
+                                                          4 * 896), C1_CALLS, HBM_PEAK_GBS,
+              "latency", "896x896 int4 g64 GEMV, seed 0 (L2-resident; us per call)"),
     ]
     return [p for p in out if p.name in phases], shapes
 
@@ -416,12 +435,56 @@ def build_qwen3_8b(torch, qlin, synth, dev, ws, phases):
         m8_steps[b] = capture_calls(torch, [calls])[0]
         m8_bytes[b] = nbytes
 
-    hold = (packed, xs, ys, X, Y, Y8, H8)
+    # the step's gate/up SwiGLU launches alone (the dominant kernel of the
+    # decode step: 52 % of its bytes), timed on their own for the roofline
+    pair_graphs, pair_bytes = {}, {}
+    Hp = torch.empty(n_of["gate"], dtype=torch.float16, device=dev)
+    for b in (4, 3, 2):
+        if f"q8_pair_int{b}" not in phases:
+            continue
+        calls, nbytes = [], 0
+        for l in layers:
+            wg, wu = packed[b][idx[(l, "gate")]], packed[b][idx[(l, "up")]]
+            x = xs[idx[(l, "gate")]]
+            calls.append(lambda wg=wg, wu=wu, x=x: qlin.gemv_swiglu(wg, wu, x, None, Hp, ws=ws,
+                                                                    want_h=False))
+            nbytes += 2 * wbytes(wg.n, wg.k, b, 64) + 2 * wg.k + 2 * wg.n
+        pair_graphs[b] = capture_calls(torch, [calls])[0]
+        pair_bytes[b] = nbytes
+
+    # prefill at M = 128 grouped like the decode step: per layer q/k/v (one
+    # launch), o, gate/up with the SwiGLU epilogue (fp16 H), down reading H
+    Y128 = {nm: torch.empty(128, n_of[nm], dtype=torch.float32, device=dev)
+            for nm in ("q", "k", "v", "o", "down")}
+    H128 = torch.empty(128, n_of["gate"], dtype=torch.float16, device=dev)
+    p128_steps = {}
+    for b in (4, 3):
+        if f"q8_prefill_step_m128_int{b}" not in phases:
+            continue
+        calls = []
+        for l in layers:
+            w = {nm: packed[b][idx[(l, nm)]] for nm in ("q", "k", "v", "o", "gate", "up", "down")}
+            k1 = w["q"].k
+            calls += [
+                lambda w=w, k1=k1: qlin.gemm_multi([w["q"], w["k"], w["v"]], X[128][:, :k1],
+                                                   [Y128["q"], Y128["k"], Y128["v"]], ws=ws),
+                lambda w=w, k1=k1: qlin.gemm(w["o"], X[128][:, :k1], Y128["o"], ws=ws),
+                lambda w=w, k1=k1: qlin.gemm_swiglu(w["gate"], w["up"], X[128][:, :k1], None,
+                                                    H128, ws=ws, want_h=False),
+                lambda w=w: qlin.gemm(w["down"], H128, Y128["down"], ws=ws),
+            ]
+        p128_steps[b] = capture_calls(torch, [calls])[0]
+
+    hold = (packed, xs, ys, X, Y, Y8, H8, Hp, Y128, H128)
 
     def run(name):
         assert hold is not None       # every buffer the graphs address stays alive
         b = int(name[-1])
-        if "m8_step" in name:
+        if "prefill_step" in name:
+            p128_steps[b].replay()
+        elif "pair" in name:
+            pair_graphs[b].replay()
+        elif "m8_step" in name:
             m8_steps[b].replay()
         elif "step" in name:
             steps[b].replay()
@@ -437,7 +500,13 @@ def build_qwen3_8b(torch, qlin, synth, dev, ws, phases):
         out.append(Phase(f"q8_decode_int{b}", run, "GB/s",
                          sum(wbytes(n, k, b, 64) + 2 * k + 4 * n for (_, _, n, k) in shapes),
                          252, HBM_PEAK_GBS, "hbm", f"k_gemv_packed<{b}> + k_gemv_narrow<{b}>"))
+        out.append(Phase(f"q8_pair_int{b}", run, "GB/s", pair_bytes.get(b, 0), 36, HBM_PEAK_GBS,
+                         "hbm", f"gate/up SwiGLU pair GEMV, 12288x4096 x 2, int{b} (36 launches)"))
     for b in (4, 3):
+        out.append(Phase(f"q8_prefill_step_m128_int{b}", run, "TFLOP/s",
+                         sum(2 * 128 * n * k for (_, _, n, k) in shapes), 144,
+                         FP16_MFMA_PEAK_TFLOPS, "mfma",
+                         f"q/k/v set, o, gate/up+SwiGLU pair, down at M = 128, int{b}"))
         out.append(Phase(f"q8_m8_int{b}", run, "GB/s",
                          sum(wbytes(n, k, b, 64) + 16 * k + 32 * n for (_, _, n, k) in shapes),
                          252, HBM_PEAK_GBS, "hbm", f"k_gemm_ksplit<{b}>"))
@@ -524,6 +593,47 @@ def build_qwen3_06b(torch, qlin, synth, dev, ws, phases):
     return [p for p in out if p.name in phases]
 
 
+def build_peaks(torch, dev, phases):
+    """The achieved peaks: a streaming read of 4 GiB (HBM) and a matrix-core
+    loop with no memory traffic (fp16 MFMA), from libqlin_peaks.so."""
+    import ctypes
+    lib = ctypes.CDLL(os.path.join(HERE, "group_wise_bit_amd", "libqlin_peaks.so"))
+    lib.qlin_peak_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
+                                          ctypes.c_void_p]
+    lib.qlin_peak_mfma.argtypes = [ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
+    lib.qlin_peak_mfma_waves.restype = ctypes.c_int64
+    src = torch.ones(PEAK_READ_BYTES // 4, dtype=torch.int32, device=dev)
+    sink = torch.zeros(4096, dtype=torch.int32, device=dev)
+    waves = int(lib.qlin_peak_mfma_waves())
+    fsink = torch.zeros(waves, dtype=torch.float32, device=dev)
+
+    def read():
+        st = lib.qlin_peak_stream_read(src.data_ptr(), PEAK_READ_BYTES, sink.data_ptr(),
+                                       torch.cuda.current_stream().cuda_stream)
+        assert st == 0, st
+
+    def mfma():
+        st = lib.qlin_peak_mfma(PEAK_MFMA_ITERS, fsink.data_ptr(),
+                                torch.cuda.current_stream().cuda_stream)
+        assert st == 0, st
+    graphs = {}
+    if "peak_stream_read" in phases:
+        graphs["peak_stream_read"] = capture_calls(torch, [[read]])[0]
+    if "peak_mfma" in phases:
+        graphs["peak_mfma"] = capture_calls(torch, [[mfma]])[0]
+    hold = (src, sink, fsink, lib)
+
+    def run(name):
+        assert hold is not None
+        graphs[name].replay()
+    out = [Phase("peak_stream_read", run, "GB/s", PEAK_READ_BYTES, 1, HBM_PEAK_GBS, "hbm",
+                 "streaming read of 4 GiB, 16-byte loads (libqlin_peaks)"),
+           Phase("peak_mfma", run, "TFLOP/s", waves * PEAK_MFMA_ITERS * 8 * 32768, 1,
+                 FP16_MFMA_PEAK_TFLOPS, "mfma",
+                 "v_mfma_f32_32x32x16_f16 loop, 8 independent accumulators per wave")]
+    return [p for p in out if p.name in phases]
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -552,19 +662,23 @@ def main():
     if "decode" in sections:
         names = ["decode_step", "decode_gemv", "prefill_step_m128", "prefill_step_m2048",
                  "prefill_m128", "prefill_m2048", "gemm_m8", "fused_gemv",
-                 "rtn_precompute", "quantize_pack", "lm_head_int8", "embed_gather"]
+                 "rtn_precompute", "quantize_pack", "lm_head_int8", "embed_gather",
+                 "c1_gemv_latency"]
         ps, decode_shapes = build_decode(torch, qlin, synth, dev, ws, chosen(names), state)
         phases += ps
     if "qwen3_8b" in sections:
-        names = [f"q8_{s}_int{b}" for b in (4, 3, 2) for s in ("step", "decode")] + [
+        names = [f"q8_{s}_int{b}" for b in (4, 3, 2) for s in ("step", "decode", "pair")] + [
             f"q8_m{m}_int{b}" for b in (4, 3) for m in (8, 128)] + [
-            f"q8_m8_step_int{b}" for b in (4, 3)]
+            f"q8_m8_step_int{b}" for b in (4, 3)] + [
+            f"q8_prefill_step_m128_int{b}" for b in (4, 3)]
         phases += build_qwen3_8b(torch, qlin, synth, dev, ws, chosen(names))
     if "qwen3_06b" in sections:
         names = ([f"q06_{k}_b{b}_{g}" for k in ("fused", "lever") for b in (8, 7, 6, 5, 4, 3, 2)
                   for g in ("g64", "row")] + ["q06_fp16_control"] +
                  [f"q06_packed_b{b}" for b in (8, 7, 6, 5, 4, 3, 2)])
         phases += build_qwen3_06b(torch, qlin, synth, dev, ws, chosen(names))
+    if "peaks" in sections:
+        phases += build_peaks(torch, dev, chosen(["peak_stream_read", "peak_mfma"]))
     torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream()
@@ -603,55 +717,75 @@ def main():
         rooflines[p.name] = {"bound": p.bound, "kernel": p.kernel, "achieved": round(rate, 2),
                              "peak": p.peak, "unit": p.unit, "frac": round(rate / p.peak, 4)}
 
+    head = HEADLINE if HEADLINE in res else None
     out = {
         "metric": "GEMV weight GB/s (% HBM peak) + prefill GEMM TFLOP/s, int4 g64",
-        "value": None, "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "value": res[head]["GB/s"] if head else None, "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": res[head]["ms_median"] if head else None,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16",
         "data": "synthetic (seeded N(0,0.02) fp16 masters, N(0,1) fp16 activations)",
-        "config": {"workload": "Qwen2.5-0.5B decode step linear layers (24 x q/k/v, o, "
-                               "gate/up, down + 151936x896 LM head = 169 matrices), int4 g64, "
-                               "M=1; q/k/v in one launch, gate/up in one launch with the "
-                               "SwiGLU combination feeding down",
+        "config": {"workload": "Qwen3-8B-shaped decode step: 36 layers x {q 4096->4096, k/v "
+                               "4096->1024 (q/k/v one launch), o 4096->4096, gate/up "
+                               "4096->12288 (one launch, SwiGLU epilogue, fp16 h), down "
+                               "12288->4096}, 252 matrices, int4 g64, M=1, 144 launches "
+                               "from one HIP graph",
                    "global_batch": 1, "seq_len": 1, "parallelism": "single GPU",
-                   "hip_graph": True, "weight_copies_rotated": ROTATE,
+                   "weight_bytes_per_step": [p for p in phases if p.name == head][0].amount
+                   if head else None,
                    "sections": sections},
+        "loop_ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "phases": res,
+        "rooflines": rooflines,
     }
-    head = "decode_step" if "decode_step" in res else (
-        "decode_gemv" if "decode_gemv" in res else None)
+    if not args.no_cpu_baseline and "qwen3_8b" in sections:
+        out["cpu_baseline"] = cpu_baseline_c5()
     if head is not None:
-        gbs = res[head]["GB/s"]
-        dec = [p for p in phases if p.name == head][0]
-        per_launch_us = res[head]["ms_median"] * 1e3 / dec.launches
-        achieved = dec.amount / dec.launches / (per_launch_us * 1e-6) / 1e9
-        out["value"] = gbs
-        out["pct_hbm_peak"] = round(100 * gbs / HBM_PEAK_GBS, 2)
-        out["config"]["launches_per_step"] = dec.launches
+        out["pct_hbm_peak"] = round(100 * res[head]["GB/s"] / HBM_PEAK_GBS, 2)
+    pair = "q8_pair_int4"
+    if pair in res:
+        ph = [p for p in phases if p.name == pair][0]
+        per_launch_us = res[pair]["ms_median"] * 1e3 / ph.launches
+        bpl = ph.amount / ph.launches
+        achieved = bpl / (per_launch_us * 1e-6) / 1e9
+        traffic = measured_traffic()
         out["roofline"] = {
-            "bound": "hbm", "kernel": f"{dec.kernel}, {dec.launches} launches per step",
+            "bound": "hbm", "kernel": "gate/up SwiGLU pair GEMV of the decode step "
+                                      "(2 x 12288x4096 int4 g64 + x + fp16 h; 36 launches)",
             "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
-            "algorithmic_bytes_per_launch": round(dec.amount / dec.launches, 1),
-            "avg_launch_us": round(per_launch_us, 3),
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+            "algorithmic_bytes_per_launch": int(bpl), "avg_launch_us": round(per_launch_us, 3),
         }
     tf = {}
-    for m in (2048, 128):
-        for key in (f"prefill_step_m{m}", f"prefill_m{m}"):
-            if key in res:
-                tf[f"M={m}"] = res[key]["TFLOP/s"]
-                break
+    for key, label in (("prefill_step_m2048", "qwen25_M2048_step"),
+                       ("prefill_step_m128", "qwen25_M128_step"),
+                       ("q8_prefill_step_m128_int4", "qwen3_8b_M128_step"),
+                       ("q8_m128_int4", "qwen3_8b_M128_separate")):
+        if key in res:
+            tf[label] = res[key]["TFLOP/s"]
     if tf:
         out["prefill_gemm_tflops"] = tf
         out["prefill_pct_fp16_mfma_peak"] = {k: round(100 * v / FP16_MFMA_PEAK_TFLOPS, 2)
                                              for k, v in tf.items()}
-    out["phases"] = res
-    out["rooflines"] = rooflines
-    if not args.no_cpu_baseline and decode_shapes is not None:
-        out["cpu_baseline"] = cpu_baseline(decode_shapes)
+    peaks = {}
+    if "peak_stream_read" in res:
+        peaks["stream_read_GBs"] = res["peak_stream_read"]["GB/s"]
+    if "peak_mfma" in res:
+        peaks["mfma_f16_TFLOPs"] = res["peak_mfma"]["TFLOP/s"]
+    if peaks:
+        if head is not None and "stream_read_GBs" in peaks:
+            peaks["value_pct_of_read"] = round(100 * res[head]["GB/s"] / peaks["stream_read_GBs"], 2)
+        if "mfma_f16_TFLOPs" in peaks and tf:
+            peaks["prefill_pct_of_mfma_loop"] = {
+                k: round(100 * v / peaks["mfma_f16_TFLOPs"], 2) for k, v in tf.items()}
+        out["achieved_peaks"] = peaks
+    if "c1_gemv_latency" in res:
+        out["c1_us_per_call"] = round(res["c1_gemv_latency"]["ms_median"] * 1e3 / C1_CALLS, 3)
     print(json.dumps(out), flush=True)
 
 
-TRAFFIC_SUMMARY = os.path.join(HERE, "profiles", "gemv_int4_qwen25_decode_step_hbm_traffic.txt")
+TRAFFIC_SUMMARY = os.path.join(HERE, "profiles",
+                               "gemv_int4_qwen3_8b_gate_up_pair_hbm_traffic.txt")
 
 
 def kernel_source_hash():
@@ -666,8 +800,9 @@ def kernel_source_hash():
 
 
 def measured_traffic():
-    """HBM bytes per decode launch from the committed rocprofv3 counter summary,
-    or None when the kernel sources changed after the counters were taken."""
+    """HBM bytes per gate/up pair launch from the committed rocprofv3 counter
+    summary, or None when the kernel sources changed after the counters were
+    taken."""
     try:
         text = open(TRAFFIC_SUMMARY).read()
     except OSError:
@@ -680,41 +815,65 @@ def measured_traffic():
     return float(vals["traffic_bytes_per_launch"])
 
 
-def cpu_baseline(shapes, min_seconds=10.0):
-    """The oracle (plain NumPy) on the same decode step, in the same unit.
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
-    The oracle's GEMV is dequantize (binary64) + binary64 matmul from the
-    codes/scales/zeros its own quantizer produced (quantization not timed).
-    It runs over the 169 matrices in order, repeating the step until at least
-    `min_seconds` of timed CPU work have accumulated."""
+
+def cpu_baseline_c5():
+    """The oracle (plain NumPy) on a bounded sample of the headline workload:
+    the seven matrices of one Qwen3-8B layer (q, k, v, o, gate, up, down;
+    193 M weights) at int4 g64, M = 1.  Three phases timed apart with
+    time.perf_counter: quantize (binary32 RTN), dequantize (binary64), matmul
+    (binary64 BLAS).  `value` is the oracle's GEMV weight-stream rate in the
+    metric's unit: algorithmic weight bytes / (dequantize + matmul) time, on
+    all host cores; the same with one BLAS thread is reported beside it.
+    (NumPy's elementwise phases run on one thread either way.)"""
     import oracle
     import synth
-    cores = os.cpu_count() or 1
+    from threadpoolctl import threadpool_limits
     try:
         cores = len(os.sched_getaffinity(0))
     except AttributeError:
-        pass
-    prepared = []
-    for (l, nm, n, k) in shapes:
-        w16 = synth.master_weights(synth.layer_rng(1, l, nm), n, k)
-        x = synth.activations(synth.act_rng(1, l, nm), 1, k)[0]
-        codes, s16, z = oracle.quantize(w16, 4, 64)
-        prepared.append((x, codes, s16, z, n * k // 2 + n * (k // 64) * 3 + 2 * k + 4 * n))
-        del w16
-    t_total, nbytes, passes = 0.0, 0, 0
-    while t_total < min_seconds:
-        for (x, codes, s16, z, b) in prepared:
-            t = time.perf_counter()
+        cores = os.cpu_count() or 1
+    layer = [(0, nm, n, k) for (l, nm, n, k) in synth.qwen3_8b_shapes() if l == 0]
+    mats = []
+    for (l, nm, n, k) in layer:
+        w16 = synth.master_weights(synth.layer_rng(5, l, nm), n, k)
+        x = synth.activations(synth.act_rng(5, l, nm), 1, k)[0]
+        mats.append((w16, x, n * k // 2 + n * (k // 64) * 3 + 2 * k + 4 * n))
+
+    def one_pass():
+        tq = td = tm = 0.0
+        for w16, x, _ in mats:
+            t0 = time.perf_counter()
+            codes, s16, z = oracle.quantize(w16, 4, 64)
+            t1 = time.perf_counter()
             what = oracle.dequantize(codes, s16, z, 64)
+            t2 = time.perf_counter()
             oracle.matmul_ref(x, what)
-            t_total += time.perf_counter() - t
-            nbytes += b
-        passes += 1
-    return {"value": round(nbytes / t_total / 1e9, 4), "unit": "GB/s", "cores": cores,
-            "kind": "oracle",
-            "sample": f"the whole 169-matrix decode step, {passes} pass(es), "
-                      f"{t_total:.1f} s timed; dequantize + fp64 matmul per matrix, "
-                      "codes from the oracle's own quantizer (not timed)"}
+            t3 = time.perf_counter()
+            tq, td, tm = tq + t1 - t0, td + t2 - t1, tm + t3 - t2
+            del codes, what
+        return tq, td, tm
+    nbytes = sum(b for *_, b in mats)
+    runs = {}
+    for label, threads in (("all_cores", cores), ("one_thread", 1)):
+        with threadpool_limits(limits=threads):
+            tq, td, tm = one_pass()
+        runs[label] = {"threads": threads, "quantize_s": round(tq, 3),
+                       "dequantize_s": round(td, 3), "matmul_s": round(tm, 3),
+                       "GBs": round(nbytes / (td + tm) / 1e9, 4)}
+    return {"value": runs["all_cores"]["GBs"], "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "sample": "one Qwen3-8B layer (q, k, v, o, gate, up, down: 193 M weights), int4 "
+                      "g64, M = 1; GB/s = weight bytes / (dequantize + matmul); quantize "
+                      "timed apart",
+            "cpu_model": cpu_model(), "phases": runs}
 
 
 if __name__ == "__main__":

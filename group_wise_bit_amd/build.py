@@ -21,6 +21,9 @@ ROOT = os.path.dirname(PKG_DIR)
 CSRC = os.path.join(PKG_DIR, "csrc")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_PATH = os.path.join(PKG_DIR, "libqlin.so")
+# measurement utilities (include/qlin_peaks.h): the achieved-peak reference kernels
+PEAKS_PATH = os.path.join(PKG_DIR, "libqlin_peaks.so")
+PEAKS_SOURCE = os.path.join(CSRC, "peaks.hip")
 API_SOURCE = os.path.join(CSRC, "qlin_api.hip")
 INST_SOURCE = os.path.join(CSRC, "inst.hip")
 HEADERS = [os.path.join(CSRC, f) for f in ("device_common.h", "codes.h", "kernels.h", "plan.h",
@@ -108,5 +111,17 @@ def build(verbose: bool = False, extra_flags=None, jobs: int | None = None,
     return out_path
 
 
+def build_peaks(verbose: bool = False) -> str:
+    """Compile libqlin_peaks.so (the achieved-peak reference kernels)."""
+    tmp = PEAKS_PATH + ".tmp"
+    cmd = [hipcc(), *HIPCC_FLAGS, "-shared", PEAKS_SOURCE, "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    _run(cmd)
+    os.replace(tmp, PEAKS_PATH)
+    return PEAKS_PATH
+
+
 if __name__ == "__main__":
     print(build(verbose=True))
+    print(build_peaks(verbose=True))

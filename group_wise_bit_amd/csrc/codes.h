@@ -205,6 +205,111 @@ __device__ __forceinline__ float block_dot(const uint32_t* wd, const f16x2* xb, 
   }
 }
 
+// ------------------------------------- GEMV decode with the zero point folded
+// sum_k x_k (q_k - z) = sum_k x_k q_k - z * sum_k x_k: the block's x sum is
+// formed once per block and wave (block_xsums), so the per-pair subtraction
+// of z goes away.  A code field masked out of a word, with nothing OR-ed in,
+// is an fp16 subnormal: field F at bit offset b of a half-word reads as
+// F * 2^(b - 24) exactly (for b + width <= 10).  One AND per code pair, one
+// v_dot2 with the fp16 x pair (exact products, fp32 sums), and the classes'
+// sums are combined with the exact powers of two.  block_xq returns
+// sum_k x_k q_k * 2^-24 for the 64 codes of one row's block.
+template <int BITS>
+__device__ __forceinline__ float block_xq(const uint32_t* wd, const f16x2* xb);
+
+// 1-bit plane: word w holds codes 32w + i at bit 16*(i % 2) + i/2.
+__device__ __forceinline__ float block_xq1(const uint32_t* wd, const f16x2* xb) {
+  float a[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int w = 0; w < 2; ++w) {
+    const uint32_t v = wd[w], vs = v >> 8;
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+      const uint32_t m = (1u << p) | (1u << (16 + p));
+      a[p] = __builtin_amdgcn_fdot2(as_h2(v & m), xb[16 * w + p], a[p], false);
+      a[p] = __builtin_amdgcn_fdot2(as_h2(vs & m), xb[16 * w + 8 + p], a[p], false);
+    }
+  }
+  return ((a[0] + a[1] * 0.5f) + (a[2] * 0.25f + a[3] * 0.125f)) +
+         ((a[4] * 0.0625f + a[5] * 0.03125f) + (a[6] * 0.015625f + a[7] * 0.0078125f));
+}
+
+template <int BITS>
+__device__ __forceinline__ float block_xq(const uint32_t* wd, const f16x2* xb) {
+  if constexpr (BITS >= 5 && BITS <= 7) {
+    // q = lo + 16 hi over the two planes
+    float hi;
+    if constexpr (BITS == 5) hi = block_xq1(wd + 8, xb);
+    else hi = block_xq<BITS - 4>(wd + 8, xb);
+    return __builtin_fmaf(16.f, hi, block_xq<4>(wd, xb));
+  } else if constexpr (BITS == 4) {
+    float a0 = 0.f, a1 = 0.f, b0 = 0.f, b1 = 0.f;
+#pragma unroll
+    for (int w = 0; w < 8; ++w) {
+      const uint32_t v = wd[w], vs = v >> 8;
+      a0 = __builtin_amdgcn_fdot2(as_h2(v & 0x000F000Fu), xb[4 * w + 0], a0, false);
+      b0 = __builtin_amdgcn_fdot2(as_h2(v & 0x00F000F0u), xb[4 * w + 1], b0, false);
+      a1 = __builtin_amdgcn_fdot2(as_h2(vs & 0x000F000Fu), xb[4 * w + 2], a1, false);
+      b1 = __builtin_amdgcn_fdot2(as_h2(vs & 0x00F000F0u), xb[4 * w + 3], b1, false);
+    }
+    return (a0 + a1) + (b0 + b1) * 0.0625f;
+  } else if constexpr (BITS == 2) {
+    float a[4] = {0.f, 0.f, 0.f, 0.f}, b[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const uint32_t v = wd[w], vs = v >> 8;
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const uint32_t m = (3u << (2 * p)) | (3u << (16 + 2 * p));
+        a[p] = __builtin_amdgcn_fdot2(as_h2(v & m), xb[8 * w + p], a[p], false);
+        b[p] = __builtin_amdgcn_fdot2(as_h2(vs & m), xb[8 * w + 4 + p], b[p], false);
+      }
+    }
+    return (a[0] + b[0]) + (a[1] + b[1]) * 0.25f + (a[2] + b[2]) * 0.0625f +
+           (a[3] + b[3]) * 0.015625f;
+  } else if constexpr (BITS == 3) {
+    float a[4] = {0.f, 0.f, 0.f, 0.f}, b[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int run = 0; run < 2; ++run) {
+      const uint32_t H = wd[3 * run + 2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const uint32_t L = wd[3 * run + u];
+        const uint32_t Hu = u ? __builtin_amdgcn_alignbit(H, H, 8) : H;
+        const uint32_t Ls = L >> 8, Hs = Hu >> 1;
+        const int xo = 16 * run + 8 * u;
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          const uint32_t m2 = (3u << (2 * p)) | (3u << (16 + 2 * p));
+          const uint32_t m1 = (1u << (2 * p + 2)) | (1u << (2 * p + 18));
+          // the pair's low bits from L, its third bits from H: a 3-bit field
+          // at offset 2p of each half
+          const uint32_t tl = (L & m2) | (Hu & m1), ts = (Ls & m2) | (Hs & m1);
+          a[p] = __builtin_amdgcn_fdot2(as_h2(tl), xb[xo + p], a[p], false);
+          b[p] = __builtin_amdgcn_fdot2(as_h2(ts), xb[xo + 4 + p], b[p], false);
+        }
+      }
+    }
+    return (a[0] + b[0]) + (a[1] + b[1]) * 0.25f + (a[2] + b[2]) * 0.0625f +
+           (a[3] + b[3]) * 0.015625f;
+  } else {  // BITS == 8: each byte into the low byte of a half, high byte 0
+    float a0 = 0.f, a1 = 0.f, b0 = 0.f, b1 = 0.f;
+#pragma unroll
+    for (int w = 0; w < 16; w += 2) {
+      const uint32_t v = wd[w], u = wd[w + 1];
+      const f16x2 h0 = as_h2(__builtin_amdgcn_perm(0u, v, 0x0c020c00u));
+      const f16x2 h1 = as_h2(__builtin_amdgcn_perm(0u, v, 0x0c030c01u));
+      const f16x2 g0 = as_h2(__builtin_amdgcn_perm(0u, u, 0x0c020c00u));
+      const f16x2 g1 = as_h2(__builtin_amdgcn_perm(0u, u, 0x0c030c01u));
+      a0 = __builtin_amdgcn_fdot2(h0, xb[2 * w + 0], a0, false);
+      b0 = __builtin_amdgcn_fdot2(h1, xb[2 * w + 1], b0, false);
+      a1 = __builtin_amdgcn_fdot2(g0, xb[2 * w + 2], a1, false);
+      b1 = __builtin_amdgcn_fdot2(g1, xb[2 * w + 3], b1, false);
+    }
+    return (a0 + a1) + (b0 + b1);
+  }
+}
+
 // -------------------------------------------- MFMA operand decode (fp16 x 8)
 // Eight consecutive codes of a block ("chunk") -> fp16 s * (q - z), rounded
 // once to nearest even, in packed fp16 arithmetic.  The magic-number trick
@@ -347,6 +452,48 @@ __device__ __forceinline__ DeqT<BITS> make_deq_b(float s, int z) {
     return make_deq(s, z);
   }
 }
+
+// The fp16 range of the matrix-core weight operand.  s * (q - z) rounded to
+// fp16 is infinite once |s (q - z)| >= 65520, which finite fp16 masters of
+// magnitude above 49120 (2 bits) ... 65248 (8 bits) can reach; that needs
+// s >= 65520 / qmax.  Before its K loop, each wave checks the scales of each
+// of its columns over its blocks (needs_wide_operand); a column with such a
+// scale is decoded with s * 2^-8 throughout and its sums are scaled by 2^8 at
+// the end (where waves split K, the work-group's waves agree per column
+// first).  Both scalings are powers of two: the blocks that needed it keep
+// exactly their rounding (s * 2^-8 >= 1, every nonzero operand normal);
+// small weights elsewhere in that column may lose low bits to fp16
+// underflow, far below the column's large products.  Columns of ordinary
+// weights are untouched.
+template <int BITS>
+__device__ __forceinline__ bool maybe_wide(float s) {
+  return s >= 65520.f / (float)((1 << BITS) - 1);
+}
+
+// Whether any of the blocks jfirst, jfirst + jstep, ... below j1 of one
+// column has a scale >= 65520 / qmax.  scol points at the column's entry of
+// its tile's first group; G == 1: one scale per row.
+template <int BITS>
+__device__ __forceinline__ bool needs_wide_operand(const uint16_t* __restrict__ scol, int G,
+                                                   int jfirst, int j1, int jstep) {
+  float smax = 0.f;
+  if (G == 1) {
+    smax = jfirst < j1 ? h2f(scol[0]) : 0.f;
+  } else {
+    for (int j0 = jfirst; j0 < j1; j0 += 8 * jstep) {
+      uint16_t v[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = scol[(int64_t)min(j0 + i * jstep, j1 - 1) * 64];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) smax = __builtin_fmaxf(smax, h2f(v[i]));
+    }
+  }
+  return maybe_wide<BITS>(smax);
+}
+
+constexpr float kWideScale = 0.00390625f;   // 2^-8
+// the inverse of an operand scale (1 or 2^-8), exact
+__device__ __forceinline__ float unscale(float f) { return f < 1.f ? 256.f : 1.f; }
 
 // fp16 x 8 held in one uint4, as an MFMA operand.
 __device__ __forceinline__ f16x8 u4_to_f16x8(uint4 v) { return __builtin_bit_cast(f16x8, v); }

@@ -278,19 +278,87 @@ __device__ __forceinline__ void load_block_words(const uint32_t* __restrict__ bl
   }
 }
 
+// DPP lane moves within rows of 16 lanes (row_mirror 0x140, row_half_mirror
+// 0x141, quad permutations).
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL,
+                                                               0xF, 0xF, false));
+}
+
+// Sum over each row of 16 lanes, left in every lane of the row: pairs, quads,
+// half rows, rows.  Each step adds a lane and its partner, so both get the
+// same (commutative) sum and every lane of a row ends with one value.
+__device__ __forceinline__ float row_sum16(float v) {
+  v += dpp_f<0xB1>(v);    // lane ^ 1
+  v += dpp_f<0x4E>(v);    // lane ^ 2
+  v += dpp_f<0x141>(v);   // mirror within 8 lanes: the other quad
+  v += dpp_f<0x140>(v);   // mirror within 16 lanes: the other half row
+  return v;
+}
+
+// The x sums of the U blocks jj[0..U-1] a wave works on (for the folded zero
+// point): lane l reads U consecutive x of block l / (64/U) (one load, issued
+// with the block loads), block_xsums_finish adds them within rows of 16 lanes
+// and reads the row sums back as wave-uniform values.
+template <int U>
+struct XsumLoad {
+  typename std::conditional<U == 4, uint2, typename std::conditional<U == 2, uint32_t, uint16_t>::type>::type v;
+};
+
+// Block u of the wave's round is jb + u * jstep, clamped below j1 (as the
+// code loads clamp it).
+template <int U>
+__device__ __forceinline__ XsumLoad<U> block_xsums_load(const f16x2* __restrict__ x2, int jb,
+                                                        int jstep, int j1, int lane) {
+  constexpr int LPB = 64 / U;   // lanes per block
+  const int u = lane / LPB, i = lane % LPB;
+  const int j = min(jb + u * jstep, j1 - 1);
+  const uint16_t* xp = reinterpret_cast<const uint16_t*>(x2) + (int64_t)j * 64 + i * U;
+  XsumLoad<U> r;
+  if constexpr (U == 4) r.v = *reinterpret_cast<const uint2*>(xp);
+  else if constexpr (U == 2) r.v = *reinterpret_cast<const uint32_t*>(xp);
+  else r.v = *xp;
+  return r;
+}
+
+template <int U>
+__device__ __forceinline__ void block_xsums_finish(const XsumLoad<U>& ld, float (&X)[U]) {
+  const f16x2 one = {(f16)1.0f, (f16)1.0f};
+  float s;
+  if constexpr (U == 4)
+    s = __builtin_amdgcn_fdot2(as_h2(ld.v.y), one,
+                               __builtin_amdgcn_fdot2(as_h2(ld.v.x), one, 0.f, false), false);
+  else if constexpr (U == 2) s = __builtin_amdgcn_fdot2(as_h2(ld.v), one, 0.f, false);
+  else s = h2f(ld.v);
+  s = row_sum16(s);
+  auto rl = [&](int l) __attribute__((always_inline)) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, s), l));
+  };
+#pragma unroll
+  for (int v = 0; v < U; ++v) {
+    if constexpr (U == 4) X[v] = rl(16 * v);
+    else if constexpr (U == 2) X[v] = rl(32 * v) + rl(32 * v + 16);
+    else X[v] = (rl(0) + rl(16)) + (rl(32) + rl(48));
+  }
+}
+
 // One wave's share of a tile's dot products, for NM matrices that share x
 // (NM = 2: gate and up): K-blocks jfirst, jfirst + jstep, ... below j1, U at a
 // time.  The loads of all U blocks of every matrix are issued first, without
 // branches: a block past the range re-reads the last block of the range and
 // gets scale 0.  The decode of block u then only waits for its own loads,
 // while x of block u+1 is fetched (scalar loads) during block u's decode.
+// The zero point is folded: block u adds s * (sum x q - z * X[u]), X[u] the
+// block's x sum (block_xsums_*), and the codes are decoded as fp16 subnormals
+// (block_xq).
 // codes_t / scale_t / zero_t point at the tile's first block / entry.
 template <int BITS, int U, int NM>
 __device__ __forceinline__ void tile_dot(const uint32_t* const (&codes_t)[NM],
                                          const uint16_t* const (&scale_t)[NM],
                                          const uint8_t* const (&zero_t)[NM],
                                          const f16x2* __restrict__ x2, int G, int jfirst, int j1,
-                                         int jstep, int lane, uint32_t magic, float (&acc)[NM]) {
+                                         int jstep, int lane, float (&acc)[NM]) {
   constexpr int WPB = 2 * BITS;
   for (int jb = jfirst; jb < j1; jb += jstep * U) {
     uint32_t wd[U][NM][WPB];
@@ -300,15 +368,29 @@ __device__ __forceinline__ void tile_dot(const uint32_t* const (&codes_t)[NM],
     for (int u = 0; u < U; ++u) {
       const int j = jb + u * jstep;
       jj[u] = j < j1 ? j : j1 - 1;
+    }
+    // the x sums' and the metadata loads first, then the codes: loads return
+    // in order, so a block's decode and its scale/zero combine wait only for
+    // its own codes
+    const XsumLoad<U> xl = block_xsums_load<U>(x2, jb, jstep, j1, lane);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
       const int64_t mi = (int64_t)((G == 1) ? 0 : jj[u]) * kTile + lane;
 #pragma unroll
       for (int m = 0; m < NM; ++m) {
-        load_block_words<BITS>(codes_t[m] + ((int64_t)jj[u] * kTile + lane) * WPB, wd[u][m]);
         sr[u][m] = scale_t[m][mi];
         z[u][m] = zero_t[m][mi];
       }
     }
-    if constexpr (U > 1) loads_issued();
+    loads_issued();
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int m = 0; m < NM; ++m)
+        load_block_words<BITS>(codes_t[m] + ((int64_t)jj[u] * kTile + lane) * WPB, wd[u][m]);
+    loads_issued();
+    float X[U];
+    block_xsums_finish<U>(xl, X);
     f16x2 xc[32], xn[32];
 #pragma unroll
     for (int i = 0; i < 32; ++i) xc[i] = x2[(int64_t)jj[0] * 32 + i];
@@ -319,9 +401,11 @@ __device__ __forceinline__ void tile_dot(const uint32_t* const (&codes_t)[NM],
         for (int i = 0; i < 32; ++i) xn[i] = x2[(int64_t)jj[u + 1] * 32 + i];
       }
 #pragma unroll
-      for (int m = 0; m < NM; ++m)
-        acc[m] = __builtin_fmaf(masked_scale(sr[u][m], jb + u * jstep < j1),
-                                block_dot<BITS>(wd[u][m], xc, z[u][m], magic), acc[m]);
+      for (int m = 0; m < NM; ++m) {
+        const float t = __builtin_fmaf(block_xq<BITS>(wd[u][m], xc), 16777216.f,
+                                       -(float)z[u][m] * X[u]);
+        acc[m] = __builtin_fmaf(masked_scale(sr[u][m], jb + u * jstep < j1), t, acc[m]);
+      }
       if (u + 1 < U) {
 #pragma unroll
         for (int i = 0; i < 32; ++i) xc[i] = xn[i];
@@ -365,7 +449,6 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemv_packed(
   constexpr int WPB = 2 * BITS;
   constexpr int NM = SWIGLU ? 2 : 1;                  // matrices per tile
   __shared__ float red[NM][WAVES][64];
-  const uint32_t magic = vreg_const(kMagic);
   const int lane = lane_id(), wave = wave_id();
   const int sp = blockIdx.y;
   // this work-group's matrix (uniform selects, no indexing of the argument)
@@ -398,7 +481,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemv_packed(
   float acc[NM];
 #pragma unroll
   for (int m = 0; m < NM; ++m) acc[m] = 0.f;
-  tile_dot<BITS, U, NM>(codes_t, scale_t, zero_t, x2, G, j0 + wave, j1, WAVES, lane, magic, acc);
+  tile_dot<BITS, U, NM>(codes_t, scale_t, zero_t, x2, G, j0 + wave, j1, WAVES, lane, acc);
 #pragma unroll
   for (int m = 0; m < NM; ++m) red[m][wave][lane] = acc[m];
   lds_barrier();
@@ -1122,6 +1205,23 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_skinny(
   for (int cg = 0; cg < 4; ++cg) acc[cg] = (f32x4){0.f, 0.f, 0.f, 0.f};
   const bool xrow = c < m;
   const uint16_t* xr = X + (int64_t)(xrow ? c : 0) * ldx;
+  // the fp16 range of the weight operand (maybe_wide): per column, the
+  // work-group's waves agree through LDS
+  float fw[4];
+  {
+    __shared__ float fwl[WAVES][4][64];
+#pragma unroll
+    for (int cg = 0; cg < 4; ++cg)
+      fwl[wave][cg][lane] = needs_wide_operand<BITS>(scale + (int64_t)t * G * kTile + 16 * cg + c,
+                                                     G, j0 + wave, j1, WAVES) ? kWideScale : 1.f;
+    __syncthreads();
+#pragma unroll
+    for (int cg = 0; cg < 4; ++cg) {
+      fw[cg] = fwl[0][cg][lane];
+#pragma unroll
+      for (int w = 1; w < WAVES; ++w) fw[cg] = __builtin_fminf(fw[cg], fwl[w][cg][lane]);
+    }
+  }
   for (int jb = j0 + wave; jb < j1; jb += WAVES * U) {
     uint4 xv[U][2];
     uint32_t wl[U][4][QW];
@@ -1155,7 +1255,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_skinny(
       const f16x8 a0 = u4_to_f16x8(xv[u][0]), a1 = u4_to_f16x8(xv[u][1]);
 #pragma unroll
       for (int cg = 0; cg < 4; ++cg) {
-        const Deq d = make_deq(su[u][cg], zu[u][cg]);
+        const Deq d = make_deq(su[u][cg] * fw[cg], zu[u][cg]);
         acc[cg] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, deq_quarter<BITS>(wl[u][cg], 0, d, magic),
                                                          acc[cg], 0, 0, 0);
         acc[cg] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, deq_quarter<BITS>(wl[u][cg], 1, d, magic),
@@ -1173,6 +1273,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_skinny(
     tot[cg] = red[0][cg][lane];
 #pragma unroll
     for (int w = 1; w < WAVES; ++w) tot[cg] += red[w][cg][lane];
+    tot[cg] *= unscale(fw[cg]);
   }
   const int64_t np = (int64_t)gridDim.x * kTile;
   if (splits > 1) {
@@ -1332,12 +1433,15 @@ __global__ __launch_bounds__(256) void k_gemm_tiles(
   }
   const uint32_t* wsrc[2];
   int64_t msrc[2];
+  float fw[2];               // the fp16 range of the weight operand (maybe_wide)
 #pragma unroll
   for (int cb = 0; cb < 2; ++cb) {
     const int r = 32 * cb + c;
     wsrc[cb] = codes + ((int64_t)tt * kb * kTile + r) * WPB;
     msrc[cb] = (int64_t)tt * G * kTile + r;
+    fw[cb] = needs_wide_operand<BITS>(scale + msrc[cb], G, ja, ja + nk, 1) ? kWideScale : 1.f;
   }
+  const bool w_wide = __builtin_amdgcn_ballot_w64(fw[0] < 1.f || fw[1] < 1.f) != 0;
 
   u32x4 xv[2][XCH];
   uint32_t wl[2][2][HW];
@@ -1379,7 +1483,7 @@ __global__ __launch_bounds__(256) void k_gemm_tiles(
     DeqT<BITS> dn[2];
     if (decode_next) {
 #pragma unroll
-      for (int cb = 0; cb < 2; ++cb) dn[cb] = make_deq_b<BITS>(sc[Q][cb], zc[Q][cb]);
+      for (int cb = 0; cb < 2; ++cb) dn[cb] = make_deq_b<BITS>(sc[Q][cb] * fw[cb], zc[Q][cb]);
     }
     // A fragments of slice s4+1 are read from LDS while slice s4's MFMAs run.
     f16x8 a[2][RB];
@@ -1420,7 +1524,7 @@ __global__ __launch_bounds__(256) void k_gemm_tiles(
   for (int i = 0; i < XCH; ++i) land_x(S0{}, i);
 #pragma unroll
   for (int cb = 0; cb < 2; ++cb) {
-    const DeqT<BITS> d = make_deq_b<BITS>(sc[0][cb], zc[0][cb]);
+    const DeqT<BITS> d = make_deq_b<BITS>(sc[0][cb] * fw[cb], zc[0][cb]);
 #pragma unroll
     for (int s4 = 0; s4 < 4; ++s4) bfrag[0][cb][s4] = deq_half<BITS>(wl[0][cb], s4, d, magic);
   }
@@ -1434,6 +1538,12 @@ __global__ __launch_bounds__(256) void k_gemm_tiles(
     issue(min(j + 3, nk - 1), S1{});
     __syncthreads();
     if (j + 2 >= nk) break;
+  }
+  if (w_wide) {
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb) acc[rb][cb] *= unscale(fw[cb]);
   }
 
   if (splits > 1) {
@@ -1571,6 +1681,27 @@ __global__ __launch_bounds__(256) void k_gemm_ksplit(
       for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[mi][rb][cb][r] = 0.f;
+  // the fp16 range of the weight operand (maybe_wide): each wave checks its
+  // own blocks of each column, the four waves agree through LDS, and the
+  // column's sums are scaled back after the reduction
+  float fw[NM][CB];
+  {
+    __shared__ float fwl[4][NM][CB][64];
+#pragma unroll
+    for (int mi = 0; mi < NM; ++mi)
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb)
+        fwl[wave][mi][cb][lane] =
+            needs_wide_operand<BITS>(ssrc[mi] + 32 * (cb0 + cb), G, j0 + wave, j1, 4)
+                ? kWideScale : 1.f;
+    __syncthreads();
+#pragma unroll
+    for (int mi = 0; mi < NM; ++mi)
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb)
+        fw[mi][cb] = __builtin_fminf(__builtin_fminf(fwl[0][mi][cb][lane], fwl[1][mi][cb][lane]),
+                                     __builtin_fminf(fwl[2][mi][cb][lane], fwl[3][mi][cb][lane]));
+  }
 
   for (int jb = j0 + wave; jb < j1; jb += 4 * U) {
     f16x8 xa[U][RB][4];
@@ -1605,7 +1736,9 @@ __global__ __launch_bounds__(256) void k_gemm_ksplit(
       for (int mi = 0; mi < NM; ++mi)
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb) {
-          const DeqT<BITS> d = make_deq_b<BITS>(masked_scale(sr[u][mi][cb], valid), zc[u][mi][cb]);
+          // (a block past the range gets scale 0; see masked_scale)
+          const DeqT<BITS> d = make_deq_b<BITS>(h2f(sr[u][mi][cb]) * (valid ? fw[mi][cb] : 0.f),
+                                                zc[u][mi][cb]);
 #pragma unroll
           for (int s = 0; s < 4; ++s) {
             const f16x8 bf = deq_half<BITS>(wl[u][mi][cb], s, d, magic);
@@ -1634,7 +1767,9 @@ __global__ __launch_bounds__(256) void k_gemm_ksplit(
 #pragma unroll
     for (int i = 0; i < PT; ++i) {
       const int e = tid + 256 * i;
-      v[mi][i] = ((red[0][e] + red[1][e]) + red[2][e]) + red[3][e];
+      // (element e's column is this lane's: e % 64 == lane)
+      v[mi][i] = (((red[0][e] + red[1][e]) + red[2][e]) + red[3][e]) *
+                 unscale(fw[mi][(e >> 10) % CB]);
     }
   }
   if (splits > 1) {
@@ -1897,6 +2032,14 @@ __global__ __launch_bounds__(256, 2) void k_gemm_lds(
     for (int cb = 0; cb < 2; ++cb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[rb][cb][r] = 0.f;
+  // the fp16 range of the weight operand over the K range (maybe_wide): the
+  // wave owns its columns, so one operand scale for the wave
+  float fw[2];
+#pragma unroll
+  for (int cb = 0; cb < 2; ++cb)
+    fw[cb] = needs_wide_operand<BITS>(scale + (int64_t)tt * G * kTile + 32 * cb + c, G, ja,
+                                      ja + nk, 1) ? kWideScale : 1.f;
+  const bool w_wide = __builtin_amdgcn_ballot_w64(fw[0] < 1.f || fw[1] < 1.f) != 0;
 
   // Block j from stage I: decode this wave's B operand from the staged codes
   // slice by slice, interleaved with the MFMAs of the previous slice.
@@ -1921,7 +2064,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm_lds(
       }
       const uint16_t sb = reinterpret_cast<const uint16_t*>(st.meta[wave])[r];
       const int zb = reinterpret_cast<const uint8_t*>(st.meta[wave])[128 + r];
-      d[cb] = make_deq_b<BITS>(h2f(sb), zb);
+      d[cb] = make_deq_b<BITS>(h2f(sb) * fw[cb], zb);
     }
 #pragma unroll
     for (int s4 = 0; s4 < 4; ++s4) {
@@ -1972,6 +2115,12 @@ __global__ __launch_bounds__(256, 2) void k_gemm_lds(
       constexpr int I = decltype(ic)::value;
       if (j + I < nk) step(j + I, ic);
     });
+  }
+  if (w_wide) {
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb) acc[rb][cb] *= unscale(fw[cb]);
   }
 
   if (splits > 1) {

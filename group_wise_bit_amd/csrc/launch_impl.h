@@ -47,15 +47,15 @@ void launch_gemv_packed_s(const PackedLaunch& L, const f16x2* x2, float* part, u
   if (c.waves == 16) {
     if (c.unroll == 1) launch_gemv_packed_w<B, 16, 1, SW>(L, x2, part, tick, c, st);
     else if (c.unroll == 2) launch_gemv_packed_w<B, 16, 2, SW>(L, x2, part, tick, c, st);
-    else launch_gemv_packed_w<B, 16, (SW ? 2 : 4), SW>(L, x2, part, tick, c, st);
+    else launch_gemv_packed_w<B, 16, ((SW && B > 4) ? 2 : 4), SW>(L, x2, part, tick, c, st);
   } else if (c.waves == 8) {
     if (c.unroll == 1) launch_gemv_packed_w<B, 8, 1, SW>(L, x2, part, tick, c, st);
     else if (c.unroll == 2) launch_gemv_packed_w<B, 8, 2, SW>(L, x2, part, tick, c, st);
-    else launch_gemv_packed_w<B, 8, (SW ? 2 : 4), SW>(L, x2, part, tick, c, st);
+    else launch_gemv_packed_w<B, 8, ((SW && B > 4) ? 2 : 4), SW>(L, x2, part, tick, c, st);
   } else {
     if (c.unroll == 1) launch_gemv_packed_w<B, 4, 1, SW>(L, x2, part, tick, c, st);
     else if (c.unroll == 2) launch_gemv_packed_w<B, 4, 2, SW>(L, x2, part, tick, c, st);
-    else launch_gemv_packed_w<B, 4, (SW ? 2 : 4), SW>(L, x2, part, tick, c, st);
+    else launch_gemv_packed_w<B, 4, ((SW && B > 4) ? 2 : 4), SW>(L, x2, part, tick, c, st);
   }
 }
 
@@ -142,6 +142,16 @@ void launch_gemm_ksplit_rb(const GemmSet& set, const GemmPlan& p, const uint16_t
   // 64-row X tiles, whose X fragments take twice the registers)
   const int per_wave = (c.kbps + 3) / 4;
   const dim3 grid(c.gx, c.gy, c.splits);
+  if constexpr (RB == 4) {
+    // 128 X rows: one block in flight per wave (the X fragments of a block
+    // take 64 registers), whole or half tiles
+    if (c.half)
+      hipLaunchKernelGGL((k_gemm_ksplit<B, 1, 4, false, false, 1>), grid, dim3(256), 0, st, set,
+                         X, ldx, m, p.kb, p.G, c.splits, c.kbps, part, tick);
+    else
+      hipLaunchKernelGGL((k_gemm_ksplit<B, 1, 4>), grid, dim3(256), 0, st, set, X, ldx, m, p.kb,
+                         p.G, c.splits, c.kbps, part, tick);
+  } else {
   if (c.half) {   // half tiles: half the codes and accumulators per wave
     if (per_wave >= 4 && RB == 1)
       hipLaunchKernelGGL((k_gemm_ksplit<B, 4, RB, false, false, 1>), grid, dim3(256), 0, st, set,
@@ -169,6 +179,7 @@ void launch_gemm_ksplit_rb(const GemmSet& set, const GemmPlan& p, const uint16_t
   else
     hipLaunchKernelGGL((k_gemm_ksplit<B, 1, RB>), grid, dim3(256), 0, st, set, X, ldx, m, p.kb,
                        p.G, c.splits, c.kbps, part, tick);
+  }
 }
 
 template <int B>
@@ -179,14 +190,15 @@ void launch_gemm_ksplit(const GemmPlan& p, const uint16_t* X, int64_t ldx, int m
     set.end[i] = c.dual   ? (p.end_tiles[i] + 1) / 2
                  : c.half ? 2 * p.end_tiles[i]
                           : p.end_tiles[i];
-  if (c.mb == 1) launch_gemm_ksplit_rb<B, 2>(set, p, X, ldx, m, c, part, tick, st);
+  if (c.mb == kMbKsplit128) launch_gemm_ksplit_rb<B, 4>(set, p, X, ldx, m, c, part, tick, st);
+  else if (c.mb == 1) launch_gemm_ksplit_rb<B, 2>(set, p, X, ldx, m, c, part, tick, st);
   else launch_gemm_ksplit_rb<B, 1>(set, p, X, ldx, m, c, part, tick, st);
 }
 
 template <int B>
 void launch_gemm_tiles(const GemmPlan& p, const uint16_t* X, int64_t ldx, int m, TilesCfg c,
                        float* part, uint32_t* tick, hipStream_t st) {
-  if (c.mb <= 1) launch_gemm_ksplit<B>(p, X, ldx, m, c, part, tick, st);
+  if (is_ksplit(c.mb)) launch_gemm_ksplit<B>(p, X, ldx, m, c, part, tick, st);
   else if (c.mb == 32) launch_tiles_mb<B, 32>(p, X, ldx, m, c, part, tick, st);
   else if (c.mb == 64) launch_tiles_mb<B, 64>(p, X, ldx, m, c, part, tick, st);
   else launch_tiles_mb<B, 128>(p, X, ldx, m, c, part, tick, st);
@@ -203,7 +215,10 @@ void launch_gemm_swiglu(const GemmSet& set, const uint16_t* X, int64_t ldx, int 
     hipLaunchKernelGGL((k_gemm_lds<B, 64, 4, true>), grid, dim3(256), 0, st, set, X, ldx, m, kb,
                        G, c.splits, c.kbps, part, tick);
   else if (c.half) {   // half tiles of both matrices
-    if (c.mb == 1)
+    if (c.mb == kMbKsplit128)
+      hipLaunchKernelGGL((k_gemm_ksplit<B, 1, 4, true, false, 1>), grid, dim3(256), 0, st, set,
+                         X, ldx, m, kb, G, c.splits, c.kbps, part, tick);
+    else if (c.mb == 1)
       hipLaunchKernelGGL((k_gemm_ksplit<B, 1, 2, true, false, 1>), grid, dim3(256), 0, st, set,
                          X, ldx, m, kb, G, c.splits, c.kbps, part, tick);
     else if ((c.kbps + 3) / 4 >= 4)

@@ -66,7 +66,14 @@ struct GemmPlan {
 // large.
 // mb = 0 / 1: k_gemm_ksplit with 32 / 64 X rows, gx in tiles (dual: in tile
 // pairs; half: in 32-row halves of tiles)
+// mb = 6: k_gemm_ksplit with 128 X rows (each wave's decoded fragment feeds
+// four MFMA row blocks), over whole or half tiles, no tile pairs.
 struct TilesCfg { int mb, gx, gy, splits, kbps; bool dual, half; };
+
+constexpr int kMbKsplit128 = 6;
+// the K-split kernel's forms and their X rows
+inline bool is_ksplit(int mb) { return mb <= 1 || mb == kMbKsplit128; }
+inline int ksplit_rows(int mb) { return mb == kMbKsplit128 ? 128 : 32 * (mb + 1); }
 
 // Kernel launchers, one instantiation per bit width (inst.hip).
 template <int B>

@@ -227,8 +227,9 @@ GemvCfg gemv_config(int64_t tiles, int kb, GemvKind kind, int bits, int64_t ws_b
   while (splits > 1 && kCounterBytes + (int64_t)splits * part_rows * 4 > ws_bytes) --splits;
   const int kbps = (kb + splits - 1) / splits;
   // blocks kept in flight per wave: the wave's share of the split, up to 4
-  // (packed), 2 (gate/up pairs, 8-row fused) or 1 (64-row fused)
-  const int unroll = fused ? (rows == 64 ? 1 : 2) : (pair ? 2 : 4);
+  // (packed; whole-tile gate/up pairs up to 4 bits), 2 (other gate/up pairs,
+  // 8-row fused) or 1 (64-row fused)
+  const int unroll = fused ? (rows == 64 ? 1 : 2) : (pair ? (rows == 64 && bits <= 4 ? 4 : 2) : 4);
   const int per_wave = (kbps + waves - 1) / waves;
   int u = 1;
   while (u < unroll && u < per_wave) u *= 2;
@@ -430,18 +431,20 @@ TilesCfg tiles_config(int64_t gx, int64_t tiles, int kb, int m, int count, bool 
   {
     int mb, sp, unused;
     if (launch_override(QLIN_TUNE_GEMM, mb, sp, unused) && mb != 16) {
-      c.mb = (mb == 2 || mb == 5) ? 1 : (mb == 3 || mb == 4) ? 0 : mb;
+      c.mb = (mb == 6 || mb == 7) ? kMbKsplit128 : (mb == 2 || mb == 5) ? 1
+             : (mb == 3 || mb == 4) ? 0 : mb;
       c.dual = mb == 2 || mb == 3;
-      c.half = mb == 4 || mb == 5;
+      c.half = mb == 4 || mb == 5 || mb == 7;
       want = sp < kb ? sp : kb;
     }
   }
   if (!pairable) c.dual = false;       // tile pairs within one matrix only
   if (want < 1) want = 1;
-  const bool ks = c.mb <= 1;
+  const bool ks = is_ksplit(c.mb);
   if (!ks) c.dual = c.half = false;
+  if (c.mb == kMbKsplit128) c.dual = false;
   if (ks) c.gx = (int)(c.dual ? (tiles + 1) / 2 : c.half ? 2 * tiles : tiles);
-  const int rows = ks ? 32 * (c.mb + 1) : c.mb;
+  const int rows = ks ? ksplit_rows(c.mb) : c.mb;
   const int64_t wg_outputs =
       (int64_t)rows * (ks ? (c.dual ? 2 * kTile : c.half ? kTile / 2 : kTile) : 256);
   c.gy = (m + rows - 1) / rows;
@@ -458,7 +461,7 @@ int64_t tiles_ws_bytes(int64_t gx, int64_t tiles, int kb, int m, int count, bool
   const TilesCfg c = tiles_config(gx, tiles, kb, m, count, pairable, bits, INT64_MAX);
   if (c.splits <= 1) return 0;
   const int64_t wg_outputs =
-      c.mb <= 1 ? 32 * (c.mb + 1) * (c.dual ? 2 * kTile : c.half ? kTile / 2 : kTile)
+      is_ksplit(c.mb) ? ksplit_rows(c.mb) * (c.dual ? 2 * kTile : c.half ? kTile / 2 : kTile)
                 : (int64_t)c.mb * 256;
   return kCounterBytes + (int64_t)c.splits * c.gy * c.gx * wg_outputs * 4;
 }
@@ -529,17 +532,18 @@ TilesCfg swiglu_config(int64_t tiles, int kb, int m, int64_t ws_bytes) {
   {
     int mb, sp, unused;
     if (launch_override(QLIN_TUNE_GEMM, mb, sp, unused) &&
-        (mb == 0 || mb == 1 || mb == 4 || mb == 5 || mb == 32 || mb == 64 || mb == 128)) {
-      c.mb = mb == 32 ? 64 : mb == 4 ? 0 : mb == 5 ? 1 : mb;
+        (mb <= 1 || (mb >= 4 && mb <= 7) || mb == 32 || mb == 64 || mb == 128)) {
+      c.mb = mb == 32 ? 64 : mb == 4 ? 0 : mb == 5 ? 1 : (mb == 6 || mb == 7) ? kMbKsplit128 : mb;
       c.half = mb == 4 || mb == 5;
       want = sp < kb ? sp : kb;
     }
   }
   if (want < 1) want = 1;
-  const bool ks = c.mb <= 1;
+  const bool ks = is_ksplit(c.mb);
   if (!ks) c.half = false;
+  if (c.mb == kMbKsplit128) c.half = true;     // two accumulator sets: half tiles only
   c.gx = (int)(ks ? (c.half ? 2 * tiles : tiles) : cols2);
-  const int rows = ks ? 32 * (c.mb + 1) : c.mb;
+  const int rows = ks ? ksplit_rows(c.mb) : c.mb;
   const int64_t wg_outputs = (int64_t)rows * (ks ? (c.half ? kTile : 2 * kTile) : 256);
   c.gy = (m + rows - 1) / rows;
   if ((int64_t)c.gx * c.gy > kMaxSplitTiles) want = 1;
@@ -553,9 +557,9 @@ TilesCfg swiglu_config(int64_t tiles, int kb, int m, int64_t ws_bytes) {
 int64_t swiglu_ws_bytes(int64_t tiles, int kb, int m) {
   const TilesCfg c = swiglu_config(tiles, kb, m, INT64_MAX);
   if (c.splits <= 1) return 0;
-  const bool ks = c.mb <= 1;
+  const bool ks = is_ksplit(c.mb);
   const int64_t wg_outputs =
-      ks ? 32 * (c.mb + 1) * (c.half ? kTile : 2 * kTile) : (int64_t)c.mb * 256;
+      ks ? ksplit_rows(c.mb) * (c.half ? kTile : 2 * kTile) : (int64_t)c.mb * 256;
   return kCounterBytes + (int64_t)c.splits * c.gy * c.gx * wg_outputs * 4;
 }
 
@@ -1020,7 +1024,7 @@ qlin_status qlin_set_launch_override(int32_t family, const int32_t* params) {
   if (b < 1 || b > 0xFFFF) return QLIN_ERR_SHAPE;
   if (family == QLIN_TUNE_GEMV) {
     if (!(a == 4 || a == 8 || a == 16) || !(c == 8 || c == 16 || c == 64)) return QLIN_ERR_SHAPE;
-  } else if (!((a >= 0 && a <= 5) || a == 16 || a == 32 || a == 64 || a == 128)) {
+  } else if (!((a >= 0 && a <= 7) || a == 16 || a == 32 || a == 64 || a == 128)) {
     return QLIN_ERR_SHAPE;
   }
   g_override[family].store((1ull << 63) | (uint64_t)(uint32_t)a | ((uint64_t)(uint32_t)b << 16) |

@@ -198,6 +198,14 @@ qlin_status qlin_gemv(const qlin_weight* w, const uint16_t* x, float* y,
  * than bf16 operands: bf16 rounding of X and of the weights alone exceeds
  * 1e-3 * max_row sum |x w| at short reductions (k = 192), at the same
  * matrix-core rate.
+ * Range: the fp16 operand holds every dequantized weight of masters with
+ * |w| <= 49120 (2 bits), 57312 (3), 61408 (4), 63456 (5), 64480 (6),
+ * 64992 (7), 65248 (8).  Beyond that a weight s * (q - z) can reach 65520,
+ * past fp16's largest value; every finite master is still accepted: a
+ * work-group (or wave) whose columns have a scale >= 65520 / (2^bits - 1)
+ * decodes its operands with the scale times 2^-8 and multiplies its sums by
+ * 2^8, so that Y stays finite and within the same tolerance (small weights
+ * beside such large ones may then lose low bits to fp16 underflow).
  * Deterministic.  Workspace as for qlin_gemv.
  */
 qlin_status qlin_gemm(const qlin_weight* w, const uint16_t* X, int32_t m, int64_t ld_x,

@@ -417,7 +417,7 @@ def test_gemm_one_hot_fp16_exact(bits, m):
 # matrix with 64 (2) / 32 (3) X rows (sets run these as 1 / 0), and over half
 # tiles with 32 (4) / 64 (5) X rows
 KSPLIT = ["0,1", "0,2", "0,5", "1,1", "1,3", "2,1", "2,3", "3,1", "3,2", "4,1", "4,3", "5,1",
-          "5,2"]
+          "5,2", "6,1", "6,3", "7,1", "7,2"]
 
 
 @pytest.mark.parametrize("bits", [2, 3, 4, 5, 6, 7, 8])
