@@ -602,8 +602,9 @@ def build_peaks(torch, dev, phases):
                                           ctypes.c_void_p]
     lib.qlin_peak_mfma.argtypes = [ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
     lib.qlin_peak_mfma_waves.restype = ctypes.c_int64
+    lib.qlin_peak_read_groups.restype = ctypes.c_int64
     src = torch.ones(PEAK_READ_BYTES // 4, dtype=torch.int32, device=dev)
-    sink = torch.zeros(4096, dtype=torch.int32, device=dev)
+    sink = torch.zeros(int(lib.qlin_peak_read_groups()), dtype=torch.int32, device=dev)
     waves = int(lib.qlin_peak_mfma_waves())
     fsink = torch.zeros(waves, dtype=torch.float32, device=dev)
 
@@ -627,7 +628,7 @@ def build_peaks(torch, dev, phases):
         assert hold is not None
         graphs[name].replay()
     out = [Phase("peak_stream_read", run, "GB/s", PEAK_READ_BYTES, 1, HBM_PEAK_GBS, "hbm",
-                 "streaming read of 4 GiB, 16-byte loads (libqlin_peaks)"),
+                 "streaming read of 4 GiB, one contiguous chunk per work-group, 16-byte loads (libqlin_peaks)"),
            Phase("peak_mfma", run, "TFLOP/s", waves * PEAK_MFMA_ITERS * 8 * 32768, 1,
                  FP16_MFMA_PEAK_TFLOPS, "mfma",
                  "v_mfma_f32_32x32x16_f16 loop, 8 independent accumulators per wave")]

@@ -7,26 +7,35 @@
 
 namespace {
 
-constexpr int kReadGroups = 4096;
-constexpr int kMfmaGroups = 1024;          // 4 per CU
+constexpr int kReadGroups = 16384;
+constexpr int kReadInFlight = 16;          // 16-byte loads in flight per thread
+constexpr int kMfmaGroups = 512;           // 2 per CU
 constexpr int kMfmaThreads = 256;
 
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
+// Each work-group reads one contiguous chunk of n16 / gridDim.x words (the
+// last one also the remainder): sequential addresses per work-group keep
+// every HBM page busy with fewer row switches than a grid-stride sweep.
 __global__ __launch_bounds__(256) void k_stream_read(const uint4* __restrict__ src, int64_t n16,
                                                      uint32_t* __restrict__ sink) {
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  const int64_t per = n16 / gridDim.x;
+  const int64_t begin = (int64_t)blockIdx.x * per;
+  const int64_t end = blockIdx.x + 1 == gridDim.x ? n16 : begin + per;
+  const uint4* p = src + begin;
+  const int64_t len = end - begin;
   uint32_t acc = 0;
-  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  // four loads in flight per thread per round
-  for (; i + 3 * stride < n16; i += 4 * stride) {
-    const uint4 a = src[i], b = src[i + stride], c = src[i + 2 * stride], d = src[i + 3 * stride];
-    acc ^= a.x ^ a.y ^ a.z ^ a.w ^ b.x ^ b.y ^ b.z ^ b.w ^ c.x ^ c.y ^ c.z ^ c.w ^ d.x ^ d.y ^
-           d.z ^ d.w;
+  int64_t i = threadIdx.x;
+  for (; i + (kReadInFlight - 1) * 256 < len; i += kReadInFlight * 256) {
+    uint4 v[kReadInFlight];
+#pragma unroll
+    for (int l = 0; l < kReadInFlight; ++l) v[l] = p[i + l * 256];
+#pragma unroll
+    for (int l = 0; l < kReadInFlight; ++l) acc ^= v[l].x ^ v[l].y ^ v[l].z ^ v[l].w;
   }
-  for (; i < n16; i += stride) {
-    const uint4 a = src[i];
+  for (; i < len; i += 256) {
+    const uint4 a = p[i];
     acc ^= a.x ^ a.y ^ a.z ^ a.w;
   }
   __shared__ uint32_t red[256];
@@ -62,9 +71,11 @@ __global__ __launch_bounds__(kMfmaThreads) void k_mfma_loop(int iters, float* __
 
 extern "C" {
 
+int64_t qlin_peak_read_groups(void) { return kReadGroups; }
+
 int qlin_peak_stream_read(const void* src, int64_t bytes, uint32_t* sink, hipStream_t stream) {
   if (src == nullptr || sink == nullptr || bytes <= 0 || (bytes & 15) != 0 ||
-      (reinterpret_cast<uintptr_t>(src) & 15) != 0)
+      (reinterpret_cast<uintptr_t>(src) & 15) != 0 || bytes / 16 < kReadGroups)
     return (int)hipErrorInvalidValue;
   hipLaunchKernelGGL(k_stream_read, dim3(kReadGroups), dim3(256), 0, stream,
                      static_cast<const uint4*>(src), bytes / 16, sink);

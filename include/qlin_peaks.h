@@ -17,10 +17,13 @@ extern "C" {
 #endif
 
 /* Streaming read: every 16-byte word of src[0, bytes) is loaded once
- * (bytes a multiple of 16, src 16-byte aligned) and folded into one uint32
- * per work-group, written to sink[0 .. 4095] (so the loads cannot be
- * removed).  grid = 4096 work-groups of 256 threads, grid-stride loop. */
+ * (bytes a multiple of 16 and at least 16 * qlin_peak_read_groups(), src
+ * 16-byte aligned; else hipErrorInvalidValue) and folded into one uint32 per
+ * work-group, written to sink[0 .. qlin_peak_read_groups() - 1] (so the loads
+ * cannot be removed).  Each of the 16384 work-groups of 256 threads reads one
+ * contiguous chunk with 16 loads in flight per thread. */
 int qlin_peak_stream_read(const void* src, int64_t bytes, uint32_t* sink, hipStream_t stream);
+int64_t qlin_peak_read_groups(void);
 
 /* Matrix-core loop: `iters` rounds of 8 independent
  * v_mfma_f32_32x32x16_f16 per wave, no memory traffic in the loop; each wave

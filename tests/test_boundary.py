@@ -425,3 +425,30 @@ def test_binding_refuses_bad_outputs_before_any_launch():
         qlin.gemm_swiglu(w, w, X, None, torch.zeros(4, 128, dtype=torch.float16))
     with pytest.raises(TypeError):
         qlin.gemm_swiglu(w, w, X, torch.zeros(8, 128, dtype=torch.float16), None)
+
+
+PEAKS_HEADER = os.path.join(ROOT, "include", "qlin_peaks.h")
+PEAKS_LIB = os.path.join(ROOT, "group_wise_bit_amd", "libqlin_peaks.so")
+
+
+def test_peaks_header_exports():
+    """The measurement library loads and exports what its header declares;
+    its host-side argument checks refuse bad reads before any launch."""
+    if not os.path.exists(PEAKS_LIB):
+        pytest.skip("libqlin_peaks.so not built")
+    text = re.sub(r"/\*.*?\*/", "", open(PEAKS_HEADER).read(), flags=re.S)
+    declared = sorted(set(re.findall(r"\b(qlin_[a-z0-9_]+)\s*\(", text)))
+    assert declared == ["qlin_peak_mfma", "qlin_peak_mfma_waves", "qlin_peak_read_groups",
+                        "qlin_peak_stream_read"]
+    plib = ctypes.CDLL(PEAKS_LIB)
+    for name in declared:
+        assert hasattr(plib, name), name
+    plib.qlin_peak_read_groups.restype = ctypes.c_int64
+    plib.qlin_peak_mfma_waves.restype = ctypes.c_int64
+    assert plib.qlin_peak_read_groups() == 16384
+    assert plib.qlin_peak_mfma_waves() == 2048
+    plib.qlin_peak_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
+                                           ctypes.c_void_p]
+    for src, nbytes in ((FAKE, 16 * 16384 + 8), (FAKE + 8, 16 * 16384), (FAKE, 16 * 100),
+                        (None, 16 * 16384)):
+        assert plib.qlin_peak_stream_read(src, nbytes, FAKE, None) != 0
