@@ -8,6 +8,7 @@
 #include <string.h>
 
 #include <atomic>
+#include <mutex>
 #include <vector>
 
 #include "../../include/qlin.h"
@@ -566,6 +567,42 @@ int64_t swiglu_ws_bytes(int64_t tiles, int kb, int m) {
 
 }  // namespace
 
+// ------------------------------------------------ no-allocation GEMV --
+// qlin_gemv_noalloc takes its split-K workspace from this file-scope device
+// array instead of a caller's buffer.  Each GPU holds its own copy (device
+// globals are per device) until the process ends; host code reaches it only
+// through the address hipGetSymbolAddress returns on that device (the array's
+// name in host code is not a device address).
+constexpr int64_t kNoAllocScratchBytes = 1 << 20;
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxScratchDevices] = {};
+
+// The current device's copy of `scratch`, looked up once per device.
+qlin_status scratch_address(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) { g_last_hip_error = (int)e; return QLIN_ERR_NO_DEVICE; }
+  if (dev < 0 || dev >= kMaxScratchDevices) return QLIN_ERR_NO_DEVICE;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || ptr == nullptr) return hip_status(e != hipSuccess ? e : hipErrorInvalidSymbol);
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return QLIN_OK;
+}
+
+// Zeroes the split-K arrival counters at the start of the scratch array (a
+// kernel, not hipMemsetAsync, so that a captured call records no memset node).
+__global__ __launch_bounds__(256) void k_clear_counters(uint32_t* __restrict__ c, int n) {
+  for (int i = threadIdx.x + blockIdx.x * 256; i < n; i += gridDim.x * 256) c[i] = 0u;
+}
+
 // Checks shared by the multi-matrix GEMV entry points: `count` packed
 // weights with one k, bits and group; outputs of `out_bytes[i]` bytes that
 // overlap nothing else.
@@ -1031,6 +1068,31 @@ qlin_status qlin_set_launch_override(int32_t family, const int32_t* params) {
                                ((uint64_t)(uint32_t)c << 32),
                            std::memory_order_relaxed);
   return QLIN_OK;
+}
+
+qlin_status qlin_gemv_noalloc(const qlin_weight* w, const uint16_t* x, float* y,
+                              hipStream_t stream) {
+  // host checks first (every error but QLIN_ERR_HIP / NO_DEVICE before any
+  // HIP call), then the scratch array's address on this device
+  qlin_status st = check_weight(w, true, true);
+  if (st != QLIN_OK) return st;
+  if (x == nullptr || y == nullptr) return QLIN_ERR_NULL;
+  const int64_t need = qlin_gemv_workspace_bytes(w);
+  if (need > kNoAllocScratchBytes) return QLIN_ERR_WORKSPACE;
+  st = check_device();
+  if (st != QLIN_OK) return st;
+  void* ws = nullptr;
+  st = scratch_address(&ws);
+  if (st != QLIN_OK) return st;
+  if (need > 0) {
+    // the launch splits K: its arrival counters must start at zero (calls
+    // leave them zero, but the array keeps whatever the last call left)
+    hipLaunchKernelGGL(k_clear_counters, dim3(16), dim3(256), 0, stream,
+                       static_cast<uint32_t*>(ws), (int)(kCounterBytes / 4));
+    st = hip_status(hipGetLastError());
+    if (st != QLIN_OK) return st;
+  }
+  return qlin_gemv(w, x, y, ws, need, stream);
 }
 
 }  // extern "C"

@@ -33,7 +33,7 @@ EXPORTS = (
     "qlin_gemv_multi_workspace_bytes", "qlin_gemv_multi",
     "qlin_gemv_swiglu_workspace_bytes", "qlin_gemv_swiglu", "qlin_embed_rows",
     "qlin_quantize_batch", "qlin_gemm_multi_workspace_bytes", "qlin_gemm_multi",
-    "qlin_gemm_swiglu_workspace_bytes", "qlin_gemm_swiglu",
+    "qlin_gemm_swiglu_workspace_bytes", "qlin_gemm_swiglu", "qlin_gemv_noalloc",
 )
 # include/qlin_tune.h (launch-shape sweeps and tests only)
 TUNE_EXPORTS = ("qlin_set_launch_override",)
@@ -120,6 +120,8 @@ def _lib() -> ctypes.CDLL:
         lib.qlin_gemm_swiglu_workspace_bytes.restype = i64
         lib.qlin_gemm_swiglu.argtypes = [wp, wp, vp, i32, i64, vp, vp, i64, vp, i64, vp]
         lib.qlin_gemm_swiglu.restype = ctypes.c_int
+        lib.qlin_gemv_noalloc.argtypes = [wp, vp, vp, vp]
+        lib.qlin_gemv_noalloc.restype = ctypes.c_int
         lib.qlin_set_launch_override.argtypes = [i32, ctypes.POINTER(i32)]
         lib.qlin_set_launch_override.restype = ctypes.c_int
         _LIB = lib
@@ -291,6 +293,20 @@ def gemv(w: QWeight, x: torch.Tensor, y: Optional[torch.Tensor] = None,
     st = _lib().qlin_gemv(ctypes.byref(ws_struct), x.data_ptr(), y.data_ptr(), _ptr(ws), wsb,
                           _stream())
     _check(st, "qlin_gemv")
+    return y
+
+
+def gemv_noalloc(w: QWeight, x: torch.Tensor, y: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """qlin_gemv_noalloc: qlin_gemv with the library's static split-K scratch
+    (no workspace, no allocation inside the library; y is allocated here only
+    when not given)."""
+    _need_x(w, x)
+    if y is None:
+        y = torch.empty(w.n, dtype=torch.float32, device=x.device)
+    _need_out(y, torch.float32, x.device, 0, w.n, "y")
+    ws_struct = w.c_struct()
+    st = _lib().qlin_gemv_noalloc(ctypes.byref(ws_struct), x.data_ptr(), y.data_ptr(), _stream())
+    _check(st, "qlin_gemv_noalloc")
     return y
 
 

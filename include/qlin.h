@@ -213,6 +213,26 @@ qlin_status qlin_gemm(const qlin_weight* w, const uint16_t* X, int32_t m, int64_
                       hipStream_t stream);
 
 /*
+ * qlin_gemv without any allocation, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): the same GEMV, same launch shapes and results as
+ * qlin_gemv with a workspace of qlin_gemv_workspace_bytes(w), but the split-K
+ * workspace is a static device array inside the library, 1 MiB (1048576
+ * bytes) per GPU, held from the library's load until the process ends.  A
+ * weight whose launch would need more (qlin_gemv_workspace_bytes(w) >
+ * 1048576: a 16-way K split of 256 tiles, for example) returns
+ * QLIN_ERR_WORKSPACE.  The first call on a device looks the array up
+ * (hipGetSymbolAddress); a call whose launch splits K first clears the
+ * array's arrival counters with a small kernel (no memset node, no
+ * allocation).  Every call on one GPU shares that GPU's array: calls that
+ * can run at the same time on one GPU (on different streams) race and must
+ * not be issued; calls on one stream are ordered and safe.  Errors as for
+ * qlin_gemv.
+ */
+qlin_status qlin_gemv_noalloc(const qlin_weight* w, const uint16_t* x, float* y,
+                              hipStream_t stream);
+
+/*
  * Several GEMMs that share X, in one launch (the prefill form of the decode
  * step's grouping: q, k and v, or gate and up, of a layer read the same
  * normalized activations):  Y_i = X . W_i^T,  i = 0 .. count-1, count <= 4.

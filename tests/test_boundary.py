@@ -31,7 +31,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     declared = header_functions()
-    assert len(declared) == 20
+    assert len(declared) == 21
     assert sorted(qlin.EXPORTS) == declared
     for name in declared:
         assert hasattr(lib, name), name
