@@ -456,11 +456,10 @@ __device__ __forceinline__ DeqT<BITS> make_deq_b(float s, int z) {
 // The fp16 range of the matrix-core weight operand.  s * (q - z) rounded to
 // fp16 is infinite once |s (q - z)| >= 65520, which finite fp16 masters of
 // magnitude above 49120 (2 bits) ... 65248 (8 bits) can reach; that needs
-// s >= 65520 / qmax.  Before its K loop, each wave checks the scales of each
-// of its columns over its blocks (needs_wide_operand); a column with such a
-// scale is decoded with s * 2^-8 throughout and its sums are scaled by 2^8 at
-// the end (where waves split K, the work-group's waves agree per column
-// first).  Both scalings are powers of two: the blocks that needed it keep
+// s >= 65520 / qmax.  Before its K loop, a work-group (or wave) scans the
+// scales of its columns over its K range (wide_rows8, wave_row_flag); a
+// column with such a scale is decoded with s * 2^-8 throughout and its sums
+// are scaled by 2^8 at the end.  Both scalings are powers of two: the blocks that needed it keep
 // exactly their rounding (s * 2^-8 >= 1, every nonzero operand normal);
 // small weights elsewhere in that column may lose low bits to fp16
 // underflow, far below the column's large products.  Columns of ordinary
@@ -470,25 +469,64 @@ __device__ __forceinline__ bool maybe_wide(float s) {
   return s >= 65520.f / (float)((1 << BITS) - 1);
 }
 
-// Whether any of the blocks jfirst, jfirst + jstep, ... below j1 of one
-// column has a scale >= 65520 / qmax.  scol points at the column's entry of
-// its tile's first group; G == 1: one scale per row.
-template <int BITS>
-__device__ __forceinline__ bool needs_wide_operand(const uint16_t* __restrict__ scol, int G,
-                                                   int jfirst, int j1, int jstep) {
-  float smax = 0.f;
-  if (G == 1) {
-    smax = jfirst < j1 ? h2f(scol[0]) : 0.f;
-  } else {
-    for (int j0 = jfirst; j0 < j1; j0 += 8 * jstep) {
-      uint16_t v[8];
+// The scan is one memory round trip: a tile's scales of ng consecutive
+// groups are ng * 128 contiguous bytes (s_tile[i]: the first group's entry
+// of row 0 of tile i).  Participant p of np (np a multiple of 8) loads the
+// 16-byte chunks p, p + np, ... of each of the NT tiles -- rows 8 (p % 8) ..
+// + 7 of one group each -- NB per tile at a time, all in flight together
+// (NB * NT * 4 registers), and keeps their largest magnitudes; bit e of
+// f[i]: row 8 (p % 8) + e of tile i has such a scale in one of those chunks.
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+template <int BITS, int NT, int NB = 8>
+__device__ __forceinline__ void wide_rows8(const uint16_t* const (&s_tile)[NT], int ng, int p,
+                                           int np, uint32_t (&f)[NT]) {
+  const int nch = ng * 8;
+  u16x2 mx[NT][4];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) v[i] = scol[(int64_t)min(j0 + i * jstep, j1 - 1) * 64];
+  for (int i = 0; i < NT; ++i)
 #pragma unroll
-      for (int i = 0; i < 8; ++i) smax = __builtin_fmaxf(smax, h2f(v[i]));
+    for (int q = 0; q < 4; ++q) mx[i][q] = (u16x2){0, 0};
+  for (int c0 = p; c0 < nch; c0 += NB * np) {
+    uint4 v[NT][NB];
+#pragma unroll
+    for (int i = 0; i < NT; ++i)
+#pragma unroll
+      for (int k = 0; k < NB; ++k) {
+        const int ch = c0 + k * np;
+        v[i][k] = ch < nch ? reinterpret_cast<const uint4*>(s_tile[i])[ch] : make_uint4(0, 0, 0, 0);
+      }
+#pragma unroll
+    for (int i = 0; i < NT; ++i)
+#pragma unroll
+      for (int k = 0; k < NB; ++k) {
+        const uint32_t w[4] = {v[i][k].x, v[i][k].y, v[i][k].z, v[i][k].w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q)   // magnitudes: the sign bit cleared
+          mx[i][q] = __builtin_elementwise_max(mx[i][q],
+                                               __builtin_bit_cast(u16x2, w[q] & 0x7FFF7FFFu));
+      }
+  }
+#pragma unroll
+  for (int i = 0; i < NT; ++i) {
+    f[i] = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      if (maybe_wide<BITS>(h2f(mx[i][q][0]))) f[i] |= 1u << (2 * q);
+      if (maybe_wide<BITS>(h2f(mx[i][q][1]))) f[i] |= 2u << (2 * q);
     }
   }
-  return maybe_wide<BITS>(smax);
+}
+
+// Whether row r of the tile is flagged, given every lane's wide_rows8
+// result (lane l: rows 8 (l % 8) + e); called by the whole wave.  Almost
+// always no lane has a flag: one ballot.  Otherwise the lanes of equal
+// l % 8 are OR-ed together and each lane reads its row's lane.
+__device__ __forceinline__ bool wave_row_flag(uint32_t f8, int r) {
+  if (__builtin_amdgcn_ballot_w64(f8 != 0) == 0) return false;
+  f8 |= __shfl_xor(f8, 8);
+  f8 |= __shfl_xor(f8, 16);
+  f8 |= __shfl_xor(f8, 32);
+  return (__shfl(f8, r >> 3) >> (r & 7)) & 1u;
 }
 
 constexpr float kWideScale = 0.00390625f;   // 2^-8

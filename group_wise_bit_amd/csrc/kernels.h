@@ -1205,21 +1205,27 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_skinny(
   for (int cg = 0; cg < 4; ++cg) acc[cg] = (f32x4){0.f, 0.f, 0.f, 0.f};
   const bool xrow = c < m;
   const uint16_t* xr = X + (int64_t)(xrow ? c : 0) * ldx;
-  // the fp16 range of the weight operand (maybe_wide): per column, the
-  // work-group's waves agree through LDS
-  float fw[4];
+  // the fp16 range of the weight operand (maybe_wide): the work-group scans
+  // its tile's scales over its K range in one round trip
+  float fw[4] = {1.f, 1.f, 1.f, 1.f};
   {
-    __shared__ float fwl[WAVES][4][64];
+    const int g0 = (G == 1) ? 0 : j0, ng = (G == 1) ? 1 : j1 - j0;
+    const int tid = threadIdx.x;
+    const uint16_t* st[1] = {scale + ((int64_t)t * G + g0) * kTile};
+    uint32_t f8[1];
+    wide_rows8<BITS, 1>(st, ng, tid, WAVES * 64, f8);
+    if (__syncthreads_or(f8[0] != 0)) {
+      // rare: OR the threads' row flags (thread t: rows 8 (t % 8) + e)
+      __shared__ uint32_t fl[8];
+      if (tid < 8) fl[tid] = 0;
+      __syncthreads();
+      if (f8[0] != 0) atomicOr(&fl[tid & 7], f8[0]);
+      __syncthreads();
 #pragma unroll
-    for (int cg = 0; cg < 4; ++cg)
-      fwl[wave][cg][lane] = needs_wide_operand<BITS>(scale + (int64_t)t * G * kTile + 16 * cg + c,
-                                                     G, j0 + wave, j1, WAVES) ? kWideScale : 1.f;
-    __syncthreads();
-#pragma unroll
-    for (int cg = 0; cg < 4; ++cg) {
-      fw[cg] = fwl[0][cg][lane];
-#pragma unroll
-      for (int w = 1; w < WAVES; ++w) fw[cg] = __builtin_fminf(fw[cg], fwl[w][cg][lane]);
+      for (int cg = 0; cg < 4; ++cg) {
+        const int r = 16 * cg + c;
+        if ((fl[r >> 3] >> (r & 7)) & 1u) fw[cg] = kWideScale;
+      }
     }
   }
   for (int jb = j0 + wave; jb < j1; jb += WAVES * U) {
@@ -1433,15 +1439,25 @@ __global__ __launch_bounds__(256) void k_gemm_tiles(
   }
   const uint32_t* wsrc[2];
   int64_t msrc[2];
-  float fw[2];               // the fp16 range of the weight operand (maybe_wide)
 #pragma unroll
   for (int cb = 0; cb < 2; ++cb) {
     const int r = 32 * cb + c;
     wsrc[cb] = codes + ((int64_t)tt * kb * kTile + r) * WPB;
     msrc[cb] = (int64_t)tt * G * kTile + r;
-    fw[cb] = needs_wide_operand<BITS>(scale + msrc[cb], G, ja, ja + nk, 1) ? kWideScale : 1.f;
   }
-  const bool w_wide = __builtin_amdgcn_ballot_w64(fw[0] < 1.f || fw[1] < 1.f) != 0;
+  // the fp16 range of the weight operand (maybe_wide): the wave scans its
+  // tile's scales over the K range in one round trip
+  float fw[2];
+  bool w_wide;
+  {
+    const int g0 = (G == 1) ? 0 : ja, ng = (G == 1) ? 1 : nk;
+    const uint16_t* st[1] = {scale + ((int64_t)tt * G + g0) * kTile};
+    uint32_t f8[1];
+    wide_rows8<BITS, 1>(st, ng, lane, 64, f8);
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) fw[cb] = wave_row_flag(f8[0], 32 * cb + c) ? kWideScale : 1.f;
+    w_wide = __builtin_amdgcn_ballot_w64(f8[0] != 0) != 0;
+  }
 
   u32x4 xv[2][XCH];
   uint32_t wl[2][2][HW];
@@ -1681,26 +1697,42 @@ __global__ __launch_bounds__(256) void k_gemm_ksplit(
       for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[mi][rb][cb][r] = 0.f;
-  // the fp16 range of the weight operand (maybe_wide): each wave checks its
-  // own blocks of each column, the four waves agree through LDS, and the
+  // the fp16 range of the weight operand (maybe_wide): the work-group scans
+  // the scales of its tiles over its K range in one round trip, and the
   // column's sums are scaled back after the reduction
   float fw[NM][CB];
   {
-    __shared__ float fwl[4][NM][CB][64];
+    const int g0 = (G == 1) ? 0 : j0, ng = (G == 1) ? 1 : j1 - j0;
+    const uint16_t* st[NM];
+    uint32_t f8[NM];
+#pragma unroll
+    for (int mi = 0; mi < NM; ++mi)
+      st[mi] = (PAIR ? set.scale[mi] : mat.scale) + ((int64_t)tl[mi] * G + g0) * kTile;
+    wide_rows8<BITS, NM, 8 / NM>(st, ng, tid, 256, f8);
+    uint32_t any = 0;
+#pragma unroll
+    for (int mi = 0; mi < NM; ++mi) any |= f8[mi];
 #pragma unroll
     for (int mi = 0; mi < NM; ++mi)
 #pragma unroll
-      for (int cb = 0; cb < CB; ++cb)
-        fwl[wave][mi][cb][lane] =
-            needs_wide_operand<BITS>(ssrc[mi] + 32 * (cb0 + cb), G, j0 + wave, j1, 4)
-                ? kWideScale : 1.f;
-    __syncthreads();
+      for (int cb = 0; cb < CB; ++cb) fw[mi][cb] = 1.f;
+    if (__syncthreads_or(any != 0)) {
+      // rare: OR the threads' row flags (thread t: rows 8 (t % 8) + e)
+      __shared__ uint32_t fl[NM][8];
+      if (tid < 8 * NM) fl[tid >> 3][tid & 7] = 0;
+      __syncthreads();
 #pragma unroll
-    for (int mi = 0; mi < NM; ++mi)
+      for (int mi = 0; mi < NM; ++mi)
+        if (f8[mi] != 0) atomicOr(&fl[mi][tid & 7], f8[mi]);
+      __syncthreads();
 #pragma unroll
-      for (int cb = 0; cb < CB; ++cb)
-        fw[mi][cb] = __builtin_fminf(__builtin_fminf(fwl[0][mi][cb][lane], fwl[1][mi][cb][lane]),
-                                     __builtin_fminf(fwl[2][mi][cb][lane], fwl[3][mi][cb][lane]));
+      for (int mi = 0; mi < NM; ++mi)
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) {
+          const int r = 32 * (cb0 + cb) + c;
+          if ((fl[mi][r >> 3] >> (r & 7)) & 1u) fw[mi][cb] = kWideScale;
+        }
+    }
   }
 
   for (int jb = j0 + wave; jb < j1; jb += 4 * U) {
@@ -2033,13 +2065,10 @@ __global__ __launch_bounds__(256, 2) void k_gemm_lds(
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[rb][cb][r] = 0.f;
   // the fp16 range of the weight operand over the K range (maybe_wide): the
-  // wave owns its columns, so one operand scale for the wave
+  // wave owns its columns; set after the prologue is issued (below), so the
+  // scan's round trip overlaps the first blocks' loads
   float fw[2];
-#pragma unroll
-  for (int cb = 0; cb < 2; ++cb)
-    fw[cb] = needs_wide_operand<BITS>(scale + (int64_t)tt * G * kTile + 32 * cb + c, G, ja,
-                                      ja + nk, 1) ? kWideScale : 1.f;
-  const bool w_wide = __builtin_amdgcn_ballot_w64(fw[0] < 1.f || fw[1] < 1.f) != 0;
+  bool w_wide;
 
   // Block j from stage I: decode this wave's B operand from the staged codes
   // slice by slice, interleaved with the MFMAs of the previous slice.
@@ -2109,6 +2138,18 @@ __global__ __launch_bounds__(256, 2) void k_gemm_lds(
     constexpr int I = decltype(ic)::value;
     if (I < nk) issue(I, ic);
   });
+  // (the scan's loads complete after the prologue's: by the time its result
+  // is used every load issued so far has landed, so the vmcnt waits of the
+  // pipeline below still count only its own loads)
+  {
+    const int g0 = (G == 1) ? 0 : ja, ng = (G == 1) ? 1 : nk;
+    const uint16_t* st[1] = {scale + ((int64_t)tt * G + g0) * kTile};
+    uint32_t f8[1];
+    wide_rows8<BITS, 1, 8>(st, ng, lane, 64, f8);
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) fw[cb] = wave_row_flag(f8[0], 32 * cb + c) ? kWideScale : 1.f;
+    w_wide = __builtin_amdgcn_ballot_w64(f8[0] != 0) != 0;
+  }
   // the loop body covers S blocks, so every stage index is a constant
   for (int j = 0; j < nk; j += S) {
     static_for<0, S>([&](auto ic) __attribute__((always_inline)) {
@@ -2159,20 +2200,22 @@ __global__ __launch_bounds__(256, 2) void k_gemm_lds(
         for (int r = 0; r < 16; ++r) acc[rb][cb][r] = 0.f;
     const float* pr = part + (wg * NQ * 256 + tid) * 4;
     for (int s2 = 0; s2 < splits; ++s2) {
-      f32x4 v[NQ];
+      // one 32-row block at a time: 8 quads in flight, not all NQ
 #pragma unroll
-      for (int i = 0; i < NQ; ++i)
+      for (int rb = 0; rb < RB; ++rb) {
+        f32x4 v[8];
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          v[i][e] = get_partial(pr + ((int64_t)s2 * groups * NQ + i) * 1024 + e);
+        for (int i = 0; i < 8; ++i)
 #pragma unroll
-      for (int rb = 0; rb < RB; ++rb)
+          for (int e = 0; e < 4; ++e)
+            v[i][e] = get_partial(pr + ((int64_t)s2 * groups * NQ + rb * 8 + i) * 1024 + e);
 #pragma unroll
         for (int cb = 0; cb < 2; ++cb)
 #pragma unroll
           for (int q = 0; q < 4; ++q)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) acc[rb][cb][4 * q + e] += v[(rb * 2 + cb) * 4 + q][e];
+            for (int e = 0; e < 4; ++e) acc[rb][cb][4 * q + e] += v[cb * 4 + q][e];
+      }
     }
   }
 
