@@ -1638,8 +1638,9 @@ __global__ __launch_bounds__(256) void k_gemm_tiles(
 // CB = 1: a work-group covers one 32-row half of each tile (grid.x = half
 // tiles, half = x mod 2), twice the work-groups for a grid too small to fill
 // the chip.
-template <int BITS, int U, int RB, bool PAIR = false, bool DUAL = false, int CB = 2>
-__global__ __launch_bounds__(256) void k_gemm_ksplit(
+template <int BITS, int U, int RB, bool PAIR = false, bool DUAL = false, int CB = 2,
+          int WAVES = 4>
+__global__ __launch_bounds__(WAVES * 64) void k_gemm_ksplit(
     const GemmSet set, const uint16_t* __restrict__ X, int64_t ldx, int m, int kb, int G,
     int splits, int kbps, float* __restrict__ part, uint32_t* __restrict__ tickets) {
   constexpr int WPB = 2 * BITS;
@@ -1649,7 +1650,8 @@ __global__ __launch_bounds__(256) void k_gemm_ksplit(
   static_assert(CB == 2 || !DUAL, "tile pairs take whole tiles");
   constexpr int NM = (PAIR || DUAL) ? 2 : 1; // tiles per work-group
   static_assert(!(PAIR && DUAL), "one of PAIR, DUAL");
-  __shared__ float red[4][NE];
+  constexpr int NT = WAVES * 64;             // threads
+  __shared__ float red[WAVES][NE];
   const int tid = threadIdx.x;
   const int lane = lane_id(), wave = wave_id();
   const int c = lane & 31, h = lane >> 5;
@@ -1708,7 +1710,7 @@ __global__ __launch_bounds__(256) void k_gemm_ksplit(
 #pragma unroll
     for (int mi = 0; mi < NM; ++mi)
       st[mi] = (PAIR ? set.scale[mi] : mat.scale) + ((int64_t)tl[mi] * G + g0) * kTile;
-    wide_rows8<BITS, NM, 8 / NM>(st, ng, tid, 256, f8);
+    wide_rows8<BITS, NM, 8 / NM>(st, ng, tid, NT, f8);
     uint32_t any = 0;
 #pragma unroll
     for (int mi = 0; mi < NM; ++mi) any |= f8[mi];
@@ -1735,14 +1737,14 @@ __global__ __launch_bounds__(256) void k_gemm_ksplit(
     }
   }
 
-  for (int jb = j0 + wave; jb < j1; jb += 4 * U) {
+  for (int jb = j0 + wave; jb < j1; jb += WAVES * U) {
     f16x8 xa[U][RB][4];
     uint32_t wl[U][NM][CB][HW];
     uint16_t sr[U][NM][CB];
     int zc[U][NM][CB];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int j = jb + 4 * u;
+      const int j = jb + WAVES * u;
       const int jj = j < j1 ? j : j1 - 1;     // past the range: re-read, scale 0
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
@@ -1763,7 +1765,7 @@ __global__ __launch_bounds__(256) void k_gemm_ksplit(
     if constexpr (U > 1 || PAIR) loads_issued();
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const bool valid = jb + 4 * u < j1;
+      const bool valid = jb + WAVES * u < j1;
 #pragma unroll
       for (int mi = 0; mi < NM; ++mi)
 #pragma unroll
@@ -1783,7 +1785,8 @@ __global__ __launch_bounds__(256) void k_gemm_ksplit(
     }
   }
   // element e = 1024 (CB rb + cb) + 64 r + lane of a wave's accumulators
-  constexpr int PT = NE / 256;               // elements per thread
+  static_assert(NE % NT == 0, "reduction split");
+  constexpr int PT = NE / NT;                // elements per thread
   float v[NM][PT];
 #pragma unroll
   for (int mi = 0; mi < NM; ++mi) {
@@ -1798,9 +1801,12 @@ __global__ __launch_bounds__(256) void k_gemm_ksplit(
     __syncthreads();
 #pragma unroll
     for (int i = 0; i < PT; ++i) {
-      const int e = tid + 256 * i;
+      const int e = tid + NT * i;
       // (element e's column is this lane's: e % 64 == lane)
-      v[mi][i] = (((red[0][e] + red[1][e]) + red[2][e]) + red[3][e]) *
+      float sum = red[0][e];
+#pragma unroll
+      for (int w = 1; w < WAVES; ++w) sum += red[w][e];   // wave order
+      v[mi][i] = sum *
                  unscale(fw[mi][(e >> 10) % CB]);
     }
   }
@@ -1813,7 +1819,7 @@ __global__ __launch_bounds__(256) void k_gemm_ksplit(
 #pragma unroll
     for (int mi = 0; mi < NM; ++mi)
 #pragma unroll
-      for (int i = 0; i < PT; ++i) put_partial(pw + mi * NE + tid + 256 * i, v[mi][i]);
+      for (int i = 0; i < PT; ++i) put_partial(pw + mi * NE + tid + NT * i, v[mi][i]);
     partials_written();
     __syncthreads();
     __shared__ uint32_t s_last;
@@ -1829,13 +1835,13 @@ __global__ __launch_bounds__(256) void k_gemm_ksplit(
     for (int mi = 0; mi < NM; ++mi)
 #pragma unroll
       for (int i = 0; i < PT; ++i)
-        v[mi][i] = sum_splits(part + (wg * NM + mi) * NE + tid + 256 * i, groups * NM * NE,
+        v[mi][i] = sum_splits(part + (wg * NM + mi) * NE + tid + NT * i, groups * NM * NE,
                               splits);
   }
   const int n = mat.n;
 #pragma unroll
   for (int i = 0; i < PT; ++i) {
-    const int e = tid + 256 * i;
+    const int e = tid + NT * i;
     const int rb = (e >> 10) / CB, cb = (e >> 10) % CB, r = (e >> 6) & 15, l = e & 63;
     const int row = m0 + 32 * rb + 8 * (r >> 2) + 4 * (l >> 5) + (r & 3);
     const int cl = 32 * (cb0 + cb) + (l & 31);

@@ -143,16 +143,48 @@ void launch_gemm_ksplit_rb(const GemmSet& set, const GemmPlan& p, const uint16_t
   const int per_wave = (c.kbps + 3) / 4;
   const dim3 grid(c.gx, c.gy, c.splits);
   if constexpr (RB == 4) {
-    // 128 X rows: one block in flight per wave (the X fragments of a block
-    // take 64 registers), whole or half tiles
-    if (c.half)
-      hipLaunchKernelGGL((k_gemm_ksplit<B, 1, 4, false, false, 1>), grid, dim3(256), 0, st, set,
+    // 128 X rows: the X fragments of a block take 64 registers; two blocks
+    // in flight per wave when the wave has them (one wave per SIMD, up to
+    // 512 registers), whole or half tiles
+    if (c.half) {
+      if (per_wave >= 2)
+        hipLaunchKernelGGL((k_gemm_ksplit<B, 2, 4, false, false, 1>), grid, dim3(256), 0, st,
+                           set, X, ldx, m, p.kb, p.G, c.splits, c.kbps, part, tick);
+      else
+        hipLaunchKernelGGL((k_gemm_ksplit<B, 1, 4, false, false, 1>), grid, dim3(256), 0, st,
+                           set, X, ldx, m, p.kb, p.G, c.splits, c.kbps, part, tick);
+    } else {
+      if (per_wave >= 2)
+        hipLaunchKernelGGL((k_gemm_ksplit<B, 2, 4>), grid, dim3(256), 0, st, set, X, ldx, m,
+                           p.kb, p.G, c.splits, c.kbps, part, tick);
+      else
+        hipLaunchKernelGGL((k_gemm_ksplit<B, 1, 4>), grid, dim3(256), 0, st, set, X, ldx, m,
+                           p.kb, p.G, c.splits, c.kbps, part, tick);
+    }
+  } else {
+  if (c.half && RB == 1 && m <= 16) {
+    // M <= 16 over half tiles: 16 waves split K, as in the decode GEMV, so
+    // that a work-group keeps up to 64 blocks in flight
+    // (a 16-wave work-group caps a wave at 128 registers: four blocks in
+    // flight fit up to 4 bits)
+    const int per16 = (c.kbps + 15) / 16;
+    const dim3 block(1024);
+    bool done = false;
+    if constexpr (B <= 4) {
+      if (per16 >= 4) {
+        hipLaunchKernelGGL((k_gemm_ksplit<B, 4, 1, false, false, 1, 16>), grid, block, 0, st,
+                           set, X, ldx, m, p.kb, p.G, c.splits, c.kbps, part, tick);
+        done = true;
+      }
+    }
+    if (done) {
+    } else if (per16 >= 2)
+      hipLaunchKernelGGL((k_gemm_ksplit<B, 2, 1, false, false, 1, 16>), grid, block, 0, st, set,
                          X, ldx, m, p.kb, p.G, c.splits, c.kbps, part, tick);
     else
-      hipLaunchKernelGGL((k_gemm_ksplit<B, 1, 4>), grid, dim3(256), 0, st, set, X, ldx, m, p.kb,
-                         p.G, c.splits, c.kbps, part, tick);
-  } else {
-  if (c.half) {   // half tiles: half the codes and accumulators per wave
+      hipLaunchKernelGGL((k_gemm_ksplit<B, 1, 1, false, false, 1, 16>), grid, block, 0, st, set,
+                         X, ldx, m, p.kb, p.G, c.splits, c.kbps, part, tick);
+  } else if (c.half) {   // half tiles: half the codes and accumulators per wave
     if (per_wave >= 4 && RB == 1)
       hipLaunchKernelGGL((k_gemm_ksplit<B, 4, RB, false, false, 1>), grid, dim3(256), 0, st, set,
                          X, ldx, m, p.kb, p.G, c.splits, c.kbps, part, tick);
@@ -163,8 +195,10 @@ void launch_gemm_ksplit_rb(const GemmSet& set, const GemmPlan& p, const uint16_t
       hipLaunchKernelGGL((k_gemm_ksplit<B, 1, RB, false, false, 1>), grid, dim3(256), 0, st, set,
                          X, ldx, m, p.kb, p.G, c.splits, c.kbps, part, tick);
   } else if (c.dual) {   // tile pairs: two accumulator sets, so at most 2 blocks in flight
-                         // (1 with 64 X rows, to keep 2 waves per SIMD)
-    if (RB == 1 && per_wave >= 2)
+                         // (1 with 64 X rows, to keep 2 waves per SIMD, unless the grid
+                         // has no more work-groups than CUs: one wave per SIMD anyway)
+    const bool one_per_cu = (int64_t)c.gx * c.gy * c.splits <= 256;
+    if ((RB == 1 || one_per_cu) && per_wave >= 2)
       hipLaunchKernelGGL((k_gemm_ksplit<B, 2, RB, false, true>), grid, dim3(256), 0, st, set, X,
                          ldx, m, p.kb, p.G, c.splits, c.kbps, part, tick);
     else
@@ -215,7 +249,10 @@ void launch_gemm_swiglu(const GemmSet& set, const uint16_t* X, int64_t ldx, int 
     hipLaunchKernelGGL((k_gemm_lds<B, 64, 4, true>), grid, dim3(256), 0, st, set, X, ldx, m, kb,
                        G, c.splits, c.kbps, part, tick);
   else if (c.half) {   // half tiles of both matrices
-    if (c.mb == kMbKsplit128)
+    if (c.mb == kMbKsplit128 && (c.kbps + 3) / 4 >= 2)
+      hipLaunchKernelGGL((k_gemm_ksplit<B, 2, 4, true, false, 1>), grid, dim3(256), 0, st, set,
+                         X, ldx, m, kb, G, c.splits, c.kbps, part, tick);
+    else if (c.mb == kMbKsplit128)
       hipLaunchKernelGGL((k_gemm_ksplit<B, 1, 4, true, false, 1>), grid, dim3(256), 0, st, set,
                          X, ldx, m, kb, G, c.splits, c.kbps, part, tick);
     else if (c.mb == 1)

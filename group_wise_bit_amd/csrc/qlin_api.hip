@@ -210,8 +210,8 @@ GemvCfg gemv_config(int64_t tiles, int kb, GemvKind kind, int bits, int64_t ws_b
   if (splits > 16) splits = 16;
   if (splits > kb) splits = kb;
   if (splits < 1) splits = 1;
-  // QLIN_TUNE_GEMV="waves,splits[,rows]" overrides the choice (launch-shape sweeps)
-  // a launch-shape override (qlin_set_launch_override: sweeps and tests)
+  // a launch-shape override (qlin_set_launch_override: waves, splits, rows;
+  // sweeps and tests) replaces the choice
   {
     int w, sp, rw;
     if (launch_override(QLIN_TUNE_GEMV, w, sp, rw)) {
@@ -413,12 +413,13 @@ TilesCfg tiles_config(int64_t gx, int64_t tiles, int kb, int m, int count, bool 
     // 128-row tiles when that already gives more work-groups than CUs (two
     // fit per CU), else 64 when that fills the chip; a smaller grid takes
     // the K-split kernel (64 X rows) for long K, 32-row tiles for short K
-    // (the K-split kernel with 32 X rows for sets, whose partly filled
-    // four-tile columns idle waves of the tiled kernel)
+    // (also for sets, despite the idle waves of their partly filled
+    // four-tile columns: Qwen2.5-0.5B q/k/v at M = 2048, 20.5 -> 16.6 us
+    // against the K-split kernel over tile pairs)
     c.mb = 128;
     if ((int64_t)c.gx * ((m + 127) / 128) < 288) {
       c.mb = 64;
-      if ((int64_t)c.gx * ((m + 63) / 64) < 256) c.mb = kb >= 32 ? 1 : (count > 1 ? 0 : 32);
+      if ((int64_t)c.gx * ((m + 63) / 64) < 256) c.mb = kb >= 32 ? 1 : 32;
     }
     // the K-split kernel over a tall M reads its X fragments through L1 for
     // every tile: over tile pairs each fragment feeds twice the MFMAs
@@ -426,9 +427,10 @@ TilesCfg tiles_config(int64_t gx, int64_t tiles, int kb, int m, int count, bool 
     // 16.5 us)
     c.dual = c.mb <= 1;
   }
-  // QLIN_TUNE_GEMM="mb,splits" overrides the choice (launch-shape sweeps;
-  // mb = 0 / 1: the K-split kernel with 32 / 64 X rows, 2 / 3: the same with
-  // 64 / 32 X rows over tile pairs, 4 / 5: with 32 / 64 X rows over half tiles)
+  // a GEMM launch-shape override (form, splits; sweeps and tests) replaces
+  // the choice: form 0 / 1 the K-split kernel with 32 / 64 X rows, 2 / 3 the
+  // same with 64 / 32 X rows over tile pairs, 4 / 5 with 32 / 64 X rows over
+  // half tiles, 6 / 7 with 128 X rows (whole / half tiles)
   {
     int mb, sp, unused;
     if (launch_override(QLIN_TUNE_GEMM, mb, sp, unused) && mb != 16) {
@@ -473,7 +475,7 @@ constexpr int kSkinnyMaxM = 16;
 // M <= 16: the K-split kernel (measured 1.1-2.5x faster than the skinny one
 // on the Qwen2.5-0.5B and Qwen3-8B shapes at M = 8, int4; over half tiles it
 // also beats it on long K over few tiles, where the skinny kernel's split
-// used to be cheaper).  QLIN_TUNE_GEMM="16,1" forces the skinny kernel,
+// used to be cheaper).  The GEMM override form 16 forces the skinny kernel,
 // which exists for 2, 3, 4 and 8 bits only.
 bool skinny_by_ksplit(int64_t tiles, int kb, int bits) {
   (void)tiles;
@@ -528,8 +530,8 @@ TilesCfg swiglu_config(int64_t tiles, int kb, int m, int64_t ws_bytes) {
       if (cols2 * ((m + 63) / 64) < 256) c.mb = 1;
     }
   }
-  // QLIN_TUNE_GEMM="mb,splits" overrides the choice (mb 32 runs as 64; 4 / 5:
-  // the K-split pair over half tiles with 32 / 64 X rows)
+  // a GEMM launch-shape override (form, splits) replaces the choice (form 32
+  // runs as 64; 4 / 5: the K-split pair over half tiles with 32 / 64 X rows)
   {
     int mb, sp, unused;
     if (launch_override(QLIN_TUNE_GEMM, mb, sp, unused) &&
