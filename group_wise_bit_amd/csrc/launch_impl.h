@@ -134,6 +134,25 @@ void launch_tiles_mb(const GemmPlan& p, const uint16_t* X, int64_t ldx, int m, T
                        tick);
 }
 
+// One wave per SIMD (no more work-groups than CUs), 32 X rows over whole
+// tiles: two sets of 4 blocks, one loading while the other is decoded.
+// Returns whether it launched.
+template <int B, int RB>
+bool launch_ksplit_db(bool want, dim3 grid, const GemmSet& set, const GemmPlan& p,
+                      const uint16_t* X, int64_t ldx, int m, const TilesCfg& c, float* part,
+                      uint32_t* tick, hipStream_t st) {
+  // 4 bits only: at 3 bits, whose decode costs more, the Qwen3-8B M = 128
+  // GEMMs measured slower with it (6.28 -> 6.37 ms)
+  if constexpr (RB == 1 && B == 4) {
+    if (want) {
+      hipLaunchKernelGGL((k_gemm_ksplit<B, 4, 1, false, false, 2, 4, true>), grid, dim3(256), 0,
+                         st, set, X, ldx, m, p.kb, p.G, c.splits, c.kbps, part, tick);
+      return true;
+    }
+  }
+  return false;
+}
+
 template <int B, int RB>
 void launch_gemm_ksplit_rb(const GemmSet& set, const GemmPlan& p, const uint16_t* X,
                            int64_t ldx, int m, TilesCfg c, float* part, uint32_t* tick,
@@ -142,6 +161,7 @@ void launch_gemm_ksplit_rb(const GemmSet& set, const GemmPlan& p, const uint16_t
   // 64-row X tiles, whose X fragments take twice the registers)
   const int per_wave = (c.kbps + 3) / 4;
   const dim3 grid(c.gx, c.gy, c.splits);
+  const bool one_per_cu = (int64_t)c.gx * c.gy * c.splits <= 256;
   if constexpr (RB == 4) {
     // 128 X rows: the X fragments of a block take 64 registers; two blocks
     // in flight per wave when the wave has them (one wave per SIMD, up to
@@ -196,14 +216,27 @@ void launch_gemm_ksplit_rb(const GemmSet& set, const GemmPlan& p, const uint16_t
                          X, ldx, m, p.kb, p.G, c.splits, c.kbps, part, tick);
   } else if (c.dual) {   // tile pairs: two accumulator sets, so at most 2 blocks in flight
                          // (1 with 64 X rows, to keep 2 waves per SIMD, unless the grid
-                         // has no more work-groups than CUs: one wave per SIMD anyway)
-    const bool one_per_cu = (int64_t)c.gx * c.gy * c.splits <= 256;
-    if ((RB == 1 || one_per_cu) && per_wave >= 2)
+                         // has no more work-groups than CUs: one wave per SIMD anyway,
+                         // and then a second set of 2 blocks loads while one is decoded)
+    bool done = false;
+    // (with 64 X rows a second set would not fit in registers; 4 bits only,
+    // as for whole tiles below)
+    if constexpr (RB == 1 && B == 4) {
+      if (one_per_cu && per_wave >= 4) {
+        hipLaunchKernelGGL((k_gemm_ksplit<B, 2, RB, false, true, 2, 4, true>), grid, dim3(256),
+                           0, st, set, X, ldx, m, p.kb, p.G, c.splits, c.kbps, part, tick);
+        done = true;
+      }
+    }
+    if (done) {
+    } else if ((RB == 1 || one_per_cu) && per_wave >= 2)
       hipLaunchKernelGGL((k_gemm_ksplit<B, 2, RB, false, true>), grid, dim3(256), 0, st, set, X,
                          ldx, m, p.kb, p.G, c.splits, c.kbps, part, tick);
     else
       hipLaunchKernelGGL((k_gemm_ksplit<B, 1, RB, false, true>), grid, dim3(256), 0, st, set, X,
                          ldx, m, p.kb, p.G, c.splits, c.kbps, part, tick);
+  } else if (launch_ksplit_db<B, RB>(one_per_cu && per_wave >= 8, grid, set, p, X, ldx, m, c,
+                                      part, tick, st)) {
   } else if (per_wave >= 4 && RB == 1)
     hipLaunchKernelGGL((k_gemm_ksplit<B, 4, RB>), grid, dim3(256), 0, st, set, X, ldx, m, p.kb,
                        p.G, c.splits, c.kbps, part, tick);
