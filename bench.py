@@ -736,8 +736,6 @@ def main():
                    if head else None,
                    "sections": sections},
         "loop_ms_per_step": round(wall * 1e3 / args.steps, 4),
-        "phases": res,
-        "rooflines": rooflines,
     }
     if not args.no_cpu_baseline and "qwen3_8b" in sections:
         out["cpu_baseline"] = cpu_baseline_c5()
@@ -782,6 +780,9 @@ def main():
         out["achieved_peaks"] = peaks
     if "c1_gemv_latency" in res:
         out["c1_us_per_call"] = round(res["c1_gemv_latency"]["ms_median"] * 1e3 / C1_CALLS, 3)
+    # the per-stage detail last, after every summary key
+    out["phases"] = res
+    out["rooflines"] = rooflines
     print(json.dumps(out), flush=True)
 
 

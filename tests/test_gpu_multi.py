@@ -221,3 +221,22 @@ def test_gemm_multi(bits, ns, k, m):
     again = [host(y) for y in qlin.gemm_multi([q for q, _ in mats], Xd)]
     for a, b in zip(Ys, again):
         assert np.array_equal(a, b)
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4, 8])
+@pytest.mark.parametrize("cfg", ["0,1", "3,1", "4,2", "16,1", "32,1", "64,1", "128,1"])
+@pytest.mark.parametrize("m", [8, 100])
+def test_gemm_multi_forced_forms(bits, cfg, m, launch_override):
+    """A ragged three-matrix set through every GEMM kernel form forced by
+    the launch-shape override, also the tiled kernels at M <= 16 (their
+    launch columns are four-tile columns, not the K-split kernel's tiles):
+    every matrix's Y within tolerance."""
+    launch_override("gemm", cfg)
+    rng = np.random.default_rng([76, bits, m])
+    k = 640
+    mats = [packed(synth.master_weights(rng, n, k), bits, 64) for n in (200, 64, 130)]
+    X = synth.activations(rng, m, k)
+    say(f"gemm_multi forced cfg={cfg} bits={bits} m={m}")
+    Ys = [host(y) for y in qlin.gemm_multi([q for q, _ in mats], dev(X))]
+    for i, (Y, (_, what)) in enumerate(zip(Ys, mats)):
+        check_tol(Y, X, what, f"{cfg} matrix {i}")
