@@ -388,7 +388,14 @@ TilesCfg tiles_config(int64_t gx, int64_t tiles, int kb, int m, int count, bool 
         if (want > 8) want = 8;
         if (want > kb / 8) want = kb / 8;
       } else if (kb >= 128) {
+        // ... but no more work-groups than CUs: the Qwen3-8B down projection
+        // (128 half-tile work-groups, 192 K-blocks) at M = 8 took 19.3 /
+        // 18.3 / 16.3 / 18.5 us at 4 / 3 / 2 / 1 splits (int4; int2, int3,
+        // int8 and M = 16 alike): two splits give 6 K-blocks per wave, four in
+        // flight, one 16-wave work-group per CU
         want = kb / 48;
+        const int64_t fill = groups < 256 ? 256 / groups : 1;
+        if (want > fill) want = (int)fill;
         if (want > 8) want = 8;
       }
     } else if (groups < 256) {
