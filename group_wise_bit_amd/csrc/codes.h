@@ -326,16 +326,20 @@ struct Deq {
   f16x2 c[4];     // (-(1024/S + z), same)
 };
 
-// S = 1, 4, 16, 64 (SH = 2) or S = 1, 2, 4, 8 (SH = 1, a 1-bit plane)
+// S = 1, 4, 16, 64 (SH = 2) or S = 1, 2, 4, 8 (SH = 1, a 1-bit plane); z is
+// a zero point, 0 .. 255.  -(1024 + z) is built as fp16 bits (exponent 10,
+// mantissa z, sign set), and -(1024/S + z) = -(1024 + z) + (1024 - 1024/S)
+// by one fp16 add, exact: both terms and the sum are integers below 2048.
 template <int SH = 2>
 __device__ __forceinline__ Deq make_deq(float s, int z) {
   Deq d;
   const f16 sh = (f16)s;                              // s is an fp16 value (or 0)
   d.s = (f16x2){sh, sh};
+  const f16 c0 = __builtin_bit_cast(f16, (uint16_t)(0xE400u | (uint32_t)z));
 #pragma unroll
   for (int p = 0; p < 4; ++p) {
     const f16 inv = (f16)(1.0f / (float)(1 << (SH * p)));
-    const f16 c = (f16)(-(float)((1024 >> (SH * p)) + z));
+    const f16 c = p == 0 ? c0 : (f16)(c0 + (f16)(float)(1024 - (1024 >> (SH * p))));
     d.inv[p] = (f16x2){inv, inv};
     d.c[p] = (f16x2){c, c};
   }

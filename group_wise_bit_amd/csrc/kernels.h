@@ -1857,9 +1857,17 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_ksplit(
       compute(b1, jb + step);
     }
   }
-  // element e = 1024 (CB rb + cb) + 64 r + lane of a wave's accumulators
-  static_assert(NE % NT == 0, "reduction split");
+  // element e = 1024 (CB rb + cb) + 64 r + lane of a wave's accumulators;
+  // thread tid sums elements e = tid + NT i = lane + 64 (wave + WAVES i), so
+  // (WAVES dividing 16) its block CB rb + cb = WAVES i / 16 is a constant and
+  // its accumulator register r = (WAVES i) % 16 + wave is wave-uniform
+  static_assert(NE % NT == 0 && 16 % WAVES == 0, "reduction split");
   constexpr int PT = NE / NT;                // elements per thread
+  float us[NM][CB];                          // the range factor of each column block
+#pragma unroll
+  for (int mi = 0; mi < NM; ++mi)
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) us[mi][cb] = unscale(fw[mi][cb]);
   float v[NM][PT];
 #pragma unroll
   for (int mi = 0; mi < NM; ++mi) {
@@ -1875,12 +1883,10 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_ksplit(
 #pragma unroll
     for (int i = 0; i < PT; ++i) {
       const int e = tid + NT * i;
-      // (element e's column is this lane's: e % 64 == lane)
       float sum = red[0][e];
 #pragma unroll
       for (int w = 1; w < WAVES; ++w) sum += red[w][e];   // wave order
-      v[mi][i] = sum *
-                 unscale(fw[mi][(e >> 10) % CB]);
+      v[mi][i] = sum * us[mi][((WAVES * i) >> 4) % CB];
     }
   }
   if (splits > 1) {
@@ -1914,10 +1920,10 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_ksplit(
   const int n = mat.n;
 #pragma unroll
   for (int i = 0; i < PT; ++i) {
-    const int e = tid + NT * i;
-    const int rb = (e >> 10) / CB, cb = (e >> 10) % CB, r = (e >> 6) & 15, l = e & 63;
-    const int row = m0 + 32 * rb + 8 * (r >> 2) + 4 * (l >> 5) + (r & 3);
-    const int cl = 32 * (cb0 + cb) + (l & 31);
+    const int rb = ((WAVES * i) >> 4) / CB, cb = ((WAVES * i) >> 4) % CB;
+    const int r = ((WAVES * i) & 15) + wave;
+    const int row = m0 + 32 * rb + 8 * (r >> 2) + 4 * h + (r & 3);
+    const int cl = 32 * (cb0 + cb) + c;
     if (row >= m) continue;
     if constexpr (PAIR) {
       const int col = tm[0] * kTile + cl;
