@@ -1699,43 +1699,21 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_ksplit(
       for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[mi][rb][cb][r] = 0.f;
-  // the fp16 range of the weight operand (maybe_wide): the work-group scans
-  // the scales of its tiles over its K range in one round trip, and the
-  // column's sums are scaled back after the reduction
-  float fw[NM][CB];
-  {
-    const int g0 = (G == 1) ? 0 : j0, ng = (G == 1) ? 1 : j1 - j0;
-    const uint16_t* st[NM];
-    uint32_t f8[NM];
+  // The fp16 range of the weight operand (maybe_wide): a column whose
+  // scales reach 65520 / qmax needs s * 2^-8 as its fp16 operand (and its
+  // sums times 2^8).  The K loop decodes every column with s itself -- exact
+  // for every other column, as a column's sums depend on its own operand
+  // only -- and each thread keeps the largest |s| it loads for its columns
+  // (smax, magnitude bits); after the loop the work-group ORs the flags, and a thread whose
+  // column has such a scale computes that column's sums again with the
+  // scaling (wide_dot; rare).  No scan of its own: scanning the scales
+  // before the loop cost a memory round trip per launch (the Qwen3-8B M = 8
+  // step 1.94 against 1.75 ms).
+  uint32_t smax[NM][CB];
 #pragma unroll
-    for (int mi = 0; mi < NM; ++mi)
-      st[mi] = (PAIR ? set.scale[mi] : mat.scale) + ((int64_t)tl[mi] * G + g0) * kTile;
-    wide_rows8<BITS, NM, 8 / NM>(st, ng, tid, NT, f8);
-    uint32_t any = 0;
+  for (int mi = 0; mi < NM; ++mi)
 #pragma unroll
-    for (int mi = 0; mi < NM; ++mi) any |= f8[mi];
-#pragma unroll
-    for (int mi = 0; mi < NM; ++mi)
-#pragma unroll
-      for (int cb = 0; cb < CB; ++cb) fw[mi][cb] = 1.f;
-    if (__syncthreads_or(any != 0)) {
-      // rare: OR the threads' row flags (thread t: rows 8 (t % 8) + e)
-      __shared__ uint32_t fl[NM][8];
-      if (tid < 8 * NM) fl[tid >> 3][tid & 7] = 0;
-      __syncthreads();
-#pragma unroll
-      for (int mi = 0; mi < NM; ++mi)
-        if (f8[mi] != 0) atomicOr(&fl[mi][tid & 7], f8[mi]);
-      __syncthreads();
-#pragma unroll
-      for (int mi = 0; mi < NM; ++mi)
-#pragma unroll
-        for (int cb = 0; cb < CB; ++cb) {
-          const int r = 32 * (cb0 + cb) + c;
-          if ((fl[mi][r >> 3] >> (r & 7)) & 1u) fw[mi][cb] = kWideScale;
-        }
-    }
-  }
+    for (int cb = 0; cb < CB; ++cb) smax[mi][cb] = 0;
 
   // the operands of U blocks as loaded
   struct Blocks {
@@ -1775,8 +1753,9 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_ksplit(
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb) {
           // (a block past the range gets scale 0; see masked_scale)
+          smax[mi][cb] = max(smax[mi][cb], bk.sr[u][mi][cb] & 0x7FFFu);
           const DeqT<BITS> d = make_deq_b<BITS>(
-              h2f(bk.sr[u][mi][cb]) * (valid ? fw[mi][cb] : 0.f), bk.zc[u][mi][cb]);
+              h2f(bk.sr[u][mi][cb]) * (valid ? 1.f : 0.f), bk.zc[u][mi][cb]);
 #pragma unroll
           for (int s = 0; s < 4; ++s) {
             const f16x8 bf = deq_half<BITS>(bk.wl[u][mi][cb], s, d, magic);
@@ -1825,7 +1804,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_ksplit(
           for (int cb = 0; cb < CB; ++cb) {
             // (a block past the range gets scale 0; see masked_scale)
             const DeqT<BITS> d = make_deq_b<BITS>(
-                h2f(sr[u][mi][cb]) * (valid ? fw[mi][cb] : 0.f), zc[u][mi][cb]);
+                h2f(sr[u][mi][cb]) * (valid ? 1.f : 0.f), zc[u][mi][cb]);
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
               const f16x8 bf = deq_half<BITS>(wl[u][mi][cb], s, d, magic);
@@ -1836,6 +1815,14 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_ksplit(
             }
           }
       }
+      // the largest scale magnitude of this thread's columns (after the
+      // decode, so that it does not change how the loads are scheduled)
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int mi = 0; mi < NM; ++mi)
+#pragma unroll
+          for (int cb = 0; cb < CB; ++cb) smax[mi][cb] = max(smax[mi][cb], sr[u][mi][cb] & 0x7FFFu);
     }
   } else {
     // two operand sets: the next U blocks' loads are in flight while this
@@ -1857,17 +1844,63 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_ksplit(
       compute(b1, jb + step);
     }
   }
+  // The columns that need the operand scale: this thread's flags, OR-ed over
+  // the work-group (bit c of wf[mi][cb]: column 32 (cb0 + cb) + c).
+  uint32_t f = 0;
+#pragma unroll
+  for (int mi = 0; mi < NM; ++mi)
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb)
+      if (maybe_wide<BITS>(h2f((uint16_t)smax[mi][cb]))) f |= 1u << (mi * CB + cb);
+  bool wide[NM][CB];
+#pragma unroll
+  for (int mi = 0; mi < NM; ++mi)
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) wide[mi][cb] = false;
+  const bool any_wide = __syncthreads_or(f != 0);
+  if (any_wide) {
+    // rare
+    __shared__ uint32_t wf[NM * CB];
+    if (tid < NM * CB) wf[tid] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < NM * CB; ++q)
+      if ((f >> q) & 1u) atomicOr(&wf[q], 1u << c);
+    __syncthreads();
+#pragma unroll
+    for (int mi = 0; mi < NM; ++mi)
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) wide[mi][cb] = (wf[mi * CB + cb] >> c) & 1u;
+  }
+  // The sums of matrix mi's column cl (0 .. 63 of its tile) for X row `row`
+  // over this work-group's K range, with the operand scale: each weight as
+  // the fp16 operand s 2^-8 (q - z) (one rounding of the exact product, as
+  // the packed multiply forms it), times x, added in fp32; then times 2^8.
+  auto wide_dot = [&](int mi, int row, int cl) {
+    if (row >= m) return 0.f;
+    const uint32_t* codes = PAIR ? set.codes[mi] : mat.codes;
+    const uint16_t* scale = PAIR ? set.scale[mi] : mat.scale;
+    const uint8_t* zero = PAIR ? set.zero[mi] : mat.zero;
+    const uint16_t* xr = X + (int64_t)row * ldx;
+    float sum = 0.f;
+    for (int j = j0; j < j1; ++j) {
+      const uint32_t* words = codes + (((int64_t)tl[mi] * kb + j) * kTile + cl) * WPB;
+      const int64_t me = ((int64_t)tl[mi] * G + ((G == 1) ? 0 : j)) * kTile + cl;
+      const float sj = h2f(scale[me]) * kWideScale;
+      const int z = zero[me];
+      for (int k = 0; k < kBlock; ++k) {
+        const f16 w = (f16)(sj * (float)((int)code_at<BITS>(words, k) - z));
+        sum += (float)w * h2f(xr[(int64_t)j * kBlock + k]);
+      }
+    }
+    return sum * 256.f;
+  };
   // element e = 1024 (CB rb + cb) + 64 r + lane of a wave's accumulators;
   // thread tid sums elements e = tid + NT i = lane + 64 (wave + WAVES i), so
   // (WAVES dividing 16) its block CB rb + cb = WAVES i / 16 is a constant and
   // its accumulator register r = (WAVES i) % 16 + wave is wave-uniform
   static_assert(NE % NT == 0 && 16 % WAVES == 0, "reduction split");
   constexpr int PT = NE / NT;                // elements per thread
-  float us[NM][CB];                          // the range factor of each column block
-#pragma unroll
-  for (int mi = 0; mi < NM; ++mi)
-#pragma unroll
-    for (int cb = 0; cb < CB; ++cb) us[mi][cb] = unscale(fw[mi][cb]);
   float v[NM][PT];
 #pragma unroll
   for (int mi = 0; mi < NM; ++mi) {
@@ -1886,7 +1919,24 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_ksplit(
       float sum = red[0][e];
 #pragma unroll
       for (int w = 1; w < WAVES; ++w) sum += red[w][e];   // wave order
-      v[mi][i] = sum * us[mi][((WAVES * i) >> 4) % CB];
+      v[mi][i] = sum;
+    }
+    if (any_wide) {
+      // (one copy of the rare loop, its result placed by an unrolled select)
+#pragma nounroll
+      for (int i = 0; i < PT; ++i) {
+        const int rb = ((WAVES * i) >> 4) / CB, cb = ((WAVES * i) >> 4) % CB;
+        const int r = ((WAVES * i) & 15) + wave;
+        bool wc = false;
+#pragma unroll
+        for (int q = 0; q < CB; ++q) wc |= q == cb && wide[mi][q];
+        if (!wc) continue;
+        const float val = wide_dot(mi, m0 + 32 * rb + 8 * (r >> 2) + 4 * h + (r & 3),
+                                   32 * (cb0 + cb) + c);
+#pragma unroll
+        for (int q = 0; q < PT; ++q)
+          if (q == i) v[mi][q] = val;
+      }
     }
   }
   if (splits > 1) {

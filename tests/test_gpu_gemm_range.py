@@ -115,3 +115,43 @@ def test_gemm_swiglu_fp16_operand_range(bits, form, m, launch_override):
     ref = oracle.swiglu_ref(X, wg, wu)
     bound = oracle.swiglu_tolerance(X, wg, wu)
     assert np.all(np.abs(H.astype(np.float64) - ref) <= bound)
+
+
+# The K-split kernel copies the scales of its K range to LDS and checks them
+# after its K loop; a K range whose scales do not fit there is scanned before
+# the loop instead.  These K reach that path: 4-wave work-groups over half
+# tiles (k = 8256, 129 groups), over tile pairs (two tiles' scales), over
+# whole tiles (k = 16448), and the 16-wave form at M <= 16 (k = 33280).
+LONG_K = [("4,1", 40, 8256), ("3,1", 40, 8256), ("0,1", 40, 16448), ("4,1", 8, 33280)]
+
+
+@pytest.mark.parametrize("bits", [2, 4, 8])
+@pytest.mark.parametrize("form,m,k", LONG_K)
+def test_gemm_fp16_operand_range_long_k(bits, form, m, k, launch_override):
+    launch_override("gemm", form)
+    n = 192
+    w16 = masters(bits, 65504, n, k, seed=bits * 11 + m)
+    qw, what = packed(w16, bits)
+    X = synth.activations(np.random.default_rng(m + k), m, k)
+    print(f"gemm range long K bits={bits} form={form} m={m} k={k}", flush=True)
+    check(host(qlin.gemm(qw, dev(X))), X, what, f"long K form={form} m={m} k={k}")
+
+
+@pytest.mark.parametrize("bits", [2, 4, 8])
+def test_gemm_swiglu_fp16_operand_range_long_k(bits, launch_override):
+    """The pair over half tiles holds two tiles' scales: k = 4160 (65 groups)
+    no longer fits, and the pair is scanned before its K loop."""
+    launch_override("gemm", "4,1")
+    n, k, m = 192, 4160, 40
+    wg16 = masters(bits, 65504, n, k, seed=bits + 13)
+    wu16 = synth.master_weights(np.random.default_rng(bits + 14), n, k)
+    gate, wg = packed(wg16, bits)
+    up, wu = packed(wu16, bits)
+    X = synth.activations(np.random.default_rng(m + 7), m, k)
+    print(f"gemm swiglu range long K bits={bits}", flush=True)
+    H, _ = qlin.gemm_swiglu(gate, up, dev(X), want_h16=False)
+    H = host(H)
+    assert np.all(np.isfinite(H))
+    ref = oracle.swiglu_ref(X, wg, wu)
+    bound = oracle.swiglu_tolerance(X, wg, wu)
+    assert np.all(np.abs(H.astype(np.float64) - ref) <= bound)
