@@ -1445,20 +1445,10 @@ __global__ __launch_bounds__(256) void k_gemm_tiles(
     wsrc[cb] = codes + ((int64_t)tt * kb * kTile + r) * WPB;
     msrc[cb] = (int64_t)tt * G * kTile + r;
   }
-  // the fp16 range of the weight operand (maybe_wide): the wave scans its
-  // tile's scales over the K range in one round trip
+  // the fp16 range of the weight operand: scale factor of each column block
+  // (set below, before the first decode) and whether any is scaled
   float fw[2];
   bool w_wide;
-  {
-    const int g0 = (G == 1) ? 0 : ja, ng = (G == 1) ? 1 : nk;
-    const uint16_t* st[1] = {scale + ((int64_t)tt * G + g0) * kTile};
-    uint32_t f8[1];
-    wide_rows8<BITS, 1>(st, ng, lane, 64, f8);
-#pragma unroll
-    for (int cb = 0; cb < 2; ++cb) fw[cb] = wave_row_flag(f8[0], 32 * cb + c) ? kWideScale : 1.f;
-    w_wide = __builtin_amdgcn_ballot_w64(f8[0] != 0) != 0;
-  }
-
   u32x4 xv[2][XCH];
   uint32_t wl[2][2][HW];
   float sc[2][2];
@@ -1536,6 +1526,19 @@ __global__ __launch_bounds__(256) void k_gemm_tiles(
   // loop bodies have no branches.
   issue(0, S0{});
   issue(nk > 1 ? 1 : 0, S1{});
+  // the fp16 range of the weight operand (maybe_wide): the wave scans its
+  // tile's scales over the K range in one round trip, issued after the first
+  // two blocks' loads so that the two round trips overlap
+  {
+    const int g0 = (G == 1) ? 0 : ja, ng = (G == 1) ? 1 : nk;
+    const uint16_t* st[1] = {scale + ((int64_t)tt * G + g0) * kTile};
+    uint32_t f8[1];
+    wide_rows8<BITS, 1>(st, ng, lane, 64, f8);
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) fw[cb] = wave_row_flag(f8[0], 32 * cb + c) ? kWideScale : 1.f;
+    w_wide = __builtin_amdgcn_ballot_w64(f8[0] != 0) != 0;
+  }
+
 #pragma unroll
   for (int i = 0; i < XCH; ++i) land_x(S0{}, i);
 #pragma unroll
