@@ -460,10 +460,13 @@ __device__ __forceinline__ DeqT<BITS> make_deq_b(float s, int z) {
 // The fp16 range of the matrix-core weight operand.  s * (q - z) rounded to
 // fp16 is infinite once |s (q - z)| >= 65520, which finite fp16 masters of
 // magnitude above 49120 (2 bits) ... 65248 (8 bits) can reach; that needs
-// s >= 65520 / qmax.  Before its K loop, a work-group (or wave) scans the
-// scales of its columns over its K range (wide_rows8, wave_row_flag); a
-// column with such a scale is decoded with s * 2^-8 throughout and its sums
-// are scaled by 2^8 at the end.  Both scalings are powers of two: the blocks that needed it keep
+// s >= 65520 / qmax.  A column with such a scale over the work-group's K
+// range is decoded with s * 2^-8 throughout and its sums are scaled by 2^8
+// at the end.  The tiled kernels find those columns before their first
+// decode, by a scan of the scales over the K range (wide_rows8,
+// wave_row_flag); the K-split kernel keeps each column's largest scale as
+// its K loop loads them and computes a flagged column's sums again after
+// the loop.  Both scalings are powers of two: the blocks that needed it keep
 // exactly their rounding (s * 2^-8 >= 1, every nonzero operand normal);
 // small weights elsewhere in that column may lose low bits to fp16
 // underflow, far below the column's large products.  Columns of ordinary
