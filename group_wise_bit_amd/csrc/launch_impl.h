@@ -141,9 +141,9 @@ template <int B, int RB>
 bool launch_ksplit_db(bool want, dim3 grid, const GemmSet& set, const GemmPlan& p,
                       const uint16_t* X, int64_t ldx, int m, const TilesCfg& c, float* part,
                       uint32_t* tick, hipStream_t st) {
-  // 4 bits only: at 3 bits, whose decode costs more, the Qwen3-8B M = 128
-  // GEMMs measured slower with it (6.28 -> 6.37 ms)
-  if constexpr (RB == 1 && B == 4) {
+  // every width (the Qwen3-8B GEMMs at M = 128: int3 6.30 -> 5.91 ms;
+  // down 2 bits 43 -> 34 us, 5 and 8 bits 3-4 % faster, q/k/v alike)
+  if constexpr (RB == 1) {
     if (want) {
       hipLaunchKernelGGL((k_gemm_ksplit<B, 4, 1, false, false, 2, 4, true>), grid, dim3(256), 0,
                          st, set, X, ldx, m, p.kb, p.G, c.splits, c.kbps, part, tick);
@@ -219,9 +219,9 @@ void launch_gemm_ksplit_rb(const GemmSet& set, const GemmPlan& p, const uint16_t
                          // has no more work-groups than CUs: one wave per SIMD anyway,
                          // and then a second set of 2 blocks loads while one is decoded)
     bool done = false;
-    // (with 64 X rows a second set would not fit in registers; 4 bits only,
+    // (with 64 X rows a second set would not fit in registers; every width,
     // as for whole tiles below)
-    if constexpr (RB == 1 && B == 4) {
+    if constexpr (RB == 1) {
       if (one_per_cu && per_wave >= 4) {
         hipLaunchKernelGGL((k_gemm_ksplit<B, 2, RB, false, true, 2, 4, true>), grid, dim3(256),
                            0, st, set, X, ldx, m, p.kb, p.G, c.splits, c.kbps, part, tick);
