@@ -406,12 +406,12 @@ TilesCfg tiles_config(int64_t gx, int64_t tiles, int kb, int m, int count, bool 
   } else if (m <= 256) {
     c.mb = 1;                              // K-split kernel, 64 X rows
   }
-  if (m > 16 && m <= 256 && pairable && bits <= 4 && kb >= 32 &&
-      tiles * ((m + 31) / 32) >= 384) {
+  if (m > 16 && m <= 256 && pairable && kb >= 32 && tiles * ((m + 31) / 32) >= 384) {
     // a large grid of long-K work-groups: 32 X rows over tile pairs, each X
     // fragment feeding twice the MFMAs (Qwen3-8B int4 at M = 128: the gate/up
     // set 61 -> 49 us, the q/k/v set 25 -> 20 us, gate alone 36 -> 32 us;
-    // wider codes, whose decode costs more, gain nothing)
+    // the q/k/v set at 5 / 6 / 8 bits 31.2 / 31.7 / 30.0 -> 28.5 / 28.9 /
+    // 25.0 us)
     c.mb = 0;
     c.half = false;
     c.dual = true;
