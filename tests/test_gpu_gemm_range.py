@@ -155,3 +155,21 @@ def test_gemm_swiglu_fp16_operand_range_long_k(bits, launch_override):
     ref = oracle.swiglu_ref(X, wg, wu)
     bound = oracle.swiglu_tolerance(X, wg, wu)
     assert np.all(np.abs(H.astype(np.float64) - ref) <= bound)
+
+
+@pytest.mark.parametrize("bits", [2, 4, 8])
+@pytest.mark.parametrize("form,m", [(None, 8), (None, 100), ("0,2", 40), ("3,1", 40),
+                                    ("32,1", 300)])
+def test_gemm_fp16_operand_range_per_channel(bits, form, m, launch_override):
+    """Per-channel scales (one group per row, group = k): the extreme rows'
+    single scale needs the operand scaling over the whole K range, in the
+    K-split kernel (one work-group or two splits) and the tiled one."""
+    launch_override("gemm", form)
+    n, k = 192, 1280
+    w16 = masters(bits, 65504, n, k, seed=bits * 5 + m)
+    qw, what = packed(w16, bits, group=k)
+    with np.errstate(over="ignore"):
+        assert not np.all(np.isfinite(what.astype(np.float16)))
+    X = synth.activations(np.random.default_rng(m + 3), m, k)
+    print(f"gemm range per-channel bits={bits} form={form} m={m}", flush=True)
+    check(host(qlin.gemm(qw, dev(X))), X, what, f"per-channel form={form} m={m}")
