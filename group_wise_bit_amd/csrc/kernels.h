@@ -1642,7 +1642,7 @@ __global__ __launch_bounds__(256) void k_gemm_tiles(
 // tiles, half = x mod 2), twice the work-groups for a grid too small to fill
 // the chip.
 template <int BITS, int U, int RB, bool PAIR = false, bool DUAL = false, int CB = 2,
-          int WAVES = 4, bool DB = false>
+          int WAVES = 4>
 __global__ __launch_bounds__(WAVES * 64) void k_gemm_ksplit(
     const GemmSet set, const uint16_t* __restrict__ X, int64_t ldx, int m, int kb, int G,
     int splits, int kbps, float* __restrict__ part, uint32_t* __restrict__ tickets) {
@@ -1718,14 +1718,12 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_ksplit(
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) smax[mi][cb] = 0;
 
-  // the operands of U blocks as loaded
-  struct Blocks {
+  constexpr int step = WAVES * U;
+  for (int jb = j0 + wave; jb < j1; jb += step) {
     f16x8 xa[U][RB][4];
     uint32_t wl[U][NM][CB][HW];
     uint16_t sr[U][NM][CB];
     int zc[U][NM][CB];
-  };
-  auto load = [&](Blocks& bk, int jb) __attribute__((always_inline)) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int j = jb + WAVES * u;
@@ -1734,20 +1732,19 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_ksplit(
       for (int rb = 0; rb < RB; ++rb) {
         const f16x8* xp = reinterpret_cast<const f16x8*>(xrow[rb] + (int64_t)jj * kBlock);
 #pragma unroll
-        for (int s = 0; s < 4; ++s) bk.xa[u][rb][s] = xp[s];
+        for (int s = 0; s < 4; ++s) xa[u][rb][s] = xp[s];
       }
       const int64_t g = (G == 1) ? 0 : jj;
 #pragma unroll
       for (int mi = 0; mi < NM; ++mi)
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb) {
-          load_half<BITS>(wsrc[mi][cb] + (int64_t)jj * kTile * WPB, h, bk.wl[u][mi][cb]);
-          bk.sr[u][mi][cb] = ssrc[mi][32 * (cb0 + cb) + g * kTile];
-          bk.zc[u][mi][cb] = zsrc[mi][32 * (cb0 + cb) + g * kTile];
+          load_half<BITS>(wsrc[mi][cb] + (int64_t)jj * kTile * WPB, h, wl[u][mi][cb]);
+          sr[u][mi][cb] = ssrc[mi][32 * (cb0 + cb) + g * kTile];
+          zc[u][mi][cb] = zsrc[mi][32 * (cb0 + cb) + g * kTile];
         }
     }
-  };
-  auto compute = [&](const Blocks& bk, int jb) __attribute__((always_inline)) {
+    if constexpr (U > 1 || PAIR) loads_issued();
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const bool valid = jb + WAVES * u < j1;
@@ -1756,96 +1753,26 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_ksplit(
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb) {
           // (a block past the range gets scale 0; see masked_scale)
-          smax[mi][cb] = max(smax[mi][cb], bk.sr[u][mi][cb] & 0x7FFFu);
           const DeqT<BITS> d = make_deq_b<BITS>(
-              h2f(bk.sr[u][mi][cb]) * (valid ? 1.f : 0.f), bk.zc[u][mi][cb]);
+              h2f(sr[u][mi][cb]) * (valid ? 1.f : 0.f), zc[u][mi][cb]);
 #pragma unroll
           for (int s = 0; s < 4; ++s) {
-            const f16x8 bf = deq_half<BITS>(bk.wl[u][mi][cb], s, d, magic);
+            const f16x8 bf = deq_half<BITS>(wl[u][mi][cb], s, d, magic);
 #pragma unroll
             for (int rb = 0; rb < RB; ++rb)
-              acc[mi][rb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bk.xa[u][rb][s], bf,
+              acc[mi][rb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(xa[u][rb][s], bf,
                                                                        acc[mi][rb][cb], 0, 0, 0);
           }
         }
     }
-  };
-  constexpr int step = WAVES * U;
-  if constexpr (!DB) {
-    for (int jb = j0 + wave; jb < j1; jb += step) {
-      f16x8 xa[U][RB][4];
-      uint32_t wl[U][NM][CB][HW];
-      uint16_t sr[U][NM][CB];
-      int zc[U][NM][CB];
+    // the largest scale magnitude of this thread's columns (after the
+    // decode, so that it does not change how the loads are scheduled)
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int j = jb + WAVES * u;
-        const int jj = j < j1 ? j : j1 - 1;     // past the range: re-read, scale 0
+    for (int u = 0; u < U; ++u)
 #pragma unroll
-        for (int rb = 0; rb < RB; ++rb) {
-          const f16x8* xp = reinterpret_cast<const f16x8*>(xrow[rb] + (int64_t)jj * kBlock);
+      for (int mi = 0; mi < NM; ++mi)
 #pragma unroll
-          for (int s = 0; s < 4; ++s) xa[u][rb][s] = xp[s];
-        }
-        const int64_t g = (G == 1) ? 0 : jj;
-#pragma unroll
-        for (int mi = 0; mi < NM; ++mi)
-#pragma unroll
-          for (int cb = 0; cb < CB; ++cb) {
-            load_half<BITS>(wsrc[mi][cb] + (int64_t)jj * kTile * WPB, h, wl[u][mi][cb]);
-            sr[u][mi][cb] = ssrc[mi][32 * (cb0 + cb) + g * kTile];
-            zc[u][mi][cb] = zsrc[mi][32 * (cb0 + cb) + g * kTile];
-          }
-      }
-      if constexpr (U > 1 || PAIR) loads_issued();
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const bool valid = jb + WAVES * u < j1;
-#pragma unroll
-        for (int mi = 0; mi < NM; ++mi)
-#pragma unroll
-          for (int cb = 0; cb < CB; ++cb) {
-            // (a block past the range gets scale 0; see masked_scale)
-            const DeqT<BITS> d = make_deq_b<BITS>(
-                h2f(sr[u][mi][cb]) * (valid ? 1.f : 0.f), zc[u][mi][cb]);
-#pragma unroll
-            for (int s = 0; s < 4; ++s) {
-              const f16x8 bf = deq_half<BITS>(wl[u][mi][cb], s, d, magic);
-#pragma unroll
-              for (int rb = 0; rb < RB; ++rb)
-                acc[mi][rb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(xa[u][rb][s], bf,
-                                                                         acc[mi][rb][cb], 0, 0, 0);
-            }
-          }
-      }
-      // the largest scale magnitude of this thread's columns (after the
-      // decode, so that it does not change how the loads are scheduled)
-#pragma unroll
-      for (int u = 0; u < U; ++u)
-#pragma unroll
-        for (int mi = 0; mi < NM; ++mi)
-#pragma unroll
-          for (int cb = 0; cb < CB; ++cb) smax[mi][cb] = max(smax[mi][cb], sr[u][mi][cb] & 0x7FFFu);
-    }
-  } else {
-    // two operand sets: the next U blocks' loads are in flight while this
-    // set is decoded (for grids of one work-group per CU, where no other
-    // wave on the SIMD would cover the memory round trip)
-    // (measured: loads skipped past the range beat unconditional re-reads,
-    // with which the compiler splits a set's loads around the other set's
-    // MFMAs -- Qwen3-8B M = 128 int4 GEMMs 5.70 against 6.02 ms)
-    Blocks b0, b1;
-    int jb = j0 + wave;
-    if (jb < j1) load(b0, jb);
-    for (; jb < j1; jb += 2 * step) {
-      if (jb + step < j1) load(b1, jb + step);
-      loads_issued();
-      compute(b0, jb);
-      if (jb + step >= j1) break;
-      if (jb + 2 * step < j1) load(b0, jb + 2 * step);
-      loads_issued();
-      compute(b1, jb + step);
-    }
+        for (int cb = 0; cb < CB; ++cb) smax[mi][cb] = max(smax[mi][cb], sr[u][mi][cb] & 0x7FFFu);
   }
   // The columns that need the operand scale: this thread's flags, OR-ed over
   // the work-group (bit c of wf[mi][cb]: column 32 (cb0 + cb) + c).

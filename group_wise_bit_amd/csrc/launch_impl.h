@@ -134,19 +134,27 @@ void launch_tiles_mb(const GemmPlan& p, const uint16_t* X, int64_t ldx, int m, T
                        tick);
 }
 
-// One wave per SIMD (no more work-groups than CUs), 32 X rows over whole
-// tiles: two sets of 4 blocks, one loading while the other is decoded.
+// Grids of no more work-groups than CUs, 32 X rows over whole tiles, long K:
+// the work-group's waves split K further -- 8 waves with 4 blocks in flight
+// each, or 16 with 2 for the widths whose decode costs more (3, 5, 6 bits;
+// 7 would spill) -- so that each SIMD runs two or four instruction streams
+// and one wave's decode goes beside another's MFMAs.  (Measured on the
+// Qwen3-8B GEMMs at M = 128, against one wave per SIMD holding two sets of
+// loads: the int4 step 4.29 -> 4.18 ms, int3 4.55 -> 4.40; o and down 7-10 %
+// faster with 16 waves than with 8 at 3 and 5 bits, equal at 2, 4 and 8.)
 // Returns whether it launched.
 template <int B, int RB>
-bool launch_ksplit_db(bool want, dim3 grid, const GemmSet& set, const GemmPlan& p,
-                      const uint16_t* X, int64_t ldx, int m, const TilesCfg& c, float* part,
-                      uint32_t* tick, hipStream_t st) {
-  // every width (the Qwen3-8B GEMMs at M = 128: int3 6.30 -> 5.91 ms;
-  // down 2 bits 43 -> 34 us, 5 and 8 bits 3-4 % faster, q/k/v alike)
+bool launch_ksplit_one_cu(bool want, dim3 grid, const GemmSet& set, const GemmPlan& p,
+                          const uint16_t* X, int64_t ldx, int m, const TilesCfg& c, float* part,
+                          uint32_t* tick, hipStream_t st) {
   if constexpr (RB == 1) {
     if (want) {
-      hipLaunchKernelGGL((k_gemm_ksplit<B, 4, 1, false, false, 2, 4, true>), grid, dim3(256), 0,
-                         st, set, X, ldx, m, p.kb, p.G, c.splits, c.kbps, part, tick);
+      if constexpr (B == 3 || B == 5 || B == 6)
+        hipLaunchKernelGGL((k_gemm_ksplit<B, 2, 1, false, false, 2, 16>), grid, dim3(1024), 0,
+                           st, set, X, ldx, m, p.kb, p.G, c.splits, c.kbps, part, tick);
+      else
+        hipLaunchKernelGGL((k_gemm_ksplit<B, 4, 1, false, false, 2, 8>), grid, dim3(512), 0, st,
+                           set, X, ldx, m, p.kb, p.G, c.splits, c.kbps, part, tick);
       return true;
     }
   }
@@ -216,15 +224,15 @@ void launch_gemm_ksplit_rb(const GemmSet& set, const GemmPlan& p, const uint16_t
                          X, ldx, m, p.kb, p.G, c.splits, c.kbps, part, tick);
   } else if (c.dual) {   // tile pairs: two accumulator sets, so at most 2 blocks in flight
                          // (1 with 64 X rows, to keep 2 waves per SIMD, unless the grid
-                         // has no more work-groups than CUs: one wave per SIMD anyway,
-                         // and then a second set of 2 blocks loads while one is decoded)
+                         // has no more work-groups than CUs: one wave per SIMD anyway)
     bool done = false;
-    // (with 64 X rows a second set would not fit in registers; every width,
-    // as for whole tiles below)
+    // a grid of no more work-groups than CUs, 32 X rows: 8 waves split K, two
+    // instruction streams per SIMD (the Qwen3-8B q/k/v set at M = 128: 20.4
+    // us, against 24.4 with 16 waves of one block)
     if constexpr (RB == 1) {
       if (one_per_cu && per_wave >= 4) {
-        hipLaunchKernelGGL((k_gemm_ksplit<B, 2, RB, false, true, 2, 4, true>), grid, dim3(256),
-                           0, st, set, X, ldx, m, p.kb, p.G, c.splits, c.kbps, part, tick);
+        hipLaunchKernelGGL((k_gemm_ksplit<B, 2, RB, false, true, 2, 8>), grid, dim3(512), 0, st,
+                           set, X, ldx, m, p.kb, p.G, c.splits, c.kbps, part, tick);
         done = true;
       }
     }
@@ -235,8 +243,8 @@ void launch_gemm_ksplit_rb(const GemmSet& set, const GemmPlan& p, const uint16_t
     else
       hipLaunchKernelGGL((k_gemm_ksplit<B, 1, RB, false, true>), grid, dim3(256), 0, st, set, X,
                          ldx, m, p.kb, p.G, c.splits, c.kbps, part, tick);
-  } else if (launch_ksplit_db<B, RB>(one_per_cu && per_wave >= 8, grid, set, p, X, ldx, m, c,
-                                      part, tick, st)) {
+  } else if (launch_ksplit_one_cu<B, RB>(one_per_cu && per_wave >= 8, grid, set, p, X, ldx, m,
+                                          c, part, tick, st)) {
   } else if (per_wave >= 4 && RB == 1)
     hipLaunchKernelGGL((k_gemm_ksplit<B, 4, RB>), grid, dim3(256), 0, st, set, X, ldx, m, p.kb,
                        p.G, c.splits, c.kbps, part, tick);
