@@ -235,6 +235,12 @@ void launch_gemm_ksplit_rb(const GemmSet& set, const GemmPlan& p, const uint16_t
                            set, X, ldx, m, p.kb, p.G, c.splits, c.kbps, part, tick);
         done = true;
       }
+    } else if constexpr (B != 5) {   // (64 X rows at 5 bits would spill)
+      if (one_per_cu && per_wave >= 4) {
+        hipLaunchKernelGGL((k_gemm_ksplit<B, 1, RB, false, true, 2, 8>), grid, dim3(512), 0, st,
+                           set, X, ldx, m, p.kb, p.G, c.splits, c.kbps, part, tick);
+        done = true;
+      }
     }
     if (done) {
     } else if ((RB == 1 || one_per_cu) && per_wave >= 2)
