@@ -1923,6 +1923,379 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_ksplit(
 }
 
 
+// ------------------------------- GEMM, weights decoded once per work-group --
+// Work-group = KG groups of 4 waves over 128 X rows x two 64-row W tiles
+// (PAIR: tile t of gate and of up; otherwise tiles 2x and 2x + 1 of one matrix
+// of the set, a tile past the matrix re-reading its last one and never
+// stored).  Group g takes the K-blocks j0 + g, j0 + g + KG, ... of the
+// work-group's range.  Per K-block, wave q of the group decodes column block q
+// -- 32 W rows (32 (q % 2) + c of tile q / 2) x 64 K -- into the group's LDS
+// buffers as the MFMA B fragments (lane (c, h), instruction s: K positions
+// 32h + 8s .. +7), so each weight is decoded once per work-group; every wave
+// of the group multiplies its 32 X rows (A fragments straight from global
+// memory; lane (c, h): X row 32q + c) by all four column blocks: 16 MFMAs per
+// wave per K-block against one block decode.  The wave decodes its next block
+// between the MFMAs of the current one, into the other of its group's two
+// buffers: a wave that writes a buffer has passed the barrier that every wave
+// reaches only after multiplying the block that buffer held before, so one
+// barrier per step suffices.  The codes, scales and zeros of the group's next
+// D blocks and the X fragments of its next block are in flight meanwhile.
+// With KG = 2 each SIMD runs two instruction streams (one wave of each
+// group); the groups meet at every step's barrier (a group with no block
+// left in a step only takes part in the barrier) and finally add their sums
+// through LDS, group 0's first; then group g finishes column half g of both
+// tiles.
+// The fp16 range of the operand as in k_gemm_ksplit: a decoding wave keeps
+// its column's largest scale, and after the loop a flagged column's sums are
+// computed again with the operand scale 2^-8.  Split K: partials per
+// work-group in thread order, the last work-group of a tile adds the splits
+// in order 0, 1, ...
+template <int BITS, bool PAIR, int D, int KG>
+__global__ __launch_bounds__(KG * 256) void k_gemm_wdec(
+    const GemmSet set, const uint16_t* __restrict__ X, int64_t ldx, int m, int kb, int G,
+    int splits, int kbps, float* __restrict__ part, uint32_t* __restrict__ tickets) {
+  constexpr int WPB = 2 * BITS;
+  constexpr int HW = WPB / 2;                // words of a half block
+  static_assert(D == 2 || D == 4 || D == 8, "blocks in flight");
+  static_assert(KG == 1 || KG == 2, "K groups");
+  __shared__ f16x8 frag[KG][2][16][64];      // [group][buffer][4 column block + s][lane]
+  __shared__ f16x8 xs[KG][2][128 * 8];       // [group][buffer][X row: 8 chunks of 16 bytes]
+  __shared__ uint32_t wf[4];
+  const int tid = threadIdx.x;
+  const int lane = lane_id(), wave = wave_id();
+  const int grp = wave >> 2, q = wave & 3;   // K group, wave within it
+  const int c = lane & 31, h = lane >> 5;
+  const GemmMat mat = gemm_mat(set, blockIdx.x);
+  int tm[2], tl[2];
+#pragma unroll
+  for (int mi = 0; mi < 2; ++mi) {
+    tm[mi] = PAIR ? mat.col : 2 * mat.col + mi;
+    tl[mi] = min(tm[mi], mat.tiles - 1);
+  }
+  const uint32_t magic = vreg_const(kMagic);
+  const int j0 = blockIdx.z * kbps;
+  const int j1 = min(kb, j0 + kbps);
+  // this group's blocks: jg, jg + KG, ... (cnt of them); steps = the first
+  // group's count, so that every wave meets the same barriers
+  const int jg = j0 + grp;
+  const int cnt = jg < j1 ? (j1 - jg + KG - 1) / KG : 0;
+  const int steps = (j1 - j0 + KG - 1) / KG;
+  // the column block this wave decodes: tile dm, rows 32 dcb ..
+  const int dm = q >> 1, dcb = q & 1;
+  const uint32_t* dcodes = PAIR ? (dm ? set.codes[1] : set.codes[0]) : mat.codes;
+  const uint16_t* dscale = PAIR ? (dm ? set.scale[1] : set.scale[0]) : mat.scale;
+  const uint8_t* dzero = PAIR ? (dm ? set.zero[1] : set.zero[0]) : mat.zero;
+  const int dt = dm ? tl[1] : tl[0];
+  const uint32_t* wsrc = dcodes + ((int64_t)dt * kb * kTile + 32 * dcb + c) * WPB;
+  const int64_t mt = (int64_t)dt * G * kTile + 32 * dcb + c;
+  const uint16_t* ssrc = dscale + mt;
+  const uint8_t* zsrc = dzero + mt;
+  // X staging: thread t of the group copies the 16-byte chunks xk = t % 8 of
+  // rows t / 8 + 32i (i = 0..3) of the block's 128 x 64 X tile into LDS, where
+  // chunk k of row r sits at position k ^ (r % 8) of the row, so that both
+  // these writes and the A-fragment reads (lanes c = 0..7 of a wave: rows
+  // r + c, one chunk each) fall on distinct banks; rows past m read row m0
+  // (never stored)
+  const int m0 = blockIdx.y * 128;
+  const int t8 = (tid & 255) >> 3, xk = tid & 7;
+  const uint16_t* xsrc[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = m0 + t8 + 32 * i;
+    xsrc[i] = X + (int64_t)(r < m ? r : m0) * ldx + 8 * xk;
+  }
+  const int xw = 8 * t8 + (xk ^ (t8 & 7));
+  f16x8(*gfrag)[16][64] = frag[KG == 1 ? 0 : grp];
+  f16x8(*gxs)[128 * 8] = xs[KG == 1 ? 0 : grp];
+
+  uint32_t wl[D][HW];
+  uint16_t sr[D];
+  int zc[D];
+  f16x8 xg[D][4];
+  uint32_t smax = 0;
+  // The group's block i (clamped to its last) into register slot u: this
+  // thread's codes, scale and zero, and its four X chunks.  Both are requested
+  // D steps ahead: loads complete in order, so a wait for one load is a wait
+  // for every older one as well.
+  auto request = [&](auto U, int i) __attribute__((always_inline)) {
+    constexpr int u = decltype(U)::value;
+    const int jj = min(jg + KG * max(0, min(i, cnt - 1)), j1 - 1);
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      xg[u][k] = *reinterpret_cast<const f16x8*>(xsrc[k] + (int64_t)jj * kBlock);
+    load_half<BITS>(wsrc + (int64_t)jj * kTile * WPB, h, wl[u]);
+    const int64_t g = (G == 1) ? 0 : jj;
+    sr[u] = ssrc[g * kTile];
+    zc[u] = zsrc[g * kTile];
+  };
+  // slot u's X chunks into the LDS buffer b
+  auto store_x = [&](auto U, int b) __attribute__((always_inline)) {
+    constexpr int u = decltype(U)::value;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) gxs[b][xw + 256 * k] = xg[u][k];
+  };
+  auto deq_of = [&](auto U) __attribute__((always_inline)) {
+    constexpr int u = decltype(U)::value;
+    smax = max(smax, (uint32_t)(sr[u] & 0x7FFFu));
+    return make_deq_b<BITS>(h2f(sr[u]), zc[u]);
+  };
+
+  f32x16 acc[4];
+#pragma unroll
+  for (int f = 0; f < 4; ++f)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[f][r] = 0.f;
+  // prologue: the group's first D blocks of codes and the X of its first
+  // block requested, its first block decoded into buffer 0, the codes of its
+  // block D requested into that slot
+  request(std::integral_constant<int, 0>(), 0);
+  request(std::integral_constant<int, 1>(), 1);
+  if constexpr (D > 2) {
+    request(std::integral_constant<int, 2>(), 2);
+    request(std::integral_constant<int, 3>(), 3);
+  }
+  if constexpr (D > 4) {
+    request(std::integral_constant<int, 4>(), 4);
+    request(std::integral_constant<int, 5>(), 5);
+    request(std::integral_constant<int, 6>(), 6);
+    request(std::integral_constant<int, 7>(), 7);
+  }
+  loads_issued();
+  if (cnt > 0) {
+    const DeqT<BITS> d = deq_of(std::integral_constant<int, 0>());
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+      gfrag[0][4 * q + s][lane] = deq_half<BITS>(wl[0], s, d, magic);
+  }
+  store_x(std::integral_constant<int, 0>(), 0);
+  request(std::integral_constant<int, 0>(), D);
+  loads_issued();
+  lds_barrier();
+  // Step i (the group's block i: its X tile and B fragments in buffer i % 2):
+  // the wave multiplies block i while it decodes block i + 1 (register slot
+  // (i + 1) % D) into the other buffer, stores its X chunks of block i + 1
+  // there, requests block i + 1 + D into that slot, and meets every wave at
+  // the barrier.  `have`: block i exists;
+  // `more`: block i + 1 exists; `sync`: step i + 1 exists.
+  auto step = [&](auto U, int i, bool have, bool more, bool sync) __attribute__((always_inline)) {
+    constexpr int u = decltype(U)::value;
+    constexpr int un = (u + 1) % D;
+    const std::integral_constant<int, un> UN;
+    f16x8(*fb)[64] = gfrag[i & 1];
+    const f16x8* xb = gxs[i & 1] + 8 * (32 * q + c);
+    f16x8(*fn)[64] = gfrag[(i + 1) & 1];
+    DeqT<BITS> d;
+    if (more) d = deq_of(UN);
+    if (have) {
+      f16x8 bq[2][4];
+#pragma unroll
+      for (int f = 0; f < 4; ++f) bq[0][f] = fb[4 * f][lane];
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const f16x8 a = xb[(4 * h + s) ^ (c & 7)];
+        if (s + 1 < 4) {
+#pragma unroll
+          for (int f = 0; f < 4; ++f) bq[(s + 1) & 1][f] = fb[4 * f + s + 1][lane];
+        }
+#pragma unroll
+        for (int f = 0; f < 4; ++f)
+          acc[f] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, bq[s & 1][f], acc[f], 0, 0, 0);
+        if (more) fn[4 * q + s][lane] = deq_half<BITS>(wl[un], s, d, magic);
+      }
+    }
+    if (more) {
+      store_x(UN, (i + 1) & 1);
+      request(UN, i + 1 + D);
+    }
+    loads_issued();
+    if (sync) lds_barrier();
+  };
+  // full rounds of D steps in which every group has its block and the next,
+  // then the rest
+  const int full = (KG == 1 ? cnt : min(cnt, (j1 - j0) / KG)) - 1;   // steps with `more` in all groups
+  int i0 = 0;
+  for (; i0 + D <= full; i0 += D) {
+    step(std::integral_constant<int, 0>(), i0, true, true, true);
+    step(std::integral_constant<int, 1>(), i0 + 1, true, true, true);
+    if constexpr (D > 2) {
+      step(std::integral_constant<int, 2>(), i0 + 2, true, true, true);
+      step(std::integral_constant<int, 3>(), i0 + 3, true, true, true);
+    }
+    if constexpr (D > 4) {
+      step(std::integral_constant<int, 4>(), i0 + 4, true, true, true);
+      step(std::integral_constant<int, 5>(), i0 + 5, true, true, true);
+      step(std::integral_constant<int, 6>(), i0 + 6, true, true, true);
+      step(std::integral_constant<int, 7>(), i0 + 7, true, true, true);
+    }
+  }
+  // the remaining steps i0 .. steps - 1 (fewer than 2D)
+#pragma unroll
+  for (int r = 0; r < 2 * D; ++r) {
+    const int i = i0 + r;
+    if (i >= steps) break;
+    // (slot (i0 + r) % D = r % D: i0 is a multiple of D)
+    auto go = [&](auto U) __attribute__((always_inline)) {
+      step(U, i, i < cnt, i + 1 < cnt, i + 1 < steps);
+    };
+    switch (r % D) {
+      case 0: go(std::integral_constant<int, 0>()); break;
+      case 1: go(std::integral_constant<int, 1 % D>()); break;
+      case 2: go(std::integral_constant<int, 2 % D>()); break;
+      case 3: go(std::integral_constant<int, 3 % D>()); break;
+      case 4: go(std::integral_constant<int, 4 % D>()); break;
+      case 5: go(std::integral_constant<int, 5 % D>()); break;
+      case 6: go(std::integral_constant<int, 6 % D>()); break;
+      default: go(std::integral_constant<int, 7 % D>()); break;
+    }
+  }
+
+  // Column blocks this thread finishes: all four (KG = 1), or half g of both
+  // tiles (f = g, 2 + g) in group g, after the groups add their sums.
+  auto keep = [&](int f) __attribute__((always_inline)) { return KG == 1 || (f & 1) == grp; };
+  if constexpr (KG == 2) {
+    // every wave is past its last multiply before the buffers are reused
+    lds_barrier();
+    float* red = reinterpret_cast<float*>(&frag[0][0][0][0]);   // [group][2][16][256]
+    const int t = tid & 255;
+#pragma unroll
+    for (int f = 0; f < 4; ++f) {
+      if (keep(f)) continue;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) red[((grp * 2 + (f >> 1)) * 16 + r) * 256 + t] = acc[f][r];
+    }
+    lds_barrier();
+#pragma unroll
+    for (int f = 0; f < 4; ++f) {
+      if (!keep(f)) continue;
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        acc[f][r] += red[(((1 - grp) * 2 + (f >> 1)) * 16 + r) * 256 + t];
+    }
+  }
+
+  // Columns that need the operand scale: bit c of wf[q] for column c of
+  // column block q (found by the waves that decode it).
+  const bool mine = maybe_wide<BITS>(h2f((uint16_t)smax));
+  if (__syncthreads_or(mine)) {
+    // rare
+    if (tid < 4) wf[tid] = 0;
+    __syncthreads();
+    if (mine) atomicOr(&wf[q], 1u << c);
+    __syncthreads();
+    uint32_t fl[4];
+#pragma unroll
+    for (int f = 0; f < 4; ++f) fl[f] = keep(f) ? wf[f] : 0u;
+#pragma nounroll
+    for (int i = 0; i < 64; ++i) {
+      const int f = i >> 4, r = i & 15;
+      const uint32_t ff = f == 0 ? fl[0] : f == 1 ? fl[1] : f == 2 ? fl[2] : fl[3];
+      if (!((ff >> c) & 1u)) continue;
+      const int row = m0 + 32 * q + 8 * (r >> 2) + 4 * h + (r & 3);
+      if (row >= m) continue;
+      const int mi = f >> 1, cl = 32 * (f & 1) + c;
+      const uint32_t* codes = PAIR ? (mi ? set.codes[1] : set.codes[0]) : mat.codes;
+      const uint16_t* scale = PAIR ? (mi ? set.scale[1] : set.scale[0]) : mat.scale;
+      const uint8_t* zero = PAIR ? (mi ? set.zero[1] : set.zero[0]) : mat.zero;
+      const int t = mi ? tl[1] : tl[0];
+      const uint16_t* xw = X + (int64_t)row * ldx;
+      // each weight as the fp16 operand s 2^-8 (q - z), times x, added in
+      // fp32, then times 2^8
+      float sum = 0.f;
+      for (int j = j0; j < j1; ++j) {
+        const uint32_t* words = codes + (((int64_t)t * kb + j) * kTile + cl) * WPB;
+        const int64_t me = ((int64_t)t * G + ((G == 1) ? 0 : j)) * kTile + cl;
+        const float sj = h2f(scale[me]) * kWideScale;
+        const int z = zero[me];
+        for (int k = 0; k < kBlock; ++k) {
+          const f16 w = (f16)(sj * (float)((int)code_at<BITS>(words, k) - z));
+          sum += (float)w * h2f(xw[(int64_t)j * kBlock + k]);
+        }
+      }
+      sum *= 256.f;
+#pragma unroll
+      for (int e = 0; e < 64; ++e)
+        if (e == i) acc[e >> 4][e & 15] = sum;
+    }
+  }
+
+  if (splits > 1) {
+    // partials [split][work-group][4 column block + register][thread of the group]
+    constexpr int NE = 4 * 16 * 256;
+    const int t = tid & 255;
+    const int64_t wg = (int64_t)blockIdx.y * gridDim.x + blockIdx.x;
+    const int64_t groups = (int64_t)gridDim.x * gridDim.y;
+    float* pw = part + (blockIdx.z * groups + wg) * NE + t;
+#pragma unroll
+    for (int f = 0; f < 4; ++f) {
+      if (!keep(f)) continue;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) put_partial(pw + (f * 16 + r) * 256, acc[f][r]);
+    }
+    partials_written();
+    __syncthreads();
+    __shared__ uint32_t s_last;
+    if (tid == 0) {
+      const uint32_t prev = __hip_atomic_fetch_add(&tickets[wg], 1u, __ATOMIC_RELAXED,
+                                                   __HIP_MEMORY_SCOPE_AGENT);
+      s_last = prev == (uint32_t)(splits - 1);
+      if (s_last) __hip_atomic_store(&tickets[wg], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __syncthreads();
+    if (!s_last) return;
+    // one column block at a time, the loads of up to 8 splits in flight
+    const float* pr = part + wg * NE + t;
+#pragma unroll
+    for (int f = 0; f < 4; ++f) {
+      if (!keep(f)) continue;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[f][r] = 0.f;
+      for (int b = 0; b < splits; b += 8) {
+        float v[8][16];
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            v[i][r] = get_partial(pr + (int64_t)min(b + i, splits - 1) * groups * NE +
+                                  (f * 16 + r) * 256);
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          if (b + i < splits)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[f][r] += v[i][r];
+      }
+    }
+  }
+
+  // element r of column block f: row m0 + 32q + 8 (r / 4) + 4h + r % 4,
+  // column 32 (f % 2) + c of tile tm[f / 2]
+  const int n = mat.n;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int row = m0 + 32 * q + 8 * (r >> 2) + 4 * h + (r & 3);
+    if (row >= m) continue;
+    if constexpr (PAIR) {
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb) {
+        if (!keep(cb)) continue;
+        const int col = tm[0] * kTile + 32 * cb + c;
+        if (col >= n) continue;
+        const int64_t o = (int64_t)row * mat.ldy + col;
+        const float hv = silu(acc[cb][r]) * acc[2 + cb][r];
+        if (mat.y != nullptr) mat.y[o] = hv;
+        if (set.h16 != nullptr) set.h16[o] = __builtin_bit_cast(uint16_t, (f16)hv);
+      }
+    } else {
+#pragma unroll
+      for (int f = 0; f < 4; ++f) {
+        if (!keep(f)) continue;
+        const int col = tm[f >> 1] * kTile + 32 * (f & 1) + c;
+        if (col < n) mat.y[(int64_t)row * mat.ldy + col] = acc[f][r];
+      }
+    }
+  }
+}
+
+
 // ------------------------------------------------- embedding-row gather --
 // Rows ids[i] of a packed weight, dequantized: out32 = s*(q - z) (exact in
 // fp32), out16 = that value rounded to fp16 (nearest even).  One work-group

@@ -279,7 +279,13 @@ void launch_gemm_ksplit(const GemmPlan& p, const uint16_t* X, int64_t ldx, int m
 template <int B>
 void launch_gemm_tiles(const GemmPlan& p, const uint16_t* X, int64_t ldx, int m, TilesCfg c,
                        float* part, uint32_t* tick, hipStream_t st) {
-  if (is_ksplit(c.mb)) launch_gemm_ksplit<B>(p, X, ldx, m, c, part, tick, st);
+  if (c.mb == kMbWdec) {
+    // launch columns are tile pairs within each matrix (pairable sets)
+    GemmSet set = p.set;
+    for (int i = 0; i < set.count; ++i) set.end[i] = (p.end_tiles[i] + 1) / 2;
+    hipLaunchKernelGGL((k_gemm_wdec<B, false, 4, 2>), dim3(c.gx, c.gy, c.splits), dim3(512), 0, st,
+                       set, X, ldx, m, p.kb, p.G, c.splits, c.kbps, part, tick);
+  } else if (is_ksplit(c.mb)) launch_gemm_ksplit<B>(p, X, ldx, m, c, part, tick, st);
   else if (c.mb == 32) launch_tiles_mb<B, 32>(p, X, ldx, m, c, part, tick, st);
   else if (c.mb == 64) launch_tiles_mb<B, 64>(p, X, ldx, m, c, part, tick, st);
   else launch_tiles_mb<B, 128>(p, X, ldx, m, c, part, tick, st);
@@ -289,7 +295,10 @@ template <int B>
 void launch_gemm_swiglu(const GemmSet& set, const uint16_t* X, int64_t ldx, int m, int kb, int G,
                         TilesCfg c, float* part, uint32_t* tick, hipStream_t st) {
   const dim3 grid(c.gx, c.gy, c.splits);
-  if (c.mb == 128)
+  if (c.mb == kMbWdec)
+    hipLaunchKernelGGL((k_gemm_wdec<B, true, 4, 2>), grid, dim3(512), 0, st, set, X, ldx, m, kb, G,
+                       c.splits, c.kbps, part, tick);
+  else if (c.mb == 128)
     hipLaunchKernelGGL((k_gemm_lds<B, 128, 3, true>), grid, dim3(256), 0, st, set, X, ldx, m, kb,
                        G, c.splits, c.kbps, part, tick);
   else if (c.mb == 64)

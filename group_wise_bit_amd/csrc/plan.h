@@ -71,6 +71,11 @@ struct GemmPlan {
 struct TilesCfg { int mb, gx, gy, splits, kbps; bool dual, half; };
 
 constexpr int kMbKsplit128 = 6;
+// mb = 8: k_gemm_wdec, 128 X rows x two tiles (a gate/up pair's tile t, or
+// tiles 2x and 2x + 1 of one matrix: gx in tile pairs, pairable sets only),
+// each weight decoded once per work-group into LDS
+constexpr int kMbWdec = 8;
+constexpr int kWdecRows = 128;
 // the K-split kernel's forms and their X rows
 inline bool is_ksplit(int mb) { return mb <= 1 || mb == kMbKsplit128; }
 inline int ksplit_rows(int mb) { return mb == kMbKsplit128 ? 128 : 32 * (mb + 1); }

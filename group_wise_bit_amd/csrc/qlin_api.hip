@@ -434,10 +434,22 @@ TilesCfg tiles_config(int64_t gx, int64_t tiles, int kb, int m, int count, bool 
     // 16.5 us)
     c.dual = c.mb <= 1;
   }
+  if (m > 64 && m <= 256 && pairable && kb >= 128) {
+    // very long K (the Qwen3-8B down projection, 4096 x 12288, at M = 128):
+    // 128 X rows over tile pairs, each weight decoded once per work-group,
+    // K split to about one work-group per CU (int4: 35.1 -> 32.9 us against
+    // the K-split kernel; 8 splits 32.9, 4 splits 41.7 us)
+    c.mb = kMbWdec;
+    c.dual = c.half = false;
+    const int64_t g = ((tiles + 1) / 2) * ((m + kWdecRows - 1) / kWdecRows);
+    want = g >= 256 ? 1 : (int)((256 + g - 1) / g);
+    if (want > 8) want = 8;
+  }
   // a GEMM launch-shape override (form, splits; sweeps and tests) replaces
   // the choice: form 0 / 1 the K-split kernel with 32 / 64 X rows, 2 / 3 the
   // same with 64 / 32 X rows over tile pairs, 4 / 5 with 32 / 64 X rows over
-  // half tiles, 6 / 7 with 128 X rows (whole / half tiles)
+  // half tiles, 6 / 7 with 128 X rows (whole / half tiles), 8 the
+  // decode-once form
   {
     int mb, sp, unused;
     if (launch_override(QLIN_TUNE_GEMM, mb, sp, unused) && mb != 16) {
@@ -449,14 +461,17 @@ TilesCfg tiles_config(int64_t gx, int64_t tiles, int kb, int m, int count, bool 
     }
   }
   if (!pairable) c.dual = false;       // tile pairs within one matrix only
+  if (c.mb == kMbWdec && !pairable) c.mb = 0;
   if (want < 1) want = 1;
-  const bool ks = is_ksplit(c.mb);
+  const bool ks = is_ksplit(c.mb), wd = c.mb == kMbWdec;
   if (!ks) c.dual = c.half = false;
   if (c.mb == kMbKsplit128) c.dual = false;
   if (ks) c.gx = (int)(c.dual ? (tiles + 1) / 2 : c.half ? 2 * tiles : tiles);
-  const int rows = ks ? ksplit_rows(c.mb) : c.mb;
+  if (wd) c.gx = (int)((tiles + 1) / 2);
+  const int rows = ks ? ksplit_rows(c.mb) : wd ? kWdecRows : c.mb;
   const int64_t wg_outputs =
-      (int64_t)rows * (ks ? (c.dual ? 2 * kTile : c.half ? kTile / 2 : kTile) : 256);
+      (int64_t)rows * (ks ? (c.dual ? 2 * kTile : c.half ? kTile / 2 : kTile)
+                          : wd ? 2 * kTile : 256);
   c.gy = (m + rows - 1) / rows;
   if ((int64_t)c.gx * c.gy > kMaxSplitTiles) want = 1;
   while (want > 1 && kCounterBytes + (int64_t)want * c.gy * c.gx * wg_outputs * 4 > ws_bytes)
@@ -472,7 +487,8 @@ int64_t tiles_ws_bytes(int64_t gx, int64_t tiles, int kb, int m, int count, bool
   if (c.splits <= 1) return 0;
   const int64_t wg_outputs =
       is_ksplit(c.mb) ? ksplit_rows(c.mb) * (c.dual ? 2 * kTile : c.half ? kTile / 2 : kTile)
-                : (int64_t)c.mb * 256;
+      : c.mb == kMbWdec ? (int64_t)kWdecRows * 2 * kTile
+                        : (int64_t)c.mb * 256;
   return kCounterBytes + (int64_t)c.splits * c.gy * c.gx * wg_outputs * 4;
 }
 
@@ -538,24 +554,35 @@ TilesCfg swiglu_config(int64_t tiles, int kb, int m, int64_t ws_bytes) {
       if (cols2 * ((m + 63) / 64) < 256) c.mb = 1;
     }
   }
+  if (m > 64 && m <= 256 && tiles * ((m + kWdecRows - 1) / kWdecRows) >= 128) {
+    // many tiles over long K (the Qwen3-8B gate/up pair, 12288 x 4096, at
+    // M = 128: 192 work-groups): 128 X rows x tile t of both matrices, each
+    // weight decoded once per work-group (int4: 51.5 -> 47.2 us against the
+    // K-split pair; a K split measured slower: 61.6 us at 2 splits)
+    c.mb = kMbWdec;
+    c.half = false;
+    want = 1;
+  }
   // a GEMM launch-shape override (form, splits) replaces the choice (form 32
-  // runs as 64; 4 / 5: the K-split pair over half tiles with 32 / 64 X rows)
+  // runs as 64; 4 / 5: the K-split pair over half tiles with 32 / 64 X rows;
+  // 8: the decode-once form)
   {
     int mb, sp, unused;
     if (launch_override(QLIN_TUNE_GEMM, mb, sp, unused) &&
-        (mb <= 1 || (mb >= 4 && mb <= 7) || mb == 32 || mb == 64 || mb == 128)) {
+        (mb <= 1 || (mb >= 4 && mb <= 8) || mb == 32 || mb == 64 || mb == 128)) {
       c.mb = mb == 32 ? 64 : mb == 4 ? 0 : mb == 5 ? 1 : (mb == 6 || mb == 7) ? kMbKsplit128 : mb;
       c.half = mb == 4 || mb == 5;
       want = sp < kb ? sp : kb;
     }
   }
   if (want < 1) want = 1;
-  const bool ks = is_ksplit(c.mb);
+  const bool ks = is_ksplit(c.mb), wd = c.mb == kMbWdec;
   if (!ks) c.half = false;
   if (c.mb == kMbKsplit128) c.half = true;     // two accumulator sets: half tiles only
-  c.gx = (int)(ks ? (c.half ? 2 * tiles : tiles) : cols2);
-  const int rows = ks ? ksplit_rows(c.mb) : c.mb;
-  const int64_t wg_outputs = (int64_t)rows * (ks ? (c.half ? kTile : 2 * kTile) : 256);
+  c.gx = (int)(ks ? (c.half ? 2 * tiles : tiles) : wd ? tiles : cols2);
+  const int rows = ks ? ksplit_rows(c.mb) : wd ? kWdecRows : c.mb;
+  const int64_t wg_outputs =
+      (int64_t)rows * (ks ? (c.half ? kTile : 2 * kTile) : wd ? 2 * kTile : 256);
   c.gy = (m + rows - 1) / rows;
   if ((int64_t)c.gx * c.gy > kMaxSplitTiles) want = 1;
   while (want > 1 && kCounterBytes + (int64_t)want * c.gy * c.gx * wg_outputs * 4 > ws_bytes)
@@ -570,7 +597,9 @@ int64_t swiglu_ws_bytes(int64_t tiles, int kb, int m) {
   if (c.splits <= 1) return 0;
   const bool ks = is_ksplit(c.mb);
   const int64_t wg_outputs =
-      ks ? ksplit_rows(c.mb) * (c.half ? kTile : 2 * kTile) : (int64_t)c.mb * 256;
+      ks ? ksplit_rows(c.mb) * (c.half ? kTile : 2 * kTile)
+      : c.mb == kMbWdec ? (int64_t)kWdecRows * 2 * kTile
+                        : (int64_t)c.mb * 256;
   return kCounterBytes + (int64_t)c.splits * c.gy * c.gx * wg_outputs * 4;
 }
 
@@ -1071,7 +1100,7 @@ qlin_status qlin_set_launch_override(int32_t family, const int32_t* params) {
   if (b < 1 || b > 0xFFFF) return QLIN_ERR_SHAPE;
   if (family == QLIN_TUNE_GEMV) {
     if (!(a == 4 || a == 8 || a == 16) || !(c == 8 || c == 16 || c == 64)) return QLIN_ERR_SHAPE;
-  } else if (!((a >= 0 && a <= 7) || a == 16 || a == 32 || a == 64 || a == 128)) {
+  } else if (!((a >= 0 && a <= 8) || a == 16 || a == 32 || a == 64 || a == 128)) {
     return QLIN_ERR_SHAPE;
   }
   g_override[family].store((1ull << 63) | (uint64_t)(uint32_t)a | ((uint64_t)(uint32_t)b << 16) |

@@ -17,8 +17,10 @@
  *   QLIN_TUNE_GEMM: params[0] = kernel form (0 / 1: K-split kernel with 32 /
  *     64 X rows; 2 / 3: the same with 64 / 32 X rows over tile pairs; 4 / 5:
  *     with 32 / 64 X rows over half tiles; 6 / 7: with 128 X rows over whole /
- *     half tiles (the SwiGLU pair always over half tiles); 16: the skinny
- *     kernel at m <= 16;
+ *     half tiles (the SwiGLU pair always over half tiles); 8: 128 X rows x
+ *     a tile pair (the SwiGLU pair: tile t of gate and of up), each weight
+ *     decoded once per work-group (a set whose matrices do not all have an
+ *     even tile count runs form 0 instead); 16: the skinny kernel at m <= 16;
  *     32 / 64 / 128: tiled kernels with that X-tile height), params[1] = K
  *     splits across work-groups (>= 1).
  * Returns QLIN_OK, or QLIN_ERR_SHAPE for an unknown family or a value out of

@@ -367,7 +367,8 @@ def test_launch_override_validation(lib):
     assert ov(1, (128, 3, 0)) == OK
     assert ov(1, (16, 1, 0)) == OK
     assert ov(1, (7, 1, 0)) == OK
-    assert ov(1, (8, 1, 0)) == SHAPE
+    assert ov(1, (8, 1, 0)) == OK
+    assert ov(1, (9, 1, 0)) == SHAPE
     assert ov(1, (96, 1, 0)) == SHAPE
     assert ov(1, None) == OK
     assert ov(2, (16, 1, 64)) == SHAPE

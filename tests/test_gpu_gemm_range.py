@@ -63,11 +63,11 @@ def check(Y, X, what, label):
 
 
 # (form, splits, m): K-split 32 / 64 / 128 X rows (whole, pairs, halves),
-# the skinny kernel, the tiled kernels
+# weights decoded once per work-group, the skinny kernel, the tiled kernels
 FORMS = [(None, 1, 8), (None, 1, 100), (None, 1, 300), ("0,1", 1, 40), ("0,2", 2, 40),
          ("1,1", 1, 100), ("2,1", 1, 100), ("3,2", 2, 40), ("4,1", 1, 8), ("5,1", 1, 100),
-         ("6,1", 1, 128), ("7,2", 2, 128), ("16,1", 1, 8), ("32,1", 1, 300), ("64,1", 1, 300),
-         ("128,2", 2, 300)]
+         ("6,1", 1, 128), ("7,2", 2, 128), ("8,1", 1, 128), ("8,3", 3, 300), ("16,1", 1, 8),
+         ("32,1", 1, 300), ("64,1", 1, 300), ("128,2", 2, 300)]
 
 
 @pytest.mark.parametrize("bits", [2, 3, 4, 5, 6, 7, 8])
@@ -99,7 +99,8 @@ def test_gemm_fp16_operand_range(bits, where, form, splits, m, launch_override):
 
 @pytest.mark.parametrize("bits", [2, 4, 8])
 @pytest.mark.parametrize("form,m", [(None, 8), (None, 128), (None, 2048), ("1,1", 100),
-                                    ("4,1", 40), ("7,1", 128), ("64,1", 300)])
+                                    ("4,1", 40), ("7,1", 128), ("8,1", 128), ("8,2", 300),
+                                    ("64,1", 300)])
 def test_gemm_swiglu_fp16_operand_range(bits, form, m, launch_override):
     launch_override("gemm", form)
     n, k = 192, 640

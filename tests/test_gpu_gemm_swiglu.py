@@ -140,10 +140,11 @@ def test_gemm_swiglu_prefill_m2048(bits, launch_override):
 
 
 # "mb,splits": K-split with 32 (0) / 64 (1) X rows, the same over half tiles
-# (4 / 5), LDS pipeline with 64 / 128 X rows (32 runs as 64), with and without
-# a K split across work-groups
-FORCED = ["0,1", "0,3", "1,1", "1,2", "4,1", "4,3", "5,1", "5,2", "6,1", "7,2", "32,1", "64,1",
-          "64,2", "128,1", "128,3"]
+# (4 / 5), the form decoding each weight once per work-group (8), LDS
+# pipeline with 64 / 128 X rows (32 runs as 64), with and without a K split
+# across work-groups
+FORCED = ["0,1", "0,3", "1,1", "1,2", "4,1", "4,3", "5,1", "5,2", "6,1", "7,2", "8,1", "8,2",
+          "32,1", "64,1", "64,2", "128,1", "128,3"]
 
 
 @pytest.mark.parametrize("bits", [2, 3, 4, 5, 6, 7, 8])
