@@ -204,6 +204,11 @@ GemvCfg gemv_config(int64_t tiles, int kb, GemvKind kind, int bits, int64_t ws_b
     rows = ((pair && tiles < 64) || (!pair && tiles >= 48)) ? 16 : 8;
     waves = ((pair && tiles < 64) || kb >= 32) ? 16 : 8;
     if (kb >= 128) splits = kb / 64;   // very long K over a few tiles
+  } else if (tiles > 64 && kb < 128 && (bits == 2 || bits == 4) && !pair) {
+    // 65-128 tiles over medium K at 2 and 4 bits: whole tiles, 16 waves, no
+    // split (the Qwen3-8B q/k/v set, 96 tiles x 64 K-blocks: int4 6.23 ->
+    // 5.68 us, int2 5.76 -> 5.55 us against four splits; int3 6.24 -> 6.62 us,
+    // so 3 bits keeps the split)
   } else {
     splits = kb >= 128 ? kb / 64 : kb / 16;
   }
