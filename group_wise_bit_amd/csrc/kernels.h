@@ -1931,15 +1931,20 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_ksplit(
 // work-group's range.  Per K-block, wave q of the group decodes column block q
 // -- 32 W rows (32 (q % 2) + c of tile q / 2) x 64 K -- into the group's LDS
 // buffers as the MFMA B fragments (lane (c, h), instruction s: K positions
-// 32h + 8s .. +7), so each weight is decoded once per work-group; every wave
-// of the group multiplies its 32 X rows (A fragments straight from global
-// memory; lane (c, h): X row 32q + c) by all four column blocks: 16 MFMAs per
-// wave per K-block against one block decode.  The wave decodes its next block
-// between the MFMAs of the current one, into the other of its group's two
-// buffers: a wave that writes a buffer has passed the barrier that every wave
-// reaches only after multiplying the block that buffer held before, so one
-// barrier per step suffices.  The codes, scales and zeros of the group's next
-// D blocks and the X fragments of its next block are in flight meanwhile.
+// 32h + 8s .. +7), so each weight is decoded once per work-group; the group's
+// 256 threads copy the block's 128 x 64 X tile into the same buffer with
+// coalesced 16-byte loads (chunk k of row r at position k ^ (r % 8) of the
+// row, so that these writes and the A-fragment reads fall on distinct
+// banks); every wave of the group multiplies its 32 X rows (lane (c, h): X
+// row 32q + c) by all four column blocks: 16 MFMAs per wave per K-block
+// against one block decode.  The wave decodes its next block between the
+// MFMAs of the current one, into the other of its group's two buffers: a wave
+// that writes a buffer has passed the barrier that every wave reaches only
+// after multiplying the block that buffer held before, so one barrier per
+// step suffices.  The codes, scales, zeros and X chunks of the group's next
+// D blocks are in flight meanwhile, in register slots (loads complete in
+// order, so a wait for one load is a wait for every older one: everything a
+// step waits for was requested D steps before).
 // With KG = 2 each SIMD runs two instruction streams (one wave of each
 // group); the groups meet at every step's barrier (a group with no block
 // left in a step only takes part in the barrier) and finally add their sums
