@@ -176,8 +176,7 @@ GemvCfg gemv_config(int64_t tiles, int kb, GemvKind kind, int bits, int64_t ws_b
   // trips.  So the packed kernels narrow the work-group first (8 or 16 rows
   // over 8 / 4 slices of each block) while tiles x K-blocks <= 4096, and split
   // K when one wave would otherwise decode many blocks in sequence (long K
-  // over up to 128 tiles; 3-bit decode, the costliest, also over 129-256
-  // tiles).  Launches of many tiles use 4-wave work-groups, so that the tail
+  // over up to 128 tiles).  Launches of many tiles use 4-wave work-groups, so that the tail
   // of the grid is short.  The fused kernel reads 2 bytes per weight and does
   // about 7 VALU ops per weight: 8-row work-groups up to 256 tiles (16 waves,
   // 8 for short K over many tiles), whole tiles beyond.
@@ -194,10 +193,9 @@ GemvCfg gemv_config(int64_t tiles, int kb, GemvKind kind, int bits, int64_t ws_b
   } else if (tiles > 256) {
     waves = 4;
   } else if (tiles > 128) {
-    if (bits == 3) {
-      waves = 8;
-      splits = 4;
-    }
+    // whole tiles, 16 waves, no split at every width (3 bits took 8 waves x 4
+    // splits until the zero point was folded; now the Qwen3-8B gate at int3
+    // 7.85 -> 7.00 us and its gate/up pair 12.3 -> 11.9 us without the split)
   } else if (tiles * kb <= 4096) {
     // (a gate/up pair of 64+ tiles: 8-row, 8-wave work-groups; Qwen2.5-0.5B
     // gate/up 4.6 -> 4.4 us)
